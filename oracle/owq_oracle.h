@@ -1,0 +1,77 @@
+/*
+ * owq_oracle.h -- plain CPU oracle of the OWQ hot path (TEST INFRASTRUCTURE).
+ *
+ * Only the test-suite, the package smoke check and the CPU-baseline leg of the
+ * benchmark may load this library. The GPU library shares no code with it.
+ *
+ * Pages cited in this file and in owq_oracle.c:
+ *   [PL] paperlayer.ai, "OWQ: Outlier-Aware Weight Quantization for Efficient
+ *        Fine-Tuning and Inference of Large Language Models" (per-section notes;
+ *        each cited heading names the paper section and page it summarises).
+ *   [EL] research.elamur.ai, "OWQ -- paper by Lee et al. (2023) -- summary and ideas".
+ *
+ * Data conventions: fp16 values are IEEE binary16 bit patterns (uint16_t).
+ * W is [N][K] row-major (row i = output channel, column j = input channel).
+ * X is [T][K] calibration activations, x is [M][K] layer input, y is [M][N].
+ * Packed codes: uint32 [N][K/32][3]; code c of a 32-column group occupies bits
+ * [3c, 3c+3) of the 96-bit little-endian integer w0 | w1<<32 | w2<<64.
+ */
+#ifndef OWQ_ORACLE_H
+#define OWQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* IEEE binary16 -> binary64, exact. */
+double owq_oracle_f16_to_f64(uint16_t h);
+/* IEEE binary32 -> binary16, round to nearest, ties to even. */
+uint16_t owq_oracle_f32_to_f16(float f);
+
+/* Min-max step size and zero point of one row over the columns with use[j] != 0
+ * (use == NULL: every column). Writes the fp16 step bits and the zero point. */
+void owq_oracle_qparams(const uint16_t* row, const uint8_t* use, int64_t K,
+                        uint16_t* s16, uint8_t* z);
+/* Round-to-nearest 3-bit code of one weight under (s16, z). */
+int owq_oracle_code(uint16_t w, uint16_t s16, uint8_t z);
+
+/* lambda[j] = 2 * sum_t X[t][j]^2 (Hessian diagonal), fp64. */
+void owq_oracle_hessian_diag(const uint16_t* X, int64_t T, int64_t K, double* lambda);
+/* e[j] = sum_i (W[i][j] - deq(code(W[i][j])))^2 under each row's full-row fit. */
+void owq_oracle_rtn_col_err(const uint16_t* W, int64_t N, int64_t K, double* e);
+/* lambda and score[j] = lambda[j] * e[j]. */
+void owq_oracle_calibrate_score(const uint16_t* W, int64_t N, int64_t K,
+                                const uint16_t* X, int64_t T,
+                                double* lambda, double* score);
+/* The k columns of largest score (ties: lower index first), written ascending. */
+void owq_oracle_select_weak(const double* score, int64_t K, int32_t k, int32_t* weak_idx);
+
+/* Latency-favoured pack: dense codes with weak columns set to the zero point,
+ * per-row fp16 step and uint8 zero, and the fp16 weak columns [N][k]. */
+void owq_oracle_pack(const uint16_t* W, int64_t N, int64_t K,
+                     const int32_t* weak_idx, int32_t k,
+                     uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                     uint16_t* w_weak);
+/* Inverse of the bit layout: codes [N][K] (values 0..7). */
+void owq_oracle_unpack_codes(const uint32_t* qcodes, int64_t N, int64_t K, uint8_t* codes);
+
+/* y and the error bound for P (token m, row i) pairs, from the packed layer.
+ * y[p]     = sum_j s_i (q_ij - z_i) x[m][j] + sum_c w_weak[i][c] x[m][idx_c]
+ * bound[p] = sum_j |s_i (q_ij - z_i) x[m][j]| + sum_c |w_weak[i][c] x[m][idx_c]| */
+void owq_oracle_linear_pairs(const uint32_t* qcodes, const uint16_t* scales,
+                             const uint8_t* zeros, int64_t N, int64_t K,
+                             const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,
+                             const uint16_t* x, int64_t M,
+                             const int64_t* pm, const int64_t* pi, int64_t P,
+                             double* y, double* bound);
+
+/* Effective bits per weight: 3 + 13k/K (storage-favoured) or 3 + 16k/K
+ * (latency-favoured, zero-filled dense matrix kept). */
+double owq_oracle_effective_bits(int64_t K, int64_t k, int latency_favored);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,114 @@
+"""Pins of the oracle's pack layout and mixed-precision linear.
+
+P9  an independent packer (Python integers, 96-bit groups) produces the same
+    bytes, and unpack(pack) recovers the codes.
+P7  k = 0 reduces y to the plain RTN matvec; k = K reduces y to the fp16
+    product W x; for any k the weak columns contribute exactly their fp16
+    product and their dense codes dequantise to 0.
+P1  bytes emitted by the pack give 3 + 16 k / K bits per weight.
+"""
+import numpy as np
+import pytest
+
+from mixed_precision_weight_amd import synth
+
+
+def _pack_python(codes: np.ndarray) -> np.ndarray:
+    N, K = codes.shape
+    out = np.zeros((N, K // 32, 3), np.uint32)
+    for i in range(N):
+        for g in range(K // 32):
+            B = 0
+            for c in range(32):
+                B |= int(codes[i, 32 * g + c]) << (3 * c)
+            for r in range(3):
+                out[i, g, r] = (B >> (32 * r)) & 0xFFFFFFFF
+    return out
+
+
+def test_pack_bytes_independent_packer(orc):
+    rng = np.random.default_rng(3)
+    W = synth.random_layer(rng, 9, 128)
+    idx = np.array([5, 40, 41, 127], np.int32)
+    p = orc.pack(W, idx)
+    codes = orc.unpack_codes(p["qcodes"], 128)
+    assert np.array_equal(_pack_python(codes), p["qcodes"])
+    # random code patterns round-trip through the independent packer + oracle unpack
+    rc = rng.integers(0, 8, (5, 96)).astype(np.uint8)
+    assert np.array_equal(orc.unpack_codes(_pack_python(rc), 96), rc)
+    # single-code patterns land where the bit order says (codes 10 and 21 straddle words)
+    for c, val in [(0, 7), (10, 5), (21, 6), (31, 7)]:
+        one = np.zeros((1, 32), np.uint8)
+        one[0, c] = val
+        q = _pack_python(one)[0, 0]
+        B = int(q[0]) | (int(q[1]) << 32) | (int(q[2]) << 64)
+        assert B == val << (3 * c)
+        assert np.array_equal(orc.unpack_codes(q.reshape(1, 1, 3), 32), one)
+
+
+def test_weak_columns_zero_filled_and_copied(orc):
+    rng = np.random.default_rng(4)
+    W = synth.random_layer(rng, 16, 64)
+    idx = np.array([0, 7, 33, 63], np.int32)
+    p = orc.pack(W, idx)
+    codes = orc.unpack_codes(p["qcodes"], 64)
+    for i in range(16):
+        assert (codes[i, idx] == p["zeros"][i]).all()
+    assert np.array_equal(p["w_weak"], W.view(np.uint16)[:, idx])
+    # the dense fit ignores the weak columns: planting a huge value there changes nothing
+    W2 = W.copy()
+    W2[:, 7] = np.float16(1000.0)
+    p2 = orc.pack(W2, idx)
+    assert np.array_equal(p2["scales"], p["scales"]) and np.array_equal(p2["zeros"], p["zeros"])
+    assert np.array_equal(p2["qcodes"], p["qcodes"])
+
+
+def test_linear_k0_is_rtn_matvec(orc):
+    rng = np.random.default_rng(5)
+    W = synth.random_layer(rng, 40, 96)
+    x = rng.standard_normal((3, 96)).astype(np.float16)
+    p = orc.pack(W, [])
+    codes = orc.unpack_codes(p["qcodes"], 96).astype(np.float64)
+    s = p["scales"].view(np.float16).astype(np.float64)
+    z = p["zeros"].astype(np.float64)
+    Wq = s[:, None] * (codes - z[:, None])
+    y, b = orc.linear_full(p, x)
+    ref = x.astype(np.float64) @ Wq.T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-15)
+    assert np.allclose(b, np.abs(x.astype(np.float64)) @ np.abs(Wq).T, rtol=1e-12, atol=1e-15)
+
+
+def test_linear_kK_is_fp16_matvec(orc):
+    rng = np.random.default_rng(6)
+    K = 64
+    W = synth.random_layer(rng, 24, K)
+    x = rng.standard_normal((2, K)).astype(np.float16)
+    p = orc.pack(W, np.arange(K, dtype=np.int32))
+    assert (p["scales"] == 0x3C00).all() and (p["zeros"] == 0).all()
+    y, _ = orc.linear_full(p, x)
+    ref = x.astype(np.float64) @ W.astype(np.float64).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_weak_contribution_exact(orc):
+    rng = np.random.default_rng(8)
+    K = 128
+    W = synth.random_layer(rng, 30, K)
+    x = rng.standard_normal((2, K)).astype(np.float16)
+    idx = np.array([1, 2, 50, 99, 127], np.int32)
+    p = orc.pack(W, idx)
+    y, _ = orc.linear_full(p, x)
+    # dense part alone: same codes with no weak columns attached
+    dense_only = dict(p, weak_idx=np.zeros(0, np.int32), w_weak=np.zeros((30, 0), np.uint16))
+    yd, _ = orc.linear_full(dense_only, x)
+    weak = x.astype(np.float64)[:, idx] @ W.astype(np.float64)[:, idx].T
+    assert np.allclose(y - yd, weak, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("N,K,k", [(768, 768, 6), (100, 4096, 32), (64, 11008, 86)])
+def test_emitted_bytes_match_effective_bits(orc, N, K, k):
+    W = np.zeros((N, K), np.float16)
+    p = orc.pack(W, np.arange(k, dtype=np.int32))
+    bits = 8 * (p["qcodes"].nbytes + p["w_weak"].nbytes) / (N * K)
+    assert bits == pytest.approx(orc.effective_bits(K, k, True), rel=1e-15)
+    assert p["w_weak"].shape == (N, k)
