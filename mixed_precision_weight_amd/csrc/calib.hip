@@ -1,0 +1,239 @@
+// calib.hip -- calibration kernels: Hessian diagonal, row fit, column RTN errors,
+// column scores (gfx950).
+//
+// The layer-wise error ||W X^T - W^ X^T||^2 splits into one quadratic error per
+// output row, all sharing the Hessian H = 2 X^T X ([PL] "Error Decomposition",
+// "Error Analysis", paper p.3 and appendix section 1 p.10). Column sensitivity
+// is the Hessian diagonal element times the squared perturbation norm of the
+// column ([PL] "Weak-column selection", paper p.4):
+//     lambda_j = 2 sum_t X[t][j]^2,   e_j = sum_i dW_ij^2,   score_j = lambda_j e_j,
+// with dW the round-to-nearest error of a full-row min-max fit.
+// [PL] = paperlayer.ai page "OWQ: Outlier-Aware Weight Quantization for
+// Efficient Fine-Tuning and Inference of Large Language Models".
+//
+// Both sums are column reductions of an fp16 [R][K] matrix streamed from HBM.
+// Kernel shape (HBM-bound): a 256-thread block owns a 64-column tile of one row
+// slice. Lane (wave w, lane l) reads 8 columns (16 B) at column 8*(l%8) of rows
+// w*8 + l/8 + 32 t, so each wave instruction reads 8 full 128-byte lines. Squares
+// of fp16 values and of the (exact) fp32 RTN errors are accumulated in fp64; the
+// 32 row phases are combined by a fixed butterfly and a fixed-order LDS sum,
+// and row slices by a fixed-order second pass: results are bitwise deterministic.
+//
+// Built with -ffp-contract=off: the quantiser steps are single IEEE operations.
+#include "owq_device.h"
+#include "owq_launch.h"
+
+namespace owq {
+
+namespace {
+
+constexpr int kTileCols = 64;   // columns per block tile
+constexpr int kPhases = 32;     // row phases per block (4 waves x 8)
+constexpr int kUnroll = 4;      // rows in flight per lane
+
+struct SqElem {  // x^2 (exact in fp32 for fp16 x)
+    __device__ __forceinline__ void row(int64_t) {}
+    __device__ __forceinline__ float val(uint16_t h) const
+    {
+        float v = h2f(h);
+        return v * v;
+    }
+    static constexpr bool kSquared = true;
+};
+
+struct ErrElem {  // dW = w - s (q - z), exact in fp32; squared in fp64 by the caller
+    const uint16_t* s16;
+    const uint8_t* z;
+    float sf;
+    int zi;
+    __device__ __forceinline__ void row(int64_t r)
+    {
+        sf = h2f(s16[r]);
+        zi = z[r];
+    }
+    __device__ __forceinline__ float val(uint16_t h) const
+    {
+        float w = h2f(h);
+        int q = rtn_code(w, sf, zi);
+        return w - sf * (float)(q - zi);
+    }
+    static constexpr bool kSquared = false;
+};
+
+template <class Elem>
+__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ A, int64_t R, int64_t K,
+                                                int64_t rows_per_slice, double* __restrict__ partial,
+                                                Elem elem)
+{
+    __shared__ double red[4][kTileCols];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cc = lane & 7;
+    const int phase = wave * 8 + (lane >> 3);
+    const int64_t col = (int64_t)blockIdx.x * kTileCols + cc * 8;
+    const bool active = col < K;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_slice;
+    const int64_t r1 = min(R, r0 + rows_per_slice);
+
+    double acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; c++)
+        acc[c] = 0.0;
+
+    for (int64_t rb = r0 + phase; rb < r1; rb += (int64_t)kPhases * kUnroll) {
+        uint4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            int64_t r = rb + (int64_t)u * kPhases;
+            v[u] = (active && r < r1) ? *reinterpret_cast<const uint4*>(A + r * K + col)
+                                      : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            int64_t r = rb + (int64_t)u * kPhases;
+            if (!(active && r < r1))
+                continue;
+            elem.row(r);
+            uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int c = 0; c < 8; c++) {
+                uint16_t h = (uint16_t)(w[c >> 1] >> (16 * (c & 1)));
+                float e = elem.val(h);
+                if (Elem::kSquared)
+                    acc[c] += (double)e;
+                else
+                    acc[c] += (double)e * (double)e;
+            }
+        }
+    }
+    // combine the 8 row phases of this wave (lanes differing in bits 3..5)
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        acc[c] += shfl_xor_f64(acc[c], 8);
+        acc[c] += shfl_xor_f64(acc[c], 16);
+        acc[c] += shfl_xor_f64(acc[c], 32);
+    }
+    if (lane < 8) {
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+            red[wave][lane * 8 + c] = acc[c];
+    }
+    __syncthreads();
+    if (threadIdx.x < kTileCols) {
+        int64_t j = (int64_t)blockIdx.x * kTileCols + threadIdx.x;
+        if (j < K) {
+            double t = red[0][threadIdx.x];
+            t += red[1][threadIdx.x];
+            t += red[2][threadIdx.x];
+            t += red[3][threadIdx.x];
+            partial[(int64_t)blockIdx.y * K + j] = t;
+        }
+    }
+}
+
+// One wave per row: min/max over all K columns -> (fp16 step, zero point).
+__global__ __launch_bounds__(256) void k_rowfit(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                                uint16_t* __restrict__ s16, uint8_t* __restrict__ z)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= N)
+        return;
+    const uint4* p = reinterpret_cast<const uint4*>(W + row * K);
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t c = lane; c < K / 8; c += 64) {
+        uint4 v = p[c];
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float f = h2f((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
+            lo = fminf(lo, f);
+            hi = fmaxf(hi, f);
+        }
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+        uint16_t s;
+        int zz;
+        qparams_from_range(lo, hi, s, zz);
+        s16[row] = s;
+        z[row] = (uint8_t)zz;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ px, int64_t sx,
+                                                  const double* __restrict__ pw, int64_t sw, int64_t K,
+                                                  double* __restrict__ lambda, double* __restrict__ score)
+{
+    int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= K)
+        return;
+    double l = 0.0;
+    for (int64_t s = 0; s < sx; s++)
+        l += px[s * K + j];
+    l *= 2.0;
+    double e = 0.0;
+    for (int64_t s = 0; s < sw; s++)
+        e += pw[s * K + j];
+    lambda[j] = l;
+    score[j] = l * e;
+}
+
+int64_t choose_slices(int64_t R, int64_t K)
+{
+    int64_t tiles = (K + kTileCols - 1) / kTileCols;
+    int64_t s = (1024 + tiles - 1) / tiles;           // ~1024 blocks in flight
+    int64_t cap = (R + 2 * kPhases - 1) / (2 * kPhases);  // >= 2 rows per phase
+    if (s > cap)
+        s = cap;
+    if (s > 65535)
+        s = 65535;
+    return s < 1 ? 1 : s;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+CalibPlan calib_plan(int64_t N, int64_t K, int64_t T)
+{
+    CalibPlan p;
+    p.sx = choose_slices(T, K);
+    p.sw = choose_slices(N, K);
+    p.rows_x = (T + p.sx - 1) / p.sx;
+    p.rows_w = (N + p.sw - 1) / p.sw;
+    size_t o = 0;
+    p.off_px = o;
+    o = align256(o + (size_t)p.sx * K * sizeof(double));
+    p.off_pw = o;
+    o = align256(o + (size_t)p.sw * K * sizeof(double));
+    p.off_s16 = o;
+    o = align256(o + (size_t)N * sizeof(uint16_t));
+    p.off_z = o;
+    o = align256(o + (size_t)N);
+    p.total = o;
+    return p;
+}
+
+hipError_t launch_calibrate(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,
+                            double* lambda, double* score, void* ws, const CalibPlan& p,
+                            hipStream_t s)
+{
+    char* base = static_cast<char*>(ws);
+    double* px = reinterpret_cast<double*>(base + p.off_px);
+    double* pw = reinterpret_cast<double*>(base + p.off_pw);
+    uint16_t* s16 = reinterpret_cast<uint16_t*>(base + p.off_s16);
+    uint8_t* z = reinterpret_cast<uint8_t*>(base + p.off_z);
+    const unsigned tiles = (unsigned)((K + kTileCols - 1) / kTileCols);
+
+    hipLaunchKernelGGL(k_colsum<SqElem>, dim3(tiles, (unsigned)p.sx), dim3(256), 0, s, X, T, K,
+                       p.rows_x, px, SqElem{});
+    hipLaunchKernelGGL(k_rowfit, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, W, N, K, s16, z);
+    hipLaunchKernelGGL(k_colsum<ErrElem>, dim3(tiles, (unsigned)p.sw), dim3(256), 0, s, W, N, K,
+                       p.rows_w, pw, ErrElem{s16, z, 1.0f, 0});
+    hipLaunchKernelGGL(k_finalize, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, px, p.sx, pw,
+                       p.sw, K, lambda, score);
+    return hipGetLastError();
+}
+
+}  // namespace owq

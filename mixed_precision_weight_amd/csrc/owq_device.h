@@ -1,0 +1,91 @@
+// owq_device.h -- device helpers shared by the gfx950 kernels of libowq.
+//
+// fp16 values travel as IEEE binary16 bit patterns (uint16_t). Conversions use
+// the hardware's round-to-nearest-even (v_cvt_f16_f32) and exact widening.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace owq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// ---------------------------------------------------------------- quantiser --
+// Min-max round-to-nearest on a 3-bit asymmetric grid (7 steps). The range
+// [lo, hi] always contains 0. Step: fp32 (hi - lo) / 7, IEEE division, rounded
+// once to fp16; zero point: rint(-lo / step) clamped to [0, 7]; a row with
+// hi == lo, or whose step rounds to fp16 zero, uses step 1 and zero point 0.
+// code(w) = clamp(rint(w / step) + z, 0, 7) with rint = round half to even.
+// These are the same IEEE operations, in the same order, as the definition;
+// the translation units that call them are compiled without FMA contraction.
+__device__ __forceinline__ void qparams_from_range(float lo, float hi, uint16_t& s16, int& z)
+{
+    if (hi == lo) {
+        s16 = 0x3c00;
+        z = 0;
+        return;
+    }
+    float s32 = (hi - lo) / 7.0f;
+    uint16_t s = f2h(s32);
+    if ((s & 0x7fff) == 0) {
+        s16 = 0x3c00;
+        z = 0;
+        return;
+    }
+    float sf = h2f(s);
+    float zr = rintf(-lo / sf);
+    z = zr < 0.0f ? 0 : (zr > 7.0f ? 7 : (int)zr);
+    s16 = s;
+}
+
+__device__ __forceinline__ int rtn_code(float w, float sf, int z)
+{
+    float r = rintf(w / sf);
+    r = fminf(fmaxf(r, -8.0f), 8.0f);  // keeps the conversion defined; clamp below saturates anyway
+    int q = (int)r + z;
+    return q < 0 ? 0 : (q > 7 ? 7 : q);
+}
+
+// ---------------------------------------------------------- wave reductions --
+// Butterfly over the 64 lanes of a wavefront (deterministic order; every lane
+// ends with the full result).
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_min(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = fminf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int o)
+{
+    uint64_t b = __builtin_bit_cast(uint64_t, v);
+    uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+    lo = __shfl_xor(lo, o, 64);
+    hi = __shfl_xor(hi, o, 64);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+}  // namespace owq

@@ -1,0 +1,147 @@
+// pack.hip -- latency-favoured OWQ storage of one layer (gfx950).
+//
+// The complete 3-bit matrix keeps zero-filled weak columns, and the weak
+// columns are stored separately in fp16 ([PL] "Storage Methods", paper appendix
+// section 2 pp.10-11). Weak columns are excluded from quantisation ([PL]
+// "Weak-column selection", paper p.4), so each row is fitted on its dense
+// columns; for an asymmetric grid, "zero-filled" is the zero-point code.
+// [PL] = paperlayer.ai page "OWQ: Outlier-Aware Weight Quantization for
+// Efficient Fine-Tuning and Inference of Large Language Models".
+//
+// Because the fitted range always contains 0, replacing the weak entries of a
+// row by +0 leaves (lo, hi) of the dense columns unchanged and gives them the
+// code clamp(rint(0/s) + z) = z. The kernel therefore zeroes the weak entries
+// (a per-group 32-bit weak mask built once per block in LDS) and runs the plain
+// full-row quantiser: one 256-thread block per row (grid-stride), each thread
+// holding GPT 32-column groups in registers, a block min/max, then 32 codes per
+// group packed into three words: code c at bits [3c, 3c+3) of w0|w1<<32|w2<<64.
+//
+// Built with -ffp-contract=off: the quantiser steps are single IEEE operations.
+#include "owq_device.h"
+#include "owq_launch.h"
+
+namespace owq {
+
+namespace {
+
+template <int GPT>
+__global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                              const int32_t* __restrict__ idx, int32_t k,
+                                              uint32_t* __restrict__ q, uint16_t* __restrict__ scales,
+                                              uint8_t* __restrict__ zeros, uint16_t* __restrict__ ww)
+{
+    extern __shared__ uint32_t wmask[];  // [G] weak-column bit mask per 32-column group
+    __shared__ float red[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t G = K / 32;
+
+    for (int64_t g = tid; g < G; g += 256)
+        wmask[g] = 0;
+    __syncthreads();
+    for (int64_t c = tid; c < k; c += 256) {
+        const int32_t j = idx[c];
+        if (j >= 0 && j < K)  // indices outside [0, K) break the caller contract; never touch memory with them
+            atomicOr(&wmask[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+
+    for (int64_t row = blockIdx.x; row < N; row += gridDim.x) {
+        const uint16_t* wr = W + row * K;
+        uint32_t v[GPT][16];
+        float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+        for (int u = 0; u < GPT; u++) {
+            int64_t g = tid + 256 * u;
+            if (g < G) {
+                const uint4* p = reinterpret_cast<const uint4*>(wr + g * 32);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    uint4 t = p[i];
+                    v[u][4 * i + 0] = t.x;
+                    v[u][4 * i + 1] = t.y;
+                    v[u][4 * i + 2] = t.z;
+                    v[u][4 * i + 3] = t.w;
+                }
+                uint32_t m = wmask[g];
+#pragma unroll
+                for (int c = 0; c < 32; c++) {
+                    if ((m >> c) & 1u)
+                        v[u][c >> 1] &= (c & 1) ? 0x0000ffffu : 0xffff0000u;
+                    float f = h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1))));
+                    lo = fminf(lo, f);
+                    hi = fmaxf(hi, f);
+                }
+            }
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if (lane == 0) {
+            red[0][wave] = lo;
+            red[1][wave] = hi;
+        }
+        __syncthreads();
+        lo = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
+        hi = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+        uint16_t s16;
+        int z;
+        qparams_from_range(lo, hi, s16, z);
+        const float sf = h2f(s16);
+#pragma unroll
+        for (int u = 0; u < GPT; u++) {
+            int64_t g = tid + 256 * u;
+            if (g < G) {
+                uint32_t o[3] = {0u, 0u, 0u};
+#pragma unroll
+                for (int c = 0; c < 32; c++) {
+                    uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), sf, z);
+                    const int pos = 3 * c, wd = pos >> 5, off = pos & 31;
+                    o[wd] |= cd << off;
+                    if (off > 29)
+                        o[wd + 1] |= cd >> (32 - off);
+                }
+                uint32_t* dst = q + (row * G + g) * 3;
+                dst[0] = o[0];
+                dst[1] = o[1];
+                dst[2] = o[2];
+            }
+        }
+        if (tid == 0) {
+            scales[row] = s16;
+            zeros[row] = (uint8_t)z;
+        }
+        for (int64_t c = tid; c < k; c += 256) {
+            const int32_t j = idx[c];
+            ww[row * k + c] = (j >= 0 && j < K) ? wr[j] : (uint16_t)0;
+        }
+        __syncthreads();  // red[] is reused by the next row
+    }
+}
+
+template <int GPT>
+hipError_t launch_pack_t(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
+                         uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
+{
+    const int64_t G = K / 32;
+    const unsigned grid = (unsigned)(N < 4096 ? N : 4096);
+    hipLaunchKernelGGL(k_pack<GPT>, dim3(grid), dim3(256), (size_t)G * sizeof(uint32_t), s, W, N, K,
+                       idx, k, q, scales, zeros, ww);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
+                       uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
+{
+    const int64_t G = K / 32;
+    const int64_t gpt = (G + 255) / 256;  // K <= 65536 -> gpt <= 8
+    if (gpt <= 1)
+        return launch_pack_t<1>(W, N, K, idx, k, q, scales, zeros, ww, s);
+    if (gpt <= 2)
+        return launch_pack_t<2>(W, N, K, idx, k, q, scales, zeros, ww, s);
+    if (gpt <= 4)
+        return launch_pack_t<4>(W, N, K, idx, k, q, scales, zeros, ww, s);
+    return launch_pack_t<8>(W, N, K, idx, k, q, scales, zeros, ww, s);
+}
+
+}  // namespace owq

@@ -1,0 +1,145 @@
+// topk.hip -- weak-column selection: the k largest column scores (gfx950).
+//
+// The top-k columns by sensitivity become the weak columns kept in fp16 ([PL]
+// "Weak-column selection", paper p.4; [PL] = paperlayer.ai page "OWQ:
+// Outlier-Aware Weight Quantization for Efficient Fine-Tuning and Inference of
+// Large Language Models"). Ties are broken by the lower column index and the
+// result is written in ascending column order.
+//
+// One 1024-thread workgroup (latency-bound, K <= 2^24 doubles read from L2):
+//  1. radix select of the k-th largest 64-bit order key, 8 bits per pass from the
+//     most significant digit: an LDS histogram of the digit among keys that match
+//     the digits fixed so far, then one wavefront scans the 256 bins;
+//  2. one ordered compaction pass: column j is taken if its key is above the
+//     threshold, or equal to it and among the first (k - #above) equal keys in
+//     index order. Ballot/popcount scans keep index order, so the output is
+//     ascending without a sort.
+#include "owq_device.h"
+#include "owq_launch.h"
+
+namespace owq {
+
+namespace {
+
+// Order-preserving map of a double to an unsigned key (+0 and -0 compare equal).
+__device__ __forceinline__ uint64_t score_key(double v)
+{
+    if (v == 0.0)
+        v = 0.0;
+    uint64_t b = __builtin_bit_cast(uint64_t, v);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t ballot)
+{
+    const int lane = threadIdx.x & 63;
+    uint64_t m = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    return (uint32_t)__popcll(ballot & m);
+}
+
+// Exclusive block-wide prefix count of `flag` in thread order; also returns the total.
+__device__ __forceinline__ uint32_t block_excl_count(bool flag, uint32_t* wave_tot, uint32_t& total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t b = __ballot(flag);
+    if (lane == 0)
+        wave_tot[wave] = (uint32_t)__popcll(b);
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+    for (int w = 0; w < 16; w++) {
+        uint32_t t = wave_tot[w];
+        before += w < wave ? t : 0;
+        tot += t;
+    }
+    __syncthreads();
+    total = tot;
+    return before + lanes_below(b);
+}
+
+__global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ score, int64_t K, int32_t k,
+                                               int32_t* __restrict__ out)
+{
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t wave_tot[16];
+    __shared__ unsigned long long sh_prefix;
+    __shared__ int sh_kk;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    uint64_t prefix = 0, mask = 0;
+    int kk = k;  // how many still to take among keys matching `prefix` on `mask`
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        if (tid < 256)
+            hist[tid] = 0;
+        __syncthreads();
+        for (int64_t j = tid; j < K; j += 1024) {
+            uint64_t key = score_key(score[j]);
+            if ((key & mask) == prefix)
+                atomicAdd(&hist[(key >> shift) & 255], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l covers digits 255-4l .. 252-4l, i.e. descending order
+            uint32_t c[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                c[i] = hist[255 - 4 * lane - i];
+            uint32_t tot = c[0] + c[1] + c[2] + c[3];
+            uint32_t incl = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                uint32_t t = __shfl_up(incl, o, 64);
+                if (lane >= o)
+                    incl += t;
+            }
+            uint32_t excl = incl - tot;
+            if (excl < (uint32_t)kk && incl >= (uint32_t)kk) {
+                uint32_t run = excl;
+                int d = 0;
+                uint32_t above = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    if (run + c[i] >= (uint32_t)kk) {
+                        d = 255 - 4 * lane - i;
+                        above = run;
+                        break;
+                    }
+                    run += c[i];
+                }
+                sh_prefix = prefix | ((uint64_t)d << shift);
+                sh_kk = kk - (int)above;
+            }
+        }
+        __syncthreads();
+        prefix = sh_prefix;
+        kk = sh_kk;
+        mask |= 0xffull << shift;
+    }
+
+    // ordered compaction: > threshold, or == threshold within the first kk in index order
+    uint32_t base = 0, eq_base = 0;
+    for (int64_t j0 = 0; j0 < K; j0 += 1024) {
+        int64_t j = j0 + tid;
+        uint64_t key = j < K ? score_key(score[j]) : 0;
+        bool gt = j < K && key > prefix;
+        bool eq = j < K && key == prefix;
+        uint32_t eq_total;
+        uint32_t eq_rank = eq_base + block_excl_count(eq, wave_tot, eq_total);
+        bool sel = gt || (eq && eq_rank < (uint32_t)kk);
+        uint32_t sel_total;
+        uint32_t pos = base + block_excl_count(sel, wave_tot, sel_total);
+        if (sel && pos < (uint32_t)k)
+            out[pos] = (int32_t)j;
+        base += sel_total;
+        eq_base += eq_total;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_select(const double* score, int64_t K, int32_t k, int32_t* idx, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_topk, dim3(1), dim3(1024), 0, s, score, K, k, idx);
+    return hipGetLastError();
+}
+
+}  // namespace owq

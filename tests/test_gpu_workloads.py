@@ -1,0 +1,83 @@
+"""GPU parity at the full workload sizes: one LLaMA-7B decoder layer (decode,
+batch sweep, batched launch), the large 8192/28672 shapes, and prefill plus
+long calibration at the MLP shapes. Inputs come from the seeded generator."""
+import numpy as np
+import pytest
+
+from mixed_precision_weight_amd import synth
+from parity_util import check_linear, dev, host
+from test_gpu_parity import _run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def owq():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from mixed_precision_weight_amd import owq as o
+    o.lib()
+    return o
+
+
+def _inputs(cfg, li, M):
+    spec = cfg.layers[li]
+    seed = cfg.seed(li)
+    return (spec, synth.weights(spec, seed), synth.calibration(spec, seed, cfg.T),
+            synth.activations(spec, seed, M))
+
+
+@pytest.mark.parametrize("li", range(7))
+def test_llama7b_layer_decode(owq, li):
+    cfg = synth.CONFIGS[1]
+    spec, W, X, x = _inputs(cfg, li, 1)
+    _run(owq, W, X, spec.k, [x], f"{cfg.name}/{spec.name}")
+
+
+@pytest.mark.parametrize("li", [0, 4, 6])
+def test_llama7b_batch_sweep(owq, li):
+    cfg = synth.CONFIGS[2]
+    spec, W, X, x = _inputs(cfg, li, 16)
+    _run(owq, W, X, spec.k, [x[:m] for m in cfg.Ms], f"{cfg.name}/{spec.name}",
+         sample=4096 * 4, rng=np.random.default_rng(li))
+
+
+def test_llama7b_layer_batched_launch(owq):
+    """One launch over the 7 linears equals the 7 single launches bit for bit."""
+    import torch
+    import oracle
+    cfg = synth.CONFIGS[1]
+    layers, xs, singles = [], [], []
+    for li, spec in enumerate(cfg.layers):
+        seed = cfg.seed(li)
+        W = synth.weights(spec, seed)
+        idx = np.sort(np.random.default_rng(li).choice(spec.K, spec.k, replace=False)).astype(np.int32)
+        p = owq.pack(dev(W), dev(idx))
+        x = dev(synth.activations(spec, seed, 1))
+        layers.append(p)
+        xs.append(x)
+        singles.append(owq.linear(p, x))
+    ys = owq.linear_batched(layers, xs)
+    torch.cuda.synchronize()
+    for a, b in zip(ys, singles):
+        assert host(a).tobytes() == host(b).tobytes()
+    # and the batched outputs meet the oracle bound
+    o = oracle.pack(synth.weights(cfg.layers[6], cfg.seed(6)), host(layers[6]["weak_idx"]))
+    yr, bnd = oracle.linear_full(o, host(xs[6]))
+    check_linear(host(ys[6]), yr, bnd, "batched down_proj")
+
+
+@pytest.mark.parametrize("li", range(3))
+def test_large_shapes(owq, li):
+    cfg = synth.CONFIGS[3]
+    spec, W, X, x = _inputs(cfg, li, 8)
+    _run(owq, W, X, spec.k, [x[:1], x], f"{cfg.name}/{spec.name}", sample=2048,
+         rng=np.random.default_rng(100 + li))
+
+
+@pytest.mark.parametrize("li", range(2))
+def test_prefill_and_long_calibration(owq, li):
+    cfg = synth.CONFIGS[4]
+    spec, W, X, x = _inputs(cfg, li, 2048)
+    _run(owq, W, X, spec.k, [x], f"{cfg.name}/{spec.name}", sample=4096,
+         rng=np.random.default_rng(200 + li))
