@@ -149,10 +149,11 @@ owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M,
                       uint16_t* y, void* stream);
 
 /* `count` independent linears with the same M in ONE kernel launch (the decode
- * GEMV only: 1 <= M <= 4). Ls: HOST array [count] of layers; xs, ys: HOST arrays
- * [count] of device pointers with the shapes owq_linear expects. Equivalent to
- * count calls of owq_linear. Returns OWQ_ERR_UNSUPPORTED outside 1 <= M <= 4,
- * 1 <= count <= 64. */
+ * GEMV only: 1 <= M <= 4 and M * K * 2 + 16384 + 64 <= 163840 for every layer,
+ * since x is staged in LDS). Ls: HOST array [count] of layers; xs, ys: HOST
+ * arrays [count] of device pointers with the shapes owq_linear expects.
+ * Equivalent to count calls of owq_linear. Returns OWQ_ERR_UNSUPPORTED outside
+ * those limits or 1 <= count <= 64. */
 owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs,
                               uint16_t* const* ys, int32_t count, int64_t M,
                               void* stream);

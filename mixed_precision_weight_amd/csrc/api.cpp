@@ -224,8 +224,9 @@ owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t
     if (M >= owq::gemm_min_m())
         return hip_status(owq::launch_gemm(d, M, s), "owq_linear (matrix-core) launch");
     hipError_t e = hipSuccess;
-    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += owq::kGemvMaxM) {
-        int64_t mm = M - m0 < owq::kGemvMaxM ? M - m0 : owq::kGemvMaxM;
+    const int64_t mt = owq::gemv_max_tokens(L->K);
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += mt) {
+        int64_t mm = M - m0 < mt ? M - m0 : mt;
         owq::LinearDesc dm = d;
         dm.x = x + m0 * L->K;
         dm.y = y + m0 * L->N;
@@ -252,6 +253,9 @@ owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs, ui
         st = check_idx_on_host(Ls[l].weak_idx, Ls[l].k, Ls[l].K, (hipStream_t)stream);
         if (st != OWQ_OK)
             return st;
+        if (!owq::gemv_fits(M, Ls[l].K))
+            return fail(OWQ_ERR_UNSUPPORTED, "layer %d: M * K = %lld exceeds the batched decode limit "
+                        "(M * K * 2 + 16 KB <= 160 KB of LDS)", l, (long long)(M * Ls[l].K));
         d[l] = desc_of(&Ls[l], xs[l], ys[l]);
     }
     hipError_t e = hipSuccess;

@@ -79,6 +79,27 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
+// DPP butterfly sum over 64 lanes: quad swaps and row rotations reduce each
+// 16-lane row, row broadcasts fold the rows into lane 63, which is returned
+// (as a wave-uniform value). No LDS traffic, ~7 dependent VALU steps.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS,
+                                                                0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v)
+{
+    v += dpp_f<0xb1>(v);        // quad_perm [1,0,3,2]
+    v += dpp_f<0x4e>(v);        // quad_perm [2,3,0,1]
+    v += dpp_f<0x124>(v);       // row_ror:4
+    v += dpp_f<0x128>(v);       // row_ror:8  -> every lane holds its 16-lane row sum
+    v += dpp_f<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+    v += dpp_f<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ __forceinline__ double shfl_xor_f64(double v, int o)
 {
     uint64_t b = __builtin_bit_cast(uint64_t, v);

@@ -41,8 +41,12 @@ struct LinearDesc {
 constexpr int kGemvMaxM = 4;        // tokens per GEMV launch
 constexpr int kGemvMaxLayers = 16;  // layers per batched GEMV launch
 
-// Decode GEMV over `count` layers (count <= kGemvMaxLayers), 1 <= M <= kGemvMaxM.
+// Decode GEMV over `count` layers (count <= kGemvMaxLayers), 1 <= M <= kGemvMaxM,
+// gemv_fits(M, K) for every layer.
 hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s);
+// Tokens per GEMV launch for a layer of K columns (x of all tokens is staged in LDS).
+int gemv_max_tokens(int64_t K);
+bool gemv_fits(int64_t M, int64_t K);
 // Matrix-core GEMM for larger M.
 hipError_t launch_gemm(const LinearDesc& d, int64_t M, hipStream_t s);
 // Smallest M routed to the matrix-core kernel (read once from OWQ_GEMM_MIN_M).
