@@ -8,15 +8,18 @@
 // p.6; [PL] = paperlayer.ai page "OWQ: Outlier-Aware Weight Quantization for
 // Efficient Fine-Tuning and Inference of Large Language Models").
 //
-// Persistent streaming design. The host gives every layer a number of blocks
-// proportional to its bytes; a block of 4 or 8 wavefronts owns a contiguous row
-// range of one layer. At block start it stages x (all K, permuted into decode-pair order)
-// and the rows' scale, zero point and weak weights in LDS, while each wavefront
-// already has a ring of D code tiles in flight. A tile is one 12-byte group per
-// lane (64 consecutive groups = 768 contiguous bytes of one row); the wave walks
-// its rows (rows rbeg + w, +4, ...) tile by tile, refilling the ring slot it
-// just consumed, so loads stay D tiles ahead of the arithmetic and HBM latency
-// overlaps the decode of earlier tiles. Rows end in a DPP wave reduction.
+// Work split: a block of 4 wavefronts owns 4 R consecutive rows of one layer
+// (R rows per wavefront); the 64 lanes of a wave split a row's K/32 groups, lane
+// l taking groups l, l + 64, ... (a "tile" is one 12-byte group per lane: 768
+// contiguous bytes of one row). K is walked in chunks of two tiles (4096
+// columns): for each chunk the block stages x in LDS in decode-pair order, every
+// wave holds its R rows' code tiles in registers, and all global loads of the
+// chunk are issued before the first wait (unconditionally, with clamped
+// indices: a load under a divergent branch would make the compiler wait for it
+// at the branch merge). The hardware overlaps the arithmetic of resident blocks
+// with the loads of others. Layers of any K share the kernel, so the decode of a
+// whole decoder layer (several linears) is one launch. Rows finish with a
+// 64-lane reduction of four rows at once (lane-half swaps, then DPP).
 //
 // Decode without per-code shifts: a 3-bit field that sits inside the mantissa of
 // an fp16 half (bits p..p+2 with p <= 7) becomes an exact fp16 number once an
@@ -49,9 +52,7 @@ struct GemvLayer {
     const uint16_t* x;
     uint16_t* y;
     int32_t N, K, k;
-    int32_t block0;    // first block of this layer
-    int32_t rpb;       // rows per block
-    int32_t ww_vec16;  // w_weak is 16-byte aligned (vector staging)
+    int32_t block0;  // first block of this layer
 };
 
 struct GemvBatch {
@@ -154,9 +155,6 @@ __device__ __forceinline__ void decode_group(uint32_t w0, uint32_t w1, uint32_t 
     p[15] = sub_h2(and_or(w2 >> 13, 0x00070000u, and_or(w0, 7u, mg.p)), n.p);
 }
 
-constexpr int kWeakLds = 256;  // weak columns per row staged in LDS (larger k reads them from HBM)
-constexpr int kDepth = 8;      // tiles in flight per wavefront in the generic stream
-constexpr int kMaxRowsPerBlock = 256;
 
 // Staged x layout (uint4 units): [m][tile u][quad qd][lane l] for group g = 64 u + l,
 // so a lane's four quads of a tile are 1 KB apart (immediate offsets) and the
@@ -186,625 +184,270 @@ __device__ __forceinline__ void store_group(const uint4 (&v)[4], uint4* __restri
         xs_mg[qd * 64] = make_uint4(pr[4 * qd], pr[4 * qd + 1], pr[4 * qd + 2], pr[4 * qd + 3]);
 }
 
-// Byte offset, inside the staged x of token m, of column j (inverse of the pair order).
-__device__ __forceinline__ int x_lds_byte(int m, int T, int j)
-{
-    const int g = j >> 5, c = j & 31;
-    int p, h;
-    if (c == 0) {
-        p = 15;
-        h = 0;
-    } else if (c == 31) {
-        p = 15;
-        h = 1;
-    } else {
-        const int r = (c - 1) / 10, t = (c - 1) - 10 * r;
-        h = t >= 5;
-        p = 5 * r + (t - 5 * h);
-    }
-    return ((xs_index(m, T, g) + ((p >> 2) << 6)) << 4) + ((p & 3) << 2) + (h << 1);
-}
-
-__host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
-
-// LDS layout of a block: x pair quads [M][T][4][64] (uint4); scale [rpb] (fp16); zero
-// point [rpb]; row results [M][rpb] (fp32); weak weights [rpb][k] (k <= kWeakLds).
-struct GemvLds {
-    size_t sc, z, y, ww, total;
-    __host__ __device__ GemvLds(int M, int G, int rpb, int k)
-    {
-        sc = (size_t)M * ((G + 63) / 64) * 64 * 4 * 16;
-        z = sc + align16((size_t)rpb * 2);
-        y = z + align16((size_t)rpb);
-        ww = y + align16((size_t)M * rpb * 4);
-        total = ww + (k <= kWeakLds ? align16((size_t)rpb * k * 2) : 0);
-    }
-};
-
-// ---------------------------------------------------------------- staging --
-// Block-level inputs: issued as loads first (registers), committed to LDS after
-// the wave's ring of code tiles is in flight, so the staging wait does not queue
-// behind the HBM loads of the ring.
-constexpr int kWwVec = 4;  // 16-byte weak-weight vectors staged per thread in the first pass
-
-template <int NT>
-struct Staging {
-    uint4 xa[4];         // one 32-column group of x per thread
-    uint4 wv[kWwVec];    // weak weights, 16-byte vectors
-    uint16_t sv;         // row scale
-    uint8_t zv;          // row zero point
-    int wj[4];           // weak indices of this lane
-};
-
-struct BlockArgs {
-    const uint16_t* X;
-    const int32_t* IDX;
-    const uint16_t* WW;
-    const uint16_t* S;
-    const uint8_t* Z;
-    int K, G, T, k, rbeg, nrb, rpb;
-    bool wl, ww16;
-};
-
-template <int M, int NT>
-__device__ __forceinline__ void stage_issue(const BlockArgs& a, int tid, int lane, Staging<NT>& st)
-{
-    const int MG = M * a.G;
-    if (tid < MG) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.X + (int64_t)(tid / a.G) * a.K + (int64_t)(tid % a.G) * 32);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++)
-            st.xa[q4] = src[q4];
-    }
-    st.sv = 0;
-    st.zv = 0;
-    if (tid < a.nrb) {  // rows per block <= kMaxRowsPerBlock <= threads per block
-        st.sv = a.S[a.rbeg + tid];
-        st.zv = a.Z[a.rbeg + tid];
-    }
-    const int E = a.wl ? a.nrb * a.k : 0;
-    if (a.ww16) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.WW + (int64_t)a.rbeg * a.k);
-#pragma unroll
-        for (int t = 0; t < kWwVec; t++) {
-            const int i = tid + NT * t;
-            st.wv[t] = (8 * i < E) ? src[i] : make_uint4(0, 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-        const int c = lane + 64 * v;
-        const int j = c < a.k ? a.IDX[c] : 0;
-        st.wj[v] = (j >= 0 && j < a.K) ? j : 0;
-    }
-}
-
-// LDS writes of the staged inputs, the block barrier, then this lane's x values at
-// the weak indices (read back from the staged x).
-template <int M, int NT>
-__device__ __forceinline__ void stage_commit(const BlockArgs& a, int tid, int lane, const Staging<NT>& st, char* base,
-                                             uint4* xs, uint16_t* s_sc, uint8_t* s_z, uint16_t* s_ww,
-                                             float (&xw)[M][4])
-{
-    const int MG = M * a.G;
-    if (tid < MG)
-        store_group(st.xa, xs + xs_index(tid / a.G, a.T, tid % a.G));
-    for (int i = tid + NT; i < MG; i += NT) {  // M * G > threads: direct copies
-        const uint4* src = reinterpret_cast<const uint4*>(a.X + (int64_t)(i / a.G) * a.K + (int64_t)(i % a.G) * 32);
-        uint4 v[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; q4++)
-            v[q4] = src[q4];
-        store_group(v, xs + xs_index(i / a.G, a.T, i % a.G));
-    }
-    if (tid < a.nrb) {
-        s_sc[tid] = st.sv;
-        s_z[tid] = st.zv;
-    }
-    const int E = a.wl ? a.nrb * a.k : 0;
-    if (a.ww16) {
-        uint4* dst = reinterpret_cast<uint4*>(s_ww);
-#pragma unroll
-        for (int t = 0; t < kWwVec; t++) {
-            const int i = tid + NT * t;
-            if (8 * i < E)
-                dst[i] = st.wv[t];
-        }
-        const uint4* src = reinterpret_cast<const uint4*>(a.WW + (int64_t)a.rbeg * a.k);
-        for (int i = tid + kWwVec * NT; 8 * i < E; i += NT)
-            dst[i] = src[i];
-    } else {
-        for (int i = tid; i < E; i += NT)
-            s_ww[i] = a.WW[(int64_t)a.rbeg * a.k + i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-        const int c = lane + 64 * v;
-#pragma unroll
-        for (int m = 0; m < M; m++)
-            xw[m][v] = c < a.k ? h2f(*reinterpret_cast<const uint16_t*>(base + x_lds_byte(m, a.T, st.wj[v]))) : 0.0f;
-    }
-}
-
-// ------------------------------------------------------------ row context --
-template <int M>
-struct RowCtx {
-    Magic mg;
-    const uint4* xs;
-    const uint16_t* s_sc;
-    const uint8_t* s_z;
-    float* s_y;
-    const uint16_t* s_ww;
-    int rpb, T, G, k;
-    bool wl;
-    int lane;
-};
-
-// Row start: zero-point constants and scale of block row rl (LDS).
-template <int M>
-__device__ __forceinline__ void row_begin(const RowCtx<M>& cx, int rl, ZeroSub& nz, float& sc, float (&acc)[M])
-{
-    const uint32_t z = (uint32_t)__builtin_amdgcn_readfirstlane((int)cx.s_z[rl]);
-    nz = make_zero_sub(z);
-    sc = h2f(cx.s_sc[rl]);
-#pragma unroll
-    for (int m = 0; m < M; m++)
-        acc[m] = 0.0f;
-}
-
-// One tile (group g of every token) of the current row.
-template <int M>
-__device__ __forceinline__ void tile_dot(const RowCtx<M>& cx, const u32x3& w, int g, const ZeroSub& nz,
-                                         float (&acc)[M])
-{
-    uint32_t p[16];
-    decode_group(w.x, w.y, w.z, cx.mg, nz, p);
-#pragma unroll
-    for (int m = 0; m < M; m++) {
-        float a = acc[m];
-        const uint4* xq4 = cx.xs + xs_index(m, cx.T, g);
-#pragma unroll
-        for (int qd = 0; qd < 4; qd++) {
-            const uint4 xq = xq4[qd << 6];
-            a = dot2(p[4 * qd + 0], xq.x, a);
-            a = dot2(p[4 * qd + 1], xq.y, a);
-            a = dot2(p[4 * qd + 2], xq.z, a);
-            a = dot2(p[4 * qd + 3], xq.w, a);
-        }
-        acc[m] = a;
-    }
-}
-
-// Per-lane partial of a finished row: scale times the dense dot, plus this
-// lane's share of the weak columns (staged in LDS).
-template <int M>
-__device__ __forceinline__ void row_partial(const RowCtx<M>& cx, int rl, float sc, const float (&acc)[M],
-                                            const float (&xw)[M][4], float (&part)[M])
-{
-#pragma unroll
-    for (int m = 0; m < M; m++)
-        part[m] = sc * acc[m];
-    if (cx.wl) {
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int c = cx.lane + 64 * v;
-            if (c < cx.k) {
-                const float w = h2f(cx.s_ww[rl * cx.k + c]);
-#pragma unroll
-                for (int m = 0; m < M; m++)
-                    part[m] += w * xw[m][v];
-            }
-        }
-    }
-}
+// ------------------------------------------------------------------ kernel --
+constexpr int kChunkTiles = 2;  // 64-group tiles per K chunk (4096 columns)
+// Rows per wavefront: enough code bytes in flight, registers bounded.
+__host__ __device__ constexpr int rows_per_wave(int M) { return M <= 2 ? 4 : 2; }
 
 __device__ __forceinline__ float f_of(uint32_t v) { return __builtin_bit_cast(float, v); }
 __device__ __forceinline__ uint32_t u_of(float v) { return __builtin_bit_cast(uint32_t, v); }
 
-// Sum over the 64 lanes of R per-lane values at once (R = 4, 8 or 16): lane-half
-// swaps (v_permlane32_swap, then v_permlane16_swap) each add two values while
-// halving their lane span, then a DPP reduction inside 16-lane rows. On return,
-// value v holds, in lanes 16 q .. 16 q + 15, the total of input R / 4 * q + v.
-template <int R>
-__device__ __forceinline__ void reduce_rows(float (&a)[R])
+// Sum over the 64 lanes of 4 per-lane values at once: a v_permlane32_swap and a
+// v_permlane16_swap step each add two values while halving their lane span, then
+// a DPP reduction inside 16-lane rows. On return a[0] holds, in lanes
+// 16 q .. 16 q + 15, the total of input reduced_index(q).
+__device__ __forceinline__ void reduce4(float (&a)[4])
 {
-    static_assert(R == 4 || R == 8 || R == 16, "R");
-    constexpr int H = R / 2, Q = R / 4;
-    float b[H];
+    float b[2];
 #pragma unroll
-    for (int i = 0; i < H; i++) {  // pairs (i, i + H): lanes 0-31 keep input i, 32-63 input i + H
-        auto t = __builtin_amdgcn_permlane32_swap(u_of(a[i]), u_of(a[i + H]), false, false);
+    for (int i = 0; i < 2; i++) {  // lanes 0-31 keep input i, lanes 32-63 input i + 2
+        auto t = __builtin_amdgcn_permlane32_swap(u_of(a[i]), u_of(a[i + 2]), false, false);
         b[i] = f_of(t[0]) + f_of(t[1]);
     }
-#pragma unroll
-    for (int i = 0; i < Q; i++) {  // pairs (i, i + Q) inside each half
-        auto t = __builtin_amdgcn_permlane16_swap(u_of(b[i]), u_of(b[i + Q]), false, false);
-        a[i] = f_of(t[0]) + f_of(t[1]);
-    }
-#pragma unroll
-    for (int i = 0; i < Q; i++) {
-        float v = a[i];
-        v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
-        v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
-        v += dpp_f<0x124>(v);  // row_ror:4
-        v += dpp_f<0x128>(v);  // row_ror:8
-        a[i] = v;
-    }
+    auto t = __builtin_amdgcn_permlane16_swap(u_of(b[0]), u_of(b[1]), false, false);
+    float v = f_of(t[0]) + f_of(t[1]);
+    v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x124>(v);  // row_ror:4
+    v += dpp_f<0x128>(v);  // row_ror:8
+    a[0] = v;
 }
-// After reduce_rows<R>, input r = i + Q * ((lane >> 4) ...) : lanes 16q..16q+15 of
-// a[i] hold input index i + (q & 1) * H ... see row_of().
-template <int R>
-__device__ __forceinline__ int reduced_index(int i, int q)
+// quarter q of the lanes holds input (q & 1) + 2 (q >> 1)
+__device__ __forceinline__ int reduced_index(int q) { return (q & 1) + ((q >> 1) << 1); }
+
+// One wavefront computes R consecutive rows of one layer; a block is 4 waves
+// (4 R rows) sharing x, staged in LDS in decode-pair order one K chunk
+// (kChunkTiles tiles, 4096 columns) at a time. For each chunk every global load
+// of the block (x of the chunk, the R rows' codes of the chunk, and with the
+// first chunk the rows' scale, zero point, weak weights and the weak indices)
+// is issued before the first wait, so a chunk costs one memory latency; the
+// hardware overlaps the arithmetic of resident blocks with the loads of others.
+// Layers of any K share this one kernel, so a batch is a single launch.
+template <int M>
+__global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
 {
-    // quarter q: half h = q >> 1 selects +H (step 1), odd quarter selects +Q (step 2)
-    return i + (q & 1) * (R / 4) + (q >> 1) * (R / 2);
-}
-
-// Stream for rows of exactly T tiles. The ring holds RPR whole rows (T * RPR
-// tiles); a tile's offset inside its row is an instruction immediate and the row
-// offset a scalar, so the loop carries no per-tile bookkeeping. Every RPR rows
-// the per-lane partials are reduced together (reduce_rows).
-template <int M, int T, int RPR, int WAVES, int NT>
-__device__ __forceinline__ void stream_rows(const RowCtx<M>& cx, const BlockArgs& ba, const Staging<NT>& st, char* base,
-                                            uint4* xs, uint16_t* s_sc, uint8_t* s_z, uint16_t* s_ww,
-                                            __amdgpu_buffer_rsrc_t qr, int voff, int wave, int nrw, int tid)
-{
-    const int rstride = WAVES * cx.G * 12;
-    u32x3 cw[RPR][T];
-    int pre = wave * cx.G * 12;  // byte offset of the next row to prefetch
-#pragma unroll
-    for (int rr = 0; rr < RPR; rr++) {
-        const int so = rr < nrw ? pre : 0x7ffff000;
-#pragma unroll
-        for (int u = 0; u < T; u++)
-            cw[rr][u] = __builtin_amdgcn_raw_buffer_load_b96(qr, voff + u * 768, so, 0);
-        pre += rstride;
-    }
-    float xw[M][4];
-    stage_commit<M, NT>(ba, tid, cx.lane, st, base, xs, s_sc, s_z, s_ww, xw);
-
-    constexpr int RR = RPR < 4 ? 4 : RPR;  // rows per reduction (zero-padded)
-    ZeroSub nz = make_zero_sub(0);
-    float sc = 0.0f;
-    for (int j0 = 0; j0 < nrw; j0 += RPR) {
-        float part[M][RR];
-#pragma unroll
-        for (int rr = 0; rr < RR; rr++)
-#pragma unroll
-            for (int m = 0; m < M; m++)
-                part[m][rr] = 0.0f;
-#pragma unroll
-        for (int rr = 0; rr < RPR; rr++) {
-            const int j = j0 + rr;
-            if (j < nrw) {
-                const int rl = wave + WAVES * j;
-                float acc[M];
-                row_begin(cx, rl, nz, sc, acc);
-#pragma unroll
-                for (int u = 0; u < T; u++) {
-                    const int g = (u << 6) + cx.lane;
-                    if (u < T - 1 || g < cx.G)
-                        tile_dot(cx, cw[rr][u], g, nz, acc);
-                }
-                float pt[M];
-                row_partial(cx, rl, sc, acc, xw, pt);
-#pragma unroll
-                for (int m = 0; m < M; m++)
-                    part[m][rr] = pt[m];
-            }
-            const int so = j + RPR < nrw ? pre : 0x7ffff000;
-#pragma unroll
-            for (int u = 0; u < T; u++)
-                cw[rr][u] = __builtin_amdgcn_raw_buffer_load_b96(qr, voff + u * 768, so, 0);
-            pre += rstride;
-        }
-        const int q = cx.lane >> 4;
-#pragma unroll
-        for (int m = 0; m < M; m++) {
-            reduce_rows<RR>(part[m]);
-#pragma unroll
-            for (int i = 0; i < RR / 4; i++) {
-                const int rr = reduced_index<RR>(i, q);
-                const int j = j0 + rr;
-                if ((cx.lane & 15) == 0 && rr < RPR && j < nrw)
-                    cx.s_y[m * cx.rpb + wave + WAVES * j] = part[m][i];
-            }
-        }
-    }
-}
-
-// Generic stream (any tiles per row): a ring of D tiles walked tile by tile,
-// one 64-lane reduction per row.
-template <int M, int D, int WAVES, int NT>
-__device__ __forceinline__ void stream_tiles(const RowCtx<M>& cx, const BlockArgs& ba, const Staging<NT>& st, char* base,
-                                             uint4* xs, uint16_t* s_sc, uint8_t* s_z, uint16_t* s_ww,
-                                             __amdgpu_buffer_rsrc_t qr, int voff, int wave, int nrw, int tid)
-{
-    const int T = cx.T;
-    const int total = nrw * T;
-    const int rstride = WAVES * cx.G * 12;
-    int prow = wave * cx.G * 12;
-    int pu = 0, pj = 0;
-    u32x3 cw[D];
-#pragma unroll
-    for (int d = 0; d < D; d++) {
-        const int so = pj < nrw ? prow + pu * 768 : 0x7ffff000;
-        cw[d] = __builtin_amdgcn_raw_buffer_load_b96(qr, voff, so, 0);
-        if (++pu == T) {
-            pu = 0;
-            ++pj;
-            prow += rstride;
-        }
-    }
-    float xw[M][4];
-    stage_commit<M, NT>(ba, tid, cx.lane, st, base, xs, s_sc, s_z, s_ww, xw);
-
-    ZeroSub nz = make_zero_sub(0);
-    float sc = 0.0f;
-    float acc[M];
-    int cj = 0, cu = 0;
-    for (int f0 = 0; f0 < total; f0 += D) {
-#pragma unroll
-        for (int d = 0; d < D; d++) {
-            if (f0 + d < total) {
-                const int rl = wave + WAVES * cj;
-                if (cu == 0)
-                    row_begin(cx, rl, nz, sc, acc);
-                const int g = (cu << 6) + cx.lane;
-                if (g < cx.G)
-                    tile_dot(cx, cw[d], g, nz, acc);
-                if (cu == T - 1) {
-                    float pt[M];
-                    row_partial(cx, rl, sc, acc, xw, pt);
-#pragma unroll
-                    for (int m = 0; m < M; m++) {
-                        const float t = wave_sum_dpp(pt[m]);
-                        if (cx.lane == 0)
-                            cx.s_y[m * cx.rpb + rl] = t;
-                    }
-                    cu = 0;
-                    ++cj;
-                } else {
-                    ++cu;
-                }
-            }
-            const int so = pj < nrw ? prow + pu * 768 : 0x7ffff000;
-            cw[d] = __builtin_amdgcn_raw_buffer_load_b96(qr, voff, so, 0);
-            if (++pu == T) {
-                pu = 0;
-                ++pj;
-                prow += rstride;
-            }
-        }
-    }
-}
-
-// Row-shape class of a layer: its tiles per row when a specialised stream exists
-// (1, 2, 3, 4 or 6), else 0 (generic tile stream).
-__host__ __device__ constexpr int row_class(int T) { return (T >= 1 && T <= 4) || T == 6 ? T : 0; }
-__host__ __device__ constexpr int rows_per_ring(int TC) { return TC == 1 ? 8 : TC == 2 ? 4 : TC == 3 ? 4 : 2; }
-
-template <int M, int TC, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void k_gemv(GemvBatch b)
-{
-    constexpr int NT = 64 * WAVES;  // threads per block
-    static_assert(NT >= kMaxRowsPerBlock, "one staging pass per row");
+    constexpr int R = rows_per_wave(M);
+    constexpr int TT = kChunkTiles;
+    constexpr int GC = 64 * TT;  // groups per chunk
     extern __shared__ uint4 smem[];
     int li = 0;
     for (int l = 1; l < b.count; l++)
         if ((int)blockIdx.x >= b.L[l].block0)
             li = l;
-    BlockArgs ba;
-    ba.X = b.L[li].x;
-    ba.IDX = b.L[li].idx;
-    ba.WW = b.L[li].ww;
-    ba.S = b.L[li].s;
-    ba.Z = b.L[li].z;
-    ba.K = b.L[li].K;
-    ba.G = ba.K >> 5;
-    ba.T = (ba.G + 63) >> 6;
-    ba.k = b.L[li].k;
-    ba.rpb = b.L[li].rpb;
-    ba.rbeg = ((int)blockIdx.x - b.L[li].block0) * ba.rpb;
-    const int N = b.L[li].N;
-    ba.nrb = min(N - ba.rbeg, ba.rpb);
-    ba.wl = ba.k <= kWeakLds;
-    ba.ww16 = b.L[li].ww_vec16;
+    const uint16_t* __restrict__ X = b.L[li].x;
+    const int32_t* __restrict__ IDX = b.L[li].idx;
+    const uint16_t* __restrict__ WW = b.L[li].ww;
+    const int N = b.L[li].N, K = b.L[li].K, k = b.L[li].k;
+    const int G = K >> 5;
     const int tid = threadIdx.x, lane = tid & 63;
-    // wave-uniform (the compiler cannot infer it from threadIdx.x >> 6)
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int brow = ((int)blockIdx.x - b.L[li].block0) * 4 * R;
+    const int row0 = brow + wave * R;     // this wave's first row
+    const int nb = min(N - brow, 4 * R);  // valid rows of the block
 
-    const GemvLds lay(M, ba.G, ba.rpb, ba.k);
-    char* base = reinterpret_cast<char*>(smem);
-    uint4* xs = smem;
-    uint16_t* s_sc = reinterpret_cast<uint16_t*>(base + lay.sc);
-    uint8_t* s_z = reinterpret_cast<uint8_t*>(base + lay.z);
-    float* s_y = reinterpret_cast<float*>(base + lay.y);
-    uint16_t* s_ww = reinterpret_cast<uint16_t*>(base + lay.ww);
-
-    Staging<NT> st;
-    stage_issue<M, NT>(ba, tid, lane, st);
-
-    // this wave's rows: rbeg + wave + WAVES * j, j < nrw; code tiles are raw buffer
-    // loads over the block's rows (a per-lane offset lane * 12 plus a wave-uniform
-    // scalar offset); lanes past a row's last group read neighbouring codes that
-    // are never used, offsets past the block's range read 0
+    // codes of the block's rows: raw buffer loads addressed by the per-lane offset
+    // (which the range check covers), so bytes past the block's valid rows read 0
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint32_t*>(b.L[li].q) + (int64_t)ba.rbeg * ba.G * 3, (short)0, ba.nrb * ba.G * 12, 0x00020000);
-    const int nrw = ba.nrb - wave > 0 ? (ba.nrb - wave + WAVES - 1) / WAVES : 0;
-    const int voff = lane * 12;
+        const_cast<uint32_t*>(b.L[li].q) + (int64_t)brow * G * 3, (short)0, nb * G * 12, 0x00020000);
+    int vrow[R];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+        vrow[r] = (wave * R + r) * G * 12 + lane * 12;
+
+    constexpr int XI = (M * GC + 255) / 256;  // staged groups per thread
+    uint4 xg[XI][4];
+    u32x3 cw[R][TT];
+    // Every load below is unconditional (indices clamped to valid data): a load
+    // under a divergent branch makes the compiler wait for it before the branch
+    // merges, which would serialise the x latency in front of the code loads.
+    // staging item i = m * GC + g (GC a power of two): token m, group g of the chunk
+    auto issue_chunk = [&](int g0, int gc) {
+#pragma unroll
+        for (int t = 0; t < XI; t++) {
+            const int i = tid + 256 * t;
+            const int m = min(i / GC, M - 1), g = min(i % GC, gc - 1);
+            const uint4* src = reinterpret_cast<const uint4*>(X + m * K + (g0 + g) * 32);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++)
+                xg[t][q4] = src[q4];
+        }
+#pragma unroll
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int u = 0; u < TT; u++)
+                cw[r][u] = __builtin_amdgcn_raw_buffer_load_b96(qr, vrow[r] + (g0 + 64 * u) * 12, 0, 0);
+    };
+
+    issue_chunk(0, min(GC, G));
+    // row scale, zero point, weak weights; weak indices and x there
+    float sc[R];
+    uint32_t zr[R];
+    float wwv[R][2];
+    const int kc = k > 0 ? k : 1;  // with k == 0 the host passes valid dummy arrays
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int row = min(row0 + r, N - 1);
+        sc[r] = h2f(b.L[li].s[row]);
+        zr[r] = (uint32_t)b.L[li].z[row];
+#pragma unroll
+        for (int v = 0; v < 2; v++) {
+            const int c = lane + 64 * v;
+            const float w = h2f(WW[(int64_t)row * k + min(c, kc - 1)]);
+            wwv[r][v] = c < k ? w : 0.0f;
+        }
+    }
+    float xw[M][2];
+#pragma unroll
+    for (int v = 0; v < 2; v++) {
+        const int c = lane + 64 * v;
+        int j = IDX[min(c, kc - 1)];
+        j = (j >= 0 && j < K) ? j : 0;
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float xv = h2f(X[(int64_t)m * K + j]);
+            xw[m][v] = c < k ? xv : 0.0f;
+        }
+    }
 
     const Magic mg = make_magic();
-    RowCtx<M> cx{mg, xs, s_sc, s_z, s_y, s_ww, ba.rpb, ba.T, ba.G, ba.k, ba.wl, lane};
-    if constexpr (TC == 0)
-        stream_tiles<M, kDepth, WAVES, NT>(cx, ba, st, base, xs, s_sc, s_z, s_ww, qr, voff, wave, nrw, tid);
-    else
-        stream_rows<M, TC, rows_per_ring(TC), WAVES, NT>(cx, ba, st, base, xs, s_sc, s_z, s_ww, qr, voff, wave, nrw,
-                                                         tid);
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            acc[r][m] = 0.0f;
 
-    // k > kWeakLds: weak columns straight from HBM, after the stream
-    if (!ba.wl) {
-        for (int j = 0; j < nrw; j++) {
-            const int rl = wave + WAVES * j;
-            float part[M];
+    for (int g0 = 0; g0 < G; g0 += GC) {
+        const int gc = min(GC, G - g0);
+        if (g0 > 0) {
+            __syncthreads();  // every wave is done with the previous chunk's x
+            issue_chunk(g0, gc);
+        }
 #pragma unroll
-            for (int m = 0; m < M; m++)
-                part[m] = 0.0f;
-            for (int c = lane; c < ba.k; c += 64) {
-                int jj = ba.IDX[c];
-                jj = (jj >= 0 && jj < ba.K) ? jj : 0;
-                const float w = h2f(ba.WW[(int64_t)(ba.rbeg + rl) * ba.k + c]);
+        for (int t = 0; t < XI; t++) {
+            const int i = tid + 256 * t;
+            if (i / GC < M && i % GC < gc)
+                store_group(xg[t], smem + xs_index(i / GC, TT, i % GC));
+        }
+        __syncthreads();
 #pragma unroll
-                for (int m = 0; m < M; m++)
-                    part[m] += w * h2f(ba.X[(int64_t)m * ba.K + jj]);
-            }
+        for (int r = 0; r < R; r++) {
+            const ZeroSub nz = make_zero_sub((uint32_t)__builtin_amdgcn_readfirstlane((int)zr[r]));
 #pragma unroll
-            for (int m = 0; m < M; m++) {
-                const float t = wave_sum_dpp(part[m]);
-                if (lane == 0)
-                    s_y[m * ba.rpb + rl] += t;
+            for (int u = 0; u < TT; u++) {
+                const int g = (u << 6) + lane;  // group within the chunk
+                if (g < gc) {
+                    uint32_t p[16];
+                    decode_group(cw[r][u].x, cw[r][u].y, cw[r][u].z, mg, nz, p);
+#pragma unroll
+                    for (int m = 0; m < M; m++) {
+                        float a = acc[r][m];
+                        const uint4* xq4 = smem + xs_index(m, TT, g);
+#pragma unroll
+                        for (int qd = 0; qd < 4; qd++) {
+                            const uint4 xq = xq4[qd << 6];
+                            a = dot2(p[4 * qd + 0], xq.x, a);
+                            a = dot2(p[4 * qd + 1], xq.y, a);
+                            a = dot2(p[4 * qd + 2], xq.z, a);
+                            a = dot2(p[4 * qd + 3], xq.w, a);
+                        }
+                        acc[r][m] = a;
+                    }
+                }
             }
         }
     }
-    __syncthreads();
+
+    // rows: scale, weak columns, 64-lane reduction of the rows together, fp16 store
     uint16_t* __restrict__ Y = b.L[li].y;
-    for (int i = tid; i < M * ba.nrb; i += NT) {
-        const int m = i / ba.nrb, r = i - m * ba.nrb;
-        Y[(int64_t)m * N + ba.rbeg + r] = f2h(s_y[m * ba.rpb + r]);
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        constexpr int RQ = (R + 3) / 4;  // groups of four rows reduced together
+        float part[RQ][4];
+#pragma unroll
+        for (int r = 0; r < 4 * RQ; r++) {
+            part[r / 4][r % 4] = 0.0f;
+            if (r < R) {
+                float t = sc[r] * acc[r][m];
+#pragma unroll
+                for (int v = 0; v < 2; v++)
+                    t += wwv[r][v] * xw[m][v];
+                part[r / 4][r % 4] = t;
+            }
+        }
+        if (k > 128) {  // remaining weak columns from global memory
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const int row = min(row0 + r, N - 1);
+                for (int c = lane + 128; c < k; c += 64) {
+                    int j = IDX[c];
+                    j = (j >= 0 && j < K) ? j : 0;
+                    part[r / 4][r % 4] += h2f(WW[(int64_t)row * k + c]) * h2f(X[(int64_t)m * K + j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int qg = 0; qg < RQ; qg++) {
+            reduce4(part[qg]);
+            const int rr = 4 * qg + reduced_index(lane >> 4);
+            if ((lane & 15) == 0 && rr < R && row0 + rr < N)
+                Y[(int64_t)m * N + row0 + rr] = f2h(part[qg][0]);
+        }
     }
-}
-
-constexpr int kWaves = 8;  // wavefronts per block
-
-template <int M, int TC>
-hipError_t launch_mc(const GemvBatch& b, int nblocks, size_t lds, hipStream_t s)
-{
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<M, TC, kWaves>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL((k_gemv<M, TC, kWaves>), dim3(nblocks), dim3(64 * kWaves), lds, s, b);
-    return hipGetLastError();
 }
 
 template <int M>
-hipError_t launch_m(const GemvBatch& b, int tc, int nblocks, size_t lds, hipStream_t s)
+hipError_t launch_m(const GemvBatch& b, int nblocks, size_t lds, hipStream_t s)
 {
-    if constexpr (M == 1) {
-        switch (tc) {
-        case 1: return launch_mc<M, 1>(b, nblocks, lds, s);
-        case 2: return launch_mc<M, 2>(b, nblocks, lds, s);
-        case 3: return launch_mc<M, 3>(b, nblocks, lds, s);
-        case 4: return launch_mc<M, 4>(b, nblocks, lds, s);
-        case 6: return launch_mc<M, 6>(b, nblocks, lds, s);
-        default: break;
-        }
-    } else if constexpr (M == 2) {
-        switch (tc) {
-        case 1: return launch_mc<M, 1>(b, nblocks, lds, s);
-        case 2: return launch_mc<M, 2>(b, nblocks, lds, s);
-        default: break;
-        }
-    }
-    return launch_mc<M, 0>(b, nblocks, lds, s);
-}
-
-int target_blocks()
-{
-    static const int t = [] {
-        const char* e = getenv("OWQ_GEMV_BLOCKS");
-        int v = e ? atoi(e) : 0;
-        return v > 0 ? v : 512;
-    }();
-    return t;
+    hipLaunchKernelGGL((k_gemv<M>), dim3(nblocks), dim3(256), lds, s, b);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 int gemv_max_tokens(int64_t K)
 {
-    // x of all tokens lives in LDS: M * K * 2 bytes, kept to 64 KB (128 KB for M = 1)
-    int64_t m = 32768 / K;
-    if (m > kGemvMaxM)
-        m = kGemvMaxM;
-    return m < 1 ? 1 : (int)m;
+    (void)K;
+    return kGemvMaxM;
 }
 
 bool gemv_fits(int64_t M, int64_t K)
 {
-    // x (M * K * 2) plus at most 16 KB of staged row data within the 160 KB of LDS
-    return M >= 1 && M <= kGemvMaxM && M * K * 2 + 16384 + 64 <= 160 * 1024;
+    (void)K;
+    return M >= 1 && M <= kGemvMaxM;
 }
 
-// One launch per row-shape class present in the batch (layers of one class share
-// a specialised kernel); blocks per layer are proportional to the layer's bytes.
+// One launch for the batch; blocks of 4 wavefronts, each wavefront owning
+// rows_per_wave(class) consecutive rows of its layer.
 hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
 {
-    const int target = target_blocks();
-    const int classes[6] = {1, 2, 3, 4, 6, 0};
-    auto class_of = [M](int64_t K) {
-        const int T = (int)((K / 32 + 63) / 64);
-        return M == 1 ? row_class(T) : (M == 2 && T <= 2 ? T : 0);
-    };
-    for (int ci = 0; ci < 6; ci++) {
-        const int tc = classes[ci];
-        double total = 0.0;  // bytes of this class: each launch spreads over the whole GPU
-        for (int l = 0; l < count; l++)
-            if (class_of(d[l].K) == tc)
-                total += (double)d[l].N * (double)d[l].K;
-        GemvBatch b{};
-        int nblocks = 0;
-        size_t lds = 0;
-        for (int l = 0; l < count; l++) {
-            const int G = (int)(d[l].K / 32);
-            if (class_of(d[l].K) != tc)
-                continue;
-            GemvLayer& L = b.L[b.count++];
-            L.q = d[l].q;
-            L.s = d[l].s;
-            L.z = d[l].z;
-            L.idx = d[l].idx;
-            L.ww = d[l].ww;
-            L.x = d[l].x;
-            L.y = d[l].y;
-            L.N = (int32_t)d[l].N;
-            L.K = (int32_t)d[l].K;
-            L.k = d[l].k;
-            L.ww_vec16 = d[l].k > 0 && ((uintptr_t)d[l].ww % 16) == 0 ? 1 : 0;
-            int nb = (int)((double)target * (double)d[l].N * (double)d[l].K / total + 0.5);
-            nb = nb < 1 ? 1 : nb;
-            int rpb = (int)((d[l].N + nb - 1) / nb);
-            rpb = (rpb + 7) & ~7;  // rows for every wave; 16-byte aligned weak-weight rows
-            // per-block row data in LDS kept to ~16 KB
-            const int rowbytes = 3 + 4 * M + (d[l].k <= kWeakLds ? 2 * d[l].k : 0);
-            int cap = (16384 / rowbytes) & ~7;
-            cap = cap < 8 ? 8 : cap;
-            cap = cap > kMaxRowsPerBlock ? kMaxRowsPerBlock : cap;
-            rpb = rpb < cap ? rpb : cap;
-            L.rpb = rpb;
-            L.block0 = nblocks;
-            nblocks += (int)((d[l].N + rpb - 1) / rpb);
-            const size_t ll = GemvLds(M, G, rpb, d[l].k).total;
-            lds = ll > lds ? ll : lds;
-        }
-        if (b.count == 0)
-            continue;
-        hipError_t e;
-        switch (M) {
-        case 1: e = launch_m<1>(b, tc, nblocks, lds, s); break;
-        case 2: e = launch_m<2>(b, tc, nblocks, lds, s); break;
-        case 3: e = launch_m<3>(b, tc, nblocks, lds, s); break;
-        default: e = launch_m<4>(b, tc, nblocks, lds, s); break;
-        }
-        if (e != hipSuccess)
-            return e;
+    GemvBatch b{};
+    int nblocks = 0;
+    for (int l = 0; l < count; l++) {
+        GemvLayer& L = b.L[b.count++];
+        L.q = d[l].q;
+        L.s = d[l].s;
+        L.z = d[l].z;
+        // with no weak columns, point the weak arrays at valid memory (the scales
+        // and the first row of x): the kernel reads them unconditionally, ignores them
+        L.idx = d[l].k > 0 ? d[l].idx : reinterpret_cast<const int32_t*>(d[l].x);
+        L.ww = d[l].k > 0 ? d[l].ww : d[l].s;
+        L.x = d[l].x;
+        L.y = d[l].y;
+        L.N = (int32_t)d[l].N;
+        L.K = (int32_t)d[l].K;
+        L.k = d[l].k;
+        L.block0 = nblocks;
+        const int rows = 4 * rows_per_wave(M);
+        nblocks += (int)((d[l].N + rows - 1) / rows);
     }
-    return hipSuccess;
+    const size_t lds = (size_t)M * kChunkTiles * 64 * 4 * 16;
+    switch (M) {
+    case 1: return launch_m<1>(b, nblocks, lds, s);
+    case 2: return launch_m<2>(b, nblocks, lds, s);
+    case 3: return launch_m<3>(b, nblocks, lds, s);
+    default: return launch_m<4>(b, nblocks, lds, s);
+    }
 }
 
 }  // namespace owq
