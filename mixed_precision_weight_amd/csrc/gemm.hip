@@ -1,14 +1,334 @@
-// gemm.hip -- matrix-core OWQ linear for larger M (gfx950). Placeholder: the
-// decode kernel handles every M until the MFMA kernel is in place.
-#include <cstdint>
+// gemm.hip -- prefill-time OWQ linear, larger batch M (gfx950 matrix cores).
+//
+//   y[m][i] = s_i * sum_j (q_ij - z_i) x[m][j] + sum_c w_weak[i][c] x[m][idx_c]
+//
+// The 3-bit matrix is dequantised on the fly and multiplied on the matrix cores
+// in fp16 with fp32 accumulation; the weak columns are a small dense fp16 block
+// applied to x gathered at the weak indices ([PL] "Real-device acceleration",
+// paper "Acceleration on Real Device" p.6; [PL] = paperlayer.ai page "OWQ:
+// Outlier-Aware Weight Quantization for Efficient Fine-Tuning and Inference of
+// Large Language Models").
+//
+// Tiling: a block owns a BM x BN tile of y (tokens x output rows) and its waves
+// form a WM x WN grid, each wave owning 32 FM tokens x 32 FN rows, i.e. FM x FN
+// accumulators of v_mfma_f32_32x32x16_f16 (A = x, B = the weights transposed).
+// K is walked in chunks of 64 columns: two 32-code groups.
+//
+// The weights never pass through LDS. The MFMA pairs the eight A and B operand
+// elements of lane l with the same eight k values of half h = l / 32, and the
+// order of a contraction is free, so lane l of a wave decodes group (chunk, h) of
+// row l % 32 of each of its row blocks (owq_decode.h) straight into B operand
+// registers: the 32 exact (q - z) values of the group feed the chunk's four
+// 16-deep MFMA steps, four decode pairs (8 values) per step.
+// x is staged through LDS in the same decode-pair order: a thread loads the 64
+// bytes of one group of one token, rearranges them in registers and writes them
+// with 128-bit stores; an A operand is then one 128-bit LDS read per lane (rows
+// padded by 16 bytes so the reads of a wave spread over all banks). LDS is
+// double buffered and the next chunk's x and codes are loaded into registers
+// while the current chunk computes: one barrier per chunk.
+//
+// Epilogue: the accumulators (sums of exact fp16 products of integer weights and
+// x) are scaled by the row step, the weak columns run as extra 16-deep MFMA
+// steps (fp16 weak weights against x gathered at weak_idx), and the result is
+// rounded to fp16 (nearest-even).
+//
+// Block order: the token block varies fastest, so consecutive blocks (which the
+// dispatcher deals round-robin to the 8 XCDs) share the rows' codes through the
+// MALL, and an XCD's blocks share tokens of x in its L2 when the token blocks
+// number 8.
 #include <cstdlib>
 
+#include "owq_decode.h"
+#include "owq_device.h"
 #include "owq_launch.h"
 
 namespace owq {
 
-int64_t gemm_min_m() { return INT64_MAX; }
+namespace {
 
-hipError_t launch_gemm(const LinearDesc&, int64_t, hipStream_t) { return hipErrorNotSupported; }
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+struct GemmArgs {
+    const uint32_t* q;
+    const uint16_t* s;
+    const uint8_t* z;
+    const int32_t* idx;
+    const uint16_t* ww;
+    const uint16_t* x;
+    uint16_t* y;
+    int32_t M, N, K, k;
+    int32_t mblocks;  // token blocks (the fastest-varying block index)
+};
+
+constexpr int kRowBytes = 2 * 64 + 16;  // LDS bytes per staged token: two groups + pad
+
+__device__ __forceinline__ half8_t as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    uint4 v = make_uint4(a, b, c, d);
+    return __builtin_bit_cast(half8_t, v);
+}
+
+template <int FM, int FN, int WM, int WN>
+struct Tile {
+    static constexpr int NT = 64 * WM * WN;  // threads
+    static constexpr int BM = 32 * FM * WM;  // tokens per block
+    static constexpr int BN = 32 * FN * WN;  // rows per block
+    static constexpr int XI = (2 * BM + NT - 1) / NT;  // staged group rows per thread
+    static constexpr int LDS = 2 * BM * kRowBytes;      // double buffer
+};
+
+template <int FM, int FN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs a)
+{
+    using T = Tile<FM, FN, WM, WN>;
+    constexpr int NT = T::NT, BM = T::BM, BN = T::BN, XI = T::XI;
+    extern __shared__ uint4 smem[];
+    char* const lds = reinterpret_cast<char*>(smem);
+
+    const int M = a.M, N = a.N, K = a.K, k = a.k;
+    const int G = K >> 5;
+    const int nchunks = (G + 1) >> 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int m0 = ((int)blockIdx.x % a.mblocks) * BM;
+    const int n0 = ((int)blockIdx.x / a.mblocks) * BN;
+    const int mv = min(BM, M - m0);  // valid tokens / rows of the block
+    const int nv = min(BN, N - n0);
+
+    // x rows and code rows of the block as buffer resources; every offset below
+    // is clamped to valid tokens, rows and groups
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.x) + (int64_t)m0 * K, (short)0, mv * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(a.q) + (int64_t)n0 * G * 3, (short)0, nv * G * 12, 0x00020000);
+
+    // staging items i = tid + NT t: token i / 2 of the block, group i % 2 of the chunk
+    int xoff[XI];
+#pragma unroll
+    for (int t = 0; t < XI; t++) {
+        const int i = tid + NT * t;
+        xoff[t] = min(i >> 1, mv - 1) * K * 2;
+    }
+    int qoff[FN];
+    float sc[FN];
+    ZeroSub zs[FN];
+#pragma unroll
+    for (int f = 0; f < FN; f++) {
+        const int r = min(wn * 32 * FN + 32 * f + l32, nv - 1);
+        qoff[f] = r * G * 12;
+        sc[f] = h2f(a.s[n0 + r]);
+        zs[f] = make_zero_sub((uint32_t)a.z[n0 + r]);
+    }
+
+    i32x4 xg[XI][4];
+    u32x3 cw[FN];
+    auto issue = [&](int c) {
+#pragma unroll
+        for (int t = 0; t < XI; t++) {
+            const int g = min(2 * c + ((tid + NT * t) & 1), G - 1);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++)
+                xg[t][q4] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[t] + g * 64 + 16 * q4, 0, 0);
+        }
+        const int g = min(2 * c + h, G - 1);
+#pragma unroll
+        for (int f = 0; f < FN; f++)
+            cw[f] = __builtin_amdgcn_raw_buffer_load_b96(qr, qoff[f] + g * 12, 0, 0);
+    };
+    // staged x of chunk c into LDS buffer c & 1, in decode-pair order; a group
+    // past the end of K (odd K / 32) is staged as zeros
+    auto stage = [&](int c) {
+        char* const buf = lds + (c & 1) * BM * kRowBytes;
+#pragma unroll
+        for (int t = 0; t < XI; t++) {
+            const int i = tid + NT * t;
+            if (i < 2 * BM) {
+                const bool live = 2 * c + (i & 1) < G;
+                uint32_t w[16], pr[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        w[4 * q4 + e] = live ? (uint32_t)xg[t][q4][e] : 0u;
+                pair_order(w, pr);
+                uint4* dst = reinterpret_cast<uint4*>(buf + (i >> 1) * kRowBytes + (i & 1) * 64);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++)
+                    dst[q4] = make_uint4(pr[4 * q4], pr[4 * q4 + 1], pr[4 * q4 + 2], pr[4 * q4 + 3]);
+            }
+        }
+    };
+
+    const Magic mg = make_magic();
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int f = 0; f < FN; f++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[i][f][r] = 0.0f;
+
+    issue(0);
+    stage(0);
+    __syncthreads();
+    const int arow = (wm * 32 * FM + l32) * kRowBytes + h * 64;  // this lane's A operand row
+    for (int c = 0; c < nchunks; c++) {
+        u32x3 cur[FN];
+#pragma unroll
+        for (int f = 0; f < FN; f++)
+            cur[f] = cw[f];
+        issue(min(c + 1, nchunks - 1));
+        uint32_t p[FN][16];
+#pragma unroll
+        for (int f = 0; f < FN; f++)
+            decode_group(cur[f].x, cur[f].y, cur[f].z, mg, zs[f], p[f]);
+        const char* const buf = lds + (c & 1) * BM * kRowBytes + arow;
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            half8_t av[FM];
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+                av[i] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(buf + i * 32 * kRowBytes + st * 16));
+#pragma unroll
+            for (int f = 0; f < FN; f++) {
+                const half8_t bv = as_h8(p[f][4 * st], p[f][4 * st + 1], p[f][4 * st + 2], p[f][4 * st + 3]);
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+                    acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv, acc[i][f], 0, 0, 0);
+            }
+        }
+        if (c + 1 < nchunks)
+            stage(c + 1);
+        __syncthreads();
+    }
+
+    // row step, then the weak columns
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int f = 0; f < FN; f++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[i][f][r] *= sc[f];
+    if (k > 0) {
+        int xrow[FM];
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            xrow[i] = min(wm * 32 * FM + 32 * i + l32, mv - 1) * K;
+        for (int cs = 0; cs < k; cs += 16) {
+            uint32_t jw[8];
+            bool on[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const int c = cs + 8 * h + e;
+                on[e] = c < k;
+                int j = a.idx[min(c, k - 1)];
+                jw[e] = (uint32_t)((j >= 0 && j < K) ? j : 0);
+            }
+            uint32_t bw[FN][4];
+#pragma unroll
+            for (int f = 0; f < FN; f++) {
+                const int64_t row = n0 + min(wn * 32 * FN + 32 * f + l32, nv - 1);
+                const uint16_t* wr = a.ww + row * k;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    const int c = cs + 8 * h + 2 * e2;
+                    const uint32_t lo = on[2 * e2] ? wr[c] : 0u;
+                    const uint32_t hi = on[2 * e2 + 1] ? wr[c + 1] : 0u;
+                    bw[f][e2] = lo | (hi << 16);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < FM; i++) {
+                const uint16_t* xm = a.x + (int64_t)m0 * K + xrow[i];
+                uint32_t aw[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    const uint32_t lo = on[2 * e2] ? xm[jw[2 * e2]] : 0u;
+                    const uint32_t hi = on[2 * e2 + 1] ? xm[jw[2 * e2 + 1]] : 0u;
+                    aw[e2] = lo | (hi << 16);
+                }
+                const half8_t av = as_h8(aw[0], aw[1], aw[2], aw[3]);
+#pragma unroll
+                for (int f = 0; f < FN; f++)
+                    acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        av, as_h8(bw[f][0], bw[f][1], bw[f][2], bw[f][3]), acc[i][f], 0, 0, 0);
+            }
+        }
+    }
+
+    // D element r of lane l: token 8 (r / 4) + 4 h + r % 4, row l % 32
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int f = 0; f < FN; f++) {
+            const int n = n0 + wn * 32 * FN + 32 * f + l32;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * 32 * FM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < M && n < N)
+                    a.y[(int64_t)m * N + n] = f2h(acc[i][f][r]);
+            }
+        }
+}
+
+template <int FM, int FN, int WM, int WN>
+hipError_t launch_tile(GemmArgs a, hipStream_t s)
+{
+    using T = Tile<FM, FN, WM, WN>;
+    a.mblocks = (a.M + T::BM - 1) / T::BM;
+    const int64_t nblocks = (int64_t)a.mblocks * ((a.N + T::BN - 1) / T::BN);
+    if (nblocks > INT32_MAX)
+        return hipErrorInvalidValue;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&k_gemm<FM, FN, WM, WN>), hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL((k_gemm<FM, FN, WM, WN>), dim3((unsigned)nblocks), dim3(T::NT), T::LDS, s, a);
+    return hipGetLastError();
+}
+
+int64_t env_min_m()
+{
+    const char* e = std::getenv("OWQ_GEMM_MIN_M");
+    if (e && *e) {
+        const long long v = std::atoll(e);
+        if (v >= 1)
+            return v;
+    }
+    return 5;
+}
+
+}  // namespace
+
+int64_t gemm_min_m()
+{
+    static const int64_t v = env_min_m();
+    return v;
+}
+
+hipError_t launch_gemm(const LinearDesc& d, int64_t M, hipStream_t s)
+{
+    GemmArgs a;
+    a.q = d.q;
+    a.s = d.s;
+    a.z = d.z;
+    a.idx = d.idx;
+    a.ww = d.ww;
+    a.x = d.x;
+    a.y = d.y;
+    a.M = (int32_t)M;
+    a.N = (int32_t)d.N;
+    a.K = (int32_t)d.K;
+    a.k = d.k;
+    a.mblocks = 1;
+    if (M >= 128)
+        return launch_tile<4, 2, 2, 2>(a, s);  // 256 tokens x 128 rows
+    return launch_tile<1, 2, 1, 4>(a, s);      // 32 tokens x 256 rows
+}
 
 }  // namespace owq

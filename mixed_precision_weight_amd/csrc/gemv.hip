@@ -21,21 +21,15 @@
 // whole decoder layer (several linears) is one launch. Rows finish with a
 // 64-lane reduction of four rows at once (lane-half swaps, then DPP).
 //
-// Decode without per-code shifts: a 3-bit field that sits inside the mantissa of
-// an fp16 half (bits p..p+2 with p <= 7) becomes an exact fp16 number once an
-// exponent is OR-ed above it: exponent 2^(10-p) gives the value 2^(10-p) + q.
-// With the sequential bit order (code c at bits 3c..3c+2 of the 96-bit group),
-// six 32-bit windows of the group (w0>>2, bits 11..42, w1, w1>>9, bits 62..93,
-// w2>>7) each hold codes at in-half positions 1/4/7 (low half) and 0/3/6 (high
-// half), so one v_and_or_b32 yields a packed pair (off_lo + q_a, off_hi + q_b);
-// codes 0 and 31 form the sixteenth pair. One v_pk_add_f16 of the row's
-// -(off + z) pair then gives (q_a - z, q_b - z) EXACTLY (small integers), and one
-// v_dot2_f32_f16 multiplies it with the matching x pair. Every product is exact,
-// so the fp32 sum's error is bounded relative to sum_j |(q_j - z) x_j|, for
-// every row, including rows whose codes all equal the zero point. Per tile:
+// Each 12-byte group is decoded in registers (owq_decode.h) to sixteen exact
+// (q_a - z, q_b - z) fp16 pairs, and one v_dot2_f32_f16 per pair multiplies it
+// with the matching x pair, staged in the same pair order. Every product is
+// exact, so the fp32 sum's error is bounded relative to sum_j |(q_j - z) x_j|,
+// for every row, including rows whose codes all equal the zero point. Per tile:
 // 5 window ops, 17 and-or, 16 packed subtracts, 16 dot2 per token.
 #include <cstdlib>
 
+#include "owq_decode.h"
 #include "owq_device.h"
 #include "owq_launch.h"
 
@@ -60,102 +54,6 @@ struct GemvBatch {
     int32_t count;
 };
 
-// Pair p of a group = (code lo[p], code hi[p]).
-__device__ constexpr int kPairLo[16] = {1, 2, 3, 4, 5, 11, 12, 13, 14, 15, 21, 22, 23, 24, 25, 0};
-__device__ constexpr int kPairHi[16] = {6, 7, 8, 9, 10, 16, 17, 18, 19, 20, 26, 27, 28, 29, 30, 31};
-
-// Field masks and exponents: low-half positions 1/4/7 with exponents 2^9/2^6/2^3,
-// high-half positions 0/3/6 with exponents 2^10/2^7/2^4 -> coefficient 1 on q.
-constexpr uint32_t kMaskA = 0x0007000eu, kMagicA = 0x64006000u;  // (512 + q, 1024 + q)
-constexpr uint32_t kMaskB = 0x00380070u, kMagicB = 0x58005400u;  // (64 + q, 128 + q)
-constexpr uint32_t kMaskC = 0x01c00380u, kMagicC = 0x4c004800u;  // (8 + q, 16 + q)
-
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-
-__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
-{
-    return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
-}
-
-// v_and_or_b32 d = (a & mask) | magic. gfx9 VOP3 takes no literal operands and
-// reads at most one SGPR, so the mask goes in an SGPR and the exponent pattern in
-// a VGPR; plain C would be split into v_and_b32 + v_or_b32 with two literals.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic)
-{
-    uint32_t d;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(magic));
-    return d;
-}
-
-struct Magic {  // exponent patterns held in VGPRs for the whole kernel
-    uint32_t a, b, c, p;
-};
-
-__device__ __forceinline__ Magic make_magic()
-{
-    Magic m;
-    // opaque to the optimiser so the constants stay in registers
-    asm volatile("v_mov_b32 %0, %1" : "=v"(m.a) : "i"(kMagicA));
-    asm volatile("v_mov_b32 %0, %1" : "=v"(m.b) : "i"(kMagicB));
-    asm volatile("v_mov_b32 %0, %1" : "=v"(m.c) : "i"(kMagicC));
-    asm volatile("v_mov_b32 %0, %1" : "=v"(m.p) : "i"(0x64006400u));
-    return m;
-}
-
-// -(off + z) for both halves of each pair type, as fp16 bit patterns:
-// off + z = 2^E + z has mantissa field z * 2^(10 - E) under exponent E.
-struct ZeroSub {
-    uint32_t a, b, c, p;
-};
-
-__device__ __forceinline__ ZeroSub make_zero_sub(uint32_t z)
-{
-    ZeroSub n;
-    n.a = ((0xe400u | z) << 16) | (0xe000u | (z << 1));          // -(1024 + z), -(512 + z)
-    n.b = ((0xd800u | (z << 3)) << 16) | (0xd400u | (z << 4));   // -(128 + z),  -(64 + z)
-    n.c = ((0xcc00u | (z << 6)) << 16) | (0xc800u | (z << 7));   // -(16 + z),   -(8 + z)
-    n.p = ((0xe400u | z) << 16) | (0xe400u | z);                 // -(1024 + z) twice
-    return n;
-}
-
-__device__ __forceinline__ uint32_t sub_h2(uint32_t a, uint32_t b)
-{
-    return __builtin_bit_cast(uint32_t, as_h2(a) + as_h2(b));
-}
-
-// Sixteen exact (q_lo - z, q_hi - z) fp16 pairs of one 96-bit group, in
-// kPairLo/kPairHi order.
-__device__ __forceinline__ void decode_group(uint32_t w0, uint32_t w1, uint32_t w2, const Magic& mg,
-                                             const ZeroSub& n, uint32_t p[16])
-{
-    const uint32_t a1 = w0 >> 2;
-    const uint32_t b1 = __builtin_amdgcn_alignbit(w1, w0, 11);
-    const uint32_t a2 = w1;
-    const uint32_t b2 = w1 >> 9;
-    const uint32_t a3 = __builtin_amdgcn_alignbit(w2, w1, 30);
-    const uint32_t b3 = w2 >> 7;
-    p[0] = sub_h2(and_or(a1, kMaskA, mg.a), n.a);
-    p[1] = sub_h2(and_or(a1, kMaskB, mg.b), n.b);
-    p[2] = sub_h2(and_or(a1, kMaskC, mg.c), n.c);
-    p[3] = sub_h2(and_or(b1, kMaskA, mg.a), n.a);
-    p[4] = sub_h2(and_or(b1, kMaskB, mg.b), n.b);
-    p[5] = sub_h2(and_or(a2, kMaskA, mg.a), n.a);
-    p[6] = sub_h2(and_or(a2, kMaskB, mg.b), n.b);
-    p[7] = sub_h2(and_or(a2, kMaskC, mg.c), n.c);
-    p[8] = sub_h2(and_or(b2, kMaskA, mg.a), n.a);
-    p[9] = sub_h2(and_or(b2, kMaskB, mg.b), n.b);
-    p[10] = sub_h2(and_or(a3, kMaskA, mg.a), n.a);
-    p[11] = sub_h2(and_or(a3, kMaskB, mg.b), n.b);
-    p[12] = sub_h2(and_or(a3, kMaskC, mg.c), n.c);
-    p[13] = sub_h2(and_or(b3, kMaskA, mg.a), n.a);
-    p[14] = sub_h2(and_or(b3, kMaskB, mg.b), n.b);
-    // (1024 + q0, 1024 + q31): code 0 at bits 0..2 of w0, code 31 at bits 29..31 of w2
-    p[15] = sub_h2(and_or(w2 >> 13, 0x00070000u, and_or(w0, 7u, mg.p)), n.p);
-}
-
-
 // Staged x layout (uint4 units): [m][tile u][quad qd][lane l] for group g = 64 u + l,
 // so a lane's four quads of a tile are 1 KB apart (immediate offsets) and the
 // lanes of a wave read consecutive 16-byte words.
@@ -172,13 +70,7 @@ __device__ __forceinline__ void store_group(const uint4 (&v)[4], uint4* __restri
         w[4 * i + 3] = v[i].w;
     }
     uint32_t pr[16];
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const int lo = kPairLo[i], hi = kPairHi[i];
-        uint32_t hl = (w[lo >> 1] >> (16 * (lo & 1))) & 0xffffu;
-        uint32_t hh = (w[hi >> 1] >> (16 * (hi & 1))) & 0xffffu;
-        pr[i] = hl | (hh << 16);
-    }
+    pair_order(w, pr);
 #pragma unroll
     for (int qd = 0; qd < 4; qd++)
         xs_mg[qd * 64] = make_uint4(pr[4 * qd], pr[4 * qd + 1], pr[4 * qd + 2], pr[4 * qd + 3]);

@@ -98,6 +98,13 @@ EDGE = [
     (64, 640, 7, (1, 2, 3, 17)),
     (300, 4096, 0, (1,)),
     (17, 28672, 221, (1, 2)),
+    # matrix-core path: ragged token and row blocks, odd group counts, all-weak
+    (200, 4128, 17, (5, 33, 300)),
+    (1, 32, 32, (5, 128)),
+    (300, 96, 0, (128, 130)),
+    (7, 64, 64, (6, 129)),
+    (33, 65536, 20, (8, 129)),
+    (513, 2048, 40, (512, 700)),
 ]
 
 
