@@ -11,16 +11,23 @@ Decode reads one of R = 8 packed copies of the layer (8 x 79 MB > 2 x the 256 MB
 Infinity Cache), written by the calibration stage R/2 steps earlier, so its
 bytes come from HBM. Inputs are resident in HBM before timing starts.
 
-Reported value: effective GB/s of the decode stage (packed codes + fp16 scales +
-uint8 zeros + fp16 weak columns + fp16 x, per linear, summed over the layer) per
-second of decode-launch time, measured with HIP events around each decode
-launch on the launch stream. Other stages are reported alongside.
+Reported value: effective GB/s of the decode launch (packed codes + fp16 scales
++ uint8 zeros + fp16 weak columns + fp16 x, per linear, summed over the layer)
+divided by its duration, measured with HIP events recorded on the launch stream
+around every decode launch of the timed steps. The other stages are timed the
+same way and reported under "kernels", each against its own roofline.
+
+--copy-reference adds, after the timed steps, three copies of a 512 MiB buffer
+(a plain copy kernel of known size) so that hardware-counter runs of this script
+can scale FETCH_SIZE / WRITE_SIZE to bytes.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,15 +35,50 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "OWQ 3.1-bit linear: effective GB/s and % HBM peak at M=1 (7B shapes); TFLOP/s at M=2048"
-HBM_PEAK_GBS = 8000.0
-MFMA_FP16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 ROTATE = 8
 PREFILL_M = 2048
+SWEEP_MS = (1, 2, 4, 8, 16)
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemv_llama7b_layer_decode_m1_hbm_traffic.txt")
+GEMV_SOURCES = ("gemv.hip", "owq_decode.h", "owq_device.h")
 
 
 def eff_bytes(N, K, k, M):
     """Algorithmic bytes of one linear: codes + scales + zeros + weak block + x."""
     return 3 * N * K // 8 + 2 * N + N + 2 * N * k + 2 * M * K
+
+
+def calib_bytes(N, K, T):
+    """Algorithmic bytes of owq_calibrate_score: X and W read once, lambda and score written."""
+    return 2 * T * K + 2 * N * K + 16 * K
+
+
+def pack_bytes(N, K, k):
+    """Algorithmic bytes of owq_pack: W and weak_idx read, codes, scales, zeros, weak block written."""
+    return 2 * N * K + 4 * k + 3 * N * K // 8 + 3 * N + 2 * N * k
+
+
+def gemv_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "mixed_precision_weight_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None when
+    there is none or the decode kernel's sources changed since it was taken."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    src = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not src or not val or src.group(1) != gemv_source_digest():
+        return None
+    return float(val.group(1))
 
 
 def cpu_baseline(cfg, min_seconds=10.0):
@@ -65,9 +107,16 @@ def cpu_baseline(cfg, min_seconds=10.0):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    return {"value": total_bytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"full 7-linear layer decode at M=1 (202.4M weights), {reps} repetition(s), "
+    return {"value": round(total_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"full 7-linear layer decode at M=1 (202.4M weights), {reps} repetition(s) in "
                       f"{el:.1f} s, single-threaded C oracle with fp64 accumulation"}
+
+
+def hbm_entry(nbytes, seconds, what):
+    gbs = nbytes / seconds / 1e9
+    return {"what": what, "us": round(seconds * 1e6, 2), "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": int(nbytes)}
 
 
 def main():
@@ -77,10 +126,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the decode batch sweep")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="end with three 512 MiB device copies (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the hot path runs on one GPU's share, see the design notes for sharding)", file=sys.stderr)
+              "(the hot path runs on one GPU's share of a layer; multi-GPU sharding is design only)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -89,20 +142,22 @@ def main():
     from mixed_precision_weight_amd import owq, synth
 
     dev = torch.device("cuda:0")
+    owq.lib()  # fails loudly if the HIP library is missing
     cfg = synth.CONFIGS[1]
     specs = cfg.layers
+    L = len(specs)
     print(f"bench: {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     W, X, x1, xp = [], [], [], []
     for li, spec in enumerate(specs):
         seed = cfg.seed(li)
         W.append(torch.from_numpy(synth.weights(spec, seed)).to(dev))
         X.append(torch.from_numpy(synth.calibration(spec, seed, cfg.T)).to(dev))
-        x1.append(torch.from_numpy(synth.activations(spec, seed, 1)).to(dev))
+        x1.append(torch.from_numpy(synth.activations(spec, seed, max(SWEEP_MS))).to(dev))
         xp.append(torch.from_numpy(synth.activations(spec, seed + 500, PREFILL_M)).to(dev))
+    xd = [x[:1] for x in x1]
 
     ws = torch.empty(max(owq.calibrate_workspace_bytes(s.N, s.K, cfg.T) for s in specs), dtype=torch.uint8,
                      device=dev)
-    lam = [torch.empty(s.K, dtype=torch.float64, device=dev) for s in specs]
     slots = []
     for r in range(ROTATE):
         slot = []
@@ -112,14 +167,25 @@ def main():
                          "zeros": torch.empty(s.N, dtype=torch.uint8, device=dev),
                          "w_weak": torch.empty((s.N, s.k), dtype=torch.float16, device=dev)})
         slots.append(slot)
-    y1 = [torch.empty((1, s.N), dtype=torch.float16, device=dev) for s in specs]
+    y1 = [torch.empty((max(SWEEP_MS), s.N), dtype=torch.float16, device=dev) for s in specs]
+    yd = [y[:1] for y in y1]
     yp = [torch.empty((PREFILL_M, s.N), dtype=torch.float16, device=dev) for s in specs]
 
-    def calibrate_pack(slot):
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def calibrate_pack(slot, ev=None):
         for li, s in enumerate(specs):
+            if ev is not None:
+                ev[3 * li].record()
             _, score = owq.calibrate(W[li], X[li], workspace=ws)
+            if ev is not None:
+                ev[3 * li + 1].record()
             idx = owq.select_weak(score, s.k)
+            if ev is not None:
+                ev[3 * li + 2].record()
             owq.pack(W[li], idx, out=slot[li])
+        if ev is not None:
+            ev[3 * L].record()
 
     # fill every rotation slot before timing
     for r in range(ROTATE):
@@ -127,42 +193,60 @@ def main():
     torch.cuda.synchronize()
 
     decode_bytes = sum(eff_bytes(s.N, s.K, s.k, 1) for s in specs)
-    prefill_flops = sum(2 * PREFILL_M * s.N * s.K for s in specs)
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    NE = 3 * L + 1 + 2 + L + 1  # calibration boundaries, decode pair, prefill boundaries
 
     def step(i, ev):
         cal_slot = slots[i % ROTATE]
         dec_slot = slots[(i + ROTATE // 2) % ROTATE]
-        ev[0].record()
-        calibrate_pack(cal_slot)
-        ev[1].record()
-        owq.linear_batched(dec_slot, x1, y1)
-        ev[2].record()
-        for li in range(len(specs)):
+        calibrate_pack(cal_slot, ev)
+        o = 3 * L + 1
+        ev[o].record()
+        owq.linear_batched(dec_slot, xd, yd)
+        ev[o + 1].record()
+        o += 2
+        for li in range(L):
+            ev[o + li].record()
             owq.linear(cal_slot[li], xp[li], yp[li])
-        ev[3].record()
+        ev[o + L].record()
 
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        step(i, [E() for _ in range(4)])
+        step(i, [E() for _ in range(NE)])
     torch.cuda.synchronize()
 
     print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
-    evs = [[E() for _ in range(4)] for _ in range(args.steps)]
+    evs = [[E() for _ in range(NE)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    print("bench: timed steps done", file=sys.stderr, flush=True)
 
-    cal_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    pre_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    dec_avg_s = float(np.mean(dec_ms)) / 1e3
-    value = decode_bytes / dec_avg_s / 1e9
-    pre_tflops = prefill_flops / (float(np.mean(pre_ms)) / 1e3) / 1e12
+    def mean_ms(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
 
+    cal_s = [mean_ms(3 * li, 3 * li + 1) / 1e3 for li in range(L)]
+    sel_s = [mean_ms(3 * li + 1, 3 * li + 2) / 1e3 for li in range(L)]
+    pak_s = [mean_ms(3 * li + 2, 3 * li + 3) / 1e3 for li in range(L)]
+    o = 3 * L + 1
+    dec_s = mean_ms(o, o + 1) / 1e3
+    dec_min_s = min(e[o].elapsed_time(e[o + 1]) for e in evs) / 1e3
+    o += 2
+    pre_s = [mean_ms(o + li, o + li + 1) / 1e3 for li in range(L)]
+
+    value = decode_bytes / dec_s / 1e9
+    cal_bytes = sum(calib_bytes(s.N, s.K, cfg.T) for s in specs)
+    pk_bytes = sum(pack_bytes(s.N, s.K, s.k) for s in specs)
+    pre_flops = sum(2 * PREFILL_M * s.N * s.K for s in specs)
+    pre_tflops = pre_flops / sum(pre_s) / 1e12
+    per_linear_prefill = {}
+    for li, s in enumerate(specs):
+        tf = 2 * PREFILL_M * s.N * s.K / pre_s[li] / 1e12
+        per_linear_prefill[f"{s.name} {s.N}x{s.K}"] = {"us": round(pre_s[li] * 1e6, 1), "tflops": round(tf, 1)}
+
+    traffic = measured_traffic()
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -175,23 +259,64 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16",
-        "data": "synthetic",
-        "config": {"workload": "llama7b_layer_decode (7 linears: 4x 4096x4096 k=32, 2x 11008x4096 k=32, "
-                               "4096x11008 k=86)",
+        "data": "synthetic (seeded Gaussian weights and activations with planted outlier channels)",
+        "config": {"workload": "llama7b_layer_decode: one LLaMA-7B decoder layer, 7 linears (4x 4096x4096 k=32, "
+                               "2x 11008x4096 k=32, 4096x11008 k=86), 3-bit codes + fp16 weak columns; "
+                               "decode M=1, calibration T=2048, prefill M=2048",
                    "decode_M": 1, "calib_T": cfg.T, "prefill_M": PREFILL_M, "bits": 3,
                    "decode_effective_bytes": decode_bytes, "rotation_copies": ROTATE},
-        "roofline": {"kernel": "k_gemv (decode, 7-linear batched launch)", "bound": "hbm",
+        "roofline": {"kernel": "k_gemv<1> (decode GEMV, one launch over the 7 linears)", "bound": "hbm",
                      "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
-        "stages": {
-            "decode_us_per_layer": round(dec_avg_s * 1e6, 2),
-            "decode_pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
-            "calibrate_select_pack_ms_per_layer": round(float(np.mean(cal_ms)), 3),
-            "prefill_ms_per_layer": round(float(np.mean(pre_ms)), 3),
-            "prefill_tflops": round(pre_tflops, 2),
-            "prefill_pct_mfma_peak": round(100 * pre_tflops / MFMA_FP16_PEAK_TFLOPS, 2),
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "kernels": {
+            "decode": dict(hbm_entry(decode_bytes, dec_s, "k_gemv<1>, 7 linears in one launch"),
+                           us_min=round(dec_min_s * 1e6, 2)),
+            "prefill": {"what": "k_gemm (MFMA 32x32x16 f16), 7 linears at M=2048", "us": round(sum(pre_s) * 1e6, 1),
+                        "bound": "mfma", "achieved": round(pre_tflops, 1), "peak": MFMA_FP16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
+                        "algorithmic_flops": pre_flops, "per_linear": per_linear_prefill},
+            "calibrate_score": hbm_entry(cal_bytes, sum(cal_s), "k_colsum x2 + k_rowfit + k_finalize, 7 linears"),
+            "select_weak": {"what": "k_topk, 7 linears", "us": round(sum(sel_s) * 1e6, 1), "bound": "latency"},
+            "pack": hbm_entry(pk_bytes, sum(pak_s), "k_pack, 7 linears"),
         },
     }
+
+    if not args.no_sweep:
+        print("bench: decode batch sweep", file=sys.stderr, flush=True)
+        sweep = {}
+        reps = 16
+        for M in SWEEP_MS:
+            xs = [x[:M] for x in x1]
+            ys = [y[:M] for y in y1]
+            evp = [(E(), E()) for _ in range(reps)]
+            for r in range(reps + 2):
+                slot = slots[r % ROTATE]
+                if r >= 2:
+                    evp[r - 2][0].record()
+                if M <= 4:
+                    owq.linear_batched(slot, xs, ys)
+                else:
+                    for li in range(L):
+                        owq.linear(slot[li], xs[li], ys[li])
+                if r >= 2:
+                    evp[r - 2][1].record()
+            torch.cuda.synchronize()
+            t = float(np.mean([a.elapsed_time(b) for a, b in evp])) / 1e3
+            nb = sum(eff_bytes(s.N, s.K, s.k, M) for s in specs)
+            sweep[f"M={M}"] = {"us_per_layer": round(t * 1e6, 2), "effective_GBps": round(nb / t / 1e9, 1),
+                               "frac_hbm": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
+                               "path": "k_gemv (one launch)" if M <= 4 else "k_gemm (7 launches)"}
+        result["decode_batch_sweep"] = sweep
+
+    if args.copy_reference:
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_reference_bytes"] = n
+
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
