@@ -143,17 +143,20 @@ typedef struct {
  *   y[m][i] = s_i * sum_j (q_ij - z_i) x[m][j] + sum_c w_weak[i][c] x[m][weak_idx[c]]
  * computed with fp32 accumulation and rounded to fp16 (nearest-even).
  * L: HOST pointer to the layer; x: fp16 [M][K]; y: fp16 [M][N] (output, must not
- * alias x or the layer). Small M runs an HBM-streaming kernel on the vector ALUs;
- * larger M runs a matrix-core (MFMA) kernel; both compute the same definition. */
+ * alias x or the layer). M <= 4 runs an HBM-streaming kernel on the vector ALUs,
+ * 5 <= M <= 16 a streaming kernel that multiplies on the matrix cores, larger M a
+ * tiled matrix-core (MFMA) GEMM; all compute the same definition. The environment
+ * variable OWQ_DECODE=matrix sends every M <= 16 to the matrix-core streaming
+ * kernel (read at each call); OWQ_GEMM_MIN_M (read once) moves the GEMM bound. */
 owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M,
                       uint16_t* y, void* stream);
 
-/* `count` independent linears with the same M in ONE kernel launch (the decode
- * GEMV only: 1 <= M <= 4 and M * K * 2 + 16384 + 64 <= 163840 for every layer,
- * since x is staged in LDS). Ls: HOST array [count] of layers; xs, ys: HOST
- * arrays [count] of device pointers with the shapes owq_linear expects.
- * Equivalent to count calls of owq_linear. Returns OWQ_ERR_UNSUPPORTED outside
- * those limits or 1 <= count <= 64. */
+/* `count` independent linears with the same M in ONE kernel launch per 16 layers,
+ * with the results owq_linear's decode kernels would give one by one (the layers
+ * run in order of decreasing K inside the launch). Ls: HOST array [count] of
+ * layers; xs, ys: HOST arrays [count] of device pointers with the shapes
+ * owq_linear expects. Returns OWQ_ERR_UNSUPPORTED unless 1 <= M <= 16 and
+ * 1 <= count <= 64. */
 owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs,
                               uint16_t* const* ys, int32_t count, int64_t M,
                               void* stream);

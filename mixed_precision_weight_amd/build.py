@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I" + os.path.join(ROOT, "include")]
 NO_CONTRACT = {"calib.hip", "pack.hip"}
-SOURCES = ["api.cpp", "calib.hip", "topk.hip", "pack.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "calib.hip", "topk.hip", "pack.hip", "gemv.hip", "mfv.hip", "gemm.hip"]
 
 
 def _compile(src: str) -> str:

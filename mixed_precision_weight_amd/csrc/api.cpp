@@ -223,14 +223,17 @@ owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t
     owq::LinearDesc d = desc_of(L, x, y);
     if (M >= owq::gemm_min_m())
         return hip_status(owq::launch_gemm(d, M, s), "owq_linear (matrix-core) launch");
+    // decode kernels, in token slices of the chosen kernel's capacity
     hipError_t e = hipSuccess;
-    const int64_t mt = owq::gemv_max_tokens(L->K);
-    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += mt) {
-        int64_t mm = M - m0 < mt ? M - m0 : mt;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess;) {
+        const bool mat = owq::decode_on_matrix_cores(M - m0);
+        const int64_t cap = mat ? owq::kMfvMaxM : owq::gemv_max_tokens(L->K);
+        const int64_t mm = M - m0 < cap ? M - m0 : cap;
         owq::LinearDesc dm = d;
         dm.x = x + m0 * L->K;
         dm.y = y + m0 * L->N;
-        e = owq::launch_gemv(&dm, 1, (int)mm, s);
+        e = mat ? owq::launch_mfv(&dm, 1, (int)mm, s) : owq::launch_gemv(&dm, 1, (int)mm, s);
+        m0 += mm;
     }
     return hip_status(e, "owq_linear (decode) launch");
 }
@@ -242,9 +245,10 @@ owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs, ui
         return fail(OWQ_ERR_NULL, "Ls, xs and ys must be non-NULL");
     if (count < 1 || count > 64)
         return fail(OWQ_ERR_UNSUPPORTED, "count = %d: need 1 <= count <= 64", count);
-    if (M < 1 || M > owq::kGemvMaxM)
+    if (M < 1 || M > owq::kMfvMaxM)
         return fail(OWQ_ERR_UNSUPPORTED, "M = %lld: the batched decode launch needs 1 <= M <= %d",
-                    (long long)M, owq::kGemvMaxM);
+                    (long long)M, owq::kMfvMaxM);
+    const bool mat = owq::decode_on_matrix_cores(M);
     std::vector<owq::LinearDesc> d((size_t)count);
     for (int32_t l = 0; l < count; l++) {
         owq_status st = check_layer(&Ls[l], M, xs[l], ys[l]);
@@ -253,15 +257,16 @@ owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs, ui
         st = check_idx_on_host(Ls[l].weak_idx, Ls[l].k, Ls[l].K, (hipStream_t)stream);
         if (st != OWQ_OK)
             return st;
-        if (!owq::gemv_fits(M, Ls[l].K))
-            return fail(OWQ_ERR_UNSUPPORTED, "layer %d: M * K = %lld exceeds the batched decode limit "
-                        "(M * K * 2 + 16 KB <= 160 KB of LDS)", l, (long long)(M * Ls[l].K));
+        if (mat ? !owq::mfv_fits(M, Ls[l].K) : !owq::gemv_fits(M, Ls[l].K))
+            return fail(OWQ_ERR_UNSUPPORTED, "layer %d: M = %lld, K = %lld outside the batched decode limits", l,
+                        (long long)M, (long long)Ls[l].K);
         d[l] = desc_of(&Ls[l], xs[l], ys[l]);
     }
     hipError_t e = hipSuccess;
     for (int32_t l0 = 0; l0 < count && e == hipSuccess; l0 += owq::kGemvMaxLayers) {
         int n = count - l0 < owq::kGemvMaxLayers ? count - l0 : owq::kGemvMaxLayers;
-        e = owq::launch_gemv(d.data() + l0, n, (int)M, (hipStream_t)stream);
+        e = mat ? owq::launch_mfv(d.data() + l0, n, (int)M, (hipStream_t)stream)
+                : owq::launch_gemv(d.data() + l0, n, (int)M, (hipStream_t)stream);
     }
     return hip_status(e, "owq_linear_batched launch");
 }

@@ -300,7 +300,7 @@ int64_t env_min_m()
         if (v >= 1)
             return v;
     }
-    return 5;
+    return 17;
 }
 
 }  // namespace

@@ -313,9 +313,20 @@ bool gemv_fits(int64_t M, int64_t K)
 // rows_per_wave(class) consecutive rows of its layer.
 hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
 {
+    // layers with the longest rows first: their blocks run longest
+    int order[kGemvMaxLayers];
+    for (int l = 0; l < count; l++)
+        order[l] = l;
+    for (int a = 1; a < count; a++)
+        for (int c = a; c > 0 && d[order[c]].K > d[order[c - 1]].K; c--) {
+            const int t = order[c];
+            order[c] = order[c - 1];
+            order[c - 1] = t;
+        }
     GemvBatch b{};
     int nblocks = 0;
-    for (int l = 0; l < count; l++) {
+    for (int o = 0; o < count; o++) {
+        const int l = order[o];
         GemvLayer& L = b.L[b.count++];
         L.q = d[l].q;
         L.s = d[l].s;

@@ -47,6 +47,13 @@ hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s);
 // Tokens per GEMV launch for a layer of K columns (x of all tokens is staged in LDS).
 int gemv_max_tokens(int64_t K);
 bool gemv_fits(int64_t M, int64_t K);
+// Matrix-core decode over `count` layers (count <= kGemvMaxLayers), 1 <= M <= kMfvMaxM.
+constexpr int kMfvMaxM = 16;
+hipError_t launch_mfv(const LinearDesc* d, int count, int M, hipStream_t s);
+bool mfv_fits(int64_t M, int64_t K);
+// Decode kernel choice for M tokens: true = matrix-core decode (launch_mfv), false =
+// vector-ALU decode (launch_gemv). OWQ_DECODE=vector|matrix overrides (read per call).
+bool decode_on_matrix_cores(int64_t M);
 // Matrix-core GEMM for larger M.
 hipError_t launch_gemm(const LinearDesc& d, int64_t M, hipStream_t s);
 // Smallest M routed to the matrix-core kernel (read once from OWQ_GEMM_MIN_M).
