@@ -12,7 +12,10 @@
 // Tiling: a block owns a BM x BN tile of y (tokens x output rows) and its waves
 // form a WM x WN grid, each wave owning 32 FM tokens x 32 FN rows, i.e. FM x FN
 // accumulators of v_mfma_f32_32x32x16_f16 (A = x, B = the weights transposed).
-// K is walked in chunks of 64 columns: two 32-code groups.
+// K is walked in chunks of 64 KH columns (2 KH 32-code groups). The large-M
+// tile is 128 tokens x 256 rows with 8 waves of 64 x 64 and two waves per SIMD:
+// measured on MI355X it beat 256 x 128 and 256 x 256 tiles, mainly because the
+// grid has enough blocks (256 for a 2048 x 4096 output) to fill every CU.
 //
 // The weights never pass through LDS. The MFMA pairs the eight A and B operand
 // elements of lane l with the same eight k values of half h = l / 32, and the
@@ -24,8 +27,10 @@
 // bytes of one group of one token, rearranges them in registers and writes them
 // with 128-bit stores; an A operand is then one 128-bit LDS read per lane (rows
 // padded by 16 bytes so the reads of a wave spread over all banks). LDS is
-// double buffered and the next chunk's x and codes are loaded into registers
-// while the current chunk computes: one barrier per chunk.
+// double buffered and loads run two chunks ahead: while chunk c computes, x and
+// codes of chunk c + 2 are loaded (x into the register set staged last, codes
+// into the set just decoded) and x of chunk c + 1 is written to LDS; one barrier
+// per chunk.
 //
 // Epilogue: the accumulators (sums of exact fp16 products of integer weights and
 // x) are scaled by the row step, the weak columns run as extra 16-deep MFMA
@@ -61,34 +66,36 @@ struct GemmArgs {
     int32_t mblocks;  // token blocks (the fastest-varying block index)
 };
 
-constexpr int kRowBytes = 2 * 64 + 16;  // LDS bytes per staged token: two groups + pad
-
 __device__ __forceinline__ half8_t as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
     uint4 v = make_uint4(a, b, c, d);
     return __builtin_bit_cast(half8_t, v);
 }
 
-template <int FM, int FN, int WM, int WN>
+// FM x FN accumulators per wave, WM x WN waves per block, KH groups per lane
+// half per K chunk (a chunk is 2 KH groups = 64 KH columns), WPE waves per SIMD.
+template <int FM, int FN, int WM, int WN, int KH, int WPE>
 struct Tile {
-    static constexpr int NT = 64 * WM * WN;  // threads
-    static constexpr int BM = 32 * FM * WM;  // tokens per block
-    static constexpr int BN = 32 * FN * WN;  // rows per block
-    static constexpr int XI = (2 * BM + NT - 1) / NT;  // staged group rows per thread
-    static constexpr int LDS = 2 * BM * kRowBytes;      // double buffer
+    static constexpr int NT = 64 * WM * WN;             // threads
+    static constexpr int BM = 32 * FM * WM;             // tokens per block
+    static constexpr int BN = 32 * FN * WN;             // rows per block
+    static constexpr int KG = 2 * KH;                   // groups per chunk
+    static constexpr int RB = KG * 64 + 16;             // LDS bytes per staged token (padded)
+    static constexpr int XI = (KG * BM + NT - 1) / NT;  // staged group rows per thread
+    static constexpr int LDS = 2 * BM * RB;             // double buffer
 };
 
-template <int FM, int FN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs a)
+template <int FM, int FN, int WM, int WN, int KH, int WPE>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k_gemm(GemmArgs a)
 {
-    using T = Tile<FM, FN, WM, WN>;
-    constexpr int NT = T::NT, BM = T::BM, BN = T::BN, XI = T::XI;
+    using T = Tile<FM, FN, WM, WN, KH, WPE>;
+    constexpr int NT = T::NT, BM = T::BM, BN = T::BN, KG = T::KG, RB = T::RB, XI = T::XI;
     extern __shared__ uint4 smem[];
     char* const lds = reinterpret_cast<char*>(smem);
 
     const int M = a.M, N = a.N, K = a.K, k = a.k;
     const int G = K >> 5;
-    const int nchunks = (G + 1) >> 1;
+    const int nchunks = (G + KG - 1) / KG;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
@@ -105,12 +112,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs a)
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(a.q) + (int64_t)n0 * G * 3, (short)0, nv * G * 12, 0x00020000);
 
-    // staging items i = tid + NT t: token i / 2 of the block, group i % 2 of the chunk
+    // staging items i = tid + NT t: token i / KG of the block, group i % KG of the chunk
     int xoff[XI];
 #pragma unroll
     for (int t = 0; t < XI; t++) {
         const int i = tid + NT * t;
-        xoff[t] = min(i >> 1, mv - 1) * K * 2;
+        xoff[t] = min(i / KG, mv - 1) * K * 2;
     }
     int qoff[FN];
     float sc[FN];
@@ -123,30 +130,38 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs a)
         zs[f] = make_zero_sub((uint32_t)a.z[n0 + r]);
     }
 
-    i32x4 xg[XI][4];
-    u32x3 cw[FN];
-    auto issue = [&](int c) {
+    // Two chunks in flight: x and codes of chunk c + 2 are loaded while chunk c
+    // computes (x into the register set just staged, codes into the set just
+    // decoded), so a load has two chunks of MFMA work to arrive in.
+    typedef i32x4 XRegs[XI][4];
+    typedef u32x3 QRegs[FN][KH];
+    auto load_x = [&](int c, XRegs& xg) {
 #pragma unroll
         for (int t = 0; t < XI; t++) {
-            const int g = min(2 * c + ((tid + NT * t) & 1), G - 1);
+            const int g = min(KG * c + (tid + NT * t) % KG, G - 1);
 #pragma unroll
             for (int q4 = 0; q4 < 4; q4++)
                 xg[t][q4] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[t] + g * 64 + 16 * q4, 0, 0);
         }
-        const int g = min(2 * c + h, G - 1);
-#pragma unroll
-        for (int f = 0; f < FN; f++)
-            cw[f] = __builtin_amdgcn_raw_buffer_load_b96(qr, qoff[f] + g * 12, 0, 0);
     };
-    // staged x of chunk c into LDS buffer c & 1, in decode-pair order; a group
-    // past the end of K (odd K / 32) is staged as zeros
-    auto stage = [&](int c) {
-        char* const buf = lds + (c & 1) * BM * kRowBytes;
+    auto load_q = [&](int c, QRegs& cw) {
+#pragma unroll
+        for (int j = 0; j < KH; j++) {
+            const int g = min(KG * c + 2 * j + h, G - 1);
+#pragma unroll
+            for (int f = 0; f < FN; f++)
+                cw[f][j] = __builtin_amdgcn_raw_buffer_load_b96(qr, qoff[f] + g * 12, 0, 0);
+        }
+    };
+    // x of chunk c into LDS buffer c & 1, in decode-pair order; a group past the
+    // end of K is staged as zeros
+    auto stage = [&](int c, const XRegs& xg) {
+        char* const buf = lds + (c & 1) * BM * RB;
 #pragma unroll
         for (int t = 0; t < XI; t++) {
             const int i = tid + NT * t;
-            if (i < 2 * BM) {
-                const bool live = 2 * c + (i & 1) < G;
+            if (KG * BM % NT == 0 || i < KG * BM) {
+                const bool live = KG * c + i % KG < G;
                 uint32_t w[16], pr[16];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++)
@@ -154,7 +169,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs a)
                     for (int e = 0; e < 4; e++)
                         w[4 * q4 + e] = live ? (uint32_t)xg[t][q4][e] : 0u;
                 pair_order(w, pr);
-                uint4* dst = reinterpret_cast<uint4*>(buf + (i >> 1) * kRowBytes + (i & 1) * 64);
+                uint4* dst = reinterpret_cast<uint4*>(buf + (i / KG) * RB + (i % KG) * 64);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++)
                     dst[q4] = make_uint4(pr[4 * q4], pr[4 * q4 + 1], pr[4 * q4 + 2], pr[4 * q4 + 3]);
@@ -172,38 +187,58 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs a)
             for (int r = 0; r < 16; r++)
                 acc[i][f][r] = 0.0f;
 
-    issue(0);
-    stage(0);
-    __syncthreads();
-    const int arow = (wm * 32 * FM + l32) * kRowBytes + h * 64;  // this lane's A operand row
-    for (int c = 0; c < nchunks; c++) {
-        u32x3 cur[FN];
+    const int arow = (wm * 32 * FM + l32) * RB + h * 64;  // this lane's A operand row
+    // chunk c: decode its codes (then reload that register set with chunk c + 2),
+    // MFMA against x staged in LDS, stage chunk c + 1, barrier
+    auto step = [&](int c, QRegs& cw, XRegs& xnext, XRegs& xfree) {
+        if (c + 2 < nchunks)
+            load_x(c + 2, xfree);
+        uint32_t p[KH][FN][16];
 #pragma unroll
-        for (int f = 0; f < FN; f++)
-            cur[f] = cw[f];
-        issue(min(c + 1, nchunks - 1));
-        uint32_t p[FN][16];
+        for (int j = 0; j < KH; j++)
 #pragma unroll
-        for (int f = 0; f < FN; f++)
-            decode_group(cur[f].x, cur[f].y, cur[f].z, mg, zs[f], p[f]);
-        const char* const buf = lds + (c & 1) * BM * kRowBytes + arow;
+            for (int f = 0; f < FN; f++)
+                decode_group(cw[f][j].x, cw[f][j].y, cw[f][j].z, mg, zs[f], p[j][f]);
+        if (c + 2 < nchunks)
+            load_q(c + 2, cw);
+        const char* const buf = lds + (c & 1) * BM * RB + arow;
 #pragma unroll
-        for (int st = 0; st < 4; st++) {
-            half8_t av[FM];
+        for (int j = 0; j < KH; j++)
 #pragma unroll
-            for (int i = 0; i < FM; i++)
-                av[i] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(buf + i * 32 * kRowBytes + st * 16));
-#pragma unroll
-            for (int f = 0; f < FN; f++) {
-                const half8_t bv = as_h8(p[f][4 * st], p[f][4 * st + 1], p[f][4 * st + 2], p[f][4 * st + 3]);
+            for (int st = 0; st < 4; st++) {
+                half8_t av[FM];
 #pragma unroll
                 for (int i = 0; i < FM; i++)
-                    acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv, acc[i][f], 0, 0, 0);
+                    av[i] = __builtin_bit_cast(
+                        half8_t, *reinterpret_cast<const uint4*>(buf + i * 32 * RB + 2 * j * 64 + st * 16));
+#pragma unroll
+                for (int f = 0; f < FN; f++) {
+                    const half8_t bv =
+                        as_h8(p[j][f][4 * st], p[j][f][4 * st + 1], p[j][f][4 * st + 2], p[j][f][4 * st + 3]);
+#pragma unroll
+                    for (int i = 0; i < FM; i++)
+                        acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv, acc[i][f], 0, 0, 0);
+                }
             }
-        }
         if (c + 1 < nchunks)
-            stage(c + 1);
+            stage(c + 1, xnext);
         __syncthreads();
+    };
+
+    XRegs xa, xb;
+    QRegs qa, qb;
+    load_x(0, xa);
+    load_q(0, qa);
+    if (nchunks > 1) {
+        load_x(1, xb);
+        load_q(1, qb);
+    }
+    stage(0, xa);
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += 2) {
+        step(c, qa, xb, xa);
+        if (c + 1 < nchunks)
+            step(c + 1, qb, xa, xb);
     }
 
     // row step, then the weak columns
@@ -276,19 +311,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs a)
         }
 }
 
-template <int FM, int FN, int WM, int WN>
+template <int FM, int FN, int WM, int WN, int KH, int WPE>
 hipError_t launch_tile(GemmArgs a, hipStream_t s)
 {
-    using T = Tile<FM, FN, WM, WN>;
+    using T = Tile<FM, FN, WM, WN, KH, WPE>;
     a.mblocks = (a.M + T::BM - 1) / T::BM;
     const int64_t nblocks = (int64_t)a.mblocks * ((a.N + T::BN - 1) / T::BN);
     if (nblocks > INT32_MAX)
         return hipErrorInvalidValue;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_gemm<FM, FN, WM, WN>), hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<FM, FN, WM, WN, KH, WPE>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
     if (attr != hipSuccess)
         return attr;
-    hipLaunchKernelGGL((k_gemm<FM, FN, WM, WN>), dim3((unsigned)nblocks), dim3(T::NT), T::LDS, s, a);
+    hipLaunchKernelGGL((k_gemm<FM, FN, WM, WN, KH, WPE>), dim3((unsigned)nblocks), dim3(T::NT), T::LDS, s, a);
     return hipGetLastError();
 }
 
@@ -327,8 +363,8 @@ hipError_t launch_gemm(const LinearDesc& d, int64_t M, hipStream_t s)
     a.k = d.k;
     a.mblocks = 1;
     if (M >= 128)
-        return launch_tile<4, 2, 2, 2>(a, s);  // 256 tokens x 128 rows
-    return launch_tile<1, 2, 1, 4>(a, s);      // 32 tokens x 256 rows
+        return launch_tile<2, 2, 2, 4, 1, 2>(a, s);  // 128 tokens x 256 rows, 8 waves of 64 x 64
+    return launch_tile<1, 2, 1, 4, 1, 2>(a, s);      // 32 tokens x 256 rows
 }
 
 }  // namespace owq
