@@ -222,26 +222,32 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
                 store_group(xg[t], smem + xs_index(i / GC, TT, i % GC));
         }
         __syncthreads();
+        // x of a tile is read from LDS once (all four quads in flight together)
+        // and shared by the R rows; lanes past the chunk's groups skip the rows
 #pragma unroll
-        for (int r = 0; r < R; r++) {
-            const ZeroSub nz = make_zero_sub((uint32_t)__builtin_amdgcn_readfirstlane((int)zr[r]));
+        for (int u = 0; u < TT; u++) {
+            const int g = (u << 6) + lane;  // group within the chunk
+            uint4 xq[M][4];
 #pragma unroll
-            for (int u = 0; u < TT; u++) {
-                const int g = (u << 6) + lane;  // group within the chunk
-                if (g < gc) {
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int qd = 0; qd < 4; qd++)
+                    xq[m][qd] = smem[xs_index(m, TT, g) + (qd << 6)];
+            if (g < gc) {
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    const ZeroSub nz = make_zero_sub((uint32_t)__builtin_amdgcn_readfirstlane((int)zr[r]));
                     uint32_t p[16];
                     decode_group(cw[r][u].x, cw[r][u].y, cw[r][u].z, mg, nz, p);
 #pragma unroll
                     for (int m = 0; m < M; m++) {
                         float a = acc[r][m];
-                        const uint4* xq4 = smem + xs_index(m, TT, g);
 #pragma unroll
                         for (int qd = 0; qd < 4; qd++) {
-                            const uint4 xq = xq4[qd << 6];
-                            a = dot2(p[4 * qd + 0], xq.x, a);
-                            a = dot2(p[4 * qd + 1], xq.y, a);
-                            a = dot2(p[4 * qd + 2], xq.z, a);
-                            a = dot2(p[4 * qd + 3], xq.w, a);
+                            a = dot2(p[4 * qd + 0], xq[m][qd].x, a);
+                            a = dot2(p[4 * qd + 1], xq[m][qd].y, a);
+                            a = dot2(p[4 * qd + 2], xq[m][qd].z, a);
+                            a = dot2(p[4 * qd + 3], xq[m][qd].w, a);
                         }
                         acc[r][m] = a;
                     }
