@@ -293,11 +293,7 @@ def main():
                 slot = slots[r % ROTATE]
                 if r >= 2:
                     evp[r - 2][0].record()
-                if M <= 4:
-                    owq.linear_batched(slot, xs, ys)
-                else:
-                    for li in range(L):
-                        owq.linear(slot[li], xs[li], ys[li])
+                owq.linear_batched(slot, xs, ys)
                 if r >= 2:
                     evp[r - 2][1].record()
             torch.cuda.synchronize()
@@ -305,7 +301,7 @@ def main():
             nb = sum(eff_bytes(s.N, s.K, s.k, M) for s in specs)
             sweep[f"M={M}"] = {"us_per_layer": round(t * 1e6, 2), "effective_GBps": round(nb / t / 1e9, 1),
                                "frac_hbm": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
-                               "path": "k_gemv (one launch)" if M <= 4 else "k_gemm (7 launches)"}
+                               "path": "k_gemv, one launch" if M <= 4 else "k_mfv, one launch"}
         result["decode_batch_sweep"] = sweep
 
     if args.copy_reference:

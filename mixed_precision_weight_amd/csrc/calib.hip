@@ -32,8 +32,9 @@ constexpr int kPhases = 32;     // row phases per block (4 waves x 8)
 constexpr int kUnroll = 4;      // rows in flight per lane
 
 struct SqElem {  // x^2 (exact in fp32 for fp16 x)
-    __device__ __forceinline__ void row(int64_t) {}
-    __device__ __forceinline__ float val(uint16_t h) const
+    struct Row {};
+    __device__ __forceinline__ Row load_row(int64_t) const { return Row{}; }
+    __device__ __forceinline__ float val(const Row&, uint16_t h) const
     {
         float v = h2f(h);
         return v * v;
@@ -44,18 +45,25 @@ struct SqElem {  // x^2 (exact in fp32 for fp16 x)
 struct ErrElem {  // dW = w - s (q - z), exact in fp32; squared in fp64 by the caller
     const uint16_t* s16;
     const uint8_t* z;
-    float sf;
-    int zi;
-    __device__ __forceinline__ void row(int64_t r)
+    struct Row {
+        uint32_t s;  // fp16 step bits
+        uint32_t z;
+    };
+    __device__ __forceinline__ Row load_row(int64_t r) const { return Row{s16[r], z[r]}; }
+    __device__ __forceinline__ float val(const Row& rw, uint16_t h) const
     {
-        sf = h2f(s16[r]);
-        zi = z[r];
-    }
-    __device__ __forceinline__ float val(uint16_t h) const
-    {
-        float w = h2f(h);
-        int q = rtn_code(w, sf, zi);
-        return w - sf * (float)(q - zi);
+        // every weight lies inside the row's full-row fit range, so |w / s| <= 8
+        const float sf = h2f((uint16_t)rw.s);
+        const float w = h2f(h);
+        const int zi = (int)rw.z;
+        float e;
+        const float t = round_quotient(w, sf, __builtin_amdgcn_rcpf(sf), e);
+        const int c = (int)t + zi;
+        if (c < 0 || c > 7) {  // clipped at a grid end: residual against the end code, exact
+            const int cq = c < 0 ? 0 : 7;
+            e = __builtin_fmaf(-(float)(cq - zi), sf, w);
+        }
+        return e;
     }
     static constexpr bool kSquared = false;
 };
@@ -71,6 +79,7 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ A, 
     const int phase = wave * 8 + (lane >> 3);
     const int64_t col = (int64_t)blockIdx.x * kTileCols + cc * 8;
     const bool active = col < K;
+    const int64_t colc = active ? col : 0;  // loads stay in bounds; inactive lanes add nothing
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_slice;
     const int64_t r1 = min(R, r0 + rows_per_slice);
 
@@ -79,25 +88,26 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ A, 
     for (int c = 0; c < 8; c++)
         acc[c] = 0.0;
 
+    // every load of an unrolled step is issued before the first use: rows are
+    // clamped to the slice instead of branched around
     for (int64_t rb = r0 + phase; rb < r1; rb += (int64_t)kPhases * kUnroll) {
         uint4 v[kUnroll];
+        typename Elem::Row rw[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            int64_t r = rb + (int64_t)u * kPhases;
-            v[u] = (active && r < r1) ? *reinterpret_cast<const uint4*>(A + r * K + col)
-                                      : make_uint4(0, 0, 0, 0);
+            const int64_t r = min(rb + (int64_t)u * kPhases, r1 - 1);
+            v[u] = *reinterpret_cast<const uint4*>(A + r * K + colc);
+            rw[u] = elem.load_row(r);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            int64_t r = rb + (int64_t)u * kPhases;
-            if (!(active && r < r1))
+            if (!(active && rb + (int64_t)u * kPhases < r1))
                 continue;
-            elem.row(r);
             uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
             for (int c = 0; c < 8; c++) {
                 uint16_t h = (uint16_t)(w[c >> 1] >> (16 * (c & 1)));
-                float e = elem.val(h);
+                float e = elem.val(rw[u], h);
                 if (Elem::kSquared)
                     acc[c] += (double)e;
                 else
@@ -139,15 +149,23 @@ __global__ __launch_bounds__(256) void k_rowfit(const uint16_t* __restrict__ W, 
     if (row >= N)
         return;
     const uint4* p = reinterpret_cast<const uint4*>(W + row * K);
+    const int64_t n16 = K / 8;  // 16-byte words of the row
     float lo = 0.0f, hi = 0.0f;
-    for (int64_t c = lane; c < K / 8; c += 64) {
-        uint4 v = p[c];
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // 8 words per lane in flight; clamped reloads of the last word change no min/max
+    for (int64_t c0 = lane; c0 < n16; c0 += 64 * 8) {
+        uint4 v[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            float f = h2f((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
-            lo = fminf(lo, f);
-            hi = fmaxf(hi, f);
+        for (int u = 0; u < 8; u++)
+            v[u] = p[min(c0 + 64 * u, n16 - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                float f = h2f((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
+                lo = fminf(lo, f);
+                hi = fmaxf(hi, f);
+            }
         }
     }
     lo = wave_min(lo);
@@ -169,10 +187,12 @@ __global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ px,
     if (j >= K)
         return;
     double l = 0.0;
+#pragma unroll 8
     for (int64_t s = 0; s < sx; s++)
         l += px[s * K + j];
     l *= 2.0;
     double e = 0.0;
+#pragma unroll 8
     for (int64_t s = 0; s < sw; s++)
         e += pw[s * K + j];
     lambda[j] = l;
@@ -230,7 +250,7 @@ hipError_t launch_calibrate(const uint16_t* W, int64_t N, int64_t K, const uint1
                        p.rows_x, px, SqElem{});
     hipLaunchKernelGGL(k_rowfit, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, W, N, K, s16, z);
     hipLaunchKernelGGL(k_colsum<ErrElem>, dim3(tiles, (unsigned)p.sw), dim3(256), 0, s, W, N, K,
-                       p.rows_w, pw, ErrElem{s16, z, 1.0f, 0});
+                       p.rows_w, pw, ErrElem{s16, z});
     hipLaunchKernelGGL(k_finalize, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, px, p.sx, pw,
                        p.sw, K, lambda, score);
     return hipGetLastError();

@@ -16,7 +16,8 @@
 // holding GPT 32-column groups in registers, a block min/max, then 32 codes per
 // group packed into three words: code c at bits [3c, 3c+3) of w0|w1<<32|w2<<64.
 //
-// Built with -ffp-contract=off: the quantiser steps are single IEEE operations.
+// Built with -ffp-contract=off: the quantiser steps are single IEEE operations
+// (the code itself comes from rint_div, which reproduces rint(w / s) exactly).
 #include "owq_device.h"
 #include "owq_launch.h"
 
@@ -86,6 +87,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
         int z;
         qparams_from_range(lo, hi, s16, z);
         const float sf = h2f(s16);
+        const float rs = __builtin_amdgcn_rcpf(sf);
 #pragma unroll
         for (int u = 0; u < GPT; u++) {
             int64_t g = tid + 256 * u;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
                 uint32_t o[3] = {0u, 0u, 0u};
 #pragma unroll
                 for (int c = 0; c < 32; c++) {
-                    uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), sf, z);
+                    uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), sf, rs, z);
                     const int pos = 3 * c, wd = pos >> 5, off = pos & 31;
                     o[wd] |= cd << off;
                     if (off > 29)

@@ -6,7 +6,9 @@
 // Large Language Models"). Ties are broken by the lower column index and the
 // result is written in ascending column order.
 //
-// One 1024-thread workgroup (latency-bound, K <= 2^24 doubles read from L2):
+// One 1024-thread workgroup (latency-bound). For K <= 16384 the keys stay in
+// registers (k_topk_reg: early-exit radix select, one ordered prefix sum);
+// larger K reads the scores from L2 on every pass (k_topk, below):
 //  1. radix select of the k-th largest 64-bit order key, 8 bits per pass from the
 //     most significant digit: an LDS histogram of the digit among keys that match
 //     the digits fixed so far, then one wavefront scans the 256 bins;
@@ -134,11 +136,155 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ score,
     }
 }
 
+// Block-wide exclusive prefix sum of one value per thread (thread order); also
+// returns the total. Two barriers.
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wave_tot, uint32_t& total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, 64);
+        if (lane >= o)
+            incl += t;
+    }
+    if (lane == 63)
+        wave_tot[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+    for (int w = 0; w < 16; w++) {
+        const uint32_t t = wave_tot[w];
+        before += w < wave ? t : 0;
+        tot += t;
+    }
+    __syncthreads();
+    total = tot;
+    return before + incl - v;
+}
+
+// K <= 1024 C: thread t holds the keys of columns C t .. C t + C - 1 in registers,
+// so index order is thread order, then register order. The radix select stops as
+// soon as the bucket holding the k-th key is taken whole (with distinct scores
+// that happens after two or three 8-bit passes); the compaction then compares
+// keys on the digits fixed so far. One ordered prefix sum places the selection.
+template <int C>
+__global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ score, int32_t K, int32_t k,
+                                                   int32_t* __restrict__ out)
+{
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t wave_tot[16];
+    __shared__ unsigned long long sh_prefix;
+    __shared__ int sh_kk, sh_done;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    uint64_t key[C];
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        const int j = C * tid + c;  // columns past K get key 0, below every finite score
+        const double v = score[min(j, K - 1)];
+        key[c] = j < K ? score_key(v) : 0ull;
+    }
+
+    uint64_t prefix = 0, mask = 0;
+    int kk = k;  // how many still to take among keys matching `prefix` on `mask`
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        if (tid < 256)
+            hist[tid] = 0;
+        __syncthreads();
+        // keys of a wave that share a digit are counted with one ballot and one
+        // atomic: the leading digits of the scores are mostly equal, and per-key
+        // atomics on one LDS bin would serialise
+#pragma unroll
+        for (int c = 0; c < C; c++) {
+            const uint32_t d = (uint32_t)(key[c] >> shift) & 255u;
+            uint64_t act = __ballot((key[c] & mask) == prefix);
+            while (act) {  // wave-uniform
+                const int leader = __builtin_ctzll(act);
+                const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+                const uint64_t same = act & __ballot(d == dl);
+                if (lane == leader)
+                    atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+                act &= ~same;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l covers digits 255-4l .. 252-4l, i.e. descending order
+            uint32_t c4[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                c4[i] = hist[255 - 4 * lane - i];
+            const uint32_t tot = c4[0] + c4[1] + c4[2] + c4[3];
+            uint32_t incl = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t t = __shfl_up(incl, o, 64);
+                if (lane >= o)
+                    incl += t;
+            }
+            const uint32_t excl = incl - tot;
+            if (excl < (uint32_t)kk && incl >= (uint32_t)kk) {
+                uint32_t run = excl;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    if (run + c4[i] >= (uint32_t)kk) {
+                        const int d = 255 - 4 * lane - i;
+                        sh_prefix = prefix | ((uint64_t)d << shift);
+                        sh_kk = kk - (int)run;
+                        sh_done = run + c4[i] == (uint32_t)kk;  // the whole bucket is taken
+                        break;
+                    }
+                    run += c4[i];
+                }
+            }
+        }
+        __syncthreads();
+        prefix = sh_prefix;
+        kk = sh_kk;
+        mask |= 0xffull << shift;
+        if (sh_done)
+            break;
+    }
+
+    // ordered selection: above the threshold on the fixed digits, or equal to it
+    // and among the first kk such keys in index order
+    uint32_t n_eq = 0;
+#pragma unroll
+    for (int c = 0; c < C; c++)
+        n_eq += (key[c] & mask) == prefix;
+    uint32_t eq_total;
+    uint32_t eq_rank = block_excl_sum(n_eq, wave_tot, eq_total);
+    bool sel[C];
+    uint32_t n_sel = 0;
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        const uint64_t m = key[c] & mask;
+        const bool eq = m == prefix;
+        sel[c] = m > prefix || (eq && eq_rank < (uint32_t)kk);
+        eq_rank += eq;
+        n_sel += sel[c];
+    }
+    uint32_t sel_total;
+    uint32_t pos = block_excl_sum(n_sel, wave_tot, sel_total);
+#pragma unroll
+    for (int c = 0; c < C; c++)
+        if (sel[c]) {
+            if (pos < (uint32_t)k)
+                out[pos] = C * tid + c;
+            pos++;
+        }
+}
+
 }  // namespace
 
 hipError_t launch_select(const double* score, int64_t K, int32_t k, int32_t* idx, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_topk, dim3(1), dim3(1024), 0, s, score, K, k, idx);
+    if (K <= 4 * 1024)
+        hipLaunchKernelGGL(k_topk_reg<4>, dim3(1), dim3(1024), 0, s, score, (int32_t)K, k, idx);
+    else if (K <= 16 * 1024)
+        hipLaunchKernelGGL(k_topk_reg<16>, dim3(1), dim3(1024), 0, s, score, (int32_t)K, k, idx);
+    else
+        hipLaunchKernelGGL(k_topk, dim3(1), dim3(1024), 0, s, score, K, k, idx);
     return hipGetLastError();
 }
 

@@ -179,3 +179,28 @@ def test_workspace_reuse_and_stream(owq):
         got = owq.calibrate(Wd, Xd, workspace=ws, stream=s)
     s.synchronize()
     assert host(got[1]).tobytes() == host(ref[1]).tobytes()
+
+
+def test_pack_and_score_exact_ties(owq):
+    """Rows built from multiples of a quarter of the step put w / s exactly on
+    half-integers in many places: codes must round those ties to even, exactly as
+    rint of the IEEE quotient does in the oracle (pack bit-exact, scores 1e-12)."""
+    import oracle
+    rng = np.random.default_rng(77)
+    N, K, k = 96, 256, 5
+    W = np.zeros((N, K), np.float16)
+    for i in range(N):
+        step = np.float16(2.0 ** rng.integers(-6, 1))   # exact fp16 step s = (hi - lo) / 7
+        zq = int(rng.integers(0, 8))                      # lo = -zq s, hi = (7 - zq) s
+        quarters = rng.integers(-4 * zq, 4 * (7 - zq) + 1, K)
+        W[i] = (quarters.astype(np.float32) * np.float32(step) / 4).astype(np.float16)
+        W[i, 0] = np.float16(-zq * float(step))           # pin the range ends
+        W[i, 1] = np.float16((7 - zq) * float(step))
+    X = synth.calibration(synth.LayerSpec("ties", N, K, k, 0.02, 2, 20.0), 5, 16)
+    Wd = dev(W)
+    lam, score = owq.calibrate(Wd, dev(X))
+    _, o_score = oracle.calibrate_score(W, X)
+    np.testing.assert_allclose(host(score), o_score, rtol=1e-12, atol=1e-300)
+    o_idx = oracle.select_weak(o_score, k)
+    packed = owq.pack(Wd, dev(o_idx.astype(np.int32)))
+    check_pack(packed, oracle.pack(W, o_idx))
