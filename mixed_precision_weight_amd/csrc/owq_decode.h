@@ -116,14 +116,18 @@ __device__ __forceinline__ void decode_group(uint32_t w0, uint32_t w1, uint32_t 
 
 // The 32 fp16 values of one x group (16 dwords, natural order) rearranged into
 // decode-pair order: dword p of the result = (x[kPairLo[p]], x[kPairHi[p]]).
+// The two halves of a pair always come from different source dwords, so each
+// output dword is one v_perm_b32 (byte select from two registers).
 __device__ __forceinline__ void pair_order(const uint32_t (&w)[16], uint32_t (&pr)[16])
 {
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         const int lo = kPairLo[i], hi = kPairHi[i];
-        const uint32_t hl = (w[lo >> 1] >> (16 * (lo & 1))) & 0xffffu;
-        const uint32_t hh = (w[hi >> 1] >> (16 * (hi & 1))) & 0xffffu;
-        pr[i] = hl | (hh << 16);
+        // v_perm_b32 d, s0, s1, sel: selector byte values 0-3 pick bytes of s1,
+        // 4-7 bytes of s0; low half from w[lo / 2] (s1), high half from w[hi / 2] (s0)
+        const uint32_t sel = (uint32_t)(2 * (lo & 1)) | (uint32_t)(2 * (lo & 1) + 1) << 8 |
+                             (uint32_t)(4 + 2 * (hi & 1)) << 16 | (uint32_t)(5 + 2 * (hi & 1)) << 24;
+        pr[i] = __builtin_amdgcn_perm(w[hi >> 1], w[lo >> 1], sel);
     }
 }
 
