@@ -25,7 +25,12 @@
  *       exists yet); the pack fits each row on its dense (non-weak) columns only;
  *   R6  score ties are broken by the lower column index; the weak indices and the
  *       weak columns are stored in ascending column order;
- *   R7  bit order: code c of a 32-column group at bits [3c, 3c+3) of w0|w1<<32|w2<<64.
+ *   R7  bit layout: a 32-column group is one 96-bit word w0|w1<<32|w2<<64 of 32
+ *       three-bit slots, slot s at bits [3s, 3s+3); column c of the group is
+ *       stored in slot kSlot[c]: columns 2p and 2p+1 take the p-th slot pair
+ *       (1,6) (2,7) (3,8) (4,9) (5,10) (11,16) (12,17) (13,18) (14,19) (15,20)
+ *       (21,26) (22,27) (23,28) (24,29) (25,30) (0,31). The pages fix only that
+ *       32 codes fill 3 uint32 along K.
  */
 #include "owq_oracle.h"
 
@@ -226,11 +231,16 @@ void owq_oracle_select_weak(const double* score, int64_t K, int32_t k, int32_t* 
 
 /* ------------------------------------------------------------------ pack ---- */
 
-/* Write code c (3 bits) of one 32-column group into its three words (R7). */
+/* Slot of column c within its 32-column group (R7). */
+static const int kSlot[32] = {1,  6,  2,  7,  3,  8,  4,  9,  5,  10, 11, 16, 12, 17, 13, 18,
+                              14, 19, 15, 20, 21, 26, 22, 27, 23, 28, 24, 29, 25, 30, 0,  31};
+
+/* Write the code of column c (3 bits) of one 32-column group into its three
+ * words (R7). */
 static void put_code(uint32_t* grp, int c, int code)
 {
     for (int b = 0; b < 3; b++) {
-        int pos = 3 * c + b;
+        int pos = 3 * kSlot[c] + b;
         if ((code >> b) & 1)
             grp[pos / 32] |= (uint32_t)1 << (pos % 32);
     }
@@ -240,7 +250,7 @@ static int get_code(const uint32_t* grp, int c)
 {
     int v = 0;
     for (int b = 0; b < 3; b++) {
-        int pos = 3 * c + b;
+        int pos = 3 * kSlot[c] + b;
         v |= (int)((grp[pos / 32] >> (pos % 32)) & 1u) << b;
     }
     return v;

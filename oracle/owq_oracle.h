@@ -13,8 +13,11 @@
  * Data conventions: fp16 values are IEEE binary16 bit patterns (uint16_t).
  * W is [N][K] row-major (row i = output channel, column j = input channel).
  * X is [T][K] calibration activations, x is [M][K] layer input, y is [M][N].
- * Packed codes: uint32 [N][K/32][3]; code c of a 32-column group occupies bits
- * [3c, 3c+3) of the 96-bit little-endian integer w0 | w1<<32 | w2<<64.
+ * Packed codes: uint32 [N][K/32][3]; a 32-column group is the 96-bit little-endian
+ * integer w0 | w1<<32 | w2<<64 of 32 three-bit slots (slot s at bits [3s, 3s+3)),
+ * and columns 2p, 2p+1 of the group occupy the p-th slot pair (1,6) (2,7) (3,8)
+ * (4,9) (5,10) (11,16) (12,17) (13,18) (14,19) (15,20) (21,26) (22,27) (23,28)
+ * (24,29) (25,30) (0,31).
  */
 #ifndef OWQ_ORACLE_H
 #define OWQ_ORACLE_H

@@ -13,6 +13,17 @@ import pytest
 from mixed_precision_weight_amd import synth
 
 
+def _slots():
+    """Slot of each column of a group, from the layout's definition: columns 2p and
+    2p + 1 take the p-th slot pair, slots (j, j + 5) for j = 1..5, 11..15, 21..25,
+    then (0, 31)."""
+    pairs = [(j, j + 5) for j in (1, 2, 3, 4, 5, 11, 12, 13, 14, 15, 21, 22, 23, 24, 25)] + [(0, 31)]
+    return [pairs[c // 2][c % 2] for c in range(32)]
+
+
+SLOT = _slots()
+
+
 def _pack_python(codes: np.ndarray) -> np.ndarray:
     N, K = codes.shape
     out = np.zeros((N, K // 32, 3), np.uint32)
@@ -20,10 +31,18 @@ def _pack_python(codes: np.ndarray) -> np.ndarray:
         for g in range(K // 32):
             B = 0
             for c in range(32):
-                B |= int(codes[i, 32 * g + c]) << (3 * c)
+                B |= int(codes[i, 32 * g + c]) << (3 * SLOT[c])
             for r in range(3):
                 out[i, g, r] = (B >> (32 * r)) & 0xFFFFFFFF
     return out
+
+
+def test_slot_layout_is_a_permutation():
+    assert sorted(SLOT) == list(range(32))
+    # each column pair shares one 32-bit window of the group, 15 bits apart
+    for p in range(15):
+        lo, hi = SLOT[2 * p], SLOT[2 * p + 1]
+        assert 3 * hi - 3 * lo == 15
 
 
 def test_pack_bytes_independent_packer(orc):
@@ -36,14 +55,17 @@ def test_pack_bytes_independent_packer(orc):
     # random code patterns round-trip through the independent packer + oracle unpack
     rc = rng.integers(0, 8, (5, 96)).astype(np.uint8)
     assert np.array_equal(orc.unpack_codes(_pack_python(rc), 96), rc)
-    # single-code patterns land where the bit order says (codes 10 and 21 straddle words)
-    for c, val in [(0, 7), (10, 5), (21, 6), (31, 7)]:
+    # single-code patterns land where the layout says (slots 10 and 21 straddle words)
+    for c, val in [(0, 7), (9, 5), (20, 6), (30, 7), (31, 3)]:
         one = np.zeros((1, 32), np.uint8)
         one[0, c] = val
         q = _pack_python(one)[0, 0]
         B = int(q[0]) | (int(q[1]) << 32) | (int(q[2]) << 64)
-        assert B == val << (3 * c)
+        assert B == val << (3 * SLOT[c])
         assert np.array_equal(orc.unpack_codes(q.reshape(1, 1, 3), 32), one)
+    # the oracle's own bytes for one row with all 32 codes distinct mod 8, column by column
+    codes = (np.arange(32) % 8).astype(np.uint8).reshape(1, 32)
+    assert np.array_equal(orc.unpack_codes(_pack_python(codes), 32), codes)
 
 
 def test_weak_columns_zero_filled_and_copied(orc):
