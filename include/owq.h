@@ -22,9 +22,14 @@
  *       W  [N][K]  weights, row i = output channel, column j = input channel
  *       X  [T][K]  calibration activations        x [M][K] layer input
  *       y  [M][N]  layer output
- *   - Packed codes: uint32 [N][K/32][3]. Code c (0..31) of the 32-column group g of
- *     row i occupies bits [3c, 3c+3) of the 96-bit little-endian integer
- *     qcodes[i][g][0] | qcodes[i][g][1] << 32 | qcodes[i][g][2] << 64.
+ *   - Packed codes: uint32 [N][K/32][3]. The 32-column group g of row i is the
+ *     96-bit little-endian integer qcodes[i][g][0] | qcodes[i][g][1] << 32 |
+ *     qcodes[i][g][2] << 64 of 32 three-bit slots, slot s at bits [3s, 3s+3).
+ *     Columns 32g + 2p and 32g + 2p + 1 occupy the p-th slot pair: (1,6) (2,7)
+ *     (3,8) (4,9) (5,10) (11,16) (12,17) (13,18) (14,19) (15,20) (21,26) (22,27)
+ *     (23,28) (24,29) (25,30) (0,31) for p = 0..15. (Only "32 codes per 3 uint32
+ *     along K" is fixed by the method; this order lets one 32-bit window of the
+ *     group hold both codes of a column pair.)
  *   - The quantiser: per output row, lo = min(0, min w), hi = max(0, max w) over the
  *     fitted columns; step s = fp16_rne((hi - lo) / 7) (IEEE fp32 division), zero
  *     point z = clamp(rint(-lo / s), 0, 7); code(w) = clamp(rint(w / s) + z, 0, 7),

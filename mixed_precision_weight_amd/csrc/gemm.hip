@@ -22,15 +22,13 @@
 // order of a contraction is free, so lane l of a wave decodes group (chunk, h) of
 // row l % 32 of each of its row blocks (owq_decode.h) straight into B operand
 // registers: the 32 exact (q - z) values of the group feed the chunk's four
-// 16-deep MFMA steps, four decode pairs (8 values) per step.
-// x is staged through LDS in the same decode-pair order: a thread loads the 64
-// bytes of one group of one token, rearranges them in registers and writes them
-// with 128-bit stores; an A operand is then one 128-bit LDS read per lane (rows
-// padded by 16 bytes so the reads of a wave spread over all banks). LDS is
-// double buffered and loads run two chunks ahead: while chunk c computes, x and
-// codes of chunk c + 2 are loaded (x into the register set staged last, codes
-// into the set just decoded) and x of chunk c + 1 is written to LDS; one barrier
-// per chunk.
+// 16-deep MFMA steps, four decode pairs (8 consecutive columns) per step.
+// x is staged through LDS as stored (decode pair p is columns 2p, 2p + 1): a
+// thread loads the 64 bytes of one group of one token and writes them with
+// 128-bit stores; an A operand is then one 128-bit LDS read per lane (rows padded
+// by 16 bytes so the reads of a wave spread over all banks). LDS is double
+// buffered; x of chunk c + 2 and codes of chunk c + 2 are loaded while chunk c
+// computes, x of chunk c + 1 is written to LDS, and one barrier closes a chunk.
 //
 // Epilogue: the accumulators (sums of exact fp16 products of integer weights and
 // x) are scaled by the row step, the weak columns run as extra 16-deep MFMA
@@ -82,7 +80,7 @@ struct Tile {
     static constexpr int KG = 2 * KH;                   // groups per chunk
     static constexpr int RB = KG * 64 + 16;             // LDS bytes per staged token (padded)
     static constexpr int XI = (KG * BM + NT - 1) / NT;  // staged group rows per thread
-    static constexpr int LDS = 2 * BM * RB;             // double buffer
+    static constexpr int LDS = 2 * BM * RB + KG * 64;   // double buffer + a spare staging row
 };
 
 template <int FM, int FN, int WM, int WN, int KH, int WPE>
@@ -119,16 +117,14 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
         const int i = tid + NT * t;
         xoff[t] = min(i / KG, mv - 1) * K * 2;
     }
-    int qoff[FN];
-    float sc[FN];
-    ZeroSub zs[FN];
+    // this lane's rows (one per row block f), clamped to the valid rows; their
+    // zero points packed one per byte
+    const int rbase = wn * 32 * FN + l32;
+    auto row_of = [&](int f) { return min(rbase + 32 * f, nv - 1); };
+    uint32_t zpk = 0;
 #pragma unroll
-    for (int f = 0; f < FN; f++) {
-        const int r = min(wn * 32 * FN + 32 * f + l32, nv - 1);
-        qoff[f] = r * G * 12;
-        sc[f] = h2f(a.s[n0 + r]);
-        zs[f] = make_zero_sub((uint32_t)a.z[n0 + r]);
-    }
+    for (int f = 0; f < FN; f++)
+        zpk |= (uint32_t)a.z[n0 + row_of(f)] << (8 * f);
 
     // Two chunks in flight: x and codes of chunk c + 2 are loaded while chunk c
     // computes (x into the register set just staged, codes into the set just
@@ -150,26 +146,28 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
             const int g = min(KG * c + 2 * j + h, G - 1);
 #pragma unroll
             for (int f = 0; f < FN; f++)
-                cw[f][j] = __builtin_amdgcn_raw_buffer_load_b96(qr, qoff[f] + g * 12, 0, 0);
+                cw[f][j] = __builtin_amdgcn_raw_buffer_load_b96(qr, (row_of(f) * G + g) * 12, 0, 0);
         }
     };
-    // x of chunk c into LDS buffer c & 1, in decode-pair order; a group past the
+    // x of chunk c into LDS buffer c & 1, in natural column order; a group past the
     // end of K is staged as zeros
     auto stage = [&](int c, const XRegs& xg) {
         char* const buf = lds + (c & 1) * BM * RB;
 #pragma unroll
         for (int t = 0; t < XI; t++) {
             const int i = tid + NT * t;
-            if (KG * BM % NT == 0 || i < KG * BM) {
-                const bool live = KG * c + i % KG < G;
-                uint32_t w[16], pr[16];
+            {
+                // threads past the tile's staging items write a spare row instead of branching
+                const bool spare = !(KG * BM % NT == 0 || i < KG * BM);
+                const bool live = !spare && KG * c + i % KG < G;
+                uint32_t pr[16];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++)
 #pragma unroll
                     for (int e = 0; e < 4; e++)
-                        w[4 * q4 + e] = live ? (uint32_t)xg[t][q4][e] : 0u;
-                pair_order(w, pr);
-                uint4* dst = reinterpret_cast<uint4*>(buf + (i / KG) * RB + (i % KG) * 64);
+                        pr[4 * q4 + e] = live ? (uint32_t)xg[t][q4][e] : 0u;
+                uint4* dst = reinterpret_cast<uint4*>(spare ? lds + 2 * BM * RB + (i % KG) * 64
+                                                            : buf + (i / KG) * RB + (i % KG) * 64);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++)
                     dst[q4] = make_uint4(pr[4 * q4], pr[4 * q4 + 1], pr[4 * q4 + 2], pr[4 * q4 + 3]);
@@ -188,40 +186,40 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
                 acc[i][f][r] = 0.0f;
 
     const int arow = (wm * 32 * FM + l32) * RB + h * 64;  // this lane's A operand row
-    // chunk c: decode its codes (then reload that register set with chunk c + 2),
-    // MFMA against x staged in LDS, stage chunk c + 1, barrier
-    auto step = [&](int c, QRegs& cw, XRegs& xnext, XRegs& xfree) {
-        if (c + 2 < nchunks)
-            load_x(c + 2, xfree);
-        uint32_t p[KH][FN][16];
-#pragma unroll
-        for (int j = 0; j < KH; j++)
-#pragma unroll
-            for (int f = 0; f < FN; f++)
-                decode_group(cw[f][j].x, cw[f][j].y, cw[f][j].z, mg, zs[f], p[j][f]);
-        if (c + 2 < nchunks)
-            load_q(c + 2, cw);
+    // Chunk c: x of chunk c + 2 is loaded while the chunk's A operands are read
+    // from LDS once and each row block's codes are decoded just before their
+    // MFMAs (one 16-register B set live at a time); then the codes of chunk c + 2
+    // are loaded into the set just used, x of c + 1 (loaded one step earlier) is
+    // staged into the other LDS buffer, and one barrier closes the chunk. All loads are unconditional with
+    // clamped addresses, and both steps of a pair always run: a branch would make
+    // the compiler wait for every outstanding load at the merge.
+    auto step = [&](int c, QRegs& qcur, XRegs& xload, XRegs& xstage) {
+        load_x(min(c + 2, nchunks - 1), xload);
         const char* const buf = lds + (c & 1) * BM * RB + arow;
 #pragma unroll
-        for (int j = 0; j < KH; j++)
+        for (int j = 0; j < KH; j++) {
+            half8_t av[4][FM];
 #pragma unroll
-            for (int st = 0; st < 4; st++) {
-                half8_t av[FM];
+            for (int st = 0; st < 4; st++)
 #pragma unroll
                 for (int i = 0; i < FM; i++)
-                    av[i] = __builtin_bit_cast(
+                    av[st][i] = __builtin_bit_cast(
                         half8_t, *reinterpret_cast<const uint4*>(buf + i * 32 * RB + 2 * j * 64 + st * 16));
 #pragma unroll
-                for (int f = 0; f < FN; f++) {
-                    const half8_t bv =
-                        as_h8(p[j][f][4 * st], p[j][f][4 * st + 1], p[j][f][4 * st + 2], p[j][f][4 * st + 3]);
+            for (int f = 0; f < FN; f++) {
+                uint32_t p[16];
+                decode_group(qcur[f][j].x, qcur[f][j].y, qcur[f][j].z, mg, make_zero_sub((zpk >> (8 * f)) & 7u), p);
+#pragma unroll
+                for (int st = 0; st < 4; st++) {
+                    const half8_t bv = as_h8(p[4 * st], p[4 * st + 1], p[4 * st + 2], p[4 * st + 3]);
 #pragma unroll
                     for (int i = 0; i < FM; i++)
-                        acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv, acc[i][f], 0, 0, 0);
+                        acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[st][i], bv, acc[i][f], 0, 0, 0);
                 }
             }
-        if (c + 1 < nchunks)
-            stage(c + 1, xnext);
+        }
+        load_q(min(c + 2, nchunks - 1), qcur);
+        stage(c + 1, xstage);  // zeros past the end of K
         __syncthreads();
     };
 
@@ -229,26 +227,27 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WP
     QRegs qa, qb;
     load_x(0, xa);
     load_q(0, qa);
-    if (nchunks > 1) {
-        load_x(1, xb);
-        load_q(1, qb);
-    }
+    load_q(min(1, nchunks - 1), qb);
     stage(0, xa);
+    load_x(min(1, nchunks - 1), xb);
     __syncthreads();
+    // x of chunk c + 1 sits in xb (c even) or xa (c odd), loaded a full step earlier;
+    // an odd chunk count runs one extra step on zero-staged x, which adds nothing
     for (int c = 0; c < nchunks; c += 2) {
-        step(c, qa, xb, xa);
-        if (c + 1 < nchunks)
-            step(c + 1, qb, xa, xb);
+        step(c, qa, xa, xb);
+        step(c + 1, qb, xb, xa);
     }
 
     // row step, then the weak columns
 #pragma unroll
-    for (int i = 0; i < FM; i++)
+    for (int f = 0; f < FN; f++) {
+        const float sc = h2f(a.s[n0 + row_of(f)]);
 #pragma unroll
-        for (int f = 0; f < FN; f++)
+        for (int i = 0; i < FM; i++)
 #pragma unroll
             for (int r = 0; r < 16; r++)
-                acc[i][f][r] *= sc[f];
+                acc[i][f][r] *= sc;
+    }
     if (k > 0) {
         int xrow[FM];
 #pragma unroll
@@ -363,7 +362,7 @@ hipError_t launch_gemm(const LinearDesc& d, int64_t M, hipStream_t s)
     a.k = d.k;
     a.mblocks = 1;
     if (M >= 128)
-        return launch_tile<2, 2, 2, 4, 1, 2>(a, s);  // 128 tokens x 256 rows, 8 waves of 64 x 64
+        return launch_tile<2, 4, 2, 2, 1, 2>(a, s);  // 128 tokens x 256 rows, 4 waves of 64 x 128
     return launch_tile<1, 2, 1, 4, 1, 2>(a, s);      // 32 tokens x 256 rows
 }
 

@@ -12,7 +12,7 @@
 // (R rows per wavefront); the 64 lanes of a wave split a row's K/32 groups, lane
 // l taking groups l, l + 64, ... (a "tile" is one 12-byte group per lane: 768
 // contiguous bytes of one row). K is walked in chunks of two tiles (4096
-// columns): for each chunk the block stages x in LDS in decode-pair order, every
+// columns): for each chunk the block stages x in LDS in natural column order, every
 // wave holds its R rows' code tiles in registers, and all global loads of the
 // chunk are issued before the first wait (unconditionally, with clamped
 // indices: a load under a divergent branch would make the compiler wait for it
@@ -22,8 +22,8 @@
 // 64-lane reduction of four rows at once (lane-half swaps, then DPP).
 //
 // Each 12-byte group is decoded in registers (owq_decode.h) to sixteen exact
-// (q_a - z, q_b - z) fp16 pairs, and one v_dot2_f32_f16 per pair multiplies it
-// with the matching x pair, staged in the same pair order. Every product is
+// (q_a - z, q_b - z) fp16 pairs of consecutive columns, and one v_dot2_f32_f16
+// per pair multiplies it with the matching x dword, staged as stored. Every product is
 // exact, so the fp32 sum's error is bounded relative to sum_j |(q_j - z) x_j|,
 // for every row, including rows whose codes all equal the zero point. Per tile:
 // 5 window ops, 17 and-or, 16 packed subtracts, 16 dot2 per token.
@@ -61,19 +61,9 @@ __device__ __forceinline__ int xs_index(int m, int T, int g) { return ((m * T + 
 
 __device__ __forceinline__ void store_group(const uint4 (&v)[4], uint4* __restrict__ xs_mg)
 {
-    uint32_t w[16];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        w[4 * i + 0] = v[i].x;
-        w[4 * i + 1] = v[i].y;
-        w[4 * i + 2] = v[i].z;
-        w[4 * i + 3] = v[i].w;
-    }
-    uint32_t pr[16];
-    pair_order(w, pr);
 #pragma unroll
     for (int qd = 0; qd < 4; qd++)
-        xs_mg[qd * 64] = make_uint4(pr[4 * qd], pr[4 * qd + 1], pr[4 * qd + 2], pr[4 * qd + 3]);
+        xs_mg[qd * 64] = v[qd];
 }
 
 // ------------------------------------------------------------------ kernel --
@@ -108,7 +98,7 @@ __device__ __forceinline__ void reduce4(float (&a)[4])
 __device__ __forceinline__ int reduced_index(int q) { return (q & 1) + ((q >> 1) << 1); }
 
 // One wavefront computes R consecutive rows of one layer; a block is 4 waves
-// (4 R rows) sharing x, staged in LDS in decode-pair order one K chunk
+// (4 R rows) sharing x, staged in LDS in natural column order one K chunk
 // (kChunkTiles tiles, 4096 columns) at a time. For each chunk every global load
 // of the block (x of the chunk, the R rows' codes of the chunk, and with the
 // first chunk the rows' scale, zero point, weak weights and the weak indices)

@@ -20,10 +20,10 @@
 // the groups 4 u + l / 16 (u < U) of each K chunk of 4 U groups, so each load
 // instruction of the wave reads 48 contiguous bytes from each of its 16 rows;
 // the 16 decode pairs of a group feed four MFMA steps (pairs 4t .. 4t + 3 in
-// step t). The contraction order is free, so x only has to be staged in the
-// same decode-pair order: the block's x chunk sits in LDS as [token][group][32
-// values in pair order] and an A operand is one 128-bit LDS read per lane. The
-// K reduction happens inside the accumulators: no cross-lane reduction.
+// step t). Decode pair p is columns (2p, 2p + 1) (the slot layout of the codes),
+// so x is staged as it is stored: the block's x chunk sits in LDS as
+// [token][group][32 values] and an A operand is one 128-bit LDS read per lane.
+// The K reduction happens inside the accumulators: no cross-lane reduction.
 //
 // Pipeline: LDS double buffer for x, the next chunk's codes and x in registers
 // while the current chunk computes, one barrier per chunk. A block is 4 waves
@@ -132,13 +132,12 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
             const int i = tid + 256 * t;
             if (i < M * GC) {
                 const bool live = c * GC + i % GC < G;
-                uint32_t w[16], pr[16];
+                uint32_t pr[16];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++)
 #pragma unroll
                     for (int e = 0; e < 4; e++)
-                        w[4 * q4 + e] = live ? (uint32_t)xg[t][q4][e] : 0u;
-                pair_order(w, pr);
+                        pr[4 * q4 + e] = live ? (uint32_t)xg[t][q4][e] : 0u;
                 uint4* dst = reinterpret_cast<uint4*>(buf + (i / GC) * RS + (i % GC) * 64);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; q4++)

@@ -1,17 +1,19 @@
 // owq_decode.h -- register decode of the packed 3-bit groups (gfx950), shared
 // by the vector-ALU and the matrix-core linear kernels.
 //
-// A group holds 32 codes of one row, code c at bits 3c..3c+2 of the 96-bit word
-// w0 | w1 << 32 | w2 << 64. A 3-bit field that sits inside the mantissa of an
-// fp16 half (bits p..p+2 with p <= 7) becomes an exact fp16 number once an
-// exponent is OR-ed above it: exponent 2^(10-p) gives the value 2^(10-p) + q.
-// Six 32-bit windows of the group (w0>>2, bits 11..42, w1, w1>>9, bits 62..93,
-// w2>>7) each hold codes at in-half positions 1/4/7 (low half) and 0/3/6 (high
-// half), so one v_and_or_b32 yields a packed pair (off_lo + q_a, off_hi + q_b);
-// codes 0 and 31 form the sixteenth pair. One v_pk_add_f16 of the row's
-// -(off + z) pair then gives (q_a - z, q_b - z) EXACTLY (small integers).
-// The sixteen pairs come out in the fixed order kPairLo / kPairHi; consumers
-// stage x in the same order (pair_order) so that pair p meets (x[lo], x[hi]).
+// A group holds the 32 codes of one row's 32 columns in the 96-bit word
+// w0 | w1 << 32 | w2 << 64, as 32 three-bit slots (slot s at bits 3s..3s+2);
+// columns 2p and 2p + 1 sit in slots kPairLo[p] and kPairHi[p]. A 3-bit field
+// that sits inside the mantissa of an fp16 half (bits p..p+2 with p <= 7)
+// becomes an exact fp16 number once an exponent is OR-ed above it: exponent
+// 2^(10-p) gives the value 2^(10-p) + q. Six 32-bit windows of the group (w0>>2,
+// bits 11..42, w1, w1>>9, bits 62..93, w2>>7) each hold slots at in-half
+// positions 1/4/7 (low half) and 0/3/6 (high half), so one v_and_or_b32 yields a
+// packed pair (off_lo + q_a, off_hi + q_b); slots 0 and 31 form the sixteenth
+// pair. One v_pk_add_f16 of the row's -(off + z) pair then gives
+// (q_a - z, q_b - z) EXACTLY (small integers). Because of the slot layout, decode
+// pair p is columns (2p, 2p + 1): the sixteen pairs come out in natural column
+// order and meet x as it is stored, one dword per column pair.
 #pragma once
 
 #include "owq_device.h"
@@ -19,7 +21,7 @@
 namespace owq {
 namespace {
 
-// Pair p of a group = (code lo[p], code hi[p]).
+// Decode pair p = the slots (kPairLo[p], kPairHi[p]) = columns (2p, 2p + 1).
 __device__ constexpr int kPairLo[16] = {1, 2, 3, 4, 5, 11, 12, 13, 14, 15, 21, 22, 23, 24, 25, 0};
 __device__ constexpr int kPairHi[16] = {6, 7, 8, 9, 10, 16, 17, 18, 19, 20, 26, 27, 28, 29, 30, 31};
 
@@ -112,23 +114,6 @@ __device__ __forceinline__ void decode_group(uint32_t w0, uint32_t w1, uint32_t 
     p[14] = sub_h2(and_or(b3, kMaskB, mg.b), n.b);
     // (1024 + q0, 1024 + q31): code 0 at bits 0..2 of w0, code 31 at bits 29..31 of w2
     p[15] = sub_h2(and_or(w2 >> 13, 0x00070000u, and_or(w0, 7u, mg.p)), n.p);
-}
-
-// The 32 fp16 values of one x group (16 dwords, natural order) rearranged into
-// decode-pair order: dword p of the result = (x[kPairLo[p]], x[kPairHi[p]]).
-// The two halves of a pair always come from different source dwords, so each
-// output dword is one v_perm_b32 (byte select from two registers).
-__device__ __forceinline__ void pair_order(const uint32_t (&w)[16], uint32_t (&pr)[16])
-{
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const int lo = kPairLo[i], hi = kPairHi[i];
-        // v_perm_b32 d, s0, s1, sel: selector byte values 0-3 pick bytes of s1,
-        // 4-7 bytes of s0; low half from w[lo / 2] (s1), high half from w[hi / 2] (s0)
-        const uint32_t sel = (uint32_t)(2 * (lo & 1)) | (uint32_t)(2 * (lo & 1) + 1) << 8 |
-                             (uint32_t)(4 + 2 * (hi & 1)) << 16 | (uint32_t)(5 + 2 * (hi & 1)) << 24;
-        pr[i] = __builtin_amdgcn_perm(w[hi >> 1], w[lo >> 1], sel);
-    }
 }
 
 }  // namespace

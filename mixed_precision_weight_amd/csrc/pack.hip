@@ -14,7 +14,10 @@
 // (a per-group 32-bit weak mask built once per block in LDS) and runs the plain
 // full-row quantiser: one 256-thread block per row (grid-stride), each thread
 // holding GPT 32-column groups in registers, a block min/max, then 32 codes per
-// group packed into three words: code c at bits [3c, 3c+3) of w0|w1<<32|w2<<64.
+// group packed into three words, the code of column c in slot kSlot[c] (bits
+// [3 kSlot[c], 3 kSlot[c] + 3) of w0|w1<<32|w2<<64): columns 2p and 2p+1 take the
+// p-th slot pair, (j, j+5) for j = 1..5, 11..15, 21..25, then (0, 31), so the
+// decoders get both codes of a column pair from one 32-bit window.
 //
 // Built with -ffp-contract=off: the quantiser steps are single IEEE operations
 // (the code itself comes from rint_div, which reproduces rint(w / s) exactly).
@@ -24,6 +27,10 @@
 namespace owq {
 
 namespace {
+
+// slot of column c within its 32-column group
+constexpr int kSlot[32] = {1,  6,  2,  7,  3,  8,  4,  9,  5,  10, 11, 16, 12, 17, 13, 18,
+                           14, 19, 15, 20, 21, 26, 22, 27, 23, 28, 24, 29, 25, 30, 0,  31};
 
 template <int GPT>
 __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, int64_t N, int64_t K,
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
 #pragma unroll
                 for (int c = 0; c < 32; c++) {
                     uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), sf, rs, z);
-                    const int pos = 3 * c, wd = pos >> 5, off = pos & 31;
+                    const int pos = 3 * kSlot[c], wd = pos >> 5, off = pos & 31;
                     o[wd] |= cd << off;
                     if (off > 29)
                         o[wd + 1] |= cd >> (32 - off);
