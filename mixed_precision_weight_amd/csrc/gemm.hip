@@ -12,10 +12,9 @@
 // Tiling: a block owns a BM x BN tile of y (tokens x output rows) and its waves
 // form a WM x WN grid, each wave owning 32 FM tokens x 32 FN rows, i.e. FM x FN
 // accumulators of v_mfma_f32_32x32x16_f16 (A = x, B = the weights transposed).
-// K is walked in chunks of 64 KH columns (2 KH 32-code groups). The large-M
-// tile is 128 tokens x 256 rows with 8 waves of 64 x 64 and two waves per SIMD:
-// measured on MI355X it beat 256 x 128 and 256 x 256 tiles, mainly because the
-// grid has enough blocks (256 for a 2048 x 4096 output) to fill every CU.
+// K is walked in chunks of 64 columns (two 32-code groups). From 128 tokens on
+// the tile is 128 tokens x 256 rows, 4 waves of 64 x 128 and two blocks per CU
+// (k_gemm_dma); below, 32 tokens x 256 rows, 4 waves of 32 x 64 (k_gemm).
 //
 // The weights never pass through LDS. The MFMA pairs the eight A and B operand
 // elements of lane l with the same eight k values of half h = l / 32, and the
@@ -23,13 +22,13 @@
 // row l % 32 of each of its row blocks (owq_decode.h) straight into B operand
 // registers: the 32 exact (q - z) values of the group feed the chunk's four
 // 16-deep MFMA steps, four decode pairs (8 consecutive columns) per step.
-// x is staged through LDS as stored (decode pair p is columns 2p, 2p + 1): a
-// thread loads the 64 bytes of one group of one token and writes them with
-// 128-bit stores; an A operand is then one 128-bit LDS read per lane (rows padded
-// by 16 bytes so the reads of a wave spread over all banks). LDS is double
-// buffered; x of chunk c + 2 and codes of chunk c + 2 are loaded while chunk c
-// computes, x of chunk c + 1 is written to LDS, and one barrier closes a chunk.
-//
+// x goes through LDS as stored (decode pair p is columns 2p, 2p + 1), so an A
+// operand is one 128-bit LDS read per lane. k_gemm_dma moves it with direct
+// global-to-LDS loads, three chunks deep; k_gemm loads it into registers and
+// writes it to a double buffer with rows padded by 16 bytes. Either way the
+// codes of chunk c + 2 are loaded while chunk c computes, and one barrier
+// closes a chunk.
+
 // Epilogue: the accumulators (sums of exact fp16 products of integer weights and
 // x) are scaled by the row step, the weak columns run as extra 16-deep MFMA
 // steps (fp16 weak weights against x gathered at weak_idx), and the result is
@@ -327,6 +326,235 @@ hipError_t launch_tile(GemmArgs a, hipStream_t s)
     return hipGetLastError();
 }
 
+// Large-M variant: x reaches LDS through gfx950 direct-to-LDS buffer loads (no
+// registers, no staging instructions), three chunks deep. A stage is the 64
+// columns of a chunk for BM tokens, 128 bytes per token; each thread moves DPW
+// 16-byte units per stage, and the unit of (token m, piece c) lands in slot
+// c ^ (m & 7) of the token's 128 bytes, so the A-operand reads of a wave (32
+// tokens, one piece) hit eight different slots of the bank window. The stages are
+// three separate LDS arrays: the compiler then waits only for the loads of the
+// stage it reads. Codes run two chunks ahead in three register sets.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int FM, int FN, int WM, int WN>
+struct DmaTile {
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int BM = 32 * FM * WM;
+    static constexpr int BN = 32 * FN * WN;
+    static constexpr int STAGE = BM * 128;
+    static constexpr int DPW = STAGE / 16 / NT;  // 16-byte units per thread per stage
+    static_assert(STAGE % (16 * NT) == 0, "a stage must split evenly over the threads");
+};
+
+template <int FM, int FN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_dma(GemmArgs a)
+{
+    using T = DmaTile<FM, FN, WM, WN>;
+    constexpr int BM = T::BM, BN = T::BN, STAGE = T::STAGE, DPW = T::DPW;
+    __shared__ __attribute__((aligned(1024))) char xs0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char xs1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char xs2[STAGE];
+
+    const int M = a.M, N = a.N, K = a.K, k = a.k;
+    const int G = K >> 5;
+    const int nchunks = (G + 1) >> 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int m0 = ((int)blockIdx.x % a.mblocks) * BM;
+    const int n0 = ((int)blockIdx.x / a.mblocks) * BN;
+    const int mv = min(BM, M - m0);
+    const int nv = min(BN, N - n0);
+
+    // x rows of the block (reads past them return zeros) and code rows
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.x) + (int64_t)m0 * K, (short)0, mv * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(a.q) + (int64_t)n0 * G * 3, (short)0, nv * G * 12, 0x00020000);
+
+    // this thread's DMA units: unit u -> token u / 8, slot u % 8, piece slot ^ (token & 7)
+    int xsrc[DPW];
+#pragma unroll
+    for (int t = 0; t < DPW; t++) {
+        const int u = (wave * DPW + t) * 64 + lane;
+        const int row = u >> 3, piece = (u & 7) ^ (row & 7);
+        xsrc[t] = min(row, mv - 1) * K * 2 + piece * 16;
+    }
+    // the second group of the last chunk lies past K when G is odd: its x pieces
+    // (4..7) are read out of range, which returns zeros
+    const int last = nchunks - 1;
+    const bool odd_tail = (G & 1) != 0;
+    int xdead[DPW];
+#pragma unroll
+    for (int t = 0; t < DPW; t++) {
+        const int u = (wave * DPW + t) * 64 + lane;
+        xdead[t] = (odd_tail && (((u & 7) ^ ((u >> 3) & 7)) >= 4)) ? 0x40000000 : 0;
+    }
+    auto dma = [&](int c, char* stage) {
+        const int cc = min(c, last);
+#pragma unroll
+        for (int t = 0; t < DPW; t++)
+            dma16(xr, stage + (wave * DPW + t) * 1024, xsrc[t] + cc * 128 + (cc == last ? xdead[t] : 0));
+    };
+
+    const int rbase = wn * 32 * FN + l32;
+    auto row_of = [&](int f) { return min(rbase + 32 * f, nv - 1); };
+    uint32_t zpk = 0;
+#pragma unroll
+    for (int f = 0; f < FN; f++)
+        zpk |= (uint32_t)a.z[n0 + row_of(f)] << (8 * f);
+    typedef u32x3 QRegs[FN];
+    auto load_q = [&](int c, QRegs& cw) {
+        const int g = min(2 * min(c, nchunks - 1) + h, G - 1);
+#pragma unroll
+        for (int f = 0; f < FN; f++)
+            cw[f] = __builtin_amdgcn_raw_buffer_load_b96(qr, (row_of(f) * G + g) * 12, 0, 0);
+    };
+
+    const Magic mg = make_magic();
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int f = 0; f < FN; f++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[i][f][r] = 0.0f;
+
+    // this lane's A operand: token row (wm 32 FM + 32 i + l32) * 128, piece h 4 + st
+    const int arow = (wm * 32 * FM + l32) * 128;
+    int aoff[4];
+#pragma unroll
+    for (int st = 0; st < 4; st++)
+        aoff[st] = ((h * 4 + st) ^ (l32 & 7)) * 16;
+    // Chunk c reads stage cur; loads chunk c + 2 into stage nxt2 and code set q2.
+    auto step = [&](int c, const char* cur, char* nxt2, const QRegs& qc, QRegs& q2) {
+        // this wave's x loads of chunk c are done once at most 2 FN + DPW newer loads
+        // remain (codes of c, x and codes of c + 1); after the barrier every wave's
+        // are, and every wave has finished reading the stage chunk c + 2 goes to. A
+        // plain barrier: a fence here would wait for all x loads in flight.
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * FN + DPW) : "memory");
+        dma(c + 2, nxt2);
+        load_q(c + 2, q2);
+        if (c < nchunks) {  // block-uniform; the steps past the end only keep the pipeline shape
+            half8_t av[4][FM];
+#pragma unroll
+            for (int st = 0; st < 4; st++)
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+                    av[st][i] =
+                        __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(cur + arow + i * 32 * 128 + aoff[st]));
+#pragma unroll
+            for (int f = 0; f < FN; f++) {
+                uint32_t p[16];
+                decode_group(qc[f].x, qc[f].y, qc[f].z, mg, make_zero_sub((zpk >> (8 * f)) & 7u), p);
+#pragma unroll
+                for (int st = 0; st < 4; st++) {
+                    const half8_t bv = as_h8(p[4 * st], p[4 * st + 1], p[4 * st + 2], p[4 * st + 3]);
+#pragma unroll
+                    for (int i = 0; i < FM; i++)
+                        acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[st][i], bv, acc[i][f], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    QRegs qa, qb, qc3;
+    dma(0, xs0);
+    load_q(0, qa);
+    dma(1, xs1);
+    load_q(1, qb);
+    for (int c = 0; c < nchunks; c += 3) {
+        step(c, xs0, xs2, qa, qc3);
+        step(c + 1, xs1, xs0, qb, qa);
+        step(c + 2, xs2, xs1, qc3, qb);
+    }
+
+    // row step, then the weak columns
+#pragma unroll
+    for (int f = 0; f < FN; f++) {
+        const float sc = h2f(a.s[n0 + row_of(f)]);
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[i][f][r] *= sc;
+    }
+    if (k > 0) {
+        int xrow[FM];
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            xrow[i] = min(wm * 32 * FM + 32 * i + l32, mv - 1) * K;
+        for (int cs = 0; cs < k; cs += 16) {
+            uint32_t jw[8];
+            bool on[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const int c = cs + 8 * h + e;
+                on[e] = c < k;
+                int j = a.idx[min(c, k - 1)];
+                jw[e] = (uint32_t)((j >= 0 && j < K) ? j : 0);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; i++) {
+                const uint16_t* xm = a.x + (int64_t)m0 * K + xrow[i];
+                uint32_t aw[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; e2++) {
+                    const uint32_t lo = on[2 * e2] ? xm[jw[2 * e2]] : 0u;
+                    const uint32_t hi = on[2 * e2 + 1] ? xm[jw[2 * e2 + 1]] : 0u;
+                    aw[e2] = lo | (hi << 16);
+                }
+                const half8_t av = as_h8(aw[0], aw[1], aw[2], aw[3]);
+#pragma unroll
+                for (int f = 0; f < FN; f++) {
+                    const uint16_t* wr = a.ww + (int64_t)(n0 + row_of(f)) * k;
+                    uint32_t bw[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; e2++) {
+                        const int c = cs + 8 * h + 2 * e2;
+                        const uint32_t lo = on[2 * e2] ? wr[c] : 0u;
+                        const uint32_t hi = on[2 * e2 + 1] ? wr[c + 1] : 0u;
+                        bw[e2] = lo | (hi << 16);
+                    }
+                    acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, as_h8(bw[0], bw[1], bw[2], bw[3]),
+                                                                       acc[i][f], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // D element r of lane l: token 8 (r / 4) + 4 h + r % 4, row l % 32
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int f = 0; f < FN; f++) {
+            const int n = n0 + wn * 32 * FN + 32 * f + l32;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * 32 * FM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < M && n < N)
+                    a.y[(int64_t)m * N + n] = f2h(acc[i][f][r]);
+            }
+        }
+}
+
+template <int FM, int FN, int WM, int WN>
+hipError_t launch_dma(GemmArgs a, hipStream_t s)
+{
+    using T = DmaTile<FM, FN, WM, WN>;
+    a.mblocks = (a.M + T::BM - 1) / T::BM;
+    const int64_t nblocks = (int64_t)a.mblocks * ((a.N + T::BN - 1) / T::BN);
+    if (nblocks > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm_dma<FM, FN, WM, WN>), dim3((unsigned)nblocks), dim3(T::NT), 0, s, a);
+    return hipGetLastError();
+}
+
 int64_t env_min_m()
 {
     const char* e = std::getenv("OWQ_GEMM_MIN_M");
@@ -362,8 +590,8 @@ hipError_t launch_gemm(const LinearDesc& d, int64_t M, hipStream_t s)
     a.k = d.k;
     a.mblocks = 1;
     if (M >= 128)
-        return launch_tile<2, 4, 2, 2, 1, 2>(a, s);  // 128 tokens x 256 rows, 4 waves of 64 x 128
-    return launch_tile<1, 2, 1, 4, 1, 2>(a, s);      // 32 tokens x 256 rows
+        return launch_dma<2, 4, 2, 2>(a, s);     // 128 tokens x 256 rows, 4 waves of 64 x 128
+    return launch_tile<1, 2, 1, 4, 1, 2>(a, s);  // 32 tokens x 256 rows, 4 waves of 32 x 64
 }
 
 }  // namespace owq
