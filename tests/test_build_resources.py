@@ -1,0 +1,43 @@
+"""The compiler's per-kernel resource figures of the built library.
+
+`build()` records, for every kernel, the registers, scratch memory and occupancy
+the compiler reported. A kernel that keeps an array or spilled registers in
+scratch memory pays a memory round trip whose wait also covers every load in
+flight, which turns the streaming kernels latency-bound; none of them may use
+scratch.
+"""
+import json
+import os
+
+import pytest
+
+from mixed_precision_weight_amd import build as B
+
+KERNELS = ("k_gemv", "k_mfv", "k_gemm_dma", "k_gemm", "k_colsum", "k_rowfit", "k_finalize", "k_topk", "k_pack")
+
+
+def _load():
+    if not os.path.exists(B.RESOURCES):
+        pytest.skip("library not built yet (no kernel resource record)")
+    with open(B.RESOURCES) as f:
+        return json.load(f)
+
+
+def test_every_kernel_is_recorded():
+    res = _load()
+    for k in KERNELS:
+        assert any(k in name for name in res), k
+
+
+def test_no_kernel_uses_scratch():
+    res = _load()
+    bad = {n: r for n, r in res.items()
+           if r.get("ScratchSize", 0) or r.get("VGPRs Spill", 0) or r.get("SGPRs Spill", 0)}
+    assert not bad, bad
+
+
+def test_register_budget_allows_resident_waves():
+    res = _load()
+    for n, r in res.items():
+        assert 1 <= r["Occupancy"] <= 8, (n, r)
+        assert r["VGPRs"] <= 256 and r["AGPRs"] <= 256, (n, r)
