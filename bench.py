@@ -5,17 +5,22 @@ One step = one pass of every hot-path stage over one LLaMA-7B decoder layer
 columns, ~3.1 bits per weight), on seeded synthetic inputs:
   1. calibration: owq_calibrate_score on T = 2048 tokens, owq_select_weak and
      owq_pack, for each of the 7 linears;
-  2. decode: owq_linear_batched over the 7 linears at M = 1 (one launch);
+  2. decode: owq_linear_batched over the 7 linears at M = 1 (one launch per
+     layer), for R = 8 distinct packed layers in a row, as a token passes
+     through consecutive decoder layers;
   3. prefill: owq_linear at M = 2048 for each of the 7 linears.
-Decode reads one of R = 8 packed copies of the layer (8 x 79 MB > 2 x the 256 MB
-Infinity Cache), written by the calibration stage R/2 steps earlier, so its
-bytes come from HBM. Inputs are resident in HBM before timing starts.
+The R = 8 packed copies of the layer take 8 x 79 MB, more than twice the 256 MB
+Infinity Cache. Decode visits them starting after the copy this step's
+calibration wrote and ending with it, so at least 7 x 79 MB stream between two
+touches of a copy and its bytes come from HBM. Inputs are resident in HBM
+before timing starts.
 
-Reported value: effective GB/s of the decode launch (packed codes + fp16 scales
-+ uint8 zeros + fp16 weak columns + fp16 x, per linear, summed over the layer)
-divided by its duration, measured with HIP events recorded on the launch stream
-around every decode launch of the timed steps. The other stages are timed the
-same way and reported under "kernels", each against its own roofline.
+Reported value: effective GB/s of decode (packed codes + fp16 scales + uint8
+zeros + fp16 weak columns + fp16 x, per linear, summed over the layer) over the
+average duration of one layer's decode launch, measured with HIP events
+recorded on the launch stream around the R back-to-back decode launches of each
+timed step. The other stages are timed with events around each launch and
+reported under "kernels", each against its own roofline.
 
 --copy-reference adds, after the timed steps, three copies of a 512 MiB buffer
 (a plain copy kernel of known size) so that hardware-counter runs of this script
@@ -197,11 +202,11 @@ def main():
 
     def step(i, ev):
         cal_slot = slots[i % ROTATE]
-        dec_slot = slots[(i + ROTATE // 2) % ROTATE]
         calibrate_pack(cal_slot, ev)
         o = 3 * L + 1
         ev[o].record()
-        owq.linear_batched(dec_slot, xd, yd)
+        for r in range(1, ROTATE + 1):  # the copy written above comes last
+            owq.linear_batched(slots[(i + r) % ROTATE], xd, yd)
         ev[o + 1].record()
         o += 2
         for li in range(L):
@@ -231,8 +236,8 @@ def main():
     sel_s = [mean_ms(3 * li + 1, 3 * li + 2) / 1e3 for li in range(L)]
     pak_s = [mean_ms(3 * li + 2, 3 * li + 3) / 1e3 for li in range(L)]
     o = 3 * L + 1
-    dec_s = mean_ms(o, o + 1) / 1e3
-    dec_min_s = min(e[o].elapsed_time(e[o + 1]) for e in evs) / 1e3
+    dec_s = mean_ms(o, o + 1) / 1e3 / ROTATE
+    dec_min_s = min(e[o].elapsed_time(e[o + 1]) for e in evs) / 1e3 / ROTATE
     o += 2
     pre_s = [mean_ms(o + li, o + li + 1) / 1e3 for li in range(L)]
 
@@ -264,14 +269,16 @@ def main():
                                "2x 11008x4096 k=32, 4096x11008 k=86), 3-bit codes + fp16 weak columns; "
                                "decode M=1, calibration T=2048, prefill M=2048",
                    "decode_M": 1, "calib_T": cfg.T, "prefill_M": PREFILL_M, "bits": 3,
-                   "decode_effective_bytes": decode_bytes, "rotation_copies": ROTATE},
+                   "decode_effective_bytes": decode_bytes, "rotation_copies": ROTATE,
+                   "decode_layers_per_step": ROTATE},
         "roofline": {"kernel": "k_gemv<1> (decode GEMV, one launch over the 7 linears)", "bound": "hbm",
                      "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernels": {
-            "decode": dict(hbm_entry(decode_bytes, dec_s, "k_gemv<1>, 7 linears in one launch"),
+            "decode": dict(hbm_entry(decode_bytes, dec_s, "k_gemv<1>, 7 linears in one launch; "
+                                     "per layer, 8 layers back to back"),
                            us_min=round(dec_min_s * 1e6, 2)),
-            "prefill": {"what": "k_gemm (MFMA 32x32x16 f16), 7 linears at M=2048", "us": round(sum(pre_s) * 1e6, 1),
+            "prefill": {"what": "k_gemm_dma (MFMA 32x32x16 f16), 7 linears at M=2048", "us": round(sum(pre_s) * 1e6, 1),
                         "bound": "mfma", "achieved": round(pre_tflops, 1), "peak": MFMA_FP16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
                         "algorithmic_flops": pre_flops, "per_linear": per_linear_prefill},
@@ -284,20 +291,19 @@ def main():
     if not args.no_sweep:
         print("bench: decode batch sweep", file=sys.stderr, flush=True)
         sweep = {}
-        reps = 16
+        reps = 2 * ROTATE
         for M in SWEEP_MS:
             xs = [x[:M] for x in x1]
             ys = [y[:M] for y in y1]
-            evp = [(E(), E()) for _ in range(reps)]
-            for r in range(reps + 2):
-                slot = slots[r % ROTATE]
-                if r >= 2:
-                    evp[r - 2][0].record()
-                owq.linear_batched(slot, xs, ys)
-                if r >= 2:
-                    evp[r - 2][1].record()
+            for r in range(ROTATE):
+                owq.linear_batched(slots[r], xs, ys)
+            a, b = E(), E()
+            a.record()
+            for r in range(reps):  # back to back, as in the timed steps
+                owq.linear_batched(slots[r % ROTATE], xs, ys)
+            b.record()
             torch.cuda.synchronize()
-            t = float(np.mean([a.elapsed_time(b) for a, b in evp])) / 1e3
+            t = a.elapsed_time(b) / 1e3 / reps
             nb = sum(eff_bytes(s.N, s.K, s.k, M) for s in specs)
             sweep[f"M={M}"] = {"us_per_layer": round(t * 1e6, 2), "effective_GBps": round(nb / t / 1e9, 1),
                                "frac_hbm": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
