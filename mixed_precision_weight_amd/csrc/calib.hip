@@ -46,24 +46,20 @@ struct ErrElem {  // dW = w - s (q - z), exact in fp32; squared in fp64 by the c
     const uint16_t* s16;
     const uint8_t* z;
     struct Row {
-        uint32_t s;  // fp16 step bits
-        uint32_t z;
+        float s, rs, hs, zf;  // step, ~1/step, step/2, zero point
     };
-    __device__ __forceinline__ Row load_row(int64_t r) const { return Row{s16[r], z[r]}; }
+    __device__ __forceinline__ Row load_row(int64_t r) const
+    {
+        const float sf = h2f(s16[r]);
+        return Row{sf, __builtin_amdgcn_rcpf(sf), 0.5f * sf, (float)z[r]};
+    }
     __device__ __forceinline__ float val(const Row& rw, uint16_t h) const
     {
-        // every weight lies inside the row's full-row fit range, so |w / s| <= 8
-        const float sf = h2f((uint16_t)rw.s);
+        // the residual against the (possibly clamped) grid point, exact: every
+        // weight lies inside the row's full-row fit range, so |w / s| <= 8 and the
+        // product of the offset and the 11-bit step has at most 14 bits
         const float w = h2f(h);
-        const int zi = (int)rw.z;
-        float e;
-        const float t = round_quotient(w, sf, __builtin_amdgcn_rcpf(sf), e);
-        const int c = (int)t + zi;
-        if (c < 0 || c > 7) {  // clipped at a grid end: residual against the end code, exact
-            const int cq = c < 0 ? 0 : 7;
-            e = __builtin_fmaf(-(float)(cq - zi), sf, w);
-        }
-        return e;
+        return __builtin_fmaf(-grid_offset(w, rw.s, rw.rs, rw.hs, rw.zf), rw.s, w);
     }
     static constexpr bool kSquared = false;
 };
@@ -110,8 +106,8 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ A, 
                 float e = elem.val(rw[u], h);
                 if (Elem::kSquared)
                     acc[c] += (double)e;
-                else
-                    acc[c] += (double)e * (double)e;
+                else  // e^2 is exact in fp64, so the fused form rounds like mul + add
+                    acc[c] = __builtin_fma((double)e, (double)e, acc[c]);
             }
         }
     }

@@ -45,57 +45,36 @@ __device__ __forceinline__ void qparams_from_range(float lo, float hi, uint16_t&
 }
 
 // rint(w / s), round half to even, for a positive fp16 step s and an fp16 weight
-// w, without an IEEE division (rs ~ 1/s, within a few ulps). The guess
-// t = rint(w rs) differs from the rounded quotient by at most one, and only when
-// w / s lies within a few ulps of a half-integer; the signs of w - (t + 1/2) s
-// and w - (t - 1/2) s, each exact after one FMA (t +- 1/2 times an 11-bit step
-// is exact and rounding keeps the sign), settle it, an exact tie going to the
-// even neighbour. The quotient of two fp16 values is never within half an fp32
-// ulp of a half-integer without being equal to it, so the result equals rint of
-// the correctly rounded fp32 quotient, as in the definition. Results beyond
-// +-16 are only meaningful up to the clamp the callers apply.
-__device__ __forceinline__ float rint_div(float w, float s, float rs)
+// w, with neither an IEEE division nor a branch (rs ~ 1/s, within a few ulps,
+// hs = s / 2). The guess t = rint(w rs) is at most one off, and only when w / s
+// lies within a few ulps of a half-integer. e = w - t s is exact after one FMA
+// (t s has at most 16 significant bits and e stays within a step of 0), so |e|
+// against s/2 classifies the quotient t + e/s exactly: below, t; above, t + 1
+// toward e; equal, the exact half-integer t +- 1/2, which rint takes to the even
+// neighbour. The quotient of two fp16 values is never within half an fp32 ulp
+// of a half-integer without being equal to it, so the result equals rint of the
+// correctly rounded fp32 quotient, as in the definition. The guess is clamped
+// to +-16; beyond that only the side matters to the callers' clamp.
+__device__ __forceinline__ float rint_quotient(float w, float s, float rs, float hs)
 {
-    float t = fminf(fmaxf(rintf(w * rs), -16.0f), 16.0f);
-    const float dh = __builtin_fmaf(-(t + 0.5f), s, w);
-    const float dl = __builtin_fmaf(-(t - 0.5f), s, w);
-    const bool odd = ((int)t & 1) != 0;
-    if (dh > 0.0f || (dh == 0.0f && odd))
-        t += 1.0f;
-    else if (dl < 0.0f || (dl == 0.0f && odd))
-        t -= 1.0f;
-    return t;
+    const float t = fminf(fmaxf(rintf(w * rs), -16.0f), 16.0f);
+    const float e = __builtin_fmaf(-t, s, w);
+    const float a = fabsf(e);
+    const float f = a > hs ? 1.0f : (a == hs ? 0.5f : 0.0f);
+    return rintf(t + __builtin_copysignf(f, e));
 }
 
-// t = rint(w / s) (round half to even) and the exact residual e = w - t s, for a
-// positive fp16 step s and an fp16 weight w with |w / s| <= 16. The guess
-// t = rint(w rs) is at most one off; e = w - t s is exact after one FMA (t s has
-// at most 16 significant bits and e stays within a step of 0), so comparing e
-// with +-s/2 finds the rounded quotient exactly (a tie goes to even), and the
-// corrected residual e -+ s is exact as well. Same result as rint_div.
-__device__ __forceinline__ float round_quotient(float w, float s, float rs, float& e)
+// Grid offset of w: clamp(rint(w / s) + z, 0, 7) - z, as a float (rs ~ 1/s,
+// hs = s / 2, zf = z).
+__device__ __forceinline__ float grid_offset(float w, float s, float rs, float hs, float zf)
 {
-    float t = rintf(w * rs);
-    e = __builtin_fmaf(-t, s, w);
-    const float hs = 0.5f * s;
-    const bool odd = ((int)t & 1) != 0;
-    if (e > hs || (e == hs && odd)) {
-        t += 1.0f;
-        e -= s;
-    } else if (e < -hs || (e == -hs && odd)) {
-        t -= 1.0f;
-        e += s;
-    }
-    return t;
+    return fminf(fmaxf(rint_quotient(w, s, rs, hs) + zf, 0.0f), 7.0f) - zf;
 }
 
-// rs: an approximation of 1 / sf (see rint_div)
-__device__ __forceinline__ int rtn_code(float w, float sf, float rs, int z)
+// The 3-bit code of w.
+__device__ __forceinline__ int rtn_code(float w, float s, float rs, float hs, float zf)
 {
-    float r = rint_div(w, sf, rs);
-    r = fminf(fmaxf(r, -8.0f), 8.0f);  // keeps the conversion defined; clamp below saturates anyway
-    int q = (int)r + z;
-    return q < 0 ? 0 : (q > 7 ? 7 : q);
+    return (int)(grid_offset(w, s, rs, hs, zf) + zf);
 }
 
 // ---------------------------------------------------------- wave reductions --

@@ -20,7 +20,8 @@
 // decoders get both codes of a column pair from one 32-bit window.
 //
 // Built with -ffp-contract=off: the quantiser steps are single IEEE operations
-// (the code itself comes from rint_div, which reproduces rint(w / s) exactly).
+// (the code itself comes from rint_quotient, which reproduces rint(w / s)
+// exactly).
 #include "owq_device.h"
 #include "owq_launch.h"
 
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
         int z;
         qparams_from_range(lo, hi, s16, z);
         const float sf = h2f(s16);
-        const float rs = __builtin_amdgcn_rcpf(sf);
+        const float rs = __builtin_amdgcn_rcpf(sf), hs = 0.5f * sf, zf = (float)z;
 #pragma unroll
         for (int u = 0; u < GPT; u++) {
             int64_t g = tid + 256 * u;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
                 uint32_t o[3] = {0u, 0u, 0u};
 #pragma unroll
                 for (int c = 0; c < 32; c++) {
-                    uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), sf, rs, z);
+                    uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), sf, rs, hs, zf);
                     const int pos = 3 * kSlot[c], wd = pos >> 5, off = pos & 31;
                     o[wd] |= cd << off;
                     if (off > 29)
