@@ -541,6 +541,9 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2,
                     a.y[(int64_t)m * N + n] = f2h(acc[i][f][r]);
             }
         }
+    // the last steps' x loads (duplicates of the last chunk) may still be in
+    // flight: none may write this block's LDS after the block has ended
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int FM, int FN, int WM, int WN>

@@ -71,19 +71,33 @@ __device__ __forceinline__ half8_t h8_of(uint32_t a, uint32_t b, uint32_t c, uin
 // U groups per lane per chunk; MC = largest token count of the instance.
 template <int U, int MC>
 struct MfvShape {
-    static constexpr int GC = 4 * U;                     // groups per chunk
-    static constexpr int RS = GC * 64 + 16;              // LDS bytes per staged token (padded)
-    static constexpr int XI = (MC * GC + 255) / 256;     // staged group rows per thread
-    static constexpr int LDS = 2 * MC * RS;              // double buffer
+    static constexpr int GC = 4 * U;             // groups per chunk
+    static constexpr int RS = GC * 64 + 16;      // LDS bytes per staged token (padded)
+    static constexpr int STAGE = MC * RS;        // one x stage
+    static constexpr int PT = GC / 16;           // 1 KB x loads per token and chunk
+    static constexpr int DPW = MC * PT / 4;      // x loads per wave and chunk
+    static constexpr int CRS = GC * 12 + 16;     // LDS bytes per row of a wave's code chunk (padded)
+    static constexpr int CQ = GC * 12 / 16;      // 16-byte pieces of a row's code chunk
+    static constexpr int CL = 16 * CQ / 64;      // code loads per lane and chunk
+    static_assert(GC % 16 == 0 && (MC * PT) % 4 == 0, "x loads must split evenly over the waves");
+    static_assert((16 * CQ) % 64 == 0 && CRS % 16 == 0, "code pieces must split evenly over the lanes");
 };
+
+__device__ __forceinline__ void dma_x(__amdgpu_buffer_rsrc_t r, char* lds, int voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
 
 template <int U, int MC>
 __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
 {
     using S = MfvShape<U, MC>;
-    constexpr int GC = S::GC, RS = S::RS, XI = S::XI;
-    extern __shared__ uint4 smem[];
-    char* const lds = reinterpret_cast<char*>(smem);
+    constexpr int GC = S::GC, RS = S::RS, STAGE = S::STAGE, PT = S::PT, DPW = S::DPW;
+    constexpr int CRS = S::CRS, CQ = S::CQ, CL = S::CL;
+    __shared__ __attribute__((aligned(1024))) char xs0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char xs1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char xs2[STAGE];
+    __shared__ __attribute__((aligned(16))) char cs[4][16 * CRS];  // each wave's code chunk
 
     int li = 0;
     for (int l = 1; l < b.count; l++)
@@ -104,80 +118,90 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
         const_cast<uint32_t*>(L.q) + (int64_t)brow * G * 3, (short)0, nb * G * 12, 0x00020000);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(L.x), (short)0, M * K * 2, 0x00020000);
-    const int qrow = rloc * G * 12;
 
-    // staging items i = tid + 256 t: token i / GC, group i % GC of the chunk
-    i32x4 xg[XI][4];
-    u32x3 cw[U];
-    auto issue = [&](int c) {
+    // x of chunk c goes to LDS by direct-to-LDS loads: load t of this wave moves
+    // 1 KB (16 groups) of token m = qi / PT, qi = wave DPW + t, to stage offset
+    // m RS + (qi % PT) KB; lanes 4 apart take consecutive groups. Groups past K
+    // are read out of the buffer's range, which gives zeros; tokens past M
+    // repeat the last token (their A rows are never read).
+    auto dma = [&](int c, char* stage) {
+        const int cc = min(c, nch - 1);
 #pragma unroll
-        for (int t = 0; t < XI; t++) {
-            const int i = tid + 256 * t;
-            const int m = min(i / GC, M - 1);
-            const int g = min(c * GC + i % GC, G - 1);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; q4++)
-                xg[t][q4] = __builtin_amdgcn_raw_buffer_load_b128(xr, (m * K + g * 32) * 2 + 16 * q4, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int g = min(c * GC + 4 * u + qd, G - 1);
-            cw[u] = __builtin_amdgcn_raw_buffer_load_b96(qr, qrow + g * 12, 0, 0);
+        for (int t = 0; t < DPW; t++) {
+            const int qi = wave * DPW + t;
+            const int m = qi / PT, part = qi % PT;
+            const int g = cc * GC + part * 16 + (lane >> 2);
+            const int off = (min(m, M - 1) * K + g * 32) * 2 + (lane & 3) * 16;
+            dma_x(xr, stage + m * RS + part * 1024, off + (g >= G ? 0x40000000 : 0));
         }
     };
-    auto stage = [&](int c) {
-        char* const buf = lds + (c & 1) * MC * RS;
+    // Codes: the wave's 16 rows x GC groups of a chunk are loaded as consecutive
+    // 16-byte pieces (piece p = 64 i + lane: row p / CQ, bytes 16 (p % CQ) of the
+    // row's chunk), so each load instruction reads whole lines; the MFMA layout
+    // wants group 4 u + l / 16 of row l % 16 in lane l, so the pieces go through
+    // the wave's own LDS rows (padded to CRS bytes: the group reads of a wave
+    // then hit distinct banks). Rows past the block and groups past K read zeros
+    // or the next row; their x is zero.
+    typedef uint4 QRegs[CL];
+    auto load_q = [&](int c, QRegs& cw) {
+        const int cc = min(c, nch - 1);
 #pragma unroll
-        for (int t = 0; t < XI; t++) {
-            const int i = tid + 256 * t;
-            if (i < M * GC) {
-                const bool live = c * GC + i % GC < G;
-                uint32_t pr[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; q4++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        pr[4 * q4 + e] = live ? (uint32_t)xg[t][q4][e] : 0u;
-                uint4* dst = reinterpret_cast<uint4*>(buf + (i / GC) * RS + (i % GC) * 64);
-#pragma unroll
-                for (int q4 = 0; q4 < 4; q4++)
-                    dst[q4] = make_uint4(pr[4 * q4], pr[4 * q4 + 1], pr[4 * q4 + 2], pr[4 * q4 + 3]);
-            }
+        for (int i = 0; i < CL; i++) {
+            const int pc = 64 * i + lane;
+            const int r = pc / CQ, o = (pc % CQ) * 16;
+            cw[i] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, ((wave * 16 + r) * G + cc * GC) * 12 + o, 0, 0));
         }
     };
+    char* const crow = cs[wave];
 
     const float sc = h2f(L.s[brow + rloc]);
     const ZeroSub zs = make_zero_sub((uint32_t)L.z[brow + rloc]);
     const Magic mg = make_magic();
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    issue(0);
-    stage(0);
-    __syncthreads();
     // this lane's A operand: token min(l16, M - 1), groups 4 u + qd of the chunk
     const int arow = min(l16, M - 1) * RS + qd * 64;
-    for (int c = 0; c < nch; c++) {
-        u32x3 cur[U];
+    // Chunk c reads stage cur and codes qc; it loads x and codes of chunk c + 2
+    // into stage nxt2 and set q2 first.
+    auto step = [&](int c, const char* cur, char* nxt2, const QRegs& qc, QRegs& q2) {
+        // this wave's x loads of chunk c are done once at most 2 U + DPW newer
+        // loads remain (codes of c, x and codes of c + 1); after the barrier every
+        // wave's are, and every wave is done with the stage chunk c + 2 goes to
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * U + DPW) : "memory");
+        dma(c + 2, nxt2);
+        load_q(c + 2, q2);
+        if (c < nch) {  // block-uniform; the steps past the end only keep the pipeline shape
 #pragma unroll
-        for (int u = 0; u < U; u++)
-            cur[u] = cw[u];
-        issue(min(c + 1, nch - 1));
-        const char* const buf = lds + (c & 1) * MC * RS + arow;
+            for (int i = 0; i < CL; i++) {
+                const int pc = 64 * i + lane;
+                *reinterpret_cast<uint4*>(crow + (pc / CQ) * CRS + (pc % CQ) * 16) = qc[i];
+            }
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            uint32_t p[16];
-            decode_group(cur[u].x, cur[u].y, cur[u].z, mg, zs, p);
+            for (int u = 0; u < U; u++) {
+                const uint32_t* gw = reinterpret_cast<const uint32_t*>(crow + l16 * CRS + (4 * u + qd) * 12);
+                uint32_t p[16];
+                decode_group(gw[0], gw[1], gw[2], mg, zs, p);
 #pragma unroll
-            for (int st = 0; st < 4; st++) {
-                const half8_t av =
-                    __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(buf + 4 * u * 64 + st * 16));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    av, h8_of(p[4 * st], p[4 * st + 1], p[4 * st + 2], p[4 * st + 3]), acc, 0, 0, 0);
+                for (int st = 0; st < 4; st++) {
+                    const half8_t av = __builtin_bit_cast(
+                        half8_t, *reinterpret_cast<const uint4*>(cur + arow + 4 * u * 64 + st * 16));
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        av, h8_of(p[4 * st], p[4 * st + 1], p[4 * st + 2], p[4 * st + 3]), acc, 0, 0, 0);
+                }
             }
         }
-        if (c + 1 < nch)
-            stage(c + 1);
-        __syncthreads();
+    };
+
+    QRegs qa, qb, qc3;
+    dma(0, xs0);
+    load_q(0, qa);
+    dma(1, xs1);
+    load_q(1, qb);
+    for (int c = 0; c < nch; c += 3) {
+        step(c, xs0, xs2, qa, qc3);
+        step(c + 1, xs1, xs0, qb, qa);
+        step(c + 2, xs2, xs1, qc3, qb);
     }
 
     // row step, then the weak columns: B = w_weak[row][cs + 8 qd + e], A = x[token][idx[...]]
@@ -219,13 +243,15 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
                 L.y[(int64_t)m * N + brow + row] = f2h(acc[r]);
         }
     }
+    // the last steps' x loads may still be in flight: none may write this
+    // block's LDS after the block has ended
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int U, int MC>
 hipError_t launch_shape(const MfvBatch& b, int nblocks, int M, hipStream_t s)
 {
-    using S = MfvShape<U, MC>;
-    hipLaunchKernelGGL((k_mfv<U, MC>), dim3(nblocks), dim3(256), S::LDS, s, b, M);
+    hipLaunchKernelGGL((k_mfv<U, MC>), dim3(nblocks), dim3(256), 0, s, b, M);
     return hipGetLastError();
 }
 
