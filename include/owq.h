@@ -148,11 +148,12 @@ typedef struct {
  *   y[m][i] = s_i * sum_j (q_ij - z_i) x[m][j] + sum_c w_weak[i][c] x[m][weak_idx[c]]
  * computed with fp32 accumulation and rounded to fp16 (nearest-even).
  * L: HOST pointer to the layer; x: fp16 [M][K]; y: fp16 [M][N] (output, must not
- * alias x or the layer). M <= 4 runs an HBM-streaming kernel on the vector ALUs,
- * 5 <= M <= 16 a streaming kernel that multiplies on the matrix cores, larger M a
+ * alias x or the layer). M <= 2 runs an HBM-streaming kernel on the vector ALUs,
+ * 3 <= M <= 16 a streaming kernel that multiplies on the matrix cores, larger M a
  * tiled matrix-core (MFMA) GEMM; all compute the same definition. The environment
- * variable OWQ_DECODE=matrix sends every M <= 16 to the matrix-core streaming
- * kernel (read at each call); OWQ_GEMM_MIN_M (read once) moves the GEMM bound. */
+ * variable OWQ_DECODE (read at each call) overrides the first split: "matrix"
+ * sends every M <= 16 to the matrix-core streaming kernel, "vector" keeps M <= 4
+ * on the vector ALUs; OWQ_GEMM_MIN_M (read once) moves the GEMM bound. */
 owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M,
                       uint16_t* y, void* stream);
 

@@ -264,7 +264,7 @@ bool decode_on_matrix_cores(int64_t M)
         return M > kGemvMaxM;
     if (e && std::strcmp(e, "matrix") == 0)
         return true;
-    return M > kGemvMaxM;
+    return M > kVectorDecodeMaxM;
 }
 
 bool mfv_fits(int64_t M, int64_t K)

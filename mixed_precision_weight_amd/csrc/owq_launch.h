@@ -39,6 +39,7 @@ struct LinearDesc {
 };
 
 constexpr int kGemvMaxM = 4;        // tokens per GEMV launch
+constexpr int kVectorDecodeMaxM = 2;  // above this the matrix-core decode is faster (measured)
 constexpr int kGemvMaxLayers = 16;  // layers per batched GEMV launch
 
 // Decode GEMV over `count` layers (count <= kGemvMaxLayers), 1 <= M <= kGemvMaxM,

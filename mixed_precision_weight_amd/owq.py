@@ -172,7 +172,7 @@ def linear(layer: dict, x: torch.Tensor, y: torch.Tensor | None = None, stream=N
 
 
 def linear_batched(layers: list, xs: list, ys: list | None = None, stream=None) -> list:
-    """Several independent decode linears (same M <= 4) in one launch."""
+    """Several independent decode linears (same 1 <= M <= 16) in one launch."""
     n = len(layers)
     Ls = (OwqLayer * n)(*[layer_struct(l) for l in layers])
     M = xs[0].shape[0]

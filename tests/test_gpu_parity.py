@@ -204,3 +204,17 @@ def test_pack_and_score_exact_ties(owq):
     o_idx = oracle.select_weak(o_score, k)
     packed = owq.pack(Wd, dev(o_idx.astype(np.int32)))
     check_pack(packed, oracle.pack(W, o_idx))
+
+
+@pytest.mark.parametrize("N,K,k,Ms", [(5, 96, 1, (3, 4)), (64, 640, 7, (3,)), (37, 11008, 86, (3, 4)),
+                                      (130, 8192, 63, (4,))])
+def test_vector_decode_three_and_four_tokens(owq, monkeypatch, N, K, k, Ms):
+    """3 and 4 tokens run on the matrix cores by default; OWQ_DECODE=vector keeps
+    them on the vector-ALU kernel, which must stay at the same bar."""
+    monkeypatch.setenv("OWQ_DECODE", "vector")
+    rng = np.random.default_rng(N * 17 + K + k)
+    W = _tiny_rows(synth.random_layer(rng, N, K, 0.02))
+    spec = synth.LayerSpec("edge", N, K, k, 0.02, max(1, K // 200), 20.0)
+    X = synth.calibration(spec, N + K, 24)
+    x = synth.activations(spec, N + K + 2, max(Ms))
+    _run(owq, W, X, k, [x[:m] for m in Ms], f"vector N={N} K={K} k={k}")
