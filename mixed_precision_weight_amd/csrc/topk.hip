@@ -172,6 +172,7 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
                                                    int32_t* __restrict__ out)
 {
     __shared__ uint32_t hist[256];
+    __shared__ uint32_t whist[16][256];  // one digit histogram per wave
     __shared__ uint32_t wave_tot[16];
     __shared__ unsigned long long sh_prefix;
     __shared__ int sh_kk, sh_done;
@@ -188,24 +189,22 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
     uint64_t prefix = 0, mask = 0;
     int kk = k;  // how many still to take among keys matching `prefix` on `mask`
     for (int shift = 56; shift >= 0; shift -= 8) {
-        if (tid < 256)
-            hist[tid] = 0;
-        __syncthreads();
-        // keys of a wave that share a digit are counted with one ballot and one
-        // atomic: the leading digits of the scores are mostly equal, and per-key
-        // atomics on one LDS bin would serialise
+        // each wave counts its keys' digits into its own LDS histogram (atomics
+        // that hit one bin serialise within the wave only), then the 16 are summed
 #pragma unroll
-        for (int c = 0; c < C; c++) {
-            const uint32_t d = (uint32_t)(key[c] >> shift) & 255u;
-            uint64_t act = __ballot((key[c] & mask) == prefix);
-            while (act) {  // wave-uniform
-                const int leader = __builtin_ctzll(act);
-                const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
-                const uint64_t same = act & __ballot(d == dl);
-                if (lane == leader)
-                    atomicAdd(&hist[dl], (uint32_t)__popcll(same));
-                act &= ~same;
-            }
+        for (int i = 0; i < 4; i++)
+            whist[wave][lane + 64 * i] = 0;
+#pragma unroll
+        for (int c = 0; c < C; c++)
+            if ((key[c] & mask) == prefix)
+                atomicAdd(&whist[wave][(uint32_t)(key[c] >> shift) & 255u], 1u);
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t t = 0;
+#pragma unroll
+            for (int w = 0; w < 16; w++)
+                t += whist[w][tid];
+            hist[tid] = t;
         }
         __syncthreads();
         if (wave == 0) {
