@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-sweep", action="store_true", help="skip the decode batch sweep")
+    ap.add_argument("--no-long-calibration", action="store_true",
+                    help="skip the long-calibration (T = 8192) timing")
     ap.add_argument("--copy-reference", action="store_true",
                     help="end with three 512 MiB device copies (counter scaling)")
     args = ap.parse_args()
@@ -309,6 +311,30 @@ def main():
                                "frac_hbm": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
                                "path": "k_gemv, one launch" if M <= 2 else "k_mfv, one launch"}
         result["decode_batch_sweep"] = sweep
+
+    if not args.no_long_calibration:
+        # long calibration (T = 8192 tokens) at the MLP shapes: X and W read once
+        print("bench: long calibration", file=sys.stderr, flush=True)
+        c4 = synth.CONFIGS[4]
+        long_cal = {}
+        for li, s in enumerate(c4.layers):
+            seed = c4.seed(li)
+            Wl = torch.from_numpy(synth.weights(s, seed)).to(dev)
+            Xl = torch.from_numpy(synth.calibration(s, seed, c4.T)).to(dev)
+            wsl = torch.empty(owq.calibrate_workspace_bytes(s.N, s.K, c4.T), dtype=torch.uint8, device=dev)
+            owq.calibrate(Wl, Xl, workspace=wsl)
+            reps = 5
+            evl = [(E(), E()) for _ in range(reps)]
+            for r in range(reps):
+                evl[r][0].record()
+                owq.calibrate(Wl, Xl, workspace=wsl)
+                evl[r][1].record()
+            torch.cuda.synchronize()
+            t = float(np.median([a.elapsed_time(b) for a, b in evl])) / 1e3
+            long_cal[f"{s.name} {s.N}x{s.K} T={c4.T}"] = hbm_entry(calib_bytes(s.N, s.K, c4.T), t,
+                                                                     "k_colsum x2 + k_rowfit + k_finalize")
+            del Wl, Xl, wsl
+        result["kernels"]["calibrate_score_long"] = long_cal
 
     if args.copy_reference:
         n = 512 << 20
