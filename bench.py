@@ -312,6 +312,52 @@ def main():
                                "path": "k_gemv, one launch" if M <= 2 else "k_mfv, one launch"}
         result["decode_batch_sweep"] = sweep
 
+        # the same decode as 7 launches per layer (one per linear), recorded in a HIP graph
+        print("bench: decode as per-linear launches in a graph", file=sys.stderr, flush=True)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(ROTATE):
+                for li in range(L):
+                    owq.linear(slots[r][li], xd[li], yd[li])
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(ROTATE):
+                for li in range(L):
+                    owq.linear(slots[(r + 1) % ROTATE][li], xd[li], yd[li])
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 10
+        a, b = E(), E()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / 1e3 / (reps * ROTATE)
+        result["kernels"]["decode_graph"] = hbm_entry(
+            decode_bytes, t, f"k_gemv<1>, 7 launches per layer ({ROTATE} layers) replayed from a HIP graph")
+        del g
+
+        # measured device-copy rate over 1 GiB (read + write), for comparison with the 8 TB/s peak
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        a, b = E(), E()
+        a.record()
+        for _ in range(5):
+            dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / 1e3 / 5
+        result["kernels"]["hbm_copy_reference"] = {"what": "device copy of 1 GiB (torch copy_)",
+                                                   "read_plus_write_GBps": round(2 * n / t / 1e9, 1),
+                                                   "frac": round(2 * n / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del src, dst
+
     if not args.no_long_calibration:
         # long calibration (T = 8192 tokens) at the MLP shapes: X and W read once
         print("bench: long calibration", file=sys.stderr, flush=True)
