@@ -165,10 +165,10 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
     // Chunk c reads stage cur and codes qc; it loads x and codes of chunk c + 2
     // into stage nxt2 and set q2 first.
     auto step = [&](int c, const char* cur, char* nxt2, const QRegs& qc, QRegs& q2) {
-        // this wave's x loads of chunk c are done once at most 2 U + DPW newer
+        // this wave's x loads of chunk c are done once at most 2 CL + DPW newer
         // loads remain (codes of c, x and codes of c + 1); after the barrier every
         // wave's are, and every wave is done with the stage chunk c + 2 goes to
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * U + DPW) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * CL + DPW) : "memory");
         dma(c + 2, nxt2);
         load_q(c + 2, q2);
         if (c < nch) {  // block-uniform; the steps past the end only keep the pipeline shape
