@@ -17,17 +17,17 @@
 // Lane layout: the MFMA pairs the 8 operand elements of lane l with the k values
 // 8 (l / 16) + e, for A row (token) l % 16 and B column (output row) l % 16.
 // A wavefront owns 16 consecutive output rows: lane l decodes, for row l % 16,
-// the groups 4 u + l / 16 (u < U) of each K chunk of 4 U groups, so each load
-// instruction of the wave reads 48 contiguous bytes from each of its 16 rows;
-// the 16 decode pairs of a group feed four MFMA steps (pairs 4t .. 4t + 3 in
-// step t). Decode pair p is columns (2p, 2p + 1) (the slot layout of the codes),
+// the groups 4 u + l / 16 (u < U) of each K chunk of 4 U groups (the codes are
+// loaded as whole lines and regrouped through LDS, see load_q); the 16 decode
+// pairs of a group feed four MFMA steps (pairs 4t .. 4t + 3 in step t). Decode pair p is columns (2p, 2p + 1) (the slot layout of the codes),
 // so x is staged as it is stored: the block's x chunk sits in LDS as
 // [token][group][32 values] and an A operand is one 128-bit LDS read per lane.
 // The K reduction happens inside the accumulators: no cross-lane reduction.
 //
-// Pipeline: LDS double buffer for x, the next chunk's codes and x in registers
-// while the current chunk computes, one barrier per chunk. A block is 4 waves
-// (64 rows) of one layer; one launch covers a batch of layers of any shapes.
+// Pipeline: x by direct-to-LDS loads into three stages and codes into three
+// register sets, two chunks ahead of the one computed, one barrier per chunk.
+// A block is W row waves (16 W rows of one layer) times S groups that split K;
+// one launch covers a batch of layers of any shapes.
 // Epilogue: row step, the weak columns as extra 32-deep MFMA steps (fp16 weak
 // weights against x gathered at weak_idx), fp16 stores.
 #include <cstdlib>
@@ -61,7 +61,6 @@ struct MfvBatch {
     int32_t count;
 };
 
-constexpr int kRowsPerBlock = 64;
 
 __device__ __forceinline__ half8_t h8_of(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
@@ -88,16 +87,27 @@ __device__ __forceinline__ void dma_x(__amdgpu_buffer_rsrc_t r, char* lds, int v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
-template <int U, int MC>
-__global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
+// S groups of W wavefronts split K: group kg walks chunks [kg P, kg P + P) of
+// the layer (P = ceil(chunks / S)) with x stages of its own, all groups in step
+// (one block barrier per chunk); at the end groups 1 .. S - 1 hand their
+// accumulators to group 0 through LDS. This cuts the chain of dependent chunks
+// of a block by S, so the blocks of long-row layers do not run on alone after
+// the others have finished.
+template <int U, int MC, int W, int S>
+__global__ __launch_bounds__(64 * W * S) void k_mfv(MfvBatch b, int M)
 {
-    using S = MfvShape<U, MC>;
-    constexpr int GC = S::GC, RS = S::RS, STAGE = S::STAGE, PT = S::PT, DPW = S::DPW;
-    constexpr int CRS = S::CRS, CQ = S::CQ, CL = S::CL;
-    __shared__ __attribute__((aligned(1024))) char xs0[STAGE];
-    __shared__ __attribute__((aligned(1024))) char xs1[STAGE];
-    __shared__ __attribute__((aligned(1024))) char xs2[STAGE];
-    __shared__ __attribute__((aligned(16))) char cs[4][16 * CRS];  // each wave's code chunk
+    using SH = MfvShape<U, MC>;
+    constexpr int GC = SH::GC, RS = SH::RS, STAGE = SH::STAGE, PT = SH::PT;
+    constexpr int DPW = MC * PT / W;  // x loads per wave and chunk
+    constexpr int D = 2;              // chunks in flight ahead of the one computed
+    static_assert((MC * PT) % W == 0, "x loads must split evenly over the waves");
+    constexpr int CRS = SH::CRS, CQ = SH::CQ, CL = SH::CL;
+    // three x stages per K group (chunks run two ahead), each its own array
+    __shared__ __attribute__((aligned(1024))) char xs0[S][STAGE];
+    __shared__ __attribute__((aligned(1024))) char xs1[S][STAGE];
+    __shared__ __attribute__((aligned(1024))) char xs2[S][STAGE];
+    __shared__ __attribute__((aligned(16))) char cs[W * S][16 * CRS];  // each wave's code chunk
+    static_assert(S == 1 || (S - 1) * W * 64 * 16 <= STAGE * S, "partial sums must fit in one stage set");
 
     int li = 0;
     for (int l = 1; l < b.count; l++)
@@ -107,11 +117,14 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
     const int N = L.N, K = L.K, k = L.k;
     const int G = K >> 5;
     const int nch = (G + GC - 1) / GC;
+    const int per = (nch + S - 1) / S;  // chunks per K group
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wid % W, kg = wid / W;  // row wave in the block, K group
+    const int c0 = kg * per, c1 = min(nch, c0 + per);  // this group's chunks
     const int l16 = lane & 15, qd = lane >> 4;
-    const int brow = ((int)blockIdx.x - L.block0) * kRowsPerBlock;
-    const int nb = min(N - brow, kRowsPerBlock);  // valid rows of the block
+    const int brow = ((int)blockIdx.x - L.block0) * 16 * W;
+    const int nb = min(N - brow, 16 * W);  // valid rows of the block
     const int rloc = min(wave * 16 + l16, nb - 1);  // this lane's row in the block (clamped)
 
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
@@ -121,18 +134,20 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
 
     // x of chunk c goes to LDS by direct-to-LDS loads: load t of this wave moves
     // 1 KB (16 groups) of token m = qi / PT, qi = wave DPW + t, to stage offset
-    // m RS + (qi % PT) KB; lanes 4 apart take consecutive groups. Groups past K
-    // are read out of the buffer's range, which gives zeros; tokens past M
-    // repeat the last token (their A rows are never read).
+    // m RS + (qi % PT) KB; lanes 4 apart take consecutive groups. Groups past K,
+    // and chunks past the group's range, are read out of the buffer's range,
+    // which gives zeros; tokens past M repeat the last token (their A rows are
+    // never read).
     auto dma = [&](int c, char* stage) {
-        const int cc = min(c, nch - 1);
+        const int cc = min(c, c1 - 1);
+        const int dead = c >= c1 ? 0x40000000 : 0;
 #pragma unroll
         for (int t = 0; t < DPW; t++) {
             const int qi = wave * DPW + t;
             const int m = qi / PT, part = qi % PT;
             const int g = cc * GC + part * 16 + (lane >> 2);
             const int off = (min(m, M - 1) * K + g * 32) * 2 + (lane & 3) * 16;
-            dma_x(xr, stage + m * RS + part * 1024, off + (g >= G ? 0x40000000 : 0));
+            dma_x(xr, stage + m * RS + part * 1024, off + (g >= G ? 0x40000000 : dead));
         }
     };
     // Codes: the wave's 16 rows x GC groups of a chunk are loaded as consecutive
@@ -144,7 +159,7 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
     // or the next row; their x is zero.
     typedef uint4 QRegs[CL];
     auto load_q = [&](int c, QRegs& cw) {
-        const int cc = min(c, nch - 1);
+        const int cc = min(c, c1 - 1);
 #pragma unroll
         for (int i = 0; i < CL; i++) {
             const int pc = 64 * i + lane;
@@ -153,25 +168,31 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, ((wave * 16 + r) * G + cc * GC) * 12 + o, 0, 0));
         }
     };
-    char* const crow = cs[wave];
+    char* const crow = cs[wid];
 
     const float sc = h2f(L.s[brow + rloc]);
     const ZeroSub zs = make_zero_sub((uint32_t)L.z[brow + rloc]);
     const Magic mg = make_magic();
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // one accumulator per group slot u: the MFMAs of different groups do not
+    // wait for each other's results
+    f32x4 accu[U];
+#pragma unroll
+    for (int u = 0; u < U; u++)
+        accu[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // this lane's A operand: token min(l16, M - 1), groups 4 u + qd of the chunk
     const int arow = min(l16, M - 1) * RS + qd * 64;
-    // Chunk c reads stage cur and codes qc; it loads x and codes of chunk c + 2
-    // into stage nxt2 and set q2 first.
-    auto step = [&](int c, const char* cur, char* nxt2, const QRegs& qc, QRegs& q2) {
-        // this wave's x loads of chunk c are done once at most 2 CL + DPW newer
-        // loads remain (codes of c, x and codes of c + 1); after the barrier every
-        // wave's are, and every wave is done with the stage chunk c + 2 goes to
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * CL + DPW) : "memory");
-        dma(c + 2, nxt2);
-        load_q(c + 2, q2);
-        if (c < nch) {  // block-uniform; the steps past the end only keep the pipeline shape
+    // Chunk c reads stage cur and codes qc; it loads x and codes of chunk c + D
+    // into stage nxt and set qn first.
+    auto step = [&](int c, const char* cur, char* nxt, const QRegs& qc, QRegs& qn) {
+        // this wave's x loads of chunk c are done once at most D CL + (D - 1) DPW
+        // newer loads remain (codes of c, x and codes of c + 1 .. c + D - 1);
+        // after the barrier every wave's are, and every wave is done with the
+        // stage chunk c + D goes to
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(D * CL + (D - 1) * DPW) : "memory");
+        dma(c + D, nxt);
+        load_q(c + D, qn);
+        if (c < c1) {  // wave-uniform; the steps past the end only keep the pipeline shape
 #pragma unroll
             for (int i = 0; i < CL; i++) {
                 const int pc = 64 * i + lane;
@@ -186,22 +207,47 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
                 for (int st = 0; st < 4; st++) {
                     const half8_t av = __builtin_bit_cast(
                         half8_t, *reinterpret_cast<const uint4*>(cur + arow + 4 * u * 64 + st * 16));
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        av, h8_of(p[4 * st], p[4 * st + 1], p[4 * st + 2], p[4 * st + 3]), acc, 0, 0, 0);
+                    accu[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        av, h8_of(p[4 * st], p[4 * st + 1], p[4 * st + 2], p[4 * st + 3]), accu[u], 0, 0, 0);
                 }
             }
         }
     };
 
     QRegs qa, qb, qc3;
-    dma(0, xs0);
-    load_q(0, qa);
-    dma(1, xs1);
-    load_q(1, qb);
-    for (int c = 0; c < nch; c += 3) {
-        step(c, xs0, xs2, qa, qc3);
-        step(c + 1, xs1, xs0, qb, qa);
-        step(c + 2, xs2, xs1, qc3, qb);
+    // the prologue issues x and codes chunk by chunk, in the order the steps
+    // do, so the waits inserted for the code registers count the same loads on
+    // the first pass through the loop as on the others
+    dma(c0, xs0[kg]);
+    load_q(c0, qa);
+    asm volatile("" ::: "memory");
+    dma(c0 + 1, xs1[kg]);
+    load_q(c0 + 1, qb);
+    asm volatile("" ::: "memory");
+    for (int c = c0; c < c0 + per; c += 3) {  // the same trip count in every group
+        step(c, xs0[kg], xs2[kg], qa, qc3);
+        step(c + 1, xs1[kg], xs0[kg], qb, qa);
+        step(c + 2, xs2[kg], xs1[kg], qc3, qb);
+    }
+    // the last steps' x loads may still be in flight: none may write LDS after
+    // this point (the stages are reused below, and the block may end)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    f32x4 acc = accu[0];
+#pragma unroll
+    for (int u = 1; u < U; u++)
+        acc += accu[u];
+
+    if constexpr (S > 1) {  // K groups 1 .. S - 1 hand their sums to group 0
+        f32x4* part = reinterpret_cast<f32x4*>(&xs0[0][0]);
+        __syncthreads();
+        if (kg > 0)
+            part[((kg - 1) * W + wave) * 64 + lane] = acc;
+        __syncthreads();
+        if (kg > 0)
+            return;
+#pragma unroll
+        for (int g2 = 1; g2 < S; g2++)
+            acc += part[((g2 - 1) * W + wave) * 64 + lane];
     }
 
     // row step, then the weak columns: B = w_weak[row][cs + 8 qd + e], A = x[token][idx[...]]
@@ -211,14 +257,14 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
     if (k > 0) {
         const uint16_t* wr = L.ww + (int64_t)(brow + rloc) * k;
         const uint16_t* xm = L.x + (int64_t)min(l16, M - 1) * K;
-        for (int cs = 0; cs < k; cs += 32) {
+        for (int cs2 = 0; cs2 < k; cs2 += 32) {
             uint32_t bw[4], aw[4];
 #pragma unroll
             for (int e2 = 0; e2 < 4; e2++) {
                 uint32_t wv[2], xv[2];
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
-                    const int c = cs + 8 * qd + 2 * e2 + h;
+                    const int c = cs2 + 8 * qd + 2 * e2 + h;
                     const bool on = c < k;
                     int j = L.idx[min(c, k - 1)];
                     j = (j >= 0 && j < K) ? j : 0;
@@ -243,15 +289,12 @@ __global__ __launch_bounds__(256) void k_mfv(MfvBatch b, int M)
                 L.y[(int64_t)m * N + brow + row] = f2h(acc[r]);
         }
     }
-    // the last steps' x loads may still be in flight: none may write this
-    // block's LDS after the block has ended
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int U, int MC>
+template <int U, int MC, int W, int S>
 hipError_t launch_shape(const MfvBatch& b, int nblocks, int M, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_mfv<U, MC>), dim3(nblocks), dim3(256), 0, s, b, M);
+    hipLaunchKernelGGL((k_mfv<U, MC, W, S>), dim3(nblocks), dim3(64 * W * S), 0, s, b, M);
     return hipGetLastError();
 }
 
@@ -284,6 +327,10 @@ hipError_t launch_mfv(const LinearDesc* d, int count, int M, hipStream_t s)
             order[c] = order[c - 1];
             order[c - 1] = t;
         }
+    // up to 4 tokens: blocks of 2 row waves x 2 K groups (the 4096 x 11008
+    // blocks then finish with the rest); more tokens: 4 row waves over the whole
+    // row (the 16-token x stages leave LDS for no second K group)
+    const int W = M <= 4 ? 2 : 4;
     MfvBatch b{};
     int nblocks = 0;
     for (int o = 0; o < count; o++) {
@@ -300,11 +347,11 @@ hipError_t launch_mfv(const LinearDesc* d, int count, int M, hipStream_t s)
         L.K = (int32_t)dl.K;
         L.k = dl.k;
         L.block0 = nblocks;
-        nblocks += (int)((dl.N + kRowsPerBlock - 1) / kRowsPerBlock);
+        nblocks += (int)((dl.N + 16 * W - 1) / (16 * W));
     }
     if (M <= 4)
-        return launch_shape<4, 4>(b, nblocks, M, s);
-    return launch_shape<4, 16>(b, nblocks, M, s);
+        return launch_shape<4, 4, 2, 2>(b, nblocks, M, s);
+    return launch_shape<4, 16, 4, 1>(b, nblocks, M, s);
 }
 
 }  // namespace owq
