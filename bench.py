@@ -22,6 +22,12 @@ recorded on the launch stream around the R back-to-back decode launches of each
 timed step. The other stages are timed with events around each launch and
 reported under "kernels", each against its own roofline.
 
+After the timed steps it also reports, each under its own key: the decode batch
+sweep (M = 1, 2, 4, 8, 16), the same M = 1 decode as one launch per linear
+replayed from a HIP graph, a 1 GiB device-copy rate, and calibration at
+T = 8192 on the two MLP shapes (flags --no-sweep, --no-extras and
+--no-long-calibration skip them, e.g. under a profiler).
+
 --copy-reference adds, after the timed steps, three copies of a 512 MiB buffer
 (a plain copy kernel of known size) so that hardware-counter runs of this script
 can scale FETCH_SIZE / WRITE_SIZE to bytes.
@@ -132,6 +138,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-sweep", action="store_true", help="skip the decode batch sweep")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-linear decode from a HIP graph and the device-copy rate (their "
+                         "dispatches, of other sizes, would mix into a profiler's per-kernel averages)")
     ap.add_argument("--no-long-calibration", action="store_true",
                     help="skip the long-calibration (T = 8192) timing")
     ap.add_argument("--copy-reference", action="store_true",
@@ -312,6 +321,7 @@ def main():
                                "path": "k_gemv, one launch" if M <= 2 else "k_mfv, one launch"}
         result["decode_batch_sweep"] = sweep
 
+    if not args.no_extras:
         # the same decode as 7 launches per layer (one per linear), recorded in a HIP graph
         print("bench: decode as per-linear launches in a graph", file=sys.stderr, flush=True)
         side = torch.cuda.Stream()
