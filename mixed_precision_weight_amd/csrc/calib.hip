@@ -45,21 +45,15 @@ struct SqElem {  // x^2 (exact in fp32 for fp16 x)
 struct ErrElem {  // dW = w - s (q - z), exact in fp32; squared in fp64 by the caller
     const uint16_t* s16;
     const uint8_t* z;
-    struct Row {
-        float s, rs, hs, zf;  // step, ~1/step, step/2, zero point
-    };
-    __device__ __forceinline__ Row load_row(int64_t r) const
-    {
-        const float sf = h2f(s16[r]);
-        return Row{sf, __builtin_amdgcn_rcpf(sf), 0.5f * sf, (float)z[r]};
-    }
+    typedef RtnRow Row;
+    __device__ __forceinline__ Row load_row(int64_t r) const { return make_rtn_row(h2f(s16[r]), z[r]); }
     __device__ __forceinline__ float val(const Row& rw, uint16_t h) const
     {
         // the residual against the (possibly clamped) grid point, exact: every
         // weight lies inside the row's full-row fit range, so |w / s| <= 8 and the
         // product of the offset and the 11-bit step has at most 14 bits
         const float w = h2f(h);
-        return __builtin_fmaf(-grid_offset(w, rw.s, rw.rs, rw.hs, rw.zf), rw.s, w);
+        return __builtin_fmaf(-grid_offset(w, rw), rw.s, w);
     }
     static constexpr bool kSquared = false;
 };

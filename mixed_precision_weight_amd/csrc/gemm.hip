@@ -464,15 +464,24 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2,
     };
 
     QRegs qa, qb, qc3;
+    // the prologue issues x and codes chunk by chunk, in the order the steps
+    // do, so the waits inserted for the code registers count the same loads on
+    // the first pass through the loop as on the others
     dma(0, xs0);
     load_q(0, qa);
+    asm volatile("" ::: "memory");
     dma(1, xs1);
     load_q(1, qb);
+    asm volatile("" ::: "memory");
     for (int c = 0; c < nchunks; c += 3) {
         step(c, xs0, xs2, qa, qc3);
         step(c + 1, xs1, xs0, qb, qa);
         step(c + 2, xs2, xs1, qc3, qb);
     }
+    // the last steps' x loads (duplicates of the last chunk) may still be in
+    // flight: none may write LDS after the block has ended (waited here, so the
+    // block need not wait for its output stores)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // row step, then the weak columns
 #pragma unroll
@@ -541,9 +550,6 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2,
                     a.y[(int64_t)m * N + n] = f2h(acc[i][f][r]);
             }
         }
-    // the last steps' x loads (duplicates of the last chunk) may still be in
-    // flight: none may write this block's LDS after the block has ended
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int FM, int FN, int WM, int WN>

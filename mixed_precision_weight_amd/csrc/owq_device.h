@@ -44,37 +44,54 @@ __device__ __forceinline__ void qparams_from_range(float lo, float hi, uint16_t&
     s16 = s;
 }
 
-// rint(w / s), round half to even, for a positive fp16 step s and an fp16 weight
-// w, with neither an IEEE division nor a branch (rs ~ 1/s, within a few ulps,
-// hs = s / 2). The guess t = rint(w rs) is at most one off, and only when w / s
-// lies within a few ulps of a half-integer. e = w - t s is exact after one FMA
-// (t s has at most 16 significant bits and e stays within a step of 0), so |e|
-// against s/2 classifies the quotient t + e/s exactly: below, t; above, t + 1
-// toward e; equal, the exact half-integer t +- 1/2, which rint takes to the even
-// neighbour. The quotient of two fp16 values is never within half an fp32 ulp
-// of a half-integer without being equal to it, so the result equals rint of the
-// correctly rounded fp32 quotient, as in the definition. The guess is clamped
-// to +-16; beyond that only the side matters to the callers' clamp.
-__device__ __forceinline__ float rint_quotient(float w, float s, float rs, float hs)
+// Per-row constants of the round-to-nearest step for a positive fp16 step s
+// and zero point z.
+struct RtnRow {
+    float s;       // step
+    float rs;      // ~1/s (hardware reciprocal, within a few ulps)
+    float hs;      // s / 2
+    float tie;     // 2^14 rs: scales the distance to s / 2, see rint_quotient
+    float lo, hi;  // -z and 7 - z: the range of code - z
+    float zf;      // z
+};
+
+__device__ __forceinline__ RtnRow make_rtn_row(float s, int z)
 {
-    const float t = fminf(fmaxf(rintf(w * rs), -16.0f), 16.0f);
-    const float e = __builtin_fmaf(-t, s, w);
-    const float a = fabsf(e);
-    const float f = a > hs ? 1.0f : (a == hs ? 0.5f : 0.0f);
+    const float rs = __builtin_amdgcn_rcpf(s);
+    return RtnRow{s, rs, 0.5f * s, 16384.0f * rs, -(float)z, 7.0f - (float)z, (float)z};
+}
+
+// rint(w / s), round half to even, for an fp16 weight w, with neither an IEEE
+// division nor a compare. The guess t = rint(w rs) differs from w / s by at
+// most 4e-6 for |w / s| <= 16, and a quotient of two fp16 values is either a
+// half-integer or at least 2^-13 away from one (its distance to h + 1/2 is a
+// multiple of an ulp of w or s over 2s). So t is the nearest integer, and
+// e = w - t s (exact after one FMA: t s has at most 16 significant bits) has
+// |e| < s / 2, except at an exact half-integer, where |e| = s / 2 and t may be
+// the odd neighbour. d = s / 2 - |e| is then 0, and at least s 2^-13 in every
+// other case, so f = max(1/2 - 2^14 d / s, 0) is 1/2 at a tie and 0 otherwise,
+// and rint(t + copysign(f, e)) takes a tie to the even neighbour. The guess is
+// clamped to +-16; beyond that (where |e| may exceed s / 2 and f 1/2) only the
+// side matters to the callers' clamp.
+__device__ __forceinline__ float rint_quotient(float w, const RtnRow& r)
+{
+    const float t = __builtin_amdgcn_fmed3f(rintf(w * r.rs), -16.0f, 16.0f);
+    const float e = __builtin_fmaf(-t, r.s, w);
+    const float d = r.hs - fabsf(e);
+    const float f = fmaxf(__builtin_fmaf(-d, r.tie, 0.5f), 0.0f);
     return rintf(t + __builtin_copysignf(f, e));
 }
 
-// Grid offset of w: clamp(rint(w / s) + z, 0, 7) - z, as a float (rs ~ 1/s,
-// hs = s / 2, zf = z).
-__device__ __forceinline__ float grid_offset(float w, float s, float rs, float hs, float zf)
+// Grid offset of w: clamp(rint(w / s) + z, 0, 7) - z, as a float.
+__device__ __forceinline__ float grid_offset(float w, const RtnRow& r)
 {
-    return fminf(fmaxf(rint_quotient(w, s, rs, hs) + zf, 0.0f), 7.0f) - zf;
+    return __builtin_amdgcn_fmed3f(rint_quotient(w, r), r.lo, r.hi);
 }
 
 // The 3-bit code of w.
-__device__ __forceinline__ int rtn_code(float w, float s, float rs, float hs, float zf)
+__device__ __forceinline__ int rtn_code(float w, const RtnRow& r)
 {
-    return (int)(grid_offset(w, s, rs, hs, zf) + zf);
+    return (int)(grid_offset(w, r) + r.zf);
 }
 
 // ---------------------------------------------------------- wave reductions --

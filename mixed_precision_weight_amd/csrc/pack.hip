@@ -94,8 +94,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
         uint16_t s16;
         int z;
         qparams_from_range(lo, hi, s16, z);
-        const float sf = h2f(s16);
-        const float rs = __builtin_amdgcn_rcpf(sf), hs = 0.5f * sf, zf = (float)z;
+        const RtnRow rr = make_rtn_row(h2f(s16), z);
 #pragma unroll
         for (int u = 0; u < GPT; u++) {
             int64_t g = tid + 256 * u;
@@ -103,7 +102,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
                 uint32_t o[3] = {0u, 0u, 0u};
 #pragma unroll
                 for (int c = 0; c < 32; c++) {
-                    uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), sf, rs, hs, zf);
+                    uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), rr);
                     const int pos = 3 * kSlot[c], wd = pos >> 5, off = pos & 31;
                     o[wd] |= cd << off;
                     if (off > 29)
@@ -194,15 +193,14 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint16_t* __restrict__ W, 
         uint16_t s16;
         int z;
         qparams_from_range(lo, hi, s16, z);
-        const float sf = h2f(s16);
-        const float rs = __builtin_amdgcn_rcpf(sf), hs = 0.5f * sf, zf = (float)z;
+        const RtnRow rr = make_rtn_row(h2f(s16), z);
 #pragma unroll
         for (int u = 0; u < GPW; u++) {
             const int g = lane + 64 * u;
             uint32_t o[3] = {0u, 0u, 0u};
 #pragma unroll
             for (int c = 0; c < 32; c++) {
-                const uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), sf, rs, hs, zf);
+                const uint32_t cd = (uint32_t)rtn_code(h2f((uint16_t)(v[u][c >> 1] >> (16 * (c & 1)))), rr);
                 const int pos = 3 * kSlot[c], wd = pos >> 5, off = pos & 31;
                 o[wd] |= cd << off;
                 if (off > 29)
