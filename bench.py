@@ -147,7 +147,7 @@ def main():
                     help="end with three 512 MiB device copies (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the hot path runs on one GPU's share of a layer; multi-GPU sharding is design only)",
               file=sys.stderr)
         sys.exit(2)
@@ -372,25 +372,31 @@ def main():
         # long calibration (T = 8192 tokens) at the MLP shapes: X and W read once
         print("bench: long calibration", file=sys.stderr, flush=True)
         c4 = synth.CONFIGS[4]
-        long_cal = {}
+        long_cal, long_sel = {}, {}
         for li, s in enumerate(c4.layers):
             seed = c4.seed(li)
             Wl = torch.from_numpy(synth.weights(s, seed)).to(dev)
             Xl = torch.from_numpy(synth.calibration(s, seed, c4.T)).to(dev)
             wsl = torch.empty(owq.calibrate_workspace_bytes(s.N, s.K, c4.T), dtype=torch.uint8, device=dev)
-            owq.calibrate(Wl, Xl, workspace=wsl)
+            _, score_l = owq.calibrate(Wl, Xl, workspace=wsl)
+            owq.select_weak(score_l, s.k)
             reps = 5
-            evl = [(E(), E()) for _ in range(reps)]
+            evl = [(E(), E(), E()) for _ in range(reps)]
             for r in range(reps):
                 evl[r][0].record()
-                owq.calibrate(Wl, Xl, workspace=wsl)
+                _, score_l = owq.calibrate(Wl, Xl, workspace=wsl)
                 evl[r][1].record()
+                owq.select_weak(score_l, s.k)
+                evl[r][2].record()
             torch.cuda.synchronize()
-            t = float(np.median([a.elapsed_time(b) for a, b in evl])) / 1e3
-            long_cal[f"{s.name} {s.N}x{s.K} T={c4.T}"] = hbm_entry(calib_bytes(s.N, s.K, c4.T), t,
-                                                                     "k_colsum x2 + k_rowfit + k_finalize")
+            t = float(np.median([a.elapsed_time(b) for a, b, _ in evl])) / 1e3
+            ts = float(np.median([b.elapsed_time(c) for _, b, c in evl])) / 1e3
+            key = f"{s.name} {s.N}x{s.K} T={c4.T}"
+            long_cal[key] = hbm_entry(calib_bytes(s.N, s.K, c4.T), t, "k_colsum x2 + k_rowfit + k_finalize")
+            long_sel[key] = {"what": f"top-{s.k} of K = {s.K}", "us": round(ts * 1e6, 2), "bound": "latency"}
             del Wl, Xl, wsl
         result["kernels"]["calibrate_score_long"] = long_cal
+        result["kernels"]["select_weak_long"] = long_sel
 
     if args.copy_reference:
         n = 512 << 20
