@@ -94,7 +94,8 @@ size_t owq_calibrate_workspace_bytes(int64_t N, int64_t K, int64_t T);
  * diagonal element ([PL] "Weak-column selection" (paper p.4)).
  * W: fp16 [N][K]; X: fp16 [T][K]; lambda, score: fp64 [K] (outputs; may not alias).
  * workspace: device scratch of >= owq_calibrate_workspace_bytes(N, K, T) bytes,
- * 256-byte aligned; its contents on entry are ignored.
+ * 256-byte aligned; its contents on entry are ignored. Two calls may share a
+ * workspace only if they are ordered (e.g. on one stream).
  * Results are bitwise deterministic for given inputs. */
 owq_status owq_calibrate_score(const uint16_t* W, int64_t N, int64_t K,
                                const uint16_t* X, int64_t T,

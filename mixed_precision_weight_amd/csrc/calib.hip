@@ -17,7 +17,7 @@
 // w*8 + l/8 + 32 t, so each wave instruction reads 8 full 128-byte lines. Squares
 // of fp16 values and of the (exact) fp32 RTN errors are accumulated in fp64; the
 // 32 row phases are combined by a fixed butterfly and a fixed-order LDS sum,
-// and row slices by a fixed-order second pass: results are bitwise deterministic.
+// and row slices by a fixed-order final pass: results are bitwise deterministic.
 //
 // Built with -ffp-contract=off: the quantiser steps are single IEEE operations.
 #include "owq_device.h"
@@ -58,19 +58,19 @@ struct ErrElem {  // dW = w - s (q - z), exact in fp32; squared in fp64 by the c
     static constexpr bool kSquared = false;
 };
 
+// Column sums of one 64-column tile over one row slice, into partial[slice][.]
 template <class Elem>
-__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ A, int64_t R, int64_t K,
-                                                int64_t rows_per_slice, double* __restrict__ partial,
-                                                Elem elem)
+__device__ __forceinline__ void colsum_tile(const uint16_t* __restrict__ A, int64_t R, int64_t K,
+                                            int64_t rows_per_slice, double* __restrict__ partial, Elem elem,
+                                            int64_t tile, int64_t slice, double (&red)[4][kTileCols])
 {
-    __shared__ double red[4][kTileCols];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cc = lane & 7;
     const int phase = wave * 8 + (lane >> 3);
-    const int64_t col = (int64_t)blockIdx.x * kTileCols + cc * 8;
+    const int64_t col = tile * kTileCols + cc * 8;
     const bool active = col < K;
     const int64_t colc = active ? col : 0;  // loads stay in bounds; inactive lanes add nothing
-    const int64_t r0 = (int64_t)blockIdx.y * rows_per_slice;
+    const int64_t r0 = slice * rows_per_slice;
     const int64_t r1 = min(R, r0 + rows_per_slice);
 
     double acc[8];
@@ -119,23 +119,23 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ A, 
     }
     __syncthreads();
     if (threadIdx.x < kTileCols) {
-        int64_t j = (int64_t)blockIdx.x * kTileCols + threadIdx.x;
+        int64_t j = tile * kTileCols + threadIdx.x;
         if (j < K) {
             double t = red[0][threadIdx.x];
             t += red[1][threadIdx.x];
             t += red[2][threadIdx.x];
             t += red[3][threadIdx.x];
-            partial[(int64_t)blockIdx.y * K + j] = t;
+            partial[slice * K + j] = t;
         }
     }
 }
 
 // One wave per row: min/max over all K columns -> (fp16 step, zero point).
-__global__ __launch_bounds__(256) void k_rowfit(const uint16_t* __restrict__ W, int64_t N, int64_t K,
-                                                uint16_t* __restrict__ s16, uint8_t* __restrict__ z)
+__device__ __forceinline__ void rowfit_rows(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                            uint16_t* __restrict__ s16, uint8_t* __restrict__ z, int64_t blk)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = blk * 4 + (threadIdx.x >> 6);
     if (row >= N)
         return;
     const uint4* p = reinterpret_cast<const uint4*>(W + row * K);
@@ -169,6 +169,33 @@ __global__ __launch_bounds__(256) void k_rowfit(const uint16_t* __restrict__ W, 
     }
 }
 
+// First launch: the X column sums (lambda partials) and the W row fits run as
+// one grid, tile-major X blocks first.
+__global__ __launch_bounds__(256) void k_calib_first(const uint16_t* __restrict__ X, int64_t T, int64_t K,
+                                                     int64_t rows_x, double* __restrict__ px, int64_t tiles,
+                                                     int64_t nx, const uint16_t* __restrict__ W, int64_t N,
+                                                     uint16_t* __restrict__ s16, uint8_t* __restrict__ z)
+{
+    __shared__ double red[4][kTileCols];
+    const int64_t b = blockIdx.x;
+    if (b < nx)
+        colsum_tile(X, T, K, rows_x, px, SqElem{}, b % tiles, b / tiles, red);
+    else
+        rowfit_rows(W, N, K, s16, z, b - nx);
+}
+
+// Second launch: the RTN-error column sums over (tile, slice) blocks.
+__global__ __launch_bounds__(256) void k_colsum_err(const uint16_t* __restrict__ W, int64_t N, int64_t K,
+                                                    int64_t rows_w, double* __restrict__ pw, ErrElem elem)
+{
+    __shared__ double red[4][kTileCols];
+    colsum_tile(W, N, K, rows_w, pw, elem, blockIdx.x, blockIdx.y, red);
+}
+
+// Third launch: lambda_j = 2 sum_s px[s][j], e_j = sum_s pw[s][j] (slices in
+// order), score_j = lambda_j e_j. A separate launch: the slice partials come
+// from blocks on all eight XCDs, whose L2 caches a device-wide fence would have
+// to write back and invalidate.
 __global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ px, int64_t sx,
                                                   const double* __restrict__ pw, int64_t sw, int64_t K,
                                                   double* __restrict__ lambda, double* __restrict__ score)
@@ -236,13 +263,14 @@ hipError_t launch_calibrate(const uint16_t* W, int64_t N, int64_t K, const uint1
     uint8_t* z = reinterpret_cast<uint8_t*>(base + p.off_z);
     const unsigned tiles = (unsigned)((K + kTileCols - 1) / kTileCols);
 
-    hipLaunchKernelGGL(k_colsum<SqElem>, dim3(tiles, (unsigned)p.sx), dim3(256), 0, s, X, T, K,
-                       p.rows_x, px, SqElem{});
-    hipLaunchKernelGGL(k_rowfit, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, W, N, K, s16, z);
-    hipLaunchKernelGGL(k_colsum<ErrElem>, dim3(tiles, (unsigned)p.sw), dim3(256), 0, s, W, N, K,
-                       p.rows_w, pw, ErrElem{s16, z});
-    hipLaunchKernelGGL(k_finalize, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, px, p.sx, pw,
-                       p.sw, K, lambda, score);
+    const int64_t nx = (int64_t)tiles * p.sx;
+    const int64_t nrow = (N + 3) / 4;
+    hipLaunchKernelGGL(k_calib_first, dim3((unsigned)(nx + nrow)), dim3(256), 0, s, X, T, K, p.rows_x, px,
+                       (int64_t)tiles, nx, W, N, s16, z);
+    hipLaunchKernelGGL(k_colsum_err, dim3(tiles, (unsigned)p.sw), dim3(256), 0, s, W, N, K, p.rows_w, pw,
+                       ErrElem{s16, z});
+    hipLaunchKernelGGL(k_finalize, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, px, p.sx, pw, p.sw, K,
+                       lambda, score);
     return hipGetLastError();
 }
 
