@@ -49,11 +49,17 @@ struct ErrElem {  // dW = w - s (q - z), exact in fp32; squared in fp64 by the c
     __device__ __forceinline__ Row load_row(int64_t r) const { return make_rtn_row(h2f(s16[r]), z[r]); }
     __device__ __forceinline__ float val(const Row& rw, uint16_t h) const
     {
-        // the residual against the (possibly clamped) grid point, exact: every
+        // The residual against the (possibly clamped) grid point, exact: every
         // weight lies inside the row's full-row fit range, so |w / s| <= 8 and the
-        // product of the offset and the 11-bit step has at most 14 bits
+        // product of the offset and the 11-bit step has at most 14 bits. The
+        // rounded quotient t = rint(w rs) is rint(w / s) except possibly at an
+        // exact half-integer (see rint_quotient), where both neighbours leave
+        // |residual| = s / 2, and the clamp to the code range maps an
+        // out-of-range neighbour onto the in-range one; the squared residual is
+        // therefore the same as with the tie rounded to even.
         const float w = h2f(h);
-        return __builtin_fmaf(-grid_offset(w, rw), rw.s, w);
+        const float q = __builtin_amdgcn_fmed3f(rintf(w * rw.rs), rw.lo, rw.hi);
+        return __builtin_fmaf(-q, rw.s, w);
     }
     static constexpr bool kSquared = false;
 };
