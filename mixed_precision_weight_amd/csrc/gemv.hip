@@ -71,9 +71,9 @@ __device__ __forceinline__ void store_group(const uint4 (&v)[4], uint4* __restri
 
 // ------------------------------------------------------------------ kernel --
 constexpr int kChunkTiles = 2;  // 64-group tiles per K chunk (4096 columns)
-// Rows per wavefront: four keeps enough code bytes in flight at every M (measured
-// against two and eight rows at M = 1..4).
-__host__ __device__ constexpr int rows_per_wave(int) { return 4; }
+// Rows per wavefront: three (76 registers at M = 1, six waves per SIMD) was
+// faster than two, four (109 registers, four waves) and eight at M = 1 and 2.
+__host__ __device__ constexpr int rows_per_wave(int) { return 3; }
 
 __device__ __forceinline__ float f_of(uint32_t v) { return __builtin_bit_cast(float, v); }
 __device__ __forceinline__ uint32_t u_of(float v) { return __builtin_bit_cast(uint32_t, v); }
@@ -164,17 +164,23 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
                 cw[r][u] = __builtin_amdgcn_raw_buffer_load_b96(qr, vrow[r] + (g0 + 64 * u) * 12, 0, 0);
     };
 
+    // row steps and zero points first: they move to scalar registers below, and
+    // waiting for them then waits for nothing issued later
+    uint32_t sv[R], zv[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int row = min(row0 + r, N - 1);
+        sv[r] = b.L[li].s[row];
+        zv[r] = b.L[li].z[row];
+    }
+    asm volatile("" ::: "memory");  // keep them ahead of the chunk's loads
     issue_chunk(0, min(GC, G));
-    // row scale, zero point, weak weights; weak indices and x there
-    float sc[R];
-    uint32_t zr[R];
+    // weak weights; weak indices and x there
     float wwv[R][2];
     const int kc = k > 0 ? k : 1;  // with k == 0 the host passes valid dummy arrays
 #pragma unroll
     for (int r = 0; r < R; r++) {
         const int row = min(row0 + r, N - 1);
-        sc[r] = h2f(b.L[li].s[row]);
-        zr[r] = (uint32_t)b.L[li].z[row];
 #pragma unroll
         for (int v = 0; v < 2; v++) {
             const int c = lane + 64 * v;
@@ -193,6 +199,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
             const float xv = h2f(X[(int64_t)m * K + j]);
             xw[m][v] = c < k ? xv : 0.0f;
         }
+    }
+
+    float sc[R];
+    uint32_t zr[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        sc[r] = h2f((uint16_t)__builtin_amdgcn_readfirstlane((int)sv[r]));
+        zr[r] = (uint32_t)__builtin_amdgcn_readfirstlane((int)zv[r]);
     }
 
     const Magic mg = make_magic();
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
             if (g < gc) {
 #pragma unroll
                 for (int r = 0; r < R; r++) {
-                    const ZeroSub nz = make_zero_sub((uint32_t)__builtin_amdgcn_readfirstlane((int)zr[r]));
+                    const ZeroSub nz = make_zero_sub(zr[r]);
                     uint32_t p[16];
                     decode_group(cw[r][u].x, cw[r][u].y, cw[r][u].z, mg, nz, p);
 #pragma unroll
