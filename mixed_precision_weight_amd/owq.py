@@ -117,9 +117,15 @@ def calibrate(W: torch.Tensor, X: torch.Tensor, workspace: torch.Tensor | None =
     return lam, score
 
 
-def select_weak(score: torch.Tensor, k: int, stream=None) -> torch.Tensor:
+def select_weak(score: torch.Tensor, k: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Indices of the k largest scores, ascending (int32 [k]); written to out if given."""
     _dev(score, torch.float64, "score")
-    out = torch.empty(max(k, 1), dtype=torch.int32, device=score.device)
+    if out is None:
+        out = torch.empty(max(k, 1), dtype=torch.int32, device=score.device)
+    else:
+        _dev(out, torch.int32, "out")
+        if out.numel() < k:
+            raise ValueError(f"out holds {out.numel()} indices, k = {k}")
     _check(lib().owq_select_weak(_ptr(score), score.numel(), int(k), _ptr(out) if k else None,
                                  _stream(stream)), "owq_select_weak")
     return out[:k]
@@ -182,3 +188,31 @@ def linear_batched(layers: list, xs: list, ys: list | None = None, stream=None) 
     yp = (_P * n)(*[y.data_ptr() for y in ys])
     _check(lib().owq_linear_batched(Ls, xp, yp, n, M, _stream(stream)), "owq_linear_batched")
     return ys
+
+
+class PreparedBatched:
+    """One owq_linear_batched call with its argument arrays built once.
+
+    For decode loops that launch the same layers on the same buffers again and
+    again: each call then only crosses into the library (which still checks the
+    arguments) instead of rebuilding the layer structs and pointer arrays. The
+    tensors must stay alive, at the same addresses, while the object is used.
+    """
+
+    def __init__(self, layers: list, xs: list, ys: list, stream=None):
+        n = len(layers)
+        for x in xs:
+            _dev(x, torch.float16, "x")
+        for y in ys:
+            _dev(y, torch.float16, "y")
+        self._keep = (list(layers), list(xs), list(ys))
+        self.Ls = (OwqLayer * n)(*[layer_struct(l) for l in layers])
+        self.xp = (_P * n)(*[x.data_ptr() for x in xs])
+        self.yp = (_P * n)(*[y.data_ptr() for y in ys])
+        self.n = n
+        self.M = xs[0].shape[0]
+        self.stream = _stream(stream)
+        self.fn = lib().owq_linear_batched
+
+    def __call__(self):
+        _check(self.fn(self.Ls, self.xp, self.yp, self.n, self.M, self.stream), "owq_linear_batched")

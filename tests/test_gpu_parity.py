@@ -127,6 +127,13 @@ def test_select_exact(owq, K, k):
     score[rng.integers(0, K, K // 10 + 1)] = 0.0
     got = host(owq.select_weak(dev(score), k))
     assert np.array_equal(got, oracle.select_weak(score, k))
+    if K == 4096:  # into a caller's buffer: the indices land there
+        import torch
+        out = torch.full((k + 3,), -1, dtype=torch.int32, device="cuda:0")
+        r = owq.select_weak(dev(score), k, out=out)
+        assert r.data_ptr() == out.data_ptr()
+        assert np.array_equal(host(out)[:k], oracle.select_weak(score, k))
+        assert (host(out)[k:] == -1).all()
 
 
 def test_select_ties(owq):

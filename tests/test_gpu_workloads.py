@@ -58,9 +58,14 @@ def test_llama7b_layer_batched_launch(owq):
         xs.append(x)
         singles.append(owq.linear(p, x))
     ys = owq.linear_batched(layers, xs)
+    yp = [torch.zeros_like(y) for y in ys]
+    call = owq.PreparedBatched(layers, xs, yp)  # arguments marshalled once, called twice
+    call()
+    call()
     torch.cuda.synchronize()
-    for a, b in zip(ys, singles):
+    for a, b, c in zip(ys, singles, yp):
         assert host(a).tobytes() == host(b).tobytes()
+        assert host(c).tobytes() == host(b).tobytes()
     # and the batched outputs meet the oracle bound
     o = oracle.pack(synth.weights(cfg.layers[6], cfg.seed(6)), host(layers[6]["weak_idx"]))
     yr, bnd = oracle.linear_full(o, host(xs[6]))
