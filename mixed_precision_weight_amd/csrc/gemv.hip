@@ -19,7 +19,7 @@
 // at the branch merge). The hardware overlaps the arithmetic of resident blocks
 // with the loads of others. Layers of any K share the kernel, so the decode of a
 // whole decoder layer (several linears) is one launch. Rows finish with a
-// 64-lane reduction of four rows at once (lane-half swaps, then DPP).
+// 64-lane reduction of up to four rows at once (lane-half swaps, then DPP).
 //
 // Each 12-byte group is decoded in registers (owq_decode.h) to sixteen exact
 // (q_a - z, q_b - z) fp16 pairs of consecutive columns, and one v_dot2_f32_f16
@@ -55,18 +55,14 @@ struct GemvBatch {
 };
 
 // Staged x layout (uint4 units): [m][tile u][quad qd][lane l] for group g = 64 u + l,
-// so a lane's four quads of a tile are 1 KB apart (immediate offsets) and the
-// lanes of a wave read consecutive 16-byte words.
-__device__ __forceinline__ int xs_index(int m, int T, int g) { return ((m * T + (g >> 6)) << 8) + (g & 63); }
-
-// Element-wise copies: a whole-struct copy out of the staging array makes the
-// compiler keep that array in scratch memory, whose reload waits for every load
-// in flight, code tiles included.
-__device__ __forceinline__ void store_group(const uint4 (&v)[4], uint4* __restrict__ xs_mg)
+// so a lane's four quads of a tile are at immediate offsets and the lanes of a
+// wave read consecutive 16-byte words. The quads are 68 slots apart: the
+// staging writes, which take consecutive 16-byte pieces of x (group g / 4, quad
+// g % 4 per lane), then spread over all 64 banks.
+constexpr int kQuadStride = 68;
+__device__ __forceinline__ int xs_slot(int m, int T, int g, int qd)
 {
-#pragma unroll
-    for (int qd = 0; qd < 4; qd++)
-        xs_mg[qd * 64] = make_uint4(v[qd].x, v[qd].y, v[qd].z, v[qd].w);
+    return (m * T + (g >> 6)) * (4 * kQuadStride) + qd * kQuadStride + (g & 63);
 }
 
 // ------------------------------------------------------------------ kernel --
@@ -140,22 +136,21 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
     for (int r = 0; r < R; r++)
         vrow[r] = (wave * R + r) * G * 12 + lane * 12;
 
-    constexpr int XI = (M * GC + 255) / 256;  // staged groups per thread
-    uint4 xg[XI][4];
+    constexpr int PC = 4 * GC;        // 16-byte pieces of x per token and chunk
+    constexpr int XP = M * PC / 256;  // staged pieces per thread
+    uint4 xg[XP];
     u32x3 cw[R][TT];
     // Every load below is unconditional (indices clamped to valid data): a load
     // under a divergent branch makes the compiler wait for it before the branch
     // merges, which would serialise the x latency in front of the code loads.
-    // staging item i = m * GC + g (GC a power of two): token m, group g of the chunk
+    // Staging item i = m PC + p: token m, piece p of the chunk (consecutive
+    // threads read consecutive 16 bytes of x).
     auto issue_chunk = [&](int g0, int gc) {
 #pragma unroll
-        for (int t = 0; t < XI; t++) {
+        for (int t = 0; t < XP; t++) {
             const int i = tid + 256 * t;
-            const int m = min(i / GC, M - 1), g = min(i % GC, gc - 1);
-            const uint4* src = reinterpret_cast<const uint4*>(X + m * K + (g0 + g) * 32);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; q4++)
-                xg[t][q4] = src[q4];
+            const int m = i / PC, pc = min(i % PC, 4 * gc - 1);
+            xg[t] = *reinterpret_cast<const uint4*>(X + m * K + g0 * 32 + pc * 8);
         }
 #pragma unroll
         for (int r = 0; r < R; r++)
@@ -224,10 +219,11 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
             issue_chunk(g0, gc);
         }
 #pragma unroll
-        for (int t = 0; t < XI; t++) {
+        for (int t = 0; t < XP; t++) {
             const int i = tid + 256 * t;
-            if (i / GC < M && i % GC < gc)
-                store_group(xg[t], smem + xs_index(i / GC, TT, i % GC));
+            const int pc = i % PC;
+            if (pc < 4 * gc)
+                smem[xs_slot(i / PC, TT, pc >> 2, pc & 3)] = make_uint4(xg[t].x, xg[t].y, xg[t].z, xg[t].w);
         }
         __syncthreads();
         // x of a tile is read from LDS once (all four quads in flight together)
@@ -240,7 +236,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
             for (int m = 0; m < M; m++)
 #pragma unroll
                 for (int qd = 0; qd < 4; qd++)
-                    xq[m][qd] = smem[xs_index(m, TT, g) + (qd << 6)];
+                    xq[m][qd] = smem[xs_slot(m, TT, g, qd)];
             if (g < gc) {
 #pragma unroll
                 for (int r = 0; r < R; r++) {
@@ -358,7 +354,7 @@ hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
         const int rows = 4 * rows_per_wave(M);
         nblocks += (int)((d[l].N + rows - 1) / rows);
     }
-    const size_t lds = (size_t)M * kChunkTiles * 64 * 4 * 16;
+    const size_t lds = (size_t)M * kChunkTiles * 4 * kQuadStride * 16;
     switch (M) {
     case 1: return launch_m<1>(b, nblocks, lds, s);
     case 2: return launch_m<2>(b, nblocks, lds, s);
