@@ -24,8 +24,9 @@
 // [token][group][32 values] and an A operand is one 128-bit LDS read per lane.
 // The K reduction happens inside the accumulators: no cross-lane reduction.
 //
-// Pipeline: x by direct-to-LDS loads into three stages and codes into three
-// register sets, two chunks ahead of the one computed, one barrier per chunk.
+// Pipeline: x by direct-to-LDS loads into D + 1 stages and codes into D + 1
+// register sets, D chunks ahead of the one computed (D = 1 or 2), one barrier
+// per chunk.
 // A block is W row waves (16 W rows of one layer) times S groups that split K;
 // one launch covers a batch of layers of any shapes.
 // Epilogue: row step, the weak columns as extra 32-deep MFMA steps (fp16 weak
@@ -93,19 +94,18 @@ __device__ __forceinline__ void dma_x(__amdgpu_buffer_rsrc_t r, char* lds, int v
 // accumulators to group 0 through LDS. This cuts the chain of dependent chunks
 // of a block by S, so the blocks of long-row layers do not run on alone after
 // the others have finished.
-template <int U, int MC, int W, int S>
+template <int U, int MC, int W, int S, int D>
 __global__ __launch_bounds__(64 * W * S) void k_mfv(MfvBatch b, int M)
 {
     using SH = MfvShape<U, MC>;
     constexpr int GC = SH::GC, RS = SH::RS, STAGE = SH::STAGE, PT = SH::PT;
     constexpr int DPW = MC * PT / W;  // x loads per wave and chunk
-    constexpr int D = 2;              // chunks in flight ahead of the one computed
     static_assert((MC * PT) % W == 0, "x loads must split evenly over the waves");
     constexpr int CRS = SH::CRS, CQ = SH::CQ, CL = SH::CL;
-    // three x stages per K group (chunks run two ahead), each its own array
+    // D + 1 x stages per K group (chunks run D ahead), each its own array
     __shared__ __attribute__((aligned(1024))) char xs0[S][STAGE];
     __shared__ __attribute__((aligned(1024))) char xs1[S][STAGE];
-    __shared__ __attribute__((aligned(1024))) char xs2[S][STAGE];
+    __shared__ __attribute__((aligned(1024))) char xs2[D == 2 ? S : 1][D == 2 ? STAGE : 16];
     __shared__ __attribute__((aligned(16))) char cs[W * S][16 * CRS];  // each wave's code chunk
     static_assert(S == 1 || (S - 1) * W * 64 * 16 <= STAGE * S, "partial sums must fit in one stage set");
 
@@ -218,16 +218,26 @@ __global__ __launch_bounds__(64 * W * S) void k_mfv(MfvBatch b, int M)
     // the prologue issues x and codes chunk by chunk, in the order the steps
     // do, so the waits inserted for the code registers count the same loads on
     // the first pass through the loop as on the others
-    dma(c0, xs0[kg]);
-    load_q(c0, qa);
-    asm volatile("" ::: "memory");
-    dma(c0 + 1, xs1[kg]);
-    load_q(c0 + 1, qb);
-    asm volatile("" ::: "memory");
-    for (int c = c0; c < c0 + per; c += 3) {  // the same trip count in every group
-        step(c, xs0[kg], xs2[kg], qa, qc3);
-        step(c + 1, xs1[kg], xs0[kg], qb, qa);
-        step(c + 2, xs2[kg], xs1[kg], qc3, qb);
+    if constexpr (D == 2) {
+        dma(c0, xs0[kg]);
+        load_q(c0, qa);
+        asm volatile("" ::: "memory");
+        dma(c0 + 1, xs1[kg]);
+        load_q(c0 + 1, qb);
+        asm volatile("" ::: "memory");
+        for (int c = c0; c < c0 + per; c += 3) {  // the same trip count in every group
+            step(c, xs0[kg], xs2[kg], qa, qc3);
+            step(c + 1, xs1[kg], xs0[kg], qb, qa);
+            step(c + 2, xs2[kg], xs1[kg], qc3, qb);
+        }
+    } else {
+        dma(c0, xs0[kg]);
+        load_q(c0, qa);
+        asm volatile("" ::: "memory");
+        for (int c = c0; c < c0 + per; c += 2) {
+            step(c, xs0[kg], xs1[kg], qa, qb);
+            step(c + 1, xs1[kg], xs0[kg], qb, qa);
+        }
     }
     // the last steps' x loads may still be in flight: none may write LDS after
     // this point (the stages are reused below, and the block may end)
@@ -291,10 +301,10 @@ __global__ __launch_bounds__(64 * W * S) void k_mfv(MfvBatch b, int M)
     }
 }
 
-template <int U, int MC, int W, int S>
+template <int U, int MC, int W, int S, int D>
 hipError_t launch_shape(const MfvBatch& b, int nblocks, int M, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_mfv<U, MC, W, S>), dim3(nblocks), dim3(64 * W * S), 0, s, b, M);
+    hipLaunchKernelGGL((k_mfv<U, MC, W, S, D>), dim3(nblocks), dim3(64 * W * S), 0, s, b, M);
     return hipGetLastError();
 }
 
@@ -349,9 +359,12 @@ hipError_t launch_mfv(const LinearDesc* d, int count, int M, hipStream_t s)
         L.block0 = nblocks;
         nblocks += (int)((dl.N + 16 * W - 1) / (16 * W));
     }
+    // x of up to 4 tokens: one chunk ahead (two stages: five waves per SIMD
+    // instead of four, 6 % faster); 16 tokens: two ahead (one ahead leaves more
+    // waves but was 3-6 % slower)
     if (M <= 4)
-        return launch_shape<4, 4, 2, 2>(b, nblocks, M, s);
-    return launch_shape<4, 16, 4, 1>(b, nblocks, M, s);
+        return launch_shape<4, 4, 2, 2, 1>(b, nblocks, M, s);
+    return launch_shape<4, 16, 4, 1, 2>(b, nblocks, M, s);
 }
 
 }  // namespace owq
