@@ -152,6 +152,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
             const int m = i / PC, pc = min(i % PC, 4 * gc - 1);
             xg[t] = *reinterpret_cast<const uint4*>(X + m * K + g0 * 32 + pc * 8);
         }
+        asm volatile("" ::: "memory");  // x ahead of the codes: its wait covers no code load
 #pragma unroll
         for (int r = 0; r < R; r++)
 #pragma unroll
@@ -168,11 +169,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
         sv[r] = b.L[li].s[row];
         zv[r] = b.L[li].z[row];
     }
+    const int kc = k > 0 ? k : 1;  // with k == 0 the host passes valid dummy arrays
+    int widx[2];  // weak indices: loaded early, so the gather's wait covers no code load
+#pragma unroll
+    for (int v = 0; v < 2; v++)
+        widx[v] = IDX[min(lane + 64 * v, kc - 1)];
     asm volatile("" ::: "memory");  // keep them ahead of the chunk's loads
     issue_chunk(0, min(GC, G));
-    // weak weights; weak indices and x there
+    // weak weights; x at the weak indices
     float wwv[R][2];
-    const int kc = k > 0 ? k : 1;  // with k == 0 the host passes valid dummy arrays
 #pragma unroll
     for (int r = 0; r < R; r++) {
         const int row = min(row0 + r, N - 1);
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
 #pragma unroll
     for (int v = 0; v < 2; v++) {
         const int c = lane + 64 * v;
-        int j = IDX[min(c, kc - 1)];
+        int j = widx[v];
         j = (j >= 0 && j < K) ? j : 0;
 #pragma unroll
         for (int m = 0; m < M; m++) {
