@@ -24,8 +24,9 @@ reported under "kernels", each against its own roofline.
 
 After the timed steps it also reports, each under its own key: the decode batch
 sweep (M = 1, 2, 4, 8, 16), the same M = 1 decode as one launch per linear
-replayed from a HIP graph, a 1 GiB device-copy rate, and calibration at
-T = 8192 on the two MLP shapes (flags --no-sweep, --no-extras and
+replayed from a HIP graph, the prefill products as plain fp16 GEMMs on the
+unquantised weights (torch, for comparison), a 1 GiB device-copy rate, and
+calibration at T = 8192 on the two MLP shapes (flags --no-sweep, --no-extras and
 --no-long-calibration skip them, e.g. under a profiler).
 
 --copy-reference adds, after the timed steps, three copies of a 512 MiB buffer
@@ -355,6 +356,26 @@ def main():
         result["kernels"]["decode_graph"] = hbm_entry(
             decode_bytes, t, f"k_gemv<1>, 7 launches per layer ({ROTATE} layers) replayed from a HIP graph")
         del g
+
+        # the same prefill products as plain fp16 GEMMs on the unquantised weights
+        # (torch / hipBLASLt), for comparison with the fused 3-bit kernel
+        ref = {}
+        for li, s in enumerate(specs):
+            for _ in range(3):
+                torch.nn.functional.linear(xp[li], W[li])
+            a, b = E(), E()
+            a.record()
+            for _ in range(5):
+                torch.nn.functional.linear(xp[li], W[li])
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3 / 5
+            ref[f"{s.name} {s.N}x{s.K}"] = round(2 * PREFILL_M * s.N * s.K / t / 1e12, 1)
+        tot = sum(2 * PREFILL_M * s.N * s.K for s in specs)
+        tt = sum(2 * PREFILL_M * s.N * s.K / (v * 1e12) for s, v in zip(specs, ref.values()))
+        result["kernels"]["prefill_fp16_gemm_reference"] = {
+            "what": "torch.nn.functional.linear on the fp16 weights (not the product path)",
+            "achieved": round(tot / tt / 1e12, 1), "unit": "TFLOP/s", "per_linear_tflops": ref}
 
         # measured device-copy rate over 1 GiB (read + write), for comparison with the 8 TB/s peak
         n = 1 << 30
