@@ -24,8 +24,8 @@ reported under "kernels", each against its own roofline.
 
 After the timed steps it also reports, each under its own key: the decode batch
 sweep (M = 1, 2, 4, 8, 16), the same M = 1 decode as one launch per linear
-replayed from a HIP graph, the prefill products as plain fp16 GEMMs on the
-unquantised weights (torch, for comparison), a 1 GiB device-copy rate, and
+replayed from a HIP graph, the M = 1 decode and the prefill products as plain
+fp16 products on the unquantised weights (torch, for comparison), a 1 GiB device-copy rate, and
 calibration at T = 8192 on the two MLP shapes (flags --no-sweep, --no-extras and
 --no-long-calibration skip them, e.g. under a profiler).
 
@@ -376,6 +376,24 @@ def main():
         result["kernels"]["prefill_fp16_gemm_reference"] = {
             "what": "torch.nn.functional.linear on the fp16 weights (not the product path)",
             "achieved": round(tot / tt / 1e12, 1), "unit": "TFLOP/s", "per_linear_tflops": ref}
+
+        # the M = 1 decode of the layer as fp16 matrix-vector products on the
+        # unquantised weights (torch), for the speed-up of the 3.1-bit format
+        for li in range(L):
+            torch.nn.functional.linear(xd[li], W[li])
+        a, b = E(), E()
+        a.record()
+        for _ in range(5):
+            for li in range(L):
+                torch.nn.functional.linear(xd[li], W[li])
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / 1e3 / 5
+        fp16_bytes = sum(2 * s.N * s.K + 2 * s.K for s in specs)
+        result["kernels"]["decode_fp16_gemv_reference"] = {
+            "what": "torch.nn.functional.linear at M = 1 on the fp16 weights, 7 launches (not the product path)",
+            "us": round(t * 1e6, 2), "achieved": round(fp16_bytes / t / 1e9, 1), "unit": "GB/s",
+            "speedup_of_owq_decode": round(t / dec_s, 2)}
 
         # measured device-copy rate over 1 GiB (read + write), for comparison with the 8 TB/s peak
         n = 1 << 30
