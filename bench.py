@@ -26,8 +26,9 @@ After the timed steps it also reports, each under its own key: the decode batch
 sweep (M = 1, 2, 4, 8, 16), the same M = 1 decode as one launch per linear
 replayed from a HIP graph, the M = 1 decode and the prefill products as plain
 fp16 products on the unquantised weights (torch, for comparison), a 1 GiB device-copy rate, and
-calibration at T = 8192 on the two MLP shapes (flags --no-sweep, --no-extras and
---no-long-calibration skip them, e.g. under a profiler).
+calibration at T = 8192 on the two MLP shapes, and the decode of the large
+shapes (8192 and 28672) at M = 1 and 8 (flags --no-sweep, --no-extras,
+--no-long-calibration and --no-large skip them, e.g. under a profiler).
 
 --copy-reference adds, after the timed steps, three copies of a 512 MiB buffer
 (a plain copy kernel of known size) so that hardware-counter runs of this script
@@ -142,6 +143,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the per-linear decode from a HIP graph and the device-copy rate (their "
                          "dispatches, of other sizes, would mix into a profiler's per-kernel averages)")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the decode timing of the large shapes (8192 and 28672)")
     ap.add_argument("--no-long-calibration", action="store_true",
                     help="skip the long-calibration (T = 8192) timing")
     ap.add_argument("--copy-reference", action="store_true",
@@ -441,6 +444,45 @@ def main():
             del Wl, Xl, wsl
         result["kernels"]["calibrate_score_long"] = long_cal
         result["kernels"]["select_weak_long"] = long_sel
+
+    if not args.no_large:
+        # decode of the large shapes (8192x8192, 28672x8192, 8192x28672) at M = 1
+        # and 8: calibrated and packed like the layer above, three copies rotated
+        # (3 x 210 MB) so the bytes come from HBM, one launch per copy
+        print("bench: large shapes", file=sys.stderr, flush=True)
+        c3 = synth.CONFIGS[3]
+        RL = 3
+        big = [[] for _ in range(RL)]
+        for li, s in enumerate(c3.layers):
+            seed = c3.seed(li)
+            Wl = torch.from_numpy(synth.weights(s, seed)).to(dev)
+            Xl = torch.from_numpy(synth.calibration(s, seed, c3.T)).to(dev)
+            wsl = torch.empty(owq.calibrate_workspace_bytes(s.N, s.K, c3.T), dtype=torch.uint8, device=dev)
+            _, score_l = owq.calibrate(Wl, Xl, workspace=wsl)
+            p = owq.pack(Wl, owq.select_weak(score_l, s.k))
+            for r in range(RL):
+                big[r].append(p if r == 0 else {key: v.clone() for key, v in p.items()})
+            del Wl, Xl, wsl, score_l
+        xb = [torch.from_numpy(synth.activations(s, c3.seed(li), 8)).to(dev) for li, s in enumerate(c3.layers)]
+        yb = [torch.empty((8, s.N), dtype=torch.float16, device=dev) for s in c3.layers]
+        large = {}
+        for M in (1, 8):
+            calls = [owq.PreparedBatched(big[r], [x[:M] for x in xb], [y[:M] for y in yb]) for r in range(RL)]
+            for r in range(RL):
+                calls[r]()
+            reps = 4 * RL
+            a, b = E(), E()
+            a.record()
+            for r in range(reps):
+                calls[r % RL]()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3 / reps
+            nb = sum(eff_bytes(s.N, s.K, s.k, M) for s in c3.layers)
+            large[f"M={M}"] = hbm_entry(nb, t, ("k_gemv" if M <= 2 else "k_mfv") +
+                                        ", 8192x8192 + 28672x8192 + 8192x28672 in one launch")
+        result["kernels"]["large_shapes_decode"] = large
+        del big, xb, yb
 
     if args.copy_reference:
         n = 512 << 20
