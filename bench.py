@@ -415,6 +415,52 @@ def main():
                                                    "frac": round(2 * n / t / 1e9 / HBM_PEAK_GBS, 4)}
         del src, dst
 
+        # measured read-only stream rates: torch.sum over 1 GiB, and over copies of the
+        # decode layer's size (one launch each, copies rotated so the last-level cache
+        # holds none of them), for comparison with the decode kernel's one launch
+        rd = {}
+        for label, nbytes, copies in (("1GiB", 1 << 30, 1), ("layer_size", decode_bytes, ROTATE)):
+            bufs = [torch.ones(nbytes // 2, dtype=torch.float16, device=dev) for _ in range(copies)]
+            for t_ in bufs:
+                torch.sum(t_)
+            reps = 8 * copies if copies > 1 else 5
+            a, b = E(), E()
+            a.record()
+            for r in range(reps):
+                torch.sum(bufs[r % copies])
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3 / reps
+            rd[label] = {"bytes": nbytes // 2 * 2, "us": round(t * 1e6, 2),
+                         "read_GBps": round(nbytes // 2 * 2 / t / 1e9, 1),
+                         "frac": round(nbytes // 2 * 2 / t / 1e9 / HBM_PEAK_GBS, 4)}
+            del bufs
+        result["kernels"]["hbm_read_reference"] = dict(
+            what="torch.sum over fp16 buffers (read-only stream, one launch per sum; not the product path)", **rd)
+
+        # the library's read-only stream at the decode kernel's geometry and the decode
+        # layer's size (one launch per copy, copies rotated): the rate one launch of
+        # this shape reaches when it does nothing with the bytes
+        sr = {}
+        for label, nbytes, copies in (("layer_size", decode_bytes // 12 * 12, ROTATE), ("1GiB", (1 << 30) // 12 * 12, 1)):
+            bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+            sinks = [owq.stream_read(b) for b in bufs]
+            reps = 8 * copies if copies > 1 else 5
+            a, b = E(), E()
+            a.record()
+            for r in range(reps):
+                owq.stream_read(bufs[r % copies], sinks[r % copies])
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3 / reps
+            sr[label] = {"bytes": nbytes, "us": round(t * 1e6, 2), "read_GBps": round(nbytes / t / 1e9, 1),
+                         "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+            del bufs, sinks
+        sr["decode_vs_layer_size_stream"] = round(value / sr["layer_size"]["read_GBps"], 4)
+        result["kernels"]["stream_read_reference"] = dict(
+            what="owq_stream_read: loads only, the M = 1 decode geometry (6 x 768 B per wavefront, 4-wave "
+                 "blocks), one launch per buffer (not the product path)", **sr)
+
     if not args.no_long_calibration:
         # long calibration (T = 8192 tokens) at the MLP shapes: X and W read once
         print("bench: long calibration", file=sys.stderr, flush=True)

@@ -168,6 +168,21 @@ owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs,
                               uint16_t* const* ys, int32_t count, int64_t M,
                               void* stream);
 
+/* ------------------------------------------------- measurement reference --- */
+
+/* Not a step of the method: a read-only HBM stream with the M = 1 decode
+ * kernel's geometry (wavefronts of 6 x 768 contiguous bytes, 12 bytes per lane
+ * per load), for reading the decode rate against a measured ceiling.
+ * src: device buffer of `bytes` bytes (12 <= bytes <= 2^40, bytes % 12 == 0,
+ * 4-byte aligned). sink: device uint32 [sink_words] (output), sink_words >=
+ * owq_stream_read_sink_words(bytes); word w receives the XOR of the 32-bit words
+ * of bytes [4608 w, 4608 (w + 1)) of src (the last one zero-padded). Returns
+ * OWQ_ERR_NULL, OWQ_ERR_SHAPE, OWQ_ERR_ALIGN or OWQ_ERR_RANGE (sink too short)
+ * before any launch. */
+int64_t owq_stream_read_sink_words(int64_t bytes);
+owq_status owq_stream_read(const void* src, int64_t bytes, uint32_t* sink,
+                           int64_t sink_words, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

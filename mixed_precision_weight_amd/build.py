@@ -32,7 +32,7 @@ NO_CONTRACT = {"calib.hip", "pack.hip"}
 RESOURCES = os.path.join(BUILD, "kernel_resources.json")
 _REMARK = re.compile(r"remark: +(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
                      r"Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]): (\S+)")
-SOURCES = ["api.cpp", "calib.hip", "topk.hip", "pack.hip", "gemv.hip", "mfv.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "calib.hip", "topk.hip", "pack.hip", "gemv.hip", "mfv.hip", "gemm.hip", "stream.hip"]
 
 
 def _resources(stderr: str) -> dict:

@@ -271,4 +271,20 @@ owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs, ui
     return hip_status(e, "owq_linear_batched launch");
 }
 
+int64_t owq_stream_read_sink_words(int64_t bytes) { return bytes > 0 ? owq::stream_read_sink_words(bytes) : 0; }
+
+owq_status owq_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words, void* stream)
+{
+    if (!src || !sink)
+        return fail(OWQ_ERR_NULL, "src and sink must be non-NULL");
+    if (bytes < 12 || bytes % 12 != 0 || bytes > ((int64_t)1 << 40))
+        return fail(OWQ_ERR_SHAPE, "bytes = %lld: need 12 <= bytes <= 2^40 and bytes %% 12 == 0", (long long)bytes);
+    if (!aligned(src, 4) || !aligned(sink, 4))
+        return fail(OWQ_ERR_ALIGN, "misaligned pointer (src and sink: 4 B)");
+    if (sink_words < owq::stream_read_sink_words(bytes))
+        return fail(OWQ_ERR_RANGE, "sink_words = %lld: need %lld", (long long)sink_words,
+                    (long long)owq::stream_read_sink_words(bytes));
+    return hip_status(owq::launch_stream_read(src, bytes, sink, (hipStream_t)stream), "owq_stream_read launch");
+}
+
 }  // extern "C"

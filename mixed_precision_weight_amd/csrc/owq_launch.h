@@ -57,6 +57,10 @@ bool mfv_fits(int64_t M, int64_t K);
 bool decode_on_matrix_cores(int64_t M);
 // Matrix-core GEMM for larger M.
 hipError_t launch_gemm(const LinearDesc& d, int64_t M, hipStream_t s);
+
+// read-only streaming reference (stream.hip): one word per 4608-byte wavefront
+int64_t stream_read_sink_words(int64_t bytes);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 // Smallest M routed to the matrix-core kernel (read once from OWQ_GEMM_MIN_M).
 int64_t gemm_min_m();
 

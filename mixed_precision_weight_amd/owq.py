@@ -41,6 +41,8 @@ EXPORTS = {
     "owq_linear": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P]),
     "owq_linear_batched": (ctypes.c_int, [ctypes.POINTER(OwqLayer), ctypes.POINTER(_P),
                                           ctypes.POINTER(_P), _I32, _I64, _P]),
+    "owq_stream_read_sink_words": (_I64, [_I64]),
+    "owq_stream_read": (ctypes.c_int, [_P, _I64, _P, _I64, _P]),
 }
 
 _lib = None
@@ -216,3 +218,22 @@ class PreparedBatched:
 
     def __call__(self):
         _check(self.fn(self.Ls, self.xp, self.yp, self.n, self.M, self.stream), "owq_linear_batched")
+
+
+# ----------------------------------------------------------- measurement aid
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Read-only HBM stream over `buf` (any dtype, contiguous, size a multiple of
+    12 bytes) with the M = 1 decode kernel's geometry; not a step of the method.
+    Returns the int32 sink: word w is the XOR of the 32-bit words of bytes
+    [4608 w, 4608 (w + 1)) of the buffer."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous CUDA (HIP) tensor")
+    nbytes = buf.numel() * buf.element_size()
+    words = lib().owq_stream_read_sink_words(nbytes)
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=buf.device)
+    _dev(sink, torch.int32, "sink")
+    _check(lib().owq_stream_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(stream)), "owq_stream_read")
+    return sink

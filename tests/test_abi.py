@@ -142,3 +142,16 @@ def test_linear_batched_validation(lib):
     Ls[1].bits = 2
     assert f(Ls, xs, ys, 2, 1, None) == 5
     assert "layer 1" in _err(lib)
+
+
+def test_stream_read_validation(lib):
+    f = lib.owq_stream_read
+    assert lib.owq_stream_read_sink_words(4608) == 1
+    assert lib.owq_stream_read_sink_words(4608 + 12) == 2
+    assert lib.owq_stream_read_sink_words(0) == 0
+    assert f(None, 4608, FAKE, 1, None) == 1
+    assert f(FAKE, 4608, None, 1, None) == 1
+    assert f(FAKE, 4600, FAKE, 1, None) == 2   # not a multiple of 12 bytes
+    assert f(FAKE, 0, FAKE, 1, None) == 2
+    assert f(FAKE + 2, 4608, FAKE, 1, None) == 4
+    assert f(FAKE, 4620, FAKE, 1, None) == 3   # needs two sink words

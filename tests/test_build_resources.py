@@ -13,7 +13,8 @@ import pytest
 
 from mixed_precision_weight_amd import build as B
 
-KERNELS = ("k_gemv", "k_mfv", "k_gemm_dma", "k_gemm", "k_calib_first", "k_colsum_err", "k_finalize", "k_topk", "k_pack")
+KERNELS = ("k_gemv", "k_mfv", "k_gemm_dma", "k_gemm", "k_calib_first", "k_colsum_err", "k_finalize", "k_topk", "k_pack",
+           "k_stream_read")
 
 
 def _load():
