@@ -7,7 +7,8 @@
 // result is written in ascending column order.
 //
 // One 1024-thread workgroup (latency-bound). For K <= 16384 the keys stay in
-// registers (k_topk_reg: early-exit radix select, one ordered prefix sum);
+// registers (k_topk_reg: early-exit radix select over the range the keys
+// still in play span, one ordered prefix sum);
 // larger K reads the scores from L2 on every pass (k_topk, below):
 //  1. radix select of the k-th largest 64-bit order key, 8 bits per pass from the
 //     most significant digit: an LDS histogram of the digit among keys that match
@@ -163,10 +164,23 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wave_to
 }
 
 // K <= 1024 C: thread t holds the keys of columns C t .. C t + C - 1 in registers,
-// so index order is thread order, then register order. The radix select stops as
-// soon as the bucket holding the k-th key is taken whole (with distinct scores
-// that happens after two or three 8-bit passes); the compaction then compares
-// keys on the digits fixed so far. One ordered prefix sum places the selection.
+// so index order is thread order, then register order. The radix select works
+// on the range [lo, hi] of the keys still in play, starting with the block's
+// smallest and largest key: each pass splits it into 256 buckets of width 2^s
+// (the smallest s that makes the range fit), so the first bucket boundaries
+// follow the keys' actual spread rather than the fixed top byte (which for
+// scores of similar magnitude holds a few values, and makes the waves' atomic
+// counts collide). It stops as soon as the bucket holding the k-th key is taken
+// whole, or when the bucket width is one (its keys are then equal). The
+// selection is every key above the final range plus the first kk in index
+// order inside it; one ordered prefix sum places it.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
+{
+    const uint32_t a = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+    const uint32_t b = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)b << 32) | a;
+}
+
 template <int C>
 __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ score, int32_t K, int32_t k,
                                                    int32_t* __restrict__ out)
@@ -174,30 +188,55 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
     __shared__ uint32_t hist[256];
     __shared__ uint32_t whist[16][256];  // one digit histogram per wave
     __shared__ uint32_t wave_tot[16];
-    __shared__ unsigned long long sh_prefix;
+    __shared__ unsigned long long sh_lo[16], sh_hi[16];
     __shared__ int sh_kk, sh_done;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (k <= 0)  // nothing to select (the host does not launch for k == 0)
+        return;
 
     uint64_t key[C];
+    uint64_t lo = ~0ull, hi = 0;
 #pragma unroll
     for (int c = 0; c < C; c++) {
         const int j = C * tid + c;  // columns past K get key 0, below every finite score
         const double v = score[min(j, K - 1)];
         key[c] = j < K ? score_key(v) : 0ull;
+        lo = j < K ? min(lo, key[c]) : lo;
+        hi = j < K ? max(hi, key[c]) : hi;
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        lo = min(lo, shfl_xor_u64(lo, o));
+        hi = max(hi, shfl_xor_u64(hi, o));
+    }
+    if (lane == 0) {
+        sh_lo[wave] = lo;
+        sh_hi[wave] = hi;
+    }
+    __syncthreads();
+    lo = sh_lo[0];
+    hi = sh_hi[0];
+    for (int w = 1; w < 16; w++) {
+        lo = min(lo, (uint64_t)sh_lo[w]);
+        hi = max(hi, (uint64_t)sh_hi[w]);
+    }
+    __syncthreads();  // sh_lo / sh_hi are rewritten below
 
-    uint64_t prefix = 0, mask = 0;
-    int kk = k;  // how many still to take among keys matching `prefix` on `mask`
-    for (int shift = 56; shift >= 0; shift -= 8) {
-        // each wave counts its keys' digits into its own LDS histogram (atomics
+    int kk = k;  // how many still to take among the keys in [lo, hi]
+    for (;;) {
+        const uint64_t span = hi - lo;
+        const int s = span == 0 ? 0 : max(56 - (int)__clzll(span), 0);  // (span >> s) < 256
+        // each wave counts its keys' buckets into its own LDS histogram (atomics
         // that hit one bin serialise within the wave only), then the 16 are summed
 #pragma unroll
         for (int i = 0; i < 4; i++)
             whist[wave][lane + 64 * i] = 0;
 #pragma unroll
-        for (int c = 0; c < C; c++)
-            if ((key[c] & mask) == prefix)
-                atomicAdd(&whist[wave][(uint32_t)(key[c] >> shift) & 255u], 1u);
+        for (int c = 0; c < C; c++) {
+            const uint64_t d = key[c] - lo;  // wraps above span for keys below lo
+            if (d <= span)
+                atomicAdd(&whist[wave][(uint32_t)(d >> s)], 1u);
+        }
         __syncthreads();
         if (tid < 256) {
             uint32_t t = 0;
@@ -208,7 +247,7 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
         }
         __syncthreads();
         if (wave == 0) {
-            // lane l covers digits 255-4l .. 252-4l, i.e. descending order
+            // lane l covers buckets 255-4l .. 252-4l, i.e. descending order
             uint32_t c4[4];
 #pragma unroll
             for (int i = 0; i < 4; i++)
@@ -227,10 +266,13 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     if (run + c4[i] >= (uint32_t)kk) {
-                        const int d = 255 - 4 * lane - i;
-                        sh_prefix = prefix | ((uint64_t)d << shift);
+                        const uint64_t b0 = lo + ((uint64_t)(255 - 4 * lane - i) << s);
+                        const uint64_t w = (1ull << s) - 1;
+                        sh_lo[0] = b0;
+                        sh_hi[0] = hi - b0 < w ? hi : b0 + w;
                         sh_kk = kk - (int)run;
-                        sh_done = run + c4[i] == (uint32_t)kk;  // the whole bucket is taken
+                        // the whole bucket is taken, or its keys are all equal
+                        sh_done = run + c4[i] == (uint32_t)kk || s == 0;
                         break;
                     }
                     run += c4[i];
@@ -238,28 +280,30 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
             }
         }
         __syncthreads();
-        prefix = sh_prefix;
+        lo = sh_lo[0];
+        hi = sh_hi[0];
         kk = sh_kk;
-        mask |= 0xffull << shift;
-        if (sh_done)
+        const bool done = sh_done;
+        __syncthreads();  // every thread has read the shared state before the next pass writes it
+        if (done)
             break;
     }
 
-    // ordered selection: above the threshold on the fixed digits, or equal to it
-    // and among the first kk such keys in index order
+    // ordered selection: above the final range, or inside it and among the first
+    // kk such keys in index order
+    const uint64_t span = hi - lo;
     uint32_t n_eq = 0;
 #pragma unroll
     for (int c = 0; c < C; c++)
-        n_eq += (key[c] & mask) == prefix;
+        n_eq += key[c] - lo <= span;
     uint32_t eq_total;
     uint32_t eq_rank = block_excl_sum(n_eq, wave_tot, eq_total);
     bool sel[C];
     uint32_t n_sel = 0;
 #pragma unroll
     for (int c = 0; c < C; c++) {
-        const uint64_t m = key[c] & mask;
-        const bool eq = m == prefix;
-        sel[c] = m > prefix || (eq && eq_rank < (uint32_t)kk);
+        const bool eq = key[c] - lo <= span;
+        sel[c] = key[c] > hi || (eq && eq_rank < (uint32_t)kk);
         eq_rank += eq;
         n_sel += sel[c];
     }

@@ -143,6 +143,11 @@ def test_select_ties(owq):
         score = rng.integers(0, 4, K).astype(np.float64)
         got = host(owq.select_weak(dev(score), k))
         assert np.array_equal(got, oracle.select_weak(score, k)), (K, k)
+    # all scores equal: the lowest k indices; all negative
+    for K, k in ((3000, 7), (11008, 86)):
+        for score in (np.full(K, 2.5), -np.exp(rng.normal(0, 2, K))):
+            got = host(owq.select_weak(dev(score), k))
+            assert np.array_equal(got, oracle.select_weak(score, k)), (K, k)
     # negative, zero of both signs, and huge values
     score = np.array([-1.0, 0.0, -0.0, 3.0, -5.0, 1e300, 0.0, -0.0, 2.0, -1e-300])
     for k in range(len(score) + 1):
