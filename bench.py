@@ -301,7 +301,7 @@ def main():
                         "bound": "mfma", "achieved": round(pre_tflops, 1), "peak": MFMA_FP16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
                         "algorithmic_flops": pre_flops, "per_linear": per_linear_prefill},
-            "calibrate_score": hbm_entry(cal_bytes, sum(cal_s), "k_colsum x2 + k_rowfit + k_finalize, 7 linears"),
+            "calibrate_score": hbm_entry(cal_bytes, sum(cal_s), "k_calib_first + k_colsum_err + k_finalize, 7 linears"),
             "select_weak": {"what": "k_topk, 7 linears", "us": round(sum(sel_s) * 1e6, 1), "bound": "latency"},
             "pack": hbm_entry(pk_bytes, sum(pak_s), "k_pack, 7 linears"),
         },
@@ -485,7 +485,7 @@ def main():
             t = float(np.median([a.elapsed_time(b) for a, b, _ in evl])) / 1e3
             ts = float(np.median([b.elapsed_time(c) for _, b, c in evl])) / 1e3
             key = f"{s.name} {s.N}x{s.K} T={c4.T}"
-            long_cal[key] = hbm_entry(calib_bytes(s.N, s.K, c4.T), t, "k_colsum x2 + k_rowfit + k_finalize")
+            long_cal[key] = hbm_entry(calib_bytes(s.N, s.K, c4.T), t, "k_calib_first + k_colsum_err + k_finalize")
             long_sel[key] = {"what": f"top-{s.k} of K = {s.K}", "us": round(ts * 1e6, 2), "bound": "latency"}
             del Wl, Xl, wsl
         result["kernels"]["calibrate_score_long"] = long_cal
