@@ -223,7 +223,9 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
     __syncthreads();  // sh_lo / sh_hi are rewritten below
 
     int kk = k;  // how many still to take among the keys in [lo, hi]
-    for (;;) {
+    // each pass leaves a range at least 2^8 times narrower, so nine passes reach
+    // width one; the bound only guarantees the loop ends
+    for (int pass = 0; pass < 10; pass++) {
         const uint64_t span = hi - lo;
         const int s = span == 0 ? 0 : max(56 - (int)__clzll(span), 0);  // (span >> s) < 256
         // each wave counts its keys' buckets into its own LDS histogram (atomics
