@@ -163,7 +163,7 @@ def main():
 
     dev = torch.device("cuda:0")
     owq.lib()  # fails loudly if the HIP library is missing
-    cfg = synth.CONFIGS[1]
+    cfg = synth.LLAMA7B_LAYER_DECODE
     specs = cfg.layers
     L = len(specs)
     print(f"bench: {cfg.name}: generating inputs", file=sys.stderr, flush=True)
@@ -464,7 +464,7 @@ def main():
     if not args.no_long_calibration:
         # long calibration (T = 8192 tokens) at the MLP shapes: X and W read once
         print("bench: long calibration", file=sys.stderr, flush=True)
-        c4 = synth.CONFIGS[4]
+        c4 = synth.LLAMA7B_MLP_PREFILL_CALIB
         long_cal, long_sel = {}, {}
         for li, s in enumerate(c4.layers):
             seed = c4.seed(li)
@@ -496,7 +496,7 @@ def main():
         # and 8: calibrated and packed like the layer above, three copies rotated
         # (3 x 210 MB) so the bytes come from HBM, one launch per copy
         print("bench: large shapes", file=sys.stderr, flush=True)
-        c3 = synth.CONFIGS[3]
+        c3 = synth.LARGE_SHAPES
         RL = 3
         big = [[] for _ in range(RL)]
         for li, s in enumerate(c3.layers):

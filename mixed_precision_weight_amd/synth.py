@@ -42,14 +42,14 @@ class LayerSpec:
 
 @dataclasses.dataclass(frozen=True)
 class Config:
-    cid: int
+    seed_base: int  # layer l of this workload draws from seed seed_base + l
     name: str
     layers: tuple
     T: int          # calibration tokens
     Ms: tuple       # decode / prefill batch sizes exercised
 
     def seed(self, layer_index: int) -> int:
-        return 1000 * self.cid + layer_index
+        return self.seed_base + layer_index
 
 
 def _n_out(K: int) -> int:
@@ -75,26 +75,27 @@ def _k_large(K: int) -> int:
     return int(round(0.0077 * K))
 
 
-CONFIGS = {
-    # OPT-125m q_proj shape, the small case the oracle finishes in seconds.
-    0: Config(0, "opt125m_q_proj", (LayerSpec("q_proj", 768, 768, 6, 0.02, 6, 20.0),),
-              T=128, Ms=(1,)),
-    # One LLaMA-7B decoder layer (7 linears), decode M = 1.
-    1: Config(1, "llama7b_layer_decode", _llama7b_layers(), T=2048, Ms=(1,)),
-    # Same shapes, decode batch sweep.
-    2: Config(2, "llama7b_layer_batch_sweep", _llama7b_layers(), T=2048, Ms=(1, 2, 4, 8, 16)),
-    # Large-model shapes.
-    3: Config(3, "large_8192_28672", (
-        LayerSpec("attn_8192x8192", 8192, 8192, _k_large(8192), 0.01, _n_out(8192), 30.0),
-        LayerSpec("up_28672x8192", 28672, 8192, _k_large(8192), 0.01, _n_out(8192), 30.0),
-        LayerSpec("down_8192x28672", 8192, 28672, _k_large(28672), 0.01, _n_out(28672), 30.0),
-    ), T=2048, Ms=(1, 8)),
-    # Prefill (M = 2048) and long calibration (T = 8192) at the MLP shapes.
-    4: Config(4, "llama7b_mlp_prefill_calib", (
-        LayerSpec("gate_proj", 11008, 4096, 32, 0.02, _n_out(4096), 20.0),
-        LayerSpec("down_proj", 4096, 11008, 86, 0.02, _n_out(11008), 20.0),
-    ), T=8192, Ms=(2048,)),
-}
+# The OPT-125m q_proj shape: the small case the oracle finishes in seconds.
+OPT125M_Q_PROJ = Config(0, "opt125m_q_proj", (LayerSpec("q_proj", 768, 768, 6, 0.02, 6, 20.0),),
+                        T=128, Ms=(1,))
+# One LLaMA-7B decoder layer (7 linears), decode M = 1.
+LLAMA7B_LAYER_DECODE = Config(1000, "llama7b_layer_decode", _llama7b_layers(), T=2048, Ms=(1,))
+# Same shapes, decode batch sweep.
+LLAMA7B_BATCH_SWEEP = Config(2000, "llama7b_layer_batch_sweep", _llama7b_layers(), T=2048, Ms=(1, 2, 4, 8, 16))
+# Large-model shapes.
+LARGE_SHAPES = Config(3000, "large_8192_28672", (
+    LayerSpec("attn_8192x8192", 8192, 8192, _k_large(8192), 0.01, _n_out(8192), 30.0),
+    LayerSpec("up_28672x8192", 28672, 8192, _k_large(8192), 0.01, _n_out(8192), 30.0),
+    LayerSpec("down_8192x28672", 8192, 28672, _k_large(28672), 0.01, _n_out(28672), 30.0),
+), T=2048, Ms=(1, 8))
+# Prefill (M = 2048) and long calibration (T = 8192) at the MLP shapes.
+LLAMA7B_MLP_PREFILL_CALIB = Config(4000, "llama7b_mlp_prefill_calib", (
+    LayerSpec("gate_proj", 11008, 4096, 32, 0.02, _n_out(4096), 20.0),
+    LayerSpec("down_proj", 4096, 11008, 86, 0.02, _n_out(11008), 20.0),
+), T=8192, Ms=(2048,))
+
+CONFIGS = {c.name: c for c in (OPT125M_Q_PROJ, LLAMA7B_LAYER_DECODE, LLAMA7B_BATCH_SWEEP, LARGE_SHAPES,
+                               LLAMA7B_MLP_PREFILL_CALIB)}
 
 
 def _streams(seed: int):

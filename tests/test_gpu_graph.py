@@ -33,10 +33,10 @@ def _path(owq, W, X, xs, ws, k):
     return [lam, score, idx, p["qcodes"], p["scales"], p["zeros"], p["w_weak"]] + ys
 
 
-@pytest.mark.parametrize("cid,li", [(0, 0), (1, 6)])
-def test_graph_replay_matches_eager(owq, cid, li):
+@pytest.mark.parametrize("workload,li", [("opt125m_q_proj", 0), ("llama7b_layer_decode", 6)])
+def test_graph_replay_matches_eager(owq, workload, li):
     import torch
-    cfg = synth.CONFIGS[cid]
+    cfg = synth.CONFIGS[workload]
     spec = cfg.layers[li]
     seed = cfg.seed(li)
     W = dev(synth.weights(spec, seed))

@@ -76,7 +76,7 @@ def _run(owq, W, X, k, xs, what, sample=None, rng=None):
 
 
 def test_small_config_full(owq):
-    cfg = synth.CONFIGS[0]
+    cfg = synth.OPT125M_Q_PROJ
     spec = cfg.layers[0]
     seed = cfg.seed(0)
     W = synth.weights(spec, seed)
@@ -157,7 +157,7 @@ def test_select_ties(owq):
 
 def test_determinism(owq):
     import torch
-    cfg = synth.CONFIGS[1]
+    cfg = synth.LLAMA7B_LAYER_DECODE
     spec = cfg.layers[6]
     rng = np.random.default_rng(0)
     W = synth.random_layer(rng, 512, spec.K)

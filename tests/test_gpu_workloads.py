@@ -29,14 +29,14 @@ def _inputs(cfg, li, M):
 
 @pytest.mark.parametrize("li", range(7))
 def test_llama7b_layer_decode(owq, li):
-    cfg = synth.CONFIGS[1]
+    cfg = synth.LLAMA7B_LAYER_DECODE
     spec, W, X, x = _inputs(cfg, li, 1)
     _run(owq, W, X, spec.k, [x], f"{cfg.name}/{spec.name}")
 
 
 @pytest.mark.parametrize("li", [0, 4, 6])
 def test_llama7b_batch_sweep(owq, li):
-    cfg = synth.CONFIGS[2]
+    cfg = synth.LLAMA7B_BATCH_SWEEP
     spec, W, X, x = _inputs(cfg, li, 16)
     _run(owq, W, X, spec.k, [x[:m] for m in cfg.Ms], f"{cfg.name}/{spec.name}",
          sample=4096 * 4, rng=np.random.default_rng(li))
@@ -46,7 +46,7 @@ def test_llama7b_layer_batched_launch(owq):
     """One launch over the 7 linears equals the 7 single launches bit for bit."""
     import torch
     import oracle
-    cfg = synth.CONFIGS[1]
+    cfg = synth.LLAMA7B_LAYER_DECODE
     layers, xs, singles = [], [], []
     for li, spec in enumerate(cfg.layers):
         seed = cfg.seed(li)
@@ -74,7 +74,7 @@ def test_llama7b_layer_batched_launch(owq):
 
 @pytest.mark.parametrize("li", range(3))
 def test_large_shapes(owq, li):
-    cfg = synth.CONFIGS[3]
+    cfg = synth.LARGE_SHAPES
     spec, W, X, x = _inputs(cfg, li, 8)
     _run(owq, W, X, spec.k, [x[:1], x], f"{cfg.name}/{spec.name}", sample=2048,
          rng=np.random.default_rng(100 + li))
@@ -82,7 +82,7 @@ def test_large_shapes(owq, li):
 
 @pytest.mark.parametrize("li", range(2))
 def test_prefill_and_long_calibration(owq, li):
-    cfg = synth.CONFIGS[4]
+    cfg = synth.LLAMA7B_MLP_PREFILL_CALIB
     spec, W, X, x = _inputs(cfg, li, 2048)
     _run(owq, W, X, spec.k, [x], f"{cfg.name}/{spec.name}", sample=4096,
          rng=np.random.default_rng(200 + li))

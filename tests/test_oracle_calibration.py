@@ -113,7 +113,7 @@ def _planted(orc, cfg, li):
 
 
 def test_planted_outliers_selected_small(orc):
-    cfg = synth.CONFIGS[0]
+    cfg = synth.OPT125M_Q_PROJ
     spec, W, outl, lam, score = _planted(orc, cfg, 0)
     weak = orc.select_weak(score, spec.k)
     assert spec.k == spec.n_out == 6
@@ -129,7 +129,7 @@ def test_planted_outliers_selected_small(orc):
 @pytest.mark.slow
 @pytest.mark.parametrize("li", [0, 6])
 def test_planted_outliers_selected_llama_shapes(orc, li):
-    cfg = synth.CONFIGS[1]
+    cfg = synth.LLAMA7B_LAYER_DECODE
     spec, W, outl, lam, score = _planted(orc, cfg, li)
     weak = set(orc.select_weak(score, spec.k))
     assert set(outl) <= weak
@@ -139,7 +139,7 @@ def test_planted_outliers_selected_llama_shapes(orc, li):
 
 
 def test_determinism(orc):
-    cfg = synth.CONFIGS[0]
+    cfg = synth.OPT125M_Q_PROJ
     spec = cfg.layers[0]
     a = synth.weights(spec, cfg.seed(0))
     b = synth.weights(spec, cfg.seed(0))
