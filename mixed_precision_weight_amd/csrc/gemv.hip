@@ -67,6 +67,7 @@ __device__ __forceinline__ int xs_slot(int m, int T, int g, int qd)
 
 // ------------------------------------------------------------------ kernel --
 constexpr int kChunkTiles = 2;  // 64-group tiles per K chunk (4096 columns)
+constexpr int kNonTemporal = 2;  // buffer-load cache-policy bits: nt
 // Rows per wavefront: three (76 registers at M = 1, six waves per SIMD) was
 // faster than two, four (109 registers, four waves) and eight at M = 1 and 2.
 __host__ __device__ constexpr int rows_per_wave(int) { return 3; }
@@ -153,11 +154,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
             xg[t] = *reinterpret_cast<const uint4*>(X + m * K + g0 * 32 + pc * 8);
         }
         asm volatile("" ::: "memory");  // x ahead of the codes: its wait covers no code load
+        // the codes are read once per launch: non-temporal loads (cache policy
+        // "nt") keep them from displacing x and the row data in the caches
 #pragma unroll
         for (int r = 0; r < R; r++)
 #pragma unroll
             for (int u = 0; u < TT; u++)
-                cw[r][u] = __builtin_amdgcn_raw_buffer_load_b96(qr, vrow[r] + (g0 + 64 * u) * 12, 0, 0);
+                cw[r][u] = __builtin_amdgcn_raw_buffer_load_b96(qr, vrow[r] + (g0 + 64 * u) * 12, 0, kNonTemporal);
     };
 
     // row steps and zero points first: they move to scalar registers below, and

@@ -100,6 +100,10 @@ __global__ __launch_bounds__(64 * W * S) void k_mfv(MfvBatch b, int M)
     using SH = MfvShape<U, MC>;
     constexpr int GC = SH::GC, RS = SH::RS, STAGE = SH::STAGE, PT = SH::PT;
     constexpr int DPW = MC * PT / W;  // x loads per wave and chunk
+    // the codes are read once per launch; with 16-token x stages non-temporal code
+    // loads (cache policy "nt") keep them from displacing x: 5-7 % faster at
+    // M = 8 and 16, while at M <= 4 they were 1-4 % slower
+    constexpr int kCodePolicy = MC == 16 ? 2 : 0;
     static_assert((MC * PT) % W == 0, "x loads must split evenly over the waves");
     constexpr int CRS = SH::CRS, CQ = SH::CQ, CL = SH::CL;
     // D + 1 x stages per K group (chunks run D ahead), each its own array
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(64 * W * S) void k_mfv(MfvBatch b, int M)
             const int pc = 64 * i + lane;
             const int r = pc / CQ, o = (pc % CQ) * 16;
             cw[i] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, ((wave * 16 + r) * G + cc * GC) * 12 + o, 0, 0));
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, ((wave * 16 + r) * G + cc * GC) * 12 + o, 0, kCodePolicy));
         }
     };
     char* const crow = cs[wid];
