@@ -458,7 +458,7 @@ def main():
             del bufs, sinks
         sr["decode_vs_layer_size_stream"] = round(value / sr["layer_size"]["read_GBps"], 4)
         result["kernels"]["stream_read_reference"] = dict(
-            what="owq_stream_read: loads only, the M = 1 decode geometry (6 x 768 B per wavefront, 4-wave "
+            what="owq_stream_read: loads only, the M = 1 decode geometry (6 x 768 B per wavefront, non-temporal, 4-wave "
                  "blocks), one launch per buffer (not the product path)", **sr)
 
     if not args.no_long_calibration:

@@ -6,7 +6,8 @@
 // Same geometry as the M = 1 decode: blocks of 4 wavefronts, each wavefront
 // reading 6 tiles of 768 contiguous bytes (lane l the 12 bytes at 12 l of each
 // tile, one dwordx3 buffer load per tile), i.e. 4608 bytes per wavefront and
-// 18432 per block, all loads issued before the first wait. The words are
+// 18432 per block, all loads issued before the first wait, with the decode's
+// non-temporal cache policy. The words are
 // combined by XOR, so nothing the hardware could skip; each wavefront stores
 // one word.
 #include "owq_device.h"
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint8_t* src, int64_t
     u32x3v v[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; t++)
-        v[t] = __builtin_amdgcn_raw_buffer_load_b96(r, t * 768 + lane * 12, 0, 0);
+        v[t] = __builtin_amdgcn_raw_buffer_load_b96(r, t * 768 + lane * 12, 0, 2);  // nt, as the decode's codes
     uint32_t x = 0;
 #pragma unroll
     for (int t = 0; t < kTiles; t++)
