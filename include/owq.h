@@ -48,8 +48,9 @@
  *     pointer after a call returns and allocates no device memory in these calls.
  *   - Thread safety: no mutable global state except the thread-local error text.
  *   - Limits: 1 <= N, M, T; 32 <= K <= 65536 with K % 32 == 0; 0 <= k <= K;
- *     bits == 3. Device pointers must be aligned to their element size, qcodes and
- *     x / X / W to 16 bytes. Inputs must be finite.
+ *     bits == 3. Device pointers must be aligned to their element size (qcodes and
+ *     weak_idx: 4 bytes, fp16 arrays: 2 bytes, fp64 arrays: 8 bytes), and x / X / W
+ *     to 16 bytes (they are read in 16-byte pieces). Inputs must be finite.
  */
 #ifndef OWQ_H
 #define OWQ_H

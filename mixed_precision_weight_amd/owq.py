@@ -81,18 +81,45 @@ def _stream(stream=None):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+def _meta(t, dtype, name: str, shape=None) -> torch.Tensor:
+    """Type, dtype, shape and contiguity of one argument. Runs before any device
+    check, so a caller's shape mistake is reported as such on any device."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
 
 
+def _on_device(*named):
+    """Every (name, tensor) is a HIP tensor, all on one device."""
+    devs = set()
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"arguments are on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _dev(t: torch.Tensor, dtype, name: str, shape=None) -> torch.Tensor:
+    _meta(t, dtype, name, shape)
+    _on_device((name, t))
+    return t
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 # ------------------------------------------------------------------ calibration
@@ -102,54 +129,87 @@ def calibrate_workspace_bytes(N: int, K: int, T: int) -> int:
     return int(lib().owq_calibrate_workspace_bytes(N, K, T))
 
 
-def calibrate(W: torch.Tensor, X: torch.Tensor, workspace: torch.Tensor | None = None, stream=None):
-    """lambda (fp64 [K]) and score (fp64 [K]) of fp16 W [N][K] and X [T][K]."""
-    _dev(W, torch.float16, "W")
-    _dev(X, torch.float16, "X")
+def _calib_shapes(W, X):
+    _meta(W, torch.float16, "W")
+    _meta(X, torch.float16, "X")
+    if W.dim() != 2 or X.dim() != 2:
+        raise ValueError(f"W and X must be 2-D, got {tuple(W.shape)} and {tuple(X.shape)}")
     N, K = W.shape
     T = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError(f"X has {X.shape[1]} columns, W has {K}: both are [*, K]")
+    return N, K, T
+
+
+def calibrate(W: torch.Tensor, X: torch.Tensor, workspace: torch.Tensor | None = None, stream=None):
+    """lambda (fp64 [K]) and score (fp64 [K]) of fp16 W [N][K] and X [T][K]."""
+    N, K, T = _calib_shapes(W, X)
+    if workspace is not None:
+        _meta(workspace, torch.uint8, "workspace")
+    _on_device(("W", W), ("X", X), ("workspace", workspace))
     nbytes = calibrate_workspace_bytes(N, K, T)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=W.device)
     lam = torch.empty(K, dtype=torch.float64, device=W.device)
     score = torch.empty(K, dtype=torch.float64, device=W.device)
     _check(lib().owq_calibrate_score(_ptr(W), N, K, _ptr(X), T, _ptr(lam), _ptr(score), _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+                                     _nbytes(workspace), _stream(stream)),
            "owq_calibrate_score")
     return lam, score
 
 
 def select_weak(score: torch.Tensor, k: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Indices of the k largest scores, ascending (int32 [k]); written to out if given."""
-    _dev(score, torch.float64, "score")
+    _meta(score, torch.float64, "score")
+    if score.dim() != 1:
+        raise ValueError(f"score must be 1-D, got shape {tuple(score.shape)}")
+    k = int(k)
+    if not 0 <= k <= score.numel():
+        raise ValueError(f"k = {k} outside [0, K = {score.numel()}]")
+    if out is not None:
+        _meta(out, torch.int32, "out")
+        if out.dim() != 1 or out.numel() < k:
+            raise ValueError(f"out must be 1-D with at least k = {k} entries, got shape {tuple(out.shape)}")
+    _on_device(("score", score), ("out", out))
     if out is None:
         out = torch.empty(max(k, 1), dtype=torch.int32, device=score.device)
-    else:
-        _dev(out, torch.int32, "out")
-        if out.numel() < k:
-            raise ValueError(f"out holds {out.numel()} indices, k = {k}")
-    _check(lib().owq_select_weak(_ptr(score), score.numel(), int(k), _ptr(out) if k else None,
+    _check(lib().owq_select_weak(_ptr(score), score.numel(), k, _ptr(out) if k else None,
                                  _stream(stream)), "owq_select_weak")
     return out[:k]
 
 
 # ------------------------------------------------------------------------ pack
 
+_PACK_OUT = ("qcodes", "scales", "zeros", "w_weak")
+
+
+def _pack_out_shapes(N: int, K: int, k: int) -> dict:
+    return {"qcodes": ((N, K // 32, 3), torch.int32), "scales": ((N,), torch.float16),
+            "zeros": ((N,), torch.uint8), "w_weak": ((N, k), torch.float16)}
+
 
 def pack(W: torch.Tensor, weak_idx: torch.Tensor, out: dict | None = None, stream=None) -> dict:
     """Latency-favoured packed layer: dict of device tensors
     qcodes int32 [N][K/32][3] (uint32 bits), scales fp16 [N], zeros uint8 [N],
     w_weak fp16 [N][k], weak_idx int32 [k]."""
-    _dev(W, torch.float16, "W")
-    _dev(weak_idx, torch.int32, "weak_idx")
+    _meta(W, torch.float16, "W")
+    _meta(weak_idx, torch.int32, "weak_idx")
+    if W.dim() != 2 or weak_idx.dim() != 1:
+        raise ValueError(f"W must be 2-D and weak_idx 1-D, got {tuple(W.shape)} and {tuple(weak_idx.shape)}")
     N, K = W.shape
     k = weak_idx.numel()
+    if K % 32 or k > K:
+        raise ValueError(f"K = {K} must be a multiple of 32 and k = {k} at most K")
+    want = _pack_out_shapes(N, K, k)
+    if out is not None:
+        for name in _PACK_OUT:
+            if name not in out:
+                raise ValueError(f"out lacks {name!r}")
+            _meta(out[name], want[name][1], f"out[{name!r}]", want[name][0])
+    _on_device(("W", W), ("weak_idx", weak_idx), *[(f"out[{n!r}]", out[n]) for n in (_PACK_OUT if out else ())])
     dev = W.device
     if out is None:
-        out = {"qcodes": torch.empty((N, K // 32, 3), dtype=torch.int32, device=dev),
-               "scales": torch.empty(N, dtype=torch.float16, device=dev),
-               "zeros": torch.empty(N, dtype=torch.uint8, device=dev),
-               "w_weak": torch.empty((N, k), dtype=torch.float16, device=dev)}
+        out = {name: torch.empty(shape, dtype=dt, device=dev) for name, (shape, dt) in want.items()}
     out["weak_idx"] = weak_idx
     _check(lib().owq_pack(_ptr(W), N, K, _ptr(weak_idx) if k else None, k, _ptr(out["qcodes"]),
                           _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["w_weak"]) if k else None,
@@ -160,30 +220,90 @@ def pack(W: torch.Tensor, weak_idx: torch.Tensor, out: dict | None = None, strea
 # ---------------------------------------------------------------------- linear
 
 
-def layer_struct(layer: dict) -> OwqLayer:
+def layer_shapes(layer: dict):
+    """(N, K, k) of a packed layer dict, after checking that its five tensors
+    agree with one another."""
+    for name in _PACK_OUT + ("weak_idx",):
+        if name not in layer:
+            raise ValueError(f"layer lacks {name!r}")
     q = layer["qcodes"]
-    N, G = q.shape[0], q.shape[1]
-    k = layer["weak_idx"].numel()
-    return OwqLayer(N, G * 32, k, 3, q.data_ptr(), layer["scales"].data_ptr(), layer["zeros"].data_ptr(),
+    _meta(q, torch.int32, "qcodes")
+    if q.dim() != 3 or q.shape[2] != 3:
+        raise ValueError(f"qcodes must be [N][K/32][3], got {tuple(q.shape)}")
+    N, K = q.shape[0], q.shape[1] * 32
+    idx = _meta(layer["weak_idx"], torch.int32, "weak_idx")
+    if idx.dim() != 1:
+        raise ValueError(f"weak_idx must be 1-D, got {tuple(idx.shape)}")
+    k = idx.numel()
+    for name, (shape, dt) in _pack_out_shapes(N, K, k).items():
+        _meta(layer[name], dt, name, shape)
+    return N, K, k
+
+
+def _layer_named(layer: dict, tag: str = ""):
+    return [(tag + n, layer[n]) for n in _PACK_OUT + ("weak_idx",)]
+
+
+def layer_struct(layer: dict) -> OwqLayer:
+    N, K, k = layer_shapes(layer)
+    return OwqLayer(N, K, k, 3, layer["qcodes"].data_ptr(), layer["scales"].data_ptr(), layer["zeros"].data_ptr(),
                     layer["weak_idx"].data_ptr() if k else None, layer["w_weak"].data_ptr() if k else None)
+
+
+def _xy_shapes(N: int, K: int, x, y, tag: str = "", M: int | None = None):
+    """x fp16 [M][K] (or [K] for M = 1); y fp16 [M][N] if given. Returns M."""
+    _meta(x, torch.float16, tag + "x")
+    if x.dim() == 1:
+        xs = (1, x.shape[0])
+    elif x.dim() == 2:
+        xs = tuple(x.shape)
+    else:
+        raise ValueError(f"{tag}x must be [M][K] or [K], got {tuple(x.shape)}")
+    if xs[1] != K:
+        raise ValueError(f"{tag}x has {xs[1]} columns, the layer has K = {K}")
+    if xs[0] < 1:
+        raise ValueError(f"{tag}x has no rows")
+    if M is not None and xs[0] != M:
+        raise ValueError(f"{tag}x has {xs[0]} rows, the batch has M = {M}")
+    if y is not None:
+        _meta(y, torch.float16, tag + "y")
+        if y.numel() != xs[0] * N or (y.dim() == 2 and tuple(y.shape) != (xs[0], N)) or y.dim() > 2:
+            raise ValueError(f"{tag}y has shape {tuple(y.shape)}, expected ({xs[0]}, {N})")
+    return xs[0]
 
 
 def linear(layer: dict, x: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """y = x W^T (fp16 [M][N]) for fp16 x [M][K] and a packed layer."""
-    _dev(x, torch.float16, "x")
+    N, K, k = layer_shapes(layer)
+    M = _xy_shapes(N, K, x, y)
+    _on_device(("x", x), ("y", y), *_layer_named(layer))
     L = layer_struct(layer)
-    M = x.shape[0] if x.dim() == 2 else 1
     if y is None:
-        y = torch.empty((M, L.N), dtype=torch.float16, device=x.device)
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     _check(lib().owq_linear(ctypes.byref(L), _ptr(x), M, _ptr(y), _stream(stream)), "owq_linear")
     return y
 
 
+def _batched_args(layers: list, xs: list, ys: list | None):
+    n = len(layers)
+    if n < 1 or len(xs) != n or (ys is not None and len(ys) != n):
+        raise ValueError(f"need as many x (and y) as layers: {n} layers, {len(xs)} x"
+                         + ("" if ys is None else f", {len(ys)} y"))
+    M = None
+    named = []
+    for i, layer in enumerate(layers):
+        N, K, _ = layer_shapes(layer)
+        M = _xy_shapes(N, K, xs[i], None if ys is None else ys[i], f"[{i}] ", M)
+        named += [(f"[{i}] x", xs[i])] + ([] if ys is None else [(f"[{i}] y", ys[i])])
+        named += _layer_named(layer, f"[{i}] ")
+    _on_device(*named)
+    return n, M
+
+
 def linear_batched(layers: list, xs: list, ys: list | None = None, stream=None) -> list:
     """Several independent decode linears (same 1 <= M <= 16) in one launch."""
-    n = len(layers)
+    n, M = _batched_args(layers, xs, ys)
     Ls = (OwqLayer * n)(*[layer_struct(l) for l in layers])
-    M = xs[0].shape[0]
     if ys is None:
         ys = [torch.empty((M, Ls[i].N), dtype=torch.float16, device=xs[i].device) for i in range(n)]
     xp = (_P * n)(*[x.data_ptr() for x in xs])
@@ -202,17 +322,13 @@ class PreparedBatched:
     """
 
     def __init__(self, layers: list, xs: list, ys: list, stream=None):
-        n = len(layers)
-        for x in xs:
-            _dev(x, torch.float16, "x")
-        for y in ys:
-            _dev(y, torch.float16, "y")
+        n, M = _batched_args(layers, xs, ys)
         self._keep = (list(layers), list(xs), list(ys))
         self.Ls = (OwqLayer * n)(*[layer_struct(l) for l in layers])
         self.xp = (_P * n)(*[x.data_ptr() for x in xs])
         self.yp = (_P * n)(*[y.data_ptr() for y in ys])
         self.n = n
-        self.M = xs[0].shape[0]
+        self.M = M
         self.stream = _stream(stream)
         self.fn = lib().owq_linear_batched
 

@@ -1,0 +1,114 @@
+"""CPU tests of the Python binding's argument checks.
+
+The binding is the one layer that sees tensor shapes, so it must reject a
+mismatched shape, dtype or layout before anything reaches the library: a
+narrower x or X would make the kernels read past the allocation, a smaller y
+write past it. These run on host tensors: a shape mistake must be reported as
+such (ValueError / TypeError naming the argument), and a call whose shapes are
+right must stop at the device check, never at a launch."""
+import pytest
+import torch
+
+from mixed_precision_weight_amd import owq
+
+N, K, k = 64, 128, 4
+
+
+def _layer(N=N, K=K, k=k):
+    return {"qcodes": torch.zeros((N, K // 32, 3), dtype=torch.int32),
+            "scales": torch.zeros(N, dtype=torch.float16),
+            "zeros": torch.zeros(N, dtype=torch.uint8),
+            "w_weak": torch.zeros((N, k), dtype=torch.float16),
+            "weak_idx": torch.arange(k, dtype=torch.int32)}
+
+
+def _host_only(fn, *a, **kw):
+    """Shapes are right: the call must stop at the device check."""
+    with pytest.raises(TypeError, match="CUDA"):
+        fn(*a, **kw)
+
+
+def test_calibrate_checks_shapes():
+    W = torch.zeros((N, K), dtype=torch.float16)
+    with pytest.raises(ValueError, match="columns"):
+        owq.calibrate(W, torch.zeros((16, K - 32), dtype=torch.float16))
+    with pytest.raises(ValueError, match="2-D"):
+        owq.calibrate(W, torch.zeros(K, dtype=torch.float16))
+    with pytest.raises(TypeError, match="float16"):
+        owq.calibrate(W.float(), torch.zeros((16, K), dtype=torch.float16))
+    with pytest.raises(ValueError, match="contiguous"):
+        owq.calibrate(torch.zeros((K, N), dtype=torch.float16).t(), torch.zeros((16, N), dtype=torch.float16))
+    with pytest.raises(TypeError, match="uint8"):
+        owq.calibrate(W, torch.zeros((16, K), dtype=torch.float16), workspace=torch.zeros(64))
+    _host_only(owq.calibrate, W, torch.zeros((16, K), dtype=torch.float16))
+
+
+def test_select_checks_k_and_out():
+    s = torch.zeros(K, dtype=torch.float64)
+    with pytest.raises(ValueError, match="outside"):
+        owq.select_weak(s, K + 1)
+    with pytest.raises(ValueError, match="outside"):
+        owq.select_weak(s, -1)
+    with pytest.raises(ValueError, match="at least"):
+        owq.select_weak(s, 8, out=torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="1-D"):
+        owq.select_weak(s.view(2, -1), 4)
+    _host_only(owq.select_weak, s, 8)
+
+
+def test_pack_checks_out_shapes():
+    W = torch.zeros((N, K), dtype=torch.float16)
+    idx = torch.arange(k, dtype=torch.int32)
+    bad = _layer()
+    bad["w_weak"] = torch.zeros((N, k - 1), dtype=torch.float16)
+    with pytest.raises(ValueError, match="w_weak"):
+        owq.pack(W, idx, out=bad)
+    bad = _layer()
+    bad["qcodes"] = torch.zeros((N - 1, K // 32, 3), dtype=torch.int32)
+    with pytest.raises(ValueError, match="qcodes"):
+        owq.pack(W, idx, out=bad)
+    bad = _layer()
+    bad["zeros"] = torch.zeros(N, dtype=torch.int32)
+    with pytest.raises(TypeError, match="zeros"):
+        owq.pack(W, idx, out=bad)
+    with pytest.raises(ValueError, match="multiple of 32"):
+        owq.pack(torch.zeros((N, K - 16), dtype=torch.float16), idx)
+    _host_only(owq.pack, W, idx, out=_layer())
+
+
+def test_linear_checks_x_y_and_layer():
+    L = _layer()
+    with pytest.raises(ValueError, match="columns"):
+        owq.linear(L, torch.zeros((1, K - 32), dtype=torch.float16))
+    with pytest.raises(ValueError, match="y has shape"):
+        owq.linear(L, torch.zeros((2, K), dtype=torch.float16), torch.zeros((1, N), dtype=torch.float16))
+    with pytest.raises(ValueError, match="y has shape"):
+        owq.linear(L, torch.zeros((2, K), dtype=torch.float16), torch.zeros((2, N - 1), dtype=torch.float16))
+    with pytest.raises(TypeError, match="y must be"):
+        owq.linear(L, torch.zeros((2, K), dtype=torch.float16), torch.zeros((2, N), dtype=torch.float32))
+    with pytest.raises(ValueError, match="contiguous"):
+        owq.linear(L, torch.zeros((K, 2), dtype=torch.float16).t())
+    bad = _layer()
+    bad["scales"] = torch.zeros(N - 1, dtype=torch.float16)
+    with pytest.raises(ValueError, match="scales"):
+        owq.linear(bad, torch.zeros((1, K), dtype=torch.float16))
+    bad = _layer()
+    bad["weak_idx"] = torch.arange(k + 1, dtype=torch.int32)  # w_weak still holds k columns
+    with pytest.raises(ValueError, match="w_weak"):
+        owq.linear(bad, torch.zeros((1, K), dtype=torch.float16))
+    _host_only(owq.linear, L, torch.zeros((3, K), dtype=torch.float16))
+    _host_only(owq.linear, L, torch.zeros(K, dtype=torch.float16))
+
+
+def test_batched_checks_common_m_and_counts():
+    Ls = [_layer(), _layer(N=32, K=256, k=2)]
+    xs = [torch.zeros((2, K), dtype=torch.float16), torch.zeros((2, 256), dtype=torch.float16)]
+    with pytest.raises(ValueError, match="rows, the batch has M"):
+        owq.linear_batched(Ls, [xs[0], torch.zeros((3, 256), dtype=torch.float16)])
+    with pytest.raises(ValueError, match="as many"):
+        owq.linear_batched(Ls, xs[:1])
+    with pytest.raises(ValueError, match="columns"):
+        owq.linear_batched(Ls, [xs[0], torch.zeros((2, K), dtype=torch.float16)])
+    with pytest.raises(ValueError, match="y has shape"):
+        owq.PreparedBatched(Ls, xs, [torch.zeros((2, N), dtype=torch.float16), torch.zeros((2, 31), dtype=torch.float16)])
+    _host_only(owq.linear_batched, Ls, xs)
