@@ -23,5 +23,6 @@ from .oracle import (  # noqa: F401
     unpack_codes,
     linear_pairs,
     linear_full,
+    linear_rows,
     effective_bits,
 )

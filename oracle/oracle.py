@@ -25,7 +25,7 @@ _I32 = ctypes.c_int32
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc: -O2, no FMA contraction, no fast-math."""
     if force or not os.path.exists(_LIB):
-        cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+        cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
                "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
         subprocess.check_call(cmd)
         os.replace(_LIB + ".tmp", _LIB)
@@ -52,6 +52,8 @@ def load():
         "owq_oracle_unpack_codes": (None, [_P, _I64, _I64, _P]),
         "owq_oracle_linear_pairs": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32,
                                            _P, _I64, _P, _P, _I64, _P, _P]),
+        "owq_oracle_linear_rows": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32,
+                                          _P, _I64, _P, _I64, _P, _P, ctypes.c_int]),
         "owq_oracle_effective_bits": (ctypes.c_double, [_I64, _I64, ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -200,6 +202,33 @@ def linear_full(layer: dict, x):
     mm, ii = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     y, b = linear_pairs(layer, x, mm.ravel(), ii.ravel())
     return y.reshape(M, N), b.reshape(M, N)
+
+
+def linear_rows(layer: dict, x, rows=None, threads: int = 0):
+    """fp64 y and bound [M][len(rows)] for every token of the listed rows (all
+    rows if None), rows spread over OpenMP threads (0: all). Bit-identical to
+    linear_pairs on the same (token, row)."""
+    q = np.ascontiguousarray(layer["qcodes"], dtype=np.uint32)
+    s = _u16(layer["scales"])
+    z = np.ascontiguousarray(layer["zeros"], dtype=np.uint8)
+    idx = np.ascontiguousarray(layer["weak_idx"], dtype=np.int32)
+    ww = _u16(layer["w_weak"])
+    x = _u16(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    M, K = x.shape
+    N = q.shape[0]
+    assert q.shape[1] * 32 == K
+    k = idx.shape[0]
+    rows = np.arange(N, dtype=np.int64) if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    assert rows.ndim == 1 and (rows >= 0).all() and (rows < N).all()
+    R = rows.shape[0]
+    y = np.zeros((M, R), np.float64)
+    b = np.zeros((M, R), np.float64)
+    load().owq_oracle_linear_rows(_ptr(q), _ptr(s), _ptr(z), N, K,
+                                  _ptr(idx) if k else None, _ptr(ww) if k else None, k,
+                                  _ptr(x), M, _ptr(rows), R, _ptr(y), _ptr(b), int(threads))
+    return y, b
 
 
 def effective_bits(K: int, k: int, latency_favored: bool) -> float:

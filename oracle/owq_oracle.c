@@ -6,6 +6,8 @@
  * the two share no source. Built with gcc -O2 -ffp-contract=off (no fused
  * multiply-add, no fast-math), so every fp32 step below is one IEEE binary32
  * operation rounded to nearest-even, and every sum is an fp64 sum in loop order.
+ * OpenMP only spreads independent outputs over threads (owq_oracle_linear_rows);
+ * it never splits a sum.
  *
  * Pages cited (see owq_oracle.h for the full titles):
  *   [PL] paperlayer.ai notes on the OWQ paper, by section heading.
@@ -35,6 +37,7 @@
 #include "owq_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -344,6 +347,57 @@ void owq_oracle_linear_pairs(const uint32_t* qcodes, const uint16_t* scales,
         y[p] = acc;
         bound[p] = bnd;
     }
+}
+
+/* The same product for every token and a list of rows, with the rows spread
+ * over OpenMP threads (threads <= 0: the OpenMP default). Each output is the
+ * sum of the same fp64 terms, in the same order, as owq_oracle_linear_pairs:
+ * the row is unpacked once into s (q_j - z) (0 at weak columns), then
+ * multiplied by x[m][j] term by term for every token m. y and bound are
+ * [M][R]. */
+void owq_oracle_linear_rows(const uint32_t* qcodes, const uint16_t* scales,
+                            const uint8_t* zeros, int64_t N, int64_t K,
+                            const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,
+                            const uint16_t* x, int64_t M,
+                            const int64_t* rows, int64_t R, double* y, double* bound,
+                            int threads)
+{
+    (void)N;
+    int64_t G = K / 32;
+    double* xf = (double*)malloc((size_t)(M * K) * sizeof(double));
+    for (int64_t e = 0; e < M * K; e++)
+        xf[e] = owq_oracle_f16_to_f64(x[e]);
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+    {
+        double* wd = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < R; r++) {
+            int64_t i = rows[r];
+            double s = owq_oracle_f16_to_f64(scales[i]);
+            int z = zeros[i];
+            for (int64_t j = 0; j < K; j++)
+                wd[j] = s * (double)(get_code(qcodes + (i * G + j / 32) * 3, (int)(j % 32)) - z);
+            for (int64_t m = 0; m < M; m++) {
+                const double* xm = xf + m * K;
+                double acc = 0.0, bnd = 0.0;
+                for (int64_t j = 0; j < K; j++) {
+                    double t = wd[j] * xm[j];
+                    acc += t;
+                    bnd += fabs(t);
+                }
+                for (int32_t c = 0; c < k; c++) {
+                    double t = owq_oracle_f16_to_f64(w_weak[i * k + c]) * xm[weak_idx[c]];
+                    acc += t;
+                    bnd += fabs(t);
+                }
+                y[m * R + r] = acc;
+                bound[m * R + r] = bnd;
+            }
+        }
+        free(wd);
+    }
+    free(xf);
 }
 
 /* Effective bit-width. The storage-favoured format drops the zero-filled codes

@@ -70,6 +70,16 @@ void owq_oracle_linear_pairs(const uint32_t* qcodes, const uint16_t* scales,
                              const int64_t* pm, const int64_t* pi, int64_t P,
                              double* y, double* bound);
 
+/* All M tokens of the listed rows (OpenMP over rows; threads <= 0: default).
+ * Each output equals owq_oracle_linear_pairs' for that (token, row) bit for bit.
+ * y[m][r], bound[m][r] for row rows[r]. */
+void owq_oracle_linear_rows(const uint32_t* qcodes, const uint16_t* scales,
+                            const uint8_t* zeros, int64_t N, int64_t K,
+                            const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,
+                            const uint16_t* x, int64_t M,
+                            const int64_t* rows, int64_t R, double* y, double* bound,
+                            int threads);
+
 /* Effective bits per weight: 3 + 13k/K (storage-favoured) or 3 + 16k/K
  * (latency-favoured, zero-filled dense matrix kept). */
 double owq_oracle_effective_bits(int64_t K, int64_t k, int latency_favored);

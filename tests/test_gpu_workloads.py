@@ -1,6 +1,8 @@
 """GPU parity at the full workload sizes: one LLaMA-7B decoder layer (decode,
 batch sweep, batched launch), the large 8192/28672 shapes, and prefill plus
-long calibration at the MLP shapes. Inputs come from the seeded generator."""
+long calibration at the MLP shapes. Inputs come from the seeded generator.
+Every output of every call is checked against the oracle (its linear runs
+the rows on all host cores); none is sampled."""
 import numpy as np
 import pytest
 
@@ -34,12 +36,11 @@ def test_llama7b_layer_decode(owq, li):
     _run(owq, W, X, spec.k, [x], f"{cfg.name}/{spec.name}")
 
 
-@pytest.mark.parametrize("li", [0, 4, 6])
+@pytest.mark.parametrize("li", range(7))
 def test_llama7b_batch_sweep(owq, li):
     cfg = synth.LLAMA7B_BATCH_SWEEP
     spec, W, X, x = _inputs(cfg, li, 16)
-    _run(owq, W, X, spec.k, [x[:m] for m in cfg.Ms], f"{cfg.name}/{spec.name}",
-         sample=4096 * 4, rng=np.random.default_rng(li))
+    _run(owq, W, X, spec.k, [x[:m] for m in cfg.Ms], f"{cfg.name}/{spec.name}")
 
 
 def test_llama7b_layer_batched_launch(owq):
@@ -68,7 +69,7 @@ def test_llama7b_layer_batched_launch(owq):
         assert host(c).tobytes() == host(b).tobytes()
     # and the batched outputs meet the oracle bound
     o = oracle.pack(synth.weights(cfg.layers[6], cfg.seed(6)), host(layers[6]["weak_idx"]))
-    yr, bnd = oracle.linear_full(o, host(xs[6]))
+    yr, bnd = oracle.linear_rows(o, host(xs[6]))
     check_linear(host(ys[6]), yr, bnd, "batched down_proj")
 
 
@@ -76,13 +77,11 @@ def test_llama7b_layer_batched_launch(owq):
 def test_large_shapes(owq, li):
     cfg = synth.LARGE_SHAPES
     spec, W, X, x = _inputs(cfg, li, 8)
-    _run(owq, W, X, spec.k, [x[:1], x], f"{cfg.name}/{spec.name}", sample=2048,
-         rng=np.random.default_rng(100 + li))
+    _run(owq, W, X, spec.k, [x[:1], x], f"{cfg.name}/{spec.name}")
 
 
 @pytest.mark.parametrize("li", range(2))
 def test_prefill_and_long_calibration(owq, li):
     cfg = synth.LLAMA7B_MLP_PREFILL_CALIB
     spec, W, X, x = _inputs(cfg, li, 2048)
-    _run(owq, W, X, spec.k, [x], f"{cfg.name}/{spec.name}", sample=4096,
-         rng=np.random.default_rng(200 + li))
+    _run(owq, W, X, spec.k, [x], f"{cfg.name}/{spec.name}")

@@ -134,3 +134,28 @@ def test_emitted_bytes_match_effective_bits(orc, N, K, k):
     bits = 8 * (p["qcodes"].nbytes + p["w_weak"].nbytes) / (N * K)
     assert bits == pytest.approx(orc.effective_bits(K, k, True), rel=1e-15)
     assert p["w_weak"].shape == (N, k)
+
+
+@pytest.mark.parametrize("N,K,k,M", [(40, 96, 0, 3), (33, 640, 7, 5), (7, 64, 64, 2)])
+def test_rows_form_equals_pair_form(orc, N, K, k, M):
+    """The threaded row form of the oracle's linear gives every output bit for
+    bit as the (token, row) pair form, for any thread count and row subset, and
+    meets the plain RTN matvec at k = 0 on its own."""
+    rng = np.random.default_rng(N + K + k)
+    W = synth.random_layer(rng, N, K)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    idx = np.sort(rng.choice(K, k, replace=False)).astype(np.int32)
+    p = orc.pack(W, idx)
+    yp, bp = orc.linear_full(p, x)
+    for threads in (1, 3, 0):
+        yr, br = orc.linear_rows(p, x, threads=threads)
+        assert yr.tobytes() == yp.tobytes() and br.tobytes() == bp.tobytes()
+    rows = np.array([N - 1, 0, N // 2], np.int64)
+    yr, br = orc.linear_rows(p, x, rows)
+    assert yr.tobytes() == np.ascontiguousarray(yp[:, rows]).tobytes()
+    if k == 0:
+        codes = orc.unpack_codes(p["qcodes"], K).astype(np.float64)
+        s = p["scales"].view(np.float16).astype(np.float64)
+        z = p["zeros"].astype(np.float64)
+        ref = x.astype(np.float64) @ (s[:, None] * (codes - z[:, None])).T
+        assert np.allclose(orc.linear_rows(p, x)[0], ref, rtol=1e-12, atol=1e-15)
