@@ -20,6 +20,9 @@ from .oracle import (  # noqa: F401
     calibrate_score,
     select_weak,
     pack,
+    pack_search,
+    search_qparams,
+    SEARCH_STEPS,
     unpack_codes,
     linear_pairs,
     linear_full,

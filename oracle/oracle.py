@@ -49,6 +49,9 @@ def load():
         "owq_oracle_calibrate_score": (None, [_P, _I64, _I64, _P, _I64, _P, _P]),
         "owq_oracle_select_weak": (None, [_P, _I64, _I32, _P]),
         "owq_oracle_pack": (None, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P]),
+        "owq_oracle_search_qparams": (None, [_P, _P, _I64, _P, ctypes.c_int, ctypes.c_int, _P, _P]),
+        "owq_oracle_pack_search": (None, [_P, _I64, _I64, _P, _I32, _P, ctypes.c_int, ctypes.c_int,
+                                          _P, _P, _P, _P, ctypes.c_int]),
         "owq_oracle_unpack_codes": (None, [_P, _I64, _I64, _P]),
         "owq_oracle_linear_pairs": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32,
                                            _P, _I64, _P, _P, _I64, _P, _P]),
@@ -153,6 +156,41 @@ def pack(W, weak_idx):
     ww = np.zeros((N, max(k, 1)), np.uint16)
     load().owq_oracle_pack(_ptr(W), N, K, _ptr(idx) if k else None, k,
                            _ptr(q), _ptr(s), _ptr(z), _ptr(ww))
+    return {"qcodes": q, "scales": s, "zeros": z,
+            "w_weak": np.ascontiguousarray(ww[:, :k]), "weak_idx": idx}
+
+
+SEARCH_STEPS = 32  # step factors 1 - a/40, a = 0..31 (1 down to 0.225), of the truncation-aware grid
+
+
+def search_qparams(row, use=None, lam=None, steps: int = SEARCH_STEPS, zsearch: bool = True):
+    """(s16 bits, z) of one row from the truncation-aware grid search."""
+    row = _u16(row)
+    use_a = None if use is None else np.ascontiguousarray(np.asarray(use, dtype=np.uint8))
+    lam_a = None if lam is None else np.ascontiguousarray(np.asarray(lam, dtype=np.float64))
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.uint8)
+    load().owq_oracle_search_qparams(_ptr(row), _ptr(use_a), row.shape[-1], _ptr(lam_a), int(steps),
+                                     1 if zsearch else 0, _ptr(s), _ptr(z))
+    return int(s[0]), int(z[0])
+
+
+def pack_search(W, weak_idx, lam=None, steps: int = SEARCH_STEPS, zsearch: bool = True, threads: int = 0):
+    """pack() with each row's step and zero point from the truncation-aware grid
+    search (optionally weighted by lam, fp64 [K]); rows over OpenMP threads."""
+    W = _u16(W)
+    N, K = W.shape
+    assert K % 32 == 0
+    idx = np.ascontiguousarray(np.asarray(weak_idx, dtype=np.int32))
+    k = idx.shape[0]
+    lam_a = None if lam is None else np.ascontiguousarray(np.asarray(lam, dtype=np.float64))
+    assert lam_a is None or lam_a.shape == (K,)
+    q = np.zeros((N, K // 32, 3), np.uint32)
+    s = np.zeros(N, np.uint16)
+    z = np.zeros(N, np.uint8)
+    ww = np.zeros((N, max(k, 1)), np.uint16)
+    load().owq_oracle_pack_search(_ptr(W), N, K, _ptr(idx) if k else None, k, _ptr(lam_a), int(steps),
+                                  1 if zsearch else 0, _ptr(q), _ptr(s), _ptr(z), _ptr(ww), int(threads))
     return {"qcodes": q, "scales": s, "zeros": z,
             "w_weak": np.ascontiguousarray(ww[:, :k]), "weak_idx": idx}
 

@@ -259,6 +259,22 @@ static int get_code(const uint32_t* grp, int c)
     return v;
 }
 
+/* One row of the latency-favoured storage under the row's (s16, z): codes of
+ * the dense columns, the zero point for the weak ones, packed 32 per group. */
+static void pack_row(const uint16_t* row, const uint8_t* weak, int64_t G, uint16_t s16, uint8_t z,
+                     uint32_t* qrow)
+{
+    for (int64_t g = 0; g < G; g++) {
+        uint32_t* grp = qrow + g * 3;
+        grp[0] = grp[1] = grp[2] = 0;
+        for (int c = 0; c < 32; c++) {
+            int64_t j = g * 32 + c;
+            int code = weak[j] ? (int)z : owq_oracle_code(row[j], s16, z);
+            put_code(grp, c, code);
+        }
+    }
+}
+
 /* Latency-favoured storage: a complete low-precision matrix whose weak columns
  * are zero-filled, plus the weak columns kept separately in fp16 ([PL] "Storage
  * Methods", appendix section 2 pp.10-11). Weak columns are excluded from
@@ -282,15 +298,121 @@ void owq_oracle_pack(const uint16_t* W, int64_t N, int64_t K,
         uint16_t s16;
         uint8_t z;
         owq_oracle_qparams(row, dense, K, &s16, &z);
-        for (int64_t g = 0; g < G; g++) {
-            uint32_t* grp = qcodes + (i * G + g) * 3;
-            grp[0] = grp[1] = grp[2] = 0;
-            for (int c = 0; c < 32; c++) {
-                int64_t j = g * 32 + c;
-                int code = weak[j] ? (int)z : owq_oracle_code(row[j], s16, z);
-                put_code(grp, c, code);
+        pack_row(row, weak, G, s16, z, qcodes + i * G * 3);
+        scales[i] = s16;
+        zeros[i] = z;
+        for (int32_t c = 0; c < k; c++)
+            w_weak[i * k + c] = row[weak_idx[c]];
+    }
+    free(weak);
+    free(dense);
+}
+
+/* ------------------------------------------------- step / zero-point search ---- */
+
+/* Truncation-aware choice of one row's step size and zero point: a 2D grid
+ * search over the step size and the zero point, with round-to-nearest codes
+ * clamped to the 3-bit range, so that a narrower range than min-max can win by
+ * truncating a few large weights ([PL] "Low-precision quantization", paper
+ * "Quantization Configuration Search", pp.4-5; the effect on quality is in
+ * "Quantization quality", p.5). Readings (the pages give neither the grid nor
+ * the objective):
+ *   S1 the grid: steps s_a = fp16(s32 * (1 - a/40)) for a = 0 .. steps-1, with
+ *      s32 = (hi - lo) / 7 the fp32 min-max step of R1/R3 (a = 0 is the min-max
+ *      step itself; the others narrow the range, none widens it; a step that
+ *      rounds to fp16 zero is skipped); zero points z = 0 .. 7 (zsearch != 0),
+ *      or only the min-max zero point of that step (zsearch == 0);
+ *   S2 the objective of a grid point is the row's reconstruction error over its
+ *      dense columns, E = sum_j omega_j (w_j - s (code_j - z))^2 with code_j =
+ *      clamp(rint(w_j / s) + z, 0, 7) as in R4 and omega_j = lambda_j (the
+ *      Hessian diagonal, the output error's diagonal weighting) when lambda is
+ *      given, else 1; each term is (d * d), then times lambda_j, added in
+ *      ascending column order in fp64;
+ *   S3 the smallest E wins; ties go to the smaller a, then the smaller z (the
+ *      order the grid is visited in);
+ *   S4 a degenerate row (hi == lo, or a min-max step that rounds to fp16 zero)
+ *      keeps R2's step 1 and zero point 0.
+ * With steps == 1 and zsearch == 0 the grid is the min-max point alone and the
+ * result is owq_oracle_qparams'. */
+void owq_oracle_search_qparams(const uint16_t* row, const uint8_t* use, int64_t K,
+                               const double* lambda, int steps, int zsearch,
+                               uint16_t* s16, uint8_t* z)
+{
+    float lo = 0.0f; /* R1: the range holds 0 */
+    float hi = 0.0f;
+    for (int64_t j = 0; j < K; j++) {
+        if (use && !use[j])
+            continue;
+        float w = f16_to_f32(row[j]);
+        if (w < lo)
+            lo = w;
+        if (w > hi)
+            hi = w;
+    }
+    *s16 = 0x3c00; /* S4 */
+    *z = 0;
+    if (hi == lo)
+        return;
+    float s_mm = (hi - lo) / 7.0f;
+    if ((owq_oracle_f32_to_f16(s_mm) & 0x7fff) == 0)
+        return;
+    double best = INFINITY;
+    for (int a = 0; a < steps; a++) {
+        float sa32 = s_mm * (1.0f - (float)a / 40.0f); /* S1 */
+        uint16_t sa = owq_oracle_f32_to_f16(sa32);
+        if ((sa & 0x7fff) == 0)
+            continue;
+        float sf = f16_to_f32(sa);
+        double sd = owq_oracle_f16_to_f64(sa);
+        int zmm = 0;
+        if (!zsearch) { /* the min-max zero point of this step (R4) */
+            float zr = rintf((-lo) / sf);
+            zmm = zr < 0.0f ? 0 : zr > 7.0f ? 7 : (int)zr;
+        }
+        for (int zc = zsearch ? 0 : zmm; zc <= (zsearch ? 7 : zmm); zc++) {
+            double E = 0.0; /* S2 */
+            for (int64_t j = 0; j < K; j++) {
+                if (use && !use[j])
+                    continue;
+                int q = owq_oracle_code(row[j], sa, (uint8_t)zc);
+                double d = owq_oracle_f16_to_f64(row[j]) - sd * (double)(q - zc);
+                double t = d * d;
+                if (lambda)
+                    t = lambda[j] * t;
+                E += t;
+            }
+            if (E < best) { /* S3: strict, so the first of equal errors stays */
+                best = E;
+                *s16 = sa;
+                *z = (uint8_t)zc;
             }
         }
+    }
+}
+
+/* owq_oracle_pack with each row's (s16, z) from the search above over its dense
+ * columns (rows spread over OpenMP threads; threads <= 0: the default). */
+void owq_oracle_pack_search(const uint16_t* W, int64_t N, int64_t K,
+                            const int32_t* weak_idx, int32_t k, const double* lambda,
+                            int steps, int zsearch,
+                            uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                            uint16_t* w_weak, int threads)
+{
+    uint8_t* weak = (uint8_t*)calloc((size_t)K, 1);
+    uint8_t* dense = (uint8_t*)malloc((size_t)K);
+    for (int32_t c = 0; c < k; c++)
+        weak[weak_idx[c]] = 1;
+    for (int64_t j = 0; j < K; j++)
+        dense[j] = !weak[j];
+    int64_t G = K / 32;
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t i = 0; i < N; i++) {
+        const uint16_t* row = W + i * K;
+        uint16_t s16;
+        uint8_t z;
+        owq_oracle_search_qparams(row, dense, K, lambda, steps, zsearch, &s16, &z);
+        pack_row(row, weak, G, s16, z, qcodes + i * G * 3);
         scales[i] = s16;
         zeros[i] = z;
         for (int32_t c = 0; c < k; c++)
@@ -387,9 +509,9 @@ void owq_oracle_linear_rows(const uint32_t* qcodes, const uint16_t* scales,
                     bnd += fabs(t);
                 }
                 for (int32_t c = 0; c < k; c++) {
-                    double t = owq_oracle_f16_to_f64(w_weak[i * k + c]) * xm[weak_idx[c]];
-                    acc += t;
-                    bnd += fabs(t);
+                    double tw = owq_oracle_f16_to_f64(w_weak[i * k + c]) * xm[weak_idx[c]];
+                    acc += tw;
+                    bnd += fabs(tw);
                 }
                 y[m * R + r] = acc;
                 bound[m * R + r] = bnd;

@@ -58,6 +58,20 @@ void owq_oracle_pack(const uint16_t* W, int64_t N, int64_t K,
                      uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
                      uint16_t* w_weak);
 /* Inverse of the bit layout: codes [N][K] (values 0..7). */
+/* Truncation-aware (step, zero point) of one row: a 2D grid search minimising
+ * the row's (optionally lambda-weighted) squared reconstruction error over the
+ * columns with use[j] != 0; grid and tie rule in owq_oracle.c (readings S1-S4).
+ * steps = number of step factors 1 - a/40; zsearch = 0 keeps the min-max zero
+ * point of each step. */
+void owq_oracle_search_qparams(const uint16_t* row, const uint8_t* use, int64_t K,
+                               const double* lambda, int steps, int zsearch,
+                               uint16_t* s16, uint8_t* z);
+/* Latency-favoured pack with searched per-row parameters (OpenMP over rows). */
+void owq_oracle_pack_search(const uint16_t* W, int64_t N, int64_t K,
+                            const int32_t* weak_idx, int32_t k, const double* lambda,
+                            int steps, int zsearch,
+                            uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                            uint16_t* w_weak, int threads);
 void owq_oracle_unpack_codes(const uint32_t* qcodes, int64_t N, int64_t K, uint8_t* codes);
 
 /* y and the error bound for P (token m, row i) pairs, from the packed layer.

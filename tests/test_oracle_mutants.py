@@ -24,7 +24,7 @@ MUTANTS = {
     "lambda sums |x| instead of x^2": ("lambda[j] += v * v;", "lambda[j] += fabs(v);"),
     "lambda reads X transposed": ("owq_oracle_f16_to_f64(X[t * K + j]);", "owq_oracle_f16_to_f64(X[j * T + t]);"),
     "range without zero": ("float lo = 0.0f, hi = 0.0f; /* R1 */", "float lo = INFINITY, hi = -INFINITY; /* R1 */"),
-    "step over 8 levels": ("(hi - lo) / 7.0f;", "(hi - lo) / 8.0f;"),
+    "step over 8 levels": ("float s32 = (hi - lo) / 7.0f;", "float s32 = (hi - lo) / 8.0f;"),
     "zero point sign": ("rintf(-lo / sf);", "rintf(lo / sf);"),
     "code rounds down": ("float r = rintf(f16_to_f32(w) / sf);", "float r = floorf(f16_to_f32(w) / sf);"),
     "zero point added before rounding": ("float r = rintf(f16_to_f32(w) / sf);",
@@ -49,6 +49,14 @@ MUTANTS = {
     "bit formulas swapped": ("double extra = latency_favored ? 16.0 : 13.0;",
                              "double extra = latency_favored ? 13.0 : 16.0;"),
     "fp16 rounding truncates": ("double q = rint(ldexp(a, 10 - E));", "double q = floor(ldexp(a, 10 - E));"),
+    "search ignores the weights": ("t = lambda[j] * t;", "t = 1.0 * t;"),
+    "search error not squared": ("double t = d * d;", "double t = fabs(d);"),
+    "search ties to the later grid point": ("if (E < best) { /* S3", "if (E <= best) { /* S3"),
+    "search steps widen the range": ("(1.0f - (float)a / 40.0f)", "(1.0f + (float)a / 40.0f)"),
+    "search keeps zero point 0": ("zc <= (zsearch ? 7 : zmm); zc++)", "zc <= (zsearch ? 0 : zmm); zc++)"),
+    "search error ignores the zero point": ("- sd * (double)(q - zc);", "- sd * (double)q;"),
+    "search fits the weak columns too": ("owq_oracle_search_qparams(row, dense, K, lambda,",
+                                         "owq_oracle_search_qparams(row, NULL, K, lambda,"),
 }
 
 
@@ -62,11 +70,12 @@ def _run_mutant(name, old, new, base):
     with open(os.path.join(work, "oracle", "owq_oracle.c"), "w") as fh:
         fh.write(src.replace(old, new))
     shutil.copytree(os.path.join(ROOT, "tests"), os.path.join(work, "tests"),
-                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutants.py", "test_gpu_*",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutants.py", "test_gpu_*", "test_zz_*",
+                                                  "test_binding_validation.py",
                                                   "test_abi.py", "test_build_resources.py",
                                                   "test_bench_accounting.py"))
     env = dict(os.environ, PYTHONPATH=ROOT)  # the seeded input generator comes from the package
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "tests"],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu", "tests"],
                        cwd=work, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-400:]
 
