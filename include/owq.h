@@ -129,6 +129,33 @@ owq_status owq_pack(const uint16_t* W, int64_t N, int64_t K,
                     uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
                     uint16_t* w_weak, void* stream);
 
+/* owq_pack with each row's step size and zero point chosen by a truncation-aware
+ * 2D grid search over both, before the codes are formed ([PL] "Low-precision
+ * quantization" (paper "Quantization Configuration Search", pp.4-5): a grid
+ * search over step size and zero point with nearest rounding and truncation, to
+ * narrow the range and reduce the reconstruction error; effect on quality: [PL]
+ * "Quantization quality", p.5). Per row, over its dense columns only:
+ *   grid    steps s_a = fp16_rne(s_mm * (1 - a/40)), a = 0..31, where s_mm =
+ *           (hi - lo) / 7 is the fp32 min-max step of the quantiser above (a = 0
+ *           is the min-max step; a step that rounds to fp16 zero is skipped),
+ *           times zero points z = 0..7;
+ *   error   E(a, z) = sum_j omega_j (w_j - s_a (code_j - z))^2 over the dense
+ *           columns in ascending order, code_j = clamp(rint(w_j / s_a) + z, 0, 7),
+ *           omega_j = lambda[j] if lambda is non-NULL, else 1, each term
+ *           (d * d) then times omega_j, summed in fp64;
+ *   choice  the smallest E; ties go to the smaller a, then the smaller z.
+ * A degenerate row (hi == lo, or s_mm rounding to fp16 zero) keeps s = 1, z = 0.
+ * Weights outside the chosen range are truncated to the nearest end code. The
+ * format, weak columns and outputs are owq_pack's; owq_linear reads it unchanged.
+ * lambda: fp64 [K] (e.g. owq_calibrate_score's Hessian diagonal, so that E is
+ * the row's output error under the diagonal Hessian) or NULL (plain squared
+ * weight error). Other arguments and errors as owq_pack. The codes, steps and
+ * zero points are bitwise identical to that definition. */
+owq_status owq_pack_search(const uint16_t* W, int64_t N, int64_t K,
+                           const int32_t* weak_idx, int32_t k, const double* lambda,
+                           uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                           uint16_t* w_weak, void* stream);
+
 /* ----------------------------------------------------------------- linear --- */
 
 /* One packed layer, as produced by owq_pack. The struct itself is HOST memory;

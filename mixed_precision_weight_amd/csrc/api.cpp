@@ -211,6 +211,36 @@ owq_status owq_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* weak
                       "owq_pack launch");
 }
 
+owq_status owq_pack_search(const uint16_t* W, int64_t N, int64_t K, const int32_t* weak_idx, int32_t k,
+                           const double* lambda, uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                           uint16_t* w_weak, void* stream)
+{
+    if (!W || !qcodes || !scales || !zeros)
+        return fail(OWQ_ERR_NULL, "W, qcodes, scales and zeros must be non-NULL");
+    if (N < 1 || N > INT32_MAX)
+        return fail(OWQ_ERR_SHAPE, "N = %lld out of range", (long long)N);
+    owq_status st = check_k_dim(K);
+    if (st != OWQ_OK)
+        return st;
+    if (k < 0 || k > K)
+        return fail(OWQ_ERR_RANGE, "k = %d outside [0, K = %lld]", k, (long long)K);
+    if (k > 0 && (!weak_idx || !w_weak))
+        return fail(OWQ_ERR_NULL, "weak_idx and w_weak must be non-NULL when k > 0");
+    if (!aligned(W, 16) || !aligned(qcodes, 4) || !aligned(scales, 2) || !aligned(lambda, 8) ||
+        (k > 0 && (!aligned(weak_idx, 4) || !aligned(w_weak, 2))))
+        return fail(OWQ_ERR_ALIGN,
+                    "misaligned pointer (W: 16 B, lambda: 8 B, qcodes/weak_idx: 4 B, fp16: 2 B)");
+    st = check_idx_on_host(weak_idx, k, K, (hipStream_t)stream);
+    if (st != OWQ_OK)
+        return st;
+    const int32_t* idx = k > 0 ? weak_idx : nullptr;
+    hipError_t e = owq::launch_search(W, N, K, idx, k, lambda, scales, zeros, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = owq::launch_pack_given(W, N, K, idx, k, qcodes, scales, zeros, k > 0 ? w_weak : nullptr,
+                                   (hipStream_t)stream);
+    return hip_status(e, "owq_pack_search launch");
+}
+
 owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* stream)
 {
     owq_status st = check_layer(L, M, x, y);

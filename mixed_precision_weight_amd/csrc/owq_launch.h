@@ -24,6 +24,14 @@ hipError_t launch_select(const double* score, int64_t K, int32_t k, int32_t* idx
 // --------------------------------------------------------------------- pack --
 hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
                        uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s);
+// The pack with each row's (step, zero point) read from scales / zeros.
+hipError_t launch_pack_given(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
+                             uint32_t* q, const uint16_t* scales, const uint8_t* zeros, uint16_t* ww,
+                             hipStream_t s);
+// Truncation-aware (step, zero point) per row over its dense columns, written to
+// scales / zeros (search.hip). lambda: fp64 [K] column weights, or NULL.
+hipError_t launch_search(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
+                         const double* lambda, uint16_t* scales, uint8_t* zeros, hipStream_t s);
 
 // ------------------------------------------------------------------- linear --
 struct LinearDesc {

@@ -33,7 +33,9 @@ namespace {
 constexpr int kSlot[32] = {1,  6,  2,  7,  3,  8,  4,  9,  5,  10, 11, 16, 12, 17, 13, 18,
                            14, 19, 15, 20, 21, 26, 22, 27, 23, 28, 24, 29, 25, 30, 0,  31};
 
-template <int GPT>
+// kGiven: each row's (step, zero point) is read from scales / zeros (written
+// there before, e.g. by the truncation-aware search) instead of fitted.
+template <int GPT, bool kGiven>
 __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, int64_t N, int64_t K,
                                               const int32_t* __restrict__ idx, int32_t k,
                                               uint32_t* __restrict__ q, uint16_t* __restrict__ scales,
@@ -82,18 +84,23 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
                 }
             }
         }
-        lo = wave_min(lo);
-        hi = wave_max(hi);
-        if (lane == 0) {
-            red[0][wave] = lo;
-            red[1][wave] = hi;
-        }
-        __syncthreads();
-        lo = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
-        hi = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
         uint16_t s16;
         int z;
-        qparams_from_range(lo, hi, s16, z);
+        if (kGiven) {
+            s16 = scales[row];
+            z = zeros[row];
+        } else {
+            lo = wave_min(lo);
+            hi = wave_max(hi);
+            if (lane == 0) {
+                red[0][wave] = lo;
+                red[1][wave] = hi;
+            }
+            __syncthreads();
+            lo = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
+            hi = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+            qparams_from_range(lo, hi, s16, z);
+        }
         const RtnRow rr = make_rtn_row(h2f(s16), z);
 #pragma unroll
         for (int u = 0; u < GPT; u++) {
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
                 dst[2] = o[2];
             }
         }
-        if (tid == 0) {
+        if (!kGiven && tid == 0) {
             scales[row] = s16;
             zeros[row] = (uint8_t)z;
         }
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
 // and no block barrier separates the load from the codes; a block of 4 waves
 // walks 4 rows at a time (grid-stride). Lanes write their groups' 12 bytes next
 // to each other, 768 contiguous bytes per store instruction.
-template <int GPW>
+template <int GPW, bool kGiven>
 __global__ __launch_bounds__(256) void k_pack_w(const uint16_t* __restrict__ W, int64_t N, int64_t K,
                                                 const int32_t* __restrict__ idx, int32_t k,
                                                 uint32_t* __restrict__ q, uint16_t* __restrict__ scales,
@@ -188,11 +195,16 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint16_t* __restrict__ W, 
                 hi2 = __builtin_elementwise_max(hi2, h);
             }
         }
-        float lo = wave_min(fminf((float)lo2.x, (float)lo2.y));
-        float hi = wave_max(fmaxf((float)hi2.x, (float)hi2.y));
         uint16_t s16;
         int z;
-        qparams_from_range(lo, hi, s16, z);
+        if (kGiven) {
+            s16 = scales[row];
+            z = zeros[row];
+        } else {
+            const float lo = wave_min(fminf((float)lo2.x, (float)lo2.y));
+            const float hi = wave_max(fmaxf((float)hi2.x, (float)hi2.y));
+            qparams_from_range(lo, hi, s16, z);
+        }
         const RtnRow rr = make_rtn_row(h2f(s16), z);
 #pragma unroll
         for (int u = 0; u < GPW; u++) {
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint16_t* __restrict__ W, 
                 dst[2] = o[2];
             }
         }
-        if (lane == 0) {
+        if (!kGiven && lane == 0) {
             scales[row] = s16;
             zeros[row] = (uint8_t)z;
         }
@@ -224,33 +236,32 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint16_t* __restrict__ W, 
     }
 }
 
-template <int GPW>
+template <int GPW, bool kGiven>
 hipError_t launch_pack_w(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
                          uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
 {
     const int64_t G = K / 32;
     const int64_t blocks = (N + 3) / 4;
     const unsigned grid = (unsigned)(blocks < 2048 ? blocks : 2048);
-    hipLaunchKernelGGL(k_pack_w<GPW>, dim3(grid), dim3(256), (size_t)G * sizeof(uint32_t), s, W, N, K,
-                       idx, k, q, scales, zeros, ww);
+    hipLaunchKernelGGL((k_pack_w<GPW, kGiven>), dim3(grid), dim3(256), (size_t)G * sizeof(uint32_t), s, W, N,
+                       K, idx, k, q, scales, zeros, ww);
     return hipGetLastError();
 }
 
-template <int GPT>
+template <int GPT, bool kGiven>
 hipError_t launch_pack_t(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
                          uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
 {
     const int64_t G = K / 32;
     const unsigned grid = (unsigned)(N < 4096 ? N : 4096);
-    hipLaunchKernelGGL(k_pack<GPT>, dim3(grid), dim3(256), (size_t)G * sizeof(uint32_t), s, W, N, K,
-                       idx, k, q, scales, zeros, ww);
+    hipLaunchKernelGGL((k_pack<GPT, kGiven>), dim3(grid), dim3(256), (size_t)G * sizeof(uint32_t), s, W, N,
+                       K, idx, k, q, scales, zeros, ww);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
-                       uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
+template <bool kGiven>
+hipError_t launch_pack_any(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
+                           uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
 {
     const int64_t G = K / 32;
     // a wave per row while a lane's groups fit in registers with room to spare
@@ -258,19 +269,36 @@ hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* i
     // block form is faster)
     const int64_t gpw = (G + 63) / 64;  // groups per lane with a wave per row
     if (gpw <= 1)
-        return launch_pack_w<1>(W, N, K, idx, k, q, scales, zeros, ww, s);
+        return launch_pack_w<1, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
     if (gpw <= 2)
-        return launch_pack_w<2>(W, N, K, idx, k, q, scales, zeros, ww, s);
+        return launch_pack_w<2, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
     if (gpw <= 3)
-        return launch_pack_w<3>(W, N, K, idx, k, q, scales, zeros, ww, s);
+        return launch_pack_w<3, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
     const int64_t gpt = (G + 255) / 256;  // K <= 65536 -> gpt <= 8
     if (gpt <= 1)
-        return launch_pack_t<1>(W, N, K, idx, k, q, scales, zeros, ww, s);
+        return launch_pack_t<1, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
     if (gpt <= 2)
-        return launch_pack_t<2>(W, N, K, idx, k, q, scales, zeros, ww, s);
+        return launch_pack_t<2, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
     if (gpt <= 4)
-        return launch_pack_t<4>(W, N, K, idx, k, q, scales, zeros, ww, s);
-    return launch_pack_t<8>(W, N, K, idx, k, q, scales, zeros, ww, s);
+        return launch_pack_t<4, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
+    return launch_pack_t<8, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
+                       uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
+{
+    return launch_pack_any<false>(W, N, K, idx, k, q, scales, zeros, ww, s);
+}
+
+hipError_t launch_pack_given(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
+                             uint32_t* q, const uint16_t* scales, const uint8_t* zeros, uint16_t* ww,
+                             hipStream_t s)
+{
+    // the kernels only read scales / zeros in this form
+    return launch_pack_any<true>(W, N, K, idx, k, q, const_cast<uint16_t*>(scales), const_cast<uint8_t*>(zeros),
+                                 ww, s);
 }
 
 }  // namespace owq

@@ -38,6 +38,7 @@ EXPORTS = {
     "owq_calibrate_score": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "owq_select_weak": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
     "owq_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
+    "owq_pack_search": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P]),
     "owq_linear": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P]),
     "owq_linear_batched": (ctypes.c_int, [ctypes.POINTER(OwqLayer), ctypes.POINTER(_P),
                                           ctypes.POINTER(_P), _I32, _I64, _P]),
@@ -214,6 +215,38 @@ def pack(W: torch.Tensor, weak_idx: torch.Tensor, out: dict | None = None, strea
     _check(lib().owq_pack(_ptr(W), N, K, _ptr(weak_idx) if k else None, k, _ptr(out["qcodes"]),
                           _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["w_weak"]) if k else None,
                           _stream(stream)), "owq_pack")
+    return out
+
+
+def pack_search(W: torch.Tensor, weak_idx: torch.Tensor, lam: torch.Tensor | None = None,
+                out: dict | None = None, stream=None) -> dict:
+    """pack() with each row's step and zero point from the truncation-aware grid
+    search (owq_pack_search); lam: optional fp64 [K] column weights (the Hessian
+    diagonal from calibrate())."""
+    _meta(W, torch.float16, "W")
+    _meta(weak_idx, torch.int32, "weak_idx")
+    if W.dim() != 2 or weak_idx.dim() != 1:
+        raise ValueError(f"W must be 2-D and weak_idx 1-D, got {tuple(W.shape)} and {tuple(weak_idx.shape)}")
+    N, K = W.shape
+    k = weak_idx.numel()
+    if K % 32 or k > K:
+        raise ValueError(f"K = {K} must be a multiple of 32 and k = {k} at most K")
+    if lam is not None:
+        _meta(lam, torch.float64, "lam", (K,))
+    want = _pack_out_shapes(N, K, k)
+    if out is not None:
+        for name in _PACK_OUT:
+            if name not in out:
+                raise ValueError(f"out lacks {name!r}")
+            _meta(out[name], want[name][1], f"out[{name!r}]", want[name][0])
+    _on_device(("W", W), ("weak_idx", weak_idx), ("lam", lam),
+               *[(f"out[{n!r}]", out[n]) for n in (_PACK_OUT if out else ())])
+    if out is None:
+        out = {name: torch.empty(shape, dtype=dt, device=W.device) for name, (shape, dt) in want.items()}
+    out["weak_idx"] = weak_idx
+    _check(lib().owq_pack_search(_ptr(W), N, K, _ptr(weak_idx) if k else None, k, _ptr(lam), _ptr(out["qcodes"]),
+                                 _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["w_weak"]) if k else None,
+                                 _stream(stream)), "owq_pack_search")
     return out
 
 

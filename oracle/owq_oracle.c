@@ -356,6 +356,17 @@ void owq_oracle_search_qparams(const uint16_t* row, const uint8_t* use, int64_t 
     float s_mm = (hi - lo) / 7.0f;
     if ((owq_oracle_f32_to_f16(s_mm) & 0x7fff) == 0)
         return;
+    /* the dense weights, widened once (exactly) for the grid's many passes */
+    int64_t n = 0;
+    float* wf = (float*)malloc((size_t)K * sizeof(float));
+    double* om = (double*)malloc((size_t)K * sizeof(double));
+    for (int64_t j = 0; j < K; j++) {
+        if (use && !use[j])
+            continue;
+        wf[n] = f16_to_f32(row[j]);
+        om[n] = lambda ? lambda[j] : 1.0;
+        n++;
+    }
     double best = INFINITY;
     for (int a = 0; a < steps; a++) {
         float sa32 = s_mm * (1.0f - (float)a / 40.0f); /* S1 */
@@ -371,14 +382,19 @@ void owq_oracle_search_qparams(const uint16_t* row, const uint8_t* use, int64_t 
         }
         for (int zc = zsearch ? 0 : zmm; zc <= (zsearch ? 7 : zmm); zc++) {
             double E = 0.0; /* S2 */
-            for (int64_t j = 0; j < K; j++) {
-                if (use && !use[j])
-                    continue;
-                int q = owq_oracle_code(row[j], sa, (uint8_t)zc);
-                double d = owq_oracle_f16_to_f64(row[j]) - sd * (double)(q - zc);
+            for (int64_t e = 0; e < n; e++) {
+                /* code = clamp(rint(w / s) + z, 0, 7) (R4), as owq_oracle_code */
+                float r = rintf(wf[e] / sf);
+                if (r < -8.0f)
+                    r = -8.0f;
+                if (r > 8.0f)
+                    r = 8.0f;
+                int q = (int)r + zc;
+                q = q < 0 ? 0 : q > 7 ? 7 : q;
+                double d = (double)wf[e] - sd * (double)(q - zc);
                 double t = d * d;
                 if (lambda)
-                    t = lambda[j] * t;
+                    t = om[e] * t;
                 E += t;
             }
             if (E < best) { /* S3: strict, so the first of equal errors stays */
@@ -388,6 +404,8 @@ void owq_oracle_search_qparams(const uint16_t* row, const uint8_t* use, int64_t 
             }
         }
     }
+    free(wf);
+    free(om);
 }
 
 /* owq_oracle_pack with each row's (s16, z) from the search above over its dense

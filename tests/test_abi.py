@@ -106,6 +106,19 @@ def test_pack_validation(lib):
     assert f(FAKE, 8, 64, FAKE, 2, FAKE + 1, FAKE, FAKE, FAKE, None) == 4
 
 
+def test_pack_search_validation(lib):
+    f = lib.owq_pack_search
+    assert f(None, 8, 64, FAKE, 2, None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE, 8, 64, None, 2, None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE, 8, 64, FAKE, 2, None, FAKE, FAKE, FAKE, None, None) == 1
+    assert f(FAKE, 8, 65, FAKE, 2, None, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert f(FAKE, 0, 64, FAKE, 2, None, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert f(FAKE, 8, 64, FAKE, 65, None, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert f(FAKE + 8, 8, 64, FAKE, 2, None, FAKE, FAKE, FAKE, FAKE, None) == 4
+    assert f(FAKE, 8, 64, FAKE, 2, FAKE + 4, FAKE, FAKE, FAKE, FAKE, None) == 4  # lambda: 8 bytes
+    assert f(FAKE, 8, 64, FAKE, 2, None, FAKE + 2, FAKE, FAKE, FAKE, None) == 4
+
+
 def _layer(owq, **kw):
     d = dict(N=8, K=64, k=2, bits=3, qcodes=FAKE, scales=FAKE, zeros=FAKE, weak_idx=FAKE, w_weak=FAKE)
     d.update(kw)

@@ -14,6 +14,7 @@ import pytest
 from mixed_precision_weight_amd import build as B
 
 KERNELS = ("k_gemv", "k_mfv", "k_gemm_dma", "k_gemm", "k_calib_first", "k_colsum_err", "k_finalize", "k_topk", "k_pack",
+           "k_search",
            "k_stream_read")
 
 
@@ -42,3 +43,23 @@ def test_register_budget_allows_resident_waves():
     for n, r in res.items():
         assert 1 <= r["Occupancy"] <= 8, (n, r)
         assert r["VGPRs"] <= 256 and r["AGPRs"] <= 256, (n, r)
+
+
+def test_exact_kernels_round_each_step():
+    """The kernels whose results must equal the definition bit for bit (the
+    calibration's fits and errors, the pack, the step / zero-point search) may not
+    contain a mixed-precision FMA with an fp16 result: the compiler forms one from
+    an fp32 multiply followed by a conversion to fp16, and it rounds the exact
+    product to fp16 once instead of rounding the fp32 product."""
+    import re
+    import subprocess
+    import tempfile
+    flags = [f for f in B.COMMON if f != "-fPIC"] + ["-ffp-contract=off", "-x", "hip", "--cuda-device-only", "-S"]
+    for src in sorted(B.NO_CONTRACT):
+        with tempfile.NamedTemporaryFile(suffix=".s") as out:
+            r = subprocess.run([B.HIPCC] + flags + ["-o", out.name, os.path.join(B.CSRC, src)],
+                               capture_output=True, text=True)
+            assert r.returncode == 0, r.stderr[-2000:]
+            asm = open(out.name).read()
+        bad = re.findall(r"v_(?:fma|mad)_mix(?:lo|hi)_f16[^\n]*", asm)
+        assert not bad, (src, bad[:4])

@@ -49,7 +49,7 @@ MUTANTS = {
     "bit formulas swapped": ("double extra = latency_favored ? 16.0 : 13.0;",
                              "double extra = latency_favored ? 13.0 : 16.0;"),
     "fp16 rounding truncates": ("double q = rint(ldexp(a, 10 - E));", "double q = floor(ldexp(a, 10 - E));"),
-    "search ignores the weights": ("t = lambda[j] * t;", "t = 1.0 * t;"),
+    "search ignores the weights": ("t = om[e] * t;", "t = 1.0 * t;"),
     "search error not squared": ("double t = d * d;", "double t = fabs(d);"),
     "search ties to the later grid point": ("if (E < best) { /* S3", "if (E <= best) { /* S3"),
     "search steps widen the range": ("(1.0f - (float)a / 40.0f)", "(1.0f + (float)a / 40.0f)"),
@@ -57,6 +57,7 @@ MUTANTS = {
     "search error ignores the zero point": ("- sd * (double)(q - zc);", "- sd * (double)q;"),
     "search fits the weak columns too": ("owq_oracle_search_qparams(row, dense, K, lambda,",
                                          "owq_oracle_search_qparams(row, NULL, K, lambda,"),
+    "search rounds the quotient down": ("float r = rintf(wf[e] / sf);", "float r = floorf(wf[e] / sf);"),
 }
 
 
