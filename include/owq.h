@@ -103,6 +103,26 @@ owq_status owq_calibrate_score(const uint16_t* W, int64_t N, int64_t K,
                                double* lambda, double* score,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* owq_calibrate_score for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * buffer the library itself holds on each GPU (a static device array of
+ * owq_calibrate_noalloc_max_workspace() bytes, created when the library is
+ * loaded on that GPU and kept until the process ends; its address is looked up
+ * once per device, on the first call with that device current). The call
+ * makes no allocation. It runs on the CURRENT device, and `stream` must belong
+ * to it. Returns OWQ_ERR_WORKSPACE, before any launch, when
+ * owq_calibrate_workspace_bytes(N, K, T) exceeds that maximum. Every call on a
+ * GPU shares that GPU's buffer: calls that overlap on one GPU (on different
+ * streams, or from different threads) race and give undefined results; calls
+ * ordered on one stream are safe. The buffer's contents from a previous call
+ * are never read. Other arguments and errors as owq_calibrate_score. */
+owq_status owq_calibrate_score_noalloc(const uint16_t* W, int64_t N, int64_t K,
+                                       const uint16_t* X, int64_t T,
+                                       double* lambda, double* score, void* stream);
+/* Bytes of the library-held workspace owq_calibrate_score_noalloc uses. */
+size_t owq_calibrate_noalloc_max_workspace(void);
+
 /* Weak-column selection: the k columns of largest score (ties: the lower column
  * index wins), written to weak_idx[0..k) in strictly ascending order ([PL]
  * "Weak-column selection" (paper p.4): the top-k columns by sensitivity are kept

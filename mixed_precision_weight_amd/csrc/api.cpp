@@ -166,6 +166,34 @@ owq_status owq_calibrate_score(const uint16_t* W, int64_t N, int64_t K, const ui
                       "owq_calibrate_score launch");
 }
 
+owq_status owq_calibrate_score_noalloc(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,
+                                       double* lambda, double* score, void* stream)
+{
+    if (!W || !X || !lambda || !score)
+        return fail(OWQ_ERR_NULL, "W, X, lambda and score must be non-NULL");
+    if (N < 1 || N > INT32_MAX || T < 1)
+        return fail(OWQ_ERR_SHAPE, "N = %lld, T = %lld: need N, T >= 1", (long long)N, (long long)T);
+    owq_status st = check_k_dim(K);
+    if (st != OWQ_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(X, 16) || !aligned(lambda, 8) || !aligned(score, 8))
+        return fail(OWQ_ERR_ALIGN, "misaligned pointer (W, X: 16 B, lambda/score: 8 B)");
+    owq::CalibPlan p = owq::calib_plan(N, K, T);
+    if (p.total > owq::kCalibScratchBytes)
+        return fail(OWQ_ERR_WORKSPACE,
+                    "N = %lld, K = %lld, T = %lld need %zu bytes of workspace; the library's own holds %zu "
+                    "(use owq_calibrate_score with a caller workspace)",
+                    (long long)N, (long long)K, (long long)T, p.total, owq::kCalibScratchBytes);
+    void* ws = nullptr;
+    hipError_t e = owq::calib_scratch(&ws);
+    if (e != hipSuccess)
+        return hip_status(e, "owq_calibrate_score_noalloc: scratch lookup");
+    return hip_status(owq::launch_calibrate(W, N, K, X, T, lambda, score, ws, p, (hipStream_t)stream),
+                      "owq_calibrate_score_noalloc launch");
+}
+
+size_t owq_calibrate_noalloc_max_workspace(void) { return owq::kCalibScratchBytes; }
+
 owq_status owq_select_weak(const double* score, int64_t K, int32_t k, int32_t* weak_idx, void* stream)
 {
     if (!score)

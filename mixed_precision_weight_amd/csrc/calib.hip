@@ -20,8 +20,17 @@
 // and row slices by a fixed-order final pass: results are bitwise deterministic.
 //
 // Built with -ffp-contract=off: the quantiser steps are single IEEE operations.
+#include <mutex>
+
 #include "owq_device.h"
 #include "owq_launch.h"
+
+// Library-owned calibration workspace for callers that cannot allocate
+// (owq_calibrate_score_noalloc). One copy per GPU, created when the library's
+// code object is loaded on that GPU and held until the process ends. In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, once per device (calib_scratch).
+static __device__ __align__(256) unsigned char scratch[owq::kCalibScratchBytes];
 
 namespace owq {
 
@@ -256,6 +265,31 @@ CalibPlan calib_plan(int64_t N, int64_t K, int64_t T)
     o = align256(o + (size_t)N);
     p.total = o;
     return p;
+}
+
+hipError_t calib_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* dev_ptr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!dev_ptr[dev]) {  // first call on this device, with it current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        dev_ptr[dev] = p;
+    }
+    *ptr = dev_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_calibrate(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,

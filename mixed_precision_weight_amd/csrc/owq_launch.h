@@ -17,6 +17,11 @@ CalibPlan calib_plan(int64_t N, int64_t K, int64_t T);
 hipError_t launch_calibrate(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,
                             double* lambda, double* score, void* ws, const CalibPlan& p,
                             hipStream_t s);
+// The library's own calibration workspace on the current device: a file-scope
+// device array of kCalibScratchBytes (256-byte aligned), its address looked up
+// once per device. Returns the HIP error of the lookup, if any.
+constexpr size_t kCalibScratchBytes = (size_t)16 << 20;
+hipError_t calib_scratch(void** ptr);
 
 // ------------------------------------------------------------------- select --
 hipError_t launch_select(const double* score, int64_t K, int32_t k, int32_t* idx, hipStream_t s);

@@ -36,6 +36,8 @@ EXPORTS = {
     "owq_last_error": (ctypes.c_char_p, []),
     "owq_calibrate_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "owq_calibrate_score": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "owq_calibrate_score_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P]),
+    "owq_calibrate_noalloc_max_workspace": (ctypes.c_size_t, []),
     "owq_select_weak": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
     "owq_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
     "owq_pack_search": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P]),
@@ -157,6 +159,29 @@ def calibrate(W: torch.Tensor, X: torch.Tensor, workspace: torch.Tensor | None =
                                      _nbytes(workspace), _stream(stream)),
            "owq_calibrate_score")
     return lam, score
+
+
+def calibrate_noalloc(W: torch.Tensor, X: torch.Tensor, lam: torch.Tensor | None = None,
+                      score: torch.Tensor | None = None, stream=None):
+    """As calibrate(), with the library's own workspace (owq_calibrate_score_noalloc:
+    no device allocation in the library). lam / score: optional fp64 [K] outputs,
+    so that a caller that cannot allocate passes its own."""
+    N, K, T = _calib_shapes(W, X)
+    for name, t in (("lam", lam), ("score", score)):
+        if t is not None:
+            _meta(t, torch.float64, name, (K,))
+    _on_device(("W", W), ("X", X), ("lam", lam), ("score", score))
+    if lam is None:
+        lam = torch.empty(K, dtype=torch.float64, device=W.device)
+    if score is None:
+        score = torch.empty(K, dtype=torch.float64, device=W.device)
+    _check(lib().owq_calibrate_score_noalloc(_ptr(W), N, K, _ptr(X), T, _ptr(lam), _ptr(score), _stream(stream)),
+           "owq_calibrate_score_noalloc")
+    return lam, score
+
+
+def calibrate_noalloc_max_workspace() -> int:
+    return int(lib().owq_calibrate_noalloc_max_workspace())
 
 
 def select_weak(score: torch.Tensor, k: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

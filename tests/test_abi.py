@@ -168,3 +168,18 @@ def test_stream_read_validation(lib):
     assert f(FAKE, 0, FAKE, 1, None) == 2
     assert f(FAKE + 2, 4608, FAKE, 1, None) == 4
     assert f(FAKE, 4620, FAKE, 1, None) == 3   # needs two sink words
+
+
+def test_calibrate_noalloc_validation(lib):
+    f = lib.owq_calibrate_score_noalloc
+    cap = lib.owq_calibrate_noalloc_max_workspace()
+    assert cap >= 1 << 20
+    assert f(None, 64, 64, FAKE, 64, FAKE, FAKE, None) == 1
+    assert f(FAKE, 64, 48, FAKE, 64, FAKE, FAKE, None) == 2
+    assert f(FAKE, 64, 64, FAKE, 0, FAKE, FAKE, None) == 2
+    assert f(FAKE + 2, 64, 64, FAKE, 64, FAKE, FAKE, None) == 4
+    # sizes whose workspace exceeds the library's own are refused before any HIP call
+    N = 1 << 23
+    assert lib.owq_calibrate_workspace_bytes(N, 4096, 16) > cap
+    assert f(FAKE, N, 4096, FAKE, 16, FAKE, FAKE, None) == 6
+    assert "library's own" in _err(lib)
