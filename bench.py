@@ -54,6 +54,13 @@ ROTATE = 8
 PREFILL_M = 2048
 SWEEP_MS = (1, 2, 4, 8, 16)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemv_llama7b_layer_decode_m1_hbm_traffic.txt")
+# vector ALU issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12 lane operations/s (fp32 and fp64 alike)
+ALU_PEAK_TOPS = 39.3
+SEARCH_GRID = 32 * 8          # (step, zero point) grid points per row
+# arithmetic of one grid point and one weight, a fused IEEE operation counted
+# once: the quotient w / s, its rounding, the clamp to [-z, 7 - z], the exact
+# residual w - s (q - z) (one fused multiply-add), its square, the weight, the sum
+SEARCH_OPS_PER_EVAL = 7
 GEMV_SOURCES = ("gemv.hip", "owq_decode.h", "owq_device.h")
 
 
@@ -122,7 +129,92 @@ def cpu_baseline(cfg, min_seconds=10.0):
             break
     return {"value": round(total_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"full 7-linear layer decode at M=1 (202.4M weights), {reps} repetition(s) in "
-                      f"{el:.1f} s, single-threaded C oracle with fp64 accumulation"}
+                      f"{el:.1f} s, single-threaded C oracle with fp64 accumulation",
+            "input_sha256_16": {spec.name: synth.sha256(x)[:16] for spec, _, x in layers}}, layers
+
+
+def host_description():
+    """The host the CPU legs ran on: CPU model, logical CPUs, the process's
+    affinity set, and the OpenMP threads the threaded oracle uses."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or aff
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": aff, "omp_threads": omp}
+
+
+def cpu_extra_legs(threads, layers):
+    """The oracle on the host, beside the GPU: OpenMP over output rows for the
+    decode batch sweep's largest batch (the 7 LLaMA-7B linears packed for the
+    single-thread leg, M = 16), the 8192x8192 large shape at M = 1 and 8, and a
+    prefill sample (the first 64 rows of each MLP linear, all 2048 tokens);
+    single-threaded for the long calibration (both MLP shapes, T = 8192, whole).
+    Each leg is timed once; the numbers are the oracle as it stands."""
+    import numpy as np
+
+    import oracle
+    from mixed_precision_weight_amd import synth
+    legs = {}
+    sweep = synth.LLAMA7B_BATCH_SWEEP
+    xs = [synth.activations(spec, sweep.seed(li), 16) for li, (spec, _, _) in enumerate(layers)]
+    t0 = time.perf_counter()
+    for (spec, p, _), x in zip(layers, xs):
+        oracle.linear_rows(p, x, threads=threads)
+    el = time.perf_counter() - t0
+    nb = sum(eff_bytes(spec.N, spec.K, spec.k, 16) for spec, _, _ in layers)
+    legs["decode_m16_threaded"] = {"value": round(nb / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+                                   "seconds": round(el, 2),
+                                   "sample": "the 7 LLaMA-7B linears at M=16 (batch-sweep inputs), every output"}
+
+    def packed(cfg, li, rows=None):
+        spec = cfg.layers[li]
+        W = synth.weights(spec, cfg.seed(li))
+        if rows is not None:  # the pack is row by row: the first rows alone pack the same
+            W = np.ascontiguousarray(W[:rows])
+        idx = np.sort(np.random.default_rng(li).choice(spec.K, spec.k, replace=False)).astype(np.int32)
+        return spec, oracle.pack(W, idx)
+
+    big = synth.LARGE_SHAPES
+    spec, p = packed(big, 0)
+    x = synth.activations(spec, big.seed(0), 8)
+    for M in (1, 8):
+        t0 = time.perf_counter()
+        oracle.linear_rows(p, x[:M], threads=threads)
+        el = time.perf_counter() - t0
+        legs[f"large_8192x8192_m{M}_threaded"] = {
+            "value": round(eff_bytes(spec.N, spec.K, spec.k, M) / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "seconds": round(el, 3), "sample": f"8192x8192 (k=63) at M={M}, every output"}
+    cfg = synth.LLAMA7B_MLP_PREFILL_CALIB
+    flops, el = 0, 0.0
+    for li, spec in enumerate(cfg.layers):
+        _, p = packed(cfg, li, rows=64)
+        x = synth.activations(spec, cfg.seed(li) + 500, PREFILL_M)
+        t0 = time.perf_counter()
+        oracle.linear_rows(p, x, threads=threads)
+        el += time.perf_counter() - t0
+        flops += 2 * PREFILL_M * 64 * spec.K
+    legs["prefill_sample_threaded"] = {"value": round(flops / el / 1e9, 3), "unit": "GFLOP/s", "cores": threads,
+                                       "seconds": round(el, 2),
+                                       "sample": "first 64 rows x 2048 tokens of 11008x4096 and 4096x11008"}
+    cal = {}
+    for li, spec in enumerate(cfg.layers):
+        W = synth.weights(spec, cfg.seed(li))
+        X = synth.calibration(spec, cfg.seed(li), cfg.T)
+        t0 = time.perf_counter()
+        oracle.calibrate_score(W, X)
+        el = time.perf_counter() - t0
+        cal[f"{spec.name} {spec.N}x{spec.K} T={cfg.T}"] = {
+            "us": round(el * 1e6, 0), "value": round(calib_bytes(spec.N, spec.K, cfg.T) / el / 1e9, 4),
+            "unit": "GB/s"}
+    legs["calibration_single_thread"] = dict(cal, cores=1, sample="the whole long-calibration workload")
+    return legs
 
 
 def hbm_entry(nbytes, seconds, what):
@@ -149,6 +241,10 @@ def main():
                     help="skip the long-calibration (T = 8192) timing")
     ap.add_argument("--copy-reference", action="store_true",
                     help="end with three 512 MiB device copies (counter scaling)")
+    ap.add_argument("--no-search", action="store_true",
+                    help="skip the timing of the truncation-aware pack (owq_pack_search)")
+    ap.add_argument("--no-cpu-extra", action="store_true",
+                    help="skip the threaded and calibration legs of the CPU oracle")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -530,6 +626,45 @@ def main():
         result["kernels"]["large_shapes_decode"] = large
         del big, xb, yb
 
+    # share of the total column score carried by the k selected columns, per
+    # linear (most of the output error comes from a few channels)
+    share = {}
+    for li, s in enumerate(specs):
+        _, score = owq.calibrate(W[li], X[li], workspace=ws)
+        sc = score.cpu().numpy()
+        top = np.sort(sc)[::-1][:s.k].sum()
+        share[f"{s.name} {s.N}x{s.K}"] = {"k": s.k, "K": s.K, "topk_share_of_score": round(float(top / sc.sum()), 4),
+                                          "k_over_K": round(s.k / s.K, 5)}
+    result["topk_score_share"] = share
+
+    if not args.no_search:
+        # truncation-aware (step, zero point) search + pack for the 7 linears,
+        # weighted by the Hessian diagonal (owq_pack_search): ALU-bound
+        print("bench: truncation-aware pack", file=sys.stderr, flush=True)
+        lams, idxs = [], []
+        for li, s in enumerate(specs):
+            lam_l, score_l = owq.calibrate(W[li], X[li], workspace=ws)
+            lams.append(lam_l)
+            idxs.append(owq.select_weak(score_l, s.k))
+        outs = [owq.pack_search(W[li], idxs[li], lams[li]) for li in range(L)]
+        reps = 3
+        ev = [[E() for _ in range(L + 1)] for _ in range(reps)]
+        for r in range(reps):
+            for li in range(L):
+                ev[r][li].record()
+                owq.pack_search(W[li], idxs[li], lams[li], out=outs[li])
+            ev[r][L].record()
+        torch.cuda.synchronize()
+        t = float(np.median([ev[r][0].elapsed_time(ev[r][L]) for r in range(reps)])) / 1e3
+        evals = sum(s.N * (s.K - s.k) * SEARCH_GRID for s in specs)
+        ops = evals * SEARCH_OPS_PER_EVAL
+        result["kernels"]["pack_search"] = {
+            "what": "k_search (32 steps x 8 zero points per row, Hessian-diagonal weighted) + k_pack with the "
+                    "chosen parameters, 7 linears", "us": round(t * 1e6, 1), "bound": "alu",
+            "achieved": round(ops / t / 1e12, 2), "peak": ALU_PEAK_TOPS, "unit": "Tops/s (lane ops)",
+            "frac": round(ops / t / 1e12 / ALU_PEAK_TOPS, 4), "grid_point_evaluations": evals,
+            "ops_per_evaluation": SEARCH_OPS_PER_EVAL}
+
     if args.copy_reference:
         n = 512 << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -541,7 +676,12 @@ def main():
 
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        result["cpu_baseline"], packed_layers = cpu_baseline(cfg, args.cpu_seconds)
+        host = host_description()
+        result["cpu_baseline"]["host"] = host
+        if not args.no_cpu_extra:
+            print("bench: CPU oracle, threaded and calibration legs", file=sys.stderr, flush=True)
+            result["cpu_baseline_extra"] = cpu_extra_legs(host["omp_threads"], packed_layers)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
