@@ -101,8 +101,11 @@ __global__ __launch_bounds__(64 * W * S) void k_mfv(MfvBatch b, int M)
     constexpr int GC = SH::GC, RS = SH::RS, STAGE = SH::STAGE, PT = SH::PT;
     constexpr int DPW = MC * PT / W;  // x loads per wave and chunk
     // the codes are read once per launch; with 16-token x stages non-temporal code
-    // loads (cache policy "nt") keep them from displacing x: 5-7 % faster at
-    // M = 8 and 16, while at M <= 4 they were 1-4 % slower
+    // loads (cache policy "nt") were 5-7 % faster at M = 8 and 16 (1-4 % slower at
+    // M <= 4). They also raise the bytes fetched: a row's code chunk is 192 bytes,
+    // 1.5 cache lines, so two chunks share a line, and without a cached copy the
+    // shared line is fetched again for the second chunk (1.31x / 1.39x of the
+    // algorithmic bytes at M = 8 / 16 against 1.09x / 1.16x with default loads)
     constexpr int kCodePolicy = MC == 16 ? 2 : 0;
     static_assert((MC * PT) % W == 0, "x loads must split evenly over the waves");
     constexpr int CRS = SH::CRS, CQ = SH::CQ, CL = SH::CL;
