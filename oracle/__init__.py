@@ -21,6 +21,8 @@ from .oracle import (  # noqa: F401
     select_weak,
     pack,
     pack_search,
+    pack_storage,
+    linear_storage_rows,
     search_qparams,
     SEARCH_STEPS,
     unpack_codes,

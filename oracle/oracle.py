@@ -52,6 +52,9 @@ def load():
         "owq_oracle_search_qparams": (None, [_P, _P, _I64, _P, ctypes.c_int, ctypes.c_int, _P, _P]),
         "owq_oracle_pack_search": (None, [_P, _I64, _I64, _P, _I32, _P, ctypes.c_int, ctypes.c_int,
                                           _P, _P, _P, _P, ctypes.c_int]),
+        "owq_oracle_pack_storage": (None, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P]),
+        "owq_oracle_linear_storage_rows": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32,
+                                                  _P, _I64, _P, _I64, _P, _P, ctypes.c_int]),
         "owq_oracle_unpack_codes": (None, [_P, _I64, _I64, _P]),
         "owq_oracle_linear_pairs": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32,
                                            _P, _I64, _P, _P, _I64, _P, _P]),
@@ -193,6 +196,51 @@ def pack_search(W, weak_idx, lam=None, steps: int = SEARCH_STEPS, zsearch: bool 
                                   1 if zsearch else 0, _ptr(q), _ptr(s), _ptr(z), _ptr(ww), int(threads))
     return {"qcodes": q, "scales": s, "zeros": z,
             "w_weak": np.ascontiguousarray(ww[:, :k]), "weak_idx": idx}
+
+
+def pack_storage(W, weak_idx):
+    """Storage-favoured form: qcodes uint32 [N][ceil((K-k)/32)][3] of the dense
+    columns only, scales, zeros, w_weak, weak_idx (as pack())."""
+    W = _u16(W)
+    N, K = W.shape
+    assert K % 32 == 0
+    idx = np.ascontiguousarray(np.asarray(weak_idx, dtype=np.int32))
+    k = idx.shape[0]
+    Gd = (K - k + 31) // 32
+    q = np.zeros((N, max(Gd, 1), 3), np.uint32)
+    s = np.zeros(N, np.uint16)
+    z = np.zeros(N, np.uint8)
+    ww = np.zeros((N, max(k, 1)), np.uint16)
+    load().owq_oracle_pack_storage(_ptr(W), N, K, _ptr(idx) if k else None, k, _ptr(q), _ptr(s), _ptr(z), _ptr(ww))
+    return {"qcodes": np.ascontiguousarray(q[:, :Gd]), "scales": s, "zeros": z,
+            "w_weak": np.ascontiguousarray(ww[:, :k]), "weak_idx": idx, "K": K}
+
+
+def linear_storage_rows(layer: dict, x, rows=None, threads: int = 0):
+    """fp64 y and bound [M][len(rows)] of the storage-favoured product (x: [M][K])."""
+    K = int(layer["K"])
+    q = np.ascontiguousarray(layer["qcodes"], dtype=np.uint32)
+    s = _u16(layer["scales"])
+    z = np.ascontiguousarray(layer["zeros"], dtype=np.uint8)
+    idx = np.ascontiguousarray(layer["weak_idx"], dtype=np.int32)
+    ww = _u16(layer["w_weak"])
+    x = _u16(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    M = x.shape[0]
+    assert x.shape[1] == K
+    N = s.shape[0]
+    k = idx.shape[0]
+    assert q.shape[1] == (K - k + 31) // 32
+    rows = np.arange(N, dtype=np.int64) if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    R = rows.shape[0]
+    y = np.zeros((M, R), np.float64)
+    b = np.zeros((M, R), np.float64)
+    qq = q if q.size else np.zeros((N, 1, 3), np.uint32)
+    load().owq_oracle_linear_storage_rows(_ptr(qq), _ptr(s), _ptr(z), N, K, _ptr(idx) if k else None,
+                                          _ptr(ww) if k else None, k, _ptr(x), M, _ptr(rows), R, _ptr(y), _ptr(b),
+                                          int(threads))
+    return y, b
 
 
 def unpack_codes(qcodes, K: int) -> np.ndarray:

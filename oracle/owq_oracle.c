@@ -308,6 +308,104 @@ void owq_oracle_pack(const uint16_t* W, int64_t N, int64_t K,
     free(dense);
 }
 
+/* --------------------------------------------------- storage-favoured form ---- */
+
+/* The storage-favoured representation keeps only the dense columns' codes (the
+ * zero-filled weak columns are removed) next to the fp16 weak columns ([PL]
+ * "Storage Methods", appendix section 2 pp.10-11: it drops the unneeded zeros at
+ * the price of extra work in the product). Readings: each row's (s16, z) is the
+ * latency-favoured pack's (fit over the dense columns, R5); the dense columns'
+ * codes follow in ascending column order, 32 to a group in the R7 layout, and the
+ * last group of a row is filled up with the zero point (it dequantises to 0).
+ * qcodes: [N][ceil((K - k) / 32)][3]. */
+void owq_oracle_pack_storage(const uint16_t* W, int64_t N, int64_t K,
+                             const int32_t* weak_idx, int32_t k,
+                             uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                             uint16_t* w_weak)
+{
+    uint8_t* weak = (uint8_t*)calloc((size_t)K, 1);
+    uint8_t* dense = (uint8_t*)malloc((size_t)K);
+    for (int32_t c = 0; c < k; c++)
+        weak[weak_idx[c]] = 1;
+    for (int64_t j = 0; j < K; j++)
+        dense[j] = !weak[j];
+    int64_t Kd = K - k;
+    int64_t Gd = (Kd + 31) / 32;
+    for (int64_t i = 0; i < N; i++) {
+        const uint16_t* row = W + i * K;
+        uint16_t s16;
+        uint8_t z;
+        owq_oracle_qparams(row, dense, K, &s16, &z);
+        uint32_t* qrow = qcodes + i * Gd * 3;
+        for (int64_t e = 0; e < Gd * 3; e++)
+            qrow[e] = 0;
+        int64_t p = 0; /* position among the dense columns */
+        for (int64_t j = 0; j < K; j++) {
+            if (weak[j])
+                continue;
+            put_code(qrow + (p / 32) * 3, (int)(p % 32), owq_oracle_code(row[j], s16, z));
+            p++;
+        }
+        for (; p < Gd * 32; p++)
+            put_code(qrow + (p / 32) * 3, (int)(p % 32), z);
+        scales[i] = s16;
+        zeros[i] = z;
+        for (int32_t c = 0; c < k; c++)
+            w_weak[i * k + c] = row[weak_idx[c]];
+    }
+    free(weak);
+    free(dense);
+}
+
+/* The product in the storage-favoured form: the dense columns' codes against x
+ * at the dense columns (gathered in ascending order), plus the weak columns, in
+ * fp64, all tokens of the listed rows (OpenMP over rows). y, bound: [M][R]. */
+void owq_oracle_linear_storage_rows(const uint32_t* qcodes, const uint16_t* scales,
+                                    const uint8_t* zeros, int64_t N, int64_t K,
+                                    const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,
+                                    const uint16_t* x, int64_t M,
+                                    const int64_t* rows, int64_t R, double* y, double* bound,
+                                    int threads)
+{
+    (void)N;
+    int64_t Kd = K - k;
+    int64_t Gd = (Kd + 31) / 32;
+    uint8_t* weak = (uint8_t*)calloc((size_t)K, 1);
+    for (int32_t c = 0; c < k; c++)
+        weak[weak_idx[c]] = 1;
+    int64_t* dcol = (int64_t*)malloc((size_t)(Kd > 0 ? Kd : 1) * sizeof(int64_t));
+    int64_t p = 0;
+    for (int64_t j = 0; j < K; j++)
+        if (!weak[j])
+            dcol[p++] = j;
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 4)
+    for (int64_t r = 0; r < R; r++) {
+        int64_t i = rows[r];
+        double s = owq_oracle_f16_to_f64(scales[i]);
+        int z = zeros[i];
+        for (int64_t m = 0; m < M; m++) {
+            const uint16_t* xm = x + m * K;
+            double acc = 0.0, bnd = 0.0;
+            for (int64_t q = 0; q < Kd; q++) {
+                int code = get_code(qcodes + (i * Gd + q / 32) * 3, (int)(q % 32));
+                double t = s * (double)(code - z) * owq_oracle_f16_to_f64(xm[dcol[q]]);
+                acc += t;
+                bnd += fabs(t);
+            }
+            for (int32_t c = 0; c < k; c++) {
+                double tw = owq_oracle_f16_to_f64(w_weak[i * k + c]) * owq_oracle_f16_to_f64(xm[(size_t)weak_idx[c]]);
+                acc += tw;
+                bnd += fabs(tw);
+            }
+            y[m * R + r] = acc;
+            bound[m * R + r] = bnd;
+        }
+    }
+    free(dcol);
+    free(weak);
+}
+
 /* ------------------------------------------------- step / zero-point search ---- */
 
 /* Truncation-aware choice of one row's step size and zero point: a 2D grid

@@ -72,6 +72,21 @@ void owq_oracle_pack_search(const uint16_t* W, int64_t N, int64_t K,
                             int steps, int zsearch,
                             uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
                             uint16_t* w_weak, int threads);
+/* Storage-favoured form: only the dense columns' codes, ascending, 32 per group
+ * (last group filled with the zero point): qcodes [N][ceil((K-k)/32)][3]; the
+ * steps, zero points and weak block are the latency-favoured pack's. */
+void owq_oracle_pack_storage(const uint16_t* W, int64_t N, int64_t K,
+                             const int32_t* weak_idx, int32_t k,
+                             uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                             uint16_t* w_weak);
+/* Its product for every token of the listed rows (OpenMP over rows); x is the
+ * full [M][K] input. y, bound: [M][R]. */
+void owq_oracle_linear_storage_rows(const uint32_t* qcodes, const uint16_t* scales,
+                                    const uint8_t* zeros, int64_t N, int64_t K,
+                                    const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,
+                                    const uint16_t* x, int64_t M,
+                                    const int64_t* rows, int64_t R, double* y, double* bound,
+                                    int threads);
 void owq_oracle_unpack_codes(const uint32_t* qcodes, int64_t N, int64_t K, uint8_t* codes);
 
 /* y and the error bound for P (token m, row i) pairs, from the packed layer.

@@ -39,8 +39,8 @@ MUTANTS = {
                                  "return 1;\n    if (sa < sb)\n        return -1;"),
     "weak codes not zero-filled": ("int code = weak[j] ? (int)z : owq_oracle_code(row[j], s16, z);",
                                    "int code = owq_oracle_code(row[j], s16, z);"),
-    "pack fits the weak columns too": ("owq_oracle_qparams(row, dense, K, &s16, &z);",
-                                       "owq_oracle_qparams(row, NULL, K, &s16, &z);"),
+    "pack fits the weak columns too": ("owq_oracle_qparams(row, dense, K, &s16, &z);\n        pack_row(",
+                                       "owq_oracle_qparams(row, NULL, K, &s16, &z);\n        pack_row("),
     "slot pair order swapped": ("static const int kSlot[32] = {1,  6,", "static const int kSlot[32] = {6,  1,"),
     "linear zero point sign": ("double t = s * (double)(q - z) *", "double t = s * (double)(q + z) *"),
     "linear drops the weak columns": ("double t = owq_oracle_f16_to_f64(w_weak[i * k + c]) *",
@@ -58,6 +58,12 @@ MUTANTS = {
     "search fits the weak columns too": ("owq_oracle_search_qparams(row, dense, K, lambda,",
                                          "owq_oracle_search_qparams(row, NULL, K, lambda,"),
     "search rounds the quotient down": ("float r = rintf(wf[e] / sf);", "float r = floorf(wf[e] / sf);"),
+    "storage fills the tail with code 0": ("put_code(qrow + (p / 32) * 3, (int)(p % 32), z);",
+                                           "put_code(qrow + (p / 32) * 3, (int)(p % 32), 0);"),
+    "storage product gathers x at the position": ("owq_oracle_f16_to_f64(xm[dcol[q]]);",
+                                                  "owq_oracle_f16_to_f64(xm[q]);"),
+    "storage codes fitted on the whole row": ("owq_oracle_qparams(row, dense, K, &s16, &z);\n        uint32_t* qrow",
+                                              "owq_oracle_qparams(row, NULL, K, &s16, &z);\n        uint32_t* qrow"),
 }
 
 
