@@ -626,6 +626,34 @@ def main():
         result["kernels"]["large_shapes_decode"] = large
         del big, xb, yb
 
+    if not args.no_extras:
+        # the storage-favoured form of the same layer at M = 1 (the pages' other
+        # format): the dense codes of K - k columns, x gathered at the dense
+        # columns, the weak columns added after the 3-bit product; 3 launches per
+        # linear, compared with the one launch per layer of the latency form
+        print("bench: storage-favoured decode", file=sys.stderr, flush=True)
+        sto = [owq.pack_storage(W[li], slots[0][li]["weak_idx"]) for li in range(L)]
+        wss = [torch.empty(owq.linear_storage_workspace_bytes(s.K, s.k, 1), dtype=torch.uint8, device=dev)
+               for s in specs]
+        for li in range(L):
+            owq.linear_storage(sto[li], xd[li], yd[li], wss[li])
+        reps = 20
+        a, b = E(), E()
+        a.record()
+        for _ in range(reps):
+            for li in range(L):
+                owq.linear_storage(sto[li], xd[li], yd[li], wss[li])
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / 1e3 / reps
+        sto_bytes = sum(3 * s.N * (s.K - s.k) // 8 + 3 * s.N + 2 * s.N * s.k + 2 * s.K for s in specs)
+        result["kernels"]["decode_storage_form"] = dict(
+            hbm_entry(sto_bytes, t, "storage-favoured form at M=1: x gathered at the dense columns, k_gemv<1> over "
+                                    "K - k columns, weak columns added; 3 launches per linear, 7 linears (one "
+                                    "copy, so partly cache-resident)"),
+            us_latency_form=round(dec_s * 1e6, 2))
+        del sto, wss
+
     # share of the total column score carried by the k selected columns, per
     # linear (most of the output error comes from a few channels)
     share = {}

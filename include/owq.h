@@ -176,6 +176,21 @@ owq_status owq_pack_search(const uint16_t* W, int64_t N, int64_t K,
                            uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
                            uint16_t* w_weak, void* stream);
 
+/* The storage-favoured OWQ form ([PL] "Storage Methods" (paper appendix section
+ * 2, pp.10-11): the zero-filled weak columns are removed from the low-precision
+ * matrix, which saves their 3 bits per weight (3 + 13k/K bits instead of
+ * 3 + 16k/K) at the price of extra work in the product). Row i keeps the codes of
+ * its dense columns only, in ascending column order, 32 to a group in the slot
+ * layout above; the last group of a row is filled with the zero point (it
+ * dequantises to 0). qcodes: uint32 [N][ceil((K - k)/32)][3] (may be NULL when
+ * k == K: no codes). Steps, zero points and the weak block are owq_pack's (each
+ * row fitted on its dense columns); other arguments and errors as owq_pack. The
+ * codes are bitwise identical to owq_pack's with the weak columns dropped. */
+owq_status owq_pack_storage(const uint16_t* W, int64_t N, int64_t K,
+                            const int32_t* weak_idx, int32_t k,
+                            uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                            uint16_t* w_weak, void* stream);
+
 /* ----------------------------------------------------------------- linear --- */
 
 /* One packed layer, as produced by owq_pack. The struct itself is HOST memory;
@@ -214,6 +229,23 @@ owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M,
  * 1 <= count <= 64. */
 owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs,
                               uint16_t* const* ys, int32_t count, int64_t M,
+                              void* stream);
+
+/* Bytes of device workspace owq_linear_storage needs (0 for invalid sizes). */
+size_t owq_linear_storage_workspace_bytes(int64_t K, int32_t k, int64_t M);
+
+/* owq_linear on a layer in the storage-favoured form (owq_pack_storage): the same
+ * product, y[m][i] = s_i sum_{dense j} (q_ij - z_i) x[m][j] + sum_c w_weak[i][c]
+ * x[m][weak_idx[c]], fp32 accumulation, fp16 output. L->K is the full column
+ * count and L->qcodes the storage-form codes (NULL allowed when k == K). The
+ * extra work of this form: x at the dense columns is gathered into the
+ * workspace, the dense product runs as a layer of ceil((K-k)/32)*32 columns, and
+ * the weak columns' product is added to y afterwards (so y is rounded to fp16
+ * twice when 0 < k < K). workspace: >= owq_linear_storage_workspace_bytes(K, k,
+ * M) bytes, 256-byte aligned, contents ignored; calls sharing it must be ordered.
+ * Errors as owq_linear, plus OWQ_ERR_WORKSPACE. */
+owq_status owq_linear_storage(const owq_layer* L, const uint16_t* x, int64_t M,
+                              uint16_t* y, void* workspace, size_t workspace_bytes,
                               void* stream);
 
 /* ------------------------------------------------- measurement reference --- */

@@ -118,6 +118,29 @@ owq::LinearDesc desc_of(const owq_layer* L, const uint16_t* x, uint16_t* y)
 
 }  // namespace
 
+namespace owq {
+
+hipError_t launch_linear_any(const LinearDesc& d, int64_t M, hipStream_t s)
+{
+    if (M >= gemm_min_m())
+        return launch_gemm(d, M, s);
+    // decode kernels, in token slices of the chosen kernel's capacity
+    hipError_t e = hipSuccess;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess;) {
+        const bool mat = decode_on_matrix_cores(M - m0);
+        const int64_t cap = mat ? kMfvMaxM : gemv_max_tokens(d.K);
+        const int64_t mm = M - m0 < cap ? M - m0 : cap;
+        LinearDesc dm = d;
+        dm.x = d.x + m0 * d.K;
+        dm.y = d.y + m0 * d.N;
+        e = mat ? launch_mfv(&dm, 1, (int)mm, s) : launch_gemv(&dm, 1, (int)mm, s);
+        m0 += mm;
+    }
+    return e;
+}
+
+}  // namespace owq
+
 extern "C" {
 
 const char* owq_status_string(owq_status s)
@@ -269,6 +292,65 @@ owq_status owq_pack_search(const uint16_t* W, int64_t N, int64_t K, const int32_
     return hip_status(e, "owq_pack_search launch");
 }
 
+owq_status owq_pack_storage(const uint16_t* W, int64_t N, int64_t K, const int32_t* weak_idx, int32_t k,
+                            uint32_t* qcodes, uint16_t* scales, uint8_t* zeros, uint16_t* w_weak, void* stream)
+{
+    if (!W || !scales || !zeros || (!qcodes && k < K))
+        return fail(OWQ_ERR_NULL, "W, scales, zeros and (unless k == K) qcodes must be non-NULL");
+    if (N < 1 || N > INT32_MAX)
+        return fail(OWQ_ERR_SHAPE, "N = %lld out of range", (long long)N);
+    owq_status st = check_k_dim(K);
+    if (st != OWQ_OK)
+        return st;
+    if (k < 0 || k > K)
+        return fail(OWQ_ERR_RANGE, "k = %d outside [0, K = %lld]", k, (long long)K);
+    if (k > 0 && (!weak_idx || !w_weak))
+        return fail(OWQ_ERR_NULL, "weak_idx and w_weak must be non-NULL when k > 0");
+    if (!aligned(W, 16) || !aligned(qcodes, 4) || !aligned(scales, 2) ||
+        (k > 0 && (!aligned(weak_idx, 4) || !aligned(w_weak, 2))))
+        return fail(OWQ_ERR_ALIGN, "misaligned pointer (W: 16 B, qcodes/weak_idx: 4 B, fp16: 2 B)");
+    st = check_idx_on_host(weak_idx, k, K, (hipStream_t)stream);
+    if (st != OWQ_OK)
+        return st;
+    return hip_status(owq::launch_pack_storage(W, N, K, k > 0 ? weak_idx : nullptr, k, qcodes, scales, zeros,
+                                               k > 0 ? w_weak : nullptr, (hipStream_t)stream),
+                      "owq_pack_storage launch");
+}
+
+size_t owq_linear_storage_workspace_bytes(int64_t K, int32_t k, int64_t M)
+{
+    if (K < 32 || K > kMaxK || K % 32 != 0 || k < 0 || k > K || M < 1 || M > INT32_MAX)
+        return 0;
+    return owq::storage_workspace_bytes(K, k, M);
+}
+
+owq_status owq_linear_storage(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    if (!L)
+        return fail(OWQ_ERR_NULL, "layer is NULL");
+    if (L->k == L->K && L->K >= 32 && !L->qcodes) {  // every column weak: no codes are stored
+        owq_layer tmp = *L;
+        tmp.qcodes = reinterpret_cast<const uint32_t*>(L->scales);
+        return owq_linear_storage(&tmp, x, M, y, workspace, workspace_bytes, stream);
+    }
+    owq_status st = check_layer(L, M, x, y);
+    if (st != OWQ_OK)
+        return st;
+    if (!workspace)
+        return fail(OWQ_ERR_NULL, "workspace must be non-NULL");
+    if (!aligned(workspace, 256))
+        return fail(OWQ_ERR_ALIGN, "misaligned workspace (256 B)");
+    const size_t need = owq::storage_workspace_bytes(L->K, L->k, M);
+    if (workspace_bytes < need)
+        return fail(OWQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    st = check_idx_on_host(L->weak_idx, L->k, L->K, (hipStream_t)stream);
+    if (st != OWQ_OK)
+        return st;
+    return hip_status(owq::launch_linear_storage(desc_of(L, x, y), M, workspace, (hipStream_t)stream),
+                      "owq_linear_storage launch");
+}
+
 owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* stream)
 {
     owq_status st = check_layer(L, M, x, y);
@@ -277,23 +359,7 @@ owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t
     st = check_idx_on_host(L->weak_idx, L->k, L->K, (hipStream_t)stream);
     if (st != OWQ_OK)
         return st;
-    hipStream_t s = (hipStream_t)stream;
-    owq::LinearDesc d = desc_of(L, x, y);
-    if (M >= owq::gemm_min_m())
-        return hip_status(owq::launch_gemm(d, M, s), "owq_linear (matrix-core) launch");
-    // decode kernels, in token slices of the chosen kernel's capacity
-    hipError_t e = hipSuccess;
-    for (int64_t m0 = 0; m0 < M && e == hipSuccess;) {
-        const bool mat = owq::decode_on_matrix_cores(M - m0);
-        const int64_t cap = mat ? owq::kMfvMaxM : owq::gemv_max_tokens(L->K);
-        const int64_t mm = M - m0 < cap ? M - m0 : cap;
-        owq::LinearDesc dm = d;
-        dm.x = x + m0 * L->K;
-        dm.y = y + m0 * L->N;
-        e = mat ? owq::launch_mfv(&dm, 1, (int)mm, s) : owq::launch_gemv(&dm, 1, (int)mm, s);
-        m0 += mm;
-    }
-    return hip_status(e, "owq_linear (decode) launch");
+    return hip_status(owq::launch_linear_any(desc_of(L, x, y), M, (hipStream_t)stream), "owq_linear launch");
 }
 
 owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs, uint16_t* const* ys,

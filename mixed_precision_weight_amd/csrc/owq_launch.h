@@ -71,6 +71,19 @@ bool decode_on_matrix_cores(int64_t M);
 // Matrix-core GEMM for larger M.
 hipError_t launch_gemm(const LinearDesc& d, int64_t M, hipStream_t s);
 
+// The linear on the latency-favoured form for any M: the GEMM from gemm_min_m()
+// tokens, else the decode kernels in token slices (api.cpp).
+hipError_t launch_linear_any(const LinearDesc& d, int64_t M, hipStream_t s);
+
+// ------------------------------------------------------ storage-favoured form --
+// Dense columns rounded up to whole groups; workspace bytes of the product.
+int64_t storage_dense_cols32(int64_t K, int32_t k);
+size_t storage_workspace_bytes(int64_t K, int32_t k, int64_t M);
+hipError_t launch_pack_storage(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
+                               uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s);
+// d: the layer with K its full column count and q its storage-form codes.
+hipError_t launch_linear_storage(const LinearDesc& d, int64_t M, void* ws, hipStream_t s);
+
 // read-only streaming reference (stream.hip): one word per 4608-byte wavefront
 int64_t stream_read_sink_words(int64_t bytes);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);

@@ -41,6 +41,9 @@ EXPORTS = {
     "owq_select_weak": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
     "owq_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
     "owq_pack_search": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P]),
+    "owq_pack_storage": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
+    "owq_linear_storage_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I64]),
+    "owq_linear_storage": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "owq_linear": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P]),
     "owq_linear_batched": (ctypes.c_int, [ctypes.POINTER(OwqLayer), ctypes.POINTER(_P),
                                           ctypes.POINTER(_P), _I32, _I64, _P]),
@@ -273,6 +276,73 @@ def pack_search(W: torch.Tensor, weak_idx: torch.Tensor, lam: torch.Tensor | Non
                                  _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["w_weak"]) if k else None,
                                  _stream(stream)), "owq_pack_search")
     return out
+
+
+# ------------------------------------------------------- storage-favoured form
+
+
+def pack_storage(W: torch.Tensor, weak_idx: torch.Tensor, out: dict | None = None, stream=None) -> dict:
+    """Storage-favoured packed layer (owq_pack_storage): qcodes int32
+    [N][ceil((K-k)/32)][3] of the dense columns only, scales, zeros, w_weak,
+    weak_idx, and "K" (the full column count)."""
+    _meta(W, torch.float16, "W")
+    _meta(weak_idx, torch.int32, "weak_idx")
+    if W.dim() != 2 or weak_idx.dim() != 1:
+        raise ValueError(f"W must be 2-D and weak_idx 1-D, got {tuple(W.shape)} and {tuple(weak_idx.shape)}")
+    N, K = W.shape
+    k = weak_idx.numel()
+    if K % 32 or k > K:
+        raise ValueError(f"K = {K} must be a multiple of 32 and k = {k} at most K")
+    want = _pack_out_shapes(N, K, k)
+    want["qcodes"] = ((N, (K - k + 31) // 32, 3), torch.int32)
+    if out is not None:
+        for name in _PACK_OUT:
+            if name not in out:
+                raise ValueError(f"out lacks {name!r}")
+            _meta(out[name], want[name][1], f"out[{name!r}]", want[name][0])
+    _on_device(("W", W), ("weak_idx", weak_idx), *[(f"out[{n!r}]", out[n]) for n in (_PACK_OUT if out else ())])
+    if out is None:
+        out = {name: torch.empty(shape, dtype=dt, device=W.device) for name, (shape, dt) in want.items()}
+    out["weak_idx"] = weak_idx
+    out["K"] = K
+    q = out["qcodes"]
+    _check(lib().owq_pack_storage(_ptr(W), N, K, _ptr(weak_idx) if k else None, k, _ptr(q) if q.numel() else None,
+                                  _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["w_weak"]) if k else None,
+                                  _stream(stream)), "owq_pack_storage")
+    return out
+
+
+def linear_storage_workspace_bytes(K: int, k: int, M: int) -> int:
+    return int(lib().owq_linear_storage_workspace_bytes(K, k, M))
+
+
+def linear_storage(layer: dict, x: torch.Tensor, y: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = x W^T for a layer in the storage-favoured form (owq_linear_storage)."""
+    if "K" not in layer:
+        raise ValueError("layer lacks 'K' (the full column count of the storage-favoured form)")
+    K = int(layer["K"])
+    q = _meta(layer["qcodes"], torch.int32, "qcodes")
+    idx = _meta(layer["weak_idx"], torch.int32, "weak_idx")
+    N, k = q.shape[0], idx.numel()
+    if q.dim() != 3 or tuple(q.shape[1:]) != ((K - k + 31) // 32, 3) or idx.dim() != 1:
+        raise ValueError(f"qcodes {tuple(q.shape)} / weak_idx {tuple(idx.shape)} do not fit K = {K}")
+    for name, (shape, dt) in _pack_out_shapes(N, K, k).items():
+        if name != "qcodes":
+            _meta(layer[name], dt, name, shape)
+    M = _xy_shapes(N, K, x, y)
+    if workspace is not None:
+        _meta(workspace, torch.uint8, "workspace")
+    _on_device(("x", x), ("y", y), ("workspace", workspace), *_layer_named(layer))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(linear_storage_workspace_bytes(K, k, M), dtype=torch.uint8, device=x.device)
+    L = OwqLayer(N, K, k, 3, q.data_ptr() if q.numel() else None, layer["scales"].data_ptr(),
+                 layer["zeros"].data_ptr(), idx.data_ptr() if k else None, layer["w_weak"].data_ptr() if k else None)
+    _check(lib().owq_linear_storage(ctypes.byref(L), _ptr(x), M, _ptr(y), _ptr(workspace), _nbytes(workspace),
+                                    _stream(stream)), "owq_linear_storage")
+    return y
 
 
 # ---------------------------------------------------------------------- linear

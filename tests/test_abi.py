@@ -119,6 +119,30 @@ def test_pack_search_validation(lib):
     assert f(FAKE, 8, 64, FAKE, 2, None, FAKE + 2, FAKE, FAKE, FAKE, None) == 4
 
 
+def test_pack_storage_validation(lib):
+    f = lib.owq_pack_storage
+    assert f(None, 8, 64, FAKE, 2, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE, 8, 64, FAKE, 2, None, FAKE, FAKE, FAKE, None) == 1   # codes needed unless k == K
+    assert f(FAKE, 8, 65, FAKE, 2, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert f(FAKE, 8, 64, FAKE, 65, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert f(FAKE + 8, 8, 64, FAKE, 2, FAKE, FAKE, FAKE, FAKE, None) == 4
+
+
+def test_linear_storage_validation(lib):
+    from mixed_precision_weight_amd import owq
+    assert lib.owq_linear_storage_workspace_bytes(4096, 32, 1) >= 2 * (4096 - 32)
+    assert lib.owq_linear_storage_workspace_bytes(4096, 4097, 1) == 0
+    assert lib.owq_linear_storage_workspace_bytes(4100, 32, 1) == 0
+    f = lib.owq_linear_storage
+    ws = lib.owq_linear_storage_workspace_bytes(64, 2, 3)
+    L = _layer(owq)
+    assert f(None, FAKE, 3, FAKE, FAKE, ws, None) == 1
+    assert f(L, FAKE, 3, FAKE, None, ws, None) == 1
+    assert f(L, FAKE, 3, FAKE, FAKE, ws - 1, None) == 6
+    assert f(L, FAKE, 3, FAKE, FAKE + 16, ws, None) == 4
+    assert f(_layer(owq, K=48), FAKE, 3, FAKE, FAKE, ws, None) == 2
+
+
 def _layer(owq, **kw):
     d = dict(N=8, K=64, k=2, bits=3, qcodes=FAKE, scales=FAKE, zeros=FAKE, weak_idx=FAKE, w_weak=FAKE)
     d.update(kw)
