@@ -29,5 +29,6 @@ from .oracle import (  # noqa: F401
     linear_pairs,
     linear_full,
     linear_rows,
+    linear_backward,
     effective_bits,
 )

@@ -55,6 +55,8 @@ def load():
         "owq_oracle_pack_storage": (None, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P]),
         "owq_oracle_linear_storage_rows": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32,
                                                   _P, _I64, _P, _I64, _P, _P, ctypes.c_int]),
+        "owq_oracle_linear_backward": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32, _P, _P, _I64,
+                                              _P, _P, _P, _P, ctypes.c_int]),
         "owq_oracle_unpack_codes": (None, [_P, _I64, _I64, _P]),
         "owq_oracle_linear_pairs": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32,
                                            _P, _I64, _P, _P, _I64, _P, _P]),
@@ -241,6 +243,36 @@ def linear_storage_rows(layer: dict, x, rows=None, threads: int = 0):
                                           _ptr(ww) if k else None, k, _ptr(x), M, _ptr(rows), R, _ptr(y), _ptr(b),
                                           int(threads))
     return y, b
+
+
+def linear_backward(layer: dict, x, dy, want_dx: bool = True, want_dw: bool = True, threads: int = 0):
+    """fp64 (dx [M][K], dx_bound, dw_weak [N][k], dw_bound) of the weak-column-tuning
+    backward for upstream gradient dy [M][N] (fp16) and input x [M][K] (fp16)."""
+    q = np.ascontiguousarray(layer["qcodes"], dtype=np.uint32)
+    s = _u16(layer["scales"])
+    z = np.ascontiguousarray(layer["zeros"], dtype=np.uint8)
+    idx = np.ascontiguousarray(layer["weak_idx"], dtype=np.int32)
+    ww = _u16(layer["w_weak"])
+    x = _u16(x)
+    dy = _u16(dy)
+    if x.ndim == 1:
+        x = x[None, :]
+    if dy.ndim == 1:
+        dy = dy[None, :]
+    M, K = x.shape
+    N = q.shape[0]
+    assert q.shape[1] * 32 == K and dy.shape == (M, N)
+    k = idx.shape[0]
+    dx = np.zeros((M, K), np.float64) if want_dx else None
+    dxb = np.zeros((M, K), np.float64) if want_dx else None
+    dw = np.zeros((N, max(k, 1)), np.float64) if want_dw else None
+    dwb = np.zeros((N, max(k, 1)), np.float64) if want_dw else None
+    load().owq_oracle_linear_backward(_ptr(q), _ptr(s), _ptr(z), N, K, _ptr(idx) if k else None,
+                                      _ptr(ww) if k else None, k, _ptr(x), _ptr(dy), M, _ptr(dx), _ptr(dxb),
+                                      _ptr(dw), _ptr(dwb), int(threads))
+    if want_dw:
+        dw, dwb = np.ascontiguousarray(dw[:, :k]), np.ascontiguousarray(dwb[:, :k])
+    return dx, dxb, dw, dwb
 
 
 def unpack_codes(qcodes, K: int) -> np.ndarray:

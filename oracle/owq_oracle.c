@@ -406,6 +406,70 @@ void owq_oracle_linear_storage_rows(const uint32_t* qcodes, const uint16_t* scal
     free(weak);
 }
 
+/* ------------------------------------------------ weak-column tuning: backward ---- */
+
+/* Weak Column Tuning trains only the fp16 weak columns and keeps the 3-bit dense
+ * matrix frozen ([PL] "Weak Column Tuning" (paper "PEFT with Weak Column Tuning",
+ * p.5); the trainable block is N x k: "Learnable Parameters", appendix section 3,
+ * p.13). For y = x W^T with W the dequantised dense matrix (0 at the weak
+ * columns) plus the weak columns, and an upstream gradient dy [M][N]:
+ *   dx[m][j]      = sum_i dy[m][i] W[i][j]          (the gradient to the layer input)
+ *   dw_weak[i][c] = sum_m dy[m][i] x[m][idx_c]      (the gradient of the weak block)
+ * in fp64 from the packed bytes; the bounds are the sums of the terms' absolute
+ * values. dx, dx_bound: [M][K]; dw, dw_bound: [N][k]. Either pair may be NULL.
+ * OpenMP over columns (dx) and rows (dw); each output is one sum in index order. */
+void owq_oracle_linear_backward(const uint32_t* qcodes, const uint16_t* scales,
+                                const uint8_t* zeros, int64_t N, int64_t K,
+                                const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,
+                                const uint16_t* x, const uint16_t* dy, int64_t M,
+                                double* dx, double* dx_bound, double* dw, double* dw_bound,
+                                int threads)
+{
+    int64_t G = K / 32;
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+    if (dx) {
+        /* the whole matrix W once, row-major, in fp64 */
+        double* Wf = (double*)malloc((size_t)(N * K) * sizeof(double));
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t i = 0; i < N; i++) {
+            double s = owq_oracle_f16_to_f64(scales[i]);
+            int z = zeros[i];
+            for (int64_t j = 0; j < K; j++)
+                Wf[i * K + j] = s * (double)(get_code(qcodes + (i * G + j / 32) * 3, (int)(j % 32)) - z);
+            for (int32_t c = 0; c < k; c++)
+                Wf[i * K + weak_idx[c]] += owq_oracle_f16_to_f64(w_weak[i * k + c]);
+        }
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 16)
+        for (int64_t j = 0; j < K; j++)
+            for (int64_t m = 0; m < M; m++) {
+                double acc = 0.0, bnd = 0.0;
+                for (int64_t i = 0; i < N; i++) {
+                    double t = owq_oracle_f16_to_f64(dy[m * N + i]) * Wf[i * K + j];
+                    acc += t;
+                    bnd += fabs(t);
+                }
+                dx[m * K + j] = acc;
+                dx_bound[m * K + j] = bnd;
+            }
+        free(Wf);
+    }
+    if (dw) {
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 16)
+        for (int64_t i = 0; i < N; i++)
+            for (int32_t c = 0; c < k; c++) {
+                double acc = 0.0, bnd = 0.0;
+                for (int64_t m = 0; m < M; m++) {
+                    double t = owq_oracle_f16_to_f64(dy[m * N + i]) *
+                               owq_oracle_f16_to_f64(x[m * K + weak_idx[c]]);
+                    acc += t;
+                    bnd += fabs(t);
+                }
+                dw[i * k + c] = acc;
+                dw_bound[i * k + c] = bnd;
+            }
+    }
+}
+
 /* ------------------------------------------------- step / zero-point search ---- */
 
 /* Truncation-aware choice of one row's step size and zero point: a 2D grid

@@ -87,6 +87,15 @@ void owq_oracle_linear_storage_rows(const uint32_t* qcodes, const uint16_t* scal
                                     const uint16_t* x, int64_t M,
                                     const int64_t* rows, int64_t R, double* y, double* bound,
                                     int threads);
+/* Backward of the mixed-precision linear for weak-column tuning: dx = dy W
+ * ([M][K]) and dw_weak = dy^T x[:, idx] ([N][k]), fp64, with bounds (sums of
+ * |terms|); either output pair may be NULL. OpenMP over columns / rows. */
+void owq_oracle_linear_backward(const uint32_t* qcodes, const uint16_t* scales,
+                                const uint8_t* zeros, int64_t N, int64_t K,
+                                const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,
+                                const uint16_t* x, const uint16_t* dy, int64_t M,
+                                double* dx, double* dx_bound, double* dw, double* dw_bound,
+                                int threads);
 void owq_oracle_unpack_codes(const uint32_t* qcodes, int64_t N, int64_t K, uint8_t* codes);
 
 /* y and the error bound for P (token m, row i) pairs, from the packed layer.

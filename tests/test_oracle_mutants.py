@@ -58,6 +58,12 @@ MUTANTS = {
     "search fits the weak columns too": ("owq_oracle_search_qparams(row, dense, K, lambda,",
                                          "owq_oracle_search_qparams(row, NULL, K, lambda,"),
     "search rounds the quotient down": ("float r = rintf(wf[e] / sf);", "float r = floorf(wf[e] / sf);"),
+    "backward drops the weak columns": ("Wf[i * K + weak_idx[c]] += owq_oracle_f16_to_f64(w_weak[i * k + c]);",
+                                        "Wf[i * K + weak_idx[c]] += 0.0 * owq_oracle_f16_to_f64(w_weak[i * k + c]);"),
+    "backward zero point sign": ("Wf[i * K + j] = s * (double)(get_code(qcodes + (i * G + j / 32) * 3, (int)(j % 32)) - z);",
+                                 "Wf[i * K + j] = s * (double)(get_code(qcodes + (i * G + j / 32) * 3, (int)(j % 32)) + z);"),
+    "weak gradient gathers x at c": ("owq_oracle_f16_to_f64(x[m * K + weak_idx[c]]);",
+                                     "owq_oracle_f16_to_f64(x[m * K + c]);"),
     "storage fills the tail with code 0": ("put_code(qrow + (p / 32) * 3, (int)(p % 32), z);",
                                            "put_code(qrow + (p / 32) * 3, (int)(p % 32), 0);"),
     "storage product gathers x at the position": ("owq_oracle_f16_to_f64(xm[dcol[q]]);",
