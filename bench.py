@@ -654,6 +654,33 @@ def main():
             us_latency_form=round(dec_s * 1e6, 2))
         del sto, wss
 
+    if not args.no_extras:
+        # weak-column-tuning backward of the layer: dx = dy W and dw_weak = dy^T
+        # x[:, idx] for the 7 linears, at M = 1 and 16 (8 packed copies rotated)
+        print("bench: weak-column-tuning backward", file=sys.stderr, flush=True)
+        bw = {}
+        bws = torch.empty(max(owq.linear_backward_workspace_bytes(s.N, s.K, s.k) for s in specs), dtype=torch.uint8,
+                          device=dev)
+        for M in (1, 16):
+            dys = [torch.randn((M, s.N), device=dev).to(torch.float16) for s in specs]
+            for li in range(L):
+                owq.linear_backward(slots[0][li], x1[li][:M], dys[li], workspace=bws)
+            reps = ROTATE
+            a, b = E(), E()
+            a.record()
+            for r in range(reps):
+                for li in range(L):
+                    owq.linear_backward(slots[r % ROTATE][li], x1[li][:M], dys[li], workspace=bws)
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3 / reps
+            nb = sum(3 * s.N * s.K // 8 + 3 * s.N + 2 * s.N * s.k + 2 * M * s.N + 2 * M * s.K + 2 * M * s.k
+                     + 4 * s.N * s.k for s in specs)
+            bw[f"M={M}"] = hbm_entry(nb, t, "k_bwd_dx_part + k_bwd_weak_part + k_bwd_dx_finalize (dx) and k_bwd_dw "
+                                            "(dw_weak), 7 linears, one call each")
+        result["kernels"]["backward_weak_column_tuning"] = bw
+        del bws
+
     # share of the total column score carried by the k selected columns, per
     # linear (most of the output error comes from a few channels)
     share = {}

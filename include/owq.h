@@ -248,6 +248,31 @@ owq_status owq_linear_storage(const owq_layer* L, const uint16_t* x, int64_t M,
                               uint16_t* y, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* ------------------------------------------ backward (weak-column tuning) --- */
+
+/* Bytes of device workspace owq_linear_backward needs to produce dx (0 for
+ * invalid sizes). */
+size_t owq_linear_backward_workspace_bytes(int64_t N, int64_t K, int32_t k);
+
+/* Backward of owq_linear for Weak Column Tuning, which trains only the fp16 weak
+ * columns and keeps the 3-bit dense matrix frozen ([PL] "Weak Column Tuning"
+ * (paper "PEFT with Weak Column Tuning", p.5); the trainable block is w_weak,
+ * N x k: "Learnable Parameters" (appendix section 3, p.13)). With W the
+ * dequantised dense matrix (0 at the weak columns) plus the weak columns and the
+ * upstream gradient dy = dL/dy:
+ *   dx[m][j]      = sum_i dy[m][i] W[i][j]         fp32 sums, fp16 [M][K]
+ *   dw_weak[i][c] = sum_m dy[m][i] x[m][idx_c]     fp32 sums, fp32 [N][k]
+ * L: HOST pointer to the packed layer (latency-favoured form); x: fp16 [M][K]
+ * (the layer input; read only for dw_weak, may be NULL otherwise); dy: fp16
+ * [M][N]; dx (may be NULL) and dw_weak (may be NULL) are outputs. dx is the
+ * transposed 3-bit product: the codes are streamed once per 4 tokens and summed
+ * over row slices in a fixed order (bitwise deterministic). workspace: >=
+ * owq_linear_backward_workspace_bytes(N, K, k) bytes, 256-byte aligned, needed
+ * only for dx. Errors as owq_linear, plus OWQ_ERR_WORKSPACE. */
+owq_status owq_linear_backward(const owq_layer* L, const uint16_t* x, const uint16_t* dy,
+                               int64_t M, uint16_t* dx, float* dw_weak,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------- measurement reference --- */
 
 /* Not a step of the method: a read-only HBM stream with the M = 1 decode

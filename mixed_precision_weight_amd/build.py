@@ -32,8 +32,8 @@ NO_CONTRACT = {"calib.hip", "pack.hip", "search.hip", "storage.hip"}
 RESOURCES = os.path.join(BUILD, "kernel_resources.json")
 _REMARK = re.compile(r"remark: +(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
                      r"Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]): (\S+)")
-SOURCES = ["api.cpp", "calib.hip", "topk.hip", "pack.hip", "search.hip", "storage.hip", "gemv.hip", "mfv.hip",
-           "gemm.hip", "stream.hip"]
+SOURCES = ["api.cpp", "calib.hip", "topk.hip", "pack.hip", "search.hip", "storage.hip", "backward.hip", "gemv.hip",
+           "mfv.hip", "gemm.hip", "stream.hip"]
 
 
 def _resources(stderr: str) -> dict:

@@ -351,6 +351,43 @@ owq_status owq_linear_storage(const owq_layer* L, const uint16_t* x, int64_t M, 
                       "owq_linear_storage launch");
 }
 
+size_t owq_linear_backward_workspace_bytes(int64_t N, int64_t K, int32_t k)
+{
+    if (N < 1 || N > INT32_MAX || K < 32 || K > kMaxK || K % 32 != 0 || k < 0 || k > K)
+        return 0;
+    return owq::bwd_plan(N, K, k).total;
+}
+
+owq_status owq_linear_backward(const owq_layer* L, const uint16_t* x, const uint16_t* dy, int64_t M, uint16_t* dx,
+                               float* dw_weak, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!L || !dy)
+        return fail(OWQ_ERR_NULL, "layer and dy must be non-NULL");
+    // check_layer wants an x and a y: x is read only for dw_weak, y is not used
+    owq_status st = check_layer(L, M, x ? x : dy, dy);
+    if (st != OWQ_OK)
+        return st;
+    if (dw_weak && L->k > 0 && !x)
+        return fail(OWQ_ERR_NULL, "x must be non-NULL for dw_weak");
+    if ((dx && !aligned(dx, 2)) || (dw_weak && !aligned(dw_weak, 4)) || !aligned(dy, 2))
+        return fail(OWQ_ERR_ALIGN, "misaligned pointer (dy, dx: 2 B, dw_weak: 4 B)");
+    owq::BwdPlan p = owq::bwd_plan(L->N, L->K, L->k);
+    if (dx) {
+        if (!workspace)
+            return fail(OWQ_ERR_NULL, "workspace must be non-NULL when dx is requested");
+        if (!aligned(workspace, 256))
+            return fail(OWQ_ERR_ALIGN, "misaligned workspace (256 B)");
+        if (workspace_bytes < p.total)
+            return fail(OWQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, p.total);
+    }
+    st = check_idx_on_host(L->weak_idx, L->k, L->K, (hipStream_t)stream);
+    if (st != OWQ_OK)
+        return st;
+    owq::LinearDesc d = desc_of(L, x, nullptr);
+    return hip_status(owq::launch_linear_backward(d, dy, M, dx, dw_weak, workspace, p, (hipStream_t)stream),
+                      "owq_linear_backward launch");
+}
+
 owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* stream)
 {
     owq_status st = check_layer(L, M, x, y);

@@ -84,6 +84,17 @@ hipError_t launch_pack_storage(const uint16_t* W, int64_t N, int64_t K, const in
 // d: the layer with K its full column count and q its storage-form codes.
 hipError_t launch_linear_storage(const LinearDesc& d, int64_t M, void* ws, hipStream_t s);
 
+// ------------------------------------------ backward (weak-column tuning) --
+struct BwdPlan {
+    int64_t slices, rows_per_slice;  // row slices of the transposed product
+    size_t off_p, off_pw, total;     // workspace byte offsets / size
+};
+BwdPlan bwd_plan(int64_t N, int64_t K, int32_t k);
+// dx = dy W (fp16 [M][K], may be NULL) and dw_weak = dy^T x[:, idx] (fp32 [N][k],
+// may be NULL); d.x is the layer input (read for dw), d.y unused.
+hipError_t launch_linear_backward(const LinearDesc& d, const uint16_t* dy, int64_t M, uint16_t* dx, float* dw,
+                                  void* ws, const BwdPlan& p, hipStream_t s);
+
 // read-only streaming reference (stream.hip): one word per 4608-byte wavefront
 int64_t stream_read_sink_words(int64_t bytes);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);

@@ -44,6 +44,9 @@ EXPORTS = {
     "owq_pack_storage": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
     "owq_linear_storage_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I64]),
     "owq_linear_storage": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "owq_linear_backward_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
+    "owq_linear_backward": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _P, _I64, _P, _P, _P, ctypes.c_size_t,
+                                           _P]),
     "owq_linear": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P]),
     "owq_linear_batched": (ctypes.c_int, [ctypes.POINTER(OwqLayer), ctypes.POINTER(_P),
                                           ctypes.POINTER(_P), _I32, _I64, _P]),
@@ -410,6 +413,39 @@ def linear(layer: dict, x: torch.Tensor, y: torch.Tensor | None = None, stream=N
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     _check(lib().owq_linear(ctypes.byref(L), _ptr(x), M, _ptr(y), _stream(stream)), "owq_linear")
     return y
+
+
+def linear_backward_workspace_bytes(N: int, K: int, k: int) -> int:
+    return int(lib().owq_linear_backward_workspace_bytes(N, K, k))
+
+
+def linear_backward(layer: dict, x: torch.Tensor | None, dy: torch.Tensor, want_dx: bool = True,
+                    want_dw: bool = True, workspace: torch.Tensor | None = None, stream=None):
+    """Weak-column-tuning backward (owq_linear_backward): (dx fp16 [M][K] or None,
+    dw_weak fp32 [N][k] or None) for the upstream gradient dy fp16 [M][N]."""
+    N, K, k = layer_shapes(layer)
+    _meta(dy, torch.float16, "dy")
+    if dy.dim() != 2 or dy.shape[1] != N:
+        raise ValueError(f"dy has shape {tuple(dy.shape)}, expected (M, {N})")
+    M = dy.shape[0]
+    if want_dw and k > 0:
+        if x is None:
+            raise ValueError("x is needed for dw_weak")
+        _xy_shapes(N, K, x, None, M=M)
+    elif x is not None:
+        _xy_shapes(N, K, x, None, M=M)
+    if workspace is not None:
+        _meta(workspace, torch.uint8, "workspace")
+    _on_device(("x", x), ("dy", dy), ("workspace", workspace), *_layer_named(layer))
+    dx = torch.empty((M, K), dtype=torch.float16, device=dy.device) if want_dx else None
+    dw = torch.empty((N, k), dtype=torch.float32, device=dy.device) if want_dw else None
+    if want_dx and workspace is None:
+        workspace = torch.empty(linear_backward_workspace_bytes(N, K, k), dtype=torch.uint8, device=dy.device)
+    L = layer_struct(layer)
+    _check(lib().owq_linear_backward(ctypes.byref(L), _ptr(x), _ptr(dy), M, _ptr(dx),
+                                     _ptr(dw) if (want_dw and k) else None, _ptr(workspace) if want_dx else None,
+                                     _nbytes(workspace) if want_dx else 0, _stream(stream)), "owq_linear_backward")
+    return dx, dw
 
 
 def _batched_args(layers: list, xs: list, ys: list | None):

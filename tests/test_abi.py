@@ -143,6 +143,23 @@ def test_linear_storage_validation(lib):
     assert f(_layer(owq, K=48), FAKE, 3, FAKE, FAKE, ws, None) == 2
 
 
+def test_linear_backward_validation(lib):
+    from mixed_precision_weight_amd import owq
+    assert lib.owq_linear_backward_workspace_bytes(4096, 4096, 32) > 0
+    assert lib.owq_linear_backward_workspace_bytes(4096, 4100, 32) == 0
+    assert lib.owq_linear_backward_workspace_bytes(0, 4096, 32) == 0
+    f = lib.owq_linear_backward
+    ws = lib.owq_linear_backward_workspace_bytes(8, 64, 2)
+    L = _layer(owq)
+    assert f(None, FAKE, FAKE, 3, FAKE, FAKE, FAKE, ws, None) == 1
+    assert f(L, FAKE, None, 3, FAKE, FAKE, FAKE, ws, None) == 1
+    assert f(L, None, FAKE, 3, None, FAKE, FAKE, ws, None) == 1       # dw_weak needs x
+    assert f(L, FAKE, FAKE, 3, FAKE, None, None, ws, None) == 1       # dx needs the workspace
+    assert f(L, FAKE, FAKE, 3, FAKE, None, FAKE, ws - 1, None) == 6
+    assert f(L, FAKE, FAKE, 3, FAKE + 1, None, FAKE, ws, None) == 4
+    assert f(L, FAKE, FAKE, 0, FAKE, None, FAKE, ws, None) == 2
+
+
 def _layer(owq, **kw):
     d = dict(N=8, K=64, k=2, bits=3, qcodes=FAKE, scales=FAKE, zeros=FAKE, weak_idx=FAKE, w_weak=FAKE)
     d.update(kw)
