@@ -22,6 +22,9 @@ from .oracle import (  # noqa: F401
     pack,
     pack_search,
     pack_storage,
+    optq_factor,
+    optq_pack,
+    f64_to_f16,
     linear_storage_rows,
     search_qparams,
     SEARCH_STEPS,

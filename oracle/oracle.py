@@ -57,6 +57,9 @@ def load():
                                                   _P, _I64, _P, _I64, _P, _P, ctypes.c_int]),
         "owq_oracle_linear_backward": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32, _P, _P, _I64,
                                               _P, _P, _P, _P, ctypes.c_int]),
+        "owq_oracle_f64_to_f16": (ctypes.c_uint16, [ctypes.c_double]),
+        "owq_oracle_optq_factor": (None, [_P, _I64, _I64, _P, _I32, _P, ctypes.c_int]),
+        "owq_oracle_optq_pack": (None, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, ctypes.c_int]),
         "owq_oracle_unpack_codes": (None, [_P, _I64, _I64, _P]),
         "owq_oracle_linear_pairs": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32,
                                            _P, _I64, _P, _P, _I64, _P, _P]),
@@ -273,6 +276,40 @@ def linear_backward(layer: dict, x, dy, want_dx: bool = True, want_dw: bool = Tr
     if want_dw:
         dw, dwb = np.ascontiguousarray(dw[:, :k]), np.ascontiguousarray(dwb[:, :k])
     return dx, dxb, dw, dwb
+
+
+def f64_to_f16(f: float) -> int:
+    return load().owq_oracle_f64_to_f16(float(f))
+
+
+def optq_factor(X, weak_idx, threads: int = 0) -> np.ndarray:
+    """U [K][K] (upper) of the damped Hessian 2 X^T X in dense-then-weak order."""
+    X = _u16(X)
+    T, K = X.shape
+    idx = np.ascontiguousarray(np.asarray(weak_idx, dtype=np.int32))
+    U = np.zeros((K, K), np.float64)
+    load().owq_oracle_optq_factor(_ptr(X), T, K, _ptr(idx) if idx.size else None, idx.shape[0], _ptr(U), int(threads))
+    return U
+
+
+def optq_pack(W, X, weak_idx, U=None, threads: int = 0) -> dict:
+    """Latency-favoured pack of W with OPTQ's sequential quantisation, the weak
+    columns last (U from optq_factor(X, weak_idx) unless given)."""
+    W = _u16(W)
+    N, K = W.shape
+    assert K % 32 == 0
+    idx = np.ascontiguousarray(np.asarray(weak_idx, dtype=np.int32))
+    k = idx.shape[0]
+    if U is None:
+        U = optq_factor(X, idx, threads)
+    U = np.ascontiguousarray(U, dtype=np.float64)
+    q = np.zeros((N, K // 32, 3), np.uint32)
+    s = np.zeros(N, np.uint16)
+    z = np.zeros(N, np.uint8)
+    ww = np.zeros((N, max(k, 1)), np.uint16)
+    load().owq_oracle_optq_pack(_ptr(W), N, K, _ptr(idx) if k else None, k, _ptr(U), _ptr(q), _ptr(s), _ptr(z),
+                                _ptr(ww), int(threads))
+    return {"qcodes": q, "scales": s, "zeros": z, "w_weak": np.ascontiguousarray(ww[:, :k]), "weak_idx": idx}
 
 
 def unpack_codes(qcodes, K: int) -> np.ndarray:

@@ -88,6 +88,31 @@ uint16_t owq_oracle_f32_to_f16(float f)
 
 static float f16_to_f32(uint16_t h) { return (float)owq_oracle_f16_to_f64(h); }
 
+/* Nearest binary16 to a binary64 value, ties to even (the same steps as the
+ * binary32 conversion, on the exact binary64 value). */
+uint16_t owq_oracle_f64_to_f16(double f)
+{
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    double a = fabs(f);
+    if (isnan(f))
+        return sign | 0x7e00;
+    if (a >= 65520.0)
+        return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) {
+        double m0 = rint(ldexp(a, 24));
+        return sign | (uint16_t)m0;
+    }
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;
+    double m = rint(ldexp(a, 10 - E));
+    if (m == 2048.0) {
+        m = 1024.0;
+        E += 1;
+    }
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)(m - 1024.0);
+}
+
 /* ------------------------------------------------------------ quantiser ---- */
 
 /* Min-max round-to-nearest parameters of one output row: step size and zero
@@ -468,6 +493,216 @@ void owq_oracle_linear_backward(const uint32_t* qcodes, const uint16_t* scales,
                 dw_bound[i * k + c] = bnd;
             }
     }
+}
+
+/* ------------------------------------------ OPTQ with the weak columns last ---- */
+
+/* OWQ quantises the dense columns with OPTQ's sequential column-by-column
+ * quantisation and error compensation, the weak columns moved to the end so that
+ * their full-precision values absorb compensation without being quantised; the
+ * Hessian 2 X^T X is shared with the weak-column selection ([PL] "OPTQ: Weight
+ * Quantization for LLMs" (pp.2-3), "OWQ: Outlier-aware Weight Quantization"
+ * (p.4), "Quantization efficiency" (paper "Quantization Speed", p.7), "B
+ * Experiment Details" (p.10): built on the OPTQ codebase). Readings (the pages
+ * give none of these):
+ *   P1 H = 2 X^T X in fp64; a column with H_jj == 0 gets H_jj = 1; every H_jj then
+ *      gains 1 % of the mean diagonal (damping);
+ *   P2 column order: the dense columns ascending, then the weak columns ascending;
+ *   P3 the compensation uses U, the upper-triangular factor with H^-1 = U^T U:
+ *      the inverse of the Cholesky factor of H taken in reversed column order
+ *      (H in reversed order = L L^T, then U reversed back from L^-1);
+ *   P4 each row's (step, zero point) is the min-max fit of its original dense
+ *      weights (R1-R5); a column's code is clamp(rint(w / s) + z, 0, 7) on the
+ *      compensated fp64 weight with an fp64 quotient; its error
+ *      e = (w - s (q - z)) / U_aa updates every later column b by e U_ab;
+ *   P5 lazy batches of 128 columns: inside a batch the updates are applied column
+ *      by column; the later batches get, per column, the sum over the batch's
+ *      quantised columns of e U_ab in ascending order, subtracted once;
+ *   P6 the weak block is the fp16 rounding (nearest-even) of the compensated weak
+ *      weights; weak codes are the zero point (latency-favoured format). */
+#define OWQ_OPTQ_BLOCK 128
+
+static int cmp_i32(const void* a, const void* b)
+{
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return x < y ? -1 : x > y ? 1 : 0;
+}
+
+/* U (upper, [K][K] row-major, lower part 0) of P3 from the damped, permuted H. */
+static void optq_factor(const double* Hp, int64_t K, double* U, int nt)
+{
+    double* Hr = (double*)malloc((size_t)(K * K) * sizeof(double));
+    double* L = (double*)calloc((size_t)(K * K), sizeof(double));
+    double* Mi = (double*)calloc((size_t)(K * K), sizeof(double));
+    for (int64_t a = 0; a < K; a++)
+        for (int64_t b = 0; b < K; b++)
+            Hr[a * K + b] = Hp[(K - 1 - a) * K + (K - 1 - b)];
+    /* Cholesky Hr = L L^T, column by column */
+    for (int64_t j = 0; j < K; j++) {
+        double d = Hr[j * K + j];
+        for (int64_t q = 0; q < j; q++)
+            d -= L[j * K + q] * L[j * K + q];
+        double ljj = sqrt(d);
+        L[j * K + j] = ljj;
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t i = j + 1; i < K; i++) {
+            double acc = Hr[i * K + j];
+            for (int64_t q = 0; q < j; q++)
+                acc -= L[i * K + q] * L[j * K + q];
+            L[i * K + j] = acc / ljj;
+        }
+    }
+    /* Mi = L^-1, column by column, rows downwards */
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 8)
+    for (int64_t j = 0; j < K; j++) {
+        Mi[j * K + j] = 1.0 / L[j * K + j];
+        for (int64_t i = j + 1; i < K; i++) {
+            double acc = 0.0;
+            for (int64_t q = j; q < i; q++)
+                acc += L[i * K + q] * Mi[q * K + j];
+            Mi[i * K + j] = -acc / L[i * K + i];
+        }
+    }
+    for (int64_t a = 0; a < K; a++)
+        for (int64_t b = 0; b < K; b++)
+            U[a * K + b] = b >= a ? Mi[(K - 1 - a) * K + (K - 1 - b)] : 0.0;
+    free(Hr);
+    free(L);
+    free(Mi);
+}
+
+void owq_oracle_optq_factor(const uint16_t* X, int64_t T, int64_t K, const int32_t* weak_idx, int32_t k,
+                            double* U, int threads)
+{
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+    double* H = (double*)malloc((size_t)(K * K) * sizeof(double));
+    double* Xf = (double*)malloc((size_t)(T * K) * sizeof(double));
+    for (int64_t e = 0; e < T * K; e++)
+        Xf[e] = owq_oracle_f16_to_f64(X[e]);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 4)
+    for (int64_t i = 0; i < K; i++)
+        for (int64_t j = 0; j < K; j++) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; t++)
+                acc += Xf[t * K + i] * Xf[t * K + j];
+            H[i * K + j] = 2.0 * acc;
+        }
+    free(Xf);
+    double dsum = 0.0; /* P1 */
+    for (int64_t j = 0; j < K; j++) {
+        if (H[j * K + j] == 0.0)
+            H[j * K + j] = 1.0;
+        dsum += H[j * K + j];
+    }
+    double damp = 0.01 * (dsum / (double)K);
+    for (int64_t j = 0; j < K; j++)
+        H[j * K + j] += damp;
+    /* P2 */
+    int32_t* perm = (int32_t*)malloc((size_t)K * sizeof(int32_t));
+    int32_t* w = (int32_t*)malloc((size_t)(k > 0 ? k : 1) * sizeof(int32_t));
+    uint8_t* weak = (uint8_t*)calloc((size_t)K, 1);
+    for (int32_t c = 0; c < k; c++) {
+        w[c] = weak_idx[c];
+        weak[weak_idx[c]] = 1;
+    }
+    qsort(w, (size_t)k, sizeof(int32_t), cmp_i32);
+    int64_t p = 0;
+    for (int64_t j = 0; j < K; j++)
+        if (!weak[j])
+            perm[p++] = (int32_t)j;
+    for (int32_t c = 0; c < k; c++)
+        perm[p++] = w[c];
+    double* Hp = (double*)malloc((size_t)(K * K) * sizeof(double));
+    for (int64_t a = 0; a < K; a++)
+        for (int64_t b = 0; b < K; b++)
+            Hp[a * K + b] = H[(int64_t)perm[a] * K + perm[b]];
+    optq_factor(Hp, K, U, nt); /* P3 */
+    free(Hp);
+    free(H);
+    free(perm);
+    free(w);
+    free(weak);
+}
+
+/* OPTQ pack: latency-favoured outputs (qcodes, scales, zeros, w_weak) of the
+ * sequential quantisation P4-P6 of every row (OpenMP over rows), given U. */
+void owq_oracle_optq_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* weak_idx, int32_t k,
+                          const double* U, uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                          uint16_t* w_weak, int threads)
+{
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+    uint8_t* weak = (uint8_t*)calloc((size_t)K, 1);
+    uint8_t* dense = (uint8_t*)malloc((size_t)K);
+    int32_t* perm = (int32_t*)malloc((size_t)K * sizeof(int32_t));
+    for (int32_t c = 0; c < k; c++)
+        weak[weak_idx[c]] = 1;
+    int64_t Kd = 0;
+    for (int64_t j = 0; j < K; j++) {
+        dense[j] = !weak[j];
+        if (!weak[j])
+            perm[Kd++] = (int32_t)j;
+    }
+    for (int32_t c = 0; c < k; c++)
+        perm[Kd + c] = weak_idx[c]; /* ascending by the caller's contract */
+    int64_t G = K / 32;
+#pragma omp parallel num_threads(nt)
+    {
+        double* wr = (double*)malloc((size_t)K * sizeof(double));
+        double* err = (double*)malloc(OWQ_OPTQ_BLOCK * sizeof(double));
+        uint8_t* code = (uint8_t*)malloc((size_t)K);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < N; i++) {
+            const uint16_t* row = W + i * K;
+            uint16_t s16;
+            uint8_t z;
+            owq_oracle_qparams(row, dense, K, &s16, &z); /* P4 */
+            double sd = owq_oracle_f16_to_f64(s16);
+            for (int64_t a = 0; a < K; a++)
+                wr[a] = owq_oracle_f16_to_f64(row[perm[a]]);
+            for (int64_t a0 = 0; a0 < K; a0 += OWQ_OPTQ_BLOCK) { /* P5 */
+                int64_t a1 = a0 + OWQ_OPTQ_BLOCK < K ? a0 + OWQ_OPTQ_BLOCK : K;
+                int64_t aq = a1 < Kd ? a1 : Kd; /* quantised columns of this batch end here */
+                for (int64_t a = a0; a < aq; a++) {
+                    double r = rint(wr[a] / sd);
+                    if (r < -8.0)
+                        r = -8.0;
+                    if (r > 8.0)
+                        r = 8.0;
+                    int q = (int)r + (int)z;
+                    q = q < 0 ? 0 : q > 7 ? 7 : q;
+                    code[perm[a]] = (uint8_t)q;
+                    double e = (wr[a] - sd * (double)(q - (int)z)) / U[a * K + a];
+                    err[a - a0] = e;
+                    for (int64_t b = a + 1; b < a1; b++)
+                        wr[b] -= e * U[a * K + b];
+                }
+                for (int64_t b = a1; b < K; b++) {
+                    double acc = 0.0;
+                    for (int64_t a = a0; a < aq; a++)
+                        acc += err[a - a0] * U[a * K + b];
+                    wr[b] -= acc;
+                }
+            }
+            for (int32_t c = 0; c < k; c++) { /* P6 */
+                code[weak_idx[c]] = z;
+                w_weak[i * k + c] = owq_oracle_f64_to_f16(wr[Kd + c]);
+            }
+            for (int64_t g = 0; g < G; g++) {
+                uint32_t* grp = qcodes + (i * G + g) * 3;
+                grp[0] = grp[1] = grp[2] = 0;
+                for (int c = 0; c < 32; c++)
+                    put_code(grp, c, code[g * 32 + c]);
+            }
+            scales[i] = s16;
+            zeros[i] = z;
+        }
+        free(wr);
+        free(err);
+        free(code);
+    }
+    free(weak);
+    free(dense);
+    free(perm);
 }
 
 /* ------------------------------------------------- step / zero-point search ---- */

@@ -96,6 +96,17 @@ void owq_oracle_linear_backward(const uint32_t* qcodes, const uint16_t* scales,
                                 const uint16_t* x, const uint16_t* dy, int64_t M,
                                 double* dx, double* dx_bound, double* dw, double* dw_bound,
                                 int threads);
+/* IEEE binary64 -> binary16, round to nearest, ties to even. */
+uint16_t owq_oracle_f64_to_f16(double f);
+/* OPTQ with the weak columns last: U [K][K] (upper; H^-1 = U^T U for the damped
+ * Hessian 2 X^T X in the order dense-then-weak), readings P1-P3 in owq_oracle.c. */
+void owq_oracle_optq_factor(const uint16_t* X, int64_t T, int64_t K, const int32_t* weak_idx, int32_t k,
+                            double* U, int threads);
+/* The sequential quantisation of every row with compensation through U
+ * (readings P4-P6), latency-favoured outputs. */
+void owq_oracle_optq_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* weak_idx, int32_t k,
+                          const double* U, uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                          uint16_t* w_weak, int threads);
 void owq_oracle_unpack_codes(const uint32_t* qcodes, int64_t N, int64_t K, uint8_t* codes);
 
 /* y and the error bound for P (token m, row i) pairs, from the packed layer.

@@ -47,3 +47,21 @@ def test_f32_to_f16_ties_and_edges(orc):
     got = _encode_many(orc, v)
     ref = v.astype(np.float16).view(np.uint16)
     assert np.array_equal(got, ref)
+
+
+def test_f64_to_f16_against_numpy(orc):
+    """The binary64 -> binary16 rounding (the OPTQ weak block) against numpy's
+    direct float64 -> float16 conversion: random values over the whole range,
+    exact midpoints between fp16 neighbours (ties go to even) and values one
+    binary64 ulp either side of them, subnormals, overflow."""
+    import numpy as np
+    rng = np.random.default_rng(9)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-8, 5, 20000),
+                        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e-9, -6e-8, 2.0 ** -25, 3 * 2.0 ** -25]])
+    h = rng.integers(0, 0x7BFF, 5000).astype(np.uint16).view(np.float16).astype(np.float64)
+    nxt = np.nextafter(h.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    mid = (h + nxt) / 2.0
+    v = np.concatenate([v, mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf), -mid])
+    got = np.array([orc.f64_to_f16(x) for x in v], np.uint16)
+    ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)

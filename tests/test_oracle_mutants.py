@@ -64,6 +64,13 @@ MUTANTS = {
                                  "Wf[i * K + j] = s * (double)(get_code(qcodes + (i * G + j / 32) * 3, (int)(j % 32)) + z);"),
     "weak gradient gathers x at c": ("owq_oracle_f16_to_f64(x[m * K + weak_idx[c]]);",
                                      "owq_oracle_f16_to_f64(x[m * K + c]);"),
+    "optq without compensation inside a batch": ("wr[b] -= e * U[a * K + b];", "wr[b] -= 0.0 * e * U[a * K + b];"),
+    "optq without the later batches' update": ("        wr[b] -= acc;", "        wr[b] -= 0.0 * acc;"),
+    "optq without damping": ("double damp = 0.01 * (dsum / (double)K);", "double damp = 0.0 * (dsum / (double)K);"),
+    "optq error not scaled by the factor's diagonal": ("double e = (wr[a] - sd * (double)(q - (int)z)) / U[a * K + a];",
+                                                      "double e = (wr[a] - sd * (double)(q - (int)z));"),
+    "optq weak block not compensated": ("w_weak[i * k + c] = owq_oracle_f64_to_f16(wr[Kd + c]);",
+                                        "w_weak[i * k + c] = row[weak_idx[c]];"),
     "storage fills the tail with code 0": ("put_code(qrow + (p / 32) * 3, (int)(p % 32), z);",
                                            "put_code(qrow + (p / 32) * 3, (int)(p % 32), 0);"),
     "storage product gathers x at the position": ("owq_oracle_f16_to_f64(xm[dcol[q]]);",
@@ -87,7 +94,9 @@ def _run_mutant(name, old, new, base):
                                                   "test_binding_validation.py",
                                                   "test_abi.py", "test_build_resources.py",
                                                   "test_bench_accounting.py"))
-    env = dict(os.environ, PYTHONPATH=ROOT)  # the seeded input generator comes from the package
+    # the seeded input generator comes from the package; one OpenMP thread per copy,
+    # since several copies run at once
+    env = dict(os.environ, PYTHONPATH=ROOT, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu", "tests"],
                        cwd=work, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-400:]
