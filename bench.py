@@ -681,6 +681,29 @@ def main():
         result["kernels"]["backward_weak_column_tuning"] = bw
         del bws
 
+    if not args.no_search:
+        # OPTQ with the weak columns last (owq_pack_optq) on the two K = 4096
+        # shapes of the layer: an offline step, timed whole
+        print("bench: OPTQ pack", file=sys.stderr, flush=True)
+        oq = {}
+        for li in (0, 4):
+            s = specs[li]
+            _, score_o = owq.calibrate(W[li], X[li], workspace=ws)
+            idx_o = owq.select_weak(score_o, s.k)
+            wso = torch.empty(owq.pack_optq_workspace_bytes(s.N, s.K, s.k), dtype=torch.uint8, device=dev)
+            outo = owq.pack_optq(W[li], X[li], idx_o, workspace=wso)
+            a, b = E(), E()
+            a.record()
+            owq.pack_optq(W[li], X[li], idx_o, out=outo, workspace=wso)
+            b.record()
+            torch.cuda.synchronize()
+            oq[f"{s.name} {s.N}x{s.K} T={cfg.T}"] = {"ms": round(a.elapsed_time(b), 2)}
+            del wso, outo
+        result["kernels"]["pack_optq"] = dict(
+            oq, what="owq_pack_optq: Hessian, damping, reversed-order Cholesky (one launch per column), triangular "
+                     "inverse, column-by-column quantisation in batches of 128 with compensation, pack; sequential "
+                     "sums in the definition's order (offline step, not tuned)")
+
     # share of the total column score carried by the k selected columns, per
     # linear (most of the output error comes from a few channels)
     share = {}

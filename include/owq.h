@@ -191,6 +191,42 @@ owq_status owq_pack_storage(const uint16_t* W, int64_t N, int64_t K,
                             uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
                             uint16_t* w_weak, void* stream);
 
+/* Bytes of device workspace owq_pack_optq needs (0 for invalid sizes): three
+ * K x K fp64 matrices, an N x K fp64 working copy of W and N x K bytes of codes. */
+size_t owq_pack_optq_workspace_bytes(int64_t N, int64_t K, int32_t k);
+
+/* Latency-favoured pack (owq_pack's outputs and format) with the dense columns
+ * quantised by OPTQ's sequential column-by-column quantisation and error
+ * compensation, the weak columns moved to the end so that their fp16 values
+ * absorb compensation without being quantised, on the Hessian 2 X^T X that the
+ * weak-column selection shares ([PL] "OPTQ: Weight Quantization for LLMs"
+ * (pp.2-3), "OWQ: Outlier-aware Weight Quantization" (p.4), "Quantization
+ * efficiency" (paper "Quantization Speed", p.7), "B Experiment Details" (p.10)).
+ * Definition (the pages give the method; these details are the library's):
+ *   H = 2 X^T X in fp64; a zero diagonal entry is set to 1, then every diagonal
+ *   entry gains 0.01 times the mean diagonal; the columns are ordered dense
+ *   ascending then weak ascending; U is the upper-triangular factor with H^-1 =
+ *   U^T U (the inverse of the Cholesky factor of H taken in reversed order);
+ *   each row's step and zero point are owq_pack's (min-max over its dense
+ *   columns); in that order, column a of a row gets the code clamp(rint(w_a /
+ *   s) + z, 0, 7) of its current (compensated, fp64) weight, and its error
+ *   e = (w_a - s (q - z)) / U_aa is subtracted from every later column b as
+ *   e U_ab, in batches of 128 columns (within a batch column by column; each
+ *   later batch receives the batch's sum over a of e_a U_ab in column order);
+ *   w_weak is the compensated weak weights rounded to fp16 (nearest-even); weak
+ *   codes are the zero point.
+ * X: fp16 [T][K] calibration input; other arguments and outputs as owq_pack.
+ * workspace: >= owq_pack_optq_workspace_bytes(N, K, k) bytes, 256-byte aligned.
+ * Every sum runs in the definition's order, so the outputs are bitwise
+ * reproducible. An offline step: the Cholesky factor takes one launch per
+ * column. */
+owq_status owq_pack_optq(const uint16_t* W, int64_t N, int64_t K,
+                         const uint16_t* X, int64_t T,
+                         const int32_t* weak_idx, int32_t k,
+                         uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                         uint16_t* w_weak, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* ----------------------------------------------------------------- linear --- */
 
 /* One packed layer, as produced by owq_pack. The struct itself is HOST memory;

@@ -351,6 +351,42 @@ owq_status owq_linear_storage(const owq_layer* L, const uint16_t* x, int64_t M, 
                       "owq_linear_storage launch");
 }
 
+size_t owq_pack_optq_workspace_bytes(int64_t N, int64_t K, int32_t k)
+{
+    if (N < 1 || N > INT32_MAX || K < 32 || K > kMaxK || K % 32 != 0 || k < 0 || k > K)
+        return 0;
+    return owq::optq_plan(N, K, k).total;
+}
+
+owq_status owq_pack_optq(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,
+                         const int32_t* weak_idx, int32_t k, uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                         uint16_t* w_weak, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!W || !X || !qcodes || !scales || !zeros || !workspace)
+        return fail(OWQ_ERR_NULL, "W, X, qcodes, scales, zeros and workspace must be non-NULL");
+    if (N < 1 || N > INT32_MAX || T < 1 || T > INT32_MAX)
+        return fail(OWQ_ERR_SHAPE, "N = %lld, T = %lld out of range", (long long)N, (long long)T);
+    owq_status st = check_k_dim(K);
+    if (st != OWQ_OK)
+        return st;
+    if (k < 0 || k > K)
+        return fail(OWQ_ERR_RANGE, "k = %d outside [0, K = %lld]", k, (long long)K);
+    if (k > 0 && (!weak_idx || !w_weak))
+        return fail(OWQ_ERR_NULL, "weak_idx and w_weak must be non-NULL when k > 0");
+    if (!aligned(W, 16) || !aligned(X, 2) || !aligned(qcodes, 4) || !aligned(scales, 2) ||
+        !aligned(workspace, 256) || (k > 0 && (!aligned(weak_idx, 4) || !aligned(w_weak, 2))))
+        return fail(OWQ_ERR_ALIGN, "misaligned pointer (W: 16 B, workspace: 256 B, qcodes/weak_idx: 4 B, fp16: 2 B)");
+    const owq::OptqPlan p = owq::optq_plan(N, K, k);
+    if (workspace_bytes < p.total)
+        return fail(OWQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, p.total);
+    st = check_idx_on_host(weak_idx, k, K, (hipStream_t)stream);
+    if (st != OWQ_OK)
+        return st;
+    return hip_status(owq::launch_pack_optq(W, N, K, X, T, k > 0 ? weak_idx : nullptr, k, qcodes, scales, zeros,
+                                            k > 0 ? w_weak : nullptr, workspace, p, (hipStream_t)stream),
+                      "owq_pack_optq launch");
+}
+
 size_t owq_linear_backward_workspace_bytes(int64_t N, int64_t K, int32_t k)
 {
     if (N < 1 || N > INT32_MAX || K < 32 || K > kMaxK || K % 32 != 0 || k < 0 || k > K)

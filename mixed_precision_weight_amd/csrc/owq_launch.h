@@ -95,6 +95,15 @@ BwdPlan bwd_plan(int64_t N, int64_t K, int32_t k);
 hipError_t launch_linear_backward(const LinearDesc& d, const uint16_t* dy, int64_t M, uint16_t* dx, float* dw,
                                   void* ws, const BwdPlan& p, hipStream_t s);
 
+// ------------------------------------------ OPTQ with the weak columns last --
+struct OptqPlan {
+    size_t off_perm, off_invr, off_h, off_l, off_lr, off_wc, off_err, off_qc, total;
+};
+OptqPlan optq_plan(int64_t N, int64_t K, int32_t k);
+hipError_t launch_pack_optq(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,
+                            const int32_t* idx, int32_t k, uint32_t* q, uint16_t* scales, uint8_t* zeros,
+                            uint16_t* ww, void* ws, const OptqPlan& p, hipStream_t s);
+
 // read-only streaming reference (stream.hip): one word per 4608-byte wavefront
 int64_t stream_read_sink_words(int64_t bytes);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);

@@ -47,6 +47,8 @@ EXPORTS = {
     "owq_linear_backward_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
     "owq_linear_backward": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _P, _I64, _P, _P, _P, ctypes.c_size_t,
                                            _P]),
+    "owq_pack_optq_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
+    "owq_pack_optq": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "owq_linear": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P]),
     "owq_linear_batched": (ctypes.c_int, [ctypes.POINTER(OwqLayer), ctypes.POINTER(_P),
                                           ctypes.POINTER(_P), _I32, _I64, _P]),
@@ -278,6 +280,42 @@ def pack_search(W: torch.Tensor, weak_idx: torch.Tensor, lam: torch.Tensor | Non
     _check(lib().owq_pack_search(_ptr(W), N, K, _ptr(weak_idx) if k else None, k, _ptr(lam), _ptr(out["qcodes"]),
                                  _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["w_weak"]) if k else None,
                                  _stream(stream)), "owq_pack_search")
+    return out
+
+
+def pack_optq_workspace_bytes(N: int, K: int, k: int) -> int:
+    return int(lib().owq_pack_optq_workspace_bytes(N, K, k))
+
+
+def pack_optq(W: torch.Tensor, X: torch.Tensor, weak_idx: torch.Tensor, out: dict | None = None,
+              workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """Latency-favoured pack with OPTQ's sequential quantisation and the weak
+    columns last (owq_pack_optq) on calibration input X [T][K]."""
+    N, K, T = _calib_shapes(W, X)
+    _meta(weak_idx, torch.int32, "weak_idx")
+    if weak_idx.dim() != 1:
+        raise ValueError(f"weak_idx must be 1-D, got {tuple(weak_idx.shape)}")
+    k = weak_idx.numel()
+    if K % 32 or k > K:
+        raise ValueError(f"K = {K} must be a multiple of 32 and k = {k} at most K")
+    want = _pack_out_shapes(N, K, k)
+    if out is not None:
+        for name in _PACK_OUT:
+            if name not in out:
+                raise ValueError(f"out lacks {name!r}")
+            _meta(out[name], want[name][1], f"out[{name!r}]", want[name][0])
+    if workspace is not None:
+        _meta(workspace, torch.uint8, "workspace")
+    _on_device(("W", W), ("X", X), ("weak_idx", weak_idx), ("workspace", workspace),
+               *[(f"out[{n!r}]", out[n]) for n in (_PACK_OUT if out else ())])
+    if out is None:
+        out = {name: torch.empty(shape, dtype=dt, device=W.device) for name, (shape, dt) in want.items()}
+    out["weak_idx"] = weak_idx
+    if workspace is None:
+        workspace = torch.empty(pack_optq_workspace_bytes(N, K, k), dtype=torch.uint8, device=W.device)
+    _check(lib().owq_pack_optq(_ptr(W), N, K, _ptr(X), T, _ptr(weak_idx) if k else None, k, _ptr(out["qcodes"]),
+                               _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["w_weak"]) if k else None,
+                               _ptr(workspace), _nbytes(workspace), _stream(stream)), "owq_pack_optq")
     return out
 
 

@@ -552,20 +552,22 @@ static void optq_factor(const double* Hp, int64_t K, double* U, int nt)
             L[i * K + j] = acc / ljj;
         }
     }
-    /* Mi = L^-1, column by column, rows downwards */
+    /* L^-1, column by column, rows downwards; column j of it is kept
+     * contiguous (Mi[j][i] = (L^-1)[i][j]) */
 #pragma omp parallel for num_threads(nt) schedule(dynamic, 8)
     for (int64_t j = 0; j < K; j++) {
-        Mi[j * K + j] = 1.0 / L[j * K + j];
+        double* mj = Mi + j * K;
+        mj[j] = 1.0 / L[j * K + j];
         for (int64_t i = j + 1; i < K; i++) {
             double acc = 0.0;
             for (int64_t q = j; q < i; q++)
-                acc += L[i * K + q] * Mi[q * K + j];
-            Mi[i * K + j] = -acc / L[i * K + i];
+                acc += L[i * K + q] * mj[q];
+            mj[i] = -acc / L[i * K + i];
         }
     }
     for (int64_t a = 0; a < K; a++)
         for (int64_t b = 0; b < K; b++)
-            U[a * K + b] = b >= a ? Mi[(K - 1 - a) * K + (K - 1 - b)] : 0.0;
+            U[a * K + b] = b >= a ? Mi[(K - 1 - b) * K + (K - 1 - a)] : 0.0;
     free(Hr);
     free(L);
     free(Mi);
@@ -576,18 +578,20 @@ void owq_oracle_optq_factor(const uint16_t* X, int64_t T, int64_t K, const int32
 {
     int nt = threads > 0 ? threads : omp_get_max_threads();
     double* H = (double*)malloc((size_t)(K * K) * sizeof(double));
-    double* Xf = (double*)malloc((size_t)(T * K) * sizeof(double));
-    for (int64_t e = 0; e < T * K; e++)
-        Xf[e] = owq_oracle_f16_to_f64(X[e]);
+    /* the columns of X, each contiguous (Xc[j][t] = X[t][j]) */
+    double* Xc = (double*)malloc((size_t)(T * K) * sizeof(double));
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t j = 0; j < K; j++)
+            Xc[j * T + t] = owq_oracle_f16_to_f64(X[(size_t)(t * K + j)]);
 #pragma omp parallel for num_threads(nt) schedule(dynamic, 4)
     for (int64_t i = 0; i < K; i++)
         for (int64_t j = 0; j < K; j++) {
             double acc = 0.0;
             for (int64_t t = 0; t < T; t++)
-                acc += Xf[t * K + i] * Xf[t * K + j];
+                acc += Xc[i * T + t] * Xc[j * T + t];
             H[i * K + j] = 2.0 * acc;
         }
-    free(Xf);
+    free(Xc);
     double dsum = 0.0; /* P1 */
     for (int64_t j = 0; j < K; j++) {
         if (H[j * K + j] == 0.0)
@@ -648,6 +652,7 @@ void owq_oracle_optq_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t
 #pragma omp parallel num_threads(nt)
     {
         double* wr = (double*)malloc((size_t)K * sizeof(double));
+        double* acc = (double*)malloc((size_t)K * sizeof(double));
         double* err = (double*)malloc(OWQ_OPTQ_BLOCK * sizeof(double));
         uint8_t* code = (uint8_t*)malloc((size_t)K);
 #pragma omp for schedule(dynamic, 4)
@@ -676,12 +681,15 @@ void owq_oracle_optq_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t
                     for (int64_t b = a + 1; b < a1; b++)
                         wr[b] -= e * U[a * K + b];
                 }
-                for (int64_t b = a1; b < K; b++) {
-                    double acc = 0.0;
-                    for (int64_t a = a0; a < aq; a++)
-                        acc += err[a - a0] * U[a * K + b];
-                    wr[b] -= acc;
-                }
+                /* per later column b: acc_b = sum over the batch, a ascending
+                 * (a outer so that U is read along its rows) */
+                for (int64_t b = a1; b < K; b++)
+                    acc[b] = 0.0;
+                for (int64_t a = a0; a < aq; a++)
+                    for (int64_t b = a1; b < K; b++)
+                        acc[b] += err[a - a0] * U[a * K + b];
+                for (int64_t b = a1; b < K; b++)
+                    wr[b] -= acc[b];
             }
             for (int32_t c = 0; c < k; c++) { /* P6 */
                 code[weak_idx[c]] = z;
@@ -697,6 +705,7 @@ void owq_oracle_optq_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t
             zeros[i] = z;
         }
         free(wr);
+        free(acc);
         free(err);
         free(code);
     }

@@ -143,6 +143,19 @@ def test_linear_storage_validation(lib):
     assert f(_layer(owq, K=48), FAKE, 3, FAKE, FAKE, ws, None) == 2
 
 
+def test_pack_optq_validation(lib):
+    f = lib.owq_pack_optq
+    ws = lib.owq_pack_optq_workspace_bytes(8, 64, 2)
+    assert ws >= 3 * 64 * 64 * 8 + 8 * 64 * 8
+    assert lib.owq_pack_optq_workspace_bytes(8, 65, 2) == 0
+    assert f(None, 8, 64, FAKE, 16, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
+    assert f(FAKE, 8, 64, None, 16, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
+    assert f(FAKE, 8, 64, FAKE, 0, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 2
+    assert f(FAKE, 8, 64, FAKE, 16, FAKE, 65, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 3
+    assert f(FAKE, 8, 64, FAKE, 16, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE + 16, ws, None) == 4
+    assert f(FAKE, 8, 64, FAKE, 16, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == 6
+
+
 def test_linear_backward_validation(lib):
     from mixed_precision_weight_amd import owq
     assert lib.owq_linear_backward_workspace_bytes(4096, 4096, 32) > 0

@@ -65,7 +65,7 @@ MUTANTS = {
     "weak gradient gathers x at c": ("owq_oracle_f16_to_f64(x[m * K + weak_idx[c]]);",
                                      "owq_oracle_f16_to_f64(x[m * K + c]);"),
     "optq without compensation inside a batch": ("wr[b] -= e * U[a * K + b];", "wr[b] -= 0.0 * e * U[a * K + b];"),
-    "optq without the later batches' update": ("        wr[b] -= acc;", "        wr[b] -= 0.0 * acc;"),
+    "optq without the later batches' update": ("wr[b] -= acc[b];", "wr[b] -= 0.0 * acc[b];"),
     "optq without damping": ("double damp = 0.01 * (dsum / (double)K);", "double damp = 0.0 * (dsum / (double)K);"),
     "optq error not scaled by the factor's diagonal": ("double e = (wr[a] - sd * (double)(q - (int)z)) / U[a * K + a];",
                                                       "double e = (wr[a] - sd * (double)(q - (int)z));"),
