@@ -673,11 +673,39 @@ def main():
                     owq.linear_backward(slots[r % ROTATE][li], x1[li][:M], dys[li], workspace=bws)
             b.record()
             torch.cuda.synchronize()
-            t = a.elapsed_time(b) / 1e3 / reps
+            t_eager = a.elapsed_time(b) / 1e3 / reps
+            # the same calls replayed from a HIP graph: device time without the
+            # Python binding's per-call cost
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for li in range(L):
+                    owq.linear_backward(slots[0][li], x1[li][:M], dys[li], workspace=bws)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(ROTATE):
+                    for li in range(L):
+                        owq.linear_backward(slots[r][li], x1[li][:M], dys[li], workspace=bws)
+            g.replay()
+            torch.cuda.synchronize()
+            greps = 5
+            a, b = E(), E()
+            a.record()
+            for _ in range(greps):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3 / (greps * ROTATE)
+            del g
             nb = sum(3 * s.N * s.K // 8 + 3 * s.N + 2 * s.N * s.k + 2 * M * s.N + 2 * M * s.K + 2 * M * s.k
                      + 4 * s.N * s.k for s in specs)
-            bw[f"M={M}"] = hbm_entry(nb, t, "k_bwd_dx_part + k_bwd_weak_part + k_bwd_dx_finalize (dx) and k_bwd_dw "
-                                            "(dw_weak), 7 linears, one call each")
+            bw[f"M={M}"] = dict(
+                hbm_entry(nb, t, "k_bwd_part (dx slice partials with the weak columns, and dw_weak) + "
+                                 "k_bwd_dx_finalize per 4-token chunk, 7 linears, one call each, replayed from a "
+                                 "HIP graph (device time)"),
+                us_eager_python_calls=round(t_eager * 1e6, 2))
         result["kernels"]["backward_weak_column_tuning"] = bw
         del bws
 
@@ -700,9 +728,9 @@ def main():
             oq[f"{s.name} {s.N}x{s.K} T={cfg.T}"] = {"ms": round(a.elapsed_time(b), 2)}
             del wso, outo
         result["kernels"]["pack_optq"] = dict(
-            oq, what="owq_pack_optq: Hessian, damping, reversed-order Cholesky (one launch per column), triangular "
-                     "inverse, column-by-column quantisation in batches of 128 with compensation, pack; sequential "
-                     "sums in the definition's order (offline step, not tuned)")
+            oq, what="owq_pack_optq: Hessian, damping, reversed-order Cholesky and triangular inverse (blocked, each "
+                     "entry's sum in the definition's order), column-by-column quantisation in batches of 128 with "
+                     "compensation, pack (offline step)")
 
     # share of the total column score carried by the k selected columns, per
     # linear (most of the output error comes from a few channels)

@@ -191,8 +191,9 @@ owq_status owq_pack_storage(const uint16_t* W, int64_t N, int64_t K,
                             uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
                             uint16_t* w_weak, void* stream);
 
-/* Bytes of device workspace owq_pack_optq needs (0 for invalid sizes): three
- * K x K fp64 matrices, an N x K fp64 working copy of W and N x K bytes of codes. */
+/* Bytes of device workspace owq_pack_optq needs (0 for invalid sizes): two
+ * K x K fp64 matrices (the Hessian, factored in place, and the inverse factor),
+ * an N x K fp64 working copy of W and N x K bytes of codes. */
 size_t owq_pack_optq_workspace_bytes(int64_t N, int64_t K, int32_t k);
 
 /* Latency-favoured pack (owq_pack's outputs and format) with the dense columns

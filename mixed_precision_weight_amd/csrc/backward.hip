@@ -11,18 +11,24 @@
 //   dw_weak[i][c] = sum_m dy[m][i] x[m][idx_c]      (fp32 sums, fp32 result)
 //
 // dx is the transposed 3-bit product: the reduction runs over the rows of the
-// packed matrix, whose codes lie along K. k_bwd_dx_part streams the codes once
-// per token chunk: a block is 4 waves over one tile of 64 groups (2048 columns)
-// and one slice of rows; lane l decodes group l of the tile (the R7 slot layout
-// gives natural column pairs) and adds s_i dy[m][i] (q_ij - z_i) into 32
-// fp32 accumulators per token, one mixed-precision FMA per weight and token (the
-// fp16 (q - z) is exact). Each wave writes its partial sums; k_bwd_weak_part sums
-// dy w_weak over the same row slices for the weak columns (the dense codes there
-// dequantise to 0), and k_bwd_dx_finalize adds the slices in a fixed order and
-// rounds to fp16: results are bitwise deterministic. Token chunks of up to 4.
+// packed matrix, whose codes lie along K. One launch (k_bwd_part) covers two
+// kinds of block:
+//  * dw blocks (first token chunk only): dw_weak, below;
+//  * dx blocks: 4 waves over one tile of 64 groups (2048 columns) and one
+//    slice of rows; lane l decodes group l of the tile (the R7 slot layout gives
+//    natural column pairs) and adds s_i dy[m][i] (q_ij - z_i) into 32 fp32
+//    accumulators per token, one mixed-precision FMA per weight and token (the
+//    fp16 (q - z) is exact). A wave loads 8 rows (4 at 3-4 tokens) before
+//    it decodes any, so that many rows of codes are in flight; the 4 waves' sums are added in LDS in
+//    wave order and the block writes one partial per slice. The weak columns
+//    of the tile then add dy w_weak over the same rows (staged in LDS, rows in
+//    order) to their column's partial.
+// k_bwd_dx_finalize adds the slices' partials in a fixed order (8 phases of
+// interleaved slices, then the phases in order) and rounds to fp16: results
+// are bitwise deterministic. Token chunks of up to 4.
 //
-// dw_weak (k_bwd_dw): a thread per row and 32 weak columns, x at the weak
-// columns staged in LDS 64 tokens at a time, fp32 FMAs in token order.
+// dw_weak: a thread per row and 32 weak columns, x at the weak columns staged
+// in LDS 64 tokens at a time, fp32 FMAs in token order.
 #include "owq_decode.h"
 #include "owq_device.h"
 #include "owq_launch.h"
@@ -34,24 +40,60 @@ namespace {
 constexpr int kBwdMaxMT = 4;      // tokens per dx pass
 constexpr int kTileGroups = 64;   // groups per column tile (one per lane)
 constexpr int kWeakTile = 32;     // weak columns per block in the weak kernels
-
-// partial sums of one token chunk over one row slice, per wave:
-// P[(slice * 4 + wave)][m][K] (fp32)
+// rows a wave loads before decoding: 8 at up to 2 tokens, else 4 (registers)
 template <int MT>
-__global__ __launch_bounds__(256) void k_bwd_dx_part(const uint32_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ scales,
-                                                     const uint8_t* __restrict__ zeros, int N, int K,
-                                                     const uint16_t* __restrict__ dy, int rows_per_slice,
-                                                     float* __restrict__ P)
+constexpr int rows_in_flight() { return MT <= 2 ? 8 : 4; }
+
+struct BwdArgs {
+    const uint32_t* q;
+    const uint16_t* scales;
+    const uint8_t* zeros;
+    const uint16_t* ww;
+    const int32_t* idx;
+    const uint16_t* dy;  // this chunk's tokens, [MT][N]
+    const uint16_t* x;   // all tokens, [M][K] (dw blocks)
+    float* P;            // partials [slices][MT][K]
+    float* dw;           // [N][k]
+    int N, K, k, M, rows_per_slice, slices, tiles, dw_blocks;
+};
+
+// dense block: partial sums of one token chunk over one row slice
+template <int MT>
+__device__ __forceinline__ void bwd_dense(const BwdArgs& a, int tile, int s, float* red)
 {
-    const int G = K >> 5;
+    const int G = a.K >> 5;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int g = blockIdx.x * kTileGroups + lane;
+    const int g = tile * kTileGroups + lane;
     const int gc = min(g, G - 1);  // lanes past the row's groups load a valid group and store nothing
-    const int s = blockIdx.y;
-    const int r0 = s * rows_per_slice, r1 = min(N, r0 + rows_per_slice);
+    const int r0 = s * a.rows_per_slice, r1 = min(a.N, r0 + a.rows_per_slice);
     const Magic mg = make_magic();
+    constexpr int kRowsInFlight = rows_in_flight<MT>();
+
+    // The tile's weak columns are [c_lo, c_hi), c_lo = #{c : idx_c < j_lo}. With
+    // at most 256 weak columns and a slice of at most 4096 weak weights, idx, the
+    // slice's weak block (contiguous in w_weak) and its dy are loaded now, beside
+    // the codes, by loads that are all unconditional (clamped indices; the
+    // branch is block-uniform): the weak step after the dense sums then waits on
+    // no load, and nothing here is waited for before the codes are requested.
+    const int j_lo = tile * kTileGroups * 32, j_hi = min(a.K, j_lo + kTileGroups * 32);
+    const int nrs = r1 - r0;
+    const bool pre = a.k > 0 && a.k <= 256 && nrs * a.k <= 4096 && MT * nrs <= 256;
+    // 32-bit registers: 16-bit values would be packed in pairs right after
+    // loading, which waits for the loads
+    uint32_t wv[16], dyh = 0;
+    int idx_t = 0;
+    if (pre) {
+        const int t = threadIdx.x;
+        idx_t = a.idx[min(t, a.k - 1)];
+        const uint16_t* __restrict__ wsl = a.ww + (int64_t)r0 * a.k;
+        const int last = nrs * a.k - 1;
+#pragma unroll
+        for (int u = 0; u < 16; u++)
+            wv[u] = wsl[min(t + 256 * u, last)];
+        const int m = min(t / nrs, MT - 1), r = t % nrs;
+        dyh = a.dy[(int64_t)m * a.N + r0 + r];
+    }
 
     float acc[MT][32];
 #pragma unroll
@@ -60,167 +102,323 @@ __global__ __launch_bounds__(256) void k_bwd_dx_part(const uint32_t* __restrict_
         for (int c = 0; c < 32; c++)
             acc[m][c] = 0.0f;
 
-    for (int r = r0 + wave; r < r1; r += 4) {
-        const uint32_t* src = q + ((int64_t)r * G + gc) * 3;
-        const uint32_t w0 = src[0], w1 = src[1], w2 = src[2];
-        const float sc = h2f(scales[r]);
-        const uint32_t z = zeros[r];
-        float coef[MT];
+    // wave w takes rows r0 + w + 4 t; kRowsInFlight of them per step, rows past
+    // the slice load its last row and take a zero coefficient (adds exact zeros)
+    for (int rb = r0 + wave; rb < r1; rb += 4 * kRowsInFlight) {
+        // every load of the step unconditional (rows clamped to the slice): a
+        // load under a branch would be waited for at the branch's end, before
+        // the next row's loads are issued
+        uint32_t w[kRowsInFlight][3];
+        uint16_t sh[kRowsInFlight], dh[kRowsInFlight][MT];
+        uint32_t z[kRowsInFlight];
 #pragma unroll
-        for (int m = 0; m < MT; m++)
-            coef[m] = sc * h2f(dy[(int64_t)m * N + r]);
-        uint32_t p[16];
-        decode_group(w0, w1, w2, mg, make_zero_sub(z), p);
+        for (int u = 0; u < kRowsInFlight; u++) {
+            const int rr = rb + 4 * u;
+            const int r = rr < r1 ? rr : r1 - 1;
+            const uint32_t* src = a.q + ((int64_t)r * G + gc) * 3;
+            w[u][0] = src[0];
+            w[u][1] = src[1];
+            w[u][2] = src[2];
+            sh[u] = a.scales[r];
+            z[u] = a.zeros[r];
 #pragma unroll
-        for (int pp = 0; pp < 16; pp++) {
-            const half2_t h = as_h2(p[pp]);
-            const float lo = (float)h.x, hi = (float)h.y;  // exact small integers
+            for (int m = 0; m < MT; m++)
+                dh[u][m] = a.dy[(int64_t)m * a.N + r];
+        }
 #pragma unroll
-            for (int m = 0; m < MT; m++) {
-                acc[m][2 * pp] = __builtin_fmaf(coef[m], lo, acc[m][2 * pp]);
-                acc[m][2 * pp + 1] = __builtin_fmaf(coef[m], hi, acc[m][2 * pp + 1]);
+        for (int u = 0; u < kRowsInFlight; u++) {
+            const bool live = rb + 4 * u < r1;
+            const float sc = h2f(sh[u]);
+            float coef[MT];
+#pragma unroll
+            for (int m = 0; m < MT; m++)
+                coef[m] = live ? sc * h2f(dh[u][m]) : 0.0f;
+            uint32_t p[16];
+            decode_group(w[u][0], w[u][1], w[u][2], mg, make_zero_sub(z[u]), p);
+#pragma unroll
+            for (int pp = 0; pp < 16; pp++) {
+                const half2_t h = as_h2(p[pp]);
+                const float lo = (float)h.x, hi = (float)h.y;  // exact small integers
+#pragma unroll
+                for (int m = 0; m < MT; m++) {
+                    acc[m][2 * pp] = __builtin_fmaf(coef[m], lo, acc[m][2 * pp]);
+                    acc[m][2 * pp + 1] = __builtin_fmaf(coef[m], hi, acc[m][2 * pp + 1]);
+                }
             }
         }
     }
-    if (g < G) {
-        float* dst = P + ((int64_t)(s * 4 + wave) * MT) * K + (int64_t)g * 32;
+    // the 4 waves' sums, added in wave order; red is [3][32][64] floats
 #pragma unroll
-        for (int m = 0; m < MT; m++)
+    for (int m = 0; m < MT; m++) {
+        if (wave > 0)
 #pragma unroll
-            for (int c = 0; c < 32; c += 4)
-                *reinterpret_cast<float4*>(dst + (int64_t)m * K + c) =
-                    make_float4(acc[m][c], acc[m][c + 1], acc[m][c + 2], acc[m][c + 3]);
+            for (int c = 0; c < 32; c++)
+                red[((wave - 1) * 32 + c) * 64 + lane] = acc[m][c];
+        __syncthreads();
+        if (wave == 0 && g < G) {
+            float* dst = a.P + ((int64_t)s * MT + m) * a.K + (int64_t)g * 32;
+#pragma unroll
+            for (int c = 0; c < 32; c += 4) {
+                float t[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    float v = acc[m][c + e];
+                    v += red[(0 * 32 + c + e) * 64 + lane];
+                    v += red[(1 * 32 + c + e) * 64 + lane];
+                    v += red[(2 * 32 + c + e) * 64 + lane];
+                    t[e] = v;
+                }
+                *reinterpret_cast<float4*>(dst + c) = make_float4(t[0], t[1], t[2], t[3]);
+            }
+        }
+        __syncthreads();
     }
-}
-
-// the weak columns' share of dx over one row slice: PW[slice][m][c] =
-// sum_{i in slice} dy[m][i] w_weak[i][c]; 8 row phases x 32 columns per block,
-// the phases added in a fixed order
-template <int MT>
-__global__ __launch_bounds__(256) void k_bwd_weak_part(const uint16_t* __restrict__ ww, int N, int k,
-                                                       const uint16_t* __restrict__ dy, int rows_per_slice,
-                                                       float* __restrict__ PW)
-{
-    __shared__ float red[8][MT][kWeakTile];
-    const int cc = threadIdx.x & 31, ph = threadIdx.x >> 5;
-    const int c = blockIdx.x * kWeakTile + cc;
-    const int s = blockIdx.y;
-    const int r0 = s * rows_per_slice, r1 = min(N, r0 + rows_per_slice);
-    float acc[MT];
+    if (a.k == 0)
+        return;
+    // the tile's weak columns [c_lo, c_hi): partial += sum over the slice's rows
+    // (in order) of dy[m][i] w_weak[i][c]
+    int n_lo = 0, n_hi = 0;
+    if (pre) {
+        // the prefetched values are first used here: this keeps the compiler
+        // from moving their conversions (and so the wait) up to the loads
 #pragma unroll
-    for (int m = 0; m < MT; m++)
-        acc[m] = 0.0f;
-    if (c < k) {
-        for (int r = r0 + ph; r < r1; r += 8) {
-            const float w = h2f(ww[(int64_t)r * k + c]);
+        for (int u = 0; u < 16; u++)
+            asm volatile("" : "+v"(wv[u]));
+        asm volatile("" : "+v"(dyh), "+v"(idx_t));
+        const bool on = (int)threadIdx.x < a.k;
+        n_lo = on && idx_t < j_lo;
+        n_hi = on && idx_t < j_hi;
+    } else {
+        for (int c = threadIdx.x; c < a.k; c += 256) {
+            const int v = a.idx[c];
+            n_lo += v < j_lo;
+            n_hi += v < j_hi;
+        }
+    }
+    int* cnt = reinterpret_cast<int*>(red + 5120);  // 8 ints past the staging area
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        n_lo += __shfl_xor(n_lo, o, 64);
+        n_hi += __shfl_xor(n_hi, o, 64);
+    }
+    if (lane == 0) {
+        cnt[wave] = n_lo;
+        cnt[4 + wave] = n_hi;
+    }
+    __syncthreads();
+    const int c_lo = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    const int c_hi = cnt[4] + cnt[5] + cnt[6] + cnt[7];
+    const int tid = threadIdx.x;
+    if (pre) {
+        // red[0, nrs k): the slice's weak weights (row-major), red[4096 + m nrs + r]:
+        // dy, ids[c]: idx[c]; column c_lo + t sums its rows in order and adds the
+        // total to the partial this block stored (the only add to that address)
+        int* ids = reinterpret_cast<int*>(red + 5376);
+        const int tot = nrs * a.k;
+#pragma unroll
+        for (int u = 0; u < 16; u++) {
+            const int e = tid + 256 * u;
+            if (e < tot)
+                red[e] = h2f((uint16_t)wv[u]);
+        }
+        if (tid < MT * nrs)
+            red[4096 + tid] = h2f((uint16_t)dyh);
+        if (tid < a.k)
+            ids[tid] = idx_t;
+        __syncthreads();
+        const int c = c_lo + tid;
+        if (c < c_hi) {
+            float wacc[MT];
 #pragma unroll
             for (int m = 0; m < MT; m++)
-                acc[m] = __builtin_fmaf(h2f(dy[(int64_t)m * N + r]), w, acc[m]);
-        }
-    }
+                wacc[m] = 0.0f;
+            for (int r = 0; r < nrs; r++) {
+                const float w = red[r * a.k + c];
 #pragma unroll
-    for (int m = 0; m < MT; m++)
-        red[ph][m][cc] = acc[m];
-    __syncthreads();
-    if (ph == 0 && c < k) {
+                for (int m = 0; m < MT; m++)
+                    wacc[m] = __builtin_fmaf(red[4096 + m * nrs + r], w, wacc[m]);
+            }
+            const int j = ids[c];
 #pragma unroll
-        for (int m = 0; m < MT; m++) {
-            float t = red[0][m][cc];
-            for (int q2 = 1; q2 < 8; q2++)
-                t += red[q2][m][cc];
-            PW[((int64_t)s * MT + m) * k + c] = t;
+            for (int m = 0; m < MT; m++)
+                atomicAddNoRet(a.P + ((int64_t)s * MT + m) * a.K + j, wacc[m]);
         }
-    }
-}
-
-// dx[m][j] = fp16(sum over the dense partials in order + the weak partials at
-// weak columns)
-__global__ __launch_bounds__(256) void k_bwd_dx_finalize(const float* __restrict__ P, int nparts,
-                                                         const float* __restrict__ PW, int nweak_parts, int MT,
-                                                         int K, const int32_t* __restrict__ idx, int k,
-                                                         uint16_t* __restrict__ dx)
-{
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // m * K + j within the chunk
-    if (e >= (int64_t)MT * K)
         return;
-    const int m = (int)(e / K), j = (int)(e % K);
-    float t = 0.0f;
-    for (int s = 0; s < nparts; s++)
-        t += P[((int64_t)s * MT + m) * K + j];
-    // the weak column j, if any: binary search in the ascending indices
-    int lo = 0, hi = k;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (idx[mid] < j)
-            lo = mid + 1;
-        else
-            hi = mid;
     }
-    if (lo < k && idx[lo] == j) {
-        float w = 0.0f;
-        for (int s = 0; s < nweak_parts; s++)
-            w += PW[((int64_t)s * MT + m) * k + lo];
-        t += w;
+    // general form: 64 columns x 64 rows staged at a time
+    for (int cb = c_lo; cb < c_hi; cb += 64) {
+        const int nc = min(64, c_hi - cb);
+        float wacc[MT];
+#pragma unroll
+        for (int m = 0; m < MT; m++)
+            wacc[m] = 0.0f;
+        for (int rb = r0; rb < r1; rb += 64) {
+            const int nr = min(64, r1 - rb);
+            // nr x nc weights, element e at (e / nc, e % nc): every load issued
+            // before the first LDS store
+            const int tot = nr * nc;
+            uint16_t v[16];
+#pragma unroll
+            for (int u = 0; u < 16; u++) {
+                const int e = tid + 256 * u;
+                const int r = e / nc, c = e - r * nc;
+                v[u] = e < tot ? a.ww[(int64_t)(rb + r) * a.k + cb + c] : (uint16_t)0;
+            }
+            const float dv = tid < MT * 64 && (tid & 63) < nr ? h2f(a.dy[(int64_t)(tid >> 6) * a.N + rb + (tid & 63)])
+                                                               : 0.0f;
+#pragma unroll
+            for (int u = 0; u < 16; u++) {
+                const int e = tid + 256 * u;
+                const int r = e / nc, c = e - r * nc;
+                if (e < tot)
+                    red[r * 64 + c] = h2f(v[u]);
+            }
+            if (tid < MT * 64)  // dy of the staged rows after the block: red[4096 + m * 64 + r]
+                red[4096 + tid] = dv;
+            __syncthreads();
+            if (tid < nc)
+                for (int r = 0; r < nr; r++) {
+                    const float w = red[r * 64 + tid];
+#pragma unroll
+                    for (int m = 0; m < MT; m++)
+                        wacc[m] = __builtin_fmaf(red[4096 + m * 64 + r], w, wacc[m]);
+                }
+            __syncthreads();
+        }
+        if (tid < nc) {
+            // the partial at a weak column was stored above by this block; this
+            // is the only add to it
+            const int j = a.idx[cb + tid];
+#pragma unroll
+            for (int m = 0; m < MT; m++)
+                atomicAddNoRet(a.P + ((int64_t)s * MT + m) * a.K + j, wacc[m]);
+        }
     }
-    dx[(int64_t)m * K + j] = f2h(t);
 }
 
-// dw[i][c] = sum_m dy[m][i] x[m][idx_c]: thread per row, 32 weak columns per block
-__global__ __launch_bounds__(256) void k_bwd_dw(const uint16_t* __restrict__ x, int M, int K,
-                                                const int32_t* __restrict__ idx, int k,
-                                                const uint16_t* __restrict__ dy, int N, float* __restrict__ dw)
+// dw block: dw[i][c] = sum_m dy[m][i] x[m][idx_c], a thread per row, 32 weak
+// columns; a.dy here points at token 0. x at the block's weak columns is staged
+// in LDS 64 tokens at a time. The first loads (the column indices, dy of the
+// first tokens) are issued together and unconditionally (clamped), and every x
+// load of a stage before the first LDS store, so the chain is indices -> x.
+__device__ __forceinline__ void bwd_dw(const BwdArgs& a, int bi, float* xs)
 {
-    constexpr int MC = 64;
-    __shared__ float xw[MC][kWeakTile];
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    const int c0 = blockIdx.y * kWeakTile;
-    const int ic = min(i, N - 1);
+    constexpr int MC = 64, MD = 8;  // tokens per stage; dy values loaded up front
+    int* cols = reinterpret_cast<int*>(xs + MC * kWeakTile);
+    const int rt = (a.N + 255) / 256;
+    const int i = (bi % rt) * 256 + threadIdx.x;
+    const int c0 = (bi / rt) * kWeakTile;
+    const int nc = min(kWeakTile, a.k - c0);
+    const int ic = min(i, a.N - 1);
+    const int jl = a.idx[c0 + min((int)threadIdx.x & (kWeakTile - 1), nc - 1)];
+    float* dys = xs + MC * kWeakTile + 64;  // [MD][256]: dy of the first tokens
+    uint32_t d0[MD];
+#pragma unroll
+    for (int mm = 0; mm < MD; mm++)
+        d0[mm] = a.dy[(int64_t)min(mm, a.M - 1) * a.N + ic];
+    if (threadIdx.x < kWeakTile)
+        cols[threadIdx.x] = (jl >= 0 && jl < a.K) ? jl : 0;
+#pragma unroll
+    for (int mm = 0; mm < MD; mm++)
+        dys[mm * 256 + threadIdx.x] = h2f((uint16_t)d0[mm]);
     float acc[kWeakTile];
 #pragma unroll
     for (int c = 0; c < kWeakTile; c++)
         acc[c] = 0.0f;
-    for (int m0 = 0; m0 < M; m0 += MC) {
-        __syncthreads();  // the previous tokens' x is no longer read
-        for (int e = threadIdx.x; e < MC * kWeakTile; e += 256) {
+    for (int m0 = 0; m0 < a.M; m0 += MC) {
+        const int mn = min(MC, a.M - m0);
+        __syncthreads();  // cols written / the previous tokens' x no longer read
+        uint32_t v[MC * kWeakTile / 256];
+#pragma unroll
+        for (int u = 0; u < MC * kWeakTile / 256; u++) {
+            const int e = threadIdx.x + 256 * u;
             const int mm = e / kWeakTile, cc = e % kWeakTile;
-            float v = 0.0f;
-            if (m0 + mm < M && c0 + cc < k) {
-                int j = idx[c0 + cc];
-                j = (j >= 0 && j < K) ? j : 0;
-                v = h2f(x[(int64_t)(m0 + mm) * K + j]);
-            }
-            xw[mm][cc] = v;
+            v[u] = a.x[(int64_t)(m0 + min(mm, mn - 1)) * a.K + cols[cc]];
+        }
+#pragma unroll
+        for (int u = 0; u < MC * kWeakTile / 256; u++) {
+            const int e = threadIdx.x + 256 * u;
+            const int mm = e / kWeakTile, cc = e % kWeakTile;
+            xs[e] = (mm < mn && cc < nc) ? h2f((uint16_t)v[u]) : 0.0f;
         }
         __syncthreads();
-        const int mn = min(MC, M - m0);
         for (int mm = 0; mm < mn; mm++) {
-            const float d = h2f(dy[(int64_t)(m0 + mm) * N + ic]);
+            const int m = m0 + mm;
+            const float d = m < MD ? dys[m * 256 + threadIdx.x] : h2f(a.dy[(int64_t)m * a.N + ic]);
 #pragma unroll
             for (int c = 0; c < kWeakTile; c++)
-                acc[c] = __builtin_fmaf(d, xw[mm][c], acc[c]);
+                acc[c] = __builtin_fmaf(d, xs[mm * kWeakTile + c], acc[c]);
         }
     }
-    if (i < N)
-        for (int c = 0; c < kWeakTile && c0 + c < k; c++)
-            dw[(int64_t)i * k + c0 + c] = acc[c];
+    if (i < a.N)
+        for (int c = 0; c < nc; c++)
+            a.dw[(int64_t)i * a.k + c0 + c] = acc[c];
+}
+
+// blocks [0, dw_blocks): dw (first, so that their short dependent chains run
+// beside the dx blocks rather than after them), then slices*tiles dx blocks
+// (slice-major within a tile column)
+template <int MT>
+__global__ __launch_bounds__(256) void k_bwd_part(BwdArgs a)
+{
+    __shared__ float red[3 * 32 * 64];  // 24 KiB, shared by the two roles
+    int b = blockIdx.x;
+    if (b < a.dw_blocks) {
+        bwd_dw(a, b, red);
+        return;
+    }
+    b -= a.dw_blocks;
+    bwd_dense<MT>(a, b % a.tiles, b / a.tiles, red);
+}
+
+// dx[m][j] = fp16(sum over the slices' partials). 32 columns x 8 phases per
+// block: phase f sums slices f, f+8, ... in order (8 loads in flight); the
+// phases are then added in order.
+__global__ __launch_bounds__(256) void k_bwd_dx_finalize(const float* __restrict__ P, int slices, int MT, int K,
+                                                         uint16_t* __restrict__ dx)
+{
+    __shared__ float red[8][32];
+    const int col = threadIdx.x & 31, ph = threadIdx.x >> 5;
+    const int64_t e = (int64_t)blockIdx.x * 32 + col;  // m * K + j within the chunk
+    const int64_t n = (int64_t)MT * K;
+    const bool ok = e < n;
+    const float* __restrict__ p = P + (ok ? e : 0);
+    float t = 0.0f;
+    if (ok) {
+        int s = ph;
+        for (; s + 56 < slices; s += 64) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                v[u] = p[(int64_t)(s + 8 * u) * n];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                t += v[u];
+        }
+        for (; s < slices; s += 8)
+            t += p[(int64_t)s * n];
+    }
+    red[ph][col] = t;
+    __syncthreads();
+    if (ph != 0 || !ok)
+        return;
+    t = red[0][col];
+#pragma unroll
+    for (int f = 1; f < 8; f++)
+        t += red[f][col];
+    dx[e] = f2h(t);
 }
 
 template <int MT>
-hipError_t dx_chunk(const LinearDesc& d, const uint16_t* dy, uint16_t* dx, const BwdPlan& p, char* ws,
-                    hipStream_t s)
+hipError_t dx_chunk(BwdArgs a, const uint16_t* dy, uint16_t* dx, bool with_dw, hipStream_t s)
 {
-    float* P = reinterpret_cast<float*>(ws + p.off_p);
-    float* PW = reinterpret_cast<float*>(ws + p.off_pw);
-    const int G = (int)(d.K / 32);
-    const int tiles = (G + kTileGroups - 1) / kTileGroups;
-    hipLaunchKernelGGL((k_bwd_dx_part<MT>), dim3(tiles, (unsigned)p.slices), dim3(256), 0, s, d.q, d.s, d.z,
-                       (int)d.N, (int)d.K, dy, (int)p.rows_per_slice, P);
-    if (d.k > 0)
-        hipLaunchKernelGGL((k_bwd_weak_part<MT>), dim3((d.k + kWeakTile - 1) / kWeakTile, (unsigned)p.slices),
-                           dim3(256), 0, s, d.ww, (int)d.N, d.k, dy, (int)p.rows_per_slice, PW);
-    const int64_t n = (int64_t)MT * d.K;
-    hipLaunchKernelGGL(k_bwd_dx_finalize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, P,
-                       (int)(4 * p.slices), PW, d.k > 0 ? (int)p.slices : 0, MT, (int)d.K, d.idx, d.k, dx);
+    a.dy = dy;
+    a.dw_blocks = with_dw ? a.dw_blocks : 0;
+    const int64_t nb = (int64_t)a.slices * a.tiles + a.dw_blocks;
+    hipLaunchKernelGGL((k_bwd_part<MT>), dim3((unsigned)nb), dim3(256), 0, s, a);
+    const int64_t n = (int64_t)MT * a.K;
+    hipLaunchKernelGGL(k_bwd_dx_finalize, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, s, a.P, a.slices, MT, a.K,
+                       dx);
     return hipGetLastError();
 }
 
@@ -229,45 +427,68 @@ hipError_t dx_chunk(const LinearDesc& d, const uint16_t* dy, uint16_t* dx, const
 BwdPlan bwd_plan(int64_t N, int64_t K, int32_t k)
 {
     BwdPlan p;
-    // row slices of at least 64 rows (16 per wave), at most 64 slices, and the
-    // dense partial sums (4 per slice, 4 tokens, K columns, fp32) within 32 MiB
-    int64_t sl = (N + 63) / 64;
-    const int64_t cap = ((int64_t)32 << 20) / (4 * kBwdMaxMT * K * (int64_t)sizeof(float));
-    if (sl > 64)
-        sl = 64;
+    // enough dense blocks to fill the GPU (512, two per CU) with slices of at
+    // least 32 rows (8 per wave), the partial sums (4 tokens, K columns, fp32 per
+    // slice) within 64 MiB
+    const int64_t tiles = (K / 32 + kTileGroups - 1) / kTileGroups;
+    int64_t sl = (512 + tiles - 1) / tiles;
+    const int64_t most = (N + 31) / 32;
+    const int64_t cap = ((int64_t)64 << 20) / (kBwdMaxMT * K * (int64_t)sizeof(float));
+    if (sl > most)
+        sl = most;
     if (sl > cap)
         sl = cap;
     p.slices = sl < 1 ? 1 : sl;
     p.rows_per_slice = (N + p.slices - 1) / p.slices;
+    p.slices = (N + p.rows_per_slice - 1) / p.rows_per_slice;  // no empty slice
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    (void)k;
     p.off_p = 0;
-    p.off_pw = al((size_t)4 * p.slices * kBwdMaxMT * K * sizeof(float));
-    p.total = p.off_pw + al((size_t)p.slices * kBwdMaxMT * (k > 0 ? k : 1) * sizeof(float));
+    p.total = al((size_t)p.slices * kBwdMaxMT * K * sizeof(float));
     return p;
 }
 
 hipError_t launch_linear_backward(const LinearDesc& d, const uint16_t* dy, int64_t M, uint16_t* dx, float* dw,
                                   void* ws, const BwdPlan& p, hipStream_t s)
 {
-    hipError_t e = hipSuccess;
-    if (dx) {
-        char* w = static_cast<char*>(ws);
-        for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kBwdMaxMT) {
-            const int mt = (int)(M - m0 < kBwdMaxMT ? M - m0 : kBwdMaxMT);
-            const uint16_t* dyc = dy + m0 * d.N;
-            uint16_t* dxc = dx + m0 * d.K;
-            switch (mt) {
-            case 1: e = dx_chunk<1>(d, dyc, dxc, p, w, s); break;
-            case 2: e = dx_chunk<2>(d, dyc, dxc, p, w, s); break;
-            case 3: e = dx_chunk<3>(d, dyc, dxc, p, w, s); break;
-            default: e = dx_chunk<4>(d, dyc, dxc, p, w, s); break;
-            }
-        }
+    BwdArgs a;
+    a.q = d.q;
+    a.scales = d.s;
+    a.zeros = d.z;
+    a.ww = d.ww;
+    a.idx = d.idx;
+    a.dy = dy;
+    a.x = d.x;
+    a.P = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_p) : nullptr;
+    a.dw = dw;
+    a.N = (int)d.N;
+    a.K = (int)d.K;
+    a.k = d.k;
+    a.M = (int)M;
+    a.rows_per_slice = (int)p.rows_per_slice;
+    a.slices = (int)p.slices;
+    a.tiles = (int)((d.K / 32 + kTileGroups - 1) / kTileGroups);
+    a.dw_blocks = (dw && d.k > 0) ? (int)((d.N + 255) / 256) * ((d.k + kWeakTile - 1) / kWeakTile) : 0;
+    if (!dx) {  // dw only: the dw blocks alone
+        if (a.dw_blocks == 0)
+            return hipSuccess;
+        BwdArgs b = a;
+        b.slices = 0;
+        hipLaunchKernelGGL((k_bwd_part<1>), dim3((unsigned)a.dw_blocks), dim3(256), 0, s, b);
+        return hipGetLastError();
     }
-    if (e == hipSuccess && dw && d.k > 0) {
-        hipLaunchKernelGGL(k_bwd_dw, dim3((unsigned)((d.N + 255) / 256), (unsigned)((d.k + kWeakTile - 1) / kWeakTile)),
-                           dim3(256), 0, s, d.x, (int)M, (int)d.K, d.idx, d.k, dy, (int)d.N, dw);
-        e = hipGetLastError();
+    hipError_t e = hipSuccess;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kBwdMaxMT) {
+        const int mt = (int)(M - m0 < kBwdMaxMT ? M - m0 : kBwdMaxMT);
+        const uint16_t* dyc = dy + m0 * d.N;
+        uint16_t* dxc = dx + m0 * d.K;
+        const bool with_dw = m0 == 0;  // the dw blocks read every token; dy is passed at token 0
+        switch (mt) {
+        case 1: e = dx_chunk<1>(a, dyc, dxc, with_dw, s); break;
+        case 2: e = dx_chunk<2>(a, dyc, dxc, with_dw, s); break;
+        case 3: e = dx_chunk<3>(a, dyc, dxc, with_dw, s); break;
+        default: e = dx_chunk<4>(a, dyc, dxc, with_dw, s); break;
+        }
     }
     return e;
 }

@@ -20,10 +20,11 @@
 //
 // Every sum runs in the same order as that definition (one thread per output,
 // sequential), so codes, steps, zero points and the weak block are bitwise the
-// oracle's. The kernels are plain vector-ALU fp64 code; the Cholesky factor
-// takes one launch per column (the dot products of a column depend on the
-// previous columns), the triangular inverse one thread per column. This is an
-// offline step: its cost is measured, not tuned.
+// oracle's. The kernels are plain vector-ALU fp64 code. The Cholesky factor and
+// the triangular inverse are blocked (a panel solve, then an update of
+// everything right of / below it) with every entry's running sum kept in the
+// definition's order: the blocking only decides when each term is added, not in
+// which order.
 //
 // Built with -ffp-contract=off: products and sums are separately rounded as in
 // the definition.
@@ -135,66 +136,229 @@ __global__ void k_optq_diag(double* __restrict__ Hr, int K, const int32_t* __res
     }
 }
 
-// column j of the Cholesky factor, written twice: transposed (Lt[q][i] = L[i][q],
-// read coalesced by the next columns) and row-major (Lr, for the inverse)
-__global__ __launch_bounds__(256) void k_optq_chol_col(const double* __restrict__ Hr, double* __restrict__ Lt,
-                                                       double* __restrict__ Lr, int K, int j)
+// The Cholesky factor in place of the Hessian (lower triangle, row-major), in
+// panels of kCholPanel columns. Each entry's value is its Hessian entry minus
+// the products L[i][q] L[j][q] for q = 0, 1, ..., j-1, subtracted one at a time
+// in that order and then, below the diagonal, divided by L[j][j]: the products
+// of the panels to the left are subtracted by k_optq_chol_trail (one panel at a
+// time, q ascending inside it), those of the entry's own panel by
+// k_optq_chol_diag / k_optq_chol_panel. Every entry thus sees the same
+// subtractions in the same order as the column-by-column definition.
+constexpr int kCholPanel = 64;
+
+// the panel's diagonal block [q0, q0 + nb)^2, a thread per row, column by column
+__global__ __launch_bounds__(64) void k_optq_chol_diag(double* __restrict__ A, int K, int q0)
 {
-    const int i = j + blockIdx.x * 256 + threadIdx.x;
-    if (i >= K)
-        return;
-    double d = Hr[(int64_t)j * K + j];
-    for (int q = 0; q < j; q++)
-        d -= Lt[(int64_t)q * K + j] * Lt[(int64_t)q * K + j];
-    const double ljj = sqrt(d);
-    double l = ljj;
-    if (i > j) {
-        double acc = Hr[(int64_t)i * K + j];
-        for (int q = 0; q < j; q++)
-            acc -= Lt[(int64_t)q * K + i] * Lt[(int64_t)q * K + j];
-        l = acc / ljj;
+    __shared__ double d[kCholPanel][kCholPanel + 1];
+    const int r = threadIdx.x;
+    const int nb = min(kCholPanel, K - q0);
+    if (r < nb)
+        for (int c = 0; c <= r; c++)
+            d[r][c] = A[(int64_t)(q0 + r) * K + q0 + c];
+    __syncthreads();
+    for (int j = 0; j < nb; j++) {
+        if (r == j) {
+            double v = d[j][j];
+            for (int q = 0; q < j; q++)
+                v -= d[j][q] * d[j][q];
+            d[j][j] = sqrt(v);
+        }
+        __syncthreads();
+        if (r > j && r < nb) {
+            double v = d[r][j];
+            for (int q = 0; q < j; q++)
+                v -= d[r][q] * d[j][q];
+            d[r][j] = v / d[j][j];
+        }
+        __syncthreads();
     }
-    Lt[(int64_t)j * K + i] = l;
-    Lr[(int64_t)i * K + j] = l;
+    if (r < nb)
+        for (int c = 0; c <= r; c++)
+            A[(int64_t)(q0 + r) * K + q0 + c] = d[r][c];
 }
 
-// L^-1, one thread per column j, rows downwards, stored transposed (Mt[j][i] =
-// (L^-1)[i][j]): each thread walks its own column and row i of L contiguously
-__global__ __launch_bounds__(64) void k_optq_tri_inv(const double* __restrict__ Lr, double* __restrict__ Mt, int K)
+// the panel's rows below its diagonal block (a full panel): a thread per row,
+// the row's kCholPanel entries in registers, column by column
+__global__ __launch_bounds__(256) void k_optq_chol_panel(double* __restrict__ A, int K, int q0)
 {
-    const int j = blockIdx.x * 64 + threadIdx.x;
-    if (j >= K)
-        return;
-    double* __restrict__ mj = Mt + (int64_t)j * K;
-    mj[j] = 1.0 / Lr[(int64_t)j * K + j];
-    for (int i = j + 1; i < K; i++) {
-        const double* __restrict__ li = Lr + (int64_t)i * K;
-        double acc = 0.0;
-        for (int q = j; q < i; q++)
-            acc += li[q] * mj[q];
-        mj[i] = -acc / li[i];
-    }
-}
-
-// Mi[i][j] = Mt[j][i] for i >= j (64 x 64 tiles through LDS)
-__global__ __launch_bounds__(256) void k_optq_transpose(const double* __restrict__ Mt, double* __restrict__ Mi, int K)
-{
-    __shared__ double t[64][65];
-    const int bj = blockIdx.x * 64, bi = blockIdx.y * 64;  // Mt rows bj.., columns bi..
-    if (bj > bi + 63)
-        return;  // the tile lies wholly above the diagonal of Mi
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int r = e / 64, c = e % 64;
-        const int j = bj + r, i = bi + c;
-        t[r][c] = (j < K && i < K) ? Mt[(int64_t)j * K + i] : 0.0;
+    __shared__ double d[kCholPanel][kCholPanel + 1];
+    for (int e = threadIdx.x; e < kCholPanel * kCholPanel; e += 256) {
+        const int r = e / kCholPanel, c = e % kCholPanel;
+        d[r][c] = c <= r ? A[(int64_t)(q0 + r) * K + q0 + c] : 0.0;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int r = e / 64, c = e % 64;  // Mi row bi + r, column bj + c
-        const int i = bi + r, j = bj + c;
-        if (i < K && j < K && i >= j)
-            Mi[(int64_t)i * K + j] = t[c][r];
+    const int i = q0 + kCholPanel + blockIdx.x * 256 + threadIdx.x;
+    if (i >= K)
+        return;
+    double* __restrict__ ai = A + (int64_t)i * K + q0;
+    double row[kCholPanel];
+#pragma unroll
+    for (int c = 0; c < kCholPanel; c++)
+        row[c] = ai[c];
+#pragma unroll
+    for (int j = 0; j < kCholPanel; j++) {
+        double v = row[j];
+#pragma unroll
+        for (int q = 0; q < j; q++)
+            v -= row[q] * d[j][q];
+        row[j] = v / d[j][j];
     }
+#pragma unroll
+    for (int c = 0; c < kCholPanel; c++)
+        ai[c] = row[c];
+}
+
+// the entries right of and below the panel [q0, q1): A[i][j] -= L[i][q] L[j][q]
+// for q = q0 .. q1-1 in order, i >= j >= q1; 64 x 64 tiles on or below the
+// diagonal, 4 x 4 entries per thread, the panel's rows staged in LDS (q-major)
+__global__ __launch_bounds__(256) void k_optq_chol_trail(double* __restrict__ A, int K, int q0)
+{
+    const int q1 = q0 + kCholPanel;
+    const int ti = blockIdx.y, tj = blockIdx.x;
+    if (tj > ti)
+        return;
+    __shared__ double li[kCholPanel][64], lj[kCholPanel][64];
+    const int i0 = q1 + ti * 64, j0 = q1 + tj * 64;
+    for (int e = threadIdx.x; e < 64 * kCholPanel; e += 256) {
+        const int r = e / kCholPanel, q = e % kCholPanel;
+        li[q][r] = i0 + r < K ? A[(int64_t)(i0 + r) * K + q0 + q] : 0.0;
+        lj[q][r] = j0 + r < K ? A[(int64_t)(j0 + r) * K + q0 + q] : 0.0;
+    }
+    __syncthreads();
+    const int ra = threadIdx.x >> 4, rb = threadIdx.x & 15;
+    double acc[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; x++)
+#pragma unroll
+        for (int y = 0; y < 4; y++) {
+            const int i = i0 + ra * 4 + x, j = j0 + rb * 4 + y;
+            acc[x][y] = (i < K && j <= i) ? A[(int64_t)i * K + j] : 0.0;
+        }
+#pragma unroll 2
+    for (int q = 0; q < kCholPanel; q++) {
+        double a4[4], b4[4];
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+            a4[x] = li[q][ra * 4 + x];
+#pragma unroll
+        for (int y = 0; y < 4; y++)
+            b4[y] = lj[q][rb * 4 + y];
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+#pragma unroll
+            for (int y = 0; y < 4; y++)
+                acc[x][y] -= a4[x] * b4[y];
+    }
+#pragma unroll
+    for (int x = 0; x < 4; x++)
+#pragma unroll
+        for (int y = 0; y < 4; y++) {
+            const int i = i0 + ra * 4 + x, j = j0 + rb * 4 + y;
+            if (i < K && j <= i)
+                A[(int64_t)i * K + j] = acc[x][y];
+        }
+}
+
+// L^-1 (row-major, upper part zero; Mi starts as zeros), in row blocks of
+// kInvBlock. Entry (i, j), i > j, is -(sum over q = j .. i-1 of L[i][q] Mi[q][j])
+// / L[i][i] with the sum taken in ascending q from +0: the terms of the blocks
+// above row i's own are added into Mi[i][j] by k_optq_inv_trail (one block at a
+// time, q ascending inside it), those of its own block by k_optq_inv_block. The
+// terms with q < j are exact zeros (Mi[q][j] = 0) that leave the running sum at
+// +0, so the sum is the definition's, term for term.
+constexpr int kInvBlock = 32;
+
+// rows [q0, q0 + nb) of L^-1: a thread per column j < q0 + nb, the block's rows
+// in order, their values in registers
+__global__ __launch_bounds__(256) void k_optq_inv_block(const double* __restrict__ L, double* __restrict__ Mi, int K,
+                                                        int q0)
+{
+    __shared__ double d[kInvBlock][kInvBlock + 1];
+    const int nb = min(kInvBlock, K - q0);
+    for (int e = threadIdx.x; e < kInvBlock * kInvBlock; e += 256) {
+        const int r = e / kInvBlock, c = e % kInvBlock;
+        d[r][c] = (r < nb && c <= r) ? L[(int64_t)(q0 + r) * K + q0 + c] : 1.0;
+    }
+    __syncthreads();
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= q0 + nb)
+        return;
+    double m[kInvBlock];
+#pragma unroll
+    for (int r = 0; r < kInvBlock; r++) {
+        const int i = q0 + r;
+        double v = 0.0;
+        if (r < nb && j <= i) {
+            if (j == i) {
+                v = 1.0 / d[r][r];
+            } else {
+                double acc = Mi[(int64_t)i * K + j];
+#pragma unroll
+                for (int c = 0; c < r; c++)
+                    acc += d[r][c] * m[c];
+                v = -acc / d[r][r];
+            }
+            Mi[(int64_t)i * K + j] = v;
+        }
+        m[r] = v;
+    }
+}
+
+// rows i >= q1 = q0 + kInvBlock, columns j < q1: Mi[i][j] += L[i][q] Mi[q][j] for
+// q = q0 .. q1-1 in order; 64 x 64 tiles, 4 x 4 entries per thread
+__global__ __launch_bounds__(256) void k_optq_inv_trail(const double* __restrict__ L, double* __restrict__ Mi, int K,
+                                                        int q0)
+{
+    const int q1 = q0 + kInvBlock;
+    __shared__ double lb[kInvBlock][64], mb[kInvBlock][64];
+    const int i0 = q1 + blockIdx.y * 64, j0 = blockIdx.x * 64;
+    for (int e = threadIdx.x; e < 64 * kInvBlock; e += 256) {
+        const int r = e / kInvBlock, q = e % kInvBlock;
+        lb[q][r] = i0 + r < K ? L[(int64_t)(i0 + r) * K + q0 + q] : 0.0;
+        const int qq = e / 64, c = e % 64;
+        mb[qq][c] = j0 + c < q1 ? Mi[(int64_t)(q0 + qq) * K + j0 + c] : 0.0;
+    }
+    __syncthreads();
+    const int ra = threadIdx.x >> 4, rb = threadIdx.x & 15;
+    double acc[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; x++)
+#pragma unroll
+        for (int y = 0; y < 4; y++) {
+            const int i = i0 + ra * 4 + x, j = j0 + rb * 4 + y;
+            acc[x][y] = (i < K && j < q1) ? Mi[(int64_t)i * K + j] : 0.0;
+        }
+#pragma unroll 2
+    for (int q = 0; q < kInvBlock; q++) {
+        double a4[4], b4[4];
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+            a4[x] = lb[q][ra * 4 + x];
+#pragma unroll
+        for (int y = 0; y < 4; y++)
+            b4[y] = mb[q][rb * 4 + y];
+#pragma unroll
+        for (int x = 0; x < 4; x++)
+#pragma unroll
+            for (int y = 0; y < 4; y++)
+                acc[x][y] += a4[x] * b4[y];
+    }
+#pragma unroll
+    for (int x = 0; x < 4; x++)
+#pragma unroll
+        for (int y = 0; y < 4; y++) {
+            const int i = i0 + ra * 4 + x, j = j0 + rb * 4 + y;
+            if (i < K && j < q1)
+                Mi[(int64_t)i * K + j] = acc[x][y];
+        }
+}
+
+// zero fill (the upper part of L^-1 must read as exact zeros)
+__global__ __launch_bounds__(256) void k_optq_zero(double* __restrict__ p, int64_t n)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e < n)
+        p[e] = 0.0;
 }
 
 // U[a][b] = Mi[K-1-a][K-1-b]
@@ -378,11 +542,9 @@ OptqPlan optq_plan(int64_t N, int64_t K, int32_t k)
     o = al256(o + (size_t)K * sizeof(int32_t));
     p.off_invr = o;
     o = al256(o + (size_t)K * sizeof(int32_t));
-    p.off_h = o;  // the Hessian, then (L^-1)^T in the same place
+    p.off_h = o;  // the Hessian, factored in place into L
     o = al256(o + (size_t)K * K * sizeof(double));
-    p.off_l = o;  // L transposed, then L^-1 row-major
-    o = al256(o + (size_t)K * K * sizeof(double));
-    p.off_lr = o;  // L row-major
+    p.off_mi = o;  // L^-1
     o = al256(o + (size_t)K * K * sizeof(double));
     p.off_wc = o;
     o = al256(o + (size_t)N * K * sizeof(double));
@@ -401,11 +563,8 @@ hipError_t launch_pack_optq(const uint16_t* W, int64_t N, int64_t K, const uint1
     char* base = static_cast<char*>(ws);
     int32_t* perm = reinterpret_cast<int32_t*>(base + p.off_perm);
     int32_t* invr = reinterpret_cast<int32_t*>(base + p.off_invr);
-    double* Hr = reinterpret_cast<double*>(base + p.off_h);
-    double* Lt = reinterpret_cast<double*>(base + p.off_l);
-    double* Lr = reinterpret_cast<double*>(base + p.off_lr);
-    double* Mt = Hr;  // the Hessian is not needed once it is factored
-    double* Mi = Lt;  // nor L transposed once L^-1 is formed
+    double* Hr = reinterpret_cast<double*>(base + p.off_h);  // H, then L
+    double* Mi = reinterpret_cast<double*>(base + p.off_mi);
     double* Wc = reinterpret_cast<double*>(base + p.off_wc);
     double* Err = reinterpret_cast<double*>(base + p.off_err);
     uint8_t* Qc = reinterpret_cast<uint8_t*>(base + p.off_qc);
@@ -420,10 +579,23 @@ hipError_t launch_pack_optq(const uint16_t* W, int64_t N, int64_t K, const uint1
     const unsigned tiles = (unsigned)((K + 63) / 64);
     hipLaunchKernelGGL(k_optq_gram, dim3(tiles, tiles), dim3(256), 0, s, X, (int)T, Ki, perm, Hr);
     hipLaunchKernelGGL(k_optq_diag, dim3(1), dim3(64), 0, s, Hr, Ki, invr);
-    for (int j = 0; j < Ki; j++)
-        hipLaunchKernelGGL(k_optq_chol_col, dim3((unsigned)((K - j + 255) / 256)), dim3(256), 0, s, Hr, Lt, Lr, Ki, j);
-    hipLaunchKernelGGL(k_optq_tri_inv, dim3((unsigned)((K + 63) / 64)), dim3(64), 0, s, Lr, Mt, Ki);
-    hipLaunchKernelGGL(k_optq_transpose, dim3(tiles, tiles), dim3(256), 0, s, Mt, Mi, Ki);
+    for (int q0 = 0; q0 < Ki; q0 += kCholPanel) {
+        hipLaunchKernelGGL(k_optq_chol_diag, dim3(1), dim3(64), 0, s, Hr, Ki, q0);
+        const int rest = Ki - q0 - kCholPanel;
+        if (rest > 0) {
+            hipLaunchKernelGGL(k_optq_chol_panel, dim3((unsigned)((rest + 255) / 256)), dim3(256), 0, s, Hr, Ki, q0);
+            const unsigned nt = (unsigned)((rest + 63) / 64);
+            hipLaunchKernelGGL(k_optq_chol_trail, dim3(nt, nt), dim3(256), 0, s, Hr, Ki, q0);
+        }
+    }
+    hipLaunchKernelGGL(k_optq_zero, dim3((unsigned)((K * K + 255) / 256)), dim3(256), 0, s, Mi, K * K);
+    for (int q0 = 0; q0 < Ki; q0 += kInvBlock) {
+        const int q1 = q0 + kInvBlock < Ki ? q0 + kInvBlock : Ki;
+        hipLaunchKernelGGL(k_optq_inv_block, dim3((unsigned)((q1 + 255) / 256)), dim3(256), 0, s, Hr, Mi, Ki, q0);
+        if (q1 < Ki)
+            hipLaunchKernelGGL(k_optq_inv_trail, dim3((unsigned)((q1 + 63) / 64), (unsigned)((Ki - q1 + 63) / 64)),
+                               dim3(256), 0, s, Hr, Mi, Ki, q0);
+    }
     hipLaunchKernelGGL(k_optq_init, dim3((unsigned)((N * K + 255) / 256)), dim3(256), 0, s, W, Ni, Ki, perm, Wc);
     const unsigned rows_blocks = (unsigned)((N + 15) / 16);
     for (int a0 = 0; a0 < Kd; a0 += kOptqBatch) {

@@ -87,7 +87,7 @@ hipError_t launch_linear_storage(const LinearDesc& d, int64_t M, void* ws, hipSt
 // ------------------------------------------ backward (weak-column tuning) --
 struct BwdPlan {
     int64_t slices, rows_per_slice;  // row slices of the transposed product
-    size_t off_p, off_pw, total;     // workspace byte offsets / size
+    size_t off_p, total;             // workspace byte offsets / size
 };
 BwdPlan bwd_plan(int64_t N, int64_t K, int32_t k);
 // dx = dy W (fp16 [M][K], may be NULL) and dw_weak = dy^T x[:, idx] (fp32 [N][k],
@@ -97,7 +97,7 @@ hipError_t launch_linear_backward(const LinearDesc& d, const uint16_t* dy, int64
 
 // ------------------------------------------ OPTQ with the weak columns last --
 struct OptqPlan {
-    size_t off_perm, off_invr, off_h, off_l, off_lr, off_wc, off_err, off_qc, total;
+    size_t off_perm, off_invr, off_h, off_mi, off_wc, off_err, off_qc, total;
 };
 OptqPlan optq_plan(int64_t N, int64_t K, int32_t k);
 hipError_t launch_pack_optq(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,

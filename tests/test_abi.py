@@ -146,7 +146,7 @@ def test_linear_storage_validation(lib):
 def test_pack_optq_validation(lib):
     f = lib.owq_pack_optq
     ws = lib.owq_pack_optq_workspace_bytes(8, 64, 2)
-    assert ws >= 3 * 64 * 64 * 8 + 8 * 64 * 8
+    assert ws >= 2 * 64 * 64 * 8 + 8 * 64 * 8  # H (factored in place into L), L^-1, W in fp64
     assert lib.owq_pack_optq_workspace_bytes(8, 65, 2) == 0
     assert f(None, 8, 64, FAKE, 16, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
     assert f(FAKE, 8, 64, None, 16, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
