@@ -659,53 +659,60 @@ def main():
         # x[:, idx] for the 7 linears, at M = 1 and 16 (8 packed copies rotated)
         print("bench: weak-column-tuning backward", file=sys.stderr, flush=True)
         bw = {}
-        bws = torch.empty(max(owq.linear_backward_workspace_bytes(s.N, s.K, s.k) for s in specs), dtype=torch.uint8,
-                          device=dev)
-        for M in (1, 16):
-            dys = [torch.randn((M, s.N), device=dev).to(torch.float16) for s in specs]
-            for li in range(L):
-                owq.linear_backward(slots[0][li], x1[li][:M], dys[li], workspace=bws)
-            reps = ROTATE
-            a, b = E(), E()
-            a.record()
-            for r in range(reps):
-                for li in range(L):
-                    owq.linear_backward(slots[r % ROTATE][li], x1[li][:M], dys[li], workspace=bws)
-            b.record()
-            torch.cuda.synchronize()
-            t_eager = a.elapsed_time(b) / 1e3 / reps
-            # the same calls replayed from a HIP graph: device time without the
-            # Python binding's per-call cost
+        bws = torch.empty(owq.linear_backward_batched_workspace_bytes(slots[0]), dtype=torch.uint8, device=dev)
+        def graph_time(fn, reps=5):
+            """Device time of fn() (ROTATE layers' calls) replayed from a HIP graph."""
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
-                for li in range(L):
-                    owq.linear_backward(slots[0][li], x1[li][:M], dys[li], workspace=bws)
+                fn()
             torch.cuda.current_stream().wait_stream(side)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for r in range(ROTATE):
-                    for li in range(L):
-                        owq.linear_backward(slots[r][li], x1[li][:M], dys[li], workspace=bws)
+                fn()
             g.replay()
             torch.cuda.synchronize()
-            greps = 5
             a, b = E(), E()
             a.record()
-            for _ in range(greps):
+            for _ in range(reps):
                 g.replay()
             b.record()
             torch.cuda.synchronize()
-            t = a.elapsed_time(b) / 1e3 / (greps * ROTATE)
             del g
+            return a.elapsed_time(b) / 1e3 / (reps * ROTATE)
+
+        for M in (1, 16):
+            dys = [torch.randn((M, s.N), device=dev).to(torch.float16) for s in specs]
+            xs_b = [x1[li][:M] for li in range(L)]
+
+            def batched():
+                for r in range(ROTATE):
+                    owq.linear_backward_batched(slots[r], xs_b, dys, workspace=bws)
+
+            def per_linear():
+                for r in range(ROTATE):
+                    for li in range(L):
+                        owq.linear_backward(slots[r][li], x1[li][:M], dys[li], workspace=bws)
+
+            batched()
+            torch.cuda.synchronize()
+            a, b = E(), E()
+            a.record()
+            batched()
+            b.record()
+            torch.cuda.synchronize()
+            t_eager = a.elapsed_time(b) / 1e3 / ROTATE
+            t = graph_time(batched)
+            t_one = graph_time(per_linear)
             nb = sum(3 * s.N * s.K // 8 + 3 * s.N + 2 * s.N * s.k + 2 * M * s.N + 2 * M * s.K + 2 * M * s.k
                      + 4 * s.N * s.k for s in specs)
             bw[f"M={M}"] = dict(
-                hbm_entry(nb, t, "k_bwd_part (dx slice partials with the weak columns, and dw_weak) + "
-                                 "k_bwd_dx_finalize per 4-token chunk, 7 linears, one call each, replayed from a "
-                                 "HIP graph (device time)"),
-                us_eager_python_calls=round(t_eager * 1e6, 2))
+                hbm_entry(nb, t, "owq_linear_backward_batched over the 7 linears (k_bwd_part: dx slice partials "
+                                 "with the weak columns, and dw_weak; k_bwd_dx_finalize), one part and one finalize "
+                                 "launch per 4 tokens, replayed from a HIP graph (device time)"),
+                us_eager_python_call=round(t_eager * 1e6, 2),
+                us_one_call_per_linear_graph=round(t_one * 1e6, 2))
         result["kernels"]["backward_weak_column_tuning"] = bw
         del bws
 

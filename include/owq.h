@@ -310,6 +310,30 @@ owq_status owq_linear_backward(const owq_layer* L, const uint16_t* x, const uint
                                int64_t M, uint16_t* dx, float* dw_weak,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace owq_linear_backward_batched needs for dx of the
+ * `count` layers Ls (HOST array): the layers' own sizes, each rounded up to 256
+ * bytes (0 for invalid sizes or count outside 1..64). */
+size_t owq_linear_backward_batched_workspace_bytes(const owq_layer* Ls, int32_t count);
+
+/* owq_linear_backward for `count` layers at once (the linears of one decoder
+ * layer in the same backward step, e.g. q/k/v or gate/up, which read one input):
+ * the same definition and the same results, bit for bit, as one call per layer,
+ * with the layers' work in ONE kernel launch (plus one for the final sums) per 16
+ * layers and 4 tokens instead of two per layer ([PL] "Weak Column Tuning" (paper
+ * "PEFT with Weak Column Tuning", p.5)). Ls: HOST array [count] of layers; xs,
+ * dys, dxs, dws: HOST arrays [count] of device pointers with the meanings and
+ * shapes of owq_linear_backward's x, dy, dx, dw_weak (xs, dxs, dws may be NULL,
+ * or hold NULL entries, for "not needed" / "not wanted"), all with the same M.
+ * workspace: >= owq_linear_backward_batched_workspace_bytes over the layers
+ * that want dx (the full Ls is always enough), 256-byte aligned; layer l's part
+ * starts at the sum of the rounded sizes of the earlier layers that want dx.
+ * Returns OWQ_ERR_UNSUPPORTED unless 1 <= count <= 64; other errors as
+ * owq_linear_backward, reported with the layer's index. */
+owq_status owq_linear_backward_batched(const owq_layer* Ls, const uint16_t* const* xs,
+                                       const uint16_t* const* dys, int32_t count, int64_t M,
+                                       uint16_t* const* dxs, float* const* dws,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------- measurement reference --- */
 
 /* Not a step of the method: a read-only HBM stream with the M = 1 decode

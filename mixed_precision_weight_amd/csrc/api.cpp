@@ -424,6 +424,81 @@ owq_status owq_linear_backward(const owq_layer* L, const uint16_t* x, const uint
                       "owq_linear_backward launch");
 }
 
+size_t owq_linear_backward_batched_workspace_bytes(const owq_layer* Ls, int32_t count)
+{
+    if (!Ls || count < 1 || count > 64)
+        return 0;
+    size_t total = 0;
+    for (int32_t l = 0; l < count; l++) {
+        const size_t b = owq_linear_backward_workspace_bytes(Ls[l].N, Ls[l].K, Ls[l].k);
+        if (b == 0)
+            return 0;
+        total += (b + 255) & ~(size_t)255;
+    }
+    return total;
+}
+
+owq_status owq_linear_backward_batched(const owq_layer* Ls, const uint16_t* const* xs, const uint16_t* const* dys,
+                                       int32_t count, int64_t M, uint16_t* const* dxs, float* const* dws,
+                                       void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!Ls || !dys)
+        return fail(OWQ_ERR_NULL, "Ls and dys must be non-NULL");
+    if (count < 1 || count > 64)
+        return fail(OWQ_ERR_UNSUPPORTED, "count = %d: need 1 <= count <= 64", count);
+    std::vector<owq::LinearDesc> d((size_t)count);
+    std::vector<owq::BwdPlan> plans((size_t)count);
+    std::vector<const uint16_t*> dy((size_t)count);
+    std::vector<uint16_t*> dx((size_t)count);
+    std::vector<float*> dw((size_t)count);
+    std::vector<void*> ws((size_t)count);
+    size_t need = 0;
+    for (int32_t l = 0; l < count; l++) {
+        const owq_layer* L = &Ls[l];
+        const uint16_t* x = xs ? xs[l] : nullptr;
+        dy[l] = dys[l];
+        dx[l] = dxs ? dxs[l] : nullptr;
+        dw[l] = dws ? dws[l] : nullptr;
+        if (!dy[l])
+            return fail(OWQ_ERR_NULL, "layer %d: dy must be non-NULL", l);
+        owq_status st = check_layer(L, M, x ? x : dy[l], dy[l]);
+        if (st != OWQ_OK)
+            return fail(st, "layer %d: %s", l, g_err);
+        if (dw[l] && L->k > 0 && !x)
+            return fail(OWQ_ERR_NULL, "layer %d: x must be non-NULL for dw_weak", l);
+        if ((dx[l] && !aligned(dx[l], 2)) || (dw[l] && !aligned(dw[l], 4)) || !aligned(dy[l], 2))
+            return fail(OWQ_ERR_ALIGN, "layer %d: misaligned pointer (dy, dx: 2 B, dw_weak: 4 B)", l);
+        st = check_idx_on_host(L->weak_idx, L->k, L->K, (hipStream_t)stream);
+        if (st != OWQ_OK)
+            return st;
+        d[l] = desc_of(L, x, nullptr);
+        plans[l] = owq::bwd_plan(L->N, L->K, L->k);
+        ws[l] = nullptr;
+        if (dx[l]) {
+            ws[l] = reinterpret_cast<void*>(need);  // offset for now
+            need += (plans[l].total + 255) & ~(size_t)255;
+        }
+    }
+    if (need > 0) {
+        if (!workspace)
+            return fail(OWQ_ERR_NULL, "workspace must be non-NULL when dx is requested");
+        if (!aligned(workspace, 256))
+            return fail(OWQ_ERR_ALIGN, "misaligned workspace (256 B)");
+        if (workspace_bytes < need)
+            return fail(OWQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+        for (int32_t l = 0; l < count; l++)
+            if (dx[l])
+                ws[l] = static_cast<char*>(workspace) + reinterpret_cast<size_t>(ws[l]);
+    }
+    hipError_t e = hipSuccess;
+    for (int32_t l0 = 0; l0 < count && e == hipSuccess; l0 += owq::kBwdMaxLayers) {
+        const int n = count - l0 < owq::kBwdMaxLayers ? count - l0 : owq::kBwdMaxLayers;
+        e = owq::launch_linear_backward_batched(d.data() + l0, dy.data() + l0, n, M, dx.data() + l0, dw.data() + l0,
+                                                ws.data() + l0, plans.data() + l0, (hipStream_t)stream);
+    }
+    return hip_status(e, "owq_linear_backward_batched launch");
+}
+
 owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* stream)
 {
     owq_status st = check_layer(L, M, x, y);

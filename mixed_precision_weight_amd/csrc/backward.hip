@@ -54,8 +54,29 @@ struct BwdArgs {
     const uint16_t* x;   // all tokens, [M][K] (dw blocks)
     float* P;            // partials [slices][MT][K]
     float* dw;           // [N][k]
-    int N, K, k, M, rows_per_slice, slices, tiles, dw_blocks;
+    uint16_t* dx;        // this chunk's tokens, [MT][K]
+    int N, K, k, M, rows_per_slice, slices, tiles, dw_blocks, dx_blocks;
 };
+
+// The layers of one launch. Blocks: the dw blocks of every layer (layer l from
+// dw0[l]), then the dx blocks of every layer (layer l from dx0[l], dx0[0] =
+// dw0[count]); the finalize launch: layer l from f0[l].
+struct BwdBatch {
+    BwdArgs L[kBwdMaxLayers];
+    int32_t dw0[kBwdMaxLayers + 1], dx0[kBwdMaxLayers + 1], f0[kBwdMaxLayers + 1];
+    int32_t count;
+};
+
+// the layer whose block range [t[l], t[l + 1]) holds b (layers with no blocks
+// are skipped: the last l with t[l] <= b)
+__device__ __forceinline__ int layer_of(const int32_t* t, int count, int b)
+{
+    int li = 0;
+    for (int l = 1; l < count; l++)
+        if (b >= t[l])
+            li = l;
+    return li;
+}
 
 // dense block: partial sums of one token chunk over one row slice
 template <int MT>
@@ -355,34 +376,40 @@ __device__ __forceinline__ void bwd_dw(const BwdArgs& a, int bi, float* xs)
             a.dw[(int64_t)i * a.k + c0 + c] = acc[c];
 }
 
-// blocks [0, dw_blocks): dw (first, so that their short dependent chains run
-// beside the dx blocks rather than after them), then slices*tiles dx blocks
+// blocks [0, dw0[count]): dw (first, so that their short dependent chains run
+// beside the dx blocks rather than after them), then the dx blocks of each layer
 // (slice-major within a tile column)
 template <int MT>
-__global__ __launch_bounds__(256) void k_bwd_part(BwdArgs a)
+__global__ __launch_bounds__(256) void k_bwd_part(const BwdBatch bt)
 {
     __shared__ float red[3 * 32 * 64];  // 24 KiB, shared by the two roles
-    int b = blockIdx.x;
-    if (b < a.dw_blocks) {
-        bwd_dw(a, b, red);
+    const int b = blockIdx.x;
+    if (b < bt.dw0[bt.count]) {
+        const int li = layer_of(bt.dw0, bt.count, b);
+        bwd_dw(bt.L[li], b - bt.dw0[li], red);
         return;
     }
-    b -= a.dw_blocks;
-    bwd_dense<MT>(a, b % a.tiles, b / a.tiles, red);
+    const int li = layer_of(bt.dx0, bt.count, b);
+    const BwdArgs& a = bt.L[li];
+    const int bb = b - bt.dx0[li];
+    bwd_dense<MT>(a, bb % a.tiles, bb / a.tiles, red);
 }
 
 // dx[m][j] = fp16(sum over the slices' partials). 32 columns x 8 phases per
 // block: phase f sums slices f, f+8, ... in order (8 loads in flight); the
 // phases are then added in order.
-__global__ __launch_bounds__(256) void k_bwd_dx_finalize(const float* __restrict__ P, int slices, int MT, int K,
-                                                         uint16_t* __restrict__ dx)
+template <int MT>
+__global__ __launch_bounds__(256) void k_bwd_dx_finalize(const BwdBatch bt)
 {
     __shared__ float red[8][32];
+    const int li = layer_of(bt.f0, bt.count, blockIdx.x);
+    const BwdArgs& a = bt.L[li];
+    const int K = a.K, slices = a.slices;
     const int col = threadIdx.x & 31, ph = threadIdx.x >> 5;
-    const int64_t e = (int64_t)blockIdx.x * 32 + col;  // m * K + j within the chunk
+    const int64_t e = (int64_t)(blockIdx.x - bt.f0[li]) * 32 + col;  // m * K + j within the chunk
     const int64_t n = (int64_t)MT * K;
     const bool ok = e < n;
-    const float* __restrict__ p = P + (ok ? e : 0);
+    const float* __restrict__ p = a.P + (ok ? e : 0);
     float t = 0.0f;
     if (ok) {
         int s = ph;
@@ -406,19 +433,35 @@ __global__ __launch_bounds__(256) void k_bwd_dx_finalize(const float* __restrict
 #pragma unroll
     for (int f = 1; f < 8; f++)
         t += red[f][col];
-    dx[e] = f2h(t);
+    a.dx[e] = f2h(t);
 }
 
+// one token chunk of every layer in bt (dy / dx already at the chunk): the part
+// launch, then the finalize launch of the layers that want dx
 template <int MT>
-hipError_t dx_chunk(BwdArgs a, const uint16_t* dy, uint16_t* dx, bool with_dw, hipStream_t s)
+hipError_t chunk_launch(BwdBatch& bt, hipStream_t s)
 {
-    a.dy = dy;
-    a.dw_blocks = with_dw ? a.dw_blocks : 0;
-    const int64_t nb = (int64_t)a.slices * a.tiles + a.dw_blocks;
-    hipLaunchKernelGGL((k_bwd_part<MT>), dim3((unsigned)nb), dim3(256), 0, s, a);
-    const int64_t n = (int64_t)MT * a.K;
-    hipLaunchKernelGGL(k_bwd_dx_finalize, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, s, a.P, a.slices, MT, a.K,
-                       dx);
+    int nb = 0;
+    for (int l = 0; l < bt.count; l++) {
+        bt.dw0[l] = nb;
+        nb += bt.L[l].dw_blocks;
+    }
+    bt.dw0[bt.count] = nb;
+    for (int l = 0; l < bt.count; l++) {
+        bt.dx0[l] = nb;
+        nb += bt.L[l].dx_blocks;
+    }
+    bt.dx0[bt.count] = nb;
+    int nf = 0;
+    for (int l = 0; l < bt.count; l++) {
+        bt.f0[l] = nf;
+        nf += bt.L[l].dx_blocks > 0 ? (int)((MT * (int64_t)bt.L[l].K + 31) / 32) : 0;
+    }
+    bt.f0[bt.count] = nf;
+    if (nb > 0)
+        hipLaunchKernelGGL((k_bwd_part<MT>), dim3((unsigned)nb), dim3(256), 0, s, bt);
+    if (nf > 0)
+        hipLaunchKernelGGL((k_bwd_dx_finalize<MT>), dim3((unsigned)nf), dim3(256), 0, s, bt);
     return hipGetLastError();
 }
 
@@ -448,49 +491,63 @@ BwdPlan bwd_plan(int64_t N, int64_t K, int32_t k)
     return p;
 }
 
-hipError_t launch_linear_backward(const LinearDesc& d, const uint16_t* dy, int64_t M, uint16_t* dx, float* dw,
-                                  void* ws, const BwdPlan& p, hipStream_t s)
+hipError_t launch_linear_backward_batched(const LinearDesc* d, const uint16_t* const* dy, int count, int64_t M,
+                                          uint16_t* const* dx, float* const* dw, void* const* ws,
+                                          const BwdPlan* p, hipStream_t s)
 {
-    BwdArgs a;
-    a.q = d.q;
-    a.scales = d.s;
-    a.zeros = d.z;
-    a.ww = d.ww;
-    a.idx = d.idx;
-    a.dy = dy;
-    a.x = d.x;
-    a.P = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_p) : nullptr;
-    a.dw = dw;
-    a.N = (int)d.N;
-    a.K = (int)d.K;
-    a.k = d.k;
-    a.M = (int)M;
-    a.rows_per_slice = (int)p.rows_per_slice;
-    a.slices = (int)p.slices;
-    a.tiles = (int)((d.K / 32 + kTileGroups - 1) / kTileGroups);
-    a.dw_blocks = (dw && d.k > 0) ? (int)((d.N + 255) / 256) * ((d.k + kWeakTile - 1) / kWeakTile) : 0;
-    if (!dx) {  // dw only: the dw blocks alone
-        if (a.dw_blocks == 0)
-            return hipSuccess;
-        BwdArgs b = a;
-        b.slices = 0;
-        hipLaunchKernelGGL((k_bwd_part<1>), dim3((unsigned)a.dw_blocks), dim3(256), 0, s, b);
-        return hipGetLastError();
+    BwdBatch bt{};
+    bt.count = count;
+    bool any_dx = false;
+    for (int l = 0; l < count; l++) {
+        BwdArgs& a = bt.L[l];
+        a.q = d[l].q;
+        a.scales = d[l].s;
+        a.zeros = d[l].z;
+        a.ww = d[l].ww;
+        a.idx = d[l].idx;
+        a.dy = dy[l];
+        a.x = d[l].x;
+        a.P = (dx[l] && ws[l]) ? reinterpret_cast<float*>(static_cast<char*>(ws[l]) + p[l].off_p) : nullptr;
+        a.dw = dw[l];
+        a.dx = dx[l];
+        a.N = (int)d[l].N;
+        a.K = (int)d[l].K;
+        a.k = d[l].k;
+        a.M = (int)M;
+        a.rows_per_slice = (int)p[l].rows_per_slice;
+        a.slices = (int)p[l].slices;
+        a.tiles = (int)((d[l].K / 32 + kTileGroups - 1) / kTileGroups);
+        a.dw_blocks = (dw[l] && d[l].k > 0) ? (int)((d[l].N + 255) / 256) * ((d[l].k + kWeakTile - 1) / kWeakTile) : 0;
+        a.dx_blocks = dx[l] ? a.slices * a.tiles : 0;
+        any_dx = any_dx || dx[l];
     }
+    if (!any_dx)  // dw only: the dw blocks alone (the token count does not matter)
+        return chunk_launch<1>(bt, s);
     hipError_t e = hipSuccess;
     for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kBwdMaxMT) {
         const int mt = (int)(M - m0 < kBwdMaxMT ? M - m0 : kBwdMaxMT);
-        const uint16_t* dyc = dy + m0 * d.N;
-        uint16_t* dxc = dx + m0 * d.K;
-        const bool with_dw = m0 == 0;  // the dw blocks read every token; dy is passed at token 0
+        BwdBatch c = bt;
+        for (int l = 0; l < count; l++) {
+            BwdArgs& a = c.L[l];
+            a.dy = dy[l] + m0 * d[l].N;  // the dw blocks read every token from dy at token 0
+            a.dx = dx[l] ? dx[l] + m0 * d[l].K : nullptr;
+            if (m0 > 0)
+                a.dw_blocks = 0;
+        }
         switch (mt) {
-        case 1: e = dx_chunk<1>(a, dyc, dxc, with_dw, s); break;
-        case 2: e = dx_chunk<2>(a, dyc, dxc, with_dw, s); break;
-        case 3: e = dx_chunk<3>(a, dyc, dxc, with_dw, s); break;
-        default: e = dx_chunk<4>(a, dyc, dxc, with_dw, s); break;
+        case 1: e = chunk_launch<1>(c, s); break;
+        case 2: e = chunk_launch<2>(c, s); break;
+        case 3: e = chunk_launch<3>(c, s); break;
+        default: e = chunk_launch<4>(c, s); break;
         }
     }
     return e;
+}
+
+hipError_t launch_linear_backward(const LinearDesc& d, const uint16_t* dy, int64_t M, uint16_t* dx, float* dw,
+                                  void* ws, const BwdPlan& p, hipStream_t s)
+{
+    return launch_linear_backward_batched(&d, &dy, 1, M, &dx, &dw, &ws, &p, s);
 }
 
 }  // namespace owq

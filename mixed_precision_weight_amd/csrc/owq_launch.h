@@ -94,6 +94,13 @@ BwdPlan bwd_plan(int64_t N, int64_t K, int32_t k);
 // may be NULL); d.x is the layer input (read for dw), d.y unused.
 hipError_t launch_linear_backward(const LinearDesc& d, const uint16_t* dy, int64_t M, uint16_t* dx, float* dw,
                                   void* ws, const BwdPlan& p, hipStream_t s);
+// The same for `count` <= kBwdMaxLayers layers in one part launch and one
+// finalize launch per 4-token chunk; dx[l] / dw[l] may be NULL, ws[l] is layer l's
+// workspace (plan p[l]) when dx[l] is wanted.
+constexpr int kBwdMaxLayers = 16;
+hipError_t launch_linear_backward_batched(const LinearDesc* d, const uint16_t* const* dy, int count, int64_t M,
+                                          uint16_t* const* dx, float* const* dw, void* const* ws,
+                                          const BwdPlan* p, hipStream_t s);
 
 // ------------------------------------------ OPTQ with the weak columns last --
 struct OptqPlan {

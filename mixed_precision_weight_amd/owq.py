@@ -47,6 +47,10 @@ EXPORTS = {
     "owq_linear_backward_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
     "owq_linear_backward": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _P, _I64, _P, _P, _P, ctypes.c_size_t,
                                            _P]),
+    "owq_linear_backward_batched_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(OwqLayer), _I32]),
+    "owq_linear_backward_batched": (ctypes.c_int, [ctypes.POINTER(OwqLayer), ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                                   _I32, _I64, ctypes.POINTER(_P), ctypes.POINTER(_P), _P,
+                                                   ctypes.c_size_t, _P]),
     "owq_pack_optq_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
     "owq_pack_optq": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "owq_linear": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P]),
@@ -484,6 +488,61 @@ def linear_backward(layer: dict, x: torch.Tensor | None, dy: torch.Tensor, want_
                                      _ptr(dw) if (want_dw and k) else None, _ptr(workspace) if want_dx else None,
                                      _nbytes(workspace) if want_dx else 0, _stream(stream)), "owq_linear_backward")
     return dx, dw
+
+
+def linear_backward_batched_workspace_bytes(layers: list) -> int:
+    Ls = (OwqLayer * len(layers))(*[layer_struct(l) for l in layers])
+    return int(lib().owq_linear_backward_batched_workspace_bytes(Ls, len(layers)))
+
+
+def linear_backward_batched(layers: list, xs: list | None, dys: list, want_dx: bool = True, want_dw: bool = True,
+                            workspace: torch.Tensor | None = None, stream=None):
+    """owq_linear_backward_batched: the backward of several layers (same M) in one
+    launch per 4 tokens. Returns (dxs, dws), lists of fp16 [M][K] / fp32 [N][k]
+    tensors (None where not wanted)."""
+    n = len(layers)
+    if n < 1 or len(dys) != n or (xs is not None and len(xs) != n):
+        raise ValueError(f"need as many dy (and x) as layers: {n} layers, {len(dys)} dy"
+                         + ("" if xs is None else f", {len(xs)} x"))
+    M = None
+    named = []
+    shapes = []
+    for i, layer in enumerate(layers):
+        N, K, k = layer_shapes(layer)
+        shapes.append((N, K, k))
+        dy = dys[i]
+        _meta(dy, torch.float16, f"[{i}] dy")
+        if dy.dim() != 2 or dy.shape[1] != N:
+            raise ValueError(f"[{i}] dy has shape {tuple(dy.shape)}, expected (M, {N})")
+        if M is None:
+            M = dy.shape[0]
+        elif dy.shape[0] != M:
+            raise ValueError(f"[{i}] dy has {dy.shape[0]} tokens, the first layer's has {M}")
+        x = None if xs is None else xs[i]
+        if want_dw and k > 0 and x is None:
+            raise ValueError(f"[{i}] x is needed for dw_weak")
+        if x is not None:
+            _xy_shapes(N, K, x, None, f"[{i}] ", M=M)
+        named += [(f"[{i}] dy", dy), (f"[{i}] x", x)] + _layer_named(layer, f"[{i}] ")
+    if workspace is not None:
+        _meta(workspace, torch.uint8, "workspace")
+        named.append(("workspace", workspace))
+    _on_device(*named)
+    dev = dys[0].device
+    dxs = [torch.empty((M, K), dtype=torch.float16, device=dev) if want_dx else None for (N, K, k) in shapes]
+    dws = [torch.empty((N, k), dtype=torch.float32, device=dev) if want_dw else None for (N, K, k) in shapes]
+    Ls = (OwqLayer * n)(*[layer_struct(l) for l in layers])
+    if want_dx and workspace is None:
+        workspace = torch.empty(int(lib().owq_linear_backward_batched_workspace_bytes(Ls, n)), dtype=torch.uint8,
+                                device=dev)
+    xp = None if xs is None else (_P * n)(*[None if x is None else x.data_ptr() for x in xs])
+    dyp = (_P * n)(*[dy.data_ptr() for dy in dys])
+    dxp = (_P * n)(*[dx.data_ptr() for dx in dxs]) if want_dx else None
+    dwp = (_P * n)(*[dw.data_ptr() if (dw is not None and dw.numel()) else None for dw in dws]) if want_dw else None
+    _check(lib().owq_linear_backward_batched(Ls, xp, dyp, n, M, dxp, dwp, _ptr(workspace) if want_dx else None,
+                                             _nbytes(workspace) if want_dx else 0, _stream(stream)),
+           "owq_linear_backward_batched")
+    return dxs, dws
 
 
 def _batched_args(layers: list, xs: list, ys: list | None):

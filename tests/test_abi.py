@@ -173,6 +173,37 @@ def test_linear_backward_validation(lib):
     assert f(L, FAKE, FAKE, 0, FAKE, None, FAKE, ws, None) == 2
 
 
+def test_linear_backward_batched_validation(lib):
+    from mixed_precision_weight_amd import owq
+    P = ctypes.c_void_p
+    Ls = (owq.OwqLayer * 2)(_layer(owq), _layer(owq, N=16))
+    per = [lib.owq_linear_backward_workspace_bytes(8, 64, 2), lib.owq_linear_backward_workspace_bytes(16, 64, 2)]
+    ws = lib.owq_linear_backward_batched_workspace_bytes(Ls, 2)
+    assert ws == sum((b + 255) // 256 * 256 for b in per)
+    assert lib.owq_linear_backward_batched_workspace_bytes(Ls, 0) == 0
+    assert lib.owq_linear_backward_batched_workspace_bytes(None, 2) == 0
+    bad = (owq.OwqLayer * 2)(_layer(owq), _layer(owq, K=40))
+    assert lib.owq_linear_backward_batched_workspace_bytes(bad, 2) == 0
+    f = lib.owq_linear_backward_batched
+    two = lambda a, b: (P * 2)(a, b)
+    xs, dys, dxs, dws = two(FAKE, FAKE), two(FAKE, FAKE), two(FAKE, FAKE), two(FAKE, FAKE)
+    assert f(None, xs, dys, 2, 3, dxs, dws, FAKE, ws, None) == 1
+    assert f(Ls, xs, None, 2, 3, dxs, dws, FAKE, ws, None) == 1
+    assert f(Ls, xs, dys, 0, 3, dxs, dws, FAKE, ws, None) == 5
+    assert f(Ls, xs, dys, 65, 3, dxs, dws, FAKE, ws, None) == 5
+    assert f(Ls, xs, two(FAKE, None), 2, 3, dxs, dws, FAKE, ws, None) == 1         # a NULL dy
+    assert f(Ls, two(FAKE, None), dys, 2, 3, dxs, dws, FAKE, ws, None) == 1        # dw_weak needs x
+    assert f(Ls, None, dys, 2, 3, dxs, dws, FAKE, ws, None) == 1
+    assert f(Ls, xs, dys, 2, 3, dxs, dws, None, ws, None) == 1                      # dx needs the workspace
+    assert f(Ls, xs, dys, 2, 3, dxs, dws, FAKE, ws - 1, None) == 6
+    assert f(Ls, xs, dys, 2, 3, dxs, dws, FAKE + 16, ws, None) == 4
+    assert f(Ls, xs, dys, 2, 3, two(FAKE, FAKE + 1), dws, FAKE, ws, None) == 4
+    assert f(Ls, xs, dys, 2, 0, dxs, dws, FAKE, ws, None) == 2
+    assert f(bad, xs, dys, 2, 3, dxs, dws, FAKE, ws, None) == 2
+    # only the layers that want dx count towards the workspace
+    assert f(Ls, xs, dys, 2, 3, two(FAKE, None), dws, FAKE, per[0] - 1, None) == 6
+
+
 def _layer(owq, **kw):
     d = dict(N=8, K=64, k=2, bits=3, qcodes=FAKE, scales=FAKE, zeros=FAKE, weak_idx=FAKE, w_weak=FAKE)
     d.update(kw)

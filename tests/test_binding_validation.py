@@ -112,3 +112,23 @@ def test_batched_checks_common_m_and_counts():
     with pytest.raises(ValueError, match="y has shape"):
         owq.PreparedBatched(Ls, xs, [torch.zeros((2, N), dtype=torch.float16), torch.zeros((2, 31), dtype=torch.float16)])
     _host_only(owq.linear_batched, Ls, xs)
+
+
+def test_backward_batched_checks_shapes_and_common_m():
+    a, b = _layer(), _layer(N=32)
+    dy_a, dy_b = torch.zeros((3, N), dtype=torch.float16), torch.zeros((3, 32), dtype=torch.float16)
+    x = torch.zeros((3, K), dtype=torch.float16)
+    with pytest.raises(ValueError, match="as many"):
+        owq.linear_backward_batched([a, b], [x, x], [dy_a])
+    with pytest.raises(ValueError, match=r"\[1\] dy has shape"):
+        owq.linear_backward_batched([a, b], [x, x], [dy_a, dy_a])
+    with pytest.raises(ValueError, match="tokens"):
+        owq.linear_backward_batched([a, b], [x, x], [dy_a, torch.zeros((2, 32), dtype=torch.float16)])
+    with pytest.raises(ValueError, match="x is needed"):
+        owq.linear_backward_batched([a, b], [x, None], [dy_a, dy_b])
+    with pytest.raises(ValueError, match="columns|shape"):
+        owq.linear_backward_batched([a, b], [x, torch.zeros((3, K - 32), dtype=torch.float16)], [dy_a, dy_b])
+    with pytest.raises(TypeError, match="float16"):
+        owq.linear_backward_batched([a, b], [x, x], [dy_a, dy_b.float()])
+    _host_only(owq.linear_backward_batched, [a, b], [x, x], [dy_a, dy_b])
+    _host_only(owq.linear_backward_batched, [a, b], None, [dy_a, dy_b], want_dw=False)

@@ -88,3 +88,42 @@ def test_edge_shapes(owq, N, K, k, M):
     W = synth.random_layer(rng, N, K, 0.02)
     idx = np.sort(rng.choice(K, k, replace=False)).astype(np.int32)
     _run(owq, W, idx, M, "edge", seed=1)
+
+
+@pytest.mark.parametrize("M", [1, 6])
+def test_batched_equals_per_layer(owq, M):
+    """owq_linear_backward_batched over the 7 LLaMA-7B linears gives bit for bit
+    what one owq_linear_backward per layer gives (the same kernels, one launch);
+    q_proj and down_proj are also checked against the oracle; then dx only and
+    dw only."""
+    import torch
+
+    import oracle
+    cfg = synth.LLAMA7B_LAYER_DECODE
+    packs, xs, dys, refs = [], [], [], []
+    for li, spec in enumerate(cfg.layers):
+        rng = np.random.default_rng(100 + li + M)
+        W = synth.weights(spec, cfg.seed(li))
+        idx = np.sort(rng.choice(spec.K, spec.k, replace=False)).astype(np.int32)
+        x = rng.standard_normal((M, spec.K)).astype(np.float16)
+        dy = rng.standard_normal((M, spec.N)).astype(np.float16)
+        packs.append(owq.pack(dev(W), dev(idx)))
+        xs.append(dev(x))
+        dys.append(dev(dy))
+        refs.append((W, idx, x, dy) if li in (0, 6) else None)
+    print(f"batched backward: 7 linears, M={M}", flush=True)
+    dxs, dws = owq.linear_backward_batched(packs, xs, dys)
+    one = [owq.linear_backward(p, x, dy) for p, x, dy in zip(packs, xs, dys)]
+    dxo, dwo = owq.linear_backward_batched(packs, None, dys, want_dw=False)
+    _, dwonly = owq.linear_backward_batched(packs, xs, dys, want_dx=False)
+    torch.cuda.synchronize()
+    for li in range(7):
+        assert host(dxs[li]).tobytes() == host(one[li][0]).tobytes(), li
+        assert host(dws[li]).tobytes() == host(one[li][1]).tobytes(), li
+        assert host(dxo[li]).tobytes() == host(dxs[li]).tobytes(), li
+        assert host(dwonly[li]).tobytes() == host(dws[li]).tobytes(), li
+        if refs[li] is not None:
+            W, idx, x, dy = refs[li]
+            rdx, rdxb, rdw, rdwb = oracle.linear_backward(oracle.pack(W, idx), x, dy)
+            check_linear(host(dxs[li]), rdx, rdxb, f"batched dx [{li}] M={M}")
+            check_linear(host(dws[li]), rdw, rdwb, f"batched dw [{li}] M={M}")
