@@ -115,22 +115,34 @@ __global__ __launch_bounds__(256) void k_optq_gram(const uint16_t* __restrict__ 
 }
 
 // the diagonal: zero entries become 1, then 1 % of the mean (summed in column
-// order) is added; one thread, the definition's order
-__global__ void k_optq_diag(double* __restrict__ Hr, int K, const int32_t* __restrict__ invr)
+// order by one thread, from LDS chunks that all threads load) is added to each
+__global__ __launch_bounds__(1024) void k_optq_diag(double* __restrict__ Hr, int K, const int32_t* __restrict__ invr)
 {
-    if (threadIdx.x != 0 || blockIdx.x != 0)
-        return;
-    double sum = 0.0;
-    for (int j = 0; j < K; j++) {
-        const int64_t a = invr[j];
-        double v = Hr[a * K + a];
-        if (v == 0.0)
-            v = 1.0;
-        Hr[a * K + a] = v;
-        sum += v;
+    constexpr int CH = 4096;
+    __shared__ double dv[CH];
+    __shared__ double sh_damp;
+    double sum = 0.0;  // thread 0's running sum
+    for (int j0 = 0; j0 < K; j0 += CH) {
+        const int n = min(CH, K - j0);
+        for (int t = threadIdx.x; t < n; t += 1024) {
+            const int64_t a = invr[j0 + t];
+            double v = Hr[a * K + a];
+            if (v == 0.0)
+                v = 1.0;
+            Hr[a * K + a] = v;
+            dv[t] = v;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0)
+            for (int t = 0; t < n; t++)
+                sum += dv[t];
+        __syncthreads();
     }
-    const double damp = 0.01 * (sum / (double)K);
-    for (int j = 0; j < K; j++) {
+    if (threadIdx.x == 0)
+        sh_damp = 0.01 * (sum / (double)K);
+    __syncthreads();
+    const double damp = sh_damp;
+    for (int j = threadIdx.x; j < K; j += 1024) {
         const int64_t a = invr[j];
         Hr[a * K + a] += damp;
     }
@@ -578,7 +590,7 @@ hipError_t launch_pack_optq(const uint16_t* W, int64_t N, int64_t K, const uint1
     hipLaunchKernelGGL(k_optq_perm, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, idx, (int)k, Ki, perm, invr);
     const unsigned tiles = (unsigned)((K + 63) / 64);
     hipLaunchKernelGGL(k_optq_gram, dim3(tiles, tiles), dim3(256), 0, s, X, (int)T, Ki, perm, Hr);
-    hipLaunchKernelGGL(k_optq_diag, dim3(1), dim3(64), 0, s, Hr, Ki, invr);
+    hipLaunchKernelGGL(k_optq_diag, dim3(1), dim3(1024), 0, s, Hr, Ki, invr);
     for (int q0 = 0; q0 < Ki; q0 += kCholPanel) {
         hipLaunchKernelGGL(k_optq_chol_diag, dim3(1), dim3(64), 0, s, Hr, Ki, q0);
         const int rest = Ki - q0 - kCholPanel;
