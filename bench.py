@@ -3,8 +3,8 @@
 One step = one pass of every hot-path stage over one LLaMA-7B decoder layer
 (q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008; k = 32 / 32 / 86 weak
 columns, ~3.1 bits per weight), on seeded synthetic inputs:
-  1. calibration: owq_calibrate_score on T = 2048 tokens, owq_select_weak and
-     owq_pack, for each of the 7 linears;
+  1. calibration: owq_calibrate_score on T = 2048 tokens for each of the 7
+     linears, owq_select_weak_batched for the 7, owq_pack for each;
   2. decode: owq_linear_batched over the 7 linears at M = 1 (one launch per
      layer), for R = 8 distinct packed layers in a row, as a token passes
      through consecutive decoder layers;
@@ -290,19 +290,25 @@ def main():
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
+    # events of the calibration phase: ev[li] before calibrating linear li, ev[L]
+    # after the last, ev[L + 1] after the selection (one batched call for the 7),
+    # ev[L + 2 + li] after packing linear li
     def calibrate_pack(slot, ev=None):
+        scores = []
         for li, s in enumerate(specs):
             if ev is not None:
-                ev[3 * li].record()
+                ev[li].record()
             _, score = owq.calibrate(W[li], X[li], workspace=ws)
-            if ev is not None:
-                ev[3 * li + 1].record()
-            idx = owq.select_weak(score, s.k, out=slot[li]["weak_idx"])
-            if ev is not None:
-                ev[3 * li + 2].record()
-            owq.pack(W[li], idx, out=slot[li])
+            scores.append(score)
         if ev is not None:
-            ev[3 * L].record()
+            ev[L].record()
+        idxs = owq.select_weak_batched(scores, [s.k for s in specs], outs=[slot[li]["weak_idx"] for li in range(L)])
+        if ev is not None:
+            ev[L + 1].record()
+        for li, s in enumerate(specs):
+            owq.pack(W[li], idxs[li], out=slot[li])
+            if ev is not None:
+                ev[L + 2 + li].record()
 
     # fill every rotation slot before timing
     for r in range(ROTATE):
@@ -313,12 +319,13 @@ def main():
     # packed copies are rewritten in place, so the pointers stay valid)
     dec_calls = [owq.PreparedBatched(slots[r], xd, yd) for r in range(ROTATE)]
     decode_bytes = sum(eff_bytes(s.N, s.K, s.k, 1) for s in specs)
-    NE = 3 * L + 1 + 2 + L + 1  # calibration boundaries, decode pair, prefill boundaries
+    CE = 2 * L + 2  # calibration-phase events
+    NE = CE + 2 + L + 1  # calibration phase, decode pair, prefill boundaries
 
     def step(i, ev):
         cal_slot = slots[i % ROTATE]
         calibrate_pack(cal_slot, ev)
-        o = 3 * L + 1
+        o = CE
         ev[o].record()
         for r in range(1, ROTATE + 1):  # the copy written above comes last
             dec_calls[(i + r) % ROTATE]()
@@ -347,10 +354,10 @@ def main():
     def mean_ms(a, b):
         return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
 
-    cal_s = [mean_ms(3 * li, 3 * li + 1) / 1e3 for li in range(L)]
-    sel_s = [mean_ms(3 * li + 1, 3 * li + 2) / 1e3 for li in range(L)]
-    pak_s = [mean_ms(3 * li + 2, 3 * li + 3) / 1e3 for li in range(L)]
-    o = 3 * L + 1
+    cal_s = [mean_ms(li, li + 1) / 1e3 for li in range(L)]
+    sel_s = [mean_ms(L, L + 1) / 1e3]
+    pak_s = [mean_ms(L + 1 + li, L + 2 + li) / 1e3 for li in range(L)]
+    o = CE
     dec_s = mean_ms(o, o + 1) / 1e3 / ROTATE
     dec_min_s = min(e[o].elapsed_time(e[o + 1]) for e in evs) / 1e3 / ROTATE
     o += 2
@@ -398,7 +405,9 @@ def main():
                         "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
                         "algorithmic_flops": pre_flops, "per_linear": per_linear_prefill},
             "calibrate_score": hbm_entry(cal_bytes, sum(cal_s), "k_calib_first + k_colsum_err + k_finalize, 7 linears"),
-            "select_weak": {"what": "k_topk, 7 linears", "us": round(sum(sel_s) * 1e6, 1), "bound": "latency"},
+            "select_weak": {"what": "k_topk_reg_batched, the 7 linears in one owq_select_weak_batched call (one "
+                                    "launch per block shape: K = 4096 and K = 11008)",
+                            "us": round(sum(sel_s) * 1e6, 1), "bound": "latency"},
             "pack": hbm_entry(pk_bytes, sum(pak_s), "k_pack, 7 linears"),
         },
     }

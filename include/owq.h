@@ -131,6 +131,17 @@ size_t owq_calibrate_noalloc_max_workspace(void);
 owq_status owq_select_weak(const double* score, int64_t K, int32_t k,
                            int32_t* weak_idx, void* stream);
 
+/* `count` independent weak-column selections (e.g. the 7 linears of a decoder
+ * layer) with the results owq_select_weak would give one by one, in one kernel
+ * launch per block shape (selections with K > 16384 get one launch each):
+ * every selection is a latency-bound single workgroup, so they run side by side.
+ * scores, weak_idxs: HOST arrays [count] of device pointers; Ks, ks: HOST arrays
+ * [count]; each selection's arguments as owq_select_weak's. Returns
+ * OWQ_ERR_UNSUPPORTED unless 1 <= count <= 64; other errors as owq_select_weak,
+ * reported with the selection's index. */
+owq_status owq_select_weak_batched(const double* const* scores, const int64_t* Ks, const int32_t* ks,
+                                   int32_t* const* weak_idxs, int32_t count, void* stream);
+
 /* ------------------------------------------------------------------- pack --- */
 
 /* Latency-favoured OWQ storage of one layer ([PL] "Storage Methods" (paper

@@ -237,6 +237,31 @@ owq_status owq_select_weak(const double* score, int64_t K, int32_t k, int32_t* w
                       "owq_select_weak launch");
 }
 
+owq_status owq_select_weak_batched(const double* const* scores, const int64_t* Ks, const int32_t* ks,
+                                   int32_t* const* weak_idxs, int32_t count, void* stream)
+{
+    if (!scores || !Ks || !ks || !weak_idxs)
+        return fail(OWQ_ERR_NULL, "scores, Ks, ks and weak_idxs must be non-NULL");
+    if (count < 1 || count > 64)
+        return fail(OWQ_ERR_UNSUPPORTED, "count = %d: need 1 <= count <= 64", count);
+    for (int32_t i = 0; i < count; i++) {
+        const int64_t K = Ks[i];
+        const int32_t k = ks[i];
+        if (!scores[i])
+            return fail(OWQ_ERR_NULL, "selection %d: score must be non-NULL", i);
+        if (K < 1 || K > (int64_t)1 << 24)
+            return fail(OWQ_ERR_SHAPE, "selection %d: K = %lld: need 1 <= K <= 2^24", i, (long long)K);
+        if (k < 0 || k > K)
+            return fail(OWQ_ERR_RANGE, "selection %d: k = %d outside [0, K = %lld]", i, k, (long long)K);
+        if (k > 0 && !weak_idxs[i])
+            return fail(OWQ_ERR_NULL, "selection %d: weak_idx must be non-NULL when k > 0", i);
+        if (!aligned(scores[i], 8) || (k > 0 && !aligned(weak_idxs[i], 4)))
+            return fail(OWQ_ERR_ALIGN, "selection %d: misaligned pointer (score: 8 B, weak_idx: 4 B)", i);
+    }
+    return hip_status(owq::launch_select_batched(scores, Ks, ks, weak_idxs, count, (hipStream_t)stream),
+                      "owq_select_weak_batched launch");
+}
+
 owq_status owq_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* weak_idx, int32_t k,
                     uint32_t* qcodes, uint16_t* scales, uint8_t* zeros, uint16_t* w_weak, void* stream)
 {

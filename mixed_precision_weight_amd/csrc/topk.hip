@@ -6,9 +6,9 @@
 // Large Language Models"). Ties are broken by the lower column index and the
 // result is written in ascending column order.
 //
-// One 1024-thread workgroup (latency-bound). For K <= 16384 the keys stay in
-// registers (k_topk_reg: early-exit radix select over the range the keys
-// still in play span, one ordered prefix sum);
+// One workgroup (latency-bound). For K <= 16384 the keys stay in registers
+// (k_topk_reg, 512 or 1024 threads: early-exit radix select over the range the
+// keys still in play span, one ordered prefix sum);
 // larger K reads the scores from L2 on every pass (k_topk, below):
 //  1. radix select of the k-th largest 64-bit order key, 8 bits per pass from the
 //     most significant digit: an LDS histogram of the digit among keys that match
@@ -137,8 +137,9 @@ __global__ __launch_bounds__(1024) void k_topk(const double* __restrict__ score,
     }
 }
 
-// Block-wide exclusive prefix sum of one value per thread (thread order); also
-// returns the total. Two barriers.
+// Block-wide exclusive prefix sum of one value per thread (thread order) over
+// NW waves; also returns the total. Two barriers.
+template <int NW>
 __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wave_tot, uint32_t& total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -153,7 +154,7 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wave_to
         wave_tot[wave] = incl;
     __syncthreads();
     uint32_t before = 0, tot = 0;
-    for (int w = 0; w < 16; w++) {
+    for (int w = 0; w < NW; w++) {
         const uint32_t t = wave_tot[w];
         before += w < wave ? t : 0;
         tot += t;
@@ -163,7 +164,7 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t* wave_to
     return before + incl - v;
 }
 
-// K <= 1024 C: thread t holds the keys of columns C t .. C t + C - 1 in registers,
+// K <= 64 NW C: thread t holds the keys of columns C t .. C t + C - 1 in registers,
 // so index order is thread order, then register order. The radix select works
 // on the range [lo, hi] of the keys still in play, starting with the block's
 // smallest and largest key: each pass splits it into 256 buckets of width 2^s
@@ -181,14 +182,14 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
     return ((uint64_t)b << 32) | a;
 }
 
-template <int C>
-__global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ score, int32_t K, int32_t k,
-                                                   int32_t* __restrict__ out)
+template <int C, int NW>
+__device__ __forceinline__ void topk_reg(const double* __restrict__ score, int32_t K, int32_t k,
+                                         int32_t* __restrict__ out)
 {
     __shared__ uint32_t hist[256];
-    __shared__ uint32_t whist[16][256];  // one digit histogram per wave
-    __shared__ uint32_t wave_tot[16];
-    __shared__ unsigned long long sh_lo[16], sh_hi[16];
+    __shared__ uint32_t whist[NW][256];  // one digit histogram per wave
+    __shared__ uint32_t wave_tot[NW];
+    __shared__ unsigned long long sh_lo[NW], sh_hi[NW];
     __shared__ int sh_kk, sh_done;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (k <= 0)  // nothing to select (the host does not launch for k == 0)
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
     __syncthreads();
     lo = sh_lo[0];
     hi = sh_hi[0];
-    for (int w = 1; w < 16; w++) {
+    for (int w = 1; w < NW; w++) {
         lo = min(lo, (uint64_t)sh_lo[w]);
         hi = max(hi, (uint64_t)sh_hi[w]);
     }
@@ -240,12 +241,12 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
                 atomicAdd(&whist[wave][(uint32_t)(d >> s)], 1u);
         }
         __syncthreads();
-        if (tid < 256) {
+        for (int b = tid; b < 256; b += 64 * NW) {
             uint32_t t = 0;
 #pragma unroll
-            for (int w = 0; w < 16; w++)
-                t += whist[w][tid];
-            hist[tid] = t;
+            for (int w = 0; w < NW; w++)
+                t += whist[w][b];
+            hist[b] = t;
         }
         __syncthreads();
         if (wave == 0) {
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
     for (int c = 0; c < C; c++)
         n_eq += key[c] - lo <= span;
     uint32_t eq_total;
-    uint32_t eq_rank = block_excl_sum(n_eq, wave_tot, eq_total);
+    uint32_t eq_rank = block_excl_sum<NW>(n_eq, wave_tot, eq_total);
     bool sel[C];
     uint32_t n_sel = 0;
 #pragma unroll
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
         n_sel += sel[c];
     }
     uint32_t sel_total;
-    uint32_t pos = block_excl_sum(n_sel, wave_tot, sel_total);
+    uint32_t pos = block_excl_sum<NW>(n_sel, wave_tot, sel_total);
 #pragma unroll
     for (int c = 0; c < C; c++)
         if (sel[c]) {
@@ -320,14 +321,79 @@ __global__ __launch_bounds__(1024) void k_topk_reg(const double* __restrict__ sc
         }
 }
 
+template <int C, int NW>
+__global__ __launch_bounds__(64 * NW) void k_topk_reg(const double* __restrict__ score, int32_t K, int32_t k,
+                                                      int32_t* __restrict__ out)
+{
+    topk_reg<C, NW>(score, K, k, out);
+}
+
+// several selections of one block shape, a block each
+struct SelBatch {
+    const double* score[kSelectMaxBatch];
+    int32_t* out[kSelectMaxBatch];
+    int32_t K[kSelectMaxBatch], k[kSelectMaxBatch];
+    int32_t count;
+};
+
+template <int C, int NW>
+__global__ __launch_bounds__(64 * NW) void k_topk_reg_batched(const SelBatch b)
+{
+    const int i = blockIdx.x;
+    topk_reg<C, NW>(b.score[i], b.K[i], b.k[i], b.out[i]);
+}
+
+// the block shape for K <= 16384: 0 = 8 x 8 waves, 1 = 11 x 16, 2 = 16 x 16, 3 = k_topk
+int shape_of(int64_t K) { return K <= 8 * 512 ? 0 : K <= 11 * 1024 ? 1 : K <= 16 * 1024 ? 2 : 3; }
+
 }  // namespace
+
+hipError_t launch_select_batched(const double* const* score, const int64_t* K, const int32_t* k,
+                                 int32_t* const* idx, int count, hipStream_t s)
+{
+    auto flush = [&](int shape, SelBatch& b) {
+        if (b.count == 0)
+            return;
+        if (shape == 0)
+            hipLaunchKernelGGL((k_topk_reg_batched<8, 8>), dim3(b.count), dim3(512), 0, s, b);
+        else if (shape == 1)
+            hipLaunchKernelGGL((k_topk_reg_batched<11, 16>), dim3(b.count), dim3(1024), 0, s, b);
+        else
+            hipLaunchKernelGGL((k_topk_reg_batched<16, 16>), dim3(b.count), dim3(1024), 0, s, b);
+        b.count = 0;
+    };
+    for (int i = 0; i < count; i++)  // large K: one launch each
+        if (k[i] > 0 && shape_of(K[i]) == 3)
+            hipLaunchKernelGGL(k_topk, dim3(1), dim3(1024), 0, s, score[i], K[i], k[i], idx[i]);
+    for (int shape = 0; shape < 3; shape++) {
+        SelBatch b{};
+        for (int i = 0; i < count; i++) {
+            if (k[i] == 0 || shape_of(K[i]) != shape)
+                continue;
+            b.score[b.count] = score[i];
+            b.out[b.count] = idx[i];
+            b.K[b.count] = (int32_t)K[i];
+            b.k[b.count] = k[i];
+            if (++b.count == kSelectMaxBatch)
+                flush(shape, b);
+        }
+        flush(shape, b);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_select(const double* score, int64_t K, int32_t k, int32_t* idx, hipStream_t s)
 {
-    if (K <= 4 * 1024)
-        hipLaunchKernelGGL(k_topk_reg<4>, dim3(1), dim3(1024), 0, s, score, (int32_t)K, k, idx);
+    // block shapes measured on lognormal scores (one launch, HIP events): at
+    // K = 4096 8 keys x 8 waves took 8.2 us against 10.4 / 9.7 / 12.1 us for
+    // 4 x 16, 16 x 4 and 32 x 2; at K = 11008 11 x 16 took 14.9 us against
+    // 17.2 / 15.2 / 18.6 us for 16 x 16, 22 x 8 and 43 x 4
+    if (K <= 8 * 512)
+        hipLaunchKernelGGL((k_topk_reg<8, 8>), dim3(1), dim3(512), 0, s, score, (int32_t)K, k, idx);
+    else if (K <= 11 * 1024)
+        hipLaunchKernelGGL((k_topk_reg<11, 16>), dim3(1), dim3(1024), 0, s, score, (int32_t)K, k, idx);
     else if (K <= 16 * 1024)
-        hipLaunchKernelGGL(k_topk_reg<16>, dim3(1), dim3(1024), 0, s, score, (int32_t)K, k, idx);
+        hipLaunchKernelGGL((k_topk_reg<16, 16>), dim3(1), dim3(1024), 0, s, score, (int32_t)K, k, idx);
     else
         hipLaunchKernelGGL(k_topk, dim3(1), dim3(1024), 0, s, score, K, k, idx);
     return hipGetLastError();

@@ -39,6 +39,8 @@ EXPORTS = {
     "owq_calibrate_score_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P]),
     "owq_calibrate_noalloc_max_workspace": (ctypes.c_size_t, []),
     "owq_select_weak": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+    "owq_select_weak_batched": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_I64), ctypes.POINTER(_I32),
+                                               ctypes.POINTER(_P), _I32, _P]),
     "owq_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
     "owq_pack_search": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P]),
     "owq_pack_storage": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
@@ -214,6 +216,36 @@ def select_weak(score: torch.Tensor, k: int, out: torch.Tensor | None = None, st
     _check(lib().owq_select_weak(_ptr(score), score.numel(), k, _ptr(out) if k else None,
                                  _stream(stream)), "owq_select_weak")
     return out[:k]
+
+
+def select_weak_batched(scores: list, ks: list, outs: list | None = None, stream=None) -> list:
+    """owq_select_weak for several score vectors in one launch per block shape;
+    returns one int32 [k] index tensor per score (written to outs[i] if given)."""
+    n = len(scores)
+    if n < 1 or len(ks) != n or (outs is not None and len(outs) != n):
+        raise ValueError(f"need one k (and out) per score: {n} scores, {len(ks)} k"
+                         + ("" if outs is None else f", {len(outs)} out"))
+    for i, (sc, k) in enumerate(zip(scores, ks)):
+        _meta(sc, torch.float64, f"[{i}] score")
+        if sc.dim() != 1:
+            raise ValueError(f"[{i}] score must be 1-D, got shape {tuple(sc.shape)}")
+        if not 0 <= int(k) <= sc.numel():
+            raise ValueError(f"[{i}] k = {k} outside [0, K = {sc.numel()}]")
+        if outs is not None:
+            _meta(outs[i], torch.int32, f"[{i}] out")
+            if outs[i].dim() != 1 or outs[i].numel() < int(k):
+                raise ValueError(f"[{i}] out must be 1-D with at least k = {k} entries, "
+                                 f"got shape {tuple(outs[i].shape)}")
+    _on_device(*[(f"[{i}] score", sc) for i, sc in enumerate(scores)],
+               *([] if outs is None else [(f"[{i}] out", o) for i, o in enumerate(outs)]))
+    if outs is None:
+        outs = [torch.empty(max(int(k), 1), dtype=torch.int32, device=sc.device) for sc, k in zip(scores, ks)]
+    sp = (_P * n)(*[sc.data_ptr() for sc in scores])
+    Kp = (_I64 * n)(*[sc.numel() for sc in scores])
+    kp = (_I32 * n)(*[int(k) for k in ks])
+    op = (_P * n)(*[o.data_ptr() for o in outs])
+    _check(lib().owq_select_weak_batched(sp, Kp, kp, op, n, _stream(stream)), "owq_select_weak_batched")
+    return [o[:int(k)] for o, k in zip(outs, ks)]
 
 
 # ------------------------------------------------------------------------ pack

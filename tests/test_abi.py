@@ -204,6 +204,25 @@ def test_linear_backward_batched_validation(lib):
     assert f(Ls, xs, dys, 2, 3, two(FAKE, None), dws, FAKE, per[0] - 1, None) == 6
 
 
+def test_select_weak_batched_validation(lib):
+    I64, I32, P = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    f = lib.owq_select_weak_batched
+    sc, out = (P * 2)(FAKE, FAKE), (P * 2)(FAKE, FAKE)
+    Ks, ks = (I64 * 2)(64, 100), (I32 * 2)(3, 4)
+    assert f(None, Ks, ks, out, 2, None) == 1
+    assert f(sc, Ks, ks, None, 2, None) == 1
+    assert f(sc, Ks, ks, out, 0, None) == 5
+    assert f(sc, Ks, ks, out, 65, None) == 5
+    assert f((P * 2)(FAKE, None), Ks, ks, out, 2, None) == 1
+    assert f(sc, (I64 * 2)(64, 0), ks, out, 2, None) == 2
+    assert f(sc, (I64 * 2)(64, (1 << 24) + 1), ks, out, 2, None) == 2
+    assert f(sc, Ks, (I32 * 2)(3, 101), out, 2, None) == 3
+    assert f(sc, Ks, (I32 * 2)(3, -1), out, 2, None) == 3
+    assert f(sc, Ks, ks, (P * 2)(FAKE, None), 2, None) == 1
+    assert f((P * 2)(FAKE, FAKE + 4), Ks, ks, out, 2, None) == 4
+    assert f(sc, Ks, ks, (P * 2)(FAKE, FAKE + 2), 2, None) == 4
+
+
 def _layer(owq, **kw):
     d = dict(N=8, K=64, k=2, bits=3, qcodes=FAKE, scales=FAKE, zeros=FAKE, weak_idx=FAKE, w_weak=FAKE)
     d.update(kw)

@@ -132,3 +132,16 @@ def test_backward_batched_checks_shapes_and_common_m():
         owq.linear_backward_batched([a, b], [x, x], [dy_a, dy_b.float()])
     _host_only(owq.linear_backward_batched, [a, b], [x, x], [dy_a, dy_b])
     _host_only(owq.linear_backward_batched, [a, b], None, [dy_a, dy_b], want_dw=False)
+
+
+def test_select_batched_checks_shapes():
+    a, b = torch.zeros(K, dtype=torch.float64), torch.zeros(2 * K, dtype=torch.float64)
+    with pytest.raises(ValueError, match="one k .*per score"):
+        owq.select_weak_batched([a, b], [3])
+    with pytest.raises(ValueError, match="outside"):
+        owq.select_weak_batched([a, b], [3, 2 * K + 1])
+    with pytest.raises(TypeError, match="float64"):
+        owq.select_weak_batched([a, b.float()], [3, 4])
+    with pytest.raises(ValueError, match="1-D"):
+        owq.select_weak_batched([a, b.reshape(2, K)], [3, 4])
+    _host_only(owq.select_weak_batched, [a, b], [3, 4])

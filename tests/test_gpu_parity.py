@@ -133,7 +133,32 @@ def test_edge_shapes(owq, N, K, k, Ms):
     _run(owq, W, X, k, [x[:m] for m in Ms], f"edge N={N} K={K} k={k}")
 
 
-@pytest.mark.parametrize("K,k", [(1, 1), (5, 2), (100, 37), (4096, 32), (28672, 221), (65536, 65536),
+def test_select_batched_matches_single(owq):
+    """owq_select_weak_batched over selections of every block shape (and k = 0,
+    k = K, K above 16384) gives exactly the single calls' and the oracle's
+    indices."""
+    import torch
+
+    import oracle
+    rng = np.random.default_rng(77)
+    cases = [(100, 37), (4096, 32), (4096, 0), (4096, 4096), (5000, 7), (11008, 86), (11264, 300), (16000, 129),
+             (20000, 500), (4096, 32), (11008, 86), (1, 1)]
+    scores = []
+    for K, _ in cases:
+        sc = rng.random(K) * np.exp(rng.normal(0, 5, K))
+        sc[rng.integers(0, K, K // 10 + 1)] = 0.0
+        scores.append(sc)
+    got = owq.select_weak_batched([dev(sc) for sc in scores], [k for _, k in cases])
+    single = [owq.select_weak(dev(sc), k) for sc, (_, k) in zip(scores, cases)]
+    torch.cuda.synchronize()
+    for sc, (K, k), g, s1 in zip(scores, cases, got, single):
+        ref = oracle.select_weak(sc, k)
+        assert np.array_equal(host(g), ref), (K, k)
+        assert np.array_equal(host(s1), ref), (K, k)
+
+
+@pytest.mark.parametrize("K,k", [(1, 1), (5, 2), (100, 37), (4096, 32), (4097, 33), (11008, 86), (11264, 3000),
+                                 (11265, 1), (16384, 129), (16385, 16385), (28672, 221), (65536, 65536),
                                  (1 << 20, 1000)])
 def test_select_exact(owq, K, k):
     import oracle
