@@ -394,11 +394,14 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2,
         const int u = (wave * DPW + t) * 64 + lane;
         xdead[t] = (odd_tail && (((u & 7) ^ ((u >> 3) & 7)) >= 4)) ? 0x40000000 : 0;
     }
+    // chunks past the end (the pipeline's tail) are read out of the buffer's
+    // range: zeros, and no fetch of the last chunk again
     auto dma = [&](int c, char* stage) {
         const int cc = min(c, last);
+        const int dead = c > last ? 0x40000000 : 0;
 #pragma unroll
         for (int t = 0; t < DPW; t++)
-            dma16(xr, stage + (wave * DPW + t) * 1024, xsrc[t] + cc * 128 + (cc == last ? xdead[t] : 0));
+            dma16(xr, stage + (wave * DPW + t) * 1024, xsrc[t] + cc * 128 + (cc == last ? xdead[t] : 0) + dead);
     };
 
     const int rbase = wn * 32 * FN + l32;
@@ -410,9 +413,10 @@ __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2,
     typedef u32x3 QRegs[FN];
     auto load_q = [&](int c, QRegs& cw) {
         const int g = min(2 * min(c, nchunks - 1) + h, G - 1);
+        const int dead = c >= nchunks ? 0x40000000 : 0;
 #pragma unroll
         for (int f = 0; f < FN; f++)
-            cw[f] = __builtin_amdgcn_raw_buffer_load_b96(qr, (row_of(f) * G + g) * 12, 0, 0);
+            cw[f] = __builtin_amdgcn_raw_buffer_load_b96(qr, (row_of(f) * G + g) * 12 + dead, 0, 0);
     };
 
     const Magic mg = make_magic();

@@ -100,13 +100,15 @@ __global__ __launch_bounds__(64 * W * S) void k_mfv(MfvBatch b, int M)
     using SH = MfvShape<U, MC>;
     constexpr int GC = SH::GC, RS = SH::RS, STAGE = SH::STAGE, PT = SH::PT;
     constexpr int DPW = MC * PT / W;  // x loads per wave and chunk
-    // the codes are read once per launch; with 16-token x stages non-temporal code
-    // loads (cache policy "nt") were 5-7 % faster at M = 8 and 16 (1-4 % slower at
-    // M <= 4). They also raise the bytes fetched: a row's code chunk is 192 bytes,
-    // 1.5 cache lines, so two chunks share a line, and without a cached copy the
-    // shared line is fetched again for the second chunk (1.31x / 1.39x of the
-    // algorithmic bytes at M = 8 / 16 against 1.09x / 1.16x with default loads)
-    constexpr int kCodePolicy = MC == 16 ? 2 : 0;
+    // the codes are read once per launch; with 8- and 16-token x stages
+    // non-temporal code loads (cache policy "nt") were 5-7 % faster (1-4 % slower
+    // at M <= 4). A row's code chunk is GC * 12 bytes: with U = 4 that is 192
+    // bytes, 1.5 cache lines, so two chunks share a line, and without a cached
+    // copy the shared line is fetched again for the second chunk (1.39x of the
+    // algorithmic bytes at M = 16, 1.16x with default loads); with U = 8 (the
+    // 8-token instance) a chunk is 384 bytes, three whole lines of rows whose
+    // length is a multiple of 128 bytes
+    constexpr int kCodePolicy = MC >= 8 ? 2 : 0;
     static_assert((MC * PT) % W == 0, "x loads must split evenly over the waves");
     constexpr int CRS = SH::CRS, CQ = SH::CQ, CL = SH::CL;
     // D + 1 x stages per K group (chunks run D ahead), each its own array
@@ -165,14 +167,18 @@ __global__ __launch_bounds__(64 * W * S) void k_mfv(MfvBatch b, int M)
     // then hit distinct banks). Rows past the block and groups past K read zeros
     // or the next row; their x is zero.
     typedef uint4 QRegs[CL];
+    // chunks past the group's range (the pipeline's tail) are read out of the
+    // buffer's range, which returns zeros and fetches nothing: clamped to the
+    // last chunk they would read it again, from memory with non-temporal loads
     auto load_q = [&](int c, QRegs& cw) {
         const int cc = min(c, c1 - 1);
+        const int dead = c >= c1 ? 0x40000000 : 0;
 #pragma unroll
         for (int i = 0; i < CL; i++) {
             const int pc = 64 * i + lane;
             const int r = pc / CQ, o = (pc % CQ) * 16;
-            cw[i] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, ((wave * 16 + r) * G + cc * GC) * 12 + o, 0, kCodePolicy));
+            cw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  qr, ((wave * 16 + r) * G + cc * GC) * 12 + o + dead, 0, kCodePolicy));
         }
     };
     char* const crow = cs[wid];
@@ -346,7 +352,7 @@ hipError_t launch_mfv(const LinearDesc* d, int count, int M, hipStream_t s)
         }
     // up to 4 tokens: blocks of 2 row waves x 2 K groups (the 4096 x 11008
     // blocks then finish with the rest); more tokens: 4 row waves over the whole
-    // row (the 16-token x stages leave LDS for no second K group)
+    // row (the 8- and 16-token x stages leave LDS for no second K group)
     const int W = M <= 4 ? 2 : 4;
     MfvBatch b{};
     int nblocks = 0;
@@ -371,6 +377,12 @@ hipError_t launch_mfv(const LinearDesc* d, int count, int M, hipStream_t s)
     // waves but was 3-6 % slower)
     if (M <= 4)
         return launch_shape<4, 4, 2, 2, 1>(b, nblocks, M, s);
+    // 5 to 8 tokens: 32-group chunks (whole cache lines of codes, see
+    // kCodePolicy), two chunks ahead; 16-token stages of 32 groups would leave
+    // one block per CU (32.7 against 32.2 us at M = 8 with 16-group chunks, 39 us
+    // at M = 16 with one chunk ahead)
+    if (M <= 8)
+        return launch_shape<8, 8, 4, 1, 2>(b, nblocks, M, s);
     return launch_shape<4, 16, 4, 1, 2>(b, nblocks, M, s);
 }
 
