@@ -313,8 +313,10 @@ size_t owq_linear_backward_workspace_bytes(int64_t N, int64_t K, int32_t k);
  * L: HOST pointer to the packed layer (latency-favoured form); x: fp16 [M][K]
  * (the layer input; read only for dw_weak, may be NULL otherwise); dy: fp16
  * [M][N]; dx (may be NULL) and dw_weak (may be NULL) are outputs. dx is the
- * transposed 3-bit product: the codes are streamed once per 4 tokens and summed
- * over row slices in a fixed order (bitwise deterministic). workspace: >=
+ * transposed 3-bit product, summed over row slices in a fixed order (bitwise
+ * deterministic): up to 4 tokens on the vector ALUs (exact products), more on
+ * the matrix cores 16 tokens per pass (fp32 products; the environment variable
+ * OWQ_BACKWARD=vector, read at each call, keeps the vector form). workspace: >=
  * owq_linear_backward_workspace_bytes(N, K, k) bytes, 256-byte aligned, needed
  * only for dx. Errors as owq_linear, plus OWQ_ERR_WORKSPACE. */
 owq_status owq_linear_backward(const owq_layer* L, const uint16_t* x, const uint16_t* dy,

@@ -29,6 +29,9 @@
 //
 // dw_weak: a thread per row and 32 weak columns, x at the weak columns staged
 // in LDS 64 tokens at a time, fp32 FMAs in token order.
+#include <cstdlib>
+#include <cstring>
+
 #include "owq_decode.h"
 #include "owq_device.h"
 #include "owq_launch.h"
@@ -55,7 +58,11 @@ struct BwdArgs {
     float* P;            // partials [slices][MT][K]
     float* dw;           // [N][k]
     uint16_t* dx;        // this chunk's tokens, [MT][K]
+    float* PW;           // matrix-core form: weak-column partials [slices][16][k]
+    float* F;            // matrix-core form: fp32 column sums [16][K]
     int N, K, k, M, rows_per_slice, slices, tiles, dw_blocks, dx_blocks;
+    int mt;              // tokens of this chunk (matrix-core form)
+    int weak_blocks;     // matrix-core form: weak-partial blocks (slices x 16-column groups)
 };
 
 // The layers of one launch. Blocks: the dw blocks of every layer (layer l from
@@ -436,6 +443,264 @@ __global__ __launch_bounds__(256) void k_bwd_dx_finalize(const BwdBatch bt)
     a.dx[e] = f2h(t);
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core form of dx for more than 4 tokens, 16 per pass. The contraction
+// runs over the rows i, while a lane's decoded group holds 32 columns of one
+// row, so the decoded codes go through LDS: a block (4 waves) owns 256 columns
+// (8 groups) and one slice of rows; per step of 32 rows, thread t decodes group
+// t % 8 of row t / 8 into the LDS tile (exact (q - z) fp16, natural column
+// order) and stores the coefficients s_i dy[m][i] (fp32, exact) of the 32 rows
+// and 16 tokens; then each wave multiplies its 64 columns with
+// v_mfma_f32_16x16x4_f32: A[m][r] = s_i dy[m][i], B[r][j] = (q_ij - z_i), 4 rows
+// per instruction, fp32 products and sums (the products of the vector form are
+// exact, these are rounded once, to fp32: the same 2^-24 per term). The tile is
+// double-buffered (one barrier per step) and the next step's loads are issued
+// before this step's products. The block stores its partial sums P[slice][m][j].
+constexpr int kMmaCols = 256;  // columns per block
+constexpr int kMmaRows = 32;   // rows per step
+constexpr int kMmaRowBytes = kMmaCols * 2 + 32;  // LDS row of the decoded tile (padded: conflict-free B reads)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s, char* lds)
+{
+    char* const tw = lds;                                 // [2][32][kMmaRowBytes]
+    float* const tc = reinterpret_cast<float*>(lds + 2 * kMmaRows * kMmaRowBytes);  // [2][32][16]
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int G = a.K >> 5;
+    const int lrow = t >> 3, lg = t & 7;
+    const int g = min(tile * 8 + lg, G - 1);  // groups past K decode a valid group; their columns are not stored
+    const int r0 = s * a.rows_per_slice, r1 = min(a.N, r0 + a.rows_per_slice);
+    const int nsteps = (r1 - r0 + kMmaRows - 1) / kMmaRows;
+    const Magic mg = make_magic();
+    // coefficient entries of this thread: e = t and t + 256 of the 32 x 16 step tile
+    // (row e / 16, token e % 16)
+    uint32_t w0, w1, w2, zb;
+    uint32_t sh[2], dh[2];
+    auto issue = [&](int st) {
+        const int rr = r0 + st * kMmaRows + lrow;
+        const int r = min(rr, r1 - 1);
+        const uint32_t* src = a.q + ((int64_t)r * G + g) * 3;
+        w0 = src[0];
+        w1 = src[1];
+        w2 = src[2];
+        zb = a.zeros[r];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int e = t + 256 * h;
+            const int cr = min(r0 + st * kMmaRows + (e >> 4), r1 - 1);
+            const int m = min(e & 15, a.mt - 1);
+            sh[h] = a.scales[cr];
+            dh[h] = a.dy[(int64_t)m * a.N + cr];
+        }
+    };
+    f32x4 acc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++)
+        acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    issue(0);
+    for (int st = 0; st < nsteps; st++) {
+        const int buf = st & 1;
+        // this step's tile: decoded codes and coefficients (rows past the slice
+        // and tokens past the chunk get a zero coefficient)
+        {
+            uint32_t p[16];
+            decode_group(w0, w1, w2, mg, make_zero_sub(zb), p);
+            uint4* dst = reinterpret_cast<uint4*>(tw + (buf * kMmaRows + lrow) * kMmaRowBytes + lg * 64);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++)
+                dst[q4] = make_uint4(p[4 * q4], p[4 * q4 + 1], p[4 * q4 + 2], p[4 * q4 + 3]);
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int e = t + 256 * h;
+                const bool live = r0 + st * kMmaRows + (e >> 4) < r1 && (e & 15) < a.mt;
+                tc[buf * 512 + e] = live ? h2f((uint16_t)sh[h]) * h2f((uint16_t)dh[h]) : 0.0f;
+            }
+        }
+        if (st + 1 < nsteps)
+            issue(st + 1);
+        __syncthreads();
+        const char* trow = tw + buf * kMmaRows * kMmaRowBytes;
+#pragma unroll
+        for (int ks = 0; ks < kMmaRows / 4; ks++) {
+            const int kr = 4 * ks + (lane >> 4);
+            const float av = tc[buf * 512 + kr * 16 + (lane & 15)];
+#pragma unroll
+            for (int cb = 0; cb < 4; cb++) {
+                const int col = 64 * wave + 16 * cb + (lane & 15);
+                const float bv = h2f(*reinterpret_cast<const uint16_t*>(trow + kr * kMmaRowBytes + col * 2));
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[cb], 0, 0, 0);
+            }
+        }
+    }
+    // D element r of lane l: token 4 (l / 16) + r, column l % 16 of the 16-column block
+#pragma unroll
+    for (int cb = 0; cb < 4; cb++) {
+        const int j = tile * kMmaCols + 64 * wave + 16 * cb + (lane & 15);
+        if (j < a.K)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int m = 4 * (lane >> 4) + r;
+                if (m < a.mt)
+                    a.P[((int64_t)s * 16 + m) * a.K + j] = acc[cb][r];
+            }
+    }
+}
+
+// weak-column partials of one row slice: PW[slice][m][c] = sum over the slice's
+// rows (in order) of dy[m][i] w_weak[i][c], 16 columns per block, thread (c, m),
+// 64 rows staged in LDS at a time (every load of a stage issued before the
+// first LDS store)
+__device__ __forceinline__ void bwd_mma_weak(const BwdArgs& a, int cg, int s, char* lds)
+{
+    float* const dyl = reinterpret_cast<float*>(lds);  // [16][64]
+    float* const wl = dyl + 16 * 64;                    // [64][16]
+    const int t = threadIdx.x;
+    const int cl = t >> 4, m = t & 15;
+    const int c0 = cg * 16;
+    const int r0 = s * a.rows_per_slice, r1 = min(a.N, r0 + a.rows_per_slice);
+    float acc = 0.0f;
+    for (int rb = r0; rb < r1; rb += 64) {
+        const int nr = min(64, r1 - rb);
+        uint32_t dv[4], wv[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int e = t + 256 * u;  // dy: token e / 64, row e % 64; w: row e / 16, column e % 16
+            const int dm = min(e >> 6, a.mt - 1), dr = min(e & 63, nr - 1);
+            dv[u] = a.dy[(int64_t)dm * a.N + rb + dr];
+            const int wr = min(e >> 4, nr - 1), wc = min(c0 + (e & 15), a.k - 1);
+            wv[u] = a.ww[(int64_t)(rb + wr) * a.k + wc];
+        }
+        __syncthreads();  // the previous stage is no longer read
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int e = t + 256 * u;
+            dyl[e] = (e >> 6) < a.mt && (e & 63) < nr ? h2f((uint16_t)dv[u]) : 0.0f;
+            wl[e] = (e >> 4) < nr && c0 + (e & 15) < a.k ? h2f((uint16_t)wv[u]) : 0.0f;
+        }
+        __syncthreads();
+        for (int r = 0; r < nr; r++)
+            acc = __builtin_fmaf(dyl[m * 64 + r], wl[r * 16 + cl], acc);
+    }
+    if (c0 + cl < a.k && m < a.mt)
+        a.PW[((int64_t)s * 16 + m) * a.k + c0 + cl] = acc;
+}
+
+// blocks: the weak-partial blocks of every layer (layer l from dw0[l]), then the
+// dense blocks (layer l from dx0[l])
+__global__ __launch_bounds__(256) void k_bwd_mma(const BwdBatch bt)
+{
+    __shared__ __attribute__((aligned(16))) char lds[2 * kMmaRows * kMmaRowBytes + 2 * kMmaRows * 16 * 4];
+    const int b = blockIdx.x;
+    if (b < bt.dw0[bt.count]) {
+        const int li = layer_of(bt.dw0, bt.count, b);
+        const BwdArgs& a = bt.L[li];
+        const int bb = b - bt.dw0[li];
+        const int ngrp = (a.k + 15) / 16;
+        bwd_mma_weak(a, bb % ngrp, bb / ngrp, lds);
+        return;
+    }
+    const int li = layer_of(bt.dx0, bt.count, b);
+    const BwdArgs& a = bt.L[li];
+    const int bb = b - bt.dx0[li];
+    bwd_mma_dense(a, bb % a.tiles, bb / a.tiles, lds);
+}
+
+// dx[m][j] = fp16(sum over the slices' partials), and the fp32 sum to F for the
+// weak columns' correction; 32 columns x 8 phases per block (as k_bwd_dx_finalize)
+__global__ __launch_bounds__(256) void k_bwd_mma_finalize(const BwdBatch bt)
+{
+    __shared__ float red[8][32];
+    const int li = layer_of(bt.f0, bt.count, blockIdx.x);
+    const BwdArgs& a = bt.L[li];
+    const int K = a.K, slices = a.slices;
+    const int col = threadIdx.x & 31, ph = threadIdx.x >> 5;
+    const int64_t e = (int64_t)(blockIdx.x - bt.f0[li]) * 32 + col;  // m * K + j, m < mt
+    const int64_t n = (int64_t)a.mt * K, stride = (int64_t)16 * K;
+    const bool ok = e < n;
+    const float* __restrict__ p = a.P + (ok ? e : 0);
+    float t = 0.0f;
+    if (ok) {
+        int s = ph;
+        for (; s + 56 < slices; s += 64) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                v[u] = p[(int64_t)(s + 8 * u) * stride];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                t += v[u];
+        }
+        for (; s < slices; s += 8)
+            t += p[(int64_t)s * stride];
+    }
+    red[ph][col] = t;
+    __syncthreads();
+    if (ph != 0 || !ok)
+        return;
+    t = red[0][col];
+#pragma unroll
+    for (int f = 1; f < 8; f++)
+        t += red[f][col];
+    a.dx[e] = f2h(t);
+    if (a.k > 0)
+        a.F[e] = t;
+}
+
+// the weak columns: dx[m][idx_c] = fp16(F[m][idx_c] + sum over the slices of
+// PW[s][m][c]) (the dense codes there are the zero point, but their partial is
+// added as for any column); a thread per (c, m)
+__global__ __launch_bounds__(256) void k_bwd_mma_weak_finalize(const BwdBatch bt)
+{
+    const int li = layer_of(bt.f0, bt.count, blockIdx.x);
+    const BwdArgs& a = bt.L[li];
+    const int64_t e = (int64_t)(blockIdx.x - bt.f0[li]) * 256 + threadIdx.x;  // c * 16 + m
+    const int c = (int)(e >> 4), m = (int)(e & 15);
+    if (c >= a.k || m >= a.mt)
+        return;
+    float w = 0.0f;
+    for (int s = 0; s < a.slices; s++)
+        w += a.PW[((int64_t)s * 16 + m) * a.k + c];
+    const int j = a.idx[c];
+    a.dx[(int64_t)m * a.K + j] = f2h(a.F[(int64_t)m * a.K + j] + w);
+}
+
+// one 16-token chunk of every layer in bt on the matrix cores
+hipError_t mma_chunk_launch(BwdBatch& bt, hipStream_t s)
+{
+    int nb = 0;
+    for (int l = 0; l < bt.count; l++) {
+        bt.dw0[l] = nb;
+        nb += bt.L[l].weak_blocks;
+    }
+    bt.dw0[bt.count] = nb;
+    for (int l = 0; l < bt.count; l++) {
+        bt.dx0[l] = nb;
+        nb += bt.L[l].dx_blocks;
+    }
+    bt.dx0[bt.count] = nb;
+    int nf = 0;
+    for (int l = 0; l < bt.count; l++) {
+        bt.f0[l] = nf;
+        nf += bt.L[l].dx_blocks > 0 ? (int)((bt.L[l].mt * (int64_t)bt.L[l].K + 31) / 32) : 0;
+    }
+    bt.f0[bt.count] = nf;
+    if (nb > 0)
+        hipLaunchKernelGGL(k_bwd_mma, dim3((unsigned)nb), dim3(256), 0, s, bt);
+    if (nf > 0)
+        hipLaunchKernelGGL(k_bwd_mma_finalize, dim3((unsigned)nf), dim3(256), 0, s, bt);
+    int nw = 0;
+    for (int l = 0; l < bt.count; l++) {
+        bt.f0[l] = nw;
+        nw += bt.L[l].weak_blocks > 0 ? (int)((16 * (int64_t)bt.L[l].k + 255) / 256) : 0;
+    }
+    bt.f0[bt.count] = nw;
+    if (nw > 0)
+        hipLaunchKernelGGL(k_bwd_mma_weak_finalize, dim3((unsigned)nw), dim3(256), 0, s, bt);
+    return hipGetLastError();
+}
+
 // one token chunk of every layer in bt (dy / dx already at the chunk): the part
 // launch, then the finalize launch of the layers that want dx
 template <int MT>
@@ -485,10 +750,25 @@ BwdPlan bwd_plan(int64_t N, int64_t K, int32_t k)
     p.rows_per_slice = (N + p.slices - 1) / p.slices;
     p.slices = (N + p.rows_per_slice - 1) / p.rows_per_slice;  // no empty slice
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    (void)k;
     p.off_p = 0;
-    p.total = al((size_t)p.slices * kBwdMaxMT * K * sizeof(float));
+    const size_t vec_total = al((size_t)p.slices * kBwdMaxMT * K * sizeof(float));
+    // matrix-core form: slices of 512 rows (a multiple of the 32-row step)
+    p.m_rows = 512;
+    p.m_slices = (N + p.m_rows - 1) / p.m_rows;
+    p.m_off_p = 0;
+    p.m_off_pw = al((size_t)p.m_slices * 16 * K * sizeof(float));
+    p.m_off_f = p.m_off_pw + al((size_t)p.m_slices * 16 * (k > 0 ? k : 1) * sizeof(float));
+    const size_t mma_total = p.m_off_f + al((size_t)16 * K * sizeof(float));
+    p.total = vec_total > mma_total ? vec_total : mma_total;
     return p;
+}
+
+// The matrix-core form for more than 4 tokens; OWQ_BACKWARD=vector (read at
+// each call) keeps the vector form at every M.
+bool mma_backward_enabled()
+{
+    const char* e = std::getenv("OWQ_BACKWARD");
+    return !(e && std::strcmp(e, "vector") == 0);
 }
 
 hipError_t launch_linear_backward_batched(const LinearDesc* d, const uint16_t* const* dy, int count, int64_t M,
@@ -523,6 +803,37 @@ hipError_t launch_linear_backward_batched(const LinearDesc* d, const uint16_t* c
     }
     if (!any_dx)  // dw only: the dw blocks alone (the token count does not matter)
         return chunk_launch<1>(bt, s);
+    if (M > kBwdMaxMT && mma_backward_enabled()) {
+        // dw_weak: the dw blocks alone, once; dx: 16 tokens per pass on the matrix cores
+        BwdBatch w = bt;
+        bool any_dw = false;
+        for (int l = 0; l < count; l++) {
+            w.L[l].dx_blocks = 0;
+            any_dw = any_dw || w.L[l].dw_blocks > 0;
+        }
+        hipError_t e = any_dw ? chunk_launch<1>(w, s) : hipSuccess;
+        for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += 16) {
+            BwdBatch c = bt;
+            for (int l = 0; l < count; l++) {
+                BwdArgs& a = c.L[l];
+                char* base = static_cast<char*>(ws[l]);
+                a.dy = dy[l] + m0 * d[l].N;
+                a.dx = dx[l] ? dx[l] + m0 * d[l].K : nullptr;
+                a.mt = (int)(M - m0 < 16 ? M - m0 : 16);
+                a.rows_per_slice = (int)p[l].m_rows;
+                a.slices = (int)p[l].m_slices;
+                a.tiles = (int)((d[l].K + kMmaCols - 1) / kMmaCols);
+                a.P = dx[l] ? reinterpret_cast<float*>(base + p[l].m_off_p) : nullptr;
+                a.PW = dx[l] ? reinterpret_cast<float*>(base + p[l].m_off_pw) : nullptr;
+                a.F = dx[l] ? reinterpret_cast<float*>(base + p[l].m_off_f) : nullptr;
+                a.dx_blocks = dx[l] ? a.slices * a.tiles : 0;
+                a.weak_blocks = (dx[l] && d[l].k > 0) ? a.slices * ((d[l].k + 15) / 16) : 0;
+                a.dw_blocks = 0;
+            }
+            e = mma_chunk_launch(c, s);
+        }
+        return e;
+    }
     hipError_t e = hipSuccess;
     for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kBwdMaxMT) {
         const int mt = (int)(M - m0 < kBwdMaxMT ? M - m0 : kBwdMaxMT);

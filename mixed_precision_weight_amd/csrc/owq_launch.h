@@ -91,8 +91,13 @@ hipError_t launch_linear_storage(const LinearDesc& d, int64_t M, void* ws, hipSt
 
 // ------------------------------------------ backward (weak-column tuning) --
 struct BwdPlan {
-    int64_t slices, rows_per_slice;  // row slices of the transposed product
-    size_t off_p, total;             // workspace byte offsets / size
+    int64_t slices, rows_per_slice;  // row slices of the transposed product (vector form, M <= 4)
+    size_t off_p;                    // its partial sums
+    // the matrix-core form (M > 4, 16 tokens per pass): row slices, partial
+    // sums of the dense part and of the weak columns, the fp32 column sums
+    int64_t m_slices, m_rows;
+    size_t m_off_p, m_off_pw, m_off_f;
+    size_t total;                    // workspace bytes (both forms share it)
 };
 BwdPlan bwd_plan(int64_t N, int64_t K, int32_t k);
 // dx = dy W (fp16 [M][K], may be NULL) and dw_weak = dy^T x[:, idx] (fp32 [N][k],
