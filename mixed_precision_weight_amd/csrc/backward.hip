@@ -331,24 +331,28 @@ __device__ __forceinline__ void bwd_dense(const BwdArgs& a, int tile, int s, flo
 // load of a stage before the first LDS store, so the chain is indices -> x.
 __device__ __forceinline__ void bwd_dw(const BwdArgs& a, int bi, float* xs)
 {
-    constexpr int MC = 64, MD = 8;  // tokens per stage; dy values loaded up front
+    // 256 working threads; in a larger block the others pass the barriers only
+    const int tid = threadIdx.x & 255;
+    const bool on = threadIdx.x < 256;
+    constexpr int MC = 64, MD = 16;  // tokens per stage; dy values loaded up front
     int* cols = reinterpret_cast<int*>(xs + MC * kWeakTile);
     const int rt = (a.N + 255) / 256;
-    const int i = (bi % rt) * 256 + threadIdx.x;
+    const int i = (bi % rt) * 256 + tid;
     const int c0 = (bi / rt) * kWeakTile;
     const int nc = min(kWeakTile, a.k - c0);
     const int ic = min(i, a.N - 1);
-    const int jl = a.idx[c0 + min((int)threadIdx.x & (kWeakTile - 1), nc - 1)];
+    const int jl = a.idx[c0 + min(tid & (kWeakTile - 1), nc - 1)];
     float* dys = xs + MC * kWeakTile + 64;  // [MD][256]: dy of the first tokens
     uint32_t d0[MD];
 #pragma unroll
     for (int mm = 0; mm < MD; mm++)
         d0[mm] = a.dy[(int64_t)min(mm, a.M - 1) * a.N + ic];
-    if (threadIdx.x < kWeakTile)
-        cols[threadIdx.x] = (jl >= 0 && jl < a.K) ? jl : 0;
+    if (on && tid < kWeakTile)
+        cols[tid] = (jl >= 0 && jl < a.K) ? jl : 0;
+    if (on)
 #pragma unroll
-    for (int mm = 0; mm < MD; mm++)
-        dys[mm * 256 + threadIdx.x] = h2f((uint16_t)d0[mm]);
+        for (int mm = 0; mm < MD; mm++)
+            dys[mm * 256 + tid] = h2f((uint16_t)d0[mm]);
     float acc[kWeakTile];
 #pragma unroll
     for (int c = 0; c < kWeakTile; c++)
@@ -359,26 +363,27 @@ __device__ __forceinline__ void bwd_dw(const BwdArgs& a, int bi, float* xs)
         uint32_t v[MC * kWeakTile / 256];
 #pragma unroll
         for (int u = 0; u < MC * kWeakTile / 256; u++) {
-            const int e = threadIdx.x + 256 * u;
+            const int e = tid + 256 * u;
             const int mm = e / kWeakTile, cc = e % kWeakTile;
             v[u] = a.x[(int64_t)(m0 + min(mm, mn - 1)) * a.K + cols[cc]];
         }
+        if (on)
 #pragma unroll
-        for (int u = 0; u < MC * kWeakTile / 256; u++) {
-            const int e = threadIdx.x + 256 * u;
-            const int mm = e / kWeakTile, cc = e % kWeakTile;
-            xs[e] = (mm < mn && cc < nc) ? h2f((uint16_t)v[u]) : 0.0f;
-        }
+            for (int u = 0; u < MC * kWeakTile / 256; u++) {
+                const int e = tid + 256 * u;
+                const int mm = e / kWeakTile, cc = e % kWeakTile;
+                xs[e] = (mm < mn && cc < nc) ? h2f((uint16_t)v[u]) : 0.0f;
+            }
         __syncthreads();
         for (int mm = 0; mm < mn; mm++) {
             const int m = m0 + mm;
-            const float d = m < MD ? dys[m * 256 + threadIdx.x] : h2f(a.dy[(int64_t)m * a.N + ic]);
+            const float d = m < MD ? dys[m * 256 + tid] : h2f(a.dy[(int64_t)m * a.N + ic]);
 #pragma unroll
             for (int c = 0; c < kWeakTile; c++)
                 acc[c] = __builtin_fmaf(d, xs[mm * kWeakTile + c], acc[c]);
         }
     }
-    if (i < a.N)
+    if (on && i < a.N)
         for (int c = 0; c < nc; c++)
             a.dw[(int64_t)i * a.k + c0 + c] = acc[c];
 }
@@ -389,7 +394,7 @@ __device__ __forceinline__ void bwd_dw(const BwdArgs& a, int bi, float* xs)
 template <int MT>
 __global__ __launch_bounds__(256) void k_bwd_part(const BwdBatch bt)
 {
-    __shared__ float red[3 * 32 * 64];  // 24 KiB, shared by the two roles
+    __shared__ float red[3 * 32 * 64 + 128];  // 24.5 KiB, shared by the two roles
     const int b = blockIdx.x;
     if (b < bt.dw0[bt.count]) {
         const int li = layer_of(bt.dw0, bt.count, b);
@@ -458,7 +463,8 @@ __global__ __launch_bounds__(256) void k_bwd_dx_finalize(const BwdBatch bt)
 // before this step's products. The block stores its partial sums P[slice][m][j].
 constexpr int kMmaCols = 256;  // columns per block
 constexpr int kMmaRows = 32;   // rows per step
-constexpr int kMmaRowBytes = kMmaCols * 2 + 32;  // LDS row of the decoded tile (padded: conflict-free B reads)
+constexpr int kMmaRowBytes = kMmaCols * 2 + 64;  // LDS row of the decoded tile (padded: 144 dwords, the
+                                                 // four rows of a B read on distinct banks)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -474,8 +480,8 @@ __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s,
     const int r0 = s * a.rows_per_slice, r1 = min(a.N, r0 + a.rows_per_slice);
     const int nsteps = (r1 - r0 + kMmaRows - 1) / kMmaRows;
     const Magic mg = make_magic();
-    // coefficient entries of this thread: e = t and t + 256 of the 32 x 16 step tile
-    // (row e / 16, token e % 16)
+    // loads of step st: the row's group and, for the coefficient entries e = t
+    // and t + 256 of the 32 x 16 tile (row e / 16, token e % 16), s and dy
     uint32_t w0, w1, w2, zb;
     uint32_t sh[2], dh[2];
     auto issue = [&](int st) {
@@ -495,49 +501,73 @@ __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s,
             dh[h] = a.dy[(int64_t)m * a.N + cr];
         }
     };
+    // step st's tile into buffer st & 1: decoded codes and coefficients (rows
+    // past the slice and tokens past the chunk get a zero coefficient)
+    auto stage = [&](int st) {
+        const int buf = st & 1;
+        uint32_t p[16];
+        decode_group(w0, w1, w2, mg, make_zero_sub(zb), p);
+        // 16-byte chunk q of group lg at slot q ^ (lg >> 2): the lanes lg and lg + 4
+        // of a 16-lane write pass then start on different banks
+        uint4* dst = reinterpret_cast<uint4*>(tw + (buf * kMmaRows + lrow) * kMmaRowBytes + lg * 64);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++)
+            dst[q4 ^ (lg >> 2)] = make_uint4(p[4 * q4], p[4 * q4 + 1], p[4 * q4 + 2], p[4 * q4 + 3]);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int e = t + 256 * h;
+            const bool live = r0 + st * kMmaRows + (e >> 4) < r1 && (e & 15) < a.mt;
+            tc[buf * 512 + e] = live ? h2f((uint16_t)sh[h]) * h2f((uint16_t)dh[h]) : 0.0f;
+        }
+    };
     f32x4 acc[4];
 #pragma unroll
     for (int cb = 0; cb < 4; cb++)
         acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     issue(0);
+    stage(0);
+    if (nsteps > 1)
+        issue(1);
+    __syncthreads();
     for (int st = 0; st < nsteps; st++) {
         const int buf = st & 1;
-        // this step's tile: decoded codes and coefficients (rows past the slice
-        // and tokens past the chunk get a zero coefficient)
-        {
-            uint32_t p[16];
-            decode_group(w0, w1, w2, mg, make_zero_sub(zb), p);
-            uint4* dst = reinterpret_cast<uint4*>(tw + (buf * kMmaRows + lrow) * kMmaRowBytes + lg * 64);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; q4++)
-                dst[q4] = make_uint4(p[4 * q4], p[4 * q4 + 1], p[4 * q4 + 2], p[4 * q4 + 3]);
-#pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const int e = t + 256 * h;
-                const bool live = r0 + st * kMmaRows + (e >> 4) < r1 && (e & 15) < a.mt;
-                tc[buf * 512 + e] = live ? h2f((uint16_t)sh[h]) * h2f((uint16_t)dh[h]) : 0.0f;
-            }
-        }
-        if (st + 1 < nsteps)
-            issue(st + 1);
-        __syncthreads();
+        // this step's operands into registers, then its 32 products; then the
+        // next step's tile into the other buffer
+        // B: lane l reads the fp16 pair of columns 64 w + 32 pb + 2 (l % 16) + (0, 1)
+        // as one dword; accumulator 2 pb + h holds the even (h = 0) or odd columns
         const char* trow = tw + buf * kMmaRows * kMmaRowBytes;
+        float av[kMmaRows / 4], bv[kMmaRows / 4][4];
 #pragma unroll
         for (int ks = 0; ks < kMmaRows / 4; ks++) {
             const int kr = 4 * ks + (lane >> 4);
-            const float av = tc[buf * 512 + kr * 16 + (lane & 15)];
+            av[ks] = tc[buf * 512 + kr * 16 + (lane & 15)];
 #pragma unroll
-            for (int cb = 0; cb < 4; cb++) {
-                const int col = 64 * wave + 16 * cb + (lane & 15);
-                const float bv = h2f(*reinterpret_cast<const uint16_t*>(trow + kr * kMmaRowBytes + col * 2));
-                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[cb], 0, 0, 0);
+            for (int pb = 0; pb < 2; pb++) {
+                const int col = 64 * wave + 32 * pb + 2 * (lane & 15);
+                const int cg = col >> 5, cq = (col >> 3) & 3;  // group, 16-byte chunk
+                const int off = cg * 64 + ((cq ^ (cg >> 2)) << 4) + (col & 7) * 2;
+                const half2_t hp = as_h2(*reinterpret_cast<const uint32_t*>(trow + kr * kMmaRowBytes + off));
+                bv[ks][2 * pb] = (float)hp.x;
+                bv[ks][2 * pb + 1] = (float)hp.y;
             }
         }
+#pragma unroll
+        for (int ks = 0; ks < kMmaRows / 4; ks++)
+#pragma unroll
+            for (int cb = 0; cb < 4; cb++)
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], bv[ks][cb], acc[cb], 0, 0, 0);
+        if (st + 1 < nsteps) {
+            stage(st + 1);
+            if (st + 2 < nsteps)
+                issue(st + 2);
+        }
+        __syncthreads();
     }
-    // D element r of lane l: token 4 (l / 16) + r, column l % 16 of the 16-column block
+    // D element r of lane l: token 4 (l / 16) + r; accumulator cb = 2 pb + h:
+    // column 64 w + 32 pb + 2 (l % 16) + h
 #pragma unroll
     for (int cb = 0; cb < 4; cb++) {
-        const int j = tile * kMmaCols + 64 * wave + 16 * cb + (lane & 15);
+        const int j = tile * kMmaCols + 64 * wave + 32 * (cb >> 1) + 2 * (lane & 15) + (cb & 1);
         if (j < a.K)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
@@ -556,7 +586,9 @@ __device__ __forceinline__ void bwd_mma_weak(const BwdArgs& a, int cg, int s, ch
 {
     float* const dyl = reinterpret_cast<float*>(lds);  // [16][64]
     float* const wl = dyl + 16 * 64;                    // [64][16]
-    const int t = threadIdx.x;
+    // 256 working threads; in a larger block the others pass the barriers only
+    const int t = threadIdx.x & 255;
+    const bool on = threadIdx.x < 256;
     const int cl = t >> 4, m = t & 15;
     const int c0 = cg * 16;
     const int r0 = s * a.rows_per_slice, r1 = min(a.N, r0 + a.rows_per_slice);
@@ -573,26 +605,33 @@ __device__ __forceinline__ void bwd_mma_weak(const BwdArgs& a, int cg, int s, ch
             wv[u] = a.ww[(int64_t)(rb + wr) * a.k + wc];
         }
         __syncthreads();  // the previous stage is no longer read
+        if (on)
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int e = t + 256 * u;
-            dyl[e] = (e >> 6) < a.mt && (e & 63) < nr ? h2f((uint16_t)dv[u]) : 0.0f;
-            wl[e] = (e >> 4) < nr && c0 + (e & 15) < a.k ? h2f((uint16_t)wv[u]) : 0.0f;
-        }
+            for (int u = 0; u < 4; u++) {
+                const int e = t + 256 * u;
+                dyl[e] = (e >> 6) < a.mt && (e & 63) < nr ? h2f((uint16_t)dv[u]) : 0.0f;
+                wl[e] = (e >> 4) < nr && c0 + (e & 15) < a.k ? h2f((uint16_t)wv[u]) : 0.0f;
+            }
         __syncthreads();
         for (int r = 0; r < nr; r++)
             acc = __builtin_fmaf(dyl[m * 64 + r], wl[r * 16 + cl], acc);
     }
-    if (c0 + cl < a.k && m < a.mt)
+    if (on && c0 + cl < a.k && m < a.mt)
         a.PW[((int64_t)s * 16 + m) * a.k + c0 + cl] = acc;
 }
 
-// blocks: the weak-partial blocks of every layer (layer l from dw0[l]), then the
-// dense blocks (layer l from dx0[l])
+// blocks: the dw_weak blocks of every layer (layer l from f0[l]; f0[count] =
+// dw0[0]), the weak-partial blocks (layer l from dw0[l]), then the dense blocks
+// (layer l from dx0[l])
 __global__ __launch_bounds__(256) void k_bwd_mma(const BwdBatch bt)
 {
     __shared__ __attribute__((aligned(16))) char lds[2 * kMmaRows * kMmaRowBytes + 2 * kMmaRows * 16 * 4];
     const int b = blockIdx.x;
+    if (b < bt.f0[bt.count]) {
+        const int li = layer_of(bt.f0, bt.count, b);
+        bwd_dw(bt.L[li], b - bt.f0[li], reinterpret_cast<float*>(lds));
+        return;
+    }
     if (b < bt.dw0[bt.count]) {
         const int li = layer_of(bt.dw0, bt.count, b);
         const BwdArgs& a = bt.L[li];
@@ -607,42 +646,32 @@ __global__ __launch_bounds__(256) void k_bwd_mma(const BwdBatch bt)
     bwd_mma_dense(a, bb % a.tiles, bb / a.tiles, lds);
 }
 
-// dx[m][j] = fp16(sum over the slices' partials), and the fp32 sum to F for the
-// weak columns' correction; 32 columns x 8 phases per block (as k_bwd_dx_finalize)
+// dx[m][j] = fp16(sum over the slices' partials, in slice order), and the fp32
+// sum to F for the weak columns' correction; a thread per output, 8 partials
+// loaded at a time
 __global__ __launch_bounds__(256) void k_bwd_mma_finalize(const BwdBatch bt)
 {
-    __shared__ float red[8][32];
     const int li = layer_of(bt.f0, bt.count, blockIdx.x);
     const BwdArgs& a = bt.L[li];
     const int K = a.K, slices = a.slices;
-    const int col = threadIdx.x & 31, ph = threadIdx.x >> 5;
-    const int64_t e = (int64_t)(blockIdx.x - bt.f0[li]) * 32 + col;  // m * K + j, m < mt
+    const int64_t e = (int64_t)(blockIdx.x - bt.f0[li]) * 256 + threadIdx.x;  // m * K + j, m < mt
     const int64_t n = (int64_t)a.mt * K, stride = (int64_t)16 * K;
-    const bool ok = e < n;
-    const float* __restrict__ p = a.P + (ok ? e : 0);
-    float t = 0.0f;
-    if (ok) {
-        int s = ph;
-        for (; s + 56 < slices; s += 64) {
-            float v[8];
-#pragma unroll
-            for (int u = 0; u < 8; u++)
-                v[u] = p[(int64_t)(s + 8 * u) * stride];
-#pragma unroll
-            for (int u = 0; u < 8; u++)
-                t += v[u];
-        }
-        for (; s < slices; s += 8)
-            t += p[(int64_t)s * stride];
-    }
-    red[ph][col] = t;
-    __syncthreads();
-    if (ph != 0 || !ok)
+    if (e >= n)
         return;
-    t = red[0][col];
+    const float* __restrict__ p = a.P + e;
+    float t = 0.0f;
+    int s = 0;
+    for (; s + 8 <= slices; s += 8) {
+        float v[8];
 #pragma unroll
-    for (int f = 1; f < 8; f++)
-        t += red[f][col];
+        for (int u = 0; u < 8; u++)
+            v[u] = p[(int64_t)(s + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            t += v[u];
+    }
+    for (; s < slices; s++)
+        t += p[(int64_t)s * stride];
     a.dx[e] = f2h(t);
     if (a.k > 0)
         a.F[e] = t;
@@ -659,10 +688,22 @@ __global__ __launch_bounds__(256) void k_bwd_mma_weak_finalize(const BwdBatch bt
     const int c = (int)(e >> 4), m = (int)(e & 15);
     if (c >= a.k || m >= a.mt)
         return;
-    float w = 0.0f;
-    for (int s = 0; s < a.slices; s++)
-        w += a.PW[((int64_t)s * 16 + m) * a.k + c];
     const int j = a.idx[c];
+    const float* __restrict__ pw = a.PW + (int64_t)m * a.k + c;
+    const int64_t stride = (int64_t)16 * a.k;
+    float w = 0.0f;
+    int s = 0;
+    for (; s + 8 <= a.slices; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            v[u] = pw[(int64_t)(s + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            w += v[u];
+    }
+    for (; s < a.slices; s++)
+        w += pw[(int64_t)s * stride];
     a.dx[(int64_t)m * a.K + j] = f2h(a.F[(int64_t)m * a.K + j] + w);
 }
 
@@ -670,6 +711,11 @@ __global__ __launch_bounds__(256) void k_bwd_mma_weak_finalize(const BwdBatch bt
 hipError_t mma_chunk_launch(BwdBatch& bt, hipStream_t s)
 {
     int nb = 0;
+    for (int l = 0; l < bt.count; l++) {  // dw_weak blocks (first chunk only)
+        bt.f0[l] = nb;
+        nb += bt.L[l].dw_blocks;
+    }
+    bt.f0[bt.count] = nb;
     for (int l = 0; l < bt.count; l++) {
         bt.dw0[l] = nb;
         nb += bt.L[l].weak_blocks;
@@ -680,14 +726,14 @@ hipError_t mma_chunk_launch(BwdBatch& bt, hipStream_t s)
         nb += bt.L[l].dx_blocks;
     }
     bt.dx0[bt.count] = nb;
+    if (nb > 0)
+        hipLaunchKernelGGL(k_bwd_mma, dim3((unsigned)nb), dim3(256), 0, s, bt);
     int nf = 0;
     for (int l = 0; l < bt.count; l++) {
         bt.f0[l] = nf;
-        nf += bt.L[l].dx_blocks > 0 ? (int)((bt.L[l].mt * (int64_t)bt.L[l].K + 31) / 32) : 0;
+        nf += bt.L[l].dx_blocks > 0 ? (int)((bt.L[l].mt * (int64_t)bt.L[l].K + 255) / 256) : 0;
     }
     bt.f0[bt.count] = nf;
-    if (nb > 0)
-        hipLaunchKernelGGL(k_bwd_mma, dim3((unsigned)nb), dim3(256), 0, s, bt);
     if (nf > 0)
         hipLaunchKernelGGL(k_bwd_mma_finalize, dim3((unsigned)nf), dim3(256), 0, s, bt);
     int nw = 0;
@@ -804,14 +850,9 @@ hipError_t launch_linear_backward_batched(const LinearDesc* d, const uint16_t* c
     if (!any_dx)  // dw only: the dw blocks alone (the token count does not matter)
         return chunk_launch<1>(bt, s);
     if (M > kBwdMaxMT && mma_backward_enabled()) {
-        // dw_weak: the dw blocks alone, once; dx: 16 tokens per pass on the matrix cores
-        BwdBatch w = bt;
-        bool any_dw = false;
-        for (int l = 0; l < count; l++) {
-            w.L[l].dx_blocks = 0;
-            any_dw = any_dw || w.L[l].dw_blocks > 0;
-        }
-        hipError_t e = any_dw ? chunk_launch<1>(w, s) : hipSuccess;
+        // dx: 16 tokens per pass on the matrix cores; dw_weak: blocks of the
+        // first pass's launch (they read every token, from dy at token 0)
+        hipError_t e = hipSuccess;
         for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += 16) {
             BwdBatch c = bt;
             for (int l = 0; l < count; l++) {
@@ -828,7 +869,8 @@ hipError_t launch_linear_backward_batched(const LinearDesc* d, const uint16_t* c
                 a.F = dx[l] ? reinterpret_cast<float*>(base + p[l].m_off_f) : nullptr;
                 a.dx_blocks = dx[l] ? a.slices * a.tiles : 0;
                 a.weak_blocks = (dx[l] && d[l].k > 0) ? a.slices * ((d[l].k + 15) / 16) : 0;
-                a.dw_blocks = 0;
+                if (m0 > 0)
+                    a.dw_blocks = 0;
             }
             e = mma_chunk_launch(c, s);
         }

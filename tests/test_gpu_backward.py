@@ -127,3 +127,29 @@ def test_batched_equals_per_layer(owq, M):
             rdx, rdxb, rdw, rdwb = oracle.linear_backward(oracle.pack(W, idx), x, dy)
             check_linear(host(dxs[li]), rdx, rdxb, f"batched dx [{li}] M={M}")
             check_linear(host(dws[li]), rdw, rdwb, f"batched dw [{li}] M={M}")
+
+
+@pytest.mark.parametrize("M", [9, 16, 33])
+def test_vector_form_above_four_tokens(owq, M, monkeypatch):
+    """Above 4 tokens dx runs on the matrix cores; OWQ_BACKWARD=vector keeps the
+    vector form (4 tokens per pass). Both meet the bound on every element."""
+    import torch
+
+    import oracle
+    rng = np.random.default_rng(M)
+    N, K, k = 300, 4128, 17
+    W = synth.random_layer(rng, N, K, 0.02)
+    idx = np.sort(rng.choice(K, k, replace=False)).astype(np.int32)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    dy = rng.standard_normal((M, N)).astype(np.float16)
+    p = owq.pack(dev(W), dev(idx))
+    print(f"vector/matrix forms: N={N} K={K} k={k} M={M}", flush=True)
+    dx_m, dw_m = owq.linear_backward(p, dev(x), dev(dy))
+    monkeypatch.setenv("OWQ_BACKWARD", "vector")
+    dx_v, dw_v = owq.linear_backward(p, dev(x), dev(dy))
+    torch.cuda.synchronize()
+    rdx, rdxb, rdw, rdwb = oracle.linear_backward(oracle.pack(W, idx), x, dy)
+    check_linear(host(dx_m), rdx, rdxb, f"matrix-core dx M={M}")
+    check_linear(host(dx_v), rdx, rdxb, f"vector dx M={M}")
+    assert host(dw_m).tobytes() == host(dw_v).tobytes()
+    check_linear(host(dw_m), rdw, rdwb, f"dw M={M}")
