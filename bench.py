@@ -3,7 +3,7 @@
 One step = one pass of every hot-path stage over one LLaMA-7B decoder layer
 (q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008; k = 32 / 32 / 86 weak
 columns, ~3.1 bits per weight), on seeded synthetic inputs:
-  1. calibration: owq_calibrate_score on T = 2048 tokens for each of the 7
+  1. calibration: owq_calibrate_score_batched on T = 2048 tokens over the 7
      linears, owq_select_weak_batched for the 7, owq_pack for each;
   2. decode: owq_linear_batched over the 7 linears at M = 1 (one launch per
      layer), for R = 8 distinct packed layers in a row, as a token passes
@@ -290,25 +290,25 @@ def main():
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    # events of the calibration phase: ev[li] before calibrating linear li, ev[L]
-    # after the last, ev[L + 1] after the selection (one batched call for the 7),
-    # ev[L + 2 + li] after packing linear li
+    ws_cal = torch.empty(owq.calibrate_batched_workspace_bytes([(s.N, s.K, cfg.T) for s in specs]),
+                         dtype=torch.uint8, device=dev)
+
+    # events of the calibration phase: ev[0] before calibrating the 7 linears
+    # (one batched call), ev[1] after it, ev[2] after the selection (one batched
+    # call for the 7), ev[3 + li] after packing linear li
     def calibrate_pack(slot, ev=None):
-        scores = []
-        for li, s in enumerate(specs):
-            if ev is not None:
-                ev[li].record()
-            _, score = owq.calibrate(W[li], X[li], workspace=ws)
-            scores.append(score)
         if ev is not None:
-            ev[L].record()
+            ev[0].record()
+        scores = [sc for _, sc in owq.calibrate_batched(W, X, workspace=ws_cal)]
+        if ev is not None:
+            ev[1].record()
         idxs = owq.select_weak_batched(scores, [s.k for s in specs], outs=[slot[li]["weak_idx"] for li in range(L)])
         if ev is not None:
-            ev[L + 1].record()
+            ev[2].record()
         for li, s in enumerate(specs):
             owq.pack(W[li], idxs[li], out=slot[li])
             if ev is not None:
-                ev[L + 2 + li].record()
+                ev[3 + li].record()
 
     # fill every rotation slot before timing
     for r in range(ROTATE):
@@ -319,7 +319,7 @@ def main():
     # packed copies are rewritten in place, so the pointers stay valid)
     dec_calls = [owq.PreparedBatched(slots[r], xd, yd) for r in range(ROTATE)]
     decode_bytes = sum(eff_bytes(s.N, s.K, s.k, 1) for s in specs)
-    CE = 2 * L + 2  # calibration-phase events
+    CE = L + 3  # calibration-phase events
     NE = CE + 2 + L + 1  # calibration phase, decode pair, prefill boundaries
 
     def step(i, ev):
@@ -354,9 +354,9 @@ def main():
     def mean_ms(a, b):
         return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
 
-    cal_s = [mean_ms(li, li + 1) / 1e3 for li in range(L)]
-    sel_s = [mean_ms(L, L + 1) / 1e3]
-    pak_s = [mean_ms(L + 1 + li, L + 2 + li) / 1e3 for li in range(L)]
+    cal_s = [mean_ms(0, 1) / 1e3]
+    sel_s = [mean_ms(1, 2) / 1e3]
+    pak_s = [mean_ms(2 + li, 3 + li) / 1e3 for li in range(L)]
     o = CE
     dec_s = mean_ms(o, o + 1) / 1e3 / ROTATE
     dec_min_s = min(e[o].elapsed_time(e[o + 1]) for e in evs) / 1e3 / ROTATE
@@ -404,7 +404,9 @@ def main():
                         "bound": "mfma", "achieved": round(pre_tflops, 1), "peak": MFMA_FP16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
                         "algorithmic_flops": pre_flops, "per_linear": per_linear_prefill},
-            "calibrate_score": hbm_entry(cal_bytes, sum(cal_s), "k_calib_first + k_colsum_err + k_finalize, 7 linears"),
+            "calibrate_score": hbm_entry(cal_bytes, sum(cal_s), "k_calib_stage, the 7 linears in one "
+                                         "owq_calibrate_score_batched call (9 launches: launch s holds the first "
+                                         "pass of linear s, the error pass of s - 1, the final sums of s - 2)"),
             "select_weak": {"what": "k_topk_reg_batched, the 7 linears in one owq_select_weak_batched call (one "
                                     "launch per block shape: K = 4096 and K = 11008)",
                             "us": round(sum(sel_s) * 1e6, 1), "bound": "latency"},
@@ -436,6 +438,19 @@ def main():
         result["decode_batch_sweep"] = sweep
 
     if not args.no_extras:
+        # the layer's calibration as one owq_calibrate_score call per linear (3
+        # launches each), for comparison with the batched call timed above
+        reps = 5
+        evc = [(E(), E()) for _ in range(reps)]
+        for r in range(reps):
+            evc[r][0].record()
+            for li in range(L):
+                owq.calibrate(W[li], X[li], workspace=ws)
+            evc[r][1].record()
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(b) for a, b in evc])) / 1e3
+        result["kernels"]["calibrate_score"]["us_one_call_per_linear"] = round(t * 1e6, 2)
+
         # the same decode as 7 launches per layer (one per linear), recorded in a HIP graph
         print("bench: decode as per-linear launches in a graph", file=sys.stderr, flush=True)
         side = torch.cuda.Stream()
@@ -590,7 +605,8 @@ def main():
             t = float(np.median([a.elapsed_time(b) for a, b, _ in evl])) / 1e3
             ts = float(np.median([b.elapsed_time(c) for _, b, c in evl])) / 1e3
             key = f"{s.name} {s.N}x{s.K} T={c4.T}"
-            long_cal[key] = hbm_entry(calib_bytes(s.N, s.K, c4.T), t, "k_calib_first + k_colsum_err + k_finalize")
+            long_cal[key] = hbm_entry(calib_bytes(s.N, s.K, c4.T), t, "owq_calibrate_score: k_calib_stage, 3 "
+                                                                       "launches (first, error, final pass)")
             long_sel[key] = {"what": f"top-{s.k} of K = {s.K}", "us": round(ts * 1e6, 2), "bound": "latency"}
             del Wl, Xl, wsl
         result["kernels"]["calibrate_score_long"] = long_cal

@@ -123,6 +123,35 @@ owq_status owq_calibrate_score_noalloc(const uint16_t* W, int64_t N, int64_t K,
 /* Bytes of the library-held workspace owq_calibrate_score_noalloc uses. */
 size_t owq_calibrate_noalloc_max_workspace(void);
 
+/* One linear of owq_calibrate_score_batched: its arguments as
+ * owq_calibrate_score's (device pointers; lambda and score are outputs). */
+typedef struct owq_calib_item {
+    const uint16_t* W;  /* fp16 [N][K] */
+    int64_t N, K;
+    const uint16_t* X;  /* fp16 [T][K] */
+    int64_t T;
+    double* lambda;     /* fp64 [K] */
+    double* score;      /* fp64 [K] */
+} owq_calib_item;
+
+/* Bytes of device workspace owq_calibrate_score_batched needs for these
+ * items: their owq_calibrate_workspace_bytes, each rounded up to 256 bytes (0
+ * for invalid sizes or count outside 1..64). */
+size_t owq_calibrate_batched_workspace_bytes(const owq_calib_item* items, int32_t count);
+
+/* owq_calibrate_score for `count` linears (e.g. the 7 of a decoder layer), bit
+ * for bit the same results, in count + 2 kernel launches instead of 3 per
+ * linear: launch s holds the first pass of linear s (X column sums, W row
+ * fits), the error pass of linear s - 1 (which re-reads a W the previous launch
+ * just streamed) and the final pass of linear s - 2 ([PL] "Weak-column
+ * selection" (paper p.4), as owq_calibrate_score). items: HOST array [count].
+ * workspace: >= owq_calibrate_batched_workspace_bytes(items, count) bytes,
+ * 256-byte aligned; item l's part starts at the sum of the earlier items'
+ * rounded sizes. Returns OWQ_ERR_UNSUPPORTED unless 1 <= count <= 64; other
+ * errors as owq_calibrate_score, reported with the item's index. */
+owq_status owq_calibrate_score_batched(const owq_calib_item* items, int32_t count, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 /* Weak-column selection: the k columns of largest score (ties: the lower column
  * index wins), written to weak_idx[0..k) in strictly ascending order ([PL]
  * "Weak-column selection" (paper p.4): the top-k columns by sensitivity are kept

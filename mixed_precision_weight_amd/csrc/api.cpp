@@ -189,6 +189,56 @@ owq_status owq_calibrate_score(const uint16_t* W, int64_t N, int64_t K, const ui
                       "owq_calibrate_score launch");
 }
 
+size_t owq_calibrate_batched_workspace_bytes(const owq_calib_item* items, int32_t count)
+{
+    if (!items || count < 1 || count > 64)
+        return 0;
+    size_t total = 0;
+    for (int32_t l = 0; l < count; l++) {
+        const size_t b = owq_calibrate_workspace_bytes(items[l].N, items[l].K, items[l].T);
+        if (b == 0)
+            return 0;
+        total += (b + 255) & ~(size_t)255;
+    }
+    return total;
+}
+
+owq_status owq_calibrate_score_batched(const owq_calib_item* items, int32_t count, void* workspace,
+                                       size_t workspace_bytes, void* stream)
+{
+    if (!items || !workspace)
+        return fail(OWQ_ERR_NULL, "items and workspace must be non-NULL");
+    if (count < 1 || count > 64)
+        return fail(OWQ_ERR_UNSUPPORTED, "count = %d: need 1 <= count <= 64", count);
+    if (!aligned(workspace, 256))
+        return fail(OWQ_ERR_ALIGN, "misaligned workspace (256 B)");
+    std::vector<owq::CalibItem> it((size_t)count);
+    std::vector<owq::CalibPlan> plans((size_t)count);
+    std::vector<void*> ws((size_t)count);
+    size_t off = 0;
+    for (int32_t l = 0; l < count; l++) {
+        const owq_calib_item& c = items[l];
+        if (!c.W || !c.X || !c.lambda || !c.score)
+            return fail(OWQ_ERR_NULL, "item %d: W, X, lambda and score must be non-NULL", l);
+        if (c.N < 1 || c.N > INT32_MAX || c.T < 1)
+            return fail(OWQ_ERR_SHAPE, "item %d: N = %lld, T = %lld: need N, T >= 1", l, (long long)c.N,
+                        (long long)c.T);
+        owq_status st = check_k_dim(c.K);
+        if (st != OWQ_OK)
+            return fail(st, "item %d: %s", l, g_err);
+        if (!aligned(c.W, 16) || !aligned(c.X, 16) || !aligned(c.lambda, 8) || !aligned(c.score, 8))
+            return fail(OWQ_ERR_ALIGN, "item %d: misaligned pointer (W, X: 16 B, lambda/score: 8 B)", l);
+        it[l] = owq::CalibItem{c.W, c.N, c.K, c.X, c.T, c.lambda, c.score};
+        plans[l] = owq::calib_plan(c.N, c.K, c.T);
+        ws[l] = static_cast<char*>(workspace) + off;
+        off += (plans[l].total + 255) & ~(size_t)255;
+    }
+    if (workspace_bytes < off)
+        return fail(OWQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, off);
+    return hip_status(owq::launch_calibrate_batched(it.data(), count, ws.data(), plans.data(), (hipStream_t)stream),
+                      "owq_calibrate_score_batched launch");
+}
+
 owq_status owq_calibrate_score_noalloc(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,
                                        double* lambda, double* score, void* stream)
 {

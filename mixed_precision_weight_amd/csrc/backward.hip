@@ -269,7 +269,7 @@ __device__ __forceinline__ void bwd_dense(const BwdArgs& a, int tile, int s, flo
             const int j = ids[c];
 #pragma unroll
             for (int m = 0; m < MT; m++)
-                atomicAddNoRet(a.P + ((int64_t)s * MT + m) * a.K + j, wacc[m]);
+                (void)unsafeAtomicAdd(a.P + ((int64_t)s * MT + m) * a.K + j, wacc[m]);
         }
         return;
     }
@@ -319,7 +319,7 @@ __device__ __forceinline__ void bwd_dense(const BwdArgs& a, int tile, int s, flo
             const int j = a.idx[cb + tid];
 #pragma unroll
             for (int m = 0; m < MT; m++)
-                atomicAddNoRet(a.P + ((int64_t)s * MT + m) * a.K + j, wacc[m]);
+                (void)unsafeAtomicAdd(a.P + ((int64_t)s * MT + m) * a.K + j, wacc[m]);
         }
     }
 }

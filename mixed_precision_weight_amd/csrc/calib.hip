@@ -11,16 +11,33 @@
 // [PL] = paperlayer.ai page "OWQ: Outlier-Aware Weight Quantization for
 // Efficient Fine-Tuning and Inference of Large Language Models".
 //
-// Both sums are column reductions of an fp16 [R][K] matrix streamed from HBM.
-// Kernel shape (HBM-bound): a 256-thread block owns a 64-column tile of one row
-// slice. Lane (wave w, lane l) reads 8 columns (16 B) at column 8*(l%8) of rows
-// w*8 + l/8 + 32 t, so each wave instruction reads 8 full 128-byte lines. Squares
-// of fp16 values and of the (exact) fp32 RTN errors are accumulated in fp64; the
-// 32 row phases are combined by a fixed butterfly and a fixed-order LDS sum,
-// and row slices by a fixed-order final pass: results are bitwise deterministic.
+// Both sums are column reductions of an fp16 [R][K] matrix streamed from HBM,
+// and e_j needs each row's fit (min and max over the whole row) first.
+//
+// W is read once: a block of the fused form owns whole rows, 8 (or 16) fp16
+// columns per lane in 16-byte words, G rows at a time with the next G rows'
+// loads in flight. Each row's min and max are reduced across the block (DPP
+// within a wave, one LDS exchange and one barrier per G rows), lane g of every
+// wave turns row g's range into (step, zero point), readlane hands them to the
+// whole wave, and every lane adds the squared RTN errors of its own columns to
+// fp64 accumulators that stay in registers across the block's rows: no
+// cross-lane sum, one [K] partial row per block. Rows wider than 4096 words
+// (K > 32768) keep the two-pass form: one wave per row fit, then column tiles
+// of the errors.
+//
+// X: a block owns a 64-column tile of one row slice. Lane (wave w, lane l) reads
+// 8 columns (16 B) at column 8*(l%8) of rows w*8 + l/8 + 8*nwaves*t, so each
+// wave instruction reads 8 full 128-byte lines; squares accumulate in fp64, the
+// 8 row phases of a wave are combined by a fixed butterfly, the waves by a
+// fixed-order LDS sum.
+//
+// A last launch sums the partial rows of every linear in a fixed order: results
+// are bitwise deterministic.
 //
 // Built with -ffp-contract=off: the quantiser steps are single IEEE operations.
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "owq_device.h"
 #include "owq_launch.h"
@@ -36,9 +53,9 @@ namespace owq {
 
 namespace {
 
-constexpr int kTileCols = 64;   // columns per block tile
-constexpr int kPhases = 32;     // row phases per block (4 waves x 8)
-constexpr int kUnroll = 4;      // rows in flight per lane
+constexpr int kTileCols = 64;   // columns per X (or two-pass error) tile
+constexpr int kUnroll = 4;      // rows in flight per lane in a tile
+constexpr int kMaxWaves = 16;   // waves per block
 
 struct SqElem {  // x^2 (exact in fp32 for fp16 x)
     struct Row {};
@@ -51,6 +68,19 @@ struct SqElem {  // x^2 (exact in fp32 for fp16 x)
     static constexpr bool kSquared = true;
 };
 
+// The residual against the (possibly clamped) grid point, exact: every weight
+// lies inside the row's full-row fit range, so |w / s| <= 8 and the product of
+// the offset and the 11-bit step has at most 14 bits. The rounded quotient
+// t = rint(w rs) is rint(w / s) except possibly at an exact half-integer (see
+// rint_quotient), where both neighbours leave |residual| = s / 2, and the clamp
+// to the code range maps an out-of-range neighbour onto the in-range one; the
+// squared residual is therefore the same as with the tie rounded to even.
+__device__ __forceinline__ float rtn_residual(float w, float s, float rs, float lo, float hi)
+{
+    const float q = __builtin_amdgcn_fmed3f(rintf(w * rs), lo, hi);
+    return __builtin_fmaf(-q, s, w);
+}
+
 struct ErrElem {  // dW = w - s (q - z), exact in fp32; squared in fp64 by the caller
     const uint16_t* s16;
     const uint8_t* z;
@@ -58,17 +88,7 @@ struct ErrElem {  // dW = w - s (q - z), exact in fp32; squared in fp64 by the c
     __device__ __forceinline__ Row load_row(int64_t r) const { return make_rtn_row(h2f(s16[r]), z[r]); }
     __device__ __forceinline__ float val(const Row& rw, uint16_t h) const
     {
-        // The residual against the (possibly clamped) grid point, exact: every
-        // weight lies inside the row's full-row fit range, so |w / s| <= 8 and the
-        // product of the offset and the 11-bit step has at most 14 bits. The
-        // rounded quotient t = rint(w rs) is rint(w / s) except possibly at an
-        // exact half-integer (see rint_quotient), where both neighbours leave
-        // |residual| = s / 2, and the clamp to the code range maps an
-        // out-of-range neighbour onto the in-range one; the squared residual is
-        // therefore the same as with the tie rounded to even.
-        const float w = h2f(h);
-        const float q = __builtin_amdgcn_fmed3f(rintf(w * rw.rs), rw.lo, rw.hi);
-        return __builtin_fmaf(-q, rw.s, w);
+        return rtn_residual(h2f(h), rw.s, rw.rs, rw.lo, rw.hi);
     }
     static constexpr bool kSquared = false;
 };
@@ -77,9 +97,11 @@ struct ErrElem {  // dW = w - s (q - z), exact in fp32; squared in fp64 by the c
 template <class Elem>
 __device__ __forceinline__ void colsum_tile(const uint16_t* __restrict__ A, int64_t R, int64_t K,
                                             int64_t rows_per_slice, double* __restrict__ partial, Elem elem,
-                                            int64_t tile, int64_t slice, double (&red)[4][kTileCols])
+                                            int64_t tile, int64_t slice, double (&red)[kMaxWaves][kTileCols])
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int phases = nwaves * 8;
     const int cc = lane & 7;
     const int phase = wave * 8 + (lane >> 3);
     const int64_t col = tile * kTileCols + cc * 8;
@@ -95,18 +117,18 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* __restrict__ A, int6
 
     // every load of an unrolled step is issued before the first use: rows are
     // clamped to the slice instead of branched around
-    for (int64_t rb = r0 + phase; rb < r1; rb += (int64_t)kPhases * kUnroll) {
+    for (int64_t rb = r0 + phase; rb < r1; rb += (int64_t)phases * kUnroll) {
         uint4 v[kUnroll];
         typename Elem::Row rw[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            const int64_t r = min(rb + (int64_t)u * kPhases, r1 - 1);
+            const int64_t r = min(rb + (int64_t)u * phases, r1 - 1);
             v[u] = *reinterpret_cast<const uint4*>(A + r * K + colc);
             rw[u] = elem.load_row(r);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            if (!(active && rb + (int64_t)u * kPhases < r1))
+            if (!(active && rb + (int64_t)u * phases < r1))
                 continue;
             uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
@@ -137,20 +159,20 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* __restrict__ A, int6
         int64_t j = tile * kTileCols + threadIdx.x;
         if (j < K) {
             double t = red[0][threadIdx.x];
-            t += red[1][threadIdx.x];
-            t += red[2][threadIdx.x];
-            t += red[3][threadIdx.x];
+            for (int w = 1; w < nwaves; w++)
+                t += red[w][threadIdx.x];
             partial[slice * K + j] = t;
         }
     }
 }
 
-// One wave per row: min/max over all K columns -> (fp16 step, zero point).
+// Two-pass form: one wave per row, min/max over all K columns -> (fp16 step,
+// zero point).
 __device__ __forceinline__ void rowfit_rows(const uint16_t* __restrict__ W, int64_t N, int64_t K,
                                             uint16_t* __restrict__ s16, uint8_t* __restrict__ z, int64_t blk)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t row = blk * 4 + (threadIdx.x >> 6);
+    const int64_t row = blk * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (row >= N)
         return;
     const uint4* p = reinterpret_cast<const uint4*>(W + row * K);
@@ -184,60 +206,313 @@ __device__ __forceinline__ void rowfit_rows(const uint16_t* __restrict__ W, int6
     }
 }
 
-// First launch: the X column sums (lambda partials) and the W row fits run as
-// one grid, tile-major X blocks first.
-__global__ __launch_bounds__(256) void k_calib_first(const uint16_t* __restrict__ X, int64_t T, int64_t K,
-                                                     int64_t rows_x, double* __restrict__ px, int64_t tiles,
-                                                     int64_t nx, const uint16_t* __restrict__ W, int64_t N,
-                                                     uint16_t* __restrict__ s16, uint8_t* __restrict__ z)
+// round(w s) for the fp16 in the low (HI = 0) or high (HI = 1) half of h2 and
+// an fp32 s: one v_fma_mix_f32 with a zero addend (the exact product rounded
+// once, as the fp32 product of the widened value; only a zero's sign may
+// differ, which no caller looks at)
+template <int HI>
+__device__ __forceinline__ float mul_h(uint32_t h2, float s)
 {
-    __shared__ double red[4][kTileCols];
-    const int64_t b = blockIdx.x;
-    if (b < nx)
-        colsum_tile(X, T, K, rows_x, px, SqElem{}, b % tiles, b / tiles, red);
+    float r;
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(s));
     else
-        rowfit_rows(W, N, K, s16, z, b - nx);
+        asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(s));
+    return r;
 }
 
-// Second launch: the RTN-error column sums over (tile, slice) blocks.
-__global__ __launch_bounds__(256) void k_colsum_err(const uint16_t* __restrict__ W, int64_t N, int64_t K,
-                                                    int64_t rows_w, double* __restrict__ pw, ErrElem elem)
+__device__ __forceinline__ uint32_t h2max(uint32_t a, uint32_t b)
 {
-    __shared__ double red[4][kTileCols];
-    colsum_tile(W, N, K, rows_w, pw, elem, blockIdx.x, blockIdx.y, red);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(__builtin_bit_cast(half2_t, a),
+                                                                      __builtin_bit_cast(half2_t, b)));
 }
 
-// Third launch: lambda_j = 2 sum_s px[s][j], e_j = sum_s pw[s][j] (slices in
-// order), score_j = lambda_j e_j. A separate launch: the slice partials come
-// from blocks on all eight XCDs, whose L2 caches a device-wide fence would have
-// to write back and invalidate.
-__global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ px, int64_t sx,
-                                                  const double* __restrict__ pw, int64_t sw, int64_t K,
-                                                  double* __restrict__ lambda, double* __restrict__ score)
+// DPP move: every lane has a source (quad permutes, row rotations)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_all(uint32_t v)
 {
-    int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= K)
-        return;
-    double l = 0.0;
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+
+// DPP move into the rows of ROWS only; the other lanes keep their own value
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_rows(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xf, false);
+}
+
+// Both halves' maxima over the wave's 64 lanes (exact), as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_h2max(uint32_t v)
+{
+    v = h2max(v, dpp_all<0xb1>(v));          // quad_perm [1,0,3,2]
+    v = h2max(v, dpp_all<0x4e>(v));          // quad_perm [2,3,0,1]
+    v = h2max(v, dpp_all<0x124>(v));         // row_ror:4
+    v = h2max(v, dpp_all<0x128>(v));         // row_ror:8
+    v = h2max(v, dpp_rows<0x142, 0xa>(v));   // row_bcast:15 into rows 1, 3
+    v = h2max(v, dpp_rows<0x143, 0xc>(v));   // row_bcast:31 into rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Fused form: rows [r0, r1) of W, every column; part = this block's [K] row of
+// column error sums, in row order. Lane slot u holds the 16-byte word
+// tid + blockDim.x u of a row. Loads go through a buffer resource over the
+// block's rows: slots past the row and rows past the block (also the
+// prefetch's tail) are read out of range, which returns zeros and fetches
+// nothing; a zero changes no min or max (the fit range contains 0), and those
+// slots and rows are never accumulated or stored. A row's range travels as the
+// fp16 pair (-min, max), reduced with one packed max.
+template <int WPL, int G>
+__device__ __forceinline__ void fit_err_rows(const uint16_t* __restrict__ W, int64_t K, int64_t r0, int64_t r1,
+                                             double* __restrict__ part, uint32_t (&mm)[2][G][kMaxWaves])
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int64_t nw = K >> 3;
+    constexpr uint32_t kDead = 0x40000000u;
+    uint32_t off[WPL];  // byte offset of the lane's word in a row, or out of range
+    bool act[WPL];
+#pragma unroll
+    for (int u = 0; u < WPL; u++) {
+        const int64_t wd = tid + (int64_t)blockDim.x * u;
+        act[u] = wd < nw;
+        off[u] = act[u] ? 16u * (uint32_t)wd : kDead;
+    }
+    const uint32_t row_bytes = (uint32_t)(2 * K);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(W + r0 * K), (short)0, (int)((r1 - r0) * row_bytes), 0x00020000);
+    double acc[WPL][8];
+#pragma unroll
+    for (int u = 0; u < WPL; u++)
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+            acc[u][c] = 0.0;
+
+    typedef uint4 Rows[G][WPL];
+    auto load = [&](Rows& d, int64_t rb) {
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            const uint32_t ro = (uint32_t)(rb + g - r0) * row_bytes;  // past r1: out of range
+#pragma unroll
+            for (int u = 0; u < WPL; u++)
+                d[g][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, ro + off[u], 0, 0));
+        }
+    };
+    // rows rb .. rb + G - 1 held in v; the next G rows' loads go to vn first
+    auto step = [&](int64_t rb, const Rows& v, Rows& vn, int buf) {
+        load(vn, rb + G);
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            uint32_t nmn = 0, mx = 0;  // (min, max) pairs of the lane's columns, from 0
+#pragma unroll
+            for (int u = 0; u < WPL; u++) {
+                const half2_t a = __builtin_bit_cast(half2_t, v[g][u].x), b = __builtin_bit_cast(half2_t, v[g][u].y);
+                const half2_t c = __builtin_bit_cast(half2_t, v[g][u].z), d = __builtin_bit_cast(half2_t, v[g][u].w);
+                half2_t m0 = __builtin_bit_cast(half2_t, nmn), m1 = __builtin_bit_cast(half2_t, mx);
+                m0 = __builtin_elementwise_minimum(__builtin_elementwise_minimum(m0, a), b);
+                m0 = __builtin_elementwise_minimum(__builtin_elementwise_minimum(m0, c), d);
+                m1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m1, a), b);
+                m1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m1, c), d);
+                nmn = __builtin_bit_cast(uint32_t, m0);
+                mx = __builtin_bit_cast(uint32_t, m1);
+            }
+            const half2_t m0 = __builtin_bit_cast(half2_t, nmn), m1 = __builtin_bit_cast(half2_t, mx);
+            const half2_t pr = {(_Float16)(-__builtin_elementwise_minimum(m0[0], m0[1])),
+                                __builtin_elementwise_maximum(m1[0], m1[1])};
+            const uint32_t r = wave_h2max(__builtin_bit_cast(uint32_t, pr));
+            if (lane == 0)
+                mm[buf][g][wave] = r;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // lane g of every wave fits row g
+        float fs = 1.0f, frs = 1.0f, flo = 0.0f, fhi = 0.0f;
+        if (lane < G) {
+            uint32_t m = 0;
+            for (int w = 0; w < nwaves; w++)
+                m = h2max(m, mm[buf][lane][w]);
+            const half2_t h = __builtin_bit_cast(half2_t, m);
+            uint16_t s16;
+            int z;
+            qparams_from_range(-(float)h[0], (float)h[1], s16, z);
+            const RtnRow rr = make_rtn_row(h2f(s16), z);
+            fs = rr.s;
+            frs = rr.rs;
+            flo = rr.lo;
+            fhi = rr.hi;
+        }
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            if (rb + g >= r1)  // block-uniform
+                break;
+            const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), g));
+            const float rs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, frs), g));
+            const float qlo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, flo), g));
+            const float qhi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fhi), g));
+#pragma unroll
+            for (int u = 0; u < WPL; u++) {
+                const uint32_t w4[4] = {v[g][u].x, v[g][u].y, v[g][u].z, v[g][u].w};
+#pragma unroll
+                for (int c = 0; c < 8; c++) {
+                    const uint32_t h2 = w4[c >> 1];
+                    const float t = (c & 1) ? mul_h<1>(h2, rs) : mul_h<0>(h2, rs);
+                    const float q = __builtin_amdgcn_fmed3f(rintf(t), qlo, qhi);
+                    const float e = __builtin_fmaf(-q, s, h2f((uint16_t)(h2 >> (16 * (c & 1)))));
+                    acc[u][c] = __builtin_fma((double)e, (double)e, acc[u][c]);
+                }
+            }
+        }
+    };
+    Rows va, vb;
+    load(va, r0);
+    for (int64_t rb = r0; rb < r1; rb += 2 * G) {  // the two row buffers take turns
+        step(rb, va, vb, 0);
+        if (rb + G >= r1)
+            break;
+        step(rb + G, vb, va, 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's out-of-range loads
+#pragma unroll
+    for (int u = 0; u < WPL; u++) {
+        if (!act[u])
+            continue;
+        double2* p = reinterpret_cast<double2*>(part + off[u] / 2);
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+            p[c] = make_double2(acc[u][2 * c], acc[u][2 * c + 1]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One launch holds up to kCalibMaxLayers linears: blocks [wb[l], wb[l+1]) are
+// linear l's W blocks, then, after every W block, [xb[l], xb[l+1]) its X
+// blocks (the long W blocks start first).
+constexpr int kCalibMaxLayers = 16;
+
+struct CalibLayer {
+    const uint16_t* W;
+    const uint16_t* X;
+    double* px;
+    double* pw;
+    uint16_t* s16;
+    uint8_t* z;
+    double* lambda;
+    double* score;
+    int64_t N, K, T, rows_x, rows_w, sx, sw, tiles;
+};
+
+struct CalibLaunch {
+    CalibLayer L[kCalibMaxLayers];
+    int32_t wb[kCalibMaxLayers + 1];
+    int32_t xb[kCalibMaxLayers + 1];
+    int32_t count;
+};
+
+__device__ __forceinline__ int layer_of(const int32_t* b0, int count, int64_t b)
+{
+    int l = 0;
+    while (l + 1 < count && b >= b0[l + 1])
+        l++;
+    return l;
+}
+
+// X column tiles of the blocks after the W blocks
+__device__ __forceinline__ void x_blocks(const CalibLaunch& c, int64_t b, double (&red)[kMaxWaves][kTileCols])
+{
+    b -= c.wb[c.count];
+    const int l = layer_of(c.xb, c.count, b);
+    const CalibLayer& L = c.L[l];
+    b -= c.xb[l];
+    colsum_tile(L.X, L.T, L.K, L.rows_x, L.px, SqElem{}, b % L.tiles, b / L.tiles, red);
+}
+
+template <int WPL, int G>
+__global__ __launch_bounds__(1024) void k_calib_fused(const CalibLaunch c)
+{
+    __shared__ double red[kMaxWaves][kTileCols];
+    __shared__ uint32_t mm[2][G][kMaxWaves];
+    const int64_t b = blockIdx.x;
+    if (b < c.wb[c.count]) {
+        const int l = layer_of(c.wb, c.count, b);
+        const CalibLayer& L = c.L[l];
+        const int64_t blk = b - c.wb[l];
+        const int64_t r0 = blk * L.rows_w;
+        fit_err_rows<WPL, G>(L.W, L.K, r0, min(L.N, r0 + L.rows_w), L.pw + blk * L.K, mm);
+    } else {
+        x_blocks(c, b, red);
+    }
+}
+
+// two-pass form, first launch: row fits (one wave per row), X tiles
+__global__ __launch_bounds__(256) void k_calib_fit(const CalibLaunch c)
+{
+    __shared__ double red[kMaxWaves][kTileCols];
+    const int64_t b = blockIdx.x;
+    if (b < c.wb[c.count]) {
+        const int l = layer_of(c.wb, c.count, b);
+        const CalibLayer& L = c.L[l];
+        rowfit_rows(L.W, L.N, L.K, L.s16, L.z, b - c.wb[l]);
+    } else {
+        x_blocks(c, b, red);
+    }
+}
+
+// two-pass form, second launch: column tiles of the RTN errors
+__global__ __launch_bounds__(256) void k_calib_err(const CalibLaunch c)
+{
+    __shared__ double red[kMaxWaves][kTileCols];
+    int64_t b = blockIdx.x;
+    const int l = layer_of(c.wb, c.count, b);
+    const CalibLayer& L = c.L[l];
+    b -= c.wb[l];
+    colsum_tile(L.W, L.N, L.K, L.rows_w, L.pw, ErrElem{L.s16, L.z}, b % L.tiles, b / L.tiles, red);
+}
+
+// lambda_j = 2 sum_s px[s][j], e_j = sum_s pw[s][j], score_j = lambda_j e_j.
+// A block of 16 waves owns 64 columns; wave w sums the slices s = w (mod 16)
+// in order, then the 16 wave sums are added in wave order.
+__global__ __launch_bounds__(1024) void k_calib_fin(const CalibLaunch c)
+{
+    __shared__ double red[2][kMaxWaves][64];
+    int64_t b = blockIdx.x;
+    const int l = layer_of(c.wb, c.count, b);
+    const CalibLayer& L = c.L[l];
+    b -= c.wb[l];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t j = b * 64 + lane;
+    const int64_t jc = j < L.K ? j : L.K - 1;
+    double sx = 0.0, sw = 0.0;
+#pragma unroll 4
+    for (int64_t s = wave; s < L.sx; s += kMaxWaves)
+        sx += L.px[s * L.K + jc];
 #pragma unroll 8
-    for (int64_t s = 0; s < sx; s++)
-        l += px[s * K + j];
-    l *= 2.0;
-    double e = 0.0;
-#pragma unroll 8
-    for (int64_t s = 0; s < sw; s++)
-        e += pw[s * K + j];
-    lambda[j] = l;
-    score[j] = l * e;
+    for (int64_t s = wave; s < L.sw; s += kMaxWaves)
+        sw += L.pw[s * L.K + jc];
+    red[0][wave][lane] = sx;
+    red[1][wave][lane] = sw;
+    __syncthreads();
+    if (threadIdx.x < 64 && j < L.K) {
+        double lam = red[0][0][lane], e = red[1][0][lane];
+        for (int w = 1; w < kMaxWaves; w++) {
+            lam += red[0][w][lane];
+            e += red[1][w][lane];
+        }
+        lam *= 2.0;
+        L.lambda[j] = lam;
+        L.score[j] = lam * e;
+    }
 }
 
-int64_t choose_slices(int64_t R, int64_t K)
+// Rows per fused W block: one [K] fp64 partial row per block costs 4 / kFusedRows
+// of W's bytes (12.5 % at 32), and a block streams kFusedRows rows.
+constexpr int64_t kFusedRows = 32;
+// fused form with 2 words per lane up to this many words per row (K = 8 x), 4 above
+constexpr int64_t kWpl2Words = 1024;
+// rows of X per tile block
+constexpr int64_t kTileRows = 512;
+
+// Row slices of a tile-form sum over R rows: kTileRows rows per block at most
+int64_t choose_slices(int64_t R)
 {
-    int64_t tiles = (K + kTileCols - 1) / kTileCols;
-    int64_t s = (1024 + tiles - 1) / tiles;           // ~1024 blocks in flight
-    int64_t cap = (R + 2 * kPhases - 1) / (2 * kPhases);  // >= 2 rows per phase
-    if (s > cap)
-        s = cap;
+    int64_t s = (R + kTileRows - 1) / kTileRows;
     if (s > 65535)
         s = 65535;
     return s < 1 ? 1 : s;
@@ -250,19 +525,37 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 CalibPlan calib_plan(int64_t N, int64_t K, int64_t T)
 {
     CalibPlan p;
-    p.sx = choose_slices(T, K);
-    p.sw = choose_slices(N, K);
+    const int64_t nw = K / 8;
+    if (nw <= kWpl2Words) {
+        p.wpl = 2;
+        p.nwaves = (int32_t)((nw + 127) / 128);
+    } else if (nw <= 4096) {  // K <= 32768
+        p.wpl = 4;
+        p.nwaves = (int32_t)((nw + 255) / 256);
+    } else {  // two-pass form
+        p.wpl = 0;
+        p.nwaves = 4;
+    }
+    p.sx = choose_slices(T);
     p.rows_x = (T + p.sx - 1) / p.sx;
-    p.rows_w = (N + p.sw - 1) / p.sw;
+    if (p.wpl) {
+        p.rows_w = kFusedRows;
+        p.sw = (N + kFusedRows - 1) / kFusedRows;
+    } else {
+        p.sw = choose_slices(N);
+        p.rows_w = (N + p.sw - 1) / p.sw;
+    }
     size_t o = 0;
     p.off_px = o;
     o = align256(o + (size_t)p.sx * K * sizeof(double));
     p.off_pw = o;
     o = align256(o + (size_t)p.sw * K * sizeof(double));
     p.off_s16 = o;
-    o = align256(o + (size_t)N * sizeof(uint16_t));
+    if (!p.wpl)
+        o = align256(o + (size_t)N * sizeof(uint16_t));
     p.off_z = o;
-    o = align256(o + (size_t)N);
+    if (!p.wpl)
+        o = align256(o + (size_t)N);
     p.total = o;
     return p;
 }
@@ -292,26 +585,91 @@ hipError_t calib_scratch(void** ptr)
     return hipSuccess;
 }
 
+hipError_t launch_calibrate_batched(const CalibItem* items, int count, void* const* ws, const CalibPlan* plans,
+                                   hipStream_t s)
+{
+    auto layer = [&](int l) {
+        CalibLayer L;
+        const CalibItem& it = items[l];
+        const CalibPlan& p = plans[l];
+        char* base = static_cast<char*>(ws[l]);
+        L.W = it.W;
+        L.X = it.X;
+        L.px = reinterpret_cast<double*>(base + p.off_px);
+        L.pw = reinterpret_cast<double*>(base + p.off_pw);
+        L.s16 = reinterpret_cast<uint16_t*>(base + p.off_s16);
+        L.z = reinterpret_cast<uint8_t*>(base + p.off_z);
+        L.lambda = it.lambda;
+        L.score = it.score;
+        L.N = it.N;
+        L.K = it.K;
+        L.T = it.T;
+        L.rows_x = p.rows_x;
+        L.rows_w = p.rows_w;
+        L.sx = p.sx;
+        L.sw = p.sw;
+        L.tiles = (it.K + kTileCols - 1) / kTileCols;
+        return L;
+    };
+    // w_blocks(l) / x_blocks(l): the blocks of linear l in one launch
+    auto run = [&](const int* ids, int n, auto kernel, int threads, auto w_blocks, auto x_blocks) {
+        CalibLaunch c{};
+        c.count = n;
+        c.wb[0] = 0;
+        for (int i = 0; i < n; i++) {
+            c.L[i] = layer(ids[i]);
+            c.wb[i + 1] = c.wb[i] + (int32_t)w_blocks(c.L[i]);
+        }
+        c.xb[0] = 0;
+        for (int i = 0; i < n; i++)
+            c.xb[i + 1] = c.xb[i] + (int32_t)x_blocks(c.L[i]);
+        const int64_t nb = (int64_t)c.wb[n] + c.xb[n];
+        if (nb > 0)
+            hipLaunchKernelGGL(kernel, dim3((unsigned)nb), dim3(threads), 0, s, c);
+    };
+    auto none = [](const CalibLayer&) { return (int64_t)0; };
+    auto xtiles = [](const CalibLayer& L) { return L.tiles * L.sx; };
+    // linears of one block shape share a launch, kCalibMaxLayers at a time
+    std::vector<char> done((size_t)count, 0);
+    for (int l0 = 0; l0 < count; l0++) {
+        if (done[l0])
+            continue;
+        std::vector<int> ids;
+        for (int l = l0; l < count; l++)
+            if (!done[l] && plans[l].wpl == plans[l0].wpl && plans[l].nwaves == plans[l0].nwaves) {
+                ids.push_back(l);
+                done[l] = 1;
+            }
+        const int wpl = plans[l0].wpl, threads = 64 * plans[l0].nwaves;
+        for (size_t i = 0; i < ids.size(); i += kCalibMaxLayers) {
+            const int n = (int)std::min(ids.size() - i, (size_t)kCalibMaxLayers);
+            const int* p = ids.data() + i;
+            auto fused = [](const CalibLayer& L) { return L.sw; };
+            if (wpl == 2) {
+                run(p, n, k_calib_fused<2, 2>, threads, fused, xtiles);
+            } else if (wpl == 4) {
+                run(p, n, k_calib_fused<4, 1>, threads, fused, xtiles);
+            } else {
+                run(p, n, k_calib_fit, 256, [](const CalibLayer& L) { return (L.N + 3) / 4; }, xtiles);
+                run(p, n, k_calib_err, 256, [](const CalibLayer& L) { return L.tiles * L.sw; }, none);
+            }
+        }
+    }
+    std::vector<int> all((size_t)count);
+    for (int l = 0; l < count; l++)
+        all[l] = l;
+    for (int i = 0; i < count; i += kCalibMaxLayers)
+        run(all.data() + i, std::min(count - i, kCalibMaxLayers), k_calib_fin, 1024,
+            [](const CalibLayer& L) { return (L.K + 63) / 64; }, none);
+    return hipGetLastError();
+}
+
 hipError_t launch_calibrate(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,
                             double* lambda, double* score, void* ws, const CalibPlan& p,
                             hipStream_t s)
 {
-    char* base = static_cast<char*>(ws);
-    double* px = reinterpret_cast<double*>(base + p.off_px);
-    double* pw = reinterpret_cast<double*>(base + p.off_pw);
-    uint16_t* s16 = reinterpret_cast<uint16_t*>(base + p.off_s16);
-    uint8_t* z = reinterpret_cast<uint8_t*>(base + p.off_z);
-    const unsigned tiles = (unsigned)((K + kTileCols - 1) / kTileCols);
-
-    const int64_t nx = (int64_t)tiles * p.sx;
-    const int64_t nrow = (N + 3) / 4;
-    hipLaunchKernelGGL(k_calib_first, dim3((unsigned)(nx + nrow)), dim3(256), 0, s, X, T, K, p.rows_x, px,
-                       (int64_t)tiles, nx, W, N, s16, z);
-    hipLaunchKernelGGL(k_colsum_err, dim3(tiles, (unsigned)p.sw), dim3(256), 0, s, W, N, K, p.rows_w, pw,
-                       ErrElem{s16, z});
-    hipLaunchKernelGGL(k_finalize, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, px, p.sx, pw, p.sw, K,
-                       lambda, score);
-    return hipGetLastError();
+    CalibItem it{W, N, K, X, T, lambda, score};
+    return launch_calibrate_batched(&it, 1, &ws, &p, s);
 }
 
 }  // namespace owq

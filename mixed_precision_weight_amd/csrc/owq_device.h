@@ -142,6 +142,37 @@ __device__ __forceinline__ float wave_sum_dpp(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// The same DPP pattern for min / max: lanes a row mask leaves out keep their own
+// value. Both are exact, so the order of the steps does not matter.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_keep(float v)
+{
+    const int b = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, ROWS, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_min_dpp(float v)
+{
+    v = fminf(v, dpp_keep<0xb1>(v));
+    v = fminf(v, dpp_keep<0x4e>(v));
+    v = fminf(v, dpp_keep<0x124>(v));
+    v = fminf(v, dpp_keep<0x128>(v));
+    v = fminf(v, dpp_keep<0x142, 0xa>(v));
+    v = fminf(v, dpp_keep<0x143, 0xc>(v));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    v = fmaxf(v, dpp_keep<0xb1>(v));
+    v = fmaxf(v, dpp_keep<0x4e>(v));
+    v = fmaxf(v, dpp_keep<0x124>(v));
+    v = fmaxf(v, dpp_keep<0x128>(v));
+    v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+    v = fmaxf(v, dpp_keep<0x143, 0xc>(v));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ __forceinline__ double shfl_xor_f64(double v, int o)
 {
     uint64_t b = __builtin_bit_cast(uint64_t, v);

@@ -9,11 +9,25 @@ namespace owq {
 
 // ---------------------------------------------------------------- calibrate --
 struct CalibPlan {
-    int64_t sx, sw;          // row slices of X and of W
+    int64_t sx, sw;          // row slices of X and of W (W: one per fused block)
     int64_t rows_x, rows_w;  // rows per slice
+    int32_t wpl, nwaves;     // fused W form: 16-byte words per lane and waves per block; wpl 0: two-pass form
     size_t off_px, off_pw, off_s16, off_z, total;  // workspace byte offsets / size
 };
 CalibPlan calib_plan(int64_t N, int64_t K, int64_t T);
+struct CalibItem {
+    const uint16_t* W;
+    int64_t N, K;
+    const uint16_t* X;
+    int64_t T;
+    double* lambda;
+    double* score;
+};
+// `count` calibrations in count + 2 launches (each linear's three passes
+// staggered over three consecutive launches); ws[l]: item l's workspace of plan
+// plans[l].
+hipError_t launch_calibrate_batched(const CalibItem* items, int count, void* const* ws, const CalibPlan* plans,
+                                   hipStream_t s);
 hipError_t launch_calibrate(const uint16_t* W, int64_t N, int64_t K, const uint16_t* X, int64_t T,
                             double* lambda, double* score, void* ws, const CalibPlan& p,
                             hipStream_t s);

@@ -24,6 +24,11 @@ _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 
 
+class OwqCalibItem(ctypes.Structure):
+    """Mirror of ``owq_calib_item`` (host struct, device pointers)."""
+    _fields_ = [("W", _P), ("N", _I64), ("K", _I64), ("X", _P), ("T", _I64), ("lam", _P), ("score", _P)]
+
+
 class OwqLayer(ctypes.Structure):
     """Mirror of ``owq_layer`` (host struct, device pointers)."""
     _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64), ("k", ctypes.c_int32),
@@ -38,6 +43,8 @@ EXPORTS = {
     "owq_calibrate_score": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "owq_calibrate_score_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P]),
     "owq_calibrate_noalloc_max_workspace": (ctypes.c_size_t, []),
+    "owq_calibrate_batched_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(OwqCalibItem), _I32]),
+    "owq_calibrate_score_batched": (ctypes.c_int, [ctypes.POINTER(OwqCalibItem), _I32, _P, ctypes.c_size_t, _P]),
     "owq_select_weak": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
     "owq_select_weak_batched": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_I64), ctypes.POINTER(_I32),
                                                ctypes.POINTER(_P), _I32, _P]),
@@ -192,6 +199,56 @@ def calibrate_noalloc(W: torch.Tensor, X: torch.Tensor, lam: torch.Tensor | None
     _check(lib().owq_calibrate_score_noalloc(_ptr(W), N, K, _ptr(X), T, _ptr(lam), _ptr(score), _stream(stream)),
            "owq_calibrate_score_noalloc")
     return lam, score
+
+
+def _calib_items(Ws: list, Xs: list, outs=None):
+    n = len(Ws)
+    if n < 1 or len(Xs) != n:
+        raise ValueError(f"need one X per W: {n} W, {len(Xs)} X")
+    items = (OwqCalibItem * n)()
+    res = []
+    shapes = []
+    for i, (W, X) in enumerate(zip(Ws, Xs)):
+        try:
+            shapes.append(_calib_shapes(W, X))
+        except (TypeError, ValueError) as e:
+            raise type(e)(f"[{i}] {e}") from None
+    _on_device(*[(f"[{i}] W", W) for i, W in enumerate(Ws)], *[(f"[{i}] X", X) for i, X in enumerate(Xs)])
+    for i, (W, X) in enumerate(zip(Ws, Xs)):
+        N, K, T = shapes[i]
+        if outs is None:
+            lam = torch.empty(K, dtype=torch.float64, device=W.device)
+            score = torch.empty(K, dtype=torch.float64, device=W.device)
+        else:
+            lam, score = outs[i]
+        items[i] = OwqCalibItem(W.data_ptr(), N, K, X.data_ptr(), T, lam.data_ptr(), score.data_ptr())
+        res.append((lam, score))
+    return items, res
+
+
+def calibrate_batched_workspace_bytes(shapes: list) -> int:
+    """Workspace of calibrate_batched for (N, K, T) per linear."""
+    n = len(shapes)
+    items = (OwqCalibItem * max(n, 1))()
+    for i, (N, K, T) in enumerate(shapes):
+        items[i] = OwqCalibItem(None, N, K, None, T, None, None)
+    return int(lib().owq_calibrate_batched_workspace_bytes(items, n))
+
+
+def calibrate_batched(Ws: list, Xs: list, workspace: torch.Tensor | None = None, stream=None) -> list:
+    """calibrate() of several linears in one pipelined sequence of launches
+    (owq_calibrate_score_batched); returns one (lambda, score) pair per linear."""
+    items, res = _calib_items(Ws, Xs)
+    n = len(Ws)
+    nbytes = int(lib().owq_calibrate_batched_workspace_bytes(items, n))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=Ws[0].device)
+    else:
+        _meta(workspace, torch.uint8, "workspace")
+        _on_device(("workspace", workspace))
+    _check(lib().owq_calibrate_score_batched(items, n, _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "owq_calibrate_score_batched")
+    return res
 
 
 def calibrate_noalloc_max_workspace() -> int:

@@ -80,6 +80,33 @@ def test_calibrate_validation(lib):
     assert "workspace" in _err(lib)
 
 
+def test_calibrate_batched_validation(lib):
+    from mixed_precision_weight_amd import owq
+    It = owq.OwqCalibItem
+    a, b = It(FAKE, 64, 64, FAKE, 32, FAKE, FAKE), It(FAKE, 128, 96, FAKE, 48, FAKE, FAKE)
+    two = (It * 2)(a, b)
+    per = [lib.owq_calibrate_workspace_bytes(64, 64, 32), lib.owq_calibrate_workspace_bytes(128, 96, 48)]
+    ws = lib.owq_calibrate_batched_workspace_bytes(two, 2)
+    assert ws == sum((x + 255) // 256 * 256 for x in per)
+    assert lib.owq_calibrate_batched_workspace_bytes(two, 0) == 0
+    assert lib.owq_calibrate_batched_workspace_bytes(None, 2) == 0
+    assert lib.owq_calibrate_batched_workspace_bytes((It * 2)(a, It(FAKE, 64, 48, FAKE, 32, FAKE, FAKE)), 2) == 0
+    f = lib.owq_calibrate_score_batched
+    assert f(None, 2, FAKE, ws, None) == 1
+    assert f(two, 2, None, ws, None) == 1
+    assert f(two, 0, FAKE, ws, None) == 5
+    assert f(two, 65, FAKE, ws, None) == 5
+    assert f(two, 2, FAKE + 16, ws, None) == 4
+    assert f(two, 2, FAKE, ws - 1, None) == 6
+    assert "workspace" in _err(lib)
+    assert f((It * 2)(a, It(FAKE, 128, 96, FAKE, 48, None, FAKE)), 2, FAKE, ws, None) == 1
+    assert "item 1" in _err(lib)
+    assert f((It * 2)(a, It(FAKE, 128, 40, FAKE, 48, FAKE, FAKE)), 2, FAKE, ws, None) == 2
+    assert f((It * 2)(a, It(FAKE, 128, 96, FAKE, 0, FAKE, FAKE)), 2, FAKE, ws, None) == 2
+    assert f((It * 2)(It(FAKE + 2, 64, 64, FAKE, 32, FAKE, FAKE), b), 2, FAKE, ws, None) == 4
+    assert "item 0" in _err(lib)
+
+
 def test_select_validation(lib):
     f = lib.owq_select_weak
     assert f(None, 64, 4, FAKE, None) == 1

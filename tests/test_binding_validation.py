@@ -43,6 +43,18 @@ def test_calibrate_checks_shapes():
     _host_only(owq.calibrate, W, torch.zeros((16, K), dtype=torch.float16))
 
 
+def test_calibrate_batched_checks_shapes():
+    W = torch.zeros((N, K), dtype=torch.float16)
+    X = torch.zeros((16, K), dtype=torch.float16)
+    with pytest.raises(ValueError, match="one X per W"):
+        owq.calibrate_batched([W, W], [X])
+    with pytest.raises(ValueError, match=r"\[1\] X has"):
+        owq.calibrate_batched([W, W], [X, torch.zeros((16, K - 32), dtype=torch.float16)])
+    with pytest.raises(TypeError, match=r"\[0\] W must be torch.float16"):
+        owq.calibrate_batched([W.float(), W], [X, X])
+    _host_only(owq.calibrate_batched, [W, W], [X, X])
+
+
 def test_select_checks_k_and_out():
     s = torch.zeros(K, dtype=torch.float64)
     with pytest.raises(ValueError, match="outside"):

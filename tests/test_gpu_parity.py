@@ -133,6 +133,37 @@ def test_edge_shapes(owq, N, K, k, Ms):
     _run(owq, W, X, k, [x[:m] for m in Ms], f"edge N={N} K={K} k={k}")
 
 
+def test_calibrate_batched_matches_single(owq):
+    """owq_calibrate_score_batched overlaps the three passes of consecutive
+    linears in shared launches: each linear's lambda and score equal its own
+    owq_calibrate_score call bit for bit (and the oracle, to the calibration
+    bar), for one, two and seven linears of mixed sizes, with a workspace full
+    of garbage."""
+    import torch
+    import oracle
+    shapes = [(1, 32, 1), (37, 4128, 24), (300, 96, 77), (5, 11008, 9), (64, 640, 300), (130, 8192, 16),
+              (513, 2048, 48)]
+    rng = np.random.default_rng(11)
+    Ws = [_tiny_rows(synth.random_layer(rng, N, K, 0.02)) for N, K, _ in shapes]
+    Xs = [synth.calibration(synth.LayerSpec("cb", N, K, 1, 0.02, max(1, K // 200), 20.0), N + K, T)
+          for N, K, T in shapes]
+    Wd, Xd = [dev(W) for W in Ws], [dev(X) for X in Xs]
+    single = [owq.calibrate(W, X) for W, X in zip(Wd, Xd)]
+    for n in (1, 2, 7):
+        print(f"calibrate_batched: {n} linears", flush=True)
+        nbytes = owq.calibrate_batched_workspace_bytes(shapes[:n])
+        ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda:0")
+        got = owq.calibrate_batched(Wd[:n], Xd[:n], workspace=ws)
+        torch.cuda.synchronize()
+        for i in range(n):
+            for a, b, what in zip(got[i], single[i], ("lambda", "score")):
+                assert host(a).tobytes() == host(b).tobytes(), (n, i, shapes[i], what)
+    for i in (0, 1, 2, 6):
+        o_lam, o_score = oracle.calibrate_score(Ws[i], Xs[i])
+        np.testing.assert_allclose(host(single[i][0]), o_lam, rtol=1e-12, atol=0, err_msg=str(shapes[i]))
+        np.testing.assert_allclose(host(single[i][1]), o_score, rtol=1e-12, atol=1e-300, err_msg=str(shapes[i]))
+
+
 def test_select_batched_matches_single(owq):
     """owq_select_weak_batched over selections of every block shape (and k = 0,
     k = K, K above 16384) gives exactly the single calls' and the oracle's
