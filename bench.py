@@ -290,8 +290,8 @@ def main():
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    ws_cal = torch.empty(owq.calibrate_batched_workspace_bytes([(s.N, s.K, cfg.T) for s in specs]),
-                         dtype=torch.uint8, device=dev)
+    # the layer's calibration, with its arguments marshalled once
+    cal_call = owq.PreparedCalibrate(W, X)
 
     # events of the calibration phase: ev[0] before calibrating the 7 linears
     # (one batched call), ev[1] after it, ev[2] after the selection (one batched
@@ -299,7 +299,7 @@ def main():
     def calibrate_pack(slot, ev=None):
         if ev is not None:
             ev[0].record()
-        scores = [sc for _, sc in owq.calibrate_batched(W, X, workspace=ws_cal)]
+        scores = [sc for _, sc in cal_call()]
         if ev is not None:
             ev[1].record()
         idxs = owq.select_weak_batched(scores, [s.k for s in specs], outs=[slot[li]["weak_idx"] for li in range(L)])
@@ -404,9 +404,9 @@ def main():
                         "bound": "mfma", "achieved": round(pre_tflops, 1), "peak": MFMA_FP16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
                         "algorithmic_flops": pre_flops, "per_linear": per_linear_prefill},
-            "calibrate_score": hbm_entry(cal_bytes, sum(cal_s), "k_calib_stage, the 7 linears in one "
-                                         "owq_calibrate_score_batched call (9 launches: launch s holds the first "
-                                         "pass of linear s, the error pass of s - 1, the final sums of s - 2)"),
+            "calibrate_score": hbm_entry(cal_bytes, sum(cal_s), "k_calib_fused, the 7 linears in one "
+                                         "owq_calibrate_score_batched call (3 launches: the K = 4096 linears, the "
+                                         "K = 11008 linear with the others' final sums, its final sums)"),
             "select_weak": {"what": "k_topk_reg_batched, the 7 linears in one owq_select_weak_batched call (one "
                                     "launch per block shape: K = 4096 and K = 11008)",
                             "us": round(sum(sel_s) * 1e6, 1), "bound": "latency"},
@@ -438,18 +438,20 @@ def main():
         result["decode_batch_sweep"] = sweep
 
     if not args.no_extras:
-        # the layer's calibration as one owq_calibrate_score call per linear (3
+        # the layer's calibration as one owq_calibrate_score call per linear (2
         # launches each), for comparison with the batched call timed above
+        one = [owq.PreparedCalibrate([W[li]], [X[li]]) for li in range(L)]
         reps = 5
         evc = [(E(), E()) for _ in range(reps)]
         for r in range(reps):
             evc[r][0].record()
             for li in range(L):
-                owq.calibrate(W[li], X[li], workspace=ws)
+                one[li]()
             evc[r][1].record()
         torch.cuda.synchronize()
         t = float(np.median([a.elapsed_time(b) for a, b in evc])) / 1e3
         result["kernels"]["calibrate_score"]["us_one_call_per_linear"] = round(t * 1e6, 2)
+        del one
 
         # the same decode as 7 launches per layer (one per linear), recorded in a HIP graph
         print("bench: decode as per-linear launches in a graph", file=sys.stderr, flush=True)
@@ -590,14 +592,14 @@ def main():
             seed = c4.seed(li)
             Wl = torch.from_numpy(synth.weights(s, seed)).to(dev)
             Xl = torch.from_numpy(synth.calibration(s, seed, c4.T)).to(dev)
-            wsl = torch.empty(owq.calibrate_workspace_bytes(s.N, s.K, c4.T), dtype=torch.uint8, device=dev)
-            _, score_l = owq.calibrate(Wl, Xl, workspace=wsl)
+            call = owq.PreparedCalibrate([Wl], [Xl])  # one linear: owq_calibrate_score's launches
+            _, score_l = call()[0]
             owq.select_weak(score_l, s.k)
             reps = 5
             evl = [(E(), E(), E()) for _ in range(reps)]
             for r in range(reps):
                 evl[r][0].record()
-                _, score_l = owq.calibrate(Wl, Xl, workspace=wsl)
+                call()
                 evl[r][1].record()
                 owq.select_weak(score_l, s.k)
                 evl[r][2].record()
@@ -605,10 +607,10 @@ def main():
             t = float(np.median([a.elapsed_time(b) for a, b, _ in evl])) / 1e3
             ts = float(np.median([b.elapsed_time(c) for _, b, c in evl])) / 1e3
             key = f"{s.name} {s.N}x{s.K} T={c4.T}"
-            long_cal[key] = hbm_entry(calib_bytes(s.N, s.K, c4.T), t, "owq_calibrate_score: k_calib_stage, 3 "
-                                                                       "launches (first, error, final pass)")
+            long_cal[key] = hbm_entry(calib_bytes(s.N, s.K, c4.T), t, "k_calib_fused (W row fits and errors, X "
+                                                                       "column tiles) + k_calib_fin, one linear")
             long_sel[key] = {"what": f"top-{s.k} of K = {s.K}", "us": round(ts * 1e6, 2), "bound": "latency"}
-            del Wl, Xl, wsl
+            del Wl, Xl, call
         result["kernels"]["calibrate_score_long"] = long_cal
         result["kernels"]["select_weak_long"] = long_sel
 

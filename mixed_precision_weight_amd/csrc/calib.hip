@@ -56,6 +56,8 @@ namespace {
 constexpr int kTileCols = 64;   // columns per X (or two-pass error) tile
 constexpr int kUnroll = 4;      // rows in flight per lane in a tile
 constexpr int kMaxWaves = 16;   // waves per block
+constexpr int kWPolicy = 2;     // buffer-load cache policy of the W rows: non-temporal (read once)
+constexpr bool kXNonTemporal = false;  // X tile loads non-temporal
 
 struct SqElem {  // x^2 (exact in fp32 for fp16 x)
     struct Row {};
@@ -123,7 +125,12 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* __restrict__ A, int6
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             const int64_t r = min(rb + (int64_t)u * phases, r1 - 1);
-            v[u] = *reinterpret_cast<const uint4*>(A + r * K + colc);
+            if constexpr (kXNonTemporal) {
+                typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+                v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(A + r * K + colc)));
+            } else {
+                v[u] = *reinterpret_cast<const uint4*>(A + r * K + colc);
+            }
             rw[u] = elem.load_row(r);
         }
 #pragma unroll
@@ -261,9 +268,9 @@ __device__ __forceinline__ uint32_t wave_h2max(uint32_t v)
 // nothing; a zero changes no min or max (the fit range contains 0), and those
 // slots and rows are never accumulated or stored. A row's range travels as the
 // fp16 pair (-min, max), reduced with one packed max.
-template <int WPL, int G>
+template <int WPL, int G, int D>
 __device__ __forceinline__ void fit_err_rows(const uint16_t* __restrict__ W, int64_t K, int64_t r0, int64_t r1,
-                                             double* __restrict__ part, uint32_t (&mm)[2][G][kMaxWaves])
+                                             double* __restrict__ part, uint32_t (&mm)[3][G][kMaxWaves])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nwaves = blockDim.x >> 6;
@@ -294,12 +301,12 @@ __device__ __forceinline__ void fit_err_rows(const uint16_t* __restrict__ W, int
             const uint32_t ro = (uint32_t)(rb + g - r0) * row_bytes;  // past r1: out of range
 #pragma unroll
             for (int u = 0; u < WPL; u++)
-                d[g][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, ro + off[u], 0, 0));
+                d[g][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, ro + off[u], 0, kWPolicy));
         }
     };
-    // rows rb .. rb + G - 1 held in v; the next G rows' loads go to vn first
+    // rows rb .. rb + G - 1 held in v; the loads of rows rb + D G .. go to vn first
     auto step = [&](int64_t rb, const Rows& v, Rows& vn, int buf) {
-        load(vn, rb + G);
+        load(vn, rb + D * G);
 #pragma unroll
         for (int g = 0; g < G; g++) {
             uint32_t nmn = 0, mx = 0;  // (min, max) pairs of the lane's columns, from 0
@@ -361,13 +368,28 @@ __device__ __forceinline__ void fit_err_rows(const uint16_t* __restrict__ W, int
             }
         }
     };
-    Rows va, vb;
-    load(va, r0);
-    for (int64_t rb = r0; rb < r1; rb += 2 * G) {  // the two row buffers take turns
-        step(rb, va, vb, 0);
-        if (rb + G >= r1)
-            break;
-        step(rb + G, vb, va, 1);
+    if constexpr (D == 1) {
+        Rows va, vb;
+        load(va, r0);
+        for (int64_t rb = r0; rb < r1; rb += 2 * G) {  // the two row buffers take turns
+            step(rb, va, vb, 0);
+            if (rb + G >= r1)
+                break;
+            step(rb + G, vb, va, 1);
+        }
+    } else {  // D == 2: three row buffers, two groups in flight
+        Rows va, vb, vc;
+        load(va, r0);
+        load(vb, r0 + G);
+        for (int64_t rb = r0; rb < r1; rb += 3 * G) {
+            step(rb, va, vc, 0);  // consecutive steps use different range slots
+            if (rb + G >= r1)
+                break;
+            step(rb + G, vb, va, 1);
+            if (rb + 2 * G >= r1)
+                break;
+            step(rb + 2 * G, vc, vb, 2);
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's out-of-range loads
 #pragma unroll
@@ -382,10 +404,13 @@ __device__ __forceinline__ void fit_err_rows(const uint16_t* __restrict__ W, int
 }
 
 // ---------------------------------------------------------------------------
-// One launch holds up to kCalibMaxLayers linears: blocks [wb[l], wb[l+1]) are
-// linear l's W blocks, then, after every W block, [xb[l], xb[l+1]) its X
-// blocks (the long W blocks start first).
+// One launch holds up to kCalibMaxLayers linears, and three kinds of blocks, in
+// this order: [wb[l], wb[l+1]) are linear l's W blocks (the long ones start
+// first), then [fb[l], fb[l+1]) its final-sum blocks, then [xb[l], xb[l+1]) its
+// X blocks. A launch of one group of linears also carries the final sums of
+// the group before it, whose partial sums the previous launch wrote.
 constexpr int kCalibMaxLayers = 16;
+constexpr int kCalibChunk = kCalibMaxLayers / 2;  // linears whose sums one launch computes
 
 struct CalibLayer {
     const uint16_t* W;
@@ -402,6 +427,7 @@ struct CalibLayer {
 struct CalibLaunch {
     CalibLayer L[kCalibMaxLayers];
     int32_t wb[kCalibMaxLayers + 1];
+    int32_t fb[kCalibMaxLayers + 1];
     int32_t xb[kCalibMaxLayers + 1];
     int32_t count;
 };
@@ -414,45 +440,95 @@ __device__ __forceinline__ int layer_of(const int32_t* b0, int count, int64_t b)
     return l;
 }
 
-// X column tiles of the blocks after the W blocks
-__device__ __forceinline__ void x_blocks(const CalibLaunch& c, int64_t b, double (&red)[kMaxWaves][kTileCols])
+// Final sums: kFinCols columns per block, kFinParts partial sums per column.
+constexpr int kFinCols = 16;
+constexpr int kFinParts = 64;
+
+// LDS of every role: the tile sums' [kMaxWaves][kTileCols] doubles and the final
+// sums' [2][kFinParts][kFinCols]
+constexpr int kCalibLds = 2 * kFinParts * kFinCols;
+
+// lambda_j = 2 sum_s px[s][j], e_j = sum_s pw[s][j], score_j = lambda_j e_j,
+// for the kFinCols columns of block blk. The order of the sums does not depend
+// on the block's size: partial sum v (0 .. kFinParts - 1) takes the slices
+// s = v (mod kFinParts) in order, and the partial sums are added in the order
+// v = 0, 1, ...; thread t computes those of column t % kFinCols with
+// v = t / kFinCols, t / kFinCols + blockDim.x / kFinCols, ...
+__device__ __forceinline__ void fin_cols(const CalibLayer& L, int64_t blk, double* lds)
+{
+    double(&red)[2][kFinParts][kFinCols] = *reinterpret_cast<double(*)[2][kFinParts][kFinCols]>(lds);
+    const int cl = threadIdx.x % kFinCols;
+    const int64_t j = blk * kFinCols + cl;
+    const int64_t jc = j < L.K ? j : L.K - 1;
+    for (int v = threadIdx.x / kFinCols; v < kFinParts; v += blockDim.x / kFinCols) {
+        double sx = 0.0, sw = 0.0;
+#pragma unroll 2
+        for (int64_t s = v; s < L.sx; s += kFinParts)
+            sx += L.px[s * L.K + jc];
+#pragma unroll 8
+        for (int64_t s = v; s < L.sw; s += kFinParts)
+            sw += L.pw[s * L.K + jc];
+        red[0][v][cl] = sx;
+        red[1][v][cl] = sw;
+    }
+    __syncthreads();
+    if (threadIdx.x < kFinCols && j < L.K) {
+        double lam = red[0][0][cl], e = red[1][0][cl];
+        for (int v = 1; v < kFinParts; v++) {
+            lam += red[0][v][cl];
+            e += red[1][v][cl];
+        }
+        lam *= 2.0;
+        L.lambda[j] = lam;
+        L.score[j] = lam * e;
+    }
+}
+
+// Final-sum and X blocks (every block at or after wb[count]); false: a W block
+__device__ __forceinline__ bool fin_or_x_blocks(const CalibLaunch& c, int64_t b, double* lds)
 {
     b -= c.wb[c.count];
+    if (b < 0)
+        return false;
+    if (b < c.fb[c.count]) {
+        const int l = layer_of(c.fb, c.count, b);
+        fin_cols(c.L[l], b - c.fb[l], lds);
+        return true;
+    }
+    b -= c.fb[c.count];
     const int l = layer_of(c.xb, c.count, b);
     const CalibLayer& L = c.L[l];
     b -= c.xb[l];
-    colsum_tile(L.X, L.T, L.K, L.rows_x, L.px, SqElem{}, b % L.tiles, b / L.tiles, red);
+    colsum_tile(L.X, L.T, L.K, L.rows_x, L.px, SqElem{}, b % L.tiles, b / L.tiles,
+                *reinterpret_cast<double(*)[kMaxWaves][kTileCols]>(lds));
+    return true;
 }
 
-template <int WPL, int G>
+template <int WPL, int G, int D>
 __global__ __launch_bounds__(1024) void k_calib_fused(const CalibLaunch c)
 {
-    __shared__ double red[kMaxWaves][kTileCols];
-    __shared__ uint32_t mm[2][G][kMaxWaves];
+    __shared__ double lds[kCalibLds];
+    __shared__ uint32_t mm[3][G][kMaxWaves];
     const int64_t b = blockIdx.x;
-    if (b < c.wb[c.count]) {
-        const int l = layer_of(c.wb, c.count, b);
-        const CalibLayer& L = c.L[l];
-        const int64_t blk = b - c.wb[l];
-        const int64_t r0 = blk * L.rows_w;
-        fit_err_rows<WPL, G>(L.W, L.K, r0, min(L.N, r0 + L.rows_w), L.pw + blk * L.K, mm);
-    } else {
-        x_blocks(c, b, red);
-    }
+    if (fin_or_x_blocks(c, b, lds))
+        return;
+    const int l = layer_of(c.wb, c.count, b);
+    const CalibLayer& L = c.L[l];
+    const int64_t blk = b - c.wb[l];
+    const int64_t r0 = blk * L.rows_w;
+    fit_err_rows<WPL, G, D>(L.W, L.K, r0, min(L.N, r0 + L.rows_w), L.pw + blk * L.K, mm);
 }
 
-// two-pass form, first launch: row fits (one wave per row), X tiles
+// two-pass form, first launch: row fits (one wave per row), final sums, X tiles
 __global__ __launch_bounds__(256) void k_calib_fit(const CalibLaunch c)
 {
-    __shared__ double red[kMaxWaves][kTileCols];
+    __shared__ double lds[kCalibLds];
     const int64_t b = blockIdx.x;
-    if (b < c.wb[c.count]) {
-        const int l = layer_of(c.wb, c.count, b);
-        const CalibLayer& L = c.L[l];
-        rowfit_rows(L.W, L.N, L.K, L.s16, L.z, b - c.wb[l]);
-    } else {
-        x_blocks(c, b, red);
-    }
+    if (fin_or_x_blocks(c, b, lds))
+        return;
+    const int l = layer_of(c.wb, c.count, b);
+    const CalibLayer& L = c.L[l];
+    rowfit_rows(L.W, L.N, L.K, L.s16, L.z, b - c.wb[l]);
 }
 
 // two-pass form, second launch: column tiles of the RTN errors
@@ -466,46 +542,25 @@ __global__ __launch_bounds__(256) void k_calib_err(const CalibLaunch c)
     colsum_tile(L.W, L.N, L.K, L.rows_w, L.pw, ErrElem{L.s16, L.z}, b % L.tiles, b / L.tiles, red);
 }
 
-// lambda_j = 2 sum_s px[s][j], e_j = sum_s pw[s][j], score_j = lambda_j e_j.
-// A block of 16 waves owns 64 columns; wave w sums the slices s = w (mod 16)
-// in order, then the 16 wave sums are added in wave order.
+// the final sums alone (after the last group of linears)
 __global__ __launch_bounds__(1024) void k_calib_fin(const CalibLaunch c)
 {
-    __shared__ double red[2][kMaxWaves][64];
-    int64_t b = blockIdx.x;
-    const int l = layer_of(c.wb, c.count, b);
-    const CalibLayer& L = c.L[l];
-    b -= c.wb[l];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t j = b * 64 + lane;
-    const int64_t jc = j < L.K ? j : L.K - 1;
-    double sx = 0.0, sw = 0.0;
-#pragma unroll 4
-    for (int64_t s = wave; s < L.sx; s += kMaxWaves)
-        sx += L.px[s * L.K + jc];
-#pragma unroll 8
-    for (int64_t s = wave; s < L.sw; s += kMaxWaves)
-        sw += L.pw[s * L.K + jc];
-    red[0][wave][lane] = sx;
-    red[1][wave][lane] = sw;
-    __syncthreads();
-    if (threadIdx.x < 64 && j < L.K) {
-        double lam = red[0][0][lane], e = red[1][0][lane];
-        for (int w = 1; w < kMaxWaves; w++) {
-            lam += red[0][w][lane];
-            e += red[1][w][lane];
-        }
-        lam *= 2.0;
-        L.lambda[j] = lam;
-        L.score[j] = lam * e;
-    }
+    __shared__ double lds[kCalibLds];
+    const int64_t b = blockIdx.x;
+    const int l = layer_of(c.fb, c.count, b);
+    fin_cols(c.L[l], b - c.fb[l], lds);
 }
 
-// Rows per fused W block: one [K] fp64 partial row per block costs 4 / kFusedRows
-// of W's bytes (12.5 % at 32), and a block streams kFusedRows rows.
+// Rows per fused W block: one [K] fp64 partial row per block costs 4 / rows of
+// W's bytes (12.5 % at 32); rows wider than kWpl2Words words take kFusedRowsWide
+// (more, shorter blocks: such a block streams as many bytes as several narrow
+// ones).
 constexpr int64_t kFusedRows = 32;
-// fused form with 2 words per lane up to this many words per row (K = 8 x), 4 above
+constexpr int64_t kFusedRowsWide = 32;
+// fused form: 2 words per lane up to kWpl2Words words per row (K = 8 x), 3 up to
+// kWpl3Words, 4 above
 constexpr int64_t kWpl2Words = 1024;
+constexpr int64_t kWpl3Words = 1536;
 // rows of X per tile block
 constexpr int64_t kTileRows = 512;
 
@@ -529,6 +584,9 @@ CalibPlan calib_plan(int64_t N, int64_t K, int64_t T)
     if (nw <= kWpl2Words) {
         p.wpl = 2;
         p.nwaves = (int32_t)((nw + 127) / 128);
+    } else if (nw <= kWpl3Words) {
+        p.wpl = 3;
+        p.nwaves = (int32_t)((nw + 191) / 192);
     } else if (nw <= 4096) {  // K <= 32768
         p.wpl = 4;
         p.nwaves = (int32_t)((nw + 255) / 256);
@@ -539,8 +597,8 @@ CalibPlan calib_plan(int64_t N, int64_t K, int64_t T)
     p.sx = choose_slices(T);
     p.rows_x = (T + p.sx - 1) / p.sx;
     if (p.wpl) {
-        p.rows_w = kFusedRows;
-        p.sw = (N + kFusedRows - 1) / kFusedRows;
+        p.rows_w = nw <= kWpl2Words ? kFusedRows : kFusedRowsWide;
+        p.sw = (N + p.rows_w - 1) / p.rows_w;
     } else {
         p.sw = choose_slices(N);
         p.rows_w = (N + p.sw - 1) / p.sw;
@@ -611,25 +669,31 @@ hipError_t launch_calibrate_batched(const CalibItem* items, int count, void* con
         L.tiles = (it.K + kTileCols - 1) / kTileCols;
         return L;
     };
-    // w_blocks(l) / x_blocks(l): the blocks of linear l in one launch
-    auto run = [&](const int* ids, int n, auto kernel, int threads, auto w_blocks, auto x_blocks) {
+    // w_blocks / x_blocks: the W and X blocks of each linear of `ids` in one
+    // launch; fin: linears whose final sums the launch also computes
+    auto run = [&](const std::vector<int>& ids, const std::vector<int>& fin, auto kernel, int threads,
+                   auto w_blocks, auto x_blocks) {
         CalibLaunch c{};
-        c.count = n;
-        c.wb[0] = 0;
-        for (int i = 0; i < n; i++) {
-            c.L[i] = layer(ids[i]);
-            c.wb[i + 1] = c.wb[i] + (int32_t)w_blocks(c.L[i]);
+        const int n = (int)ids.size(), n2 = n + (int)fin.size();
+        c.count = n2;
+        c.wb[0] = c.fb[0] = c.xb[0] = 0;
+        for (int i = 0; i < n2; i++) {
+            const bool main = i < n;
+            c.L[i] = layer(main ? ids[i] : fin[i - n]);
+            c.wb[i + 1] = c.wb[i] + (int32_t)(main ? w_blocks(c.L[i]) : 0);
+            c.fb[i + 1] = c.fb[i] + (int32_t)(main ? 0 : (c.L[i].K + kFinCols - 1) / kFinCols);
+            c.xb[i + 1] = c.xb[i] + (int32_t)(main ? x_blocks(c.L[i]) : 0);
         }
-        c.xb[0] = 0;
-        for (int i = 0; i < n; i++)
-            c.xb[i + 1] = c.xb[i] + (int32_t)x_blocks(c.L[i]);
-        const int64_t nb = (int64_t)c.wb[n] + c.xb[n];
+        const int64_t nb = (int64_t)c.wb[n2] + c.fb[n2] + c.xb[n2];
         if (nb > 0)
             hipLaunchKernelGGL(kernel, dim3((unsigned)nb), dim3(threads), 0, s, c);
     };
     auto none = [](const CalibLayer&) { return (int64_t)0; };
     auto xtiles = [](const CalibLayer& L) { return L.tiles * L.sx; };
-    // linears of one block shape share a launch, kCalibMaxLayers at a time
+    auto fused = [](const CalibLayer& L) { return L.sw; };
+    // linears of one block shape share a launch, kCalibChunk at a time; each
+    // launch also finishes the previous chunk
+    std::vector<int> pending;
     std::vector<char> done((size_t)count, 0);
     for (int l0 = 0; l0 < count; l0++) {
         if (done[l0])
@@ -641,26 +705,22 @@ hipError_t launch_calibrate_batched(const CalibItem* items, int count, void* con
                 done[l] = 1;
             }
         const int wpl = plans[l0].wpl, threads = 64 * plans[l0].nwaves;
-        for (size_t i = 0; i < ids.size(); i += kCalibMaxLayers) {
-            const int n = (int)std::min(ids.size() - i, (size_t)kCalibMaxLayers);
-            const int* p = ids.data() + i;
-            auto fused = [](const CalibLayer& L) { return L.sw; };
+        for (size_t i = 0; i < ids.size(); i += kCalibChunk) {
+            const std::vector<int> chunk(ids.begin() + i, ids.begin() + std::min(ids.size(), i + kCalibChunk));
             if (wpl == 2) {
-                run(p, n, k_calib_fused<2, 2>, threads, fused, xtiles);
+                run(chunk, pending, k_calib_fused<2, 2, 1>, threads, fused, xtiles);
+            } else if (wpl == 3) {
+                run(chunk, pending, k_calib_fused<3, 2, 1>, threads, fused, xtiles);
             } else if (wpl == 4) {
-                run(p, n, k_calib_fused<4, 1>, threads, fused, xtiles);
+                run(chunk, pending, k_calib_fused<4, 1, 1>, threads, fused, xtiles);
             } else {
-                run(p, n, k_calib_fit, 256, [](const CalibLayer& L) { return (L.N + 3) / 4; }, xtiles);
-                run(p, n, k_calib_err, 256, [](const CalibLayer& L) { return L.tiles * L.sw; }, none);
+                run(chunk, pending, k_calib_fit, 256, [](const CalibLayer& L) { return (L.N + 3) / 4; }, xtiles);
+                run(chunk, {}, k_calib_err, 256, [](const CalibLayer& L) { return L.tiles * L.sw; }, none);
             }
+            pending = chunk;
         }
     }
-    std::vector<int> all((size_t)count);
-    for (int l = 0; l < count; l++)
-        all[l] = l;
-    for (int i = 0; i < count; i += kCalibMaxLayers)
-        run(all.data() + i, std::min(count - i, kCalibMaxLayers), k_calib_fin, 1024,
-            [](const CalibLayer& L) { return (L.K + 63) / 64; }, none);
+    run({}, pending, k_calib_fin, 1024, none, none);
     return hipGetLastError();
 }
 

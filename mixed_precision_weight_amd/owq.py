@@ -686,6 +686,32 @@ class PreparedBatched:
         _check(self.fn(self.Ls, self.xp, self.yp, self.n, self.M, self.stream), "owq_linear_batched")
 
 
+class PreparedCalibrate:
+    """One owq_calibrate_score_batched call with its item array, outputs and
+    workspace built once (outputs: `results`, one (lambda, score) pair per
+    linear, rewritten by every call). The W and X tensors must stay alive, at
+    the same addresses, while the object is used."""
+
+    def __init__(self, Ws: list, Xs: list, workspace: torch.Tensor | None = None, stream=None):
+        self.items, self.results = _calib_items(Ws, Xs)
+        self.n = len(Ws)
+        nbytes = int(lib().owq_calibrate_batched_workspace_bytes(self.items, self.n))
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=Ws[0].device)
+        else:
+            _meta(workspace, torch.uint8, "workspace")
+            _on_device(("workspace", workspace))
+        self._keep = (list(Ws), list(Xs), workspace)
+        self.ws = _ptr(workspace)
+        self.ws_bytes = _nbytes(workspace)
+        self.stream = _stream(stream)
+        self.fn = lib().owq_calibrate_score_batched
+
+    def __call__(self) -> list:
+        _check(self.fn(self.items, self.n, self.ws, self.ws_bytes, self.stream), "owq_calibrate_score_batched")
+        return self.results
+
+
 # ----------------------------------------------------------- measurement aid
 
 

@@ -154,10 +154,14 @@ def test_calibrate_batched_matches_single(owq):
         nbytes = owq.calibrate_batched_workspace_bytes(shapes[:n])
         ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda:0")
         got = owq.calibrate_batched(Wd[:n], Xd[:n], workspace=ws)
+        prepared = owq.PreparedCalibrate(Wd[:n], Xd[:n])
+        again = [tuple(t.clone() for t in pair) for pair in prepared()]
+        prepared()  # a second call on the same buffers
         torch.cuda.synchronize()
         for i in range(n):
-            for a, b, what in zip(got[i], single[i], ("lambda", "score")):
+            for a, b, c, d, what in zip(got[i], single[i], again[i], prepared.results[i], ("lambda", "score")):
                 assert host(a).tobytes() == host(b).tobytes(), (n, i, shapes[i], what)
+                assert host(c).tobytes() == host(b).tobytes() == host(d).tobytes(), (n, i, shapes[i], what)
     for i in (0, 1, 2, 6):
         o_lam, o_score = oracle.calibrate_score(Ws[i], Xs[i])
         np.testing.assert_allclose(host(single[i][0]), o_lam, rtol=1e-12, atol=0, err_msg=str(shapes[i]))
