@@ -434,7 +434,7 @@ def main():
                                               "median of 10 calls, each after a read-only pass over 1 GiB"),
                                     us_in_step=round(cal_in_step * 1e6, 2)),
             "select_weak": {"what": "k_topk_reg_batched, the 7 linears in one owq_select_weak_batched call (one "
-                                    "launch per block shape: K = 4096 and K = 11008)",
+                                    "launch, 11 keys x 16 waves per selection)",
                             "us": round(sum(sel_s) * 1e6, 1), "bound": "latency"},
             "pack": hbm_entry(pk_bytes, sum(pak_s), "k_pack, 7 linears"),
         },

@@ -162,8 +162,9 @@ owq_status owq_select_weak(const double* score, int64_t K, int32_t k,
 
 /* `count` independent weak-column selections (e.g. the 7 linears of a decoder
  * layer) with the results owq_select_weak would give one by one, in one kernel
- * launch per block shape (selections with K > 16384 get one launch each):
- * every selection is a latency-bound single workgroup, so they run side by side.
+ * launch (with the widest block shape any of them needs; selections with
+ * K > 16384 get one launch each): every selection is a latency-bound single
+ * workgroup, so they run side by side.
  * scores, weak_idxs: HOST arrays [count] of device pointers; Ks, ks: HOST arrays
  * [count]; each selection's arguments as owq_select_weak's. Returns
  * OWQ_ERR_UNSUPPORTED unless 1 <= count <= 64; other errors as owq_select_weak,

@@ -39,8 +39,9 @@ hipError_t calib_scratch(void** ptr);
 
 // ------------------------------------------------------------------- select --
 hipError_t launch_select(const double* score, int64_t K, int32_t k, int32_t* idx, hipStream_t s);
-// `count` selections (k[i] == 0 skipped): one block each, one launch per block
-// shape and kSelectMaxBatch selections (one per selection above K = 16384)
+// `count` selections (k[i] == 0 skipped): one block each, one launch per
+// kSelectMaxBatch selections with the widest block shape among them (one
+// launch per selection above K = 16384)
 constexpr int kSelectMaxBatch = 64;
 hipError_t launch_select_batched(const double* const* score, const int64_t* K, const int32_t* k,
                                  int32_t* const* idx, int count, hipStream_t s);

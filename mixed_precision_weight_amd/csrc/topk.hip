@@ -17,6 +17,8 @@
 //     threshold, or equal to it and among the first (k - #above) equal keys in
 //     index order. Ballot/popcount scans keep index order, so the output is
 //     ascending without a sort.
+#include <algorithm>
+
 #include "owq_device.h"
 #include "owq_launch.h"
 
@@ -365,20 +367,26 @@ hipError_t launch_select_batched(const double* const* score, const int64_t* K, c
     for (int i = 0; i < count; i++)  // large K: one launch each
         if (k[i] > 0 && shape_of(K[i]) == 3)
             hipLaunchKernelGGL(k_topk, dim3(1), dim3(1024), 0, s, score[i], K[i], k[i], idx[i]);
-    for (int shape = 0; shape < 3; shape++) {
-        SelBatch b{};
-        for (int i = 0; i < count; i++) {
-            if (k[i] == 0 || shape_of(K[i]) != shape)
-                continue;
-            b.score[b.count] = score[i];
-            b.out[b.count] = idx[i];
-            b.K[b.count] = (int32_t)K[i];
-            b.k[b.count] = k[i];
-            if (++b.count == kSelectMaxBatch)
-                flush(shape, b);
-        }
-        flush(shape, b);
+    // the register-path selections run side by side in one launch, with the
+    // widest block shape any of them needs: the launch then takes about as long
+    // as its slowest selection, where one launch per shape would add them up
+    // (the selected set is unique, so the shape does not change a result)
+    int shape = -1;
+    for (int i = 0; i < count; i++)
+        if (k[i] > 0 && shape_of(K[i]) < 3)
+            shape = std::max(shape, shape_of(K[i]));
+    SelBatch b{};
+    for (int i = 0; i < count; i++) {
+        if (k[i] == 0 || shape_of(K[i]) == 3)
+            continue;
+        b.score[b.count] = score[i];
+        b.out[b.count] = idx[i];
+        b.K[b.count] = (int32_t)K[i];
+        b.k[b.count] = k[i];
+        if (++b.count == kSelectMaxBatch)
+            flush(shape, b);
     }
+    flush(shape, b);
     return hipGetLastError();
 }
 

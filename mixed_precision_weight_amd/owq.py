@@ -276,7 +276,7 @@ def select_weak(score: torch.Tensor, k: int, out: torch.Tensor | None = None, st
 
 
 def select_weak_batched(scores: list, ks: list, outs: list | None = None, stream=None) -> list:
-    """owq_select_weak for several score vectors in one launch per block shape;
+    """owq_select_weak for several score vectors in one launch;
     returns one int32 [k] index tensor per score (written to outs[i] if given)."""
     n = len(scores)
     if n < 1 or len(ks) != n or (outs is not None and len(outs) != n):
