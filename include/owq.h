@@ -190,6 +190,26 @@ owq_status owq_pack(const uint16_t* W, int64_t N, int64_t K,
                     uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
                     uint16_t* w_weak, void* stream);
 
+/* One linear of owq_pack_batched: owq_pack's arguments (device pointers). */
+typedef struct owq_pack_item {
+    const uint16_t* W;        /* fp16 [N][K] */
+    int64_t N, K;
+    const int32_t* weak_idx;  /* int32 [k], ascending (may be NULL iff k == 0) */
+    int32_t k;
+    uint32_t* qcodes;         /* [N][K/32][3] (output) */
+    uint16_t* scales;         /* fp16 [N] (output) */
+    uint8_t* zeros;           /* uint8 [N] (output) */
+    uint16_t* w_weak;         /* fp16 [N][k] (output; may be NULL iff k == 0) */
+} owq_pack_item;
+
+/* owq_pack for `count` linears (e.g. the 7 of a decoder layer), bit for bit the
+ * same outputs ([PL] "Storage Methods", paper appendix section 2, as owq_pack),
+ * with the linears of one kernel form in one launch (every row is independent,
+ * so the rows of all of them stream side by side). items: HOST array [count].
+ * Returns OWQ_ERR_UNSUPPORTED unless 1 <= count <= 64; other errors as
+ * owq_pack, reported with the item's index. */
+owq_status owq_pack_batched(const owq_pack_item* items, int32_t count, void* stream);
+
 /* owq_pack with each row's step size and zero point chosen by a truncation-aware
  * 2D grid search over both, before the codes are formed ([PL] "Low-precision
  * quantization" (paper "Quantization Configuration Search", pp.4-5): a grid

@@ -25,6 +25,15 @@ owq_status fail(owq_status s, const char* fmt, ...)
     return s;
 }
 
+// The last error again, prefixed with "<what> <i>: " (the message is copied
+// first: formatting a buffer into itself is undefined).
+owq_status fail_at(owq_status s, const char* what, int i)
+{
+    char msg[sizeof g_err];
+    snprintf(msg, sizeof msg, "%s", g_err);
+    return fail(s, "%s %d: %s", what, i, msg);
+}
+
 owq_status hip_status(hipError_t e, const char* what)
 {
     if (e == hipSuccess) {
@@ -225,7 +234,7 @@ owq_status owq_calibrate_score_batched(const owq_calib_item* items, int32_t coun
                         (long long)c.T);
         owq_status st = check_k_dim(c.K);
         if (st != OWQ_OK)
-            return fail(st, "item %d: %s", l, g_err);
+            return fail_at(st, "item", l);
         if (!aligned(c.W, 16) || !aligned(c.X, 16) || !aligned(c.lambda, 8) || !aligned(c.score, 8))
             return fail(OWQ_ERR_ALIGN, "item %d: misaligned pointer (W, X: 16 B, lambda/score: 8 B)", l);
         it[l] = owq::CalibItem{c.W, c.N, c.K, c.X, c.T, c.lambda, c.score};
@@ -335,6 +344,38 @@ owq_status owq_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* weak
     return hip_status(owq::launch_pack(W, N, K, k > 0 ? weak_idx : nullptr, k, qcodes, scales, zeros,
                                        k > 0 ? w_weak : nullptr, (hipStream_t)stream),
                       "owq_pack launch");
+}
+
+owq_status owq_pack_batched(const owq_pack_item* items, int32_t count, void* stream)
+{
+    if (!items)
+        return fail(OWQ_ERR_NULL, "items must be non-NULL");
+    if (count < 1 || count > 64)
+        return fail(OWQ_ERR_UNSUPPORTED, "count = %d: need 1 <= count <= 64", count);
+    std::vector<owq::PackItem> it((size_t)count);
+    for (int32_t l = 0; l < count; l++) {
+        const owq_pack_item& c = items[l];
+        if (!c.W || !c.qcodes || !c.scales || !c.zeros)
+            return fail(OWQ_ERR_NULL, "item %d: W, qcodes, scales and zeros must be non-NULL", l);
+        if (c.N < 1 || c.N > INT32_MAX)
+            return fail(OWQ_ERR_SHAPE, "item %d: N = %lld out of range", l, (long long)c.N);
+        owq_status st = check_k_dim(c.K);
+        if (st != OWQ_OK)
+            return fail_at(st, "item", l);
+        if (c.k < 0 || c.k > c.K)
+            return fail(OWQ_ERR_RANGE, "item %d: k = %d outside [0, K = %lld]", l, c.k, (long long)c.K);
+        if (c.k > 0 && (!c.weak_idx || !c.w_weak))
+            return fail(OWQ_ERR_NULL, "item %d: weak_idx and w_weak must be non-NULL when k > 0", l);
+        if (!aligned(c.W, 16) || !aligned(c.qcodes, 4) || !aligned(c.scales, 2) ||
+            (c.k > 0 && (!aligned(c.weak_idx, 4) || !aligned(c.w_weak, 2))))
+            return fail(OWQ_ERR_ALIGN, "item %d: misaligned pointer (W: 16 B, qcodes/weak_idx: 4 B, fp16: 2 B)", l);
+        st = check_idx_on_host(c.weak_idx, c.k, c.K, (hipStream_t)stream);
+        if (st != OWQ_OK)
+            return fail_at(st, "item", l);
+        it[l] = owq::PackItem{c.W, c.N, c.K, c.k > 0 ? c.weak_idx : nullptr, c.k, c.qcodes, c.scales, c.zeros,
+                              c.k > 0 ? c.w_weak : nullptr};
+    }
+    return hip_status(owq::launch_pack_batched(it.data(), count, (hipStream_t)stream), "owq_pack_batched launch");
 }
 
 owq_status owq_pack_search(const uint16_t* W, int64_t N, int64_t K, const int32_t* weak_idx, int32_t k,
@@ -538,7 +579,7 @@ owq_status owq_linear_backward_batched(const owq_layer* Ls, const uint16_t* cons
             return fail(OWQ_ERR_NULL, "layer %d: dy must be non-NULL", l);
         owq_status st = check_layer(L, M, x ? x : dy[l], dy[l]);
         if (st != OWQ_OK)
-            return fail(st, "layer %d: %s", l, g_err);
+            return fail_at(st, "layer", l);
         if (dw[l] && L->k > 0 && !x)
             return fail(OWQ_ERR_NULL, "layer %d: x must be non-NULL for dw_weak", l);
         if ((dx[l] && !aligned(dx[l], 2)) || (dw[l] && !aligned(dw[l], 4)) || !aligned(dy[l], 2))
@@ -600,7 +641,7 @@ owq_status owq_linear_batched(const owq_layer* Ls, const uint16_t* const* xs, ui
     for (int32_t l = 0; l < count; l++) {
         owq_status st = check_layer(&Ls[l], M, xs[l], ys[l]);
         if (st != OWQ_OK)
-            return fail(st, "layer %d: %s", l, g_err);
+            return fail_at(st, "layer", l);
         st = check_idx_on_host(Ls[l].weak_idx, Ls[l].k, Ls[l].K, (hipStream_t)stream);
         if (st != OWQ_OK)
             return st;

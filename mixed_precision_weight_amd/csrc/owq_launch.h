@@ -47,6 +47,20 @@ hipError_t launch_select_batched(const double* const* score, const int64_t* K, c
                                  int32_t* const* idx, int count, hipStream_t s);
 
 // --------------------------------------------------------------------- pack --
+// one linear of a batched pack: owq_pack's arguments (idx, ww NULL when k == 0)
+struct PackItem {
+    const uint16_t* W;
+    int64_t N, K;
+    const int32_t* idx;
+    int32_t k;
+    uint32_t* q;
+    uint16_t* scales;
+    uint8_t* zeros;
+    uint16_t* ww;
+};
+// linears per launch: those of one kernel form share a launch
+constexpr int kPackMaxLayers = 16;
+hipError_t launch_pack_batched(const PackItem* items, int count, hipStream_t s);
 hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
                        uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s);
 // The pack with each row's (step, zero point) read from scales / zeros.

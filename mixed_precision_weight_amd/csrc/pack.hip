@@ -22,6 +22,9 @@
 // Built with -ffp-contract=off: the quantiser steps are single IEEE operations
 // (the code itself comes from rint_quotient, which reproduces rint(w / s)
 // exactly).
+#include <algorithm>
+#include <vector>
+
 #include "owq_device.h"
 #include "owq_launch.h"
 
@@ -33,14 +36,49 @@ namespace {
 constexpr int kSlot[32] = {1,  6,  2,  7,  3,  8,  4,  9,  5,  10, 11, 16, 12, 17, 13, 18,
                            14, 19, 15, 20, 21, 26, 22, 27, 23, 28, 24, 29, 25, 30, 0,  31};
 
+// One launch packs up to kPackMaxLayers linears of one kernel form: blocks
+// [b0[l], b0[l+1]) walk linear l's rows (grid-stride over that range).
+struct PackLayer {
+    const uint16_t* W;
+    const int32_t* idx;
+    uint32_t* q;
+    uint16_t* scales;
+    uint8_t* zeros;
+    uint16_t* ww;
+    int64_t N, K;
+    int32_t k, pad;
+};
+
+struct PackBatch {
+    PackLayer L[kPackMaxLayers];
+    int32_t b0[kPackMaxLayers + 1];
+    int32_t count;
+};
+
+__device__ __forceinline__ int pack_layer_of(const PackBatch& b)
+{
+    int l = 0;
+    while (l + 1 < b.count && (int)blockIdx.x >= b.b0[l + 1])
+        l++;
+    return l;
+}
+
 // kGiven: each row's (step, zero point) is read from scales / zeros (written
 // there before, e.g. by the truncation-aware search) instead of fitted.
 template <int GPT, bool kGiven>
-__global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, int64_t N, int64_t K,
-                                              const int32_t* __restrict__ idx, int32_t k,
-                                              uint32_t* __restrict__ q, uint16_t* __restrict__ scales,
-                                              uint8_t* __restrict__ zeros, uint16_t* __restrict__ ww)
+__global__ __launch_bounds__(256) void k_pack(const PackBatch b)
 {
+    const int li = pack_layer_of(b);
+    const PackLayer& PL = b.L[li];
+    const uint16_t* __restrict__ W = PL.W;
+    const int64_t N = PL.N, K = PL.K;
+    const int32_t* __restrict__ idx = PL.idx;
+    const int32_t k = PL.k;
+    uint32_t* __restrict__ q = PL.q;
+    uint16_t* __restrict__ scales = PL.scales;
+    uint8_t* __restrict__ zeros = PL.zeros;
+    uint16_t* __restrict__ ww = PL.ww;
+    const int64_t blk = (int64_t)blockIdx.x - b.b0[li], nblk = b.b0[li + 1] - b.b0[li];
     extern __shared__ uint32_t wmask[];  // [G] weak-column bit mask per 32-column group
     __shared__ float red[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -56,7 +94,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
     }
     __syncthreads();
 
-    for (int64_t row = blockIdx.x; row < N; row += gridDim.x) {
+    for (int64_t row = blk; row < N; row += nblk) {
         const uint16_t* wr = W + row * K;
         uint32_t v[GPT][16];
         float lo = 0.0f, hi = 0.0f;
@@ -139,11 +177,19 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ W, in
 // walks 4 rows at a time (grid-stride). Lanes write their groups' 12 bytes next
 // to each other, 768 contiguous bytes per store instruction.
 template <int GPW, bool kGiven>
-__global__ __launch_bounds__(256) void k_pack_w(const uint16_t* __restrict__ W, int64_t N, int64_t K,
-                                                const int32_t* __restrict__ idx, int32_t k,
-                                                uint32_t* __restrict__ q, uint16_t* __restrict__ scales,
-                                                uint8_t* __restrict__ zeros, uint16_t* __restrict__ ww)
+__global__ __launch_bounds__(256) void k_pack_w(const PackBatch b)
 {
+    const int li = pack_layer_of(b);
+    const PackLayer& PL = b.L[li];
+    const uint16_t* __restrict__ W = PL.W;
+    const int64_t N = PL.N, K = PL.K;
+    const int32_t* __restrict__ idx = PL.idx;
+    const int32_t k = PL.k;
+    uint32_t* __restrict__ q = PL.q;
+    uint16_t* __restrict__ scales = PL.scales;
+    uint8_t* __restrict__ zeros = PL.zeros;
+    uint16_t* __restrict__ ww = PL.ww;
+    const int64_t blk = (int64_t)blockIdx.x - b.b0[li], nblk = b.b0[li + 1] - b.b0[li];
     extern __shared__ uint32_t wmask[];  // [G] weak-column bit mask per 32-column group
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = (int)(K / 32);
@@ -162,7 +208,7 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint16_t* __restrict__ W, 
     for (int u = 0; u < GPW; u++)
         m[u] = wmask[min(lane + 64 * u, G - 1)];
 
-    for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < N; row += (int64_t)gridDim.x * 4) {
+    for (int64_t row = blk * 4 + wave; row < N; row += nblk * 4) {
         const uint16_t* wr = W + row * K;
         uint32_t v[GPW][16];
         // every load first (clamped to the row), then the weak entries zeroed
@@ -236,26 +282,71 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint16_t* __restrict__ W, 
     }
 }
 
-template <int GPW, bool kGiven>
-hipError_t launch_pack_w(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
-                         uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
+// The kernel form of a linear: 1, 2, 3 = a wave per row with that many groups
+// per lane; 4 + t = a block per row with 1, 2, 4, 8 groups per thread (t = 0..3).
+int pack_form(int64_t K)
 {
     const int64_t G = K / 32;
-    const int64_t blocks = (N + 3) / 4;
-    const unsigned grid = (unsigned)(blocks < 2048 ? blocks : 2048);
-    hipLaunchKernelGGL((k_pack_w<GPW, kGiven>), dim3(grid), dim3(256), (size_t)G * sizeof(uint32_t), s, W, N,
-                       K, idx, k, q, scales, zeros, ww);
-    return hipGetLastError();
+    // a wave per row while a lane's groups fit in registers with room to spare
+    // (measured: K = 4096 17.5 us vs 20 us a block per row; at K = 11008 the
+    // block form is faster)
+    const int64_t gpw = (G + 63) / 64;  // groups per lane with a wave per row
+    if (gpw <= 3)
+        return (int)gpw;
+    const int64_t gpt = (G + 255) / 256;  // K <= 65536 -> gpt <= 8
+    return gpt <= 1 ? 4 : gpt <= 2 ? 5 : gpt <= 4 ? 6 : 7;
 }
 
-template <int GPT, bool kGiven>
-hipError_t launch_pack_t(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
-                         uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
+template <bool kGiven>
+void launch_pack_form(int form, const PackBatch& b, size_t lds, hipStream_t s)
 {
-    const int64_t G = K / 32;
-    const unsigned grid = (unsigned)(N < 4096 ? N : 4096);
-    hipLaunchKernelGGL((k_pack<GPT, kGiven>), dim3(grid), dim3(256), (size_t)G * sizeof(uint32_t), s, W, N,
-                       K, idx, k, q, scales, zeros, ww);
+    const dim3 grid((unsigned)b.b0[b.count]), block(256);
+    switch (form) {
+    case 1: hipLaunchKernelGGL((k_pack_w<1, kGiven>), grid, block, lds, s, b); break;
+    case 2: hipLaunchKernelGGL((k_pack_w<2, kGiven>), grid, block, lds, s, b); break;
+    case 3: hipLaunchKernelGGL((k_pack_w<3, kGiven>), grid, block, lds, s, b); break;
+    case 4: hipLaunchKernelGGL((k_pack<1, kGiven>), grid, block, lds, s, b); break;
+    case 5: hipLaunchKernelGGL((k_pack<2, kGiven>), grid, block, lds, s, b); break;
+    case 6: hipLaunchKernelGGL((k_pack<4, kGiven>), grid, block, lds, s, b); break;
+    default: hipLaunchKernelGGL((k_pack<8, kGiven>), grid, block, lds, s, b); break;
+    }
+}
+
+// Linears of one kernel form share a launch, kPackMaxLayers at a time. Blocks
+// per linear: a wave-per-row block takes 4 rows per step, at most 2048 blocks;
+// a block-per-row block one row, at most 4096 blocks (grid-stride beyond).
+template <bool kGiven>
+hipError_t launch_pack_batched_any(const PackItem* items, int count, hipStream_t s)
+{
+    std::vector<char> done((size_t)count, 0);
+    for (int l0 = 0; l0 < count; l0++) {
+        if (done[l0])
+            continue;
+        const int form = pack_form(items[l0].K);
+        PackBatch b{};
+        size_t lds = 0;
+        auto flush = [&]() {
+            if (b.count > 0)
+                launch_pack_form<kGiven>(form, b, lds, s);
+            b.count = 0;
+            lds = 0;
+        };
+        for (int l = l0; l < count; l++) {
+            if (done[l] || pack_form(items[l].K) != form)
+                continue;
+            done[l] = 1;
+            const PackItem& it = items[l];
+            PackLayer& L = b.L[b.count];
+            L = PackLayer{it.W, it.idx, it.q, it.scales, it.zeros, it.ww, it.N, it.K, it.k, 0};
+            const int64_t nb = form <= 3 ? std::min<int64_t>((it.N + 3) / 4, 2048) : std::min<int64_t>(it.N, 4096);
+            b.b0[0] = 0;
+            b.b0[b.count + 1] = b.b0[b.count] + (int32_t)nb;
+            lds = std::max(lds, (size_t)(it.K / 32) * sizeof(uint32_t));
+            if (++b.count == kPackMaxLayers)
+                flush();
+        }
+        flush();
+    }
     return hipGetLastError();
 }
 
@@ -263,28 +354,16 @@ template <bool kGiven>
 hipError_t launch_pack_any(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
                            uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)
 {
-    const int64_t G = K / 32;
-    // a wave per row while a lane's groups fit in registers with room to spare
-    // (measured: K = 4096 17.5 us vs 20 us a block per row; at K = 11008 the
-    // block form is faster)
-    const int64_t gpw = (G + 63) / 64;  // groups per lane with a wave per row
-    if (gpw <= 1)
-        return launch_pack_w<1, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
-    if (gpw <= 2)
-        return launch_pack_w<2, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
-    if (gpw <= 3)
-        return launch_pack_w<3, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
-    const int64_t gpt = (G + 255) / 256;  // K <= 65536 -> gpt <= 8
-    if (gpt <= 1)
-        return launch_pack_t<1, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
-    if (gpt <= 2)
-        return launch_pack_t<2, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
-    if (gpt <= 4)
-        return launch_pack_t<4, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
-    return launch_pack_t<8, kGiven>(W, N, K, idx, k, q, scales, zeros, ww, s);
+    const PackItem it{W, N, K, idx, k, q, scales, zeros, ww};
+    return launch_pack_batched_any<kGiven>(&it, 1, s);
 }
 
 }  // namespace
+
+hipError_t launch_pack_batched(const PackItem* items, int count, hipStream_t s)
+{
+    return launch_pack_batched_any<false>(items, count, s);
+}
 
 hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k,
                        uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s)

@@ -29,6 +29,12 @@ class OwqCalibItem(ctypes.Structure):
     _fields_ = [("W", _P), ("N", _I64), ("K", _I64), ("X", _P), ("T", _I64), ("lam", _P), ("score", _P)]
 
 
+class OwqPackItem(ctypes.Structure):
+    """Mirror of ``owq_pack_item`` (host struct, device pointers)."""
+    _fields_ = [("W", _P), ("N", _I64), ("K", _I64), ("weak_idx", _P), ("k", _I32), ("qcodes", _P),
+                ("scales", _P), ("zeros", _P), ("w_weak", _P)]
+
+
 class OwqLayer(ctypes.Structure):
     """Mirror of ``owq_layer`` (host struct, device pointers)."""
     _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64), ("k", ctypes.c_int32),
@@ -49,6 +55,7 @@ EXPORTS = {
     "owq_select_weak_batched": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.POINTER(_I64), ctypes.POINTER(_I32),
                                                ctypes.POINTER(_P), _I32, _P]),
     "owq_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
+    "owq_pack_batched": (ctypes.c_int, [ctypes.POINTER(OwqPackItem), _I32, _P]),
     "owq_pack_search": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P]),
     "owq_pack_storage": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
     "owq_linear_storage_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I64]),
@@ -315,33 +322,66 @@ def _pack_out_shapes(N: int, K: int, k: int) -> dict:
             "zeros": ((N,), torch.uint8), "w_weak": ((N, k), torch.float16)}
 
 
-def pack(W: torch.Tensor, weak_idx: torch.Tensor, out: dict | None = None, stream=None) -> dict:
-    """Latency-favoured packed layer: dict of device tensors
-    qcodes int32 [N][K/32][3] (uint32 bits), scales fp16 [N], zeros uint8 [N],
-    w_weak fp16 [N][k], weak_idx int32 [k]."""
-    _meta(W, torch.float16, "W")
-    _meta(weak_idx, torch.int32, "weak_idx")
+def _pack_args(W, weak_idx, out, where="", device_check=True):
+    """Checked shapes (N, K, k) of one pack, and its out dict (allocated if None;
+    device_check=False: the caller checks the devices of every pack first)."""
+    _meta(W, torch.float16, f"{where}W")
+    _meta(weak_idx, torch.int32, f"{where}weak_idx")
     if W.dim() != 2 or weak_idx.dim() != 1:
-        raise ValueError(f"W must be 2-D and weak_idx 1-D, got {tuple(W.shape)} and {tuple(weak_idx.shape)}")
+        raise ValueError(f"{where}W must be 2-D and weak_idx 1-D, got {tuple(W.shape)} and {tuple(weak_idx.shape)}")
     N, K = W.shape
     k = weak_idx.numel()
     if K % 32 or k > K:
-        raise ValueError(f"K = {K} must be a multiple of 32 and k = {k} at most K")
+        raise ValueError(f"{where}K = {K} must be a multiple of 32 and k = {k} at most K")
     want = _pack_out_shapes(N, K, k)
     if out is not None:
         for name in _PACK_OUT:
             if name not in out:
-                raise ValueError(f"out lacks {name!r}")
-            _meta(out[name], want[name][1], f"out[{name!r}]", want[name][0])
-    _on_device(("W", W), ("weak_idx", weak_idx), *[(f"out[{n!r}]", out[n]) for n in (_PACK_OUT if out else ())])
-    dev = W.device
+                raise ValueError(f"{where}out lacks {name!r}")
+            _meta(out[name], want[name][1], f"{where}out[{name!r}]", want[name][0])
+    if device_check:
+        _on_device((f"{where}W", W), (f"{where}weak_idx", weak_idx),
+                   *[(f"{where}out[{n!r}]", out[n]) for n in (_PACK_OUT if out else ())])
     if out is None:
-        out = {name: torch.empty(shape, dtype=dt, device=dev) for name, (shape, dt) in want.items()}
+        out = {name: torch.empty(shape, dtype=dt, device=W.device) for name, (shape, dt) in want.items()}
     out["weak_idx"] = weak_idx
+    return N, K, k, out
+
+
+def pack(W: torch.Tensor, weak_idx: torch.Tensor, out: dict | None = None, stream=None) -> dict:
+    """Latency-favoured packed layer: dict of device tensors
+    qcodes int32 [N][K/32][3] (uint32 bits), scales fp16 [N], zeros uint8 [N],
+    w_weak fp16 [N][k], weak_idx int32 [k]."""
+    N, K, k, out = _pack_args(W, weak_idx, out)
     _check(lib().owq_pack(_ptr(W), N, K, _ptr(weak_idx) if k else None, k, _ptr(out["qcodes"]),
                           _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["w_weak"]) if k else None,
                           _stream(stream)), "owq_pack")
     return out
+
+
+def pack_batched(Ws: list, weak_idxs: list, outs: list | None = None, stream=None) -> list:
+    """pack() of several linears (owq_pack_batched: the linears of one kernel
+    form in one launch); returns one packed dict per linear (outs[i] if given)."""
+    n = len(Ws)
+    if n < 1 or len(weak_idxs) != n or (outs is not None and len(outs) != n):
+        raise ValueError(f"need one weak_idx (and out) per W: {n} W, {len(weak_idxs)} weak_idx"
+                         + ("" if outs is None else f", {len(outs)} out"))
+    named = []
+    for i, (W, ix) in enumerate(zip(Ws, weak_idxs)):  # every shape first, then every device
+        _pack_args(W, ix, None if outs is None else outs[i], f"[{i}] ", device_check=False)
+        named += [(f"[{i}] W", W), (f"[{i}] weak_idx", ix)]
+        if outs is not None:
+            named += [(f"[{i}] out[{n!r}]", outs[i][n]) for n in _PACK_OUT]
+    _on_device(*named)
+    args = [_pack_args(W, ix, None if outs is None else outs[i], f"[{i}] ", device_check=False)
+            for i, (W, ix) in enumerate(zip(Ws, weak_idxs))]
+    items = (OwqPackItem * n)()
+    for i, (W, (N, K, k, out)) in enumerate(zip(Ws, args)):
+        items[i] = OwqPackItem(W.data_ptr(), N, K, out["weak_idx"].data_ptr() if k else None, k,
+                               out["qcodes"].data_ptr(), out["scales"].data_ptr(), out["zeros"].data_ptr(),
+                               out["w_weak"].data_ptr() if k else None)
+    _check(lib().owq_pack_batched(items, n, _stream(stream)), "owq_pack_batched")
+    return [a[3] for a in args]
 
 
 def pack_search(W: torch.Tensor, weak_idx: torch.Tensor, lam: torch.Tensor | None = None,

@@ -133,6 +133,26 @@ def test_pack_validation(lib):
     assert f(FAKE, 8, 64, FAKE, 2, FAKE + 1, FAKE, FAKE, FAKE, None) == 4
 
 
+def test_pack_batched_validation(lib):
+    from mixed_precision_weight_amd import owq
+    It = owq.OwqPackItem
+    a = It(FAKE, 8, 64, FAKE, 2, FAKE, FAKE, FAKE, FAKE)
+    f = lib.owq_pack_batched
+    two = lambda x, y: (It * 2)(x, y)
+    assert f(None, 2, None) == 1
+    assert f(two(a, a), 0, None) == 5
+    assert f(two(a, a), 65, None) == 5
+    assert f(two(a, It(None, 8, 64, FAKE, 2, FAKE, FAKE, FAKE, FAKE)), 2, None) == 1
+    assert "item 1" in _err(lib)
+    assert f(two(a, It(FAKE, 8, 65, FAKE, 2, FAKE, FAKE, FAKE, FAKE)), 2, None) == 2
+    assert f(two(a, It(FAKE, 0, 64, FAKE, 2, FAKE, FAKE, FAKE, FAKE)), 2, None) == 2
+    assert f(two(a, It(FAKE, 8, 64, FAKE, 65, FAKE, FAKE, FAKE, FAKE)), 2, None) == 3
+    assert f(two(It(FAKE, 8, 64, None, 2, FAKE, FAKE, FAKE, FAKE), a), 2, None) == 1
+    assert "item 0" in _err(lib)
+    assert f(two(a, It(FAKE + 8, 8, 64, FAKE, 2, FAKE, FAKE, FAKE, FAKE)), 2, None) == 4
+    assert f(two(a, It(FAKE, 8, 64, FAKE, 2, FAKE, FAKE + 1, FAKE, FAKE)), 2, None) == 4
+
+
 def test_pack_search_validation(lib):
     f = lib.owq_pack_search
     assert f(None, 8, 64, FAKE, 2, None, FAKE, FAKE, FAKE, FAKE, None) == 1

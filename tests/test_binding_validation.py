@@ -55,6 +55,22 @@ def test_calibrate_batched_checks_shapes():
     _host_only(owq.calibrate_batched, [W, W], [X, X])
 
 
+def test_pack_batched_checks_shapes():
+    W = torch.zeros((N, K), dtype=torch.float16)
+    ix = torch.arange(k, dtype=torch.int32)
+    with pytest.raises(ValueError, match="one weak_idx"):
+        owq.pack_batched([W, W], [ix])
+    with pytest.raises(ValueError, match=r"\[1\] K = 40"):
+        owq.pack_batched([W, torch.zeros((N, 40), dtype=torch.float16)], [ix, ix])
+    with pytest.raises(TypeError, match=r"\[0\] weak_idx must be torch.int32"):
+        owq.pack_batched([W, W], [ix.long(), ix])
+    bad = _layer()
+    bad["scales"] = torch.zeros(N + 1, dtype=torch.float16)
+    with pytest.raises(ValueError, match=r"\[1\] out\['scales'\]"):
+        owq.pack_batched([W, W], [ix, ix], outs=[_layer(), bad])
+    _host_only(owq.pack_batched, [W, W], [ix, ix])
+
+
 def test_select_checks_k_and_out():
     s = torch.zeros(K, dtype=torch.float64)
     with pytest.raises(ValueError, match="outside"):

@@ -168,6 +168,34 @@ def test_calibrate_batched_matches_single(owq):
         np.testing.assert_allclose(host(single[i][1]), o_score, rtol=1e-12, atol=1e-300, err_msg=str(shapes[i]))
 
 
+def test_pack_batched_matches_single(owq):
+    """owq_pack_batched puts the linears of one kernel form in one launch: every
+    packed array equals its own owq_pack call bit for bit (and the oracle's),
+    over all the kernel forms (a wave per row with 1-3 groups per lane, a block
+    per row with 1-8 groups per thread), mixed in one batch, k = 0 included."""
+    import torch
+    import oracle
+    shapes = [(1, 32, 0), (37, 4096, 5), (300, 4128, 17), (4, 6144, 64), (130, 8192, 63), (9, 11008, 86),
+              (5, 32768, 3), (3, 65536, 5), (4100, 4096, 32), (64, 640, 0)]
+    rng = np.random.default_rng(23)
+    Ws, idxs = [], []
+    for N, K, k in shapes:
+        Ws.append(_tiny_rows(synth.random_layer(rng, N, K, 0.02)))
+        idxs.append(np.sort(rng.choice(K, k, replace=False)).astype(np.int32))
+    Wd = [dev(W) for W in Ws]
+    Id = [dev(ix) for ix in idxs]
+    single = [owq.pack(W, ix) for W, ix in zip(Wd, Id)]
+    for sel in (list(range(len(shapes))), [8, 1, 8], [3]):
+        print(f"pack_batched: {[shapes[i] for i in sel]}", flush=True)
+        got = owq.pack_batched([Wd[i] for i in sel], [Id[i] for i in sel])
+        torch.cuda.synchronize()
+        for i, g in zip(sel, got):
+            for name in ("qcodes", "scales", "zeros", "w_weak"):
+                assert host(g[name]).tobytes() == host(single[i][name]).tobytes(), (shapes[i], name)
+    for i in (1, 2, 5):
+        check_pack(single[i], oracle.pack(Ws[i], idxs[i]))
+
+
 def test_select_batched_matches_single(owq):
     """owq_select_weak_batched over selections of every block shape (and k = 0,
     k = K, K above 16384) gives exactly the single calls' and the oracle's
