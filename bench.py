@@ -310,6 +310,29 @@ def main():
             ts.append(a.elapsed_time(b) / 1e3)
         return float(np.median(ts))
 
+    def graph_time(fn, reps=5):
+        """Device time of fn() (ROTATE layers' calls) replayed from a HIP graph."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = E(), E()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) / 1e3 / (reps * ROTATE)
+
+
     # the layer's calibration, with its arguments marshalled once
     cal_call = owq.PreparedCalibrate(W, X)
 
@@ -679,25 +702,29 @@ def main():
         # columns, the weak columns added after the 3-bit product; 3 launches per
         # linear, compared with the one launch per layer of the latency form
         print("bench: storage-favoured decode", file=sys.stderr, flush=True)
-        sto = [owq.pack_storage(W[li], slots[0][li]["weak_idx"]) for li in range(L)]
-        wss = [torch.empty(owq.linear_storage_workspace_bytes(s.K, s.k, 1), dtype=torch.uint8, device=dev)
-               for s in specs]
-        for li in range(L):
-            owq.linear_storage(sto[li], xd[li], yd[li], wss[li])
-        reps = 20
-        a, b = E(), E()
-        a.record()
-        for _ in range(reps):
-            for li in range(L):
-                owq.linear_storage(sto[li], xd[li], yd[li], wss[li])
-        b.record()
-        torch.cuda.synchronize()
-        t = a.elapsed_time(b) / 1e3 / reps
+        # ROTATE copies in the storage form, the 7 linears of a copy in one
+        # owq_linear_storage_batched call; device time from a HIP graph
+        sto = [[owq.pack_storage(W[li], slots[r][li]["weak_idx"]) for li in range(L)] for r in range(ROTATE)]
+        wss = torch.empty(owq.linear_storage_batched_workspace_bytes(sto[0], 1), dtype=torch.uint8, device=dev)
+
+        def storage_batched():
+            for r in range(ROTATE):
+                owq.linear_storage_batched(sto[r], xd, yd, workspace=wss)
+
+        def storage_per_linear():
+            for r in range(ROTATE):
+                for li in range(L):
+                    owq.linear_storage(sto[r][li], xd[li], yd[li], wss)
+
+        t = graph_time(storage_batched)
+        t_one = graph_time(storage_per_linear)
         sto_bytes = sum(3 * s.N * (s.K - s.k) // 8 + 3 * s.N + 2 * s.N * s.k + 2 * s.K for s in specs)
         result["kernels"]["decode_storage_form"] = dict(
-            hbm_entry(sto_bytes, t, "storage-favoured form at M=1: x gathered at the dense columns, k_gemv<1> over "
-                                    "K - k columns, weak columns added; 3 launches per linear, 7 linears (one "
-                                    "copy, so partly cache-resident)"),
+            hbm_entry(sto_bytes, t, "storage-favoured form at M=1: owq_linear_storage_batched over the 7 linears "
+                                    "(x gathered at the dense columns, k_gemv<1> over K - k columns, weak columns "
+                                    "added: 3 launches per layer), 8 copies rotated, replayed from a HIP graph "
+                                    "(device time)"),
+            us_one_call_per_linear_graph=round(t_one * 1e6, 2),
             us_latency_form=round(dec_s * 1e6, 2))
         del sto, wss
 
@@ -707,28 +734,6 @@ def main():
         print("bench: weak-column-tuning backward", file=sys.stderr, flush=True)
         bw = {}
         bws = torch.empty(owq.linear_backward_batched_workspace_bytes(slots[0]), dtype=torch.uint8, device=dev)
-        def graph_time(fn, reps=5):
-            """Device time of fn() (ROTATE layers' calls) replayed from a HIP graph."""
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                fn()
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fn()
-            g.replay()
-            torch.cuda.synchronize()
-            a, b = E(), E()
-            a.record()
-            for _ in range(reps):
-                g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            del g
-            return a.elapsed_time(b) / 1e3 / (reps * ROTATE)
-
         for M in (1, 16):
             dys = [torch.randn((M, s.N), device=dev).to(torch.float16) for s in specs]
             xs_b = [x1[li][:M] for li in range(L)]

@@ -346,6 +346,25 @@ owq_status owq_linear_storage(const owq_layer* L, const uint16_t* x, int64_t M,
                               uint16_t* y, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Bytes of device workspace owq_linear_storage_batched needs for these layers
+ * at M tokens: their owq_linear_storage_workspace_bytes, each rounded up to 256
+ * bytes (0 for invalid sizes or count outside 1..64). */
+size_t owq_linear_storage_batched_workspace_bytes(const owq_layer* Ls, int32_t count, int64_t M);
+
+/* owq_linear_storage for `count` layers at the same M (e.g. the 7 linears of a
+ * decoder layer), bit for bit the same outputs ([PL] "Storage Methods", paper
+ * appendix section 2, as owq_linear_storage), in three launches instead of three
+ * per layer: the dense-column gathers of every layer, the dense products (one
+ * decode launch when M is in its range), the weak columns of every layer. Ls,
+ * xs, ys: HOST arrays [count] (structs and device pointers). workspace: >=
+ * owq_linear_storage_batched_workspace_bytes(Ls, count, M) bytes, 256-byte
+ * aligned; layer l's part starts at the sum of the earlier layers' rounded
+ * sizes. Returns OWQ_ERR_UNSUPPORTED unless 1 <= count <= 64; other errors as
+ * owq_linear_storage, reported with the layer's index. */
+owq_status owq_linear_storage_batched(const owq_layer* Ls, const uint16_t* const* xs, uint16_t* const* ys,
+                                      int32_t count, int64_t M, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
 /* ------------------------------------------ backward (weak-column tuning) --- */
 
 /* Bytes of device workspace owq_linear_backward needs to produce dx (0 for

@@ -467,6 +467,55 @@ owq_status owq_linear_storage(const owq_layer* L, const uint16_t* x, int64_t M, 
                       "owq_linear_storage launch");
 }
 
+size_t owq_linear_storage_batched_workspace_bytes(const owq_layer* Ls, int32_t count, int64_t M)
+{
+    if (!Ls || count < 1 || count > 64)
+        return 0;
+    size_t total = 0;
+    for (int32_t l = 0; l < count; l++) {
+        const size_t b = owq_linear_storage_workspace_bytes(Ls[l].K, Ls[l].k, M);
+        if (b == 0)
+            return 0;
+        total += (b + 255) & ~(size_t)255;
+    }
+    return total;
+}
+
+owq_status owq_linear_storage_batched(const owq_layer* Ls, const uint16_t* const* xs, uint16_t* const* ys,
+                                      int32_t count, int64_t M, void* workspace, size_t workspace_bytes,
+                                      void* stream)
+{
+    if (!Ls || !xs || !ys)
+        return fail(OWQ_ERR_NULL, "Ls, xs and ys must be non-NULL");
+    if (count < 1 || count > 64)
+        return fail(OWQ_ERR_UNSUPPORTED, "count = %d: need 1 <= count <= 64", count);
+    if (!workspace)
+        return fail(OWQ_ERR_NULL, "workspace must be non-NULL");
+    if (!aligned(workspace, 256))
+        return fail(OWQ_ERR_ALIGN, "misaligned workspace (256 B)");
+    std::vector<owq::LinearDesc> d((size_t)count);
+    std::vector<void*> ws((size_t)count);
+    size_t off = 0;
+    for (int32_t l = 0; l < count; l++) {
+        owq_layer L = Ls[l];
+        if (L.k == L.K && L.K >= 32 && !L.qcodes)  // every column weak: no codes are stored
+            L.qcodes = reinterpret_cast<const uint32_t*>(L.scales);
+        owq_status st = check_layer(&L, M, xs[l], ys[l]);
+        if (st != OWQ_OK)
+            return fail_at(st, "layer", l);
+        st = check_idx_on_host(L.weak_idx, L.k, L.K, (hipStream_t)stream);
+        if (st != OWQ_OK)
+            return fail_at(st, "layer", l);
+        d[l] = desc_of(&L, xs[l], ys[l]);
+        ws[l] = static_cast<char*>(workspace) + off;
+        off += (owq::storage_workspace_bytes(L.K, L.k, M) + 255) & ~(size_t)255;
+    }
+    if (workspace_bytes < off)
+        return fail(OWQ_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, off);
+    return hip_status(owq::launch_linear_storage_batched(d.data(), count, M, ws.data(), (hipStream_t)stream),
+                      "owq_linear_storage_batched launch");
+}
+
 size_t owq_pack_optq_workspace_bytes(int64_t N, int64_t K, int32_t k)
 {
     if (N < 1 || N > INT32_MAX || K < 32 || K > kMaxK || K % 32 != 0 || k < 0 || k > K)

@@ -117,6 +117,9 @@ hipError_t launch_pack_storage(const uint16_t* W, int64_t N, int64_t K, const in
                                uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s);
 // d: the layer with K its full column count and q its storage-form codes.
 hipError_t launch_linear_storage(const LinearDesc& d, int64_t M, void* ws, hipStream_t s);
+// `count` layers: three launches per kGemvMaxLayers layers (gathers, dense
+// products, weak columns); ws[l]: layer l's workspace
+hipError_t launch_linear_storage_batched(const LinearDesc* d, int count, int64_t M, void* const* ws, hipStream_t s);
 
 // ------------------------------------------ backward (weak-column tuning) --
 struct BwdPlan {

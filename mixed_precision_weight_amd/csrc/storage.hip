@@ -19,6 +19,9 @@
 // does not decrease with c), found by binary search.
 //
 // Built with -ffp-contract=off: the quantiser steps are single IEEE operations.
+#include <algorithm>
+#include <vector>
+
 #include "owq_device.h"
 #include "owq_launch.h"
 
@@ -131,38 +134,69 @@ __global__ __launch_bounds__(256) void k_pack_storage(const uint16_t* __restrict
     }
 }
 
-// x_d[m][p] = x[m][d_p] for p < K - k, 0 up to Kd32. Thread p (grid x) finds d_p
-// once and walks blockDim.y-strided tokens.
-__global__ __launch_bounds__(256) void k_gather_dense(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                      const int32_t* __restrict__ idx, int32_t k, int64_t Kd32,
-                                                      uint16_t* __restrict__ xd)
+// Several layers' gathers and weak additions in one launch each: blocks
+// [b0[l], b0[l+1]) of grid x belong to layer l, grid y walks the tokens.
+struct StorageStep {
+    const uint16_t* x;
+    const int32_t* idx;
+    const uint16_t* ww;
+    uint16_t* xd;  // gather: the layer's x_d
+    uint16_t* y;   // weak addition: the layer's y
+    int64_t K, Kd32, N;
+    int32_t k, add;
+};
+
+struct StorageBatch {
+    StorageStep L[kGemvMaxLayers];
+    int32_t b0[kGemvMaxLayers + 1];
+    int32_t count;
+};
+
+__device__ __forceinline__ int storage_layer_of(const StorageBatch& b)
 {
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (p >= Kd32)
-        return;
-    const int64_t Kd = K - k;
-    const int64_t j = p < Kd ? p + weak_before_dense(idx, k, (int)p) : -1;
-    for (int64_t m = blockIdx.y; m < M; m += gridDim.y)
-        xd[m * Kd32 + p] = j >= 0 ? x[m * K + j] : (uint16_t)0;
+    int l = 0;
+    while (l + 1 < b.count && (int)blockIdx.x >= b.b0[l + 1])
+        l++;
+    return l;
 }
 
-// y[m][i] = fp16(y_in + sum_c w_weak[i][c] x[m][idx_c]), y_in = y[m][i] (fp16) or 0
-__global__ __launch_bounds__(256) void k_weak_add(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                  const int32_t* __restrict__ idx, int32_t k,
-                                                  const uint16_t* __restrict__ ww, int64_t N, int add,
-                                                  uint16_t* __restrict__ y)
+__global__ __launch_bounds__(256) void k_gather_dense_batched(const StorageBatch b, int64_t M)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= N)
+    const int l = storage_layer_of(b);
+    const StorageStep& L = b.L[l];
+    const int64_t p = (int64_t)(blockIdx.x - b.b0[l]) * 256 + threadIdx.x;
+    if (p >= L.Kd32)
+        return;
+    const int64_t Kd = L.K - L.k;
+    const int64_t j = p < Kd ? p + weak_before_dense(L.idx, L.k, (int)p) : -1;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y)
+        L.xd[m * L.Kd32 + p] = j >= 0 ? L.x[m * L.K + j] : (uint16_t)0;
+}
+
+// y[m][i] = fp16(y_in + sum_c w_weak[i][c] x[m][idx_c]) (y_in = y[m][i] or 0): a
+// wave per row (4 rows per block); lane l takes the weak columns l, l + 64, ...
+// (the row's weights read contiguously), the lane sums are added by a fixed
+// butterfly, then y_in.
+__global__ __launch_bounds__(256) void k_weak_add_batched(const StorageBatch b, int64_t M)
+{
+    const int l = storage_layer_of(b);
+    const StorageStep& L = b.L[l];
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)(blockIdx.x - b.b0[l]) * 4 + (threadIdx.x >> 6);
+    if (i >= L.N)  // wave-uniform
         return;
     for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
-        float acc = add ? h2f(y[m * N + i]) : 0.0f;
-        for (int c = 0; c < k; c++) {
-            int32_t j = idx[c];
-            j = (j >= 0 && j < K) ? j : 0;
-            acc = __builtin_fmaf(h2f(ww[i * k + c]), h2f(x[m * K + j]), acc);
+        float acc = 0.0f;
+        for (int c = lane; c < L.k; c += 64) {
+            int32_t j = L.idx[c];
+            j = (j >= 0 && j < L.K) ? j : 0;
+            acc = __builtin_fmaf(h2f(L.ww[i * L.k + c]), h2f(L.x[m * L.K + j]), acc);
         }
-        y[m * N + i] = f2h(acc);
+        acc = wave_sum(acc);
+        if (lane == 0) {
+            const float yin = L.add ? h2f(L.y[m * L.N + i]) : 0.0f;
+            L.y[m * L.N + i] = f2h(yin + acc);
+        }
     }
 }
 
@@ -187,33 +221,81 @@ hipError_t launch_pack_storage(const uint16_t* W, int64_t N, int64_t K, const in
 
 hipError_t launch_linear_storage(const LinearDesc& d, int64_t M, void* ws, hipStream_t s)
 {
-    const int64_t Kd32 = storage_dense_cols32(d.K, d.k);
-    hipError_t e = hipSuccess;
-    if (Kd32 > 0) {
-        uint16_t* xd = static_cast<uint16_t*>(ws);
-        const unsigned gy = (unsigned)(M < 64 ? M : 64);
-        hipLaunchKernelGGL(k_gather_dense, dim3((unsigned)((Kd32 + 255) / 256), gy), dim3(256), 0, s, d.x, M, d.K,
-                           d.idx, d.k, Kd32, xd);
-        e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-        LinearDesc dd = d;  // the 3-bit codes against x_d as a layer of Kd32 columns, no weak columns
-        dd.x = xd;
-        dd.K = Kd32;
-        dd.k = 0;
-        dd.idx = nullptr;
-        dd.ww = nullptr;
-        e = launch_linear_any(dd, M, s);
-        if (e != hipSuccess)
-            return e;
+    return launch_linear_storage_batched(&d, 1, M, &ws, s);
+}
+
+hipError_t launch_linear_storage_batched(const LinearDesc* d, int count, int64_t M, void* const* ws, hipStream_t s)
+{
+    for (int l0 = 0; l0 < count; l0 += kGemvMaxLayers) {
+        const int n = std::min(count - l0, kGemvMaxLayers);
+        const LinearDesc* dl = d + l0;
+        // 1. x at the dense columns of every layer
+        StorageBatch g{};
+        std::vector<LinearDesc> dense;
+        for (int i = 0; i < n; i++) {
+            const int64_t Kd32 = storage_dense_cols32(dl[i].K, dl[i].k);
+            if (Kd32 == 0)
+                continue;
+            StorageStep& L = g.L[g.count];
+            L = StorageStep{dl[i].x, dl[i].idx, nullptr, static_cast<uint16_t*>(ws[l0 + i]), nullptr, dl[i].K, Kd32,
+                            0, dl[i].k, 0};
+            g.b0[0] = 0;
+            g.b0[g.count + 1] = g.b0[g.count] + (int32_t)((Kd32 + 255) / 256);
+            g.count++;
+            LinearDesc dd = dl[i];  // the codes against x_d as a layer of Kd32 columns, no weak columns
+            dd.x = L.xd;
+            dd.K = Kd32;
+            dd.k = 0;
+            dd.idx = nullptr;
+            dd.ww = nullptr;
+            dense.push_back(dd);
+        }
+        hipError_t e = hipSuccess;
+        if (g.count > 0) {
+            hipLaunchKernelGGL(k_gather_dense_batched, dim3((unsigned)g.b0[g.count], (unsigned)std::min<int64_t>(M, 64)),
+                               dim3(256), 0, s, g, M);
+            e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+            // 2. the dense products, in one decode launch when every layer fits it
+            bool one = M <= kMfvMaxM && M < gemm_min_m();  // the kernels owq_linear_storage would use
+            const bool mat = decode_on_matrix_cores(M);
+            for (const LinearDesc& dd : dense)
+                one = one && (mat ? mfv_fits(M, dd.K) : gemv_fits(M, dd.K));
+            if (one) {
+                e = mat ? launch_mfv(dense.data(), (int)dense.size(), (int)M, s)
+                        : launch_gemv(dense.data(), (int)dense.size(), (int)M, s);
+            } else {
+                for (const LinearDesc& dd : dense)
+                    if (e == hipSuccess)
+                        e = launch_linear_any(dd, M, s);
+            }
+            if (e != hipSuccess)
+                return e;
+        }
+        // 3. the weak columns of every layer (a layer with no dense columns gets
+        // its whole product here)
+        StorageBatch w{};
+        for (int i = 0; i < n; i++) {
+            const int64_t Kd32 = storage_dense_cols32(dl[i].K, dl[i].k);
+            if (dl[i].k == 0 && Kd32 > 0)
+                continue;
+            StorageStep& L = w.L[w.count];
+            L = StorageStep{dl[i].x, dl[i].idx, dl[i].ww, nullptr, dl[i].y, dl[i].K, Kd32, dl[i].N, dl[i].k,
+                            Kd32 > 0 ? 1 : 0};
+            w.b0[0] = 0;
+            w.b0[w.count + 1] = w.b0[w.count] + (int32_t)((dl[i].N + 3) / 4);
+            w.count++;
+        }
+        if (w.count > 0) {
+            hipLaunchKernelGGL(k_weak_add_batched, dim3((unsigned)w.b0[w.count], (unsigned)std::min<int64_t>(M, 256)),
+                               dim3(256), 0, s, w, M);
+            e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
     }
-    if (d.k > 0 || Kd32 == 0) {
-        const unsigned gy = (unsigned)(M < 256 ? M : 256);
-        hipLaunchKernelGGL(k_weak_add, dim3((unsigned)((d.N + 255) / 256), gy), dim3(256), 0, s, d.x, M, d.K,
-                           d.idx, d.k, d.ww, d.N, Kd32 > 0 ? 1 : 0, d.y);
-        e = hipGetLastError();
-    }
-    return e;
+    return hipSuccess;
 }
 
 }  // namespace owq

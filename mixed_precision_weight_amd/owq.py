@@ -60,6 +60,9 @@ EXPORTS = {
     "owq_pack_storage": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]),
     "owq_linear_storage_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I64]),
     "owq_linear_storage": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "owq_linear_storage_batched_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(OwqLayer), _I32, _I64]),
+    "owq_linear_storage_batched": (ctypes.c_int, [ctypes.POINTER(OwqLayer), ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                                  _I32, _I64, _P, ctypes.c_size_t, _P]),
     "owq_linear_backward_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
     "owq_linear_backward": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _P, _I64, _P, _P, _P, ctypes.c_size_t,
                                            _P]),
@@ -490,21 +493,29 @@ def linear_storage_workspace_bytes(K: int, k: int, M: int) -> int:
     return int(lib().owq_linear_storage_workspace_bytes(K, k, M))
 
 
+def _storage_args(layer: dict, x: torch.Tensor, y, where: str = ""):
+    """Checked shapes of one storage-form product: (OwqLayer, N, K, k, M)."""
+    if "K" not in layer:
+        raise ValueError(f"{where}layer lacks 'K' (the full column count of the storage-favoured form)")
+    K = int(layer["K"])
+    q = _meta(layer["qcodes"], torch.int32, f"{where}qcodes")
+    idx = _meta(layer["weak_idx"], torch.int32, f"{where}weak_idx")
+    N, k = q.shape[0], idx.numel()
+    if q.dim() != 3 or tuple(q.shape[1:]) != ((K - k + 31) // 32, 3) or idx.dim() != 1:
+        raise ValueError(f"{where}qcodes {tuple(q.shape)} / weak_idx {tuple(idx.shape)} do not fit K = {K}")
+    for name, (shape, dt) in _pack_out_shapes(N, K, k).items():
+        if name != "qcodes":
+            _meta(layer[name], dt, f"{where}{name}", shape)
+    M = _xy_shapes(N, K, x, y, tag=where)
+    L = OwqLayer(N, K, k, 3, q.data_ptr() if q.numel() else None, layer["scales"].data_ptr(),
+                 layer["zeros"].data_ptr(), idx.data_ptr() if k else None, layer["w_weak"].data_ptr() if k else None)
+    return L, N, K, k, M
+
+
 def linear_storage(layer: dict, x: torch.Tensor, y: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """y = x W^T for a layer in the storage-favoured form (owq_linear_storage)."""
-    if "K" not in layer:
-        raise ValueError("layer lacks 'K' (the full column count of the storage-favoured form)")
-    K = int(layer["K"])
-    q = _meta(layer["qcodes"], torch.int32, "qcodes")
-    idx = _meta(layer["weak_idx"], torch.int32, "weak_idx")
-    N, k = q.shape[0], idx.numel()
-    if q.dim() != 3 or tuple(q.shape[1:]) != ((K - k + 31) // 32, 3) or idx.dim() != 1:
-        raise ValueError(f"qcodes {tuple(q.shape)} / weak_idx {tuple(idx.shape)} do not fit K = {K}")
-    for name, (shape, dt) in _pack_out_shapes(N, K, k).items():
-        if name != "qcodes":
-            _meta(layer[name], dt, name, shape)
-    M = _xy_shapes(N, K, x, y)
+    L, N, K, k, M = _storage_args(layer, x, y)
     if workspace is not None:
         _meta(workspace, torch.uint8, "workspace")
     _on_device(("x", x), ("y", y), ("workspace", workspace), *_layer_named(layer))
@@ -512,11 +523,53 @@ def linear_storage(layer: dict, x: torch.Tensor, y: torch.Tensor | None = None,
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     if workspace is None:
         workspace = torch.empty(linear_storage_workspace_bytes(K, k, M), dtype=torch.uint8, device=x.device)
-    L = OwqLayer(N, K, k, 3, q.data_ptr() if q.numel() else None, layer["scales"].data_ptr(),
-                 layer["zeros"].data_ptr(), idx.data_ptr() if k else None, layer["w_weak"].data_ptr() if k else None)
     _check(lib().owq_linear_storage(ctypes.byref(L), _ptr(x), M, _ptr(y), _ptr(workspace), _nbytes(workspace),
                                     _stream(stream)), "owq_linear_storage")
     return y
+
+
+def linear_storage_batched_workspace_bytes(layers: list, M: int) -> int:
+    """Workspace of linear_storage_batched for these storage-form layers at M tokens."""
+    n = len(layers)
+    Ls = (OwqLayer * max(n, 1))()
+    for i, l in enumerate(layers):
+        q, idx = l["qcodes"], l["weak_idx"]
+        Ls[i] = OwqLayer(q.shape[0], int(l["K"]), idx.numel(), 3, None, None, None, None, None)
+    return int(lib().owq_linear_storage_batched_workspace_bytes(Ls, n, M))
+
+
+def linear_storage_batched(layers: list, xs: list, ys: list | None = None, workspace: torch.Tensor | None = None,
+                           stream=None) -> list:
+    """linear_storage() of several layers at one M (owq_linear_storage_batched:
+    three launches for all of them); returns one y per layer (ys[i] if given)."""
+    n = len(layers)
+    if n < 1 or len(xs) != n or (ys is not None and len(ys) != n):
+        raise ValueError(f"need one x (and y) per layer: {n} layers, {len(xs)} x"
+                         + ("" if ys is None else f", {len(ys)} y"))
+    args = [_storage_args(l, x, None if ys is None else ys[i], f"[{i}] ")
+            for i, (l, x) in enumerate(zip(layers, xs))]
+    Ms = {a[4] for a in args}
+    if len(Ms) != 1:
+        raise ValueError(f"every x must have the same M, got {sorted(Ms)}")
+    M = Ms.pop()
+    if workspace is not None:
+        _meta(workspace, torch.uint8, "workspace")
+    named = [("workspace", workspace)]
+    for i, (l, x) in enumerate(zip(layers, xs)):
+        named += [(f"[{i}] x", x), (f"[{i}] y", None if ys is None else ys[i])]
+        named += [(f"[{i}] {nm}", t) for nm, t in _layer_named(l)]
+    _on_device(*named)
+    if ys is None:
+        ys = [torch.empty((M, a[1]), dtype=torch.float16, device=xs[0].device) for a in args]
+    Ls = (OwqLayer * n)(*[a[0] for a in args])
+    nbytes = int(lib().owq_linear_storage_batched_workspace_bytes(Ls, n, M))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=xs[0].device)
+    xp = (_P * n)(*[x.data_ptr() for x in xs])
+    yp = (_P * n)(*[y.data_ptr() for y in ys])
+    _check(lib().owq_linear_storage_batched(Ls, xp, yp, n, M, _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "owq_linear_storage_batched")
+    return ys
 
 
 # ---------------------------------------------------------------------- linear

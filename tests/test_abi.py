@@ -190,6 +190,30 @@ def test_linear_storage_validation(lib):
     assert f(_layer(owq, K=48), FAKE, 3, FAKE, FAKE, ws, None) == 2
 
 
+def test_linear_storage_batched_validation(lib):
+    from mixed_precision_weight_amd import owq
+    P = ctypes.c_void_p
+    Ls = (owq.OwqLayer * 2)(_layer(owq), _layer(owq, N=16))
+    per = [lib.owq_linear_storage_workspace_bytes(64, 2, 3)] * 2
+    ws = lib.owq_linear_storage_batched_workspace_bytes(Ls, 2, 3)
+    assert ws == sum((b + 255) // 256 * 256 for b in per)
+    assert lib.owq_linear_storage_batched_workspace_bytes(Ls, 0, 3) == 0
+    assert lib.owq_linear_storage_batched_workspace_bytes(None, 2, 3) == 0
+    f = lib.owq_linear_storage_batched
+    two = lambda a, b: (P * 2)(a, b)
+    xs, ys = two(FAKE, FAKE), two(FAKE, FAKE)
+    assert f(None, xs, ys, 2, 3, FAKE, ws, None) == 1
+    assert f(Ls, None, ys, 2, 3, FAKE, ws, None) == 1
+    assert f(Ls, xs, ys, 0, 3, FAKE, ws, None) == 5
+    assert f(Ls, xs, ys, 65, 3, FAKE, ws, None) == 5
+    assert f(Ls, xs, ys, 2, 3, None, ws, None) == 1
+    assert f(Ls, xs, ys, 2, 3, FAKE + 16, ws, None) == 4
+    assert f(Ls, xs, ys, 2, 3, FAKE, ws - 1, None) == 6
+    assert f(Ls, two(FAKE, None), ys, 2, 3, FAKE, ws, None) == 1
+    assert "layer 1" in _err(lib)
+    assert f((owq.OwqLayer * 2)(_layer(owq), _layer(owq, K=48)), xs, ys, 2, 3, FAKE, ws, None) == 2
+
+
 def test_pack_optq_validation(lib):
     f = lib.owq_pack_optq
     ws = lib.owq_pack_optq_workspace_bytes(8, 64, 2)

@@ -71,6 +71,20 @@ def test_pack_batched_checks_shapes():
     _host_only(owq.pack_batched, [W, W], [ix, ix])
 
 
+def test_linear_storage_batched_checks_shapes():
+    L = _layer()
+    L["qcodes"] = torch.zeros((N, (K - k + 31) // 32, 3), dtype=torch.int32)
+    L["K"] = K
+    x = torch.zeros((2, K), dtype=torch.float16)
+    with pytest.raises(ValueError, match="one x"):
+        owq.linear_storage_batched([L, L], [x])
+    with pytest.raises(ValueError, match=r"\[1\] x has"):
+        owq.linear_storage_batched([L, L], [x, torch.zeros((2, K - 32), dtype=torch.float16)])
+    with pytest.raises(ValueError, match="same M"):
+        owq.linear_storage_batched([L, L], [x, torch.zeros((3, K), dtype=torch.float16)])
+    _host_only(owq.linear_storage_batched, [L, L], [x, x])
+
+
 def test_select_checks_k_and_out():
     s = torch.zeros(K, dtype=torch.float64)
     with pytest.raises(ValueError, match="outside"):

@@ -86,3 +86,27 @@ def test_edge_shapes(owq, N, K, k, Ms):
     spec = synth.LayerSpec("edge", N, K, k, 0.02, max(1, K // 200), 20.0)
     x = _quiet_columns(synth.activations(spec, N + K + 3, max(Ms)))
     _run(owq, W, idx, [x[:m] for m in Ms], "edge")
+
+
+def test_batched_matches_per_layer(owq):
+    """owq_linear_storage_batched (three launches for all the layers) gives every
+    layer's owq_linear_storage output bit for bit: layers of several K, one with
+    no weak column and one with every column weak, at decode M (vector and
+    matrix-core kernels, one launch for all) and at a prefill M (per-layer GEMM)."""
+    import torch
+    shapes = [(37, 4096, 32), (300, 4128, 17), (5, 96, 0), (7, 64, 64), (64, 11008, 86), (1, 32, 1)]
+    rng = np.random.default_rng(31)
+    layers = []
+    for N, K, k in shapes:
+        W = _tiny_rows(synth.random_layer(rng, N, K, 0.02))
+        idx = np.sort(rng.choice(K, k, replace=False)).astype(np.int32)
+        layers.append(owq.pack_storage(dev(W), dev(idx)))
+    for M in (1, 2, 5, 16, 40):
+        print(f"storage batched: M={M}", flush=True)
+        xs = [dev(_quiet_columns(synth.activations(synth.LayerSpec("b", N, K, k, 0.02, max(1, K // 200), 20.0),
+                                                   N + K + M, M))) for N, K, k in shapes]
+        single = [owq.linear_storage(l, x) for l, x in zip(layers, xs)]
+        got = owq.linear_storage_batched(layers, xs)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            assert host(got[i]).tobytes() == host(single[i]).tobytes(), (M, shapes[i])
