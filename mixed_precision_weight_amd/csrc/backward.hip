@@ -43,6 +43,11 @@ namespace {
 constexpr int kBwdMaxMT = 4;      // tokens per dx pass
 constexpr int kTileGroups = 64;   // groups per column tile (one per lane)
 constexpr int kWeakTile = 32;     // weak columns per block in the weak kernels
+// rows per slice at least: every slice writes (and the finalize reads) 4 MT K
+// bytes of partial sums. 64 against 32 rows: 57.5 -> 49.6 us for the 7 LLaMA-7B
+// linears at M = 1, 115 -> 92 us at M = 4 (128: 48.0 and 97 us); loading a
+// step's rows while the previous step is decoded did not help (56 us at M = 1)
+constexpr int kBwdMinRows = 64;
 // rows a wave loads before decoding: 8 at up to 2 tokens, else 4 (registers)
 template <int MT>
 constexpr int rows_in_flight() { return MT <= 2 ? 8 : 4; }
@@ -132,27 +137,37 @@ __device__ __forceinline__ void bwd_dense(const BwdArgs& a, int tile, int s, flo
 
     // wave w takes rows r0 + w + 4 t; kRowsInFlight of them per step, rows past
     // the slice load its last row and take a zero coefficient (adds exact zeros)
-    for (int rb = r0 + wave; rb < r1; rb += 4 * kRowsInFlight) {
-        // every load of the step unconditional (rows clamped to the slice): a
-        // load under a branch would be waited for at the branch's end, before
-        // the next row's loads are issued
+    struct Rows {
         uint32_t w[kRowsInFlight][3];
         uint16_t sh[kRowsInFlight], dh[kRowsInFlight][MT];
         uint32_t z[kRowsInFlight];
+    };
+    // every load of a step unconditional (rows clamped to the slice): a load
+    // under a branch would be waited for at the branch's end, before the next
+    // row's loads are issued
+    auto load_rows = [&](int rb, Rows& R) {
 #pragma unroll
         for (int u = 0; u < kRowsInFlight; u++) {
             const int rr = rb + 4 * u;
             const int r = rr < r1 ? rr : r1 - 1;
             const uint32_t* src = a.q + ((int64_t)r * G + gc) * 3;
-            w[u][0] = src[0];
-            w[u][1] = src[1];
-            w[u][2] = src[2];
-            sh[u] = a.scales[r];
-            z[u] = a.zeros[r];
+            R.w[u][0] = src[0];
+            R.w[u][1] = src[1];
+            R.w[u][2] = src[2];
+            R.sh[u] = a.scales[r];
+            R.z[u] = a.zeros[r];
 #pragma unroll
             for (int m = 0; m < MT; m++)
-                dh[u][m] = a.dy[(int64_t)m * a.N + r];
+                R.dh[u][m] = a.dy[(int64_t)m * a.N + r];
         }
+    };
+    for (int rb = r0 + wave; rb < r1; rb += 4 * kRowsInFlight) {
+        Rows R;
+        load_rows(rb, R);
+        auto& w = R.w;
+        auto& sh = R.sh;
+        auto& dh = R.dh;
+        auto& z = R.z;
 #pragma unroll
         for (int u = 0; u < kRowsInFlight; u++) {
             const bool live = rb + 4 * u < r1;
@@ -782,11 +797,11 @@ BwdPlan bwd_plan(int64_t N, int64_t K, int32_t k)
 {
     BwdPlan p;
     // enough dense blocks to fill the GPU (512, two per CU) with slices of at
-    // least 32 rows (8 per wave), the partial sums (4 tokens, K columns, fp32 per
+    // least kBwdMinRows rows, the partial sums (4 tokens, K columns, fp32 per
     // slice) within 64 MiB
     const int64_t tiles = (K / 32 + kTileGroups - 1) / kTileGroups;
     int64_t sl = (512 + tiles - 1) / tiles;
-    const int64_t most = (N + 31) / 32;
+    const int64_t most = (N + kBwdMinRows - 1) / kBwdMinRows;
     const int64_t cap = ((int64_t)64 << 20) / (kBwdMaxMT * K * (int64_t)sizeof(float));
     if (sl > most)
         sl = most;
