@@ -142,14 +142,14 @@ def test_calibrate_batched_matches_single(owq):
     import torch
     import oracle
     shapes = [(1, 32, 1), (37, 4128, 24), (300, 96, 77), (5, 11008, 9), (64, 640, 300), (130, 8192, 16),
-              (513, 2048, 48)]
+              (513, 2048, 48), (3, 65536, 40), (40, 24576, 33)]  # K > 32768: the two-pass form
     rng = np.random.default_rng(11)
     Ws = [_tiny_rows(synth.random_layer(rng, N, K, 0.02)) for N, K, _ in shapes]
     Xs = [synth.calibration(synth.LayerSpec("cb", N, K, 1, 0.02, max(1, K // 200), 20.0), N + K, T)
           for N, K, T in shapes]
     Wd, Xd = [dev(W) for W in Ws], [dev(X) for X in Xs]
     single = [owq.calibrate(W, X) for W, X in zip(Wd, Xd)]
-    for n in (1, 2, 7):
+    for n in (1, 2, 7, 9):
         print(f"calibrate_batched: {n} linears", flush=True)
         nbytes = owq.calibrate_batched_workspace_bytes(shapes[:n])
         ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda:0")
@@ -162,7 +162,7 @@ def test_calibrate_batched_matches_single(owq):
             for a, b, c, d, what in zip(got[i], single[i], again[i], prepared.results[i], ("lambda", "score")):
                 assert host(a).tobytes() == host(b).tobytes(), (n, i, shapes[i], what)
                 assert host(c).tobytes() == host(b).tobytes() == host(d).tobytes(), (n, i, shapes[i], what)
-    for i in (0, 1, 2, 6):
+    for i in (0, 1, 2, 6, 7):
         o_lam, o_score = oracle.calibrate_score(Ws[i], Xs[i])
         np.testing.assert_allclose(host(single[i][0]), o_lam, rtol=1e-12, atol=0, err_msg=str(shapes[i]))
         np.testing.assert_allclose(host(single[i][1]), o_score, rtol=1e-12, atol=1e-300, err_msg=str(shapes[i]))
