@@ -34,7 +34,7 @@ hipError_t launch_calibrate(const uint16_t* W, int64_t N, int64_t K, const uint1
 // The library's own calibration workspace on the current device: a file-scope
 // device array of kCalibScratchBytes (256-byte aligned), its address looked up
 // once per device. Returns the HIP error of the lookup, if any.
-constexpr size_t kCalibScratchBytes = (size_t)16 << 20;
+constexpr size_t kCalibScratchBytes = (size_t)64 << 20;
 hipError_t calib_scratch(void** ptr);
 
 // ------------------------------------------------------------------- select --
