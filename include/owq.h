@@ -384,8 +384,10 @@ size_t owq_linear_backward_workspace_bytes(int64_t N, int64_t K, int32_t k);
  * [M][N]; dx (may be NULL) and dw_weak (may be NULL) are outputs. dx is the
  * transposed 3-bit product, summed over row slices in a fixed order (bitwise
  * deterministic): up to 4 tokens on the vector ALUs (exact products), more on
- * the matrix cores 16 tokens per pass (fp32 products; the environment variable
- * OWQ_BACKWARD=vector, read at each call, keeps the vector form). workspace: >=
+ * the matrix cores 16 tokens per pass (exact products: dy times s (q - z) split
+ * into two fp16 values; fp32 products for 32-row steps holding a step above
+ * 9352; the environment variable OWQ_BACKWARD=vector, read at each call, keeps
+ * the vector form). workspace: >=
  * owq_linear_backward_workspace_bytes(N, K, k) bytes, 256-byte aligned, needed
  * only for dx. Errors as owq_linear, plus OWQ_ERR_WORKSPACE. */
 owq_status owq_linear_backward(const owq_layer* L, const uint16_t* x, const uint16_t* dy,

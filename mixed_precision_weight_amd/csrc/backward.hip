@@ -469,24 +469,47 @@ __global__ __launch_bounds__(256) void k_bwd_dx_finalize(const BwdBatch bt)
 // row, so the decoded codes go through LDS: a block (4 waves) owns 256 columns
 // (8 groups) and one slice of rows; per step of 32 rows, thread t decodes group
 // t % 8 of row t / 8 into the LDS tile (exact (q - z) fp16, natural column
-// order) and stores the coefficients s_i dy[m][i] (fp32, exact) of the 32 rows
-// and 16 tokens; then each wave multiplies its 64 columns with
-// v_mfma_f32_16x16x4_f32: A[m][r] = s_i dy[m][i], B[r][j] = (q_ij - z_i), 4 rows
-// per instruction, fp32 products and sums (the products of the vector form are
-// exact, these are rounded once, to fp32: the same 2^-24 per term). The tile is
-// double-buffered (one barrier per step) and the next step's loads are issued
-// before this step's products. The block stores its partial sums P[slice][m][j].
+// order), and the step's dy (fp16, 16 tokens) and steps s_i go to LDS beside it.
+// Each wave then multiplies its 64 columns with v_mfma_f32_16x16x32_f16:
+// A[m][r] = dy[m][i] (exact), B[r][j] = s_i (q_ij - z_i) as the exact sum of two
+// fp16 values B_hi = fp16(s (q - z)) (v_pk_mul_f16) and B_lo = s (q - z) - B_hi
+// (v_pk_fma_f16, exact: s (q - z) is a multiple of s's last bit with at most 14
+// significant bits, so the remainder has at most 3 and lies on fp16's grid, also
+// where it is subnormal), two MFMAs per 32 rows. Every product dy B_hi, dy B_lo
+// is exact in fp32 and only the sums round, as in the vector form. The k index
+// of the MFMA (8 (l / 16) + e for lane l, operand element e) takes the step's
+// row 4 e + l / 16, so the four rows of one B read are consecutive (distinct
+// banks with the padded tile rows); the dy tile is stored in that order.
+// B_hi overflows fp16 only if s (q - z) > 65504, i.e. s > 9352: a step with
+// such a row multiplies in fp32 instead (v_mfma_f32_16x16x4_f32 with
+// A = s_i dy[m][i], exact in fp32, B = q - z), decided for the whole block at
+// the step's barrier. The tile is double-buffered (one barrier per step) and
+// the next step's loads are issued before this step's products. The block
+// stores its partial sums P[slice][m][j].
 constexpr int kMmaCols = 256;  // columns per block
 constexpr int kMmaRows = 32;   // rows per step
 constexpr int kMmaRowBytes = kMmaCols * 2 + 64;  // LDS row of the decoded tile (padded: 144 dwords, the
                                                  // four rows of a B read on distinct banks)
+constexpr uint16_t kMmaMaxStep = 0x7091;  // fp16 9352: 7 s <= 65504
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// position of step row r in the dy and step tiles: row 4 e + c at 8 c + e
+__device__ __forceinline__ int mma_kpos(int r) { return 8 * (r & 3) + (r >> 2); }
+
+__device__ __forceinline__ half8_t mma_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    return __builtin_bit_cast(half8_t, make_uint4(a, b, c, d));
+}
+
 __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s, char* lds)
 {
-    char* const tw = lds;                                 // [2][32][kMmaRowBytes]
-    float* const tc = reinterpret_cast<float*>(lds + 2 * kMmaRows * kMmaRowBytes);  // [2][32][16]
+    char* const tw = lds;  // [2][32][kMmaRowBytes]
+    // [2][16][32] dy (token-major, rows at mma_kpos), then [2][32] steps
+    uint16_t* const tdy = reinterpret_cast<uint16_t*>(lds + 2 * kMmaRows * kMmaRowBytes);
+    uint16_t* const tsv = tdy + 2 * 16 * kMmaRows;
+    // [2] step tags: stage(st) stores st in slot st & 1 if the step needs the fp32 form
+    int* const tbig = reinterpret_cast<int*>(tsv + 2 * kMmaRows);
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int G = a.K >> 5;
@@ -495,8 +518,8 @@ __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s,
     const int r0 = s * a.rows_per_slice, r1 = min(a.N, r0 + a.rows_per_slice);
     const int nsteps = (r1 - r0 + kMmaRows - 1) / kMmaRows;
     const Magic mg = make_magic();
-    // loads of step st: the row's group and, for the coefficient entries e = t
-    // and t + 256 of the 32 x 16 tile (row e / 16, token e % 16), s and dy
+    // loads of step st: the row's group and, for the entries e = t and t + 256
+    // of the 32 x 16 dy tile (row e / 16, token e % 16), s and dy
     uint32_t w0, w1, w2, zb;
     uint32_t sh[2], dh[2];
     auto issue = [&](int st) {
@@ -516,8 +539,8 @@ __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s,
             dh[h] = a.dy[(int64_t)m * a.N + cr];
         }
     };
-    // step st's tile into buffer st & 1: decoded codes and coefficients (rows
-    // past the slice and tokens past the chunk get a zero coefficient)
+    // step st's tiles into buffer st & 1 (rows past the slice and tokens past
+    // the chunk get dy = 0); a live row's step above kMmaMaxStep tags the step
     auto stage = [&](int st) {
         const int buf = st & 1;
         uint32_t p[16];
@@ -528,49 +551,93 @@ __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s,
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++)
             dst[q4 ^ (lg >> 2)] = make_uint4(p[4 * q4], p[4 * q4 + 1], p[4 * q4 + 2], p[4 * q4 + 3]);
+        bool big = false;
 #pragma unroll
         for (int h = 0; h < 2; h++) {
             const int e = t + 256 * h;
-            const bool live = r0 + st * kMmaRows + (e >> 4) < r1 && (e & 15) < a.mt;
-            tc[buf * 512 + e] = live ? h2f((uint16_t)sh[h]) * h2f((uint16_t)dh[h]) : 0.0f;
+            const int r = e >> 4, m = e & 15;
+            const bool row_live = r0 + st * kMmaRows + r < r1;
+            tdy[(buf * 16 + m) * kMmaRows + mma_kpos(r)] = row_live && m < a.mt ? (uint16_t)dh[h] : (uint16_t)0;
+            if (m == 0) {
+                tsv[buf * kMmaRows + mma_kpos(r)] = (uint16_t)sh[h];
+                big = big || (row_live && (uint16_t)sh[h] > kMmaMaxStep);
+            }
         }
+        if (big)
+            tbig[buf] = st;
     };
     f32x4 acc[4];
 #pragma unroll
     for (int cb = 0; cb < 4; cb++)
         acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int kg = lane >> 4, l16 = lane & 15;
+    // the dword of column pair (c, c + 1), c = 64 w + 32 pb + 2 (l % 16), in a tile row
+    int boff[2];
+#pragma unroll
+    for (int pb = 0; pb < 2; pb++) {
+        const int col = 64 * wave + 32 * pb + 2 * l16;
+        const int cg = col >> 5, cq = (col >> 3) & 3;  // group, 16-byte chunk
+        boff[pb] = cg * 64 + ((cq ^ (cg >> 2)) << 4) + (col & 7) * 2;
+    }
+    if (t < 2)
+        tbig[t] = -1;
     issue(0);
+    __syncthreads();
     stage(0);
     if (nsteps > 1)
         issue(1);
     __syncthreads();
     for (int st = 0; st < nsteps; st++) {
         const int buf = st & 1;
-        // this step's operands into registers, then its 32 products; then the
-        // next step's tile into the other buffer
-        // B: lane l reads the fp16 pair of columns 64 w + 32 pb + 2 (l % 16) + (0, 1)
-        // as one dword; accumulator 2 pb + h holds the even (h = 0) or odd columns
+        const bool big = tbig[buf] == st;  // block-uniform
+        // this step's operands into registers and its products; then the next
+        // step's tiles into the other buffer.
+        // Accumulator 2 pb + h holds the even (h = 0) or odd columns of pair block pb.
         const char* trow = tw + buf * kMmaRows * kMmaRowBytes;
-        float av[kMmaRows / 4], bv[kMmaRows / 4][4];
-#pragma unroll
-        for (int ks = 0; ks < kMmaRows / 4; ks++) {
-            const int kr = 4 * ks + (lane >> 4);
-            av[ks] = tc[buf * 512 + kr * 16 + (lane & 15)];
+        if (!big) {
+            // A: dy of token l % 16 at rows 4 e + l / 16; steps of the same rows, in pairs
+            const half8_t av = *reinterpret_cast<const half8_t*>(tdy + (buf * 16 + l16) * kMmaRows + 8 * kg);
+            const uint4 sq = *reinterpret_cast<const uint4*>(tsv + buf * kMmaRows + 8 * kg);
+            const uint32_t sp[4] = {sq.x, sq.y, sq.z, sq.w};
 #pragma unroll
             for (int pb = 0; pb < 2; pb++) {
-                const int col = 64 * wave + 32 * pb + 2 * (lane & 15);
-                const int cg = col >> 5, cq = (col >> 3) & 3;  // group, 16-byte chunk
-                const int off = cg * 64 + ((cq ^ (cg >> 2)) << 4) + (col & 7) * 2;
-                const half2_t hp = as_h2(*reinterpret_cast<const uint32_t*>(trow + kr * kMmaRowBytes + off));
-                bv[ks][2 * pb] = (float)hp.x;
-                bv[ks][2 * pb + 1] = (float)hp.y;
+                uint32_t d[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    d[e] = *reinterpret_cast<const uint32_t*>(trow + (4 * e + kg) * kMmaRowBytes + boff[pb]);
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    // (q - z) of column 2 (l % 16) + h at rows 4 e + l / 16, e = 2 i, 2 i + 1
+                    uint32_t bh[4], bl[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const uint32_t qz = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], h ? 0x07060302u : 0x05040100u);
+                        const half2_t sv = as_h2(sp[i]), qv = as_h2(qz);
+                        const half2_t hi = sv * qv;
+                        const half2_t lo = __builtin_elementwise_fma(sv, qv, -hi);
+                        bh[i] = __builtin_bit_cast(uint32_t, hi);
+                        bl[i] = __builtin_bit_cast(uint32_t, lo);
+                    }
+                    f32x4& c = acc[2 * pb + h];
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, mma_h8(bh[0], bh[1], bh[2], bh[3]), c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, mma_h8(bl[0], bl[1], bl[2], bl[3]), c, 0, 0, 0);
+                }
+            }
+        } else {
+            // fp32 form: k-step ks takes rows 4 ks + l / 16; A = s dy (exact in fp32)
+#pragma unroll
+            for (int ks = 0; ks < kMmaRows / 4; ks++) {
+                const int kr = 4 * ks + kg;
+                const float av = h2f(tsv[buf * kMmaRows + mma_kpos(kr)]) *
+                                 h2f(tdy[(buf * 16 + l16) * kMmaRows + mma_kpos(kr)]);
+#pragma unroll
+                for (int pb = 0; pb < 2; pb++) {
+                    const half2_t hp = as_h2(*reinterpret_cast<const uint32_t*>(trow + kr * kMmaRowBytes + boff[pb]));
+                    acc[2 * pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, (float)hp.x, acc[2 * pb], 0, 0, 0);
+                    acc[2 * pb + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, (float)hp.y, acc[2 * pb + 1], 0, 0, 0);
+                }
             }
         }
-#pragma unroll
-        for (int ks = 0; ks < kMmaRows / 4; ks++)
-#pragma unroll
-            for (int cb = 0; cb < 4; cb++)
-                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], bv[ks][cb], acc[cb], 0, 0, 0);
         if (st + 1 < nsteps) {
             stage(st + 1);
             if (st + 2 < nsteps)
