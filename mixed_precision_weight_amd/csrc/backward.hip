@@ -31,6 +31,7 @@
 // in LDS 64 tokens at a time, fp32 FMAs in token order.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "owq_decode.h"
 #include "owq_device.h"
@@ -480,10 +481,11 @@ __global__ __launch_bounds__(256) void k_bwd_dx_finalize(const BwdBatch bt)
 // of the MFMA (8 (l / 16) + e for lane l, operand element e) takes the step's
 // row 4 e + l / 16, so the four rows of one B read are consecutive (distinct
 // banks with the padded tile rows); the dy tile is stored in that order.
-// B_hi overflows fp16 only if s (q - z) > 65504, i.e. s > 9352: a step with
-// such a row multiplies in fp32 instead (v_mfma_f32_16x16x4_f32 with
-// A = s_i dy[m][i], exact in fp32, B = q - z), decided for the whole block at
-// the step's barrier. The tile is double-buffered (one barrier per step) and
+// B_hi overflows fp16 only if s (q - z) > 65504, i.e. s > 9352: a block whose
+// row slice holds such a row multiplies in fp32 instead (v_mfma_f32_16x16x4_f32
+// with A = s_i dy[m][i], exact in fp32, B = q - z); the two forms are separate
+// loops, so neither carries the other's accumulator copies. The tile is
+// double-buffered (one barrier per step) and
 // the next step's loads are issued before this step's products. The block
 // stores its partial sums P[slice][m][j].
 constexpr int kMmaCols = 256;  // columns per block
@@ -508,8 +510,6 @@ __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s,
     // [2][16][32] dy (token-major, rows at mma_kpos), then [2][32] steps
     uint16_t* const tdy = reinterpret_cast<uint16_t*>(lds + 2 * kMmaRows * kMmaRowBytes);
     uint16_t* const tsv = tdy + 2 * 16 * kMmaRows;
-    // [2] step tags: stage(st) stores st in slot st & 1 if the step needs the fp32 form
-    int* const tbig = reinterpret_cast<int*>(tsv + 2 * kMmaRows);
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int G = a.K >> 5;
@@ -540,7 +540,7 @@ __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s,
         }
     };
     // step st's tiles into buffer st & 1 (rows past the slice and tokens past
-    // the chunk get dy = 0); a live row's step above kMmaMaxStep tags the step
+    // the chunk get dy = 0)
     auto stage = [&](int st) {
         const int buf = st & 1;
         uint32_t p[16];
@@ -551,25 +551,16 @@ __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s,
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++)
             dst[q4 ^ (lg >> 2)] = make_uint4(p[4 * q4], p[4 * q4 + 1], p[4 * q4 + 2], p[4 * q4 + 3]);
-        bool big = false;
 #pragma unroll
         for (int h = 0; h < 2; h++) {
             const int e = t + 256 * h;
             const int r = e >> 4, m = e & 15;
             const bool row_live = r0 + st * kMmaRows + r < r1;
             tdy[(buf * 16 + m) * kMmaRows + mma_kpos(r)] = row_live && m < a.mt ? (uint16_t)dh[h] : (uint16_t)0;
-            if (m == 0) {
+            if (m == 0)
                 tsv[buf * kMmaRows + mma_kpos(r)] = (uint16_t)sh[h];
-                big = big || (row_live && (uint16_t)sh[h] > kMmaMaxStep);
-            }
         }
-        if (big)
-            tbig[buf] = st;
     };
-    f32x4 acc[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; cb++)
-        acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int kg = lane >> 4, l16 = lane & 15;
     // the dword of column pair (c, c + 1), c = 64 w + 32 pb + 2 (l % 16), in a tile row
     int boff[2];
@@ -579,85 +570,114 @@ __device__ __forceinline__ void bwd_mma_dense(const BwdArgs& a, int tile, int s,
         const int cg = col >> 5, cq = (col >> 3) & 3;  // group, 16-byte chunk
         boff[pb] = cg * 64 + ((cq ^ (cg >> 2)) << 4) + (col & 7) * 2;
     }
-    if (t < 2)
-        tbig[t] = -1;
+    // a step above kMmaMaxStep anywhere in the slice: the block multiplies in
+    // fp32 (flag word after the step tiles, cleared before the first barrier)
+    int* const tbig = reinterpret_cast<int*>(tsv + 2 * kMmaRows);
+    if (t == 0)
+        *tbig = 0;
     issue(0);
+    bool big = false;
+    for (int r = r0 + t; r < r1; r += 256)
+        big = big || a.scales[r] > kMmaMaxStep;
     __syncthreads();
+    if (big)
+        *tbig = 1;
     stage(0);
     if (nsteps > 1)
         issue(1);
     __syncthreads();
-    for (int st = 0; st < nsteps; st++) {
-        const int buf = st & 1;
-        const bool big = tbig[buf] == st;  // block-uniform
-        // this step's operands into registers and its products; then the next
-        // step's tiles into the other buffer.
-        // Accumulator 2 pb + h holds the even (h = 0) or odd columns of pair block pb.
-        const char* trow = tw + buf * kMmaRows * kMmaRowBytes;
-        if (!big) {
-            // A: dy of token l % 16 at rows 4 e + l / 16; steps of the same rows, in pairs
-            const half8_t av = *reinterpret_cast<const half8_t*>(tdy + (buf * 16 + l16) * kMmaRows + 8 * kg);
-            const uint4 sq = *reinterpret_cast<const uint4*>(tsv + buf * kMmaRows + 8 * kg);
-            const uint32_t sp[4] = {sq.x, sq.y, sq.z, sq.w};
+    big = *tbig != 0;  // block-uniform
+    // the step loop with the products of one form; accumulator 2 pb + h holds
+    // the even (h = 0) or odd columns of pair block pb
+    auto run = [&](auto fp16_form) {
+        constexpr bool kF16 = decltype(fp16_form)::value;
+        // acc: the fp32 form's sums or the fp16 form's B_hi products; accl: the
+        // B_lo products (apart, so that no MFMA waits on the one before it)
+        f32x4 acc[4], accl[4];
 #pragma unroll
-            for (int pb = 0; pb < 2; pb++) {
-                uint32_t d[8];
-#pragma unroll
-                for (int e = 0; e < 8; e++)
-                    d[e] = *reinterpret_cast<const uint32_t*>(trow + (4 * e + kg) * kMmaRowBytes + boff[pb]);
-#pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    // (q - z) of column 2 (l % 16) + h at rows 4 e + l / 16, e = 2 i, 2 i + 1
-                    uint32_t bh[4], bl[4];
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const uint32_t qz = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], h ? 0x07060302u : 0x05040100u);
-                        const half2_t sv = as_h2(sp[i]), qv = as_h2(qz);
-                        const half2_t hi = sv * qv;
-                        const half2_t lo = __builtin_elementwise_fma(sv, qv, -hi);
-                        bh[i] = __builtin_bit_cast(uint32_t, hi);
-                        bl[i] = __builtin_bit_cast(uint32_t, lo);
-                    }
-                    f32x4& c = acc[2 * pb + h];
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, mma_h8(bh[0], bh[1], bh[2], bh[3]), c, 0, 0, 0);
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, mma_h8(bl[0], bl[1], bl[2], bl[3]), c, 0, 0, 0);
-                }
-            }
-        } else {
-            // fp32 form: k-step ks takes rows 4 ks + l / 16; A = s dy (exact in fp32)
-#pragma unroll
-            for (int ks = 0; ks < kMmaRows / 4; ks++) {
-                const int kr = 4 * ks + kg;
-                const float av = h2f(tsv[buf * kMmaRows + mma_kpos(kr)]) *
-                                 h2f(tdy[(buf * 16 + l16) * kMmaRows + mma_kpos(kr)]);
+        for (int cb = 0; cb < 4; cb++) {
+            acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            accl[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        for (int st = 0; st < nsteps; st++) {
+            const int buf = st & 1;
+            // this step's operands into registers and its products; then the
+            // next step's tiles into the other buffer
+            const char* trow = tw + buf * kMmaRows * kMmaRowBytes;
+            if constexpr (kF16) {
+                // A: dy of token l % 16 at rows 4 e + l / 16; steps of the same rows, in pairs
+                const half8_t av = *reinterpret_cast<const half8_t*>(tdy + (buf * 16 + l16) * kMmaRows + 8 * kg);
+                const uint4 sq = *reinterpret_cast<const uint4*>(tsv + buf * kMmaRows + 8 * kg);
+                const uint32_t sp[4] = {sq.x, sq.y, sq.z, sq.w};
 #pragma unroll
                 for (int pb = 0; pb < 2; pb++) {
-                    const half2_t hp = as_h2(*reinterpret_cast<const uint32_t*>(trow + kr * kMmaRowBytes + boff[pb]));
-                    acc[2 * pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, (float)hp.x, acc[2 * pb], 0, 0, 0);
-                    acc[2 * pb + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, (float)hp.y, acc[2 * pb + 1], 0, 0, 0);
+                    uint32_t d[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        d[e] = *reinterpret_cast<const uint32_t*>(trow + (4 * e + kg) * kMmaRowBytes + boff[pb]);
+#pragma unroll
+                    for (int h = 0; h < 2; h++) {
+                        // (q - z) of column 2 (l % 16) + h at rows 4 e + l / 16, e = 2 i, 2 i + 1
+                        uint32_t bh[4], bl[4];
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const uint32_t qz =
+                                __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], h ? 0x07060302u : 0x05040100u);
+                            const half2_t sv = as_h2(sp[i]), qv = as_h2(qz);
+                            const half2_t hi = sv * qv;
+                            const half2_t lo = __builtin_elementwise_fma(sv, qv, -hi);
+                            bh[i] = __builtin_bit_cast(uint32_t, hi);
+                            bl[i] = __builtin_bit_cast(uint32_t, lo);
+                        }
+                        const int cb = 2 * pb + h;
+                        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, mma_h8(bh[0], bh[1], bh[2], bh[3]), acc[cb],
+                                                                          0, 0, 0);
+                        accl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, mma_h8(bl[0], bl[1], bl[2], bl[3]),
+                                                                           accl[cb], 0, 0, 0);
+                    }
+                }
+            } else {
+                // k-step ks takes rows 4 ks + l / 16; A = s dy (exact in fp32), B = q - z
+#pragma unroll
+                for (int ks = 0; ks < kMmaRows / 4; ks++) {
+                    const int kr = 4 * ks + kg;
+                    const float av = h2f(tsv[buf * kMmaRows + mma_kpos(kr)]) *
+                                     h2f(tdy[(buf * 16 + l16) * kMmaRows + mma_kpos(kr)]);
+#pragma unroll
+                    for (int pb = 0; pb < 2; pb++) {
+                        const half2_t hp =
+                            as_h2(*reinterpret_cast<const uint32_t*>(trow + kr * kMmaRowBytes + boff[pb]));
+                        acc[2 * pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, (float)hp.x, acc[2 * pb], 0, 0, 0);
+                        acc[2 * pb + 1] =
+                            __builtin_amdgcn_mfma_f32_16x16x4f32(av, (float)hp.y, acc[2 * pb + 1], 0, 0, 0);
+                    }
                 }
             }
-        }
-        if (st + 1 < nsteps) {
-            stage(st + 1);
-            if (st + 2 < nsteps)
-                issue(st + 2);
-        }
-        __syncthreads();
-    }
-    // D element r of lane l: token 4 (l / 16) + r; accumulator cb = 2 pb + h:
-    // column 64 w + 32 pb + 2 (l % 16) + h
-#pragma unroll
-    for (int cb = 0; cb < 4; cb++) {
-        const int j = tile * kMmaCols + 64 * wave + 32 * (cb >> 1) + 2 * (lane & 15) + (cb & 1);
-        if (j < a.K)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int m = 4 * (lane >> 4) + r;
-                if (m < a.mt)
-                    a.P[((int64_t)s * 16 + m) * a.K + j] = acc[cb][r];
+            if (st + 1 < nsteps) {
+                stage(st + 1);
+                if (st + 2 < nsteps)
+                    issue(st + 2);
             }
-    }
+            __syncthreads();
+        }
+        // D element r of lane l: token 4 (l / 16) + r; accumulator cb = 2 pb + h:
+        // column 64 w + 32 pb + 2 (l % 16) + h
+#pragma unroll
+        for (int cb = 0; cb < 4; cb++) {
+            const int j = tile * kMmaCols + 64 * wave + 32 * (cb >> 1) + 2 * (lane & 15) + (cb & 1);
+            if (j < a.K)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int m = 4 * (lane >> 4) + r;
+                    if (m < a.mt)
+                        a.P[((int64_t)s * 16 + m) * a.K + j] = kF16 ? acc[cb][r] + accl[cb][r] : acc[cb][r];
+                }
+        }
+    };
+    if (big)
+        run(std::false_type{});
+    else
+        run(std::true_type{});
 }
 
 // weak-column partials of one row slice: PW[slice][m][c] = sum over the slice's

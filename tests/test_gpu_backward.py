@@ -157,22 +157,21 @@ def test_vector_form_above_four_tokens(owq, M, monkeypatch):
 
 @pytest.mark.parametrize("M", [16, 20])
 def test_matrix_core_step_ranges(owq, M):
-    """The matrix-core form splits s (q - z) into two fp16 values and falls back
-    to fp32 products for a 32-row step that holds a row with s > 9352 (where
-    7 s overflows fp16). Rows with such steps (weights near +-40000 and
-    -30000 .. 40000) sit in steps 0 and 9 of the first 512-row slice, a row
-    whose step (9344) is just below the limit in step 10, a row of fp16
-    subnormal weights (subnormal step) in step 0, and the second slice has
-    none: every element stays within the bound."""
+    """The matrix-core form splits s (q - z) into two fp16 values; a block whose
+    512-row slice holds a row with s > 9352 (where 7 s overflows fp16) keeps
+    fp32 products. The first slice holds two such rows (weights near +-40000,
+    and -30000 .. 40000) and a row of fp16 subnormal weights; the second holds
+    a row whose step (9344) is just below the limit and a row of subnormal
+    steps, and runs the fp16 form: every element stays within the bound."""
     rng = np.random.default_rng(77 + M)
     N, K = 600, 4096
     W = synth.random_layer(rng, N, K, 0.02)
     W[5, :] = rng.uniform(-40000, 40000, K).astype(np.float16)
     W[300, ::3] = np.float16(40000)
     W[300, 1::3] = np.float16(-30000)
-    W[330, ::2] = np.float16(32700)  # step 9344: the largest range below the limit
-    W[330, 1::2] = np.float16(-32700)
     W[7, :] = (rng.uniform(-1, 1, K) * 1e-5).astype(np.float16)
+    W[540, ::2] = np.float16(32700)  # step 9344: the largest range below the limit
+    W[540, 1::2] = np.float16(-32700)
     W[520, :] = (rng.uniform(-1, 1, K) * 1e-6).astype(np.float16)
     idx = np.sort(rng.choice(K, 40, replace=False)).astype(np.int32)
     _run_scaled(owq, W, idx, M, "step ranges", dy_scale=1e-2)
