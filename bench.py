@@ -760,9 +760,11 @@ def main():
             nb = sum(3 * s.N * s.K // 8 + 3 * s.N + 2 * s.N * s.k + 2 * M * s.N + 2 * M * s.K + 2 * M * s.k
                      + 4 * s.N * s.k for s in specs)
             bw[f"M={M}"] = dict(
-                hbm_entry(nb, t, "owq_linear_backward_batched over the 7 linears (k_bwd_part: dx slice partials "
-                                 "with the weak columns, and dw_weak; k_bwd_dx_finalize), one part and one finalize "
-                                 "launch per 4 tokens, replayed from a HIP graph (device time)"),
+                hbm_entry(nb, t, "owq_linear_backward_batched over the 7 linears, replayed from a HIP graph "
+                                 "(device time): up to 4 tokens k_bwd_part (dx slice partials with the weak columns, "
+                                 "and dw_weak) + k_bwd_dx_finalize per 4 tokens; more tokens k_bwd_mma (dx on the "
+                                 "matrix cores in fp16, 16 tokens per pass, weak-column partials, dw_weak) + "
+                                 "k_bwd_mma_finalize + k_bwd_mma_weak_finalize per 16 tokens"),
                 us_eager_python_call=round(t_eager * 1e6, 2),
                 us_one_call_per_linear_graph=round(t_one * 1e6, 2))
         result["kernels"]["backward_weak_column_tuning"] = bw
