@@ -385,7 +385,7 @@ size_t owq_linear_backward_workspace_bytes(int64_t N, int64_t K, int32_t k);
  * transposed 3-bit product, summed over row slices in a fixed order (bitwise
  * deterministic): up to 4 tokens on the vector ALUs (exact products), more on
  * the matrix cores 16 tokens per pass (exact products: dy times s (q - z) split
- * into two fp16 values; fp32 products for 32-row steps holding a step above
+ * into two fp16 values; fp32 products for a 512-row slice holding a step above
  * 9352; the environment variable OWQ_BACKWARD=vector, read at each call, keeps
  * the vector form). workspace: >=
  * owq_linear_backward_workspace_bytes(N, K, k) bytes, 256-byte aligned, needed
