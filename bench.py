@@ -31,7 +31,10 @@ replayed from a HIP graph, the M = 1 decode and the prefill products as plain
 fp16 products on the unquantised weights (torch, for comparison), a 1 GiB device-copy rate, and
 calibration at T = 8192 on the two MLP shapes, and the decode of the large
 shapes (8192 and 28672) at M = 1 and 8 (flags --no-sweep, --no-extras,
---no-long-calibration and --no-large skip them, e.g. under a profiler).
+--no-long-calibration and --no-large skip them, e.g. under a profiler). The
+extras also time the storage-favoured form, one GPU's share of the layer at
+8-way column-parallel sharding (N / 8 rows of each linear), the
+weak-column-tuning backward, the OPTQ pack and the truncation-aware pack.
 
 --copy-reference adds, after the timed steps, three copies of a 512 MiB buffer
 (a plain copy kernel of known size) so that hardware-counter runs of this script
@@ -359,7 +362,8 @@ def main():
 
     # the decode launches of each copy, with their arguments marshalled once (the
     # packed copies are rewritten in place, so the pointers stay valid)
-    dec_calls = [owq.PreparedBatched(slots[r], xd, yd) for r in range(ROTATE)]
+    cur = torch.cuda.current_stream()  # the timed calls' stream, fixed once
+    dec_calls = [owq.PreparedBatched(slots[r], xd, yd, stream=cur) for r in range(ROTATE)]
     decode_bytes = sum(eff_bytes(s.N, s.K, s.k, 1) for s in specs)
     CE = 4  # calibration-phase events
     NE = CE + 2 + L + 1  # calibration phase, decode pair, prefill boundaries
@@ -471,7 +475,7 @@ def main():
         for M in SWEEP_MS:
             xs = [x[:M] for x in x1]
             ys = [y[:M] for y in y1]
-            calls = [owq.PreparedBatched(slots[r], xs, ys) for r in range(ROTATE)]
+            calls = [owq.PreparedBatched(slots[r], xs, ys, stream=cur) for r in range(ROTATE)]
             for r in range(ROTATE):
                 calls[r]()
             a, b = E(), E()
@@ -679,7 +683,8 @@ def main():
         yb = [torch.empty((8, s.N), dtype=torch.float16, device=dev) for s in c3.layers]
         large = {}
         for M in (1, 8):
-            calls = [owq.PreparedBatched(big[r], [x[:M] for x in xb], [y[:M] for y in yb]) for r in range(RL)]
+            calls = [owq.PreparedBatched(big[r], [x[:M] for x in xb], [y[:M] for y in yb], stream=cur)
+                     for r in range(RL)]
             for r in range(RL):
                 calls[r]()
             reps = 4 * RL
@@ -727,6 +732,40 @@ def main():
             us_one_call_per_linear_graph=round(t_one * 1e6, 2),
             us_latency_form=round(dec_s * 1e6, 2))
         del sto, wss
+
+        # one GPU's share of the layer under 8-way column-parallel sharding (the
+        # multi-GPU layout: every GPU holds N / 8 rows of each linear, x and the
+        # weak index set replicated, no exchange for y = W x): the same batched
+        # M = 1 decode over row slices of the packed layers, 56 copies (the 8
+        # shards of 7 layer copies, 555 MB) rotated so the footprint exceeds the
+        # 256 MB Infinity Cache
+        print("bench: one GPU's share at 8-way sharding", file=sys.stderr, flush=True)
+        G, NSH = 8, 56
+        shard = []
+        for r in range(NSH):
+            g, src = r % G, slots[r % ROTATE]
+            lay = []
+            for li, sp in enumerate(specs):
+                a, b = (sp.N // G) * g, (sp.N // G) * (g + 1)
+                lay.append({"qcodes": src[li]["qcodes"][a:b].clone(), "scales": src[li]["scales"][a:b].clone(),
+                            "zeros": src[li]["zeros"][a:b].clone(), "w_weak": src[li]["w_weak"][a:b].clone(),
+                            "weak_idx": src[li]["weak_idx"]})
+            shard.append(lay)
+        ysh = [torch.empty((1, sp.N // G), dtype=torch.float16, device=dev) for sp in specs]
+
+        def shard_all():  # the stream is taken at each call (graph capture)
+            for r in range(NSH):
+                owq.linear_batched(shard[r], xd, ysh)
+
+        t = graph_time(shard_all) * ROTATE / NSH
+        sh_bytes = sum(eff_bytes(sp.N // G, sp.K, sp.k, 1) for sp in specs)
+        result["kernels"]["decode_shard_g8"] = dict(
+            hbm_entry(sh_bytes, t, "one GPU's share of the layer at 8-way column-parallel sharding (N / 8 rows of "
+                                   "each linear, x replicated): owq_linear_batched at M = 1, one k_gemv<1> launch, "
+                                   "56 copies rotated, replayed from a HIP graph (device time); the collective "
+                                   "(an all-gather of y, if the next layer needs it whole) is not measured"),
+            rows_per_gpu={sp.name: sp.N // G for sp in specs})
+        del shard
 
     if not args.no_extras:
         # weak-column-tuning backward of the layer: dx = dy W and dw_weak = dy^T

@@ -762,6 +762,9 @@ class PreparedBatched:
     again: each call then only crosses into the library (which still checks the
     arguments) instead of rebuilding the layer structs and pointer arrays. The
     tensors must stay alive, at the same addresses, while the object is used.
+    With stream=None each call enqueues on torch's current stream at that call
+    (so calls made under HIP graph capture are captured); a given stream is
+    used for every call.
     """
 
     def __init__(self, layers: list, xs: list, ys: list, stream=None):
@@ -772,18 +775,20 @@ class PreparedBatched:
         self.yp = (_P * n)(*[y.data_ptr() for y in ys])
         self.n = n
         self.M = M
-        self.stream = _stream(stream)
+        self.stream = None if stream is None else _stream(stream)
         self.fn = lib().owq_linear_batched
 
     def __call__(self):
-        _check(self.fn(self.Ls, self.xp, self.yp, self.n, self.M, self.stream), "owq_linear_batched")
+        st = self.stream if self.stream is not None else _stream()
+        _check(self.fn(self.Ls, self.xp, self.yp, self.n, self.M, st), "owq_linear_batched")
 
 
 class PreparedCalibrate:
     """One owq_calibrate_score_batched call with its item array, outputs and
     workspace built once (outputs: `results`, one (lambda, score) pair per
     linear, rewritten by every call). The W and X tensors must stay alive, at
-    the same addresses, while the object is used."""
+    the same addresses, while the object is used. With stream=None each call
+    enqueues on torch's current stream at that call."""
 
     def __init__(self, Ws: list, Xs: list, workspace: torch.Tensor | None = None, stream=None):
         self.items, self.results = _calib_items(Ws, Xs)
@@ -797,11 +802,12 @@ class PreparedCalibrate:
         self._keep = (list(Ws), list(Xs), workspace)
         self.ws = _ptr(workspace)
         self.ws_bytes = _nbytes(workspace)
-        self.stream = _stream(stream)
+        self.stream = None if stream is None else _stream(stream)
         self.fn = lib().owq_calibrate_score_batched
 
     def __call__(self) -> list:
-        _check(self.fn(self.items, self.n, self.ws, self.ws_bytes, self.stream), "owq_calibrate_score_batched")
+        st = self.stream if self.stream is not None else _stream()
+        _check(self.fn(self.items, self.n, self.ws, self.ws_bytes, st), "owq_calibrate_score_batched")
         return self.results
 
 

@@ -296,6 +296,56 @@ def test_workspace_reuse_and_stream(owq):
     assert host(got[1]).tobytes() == host(ref[1]).tobytes()
 
 
+def test_prepared_calls_under_graph_capture(owq):
+    """PreparedBatched and PreparedCalibrate built with stream=None enqueue on
+    the stream current at each call, so a HIP graph captures them. The graph
+    is replayed three times, with eager work (clearing the outputs and a
+    change of inputs) between replays, and every replay equals the eager
+    result of its inputs."""
+    import torch
+    rng = np.random.default_rng(5)
+    shapes = [(96, 256, 3), (40, 512, 0), (130, 1024, 9)]
+    layers, xs, Ws, Xs = [], [], [], []
+    for N, K, k in shapes:
+        W = synth.random_layer(rng, N, K)
+        idx = np.sort(rng.choice(K, k, replace=False)).astype(np.int32)
+        layers.append(owq.pack(dev(W), dev(idx)))
+        xs.append(dev((rng.standard_normal((1, K))).astype(np.float16)))
+        Ws.append(dev(W))
+        Xs.append(dev((rng.standard_normal((64, K))).astype(np.float16)))
+    ys = [torch.zeros((1, N), dtype=torch.float16, device="cuda:0") for N, _, _ in shapes]
+    dec = owq.PreparedBatched(layers, xs, ys)
+    cal = owq.PreparedCalibrate(Ws, Xs)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capturing stream
+        dec()
+        cal()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec()
+        cal()
+    for rep in range(3):
+        for y in ys:
+            y.zero_()
+        for x in xs:  # new inputs each replay (same addresses)
+            x.copy_(dev((rng.standard_normal(tuple(x.shape))).astype(np.float16)))
+        torch.cuda.synchronize()
+        want = owq.linear_batched(layers, xs)
+        want_cal = owq.calibrate_batched(Ws, Xs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ys, want):
+            assert host(a).tobytes() == host(b).tobytes(), f"replay {rep}"
+        for (la, sa), (lb, sb) in zip(cal.results, want_cal):
+            assert host(la).tobytes() == host(lb).tobytes(), f"replay {rep}"
+            assert host(sa).tobytes() == host(sb).tobytes(), f"replay {rep}"
+    del g
+
+
 def test_pack_and_score_exact_ties(owq):
     """Rows built from multiples of a quarter of the step put w / s exactly on
     half-integers in many places: codes must round those ties to even, exactly as

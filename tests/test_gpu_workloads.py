@@ -73,6 +73,38 @@ def test_llama7b_layer_batched_launch(owq):
     check_linear(host(ys[6]), yr, bnd, "batched down_proj")
 
 
+@pytest.mark.parametrize("g", [0, 7])
+def test_llama7b_layer_shard_g8(owq, g):
+    """One GPU's share at 8-way column-parallel sharding: rows [g N/8, (g+1) N/8)
+    of each of the 7 packed linears, decoded in one batched launch at M = 1,
+    equal bit for bit to the same rows of the full layer's output, and every
+    output within the oracle's bound."""
+    import torch
+    import oracle
+    cfg = synth.LLAMA7B_LAYER_DECODE
+    full, shard, xs, Ws = [], [], [], []
+    for li, spec in enumerate(cfg.layers):
+        seed = cfg.seed(li)
+        W = synth.weights(spec, seed)
+        idx = np.sort(np.random.default_rng(li).choice(spec.K, spec.k, replace=False)).astype(np.int32)
+        p = owq.pack(dev(W), dev(idx))
+        a, b = (spec.N // 8) * g, (spec.N // 8) * (g + 1)
+        shard.append({key: (v if key == "weak_idx" else v[a:b].clone()) for key, v in p.items()})
+        full.append(p)
+        xs.append(dev(synth.activations(spec, seed, 1)))
+        Ws.append((W[a:b], idx))
+    print(f"shard g={g} of 8: rows {[s.N // 8 for s in cfg.layers]}", flush=True)
+    yf = owq.linear_batched(full, xs)
+    ys = owq.linear_batched(shard, xs)
+    torch.cuda.synchronize()
+    for li, spec in enumerate(cfg.layers):
+        a, b = (spec.N // 8) * g, (spec.N // 8) * (g + 1)
+        assert host(ys[li]).tobytes() == host(yf[li])[:, a:b].tobytes(), spec.name
+        Wsh, idx = Ws[li]
+        yr, bnd = oracle.linear_rows(oracle.pack(np.ascontiguousarray(Wsh), idx), host(xs[li]))
+        check_linear(host(ys[li]), yr, bnd, f"shard {g} {spec.name}")
+
+
 @pytest.mark.parametrize("li", range(3))
 def test_large_shapes(owq, li):
     cfg = synth.LARGE_SHAPES
