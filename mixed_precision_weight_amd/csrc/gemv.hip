@@ -1,4 +1,4 @@
-// gemv.hip -- decode-time OWQ linear, small batch M (gfx950, vector ALUs).
+// gemv.hip -- decode-time OWQ linear, small batch M (gfx950, vector-ALU decode).
 //
 //   y[m][i] = s_i * sum_j (q_ij - z_i) x[m][j] + sum_c w_weak[i][c] x[m][idx_c]
 //
@@ -27,7 +27,21 @@
 // exact, so the fp32 sum's error is bounded relative to sum_j |(q_j - z) x_j|,
 // for every row, including rows whose codes all equal the zero point. Per tile:
 // 5 window ops, 17 and-or, 16 packed subtracts, 16 dot2 per token.
+//
+// With two tokens the dot2 work doubles, and the products move to the matrix
+// cores instead: v_mfma_f32_16x16x32_f16 pairs the 8 A and the 8 B elements of
+// each lane with the same 8 k indices, for A row and B column l % 16, so entry
+// (i, i) of its 16 x 16 result is the sum, over lanes i, i + 16, i + 32 and
+// i + 48, of each lane's own 8 decoded values times its own 8 x values. One MFMA
+// per token and 8 columns (A = the lane's x quad, B = four decode pairs) keeps
+// the lane layout, the loads and the staging of the vector form; the diagonal
+// is read out at the end (15 of 16 results are discarded, the matrix cores have
+// the throughput to spare) and the 64-lane reduction follows as before. The
+// products stay exact and are summed in fp32. Lanes past a chunk's groups meet
+// x staged as zeros.
 #include <cstdlib>
+#include <cstring>
+#include <type_traits>
 
 #include "owq_decode.h"
 #include "owq_device.h"
@@ -68,9 +82,9 @@ __device__ __forceinline__ int xs_slot(int m, int T, int g, int qd)
 // ------------------------------------------------------------------ kernel --
 constexpr int kChunkTiles = 2;  // 64-group tiles per K chunk (4096 columns)
 constexpr int kNonTemporal = 2;  // buffer-load cache-policy bits: nt
-// Rows per wavefront: three (76 registers at M = 1, six waves per SIMD) was
+// Rows per wavefront: three (71 registers at M = 1, seven waves per SIMD) was
 // faster than two, four (109 registers, four waves) and eight at M = 1 and 2.
-__host__ __device__ constexpr int rows_per_wave(int) { return 3; }
+constexpr int kRowsPerWave = 3;
 
 __device__ __forceinline__ float f_of(uint32_t v) { return __builtin_bit_cast(float, v); }
 __device__ __forceinline__ uint32_t u_of(float v) { return __builtin_bit_cast(uint32_t, v); }
@@ -106,10 +120,9 @@ __device__ __forceinline__ int reduced_index(int q) { return (q & 1) + ((q >> 1)
 // is issued before the first wait, so a chunk costs one memory latency; the
 // hardware overlaps the arithmetic of resident blocks with the loads of others.
 // Layers of any K share this one kernel, so a batch is a single launch.
-template <int M>
-__global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
+template <int M, bool MMA, int R>
+__device__ __forceinline__ void gemv_body(const GemvBatch& b)
 {
-    constexpr int R = rows_per_wave(M);
     constexpr int TT = kChunkTiles;
     constexpr int GC = 64 * TT;  // groups per chunk
     extern __shared__ uint4 smem[];
@@ -214,11 +227,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
 
     const Magic mg = make_magic();
     float acc[R][M];
+    float4_t macc[MMA ? R : 1][MMA ? M : 1];
 #pragma unroll
     for (int r = 0; r < R; r++)
 #pragma unroll
-        for (int m = 0; m < M; m++)
+        for (int m = 0; m < M; m++) {
             acc[r][m] = 0.0f;
+            if (MMA)
+                macc[r][m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 
     for (int g0 = 0; g0 < G; g0 += GC) {
         const int gc = min(GC, G - g0);
@@ -230,8 +247,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
         for (int t = 0; t < XP; t++) {
             const int i = tid + 256 * t;
             const int pc = i % PC;
-            if (pc < 4 * gc)
+            if (MMA) {  // every slot is written: x, or zeros past the chunk's groups
+                const bool on = pc < 4 * gc;
+                smem[xs_slot(i / PC, TT, pc >> 2, pc & 3)] =
+                    make_uint4(on ? xg[t].x : 0u, on ? xg[t].y : 0u, on ? xg[t].z : 0u, on ? xg[t].w : 0u);
+            } else if (pc < 4 * gc) {
                 smem[xs_slot(i / PC, TT, pc >> 2, pc & 3)] = make_uint4(xg[t].x, xg[t].y, xg[t].z, xg[t].w);
+            }
         }
         __syncthreads();
         // x of a tile is read from LDS once (all four quads in flight together)
@@ -240,12 +262,40 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
         for (int u = 0; u < TT; u++) {
             const int g = (u << 6) + lane;  // group within the chunk
             uint4 xq[M][4];
+            if (!MMA) {
 #pragma unroll
-            for (int m = 0; m < M; m++)
+                for (int m = 0; m < M; m++)
 #pragma unroll
-                for (int qd = 0; qd < 4; qd++)
-                    xq[m][qd] = smem[xs_slot(m, TT, g, qd)];
-            if (g < gc) {
+                    for (int qd = 0; qd < 4; qd++)
+                        xq[m][qd] = smem[xs_slot(m, TT, g, qd)];
+            }
+            if (MMA) {
+                // lanes past the chunk's groups meet zeros in x: their products are 0.
+                // Quad qd of x (columns 8 qd .. 8 qd + 7 of the lane's group) meets
+                // decode pairs 4 qd .. 4 qd + 3 of each row.
+                auto quad = [&](auto qdc) {
+                    constexpr int qd = decltype(qdc)::value;
+                    uint4 xv[M];
+#pragma unroll
+                    for (int m = 0; m < M; m++)
+                        xv[m] = smem[xs_slot(m, TT, g, qd)];
+#pragma unroll
+                    for (int r = 0; r < R; r++) {
+                        const ZeroSub nz = make_zero_sub(zr[r]);
+                        uint32_t p[4];
+                        decode_quad<qd>(cw[r][u].x, cw[r][u].y, cw[r][u].z, mg, nz, p);
+                        const half8_t bq = __builtin_bit_cast(half8_t, make_uint4(p[0], p[1], p[2], p[3]));
+#pragma unroll
+                        for (int m = 0; m < M; m++)
+                            macc[r][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(half8_t, xv[m]), bq, macc[r][m], 0, 0, 0);
+                    }
+                };
+                quad(std::integral_constant<int, 0>{});
+                quad(std::integral_constant<int, 1>{});
+                quad(std::integral_constant<int, 2>{});
+                quad(std::integral_constant<int, 3>{});
+            } else if (g < gc) {
 #pragma unroll
                 for (int r = 0; r < R; r++) {
                     const ZeroSub nz = make_zero_sub(zr[r]);
@@ -266,6 +316,24 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
                 }
             }
         }
+    }
+
+    if (MMA) {
+        // The MFMA pairs lane l's A and B elements with the same k index, for A row
+        // and B column l % 16: entry (i, i) of the 16 x 16 result sums the products
+        // of lanes i, i + 16, i + 32 and i + 48 with their own x, i.e. of their own
+        // groups. Entry (i, i) is element i % 4 of lane 16 (i / 4) + i; the other
+        // entries pair one lane's codes with another lane's x and are dropped.
+        const bool diag = (lane >> 4) == ((lane & 15) >> 2);
+        const int e = lane & 3;
+#pragma unroll
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const float4_t c = macc[r][m];
+                const float v = e == 0 ? c[0] : e == 1 ? c[1] : e == 2 ? c[2] : c[3];
+                acc[r][m] = diag ? v : 0.0f;
+            }
     }
 
     // rows: scale, weak columns, 64-lane reduction of the rows together, fp16 store
@@ -307,13 +375,39 @@ __global__ __launch_bounds__(256) void k_gemv(GemvBatch b)
 }
 
 template <int M>
+__global__ __launch_bounds__(256) void k_gemv(GemvBatch b) { gemv_body<M, false, kRowsPerWave>(b); }
+// the matrix-core products at five waves per SIMD (95 registers, no spills);
+// without the occupancy bound the compiler takes 138 and runs three
+template <int M>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_gemv_mfma(GemvBatch b)
+{
+    gemv_body<M, true, kRowsPerWave>(b);
+}
+
+template <int M>
 hipError_t launch_m(const GemvBatch& b, int nblocks, size_t lds, hipStream_t s)
 {
+    if constexpr (M <= 2) {
+        if (gemv_products_on_matrix_cores(M)) {
+            hipLaunchKernelGGL((k_gemv_mfma<M>), dim3(nblocks), dim3(256), lds, s, b);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((k_gemv<M>), dim3(nblocks), dim3(256), lds, s, b);
     return hipGetLastError();
 }
 
 }  // namespace
+
+bool gemv_products_on_matrix_cores(int64_t M)
+{
+    const char* e = std::getenv("OWQ_GEMV_PRODUCTS");
+    if (e && std::strcmp(e, "dot2") == 0)
+        return false;
+    if (e && std::strcmp(e, "mfma") == 0)
+        return M <= 2;
+    return M == 2;
+}
 
 int gemv_max_tokens(int64_t K)
 {
@@ -328,7 +422,7 @@ bool gemv_fits(int64_t M, int64_t K)
 }
 
 // One launch for the batch; blocks of 4 wavefronts, each wavefront owning
-// rows_per_wave(class) consecutive rows of its layer.
+// kRowsPerWave consecutive rows of its layer.
 hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
 {
     // layers with the longest rows first: their blocks run longest
@@ -359,7 +453,7 @@ hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
         L.K = (int32_t)d[l].K;
         L.k = d[l].k;
         L.block0 = nblocks;
-        const int rows = 4 * rows_per_wave(M);
+        const int rows = 4 * kRowsPerWave;
         nblocks += (int)((d[l].N + rows - 1) / rows);
     }
     const size_t lds = (size_t)M * kChunkTiles * 4 * kQuadStride * 16;

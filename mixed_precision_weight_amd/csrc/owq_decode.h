@@ -116,5 +116,38 @@ __device__ __forceinline__ void decode_group(uint32_t w0, uint32_t w1, uint32_t 
     p[15] = sub_h2(and_or(w2 >> 13, 0x00070000u, and_or(w0, 7u, mg.p)), n.p);
 }
 
+// The four pairs 4 qd .. 4 qd + 3 of a group (columns 8 qd .. 8 qd + 7), the same
+// values as decode_group's p[4 qd .. 4 qd + 3].
+template <int QD>
+__device__ __forceinline__ void decode_quad(uint32_t w0, uint32_t w1, uint32_t w2, const Magic& mg,
+                                            const ZeroSub& n, uint32_t p[4])
+{
+    if constexpr (QD == 0) {
+        const uint32_t a1 = w0 >> 2;
+        p[0] = sub_h2(and_or(a1, kMaskA, mg.a), n.a);
+        p[1] = sub_h2(and_or(a1, kMaskB, mg.b), n.b);
+        p[2] = sub_h2(and_or(a1, kMaskC, mg.c), n.c);
+        p[3] = sub_h2(and_or(__builtin_amdgcn_alignbit(w1, w0, 11), kMaskA, mg.a), n.a);
+    } else if constexpr (QD == 1) {
+        p[0] = sub_h2(and_or(__builtin_amdgcn_alignbit(w1, w0, 11), kMaskB, mg.b), n.b);
+        p[1] = sub_h2(and_or(w1, kMaskA, mg.a), n.a);
+        p[2] = sub_h2(and_or(w1, kMaskB, mg.b), n.b);
+        p[3] = sub_h2(and_or(w1, kMaskC, mg.c), n.c);
+    } else if constexpr (QD == 2) {
+        const uint32_t b2 = w1 >> 9;
+        const uint32_t a3 = __builtin_amdgcn_alignbit(w2, w1, 30);
+        p[0] = sub_h2(and_or(b2, kMaskA, mg.a), n.a);
+        p[1] = sub_h2(and_or(b2, kMaskB, mg.b), n.b);
+        p[2] = sub_h2(and_or(a3, kMaskA, mg.a), n.a);
+        p[3] = sub_h2(and_or(a3, kMaskB, mg.b), n.b);
+    } else {
+        const uint32_t b3 = w2 >> 7;
+        p[0] = sub_h2(and_or(__builtin_amdgcn_alignbit(w2, w1, 30), kMaskC, mg.c), n.c);
+        p[1] = sub_h2(and_or(b3, kMaskA, mg.a), n.a);
+        p[2] = sub_h2(and_or(b3, kMaskB, mg.b), n.b);
+        p[3] = sub_h2(and_or(w2 >> 13, 0x00070000u, and_or(w0, 7u, mg.p)), n.p);
+    }
+}
+
 }  // namespace
 }  // namespace owq

@@ -95,6 +95,10 @@ hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s);
 // Tokens per GEMV launch for a layer of K columns (x of all tokens is staged in LDS).
 int gemv_max_tokens(int64_t K);
 bool gemv_fits(int64_t M, int64_t K);
+// Products of the vector-ALU decode for M tokens: true = one v_mfma_f32_16x16x32_f16
+// per token and 8 columns (M <= 2), false = v_dot2 per column pair.
+// OWQ_GEMV_PRODUCTS=dot2|mfma overrides (read per call).
+bool gemv_products_on_matrix_cores(int64_t M);
 // Matrix-core decode over `count` layers (count <= kGemvMaxLayers), 1 <= M <= kMfvMaxM.
 constexpr int kMfvMaxM = 16;
 hipError_t launch_mfv(const LinearDesc* d, int count, int M, hipStream_t s);

@@ -383,3 +383,20 @@ def test_vector_decode_three_and_four_tokens(owq, monkeypatch, N, K, k, Ms):
     X = synth.calibration(spec, N + K, 24)
     x = _quiet_columns(synth.activations(spec, N + K + 2, max(Ms)))
     _run(owq, W, X, k, [x[:m] for m in Ms], f"vector N={N} K={K} k={k}")
+
+
+@pytest.mark.parametrize("products", ["dot2", "mfma"])
+@pytest.mark.parametrize("N,K,k", [(5, 96, 1), (64, 640, 7), (37, 11008, 86), (130, 8192, 63), (64, 640, 130)])
+def test_vector_decode_product_forms(owq, monkeypatch, products, N, K, k):
+    """The vector-ALU decode's products by v_dot2 (the default for one token) and
+    on the matrix cores with the diagonal read-out (the default for two) meet the
+    same bar for one and two tokens: ragged chunk tails (K = 96, 640, 11008),
+    more than 128 weak columns, rows whose weights sit far below their step."""
+    monkeypatch.setenv("OWQ_DECODE", "vector")
+    monkeypatch.setenv("OWQ_GEMV_PRODUCTS", products)
+    rng = np.random.default_rng(N * 13 + K + k)
+    W = _tiny_rows(synth.random_layer(rng, N, K, 0.02))
+    spec = synth.LayerSpec("edge", N, K, k, 0.02, max(1, K // 200), 20.0)
+    X = synth.calibration(spec, N + K, 24)
+    x = _quiet_columns(synth.activations(spec, N + K + 5, 2))
+    _run(owq, W, X, k, [x[:1], x[:2]], f"products={products} N={N} K={K} k={k}")
