@@ -488,7 +488,8 @@ def main():
             nb = sum(eff_bytes(s.N, s.K, s.k, M) for s in specs)
             sweep[f"M={M}"] = {"us_per_layer": round(t * 1e6, 2), "effective_GBps": round(nb / t / 1e9, 1),
                                "frac_hbm": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
-                               "path": "k_gemv, one launch" if M <= 2 else "k_mfv, one launch"}
+                               "path": ("k_gemv, one launch" if M == 1 else "k_gemv_mfma (products on the matrix cores), one launch"
+                                        if M == 2 else "k_mfv, one launch")}
         result["decode_batch_sweep"] = sweep
 
     if not args.no_extras:
