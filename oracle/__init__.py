@@ -22,6 +22,8 @@ from .oracle import (  # noqa: F401
     pack,
     pack_search,
     pack_storage,
+    pack_grouped,
+    linear_grouped_rows,
     optq_factor,
     optq_pack,
     f64_to_f16,

@@ -66,6 +66,9 @@ def load():
         "owq_oracle_linear_rows": (None, [_P, _P, _P, _I64, _I64, _P, _P, _I32,
                                           _P, _I64, _P, _I64, _P, _P, ctypes.c_int]),
         "owq_oracle_effective_bits": (ctypes.c_double, [_I64, _I64, ctypes.c_int]),
+        "owq_oracle_pack_grouped": (None, [_P, _I64, _I64, _P, _I32, _I64, _P, _P, _P, _P]),
+        "owq_oracle_linear_grouped_rows": (None, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _I32,
+                                                  _P, _I64, _P, _I64, _P, _P, ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -388,3 +391,47 @@ def linear_rows(layer: dict, x, rows=None, threads: int = 0):
 
 def effective_bits(K: int, k: int, latency_favored: bool) -> float:
     return load().owq_oracle_effective_bits(int(K), int(k), 1 if latency_favored else 0)
+
+
+def pack_grouped(W, weak_idx, G: int):
+    """Group-wise form: dict(qcodes uint32[N][K/32][3], scales uint16[N][K/G],
+    zeros uint8[N][K/G], w_weak uint16[N][k], weak_idx int32[k], group G)."""
+    W = _u16(W)
+    N, K = W.shape
+    assert K % 32 == 0 and G % 32 == 0 and G > 0 and K % G == 0
+    idx = np.ascontiguousarray(np.asarray(weak_idx, dtype=np.int32))
+    k = idx.shape[0]
+    q = np.zeros((N, K // 32, 3), np.uint32)
+    s = np.zeros((N, K // G), np.uint16)
+    z = np.zeros((N, K // G), np.uint8)
+    ww = np.zeros((N, max(k, 1)), np.uint16)
+    load().owq_oracle_pack_grouped(_ptr(W), N, K, _ptr(idx) if k else None, k, int(G),
+                                   _ptr(q), _ptr(s), _ptr(z), _ptr(ww))
+    return {"qcodes": q, "scales": s, "zeros": z,
+            "w_weak": np.ascontiguousarray(ww[:, :k]), "weak_idx": idx, "group": int(G)}
+
+
+def linear_grouped_rows(layer: dict, x, rows=None, threads: int = 0):
+    """fp64 y and bound [M][len(rows)] of the group-wise form (all rows if None)."""
+    q = np.ascontiguousarray(layer["qcodes"], dtype=np.uint32)
+    s = _u16(layer["scales"])
+    z = np.ascontiguousarray(layer["zeros"], dtype=np.uint8)
+    idx = np.ascontiguousarray(layer["weak_idx"], dtype=np.int32)
+    ww = _u16(layer["w_weak"])
+    G = int(layer["group"])
+    x = _u16(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    M, K = x.shape
+    N = q.shape[0]
+    assert q.shape[1] * 32 == K and s.shape == (N, K // G) and z.shape == (N, K // G)
+    k = idx.shape[0]
+    rows = np.arange(N, dtype=np.int64) if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    assert rows.ndim == 1 and (rows >= 0).all() and (rows < N).all()
+    R = rows.shape[0]
+    y = np.zeros((M, R), np.float64)
+    b = np.zeros((M, R), np.float64)
+    load().owq_oracle_linear_grouped_rows(_ptr(q), _ptr(s), _ptr(z), N, K, G,
+                                          _ptr(idx) if k else None, _ptr(ww) if k else None, k,
+                                          _ptr(x), M, _ptr(rows), R, _ptr(y), _ptr(b), int(threads))
+    return y, b

@@ -946,6 +946,99 @@ void owq_oracle_linear_rows(const uint32_t* qcodes, const uint16_t* scales,
     free(xf);
 }
 
+/* ---------------------------------------------------- group-wise scales ---- */
+
+/* Group-wise quantisation on top of OWQ: each output row is split into groups of
+ * G consecutive input columns, and every (row, group) gets a step size and zero
+ * point of its own ([PL] "Comparison with group-wise quantization", paper p.8,
+ * which reports that it adds little on top of OWQ; the group size there is
+ * OPTQ's 128). Readings (the pages give no format): G is a multiple of 32 that
+ * divides K; each (row, group) is fitted exactly like a row (R1-R4) on the
+ * group's dense columns only (R5), so a group of weak columns only, or one whose
+ * dense entries are all 0, gets step 1 and zero point 0 (R2); weak columns keep
+ * their group's zero point as code; codes keep the R7 layout; scales and zeros
+ * are [N][K/G], group-major within a row. */
+void owq_oracle_pack_grouped(const uint16_t* W, int64_t N, int64_t K,
+                             const int32_t* weak_idx, int32_t k, int64_t G,
+                             uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                             uint16_t* w_weak)
+{
+    uint8_t* weak = (uint8_t*)calloc((size_t)K, 1);
+    uint8_t* dense = (uint8_t*)malloc((size_t)K);
+    for (int32_t c = 0; c < k; c++)
+        weak[weak_idx[c]] = 1;
+    for (int64_t j = 0; j < K; j++)
+        dense[j] = !weak[j];
+    int64_t NG = K / G, CG = G / 32;
+    for (int64_t i = 0; i < N; i++) {
+        const uint16_t* row = W + i * K;
+        for (int64_t g = 0; g < NG; g++) {
+            uint16_t s16;
+            uint8_t z;
+            owq_oracle_qparams(row + g * G, dense + g * G, G, &s16, &z);
+            pack_row(row + g * G, weak + g * G, CG, s16, z, qcodes + (i * (K / 32) + g * CG) * 3);
+            scales[i * NG + g] = s16;
+            zeros[i * NG + g] = z;
+        }
+        for (int32_t c = 0; c < k; c++)
+            w_weak[i * k + c] = row[weak_idx[c]];
+    }
+    free(weak);
+    free(dense);
+}
+
+/* The product of the group-wise form for every token and a list of rows (rows
+ * over OpenMP threads, threads <= 0: the OpenMP default): y[m][r] = sum_j
+ * s_ig (q_ij - z_ig) x[m][j] + sum_c w_weak[i][c] x[m][idx_c] with g = j / G,
+ * one fp64 sum per output in column order, then the weak columns; bound[m][r]
+ * is the same sum of absolute terms. y and bound are [M][R]. */
+void owq_oracle_linear_grouped_rows(const uint32_t* qcodes, const uint16_t* scales,
+                                    const uint8_t* zeros, int64_t N, int64_t K, int64_t G,
+                                    const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,
+                                    const uint16_t* x, int64_t M,
+                                    const int64_t* rows, int64_t R, double* y, double* bound,
+                                    int threads)
+{
+    (void)N;
+    int64_t NC = K / 32, NG = K / G;
+    double* xf = (double*)malloc((size_t)(M * K) * sizeof(double));
+    for (int64_t e = 0; e < M * K; e++)
+        xf[e] = owq_oracle_f16_to_f64(x[e]);
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+    {
+        double* wd = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < R; r++) {
+            int64_t i = rows[r];
+            for (int64_t j = 0; j < K; j++) {
+                int64_t g = j / G;
+                double s = owq_oracle_f16_to_f64(scales[i * NG + g]);
+                int z = zeros[i * NG + g];
+                wd[j] = s * (double)(get_code(qcodes + (i * NC + j / 32) * 3, (int)(j % 32)) - z);
+            }
+            for (int64_t m = 0; m < M; m++) {
+                const double* xm = xf + m * K;
+                double acc = 0.0, bnd = 0.0;
+                for (int64_t j = 0; j < K; j++) {
+                    double t = wd[j] * xm[j];
+                    acc += t;
+                    bnd += fabs(t);
+                }
+                for (int32_t c = 0; c < k; c++) {
+                    double tw = owq_oracle_f16_to_f64(w_weak[i * k + c]) * xm[weak_idx[c]];
+                    acc += tw;
+                    bnd += fabs(tw);
+                }
+                y[m * R + r] = acc;
+                bound[m * R + r] = bnd;
+            }
+        }
+        free(wd);
+    }
+    free(xf);
+}
+
 /* Effective bit-width. The storage-favoured format drops the zero-filled codes
  * of the k weak columns and adds them in fp16 (16 - 3 = 13 extra bits per weak
  * weight); the latency-favoured format keeps the full 3-bit matrix (16 extra

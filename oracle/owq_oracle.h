@@ -122,6 +122,18 @@ void owq_oracle_linear_pairs(const uint32_t* qcodes, const uint16_t* scales,
 /* All M tokens of the listed rows (OpenMP over rows; threads <= 0: default).
  * Each output equals owq_oracle_linear_pairs' for that (token, row) bit for bit.
  * y[m][r], bound[m][r] for row rows[r]. */
+/* Group-wise scales on top of OWQ: a step and zero point per (row, group of G
+ * columns), G a multiple of 32 dividing K; scales and zeros are [N][K/G]. */
+void owq_oracle_pack_grouped(const uint16_t* W, int64_t N, int64_t K,
+                             const int32_t* weak_idx, int32_t k, int64_t G,
+                             uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                             uint16_t* w_weak);
+void owq_oracle_linear_grouped_rows(const uint32_t* qcodes, const uint16_t* scales,
+                                    const uint8_t* zeros, int64_t N, int64_t K, int64_t G,
+                                    const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,
+                                    const uint16_t* x, int64_t M,
+                                    const int64_t* rows, int64_t R, double* y, double* bound,
+                                    int threads);
 void owq_oracle_linear_rows(const uint32_t* qcodes, const uint16_t* scales,
                             const uint8_t* zeros, int64_t N, int64_t K,
                             const int32_t* weak_idx, const uint16_t* w_weak, int32_t k,

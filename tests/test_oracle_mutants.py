@@ -58,6 +58,12 @@ MUTANTS = {
     "search fits the weak columns too": ("owq_oracle_search_qparams(row, dense, K, lambda,",
                                          "owq_oracle_search_qparams(row, NULL, K, lambda,"),
     "search rounds the quotient down": ("float r = rintf(wf[e] / sf);", "float r = floorf(wf[e] / sf);"),
+    "groups fit the weak columns too": ("owq_oracle_qparams(row + g * G, dense + g * G, G, &s16, &z);",
+                                        "owq_oracle_qparams(row + g * G, NULL, G, &s16, &z);"),
+    "groups share the first group's step": ("scales[i * NG + g] = s16;", "scales[i * NG + g] = scales[i * NG];"),
+    "grouped product reads the row's first step": ("double s = owq_oracle_f16_to_f64(scales[i * NG + g]);",
+                                                   "double s = owq_oracle_f16_to_f64(scales[i * NG]);"),
+    "grouped product ignores the zero point": ("int z = zeros[i * NG + g];", "int z = 0;"),
     "backward drops the weak columns": ("Wf[i * K + weak_idx[c]] += owq_oracle_f16_to_f64(w_weak[i * k + c]);",
                                         "Wf[i * K + weak_idx[c]] += 0.0 * owq_oracle_f16_to_f64(w_weak[i * k + c]);"),
     "backward zero point sign": ("Wf[i * K + j] = s * (double)(get_code(qcodes + (i * G + j / 32) * 3, (int)(j % 32)) - z);",
