@@ -310,7 +310,9 @@ typedef struct {
  *   y[m][i] = s_i * sum_j (q_ij - z_i) x[m][j] + sum_c w_weak[i][c] x[m][weak_idx[c]]
  * computed with fp32 accumulation and rounded to fp16 (nearest-even).
  * L: HOST pointer to the layer; x: fp16 [M][K]; y: fp16 [M][N] (output, must not
- * alias x or the layer). M <= 2 runs an HBM-streaming kernel on the vector ALUs,
+ * alias x or the layer). M <= 2 runs an HBM-streaming kernel that decodes on the
+ * vector ALUs (one token multiplies there too, two on the matrix cores;
+ * OWQ_GEMV_PRODUCTS=dot2|mfma, read at each call, overrides that choice),
  * 3 <= M <= 16 a streaming kernel that multiplies on the matrix cores, larger M a
  * tiled matrix-core (MFMA) GEMM; all compute the same definition. The environment
  * variable OWQ_DECODE (read at each call) overrides the first split: "matrix"
@@ -345,6 +347,51 @@ size_t owq_linear_storage_workspace_bytes(int64_t K, int32_t k, int64_t M);
 owq_status owq_linear_storage(const owq_layer* L, const uint16_t* x, int64_t M,
                               uint16_t* y, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* ------------------------------------------------------- group-wise form --- */
+
+/* Group-wise scales on top of OWQ ([PL] "Comparison with group-wise
+ * quantization", paper p.8: a step size and zero point per group of input
+ * columns, which the pages find adds little to OWQ; their grouped baseline uses
+ * groups of 128). Definition (the pages give no format; these details are the
+ * library's): row i is split into groups of G consecutive columns; each (row,
+ * group) is fitted like a row of owq_pack on the group's dense columns only
+ * (lo = min(0, min w), hi = max(0, max w), step fp16((hi - lo) / 7), zero point
+ * clamp(rint(-lo / step), 0, 7); hi == lo, or a step that rounds to fp16 zero,
+ * gives step 1 and zero point 0, as for a group of weak columns only); dense
+ * codes are clamp(rint(w / step) + z, 0, 7), weak columns take their group's
+ * zero point; codes in owq_pack's slot layout. G must be a power of two from 32
+ * to 2048 dividing K (OWQ_ERR_UNSUPPORTED otherwise).
+ * scales: fp16 [N][K/G], zeros: uint8 [N][K/G] (group-major within a row);
+ * other arguments, layouts and errors as owq_pack. Bitwise reproducible. */
+owq_status owq_pack_grouped(const uint16_t* W, int64_t N, int64_t K,
+                            const int32_t* weak_idx, int32_t k, int64_t G,
+                            uint32_t* qcodes, uint16_t* scales, uint8_t* zeros,
+                            uint16_t* w_weak, void* stream);
+
+/* One layer in the group-wise form (owq_pack_grouped). HOST struct, device
+ * pointers. */
+typedef struct {
+    int64_t N, K, G;            /* output rows, input columns, columns per group */
+    int32_t k;                  /* weak columns */
+    int32_t bits;               /* must be 3 */
+    const uint32_t* qcodes;     /* [N][K/32][3] */
+    const uint16_t* scales;     /* fp16 [N][K/G] */
+    const uint8_t* zeros;       /* [N][K/G] */
+    const int32_t* weak_idx;    /* [k], ascending (NULL iff k == 0) */
+    const uint16_t* w_weak;     /* fp16 [N][k] (NULL iff k == 0) */
+} owq_grouped_layer;
+
+/* Product of the group-wise form ([PL] "Comparison with group-wise
+ * quantization", p.8, on the product of "Real-device acceleration", p.6):
+ *   y[m][i] = sum_g s_ig sum_{j in g} (q_ij - z_ig) x[m][j] + sum_c w_weak[i][c] x[m][weak_idx[c]]
+ * with exact fp16 products, fp32 sums (one per 32 columns, scaled by its
+ * group's step) and an fp16 output (nearest-even). x: fp16 [M][K], y: fp16
+ * [M][N] (must not alias x or the layer). One launch per 4 tokens (a vector-ALU
+ * kernel, a wavefront per row). Errors as owq_linear, plus OWQ_ERR_UNSUPPORTED
+ * for a G that owq_pack_grouped rejects. */
+owq_status owq_linear_grouped(const owq_grouped_layer* L, const uint16_t* x, int64_t M,
+                              uint16_t* y, void* stream);
 
 /* Bytes of device workspace owq_linear_storage_batched needs for these layers
  * at M tokens: their owq_linear_storage_workspace_bytes, each rounded up to 256

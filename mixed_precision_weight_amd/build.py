@@ -28,12 +28,12 @@ COMMON = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
           "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I" + os.path.join(ROOT, "include")]
-NO_CONTRACT = {"calib.hip", "pack.hip", "search.hip", "storage.hip", "optq.hip", "backward.hip"}
+NO_CONTRACT = {"calib.hip", "pack.hip", "grouped.hip", "search.hip", "storage.hip", "optq.hip", "backward.hip"}
 RESOURCES = os.path.join(BUILD, "kernel_resources.json")
 _REMARK = re.compile(r"remark: +(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
                      r"Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]): (\S+)")
 SOURCES = ["api.cpp", "calib.hip", "topk.hip", "pack.hip", "search.hip", "storage.hip", "backward.hip", "optq.hip",
-           "gemv.hip", "mfv.hip", "gemm.hip", "stream.hip"]
+           "gemv.hip", "mfv.hip", "gemm.hip", "stream.hip", "grouped.hip"]
 
 
 def _resources(stderr: str) -> dict:

@@ -664,6 +664,53 @@ owq_status owq_linear_backward_batched(const owq_layer* Ls, const uint16_t* cons
     return hip_status(e, "owq_linear_backward_batched launch");
 }
 
+owq_status owq_pack_grouped(const uint16_t* W, int64_t N, int64_t K, const int32_t* weak_idx, int32_t k,
+                            int64_t G, uint32_t* qcodes, uint16_t* scales, uint8_t* zeros, uint16_t* w_weak,
+                            void* stream)
+{
+    if (!W || !qcodes || !scales || !zeros)
+        return fail(OWQ_ERR_NULL, "W, qcodes, scales and zeros must be non-NULL");
+    if (N < 1 || N > INT32_MAX)
+        return fail(OWQ_ERR_SHAPE, "N = %lld out of range", (long long)N);
+    owq_status st = check_k_dim(K);
+    if (st != OWQ_OK)
+        return st;
+    if (!owq::grouped_size_supported(G, K))
+        return fail(OWQ_ERR_UNSUPPORTED, "G = %lld: need a power of two in [32, 2048] dividing K = %lld",
+                    (long long)G, (long long)K);
+    if (k < 0 || k > K)
+        return fail(OWQ_ERR_RANGE, "k = %d outside [0, K = %lld]", k, (long long)K);
+    if (k > 0 && (!weak_idx || !w_weak))
+        return fail(OWQ_ERR_NULL, "weak_idx and w_weak must be non-NULL when k > 0");
+    if (!aligned(W, 16) || !aligned(qcodes, 4) || !aligned(scales, 2) ||
+        (k > 0 && (!aligned(weak_idx, 4) || !aligned(w_weak, 2))))
+        return fail(OWQ_ERR_ALIGN, "misaligned pointer (W: 16 B, qcodes/weak_idx: 4 B, fp16: 2 B)");
+    st = check_idx_on_host(weak_idx, k, K, (hipStream_t)stream);
+    if (st != OWQ_OK)
+        return st;
+    return hip_status(owq::launch_pack_grouped(W, N, K, k > 0 ? weak_idx : nullptr, k, G, qcodes, scales, zeros,
+                                               k > 0 ? w_weak : nullptr, (hipStream_t)stream),
+                      "owq_pack_grouped launch");
+}
+
+owq_status owq_linear_grouped(const owq_grouped_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* stream)
+{
+    if (!L)
+        return fail(OWQ_ERR_NULL, "layer is NULL");
+    owq_layer base{L->N, L->K, L->k, L->bits, L->qcodes, L->scales, L->zeros, L->weak_idx, L->w_weak};
+    owq_status st = check_layer(&base, M, x, y);
+    if (st != OWQ_OK)
+        return st;
+    if (!owq::grouped_size_supported(L->G, L->K))
+        return fail(OWQ_ERR_UNSUPPORTED, "G = %lld: need a power of two in [32, 2048] dividing K = %lld",
+                    (long long)L->G, (long long)L->K);
+    st = check_idx_on_host(L->weak_idx, L->k, L->K, (hipStream_t)stream);
+    if (st != OWQ_OK)
+        return st;
+    return hip_status(owq::launch_linear_grouped(desc_of(&base, x, y), L->G, M, (hipStream_t)stream),
+                      "owq_linear_grouped launch");
+}
+
 owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* stream)
 {
     owq_status st = check_layer(L, M, x, y);

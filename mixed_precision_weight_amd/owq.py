@@ -42,6 +42,13 @@ class OwqLayer(ctypes.Structure):
                 ("weak_idx", _P), ("w_weak", _P)]
 
 
+class OwqGroupedLayer(ctypes.Structure):
+    """Mirror of ``owq_grouped_layer`` (host struct, device pointers)."""
+    _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64), ("G", ctypes.c_int64), ("k", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("qcodes", _P), ("scales", _P), ("zeros", _P),
+                ("weak_idx", _P), ("w_weak", _P)]
+
+
 EXPORTS = {
     "owq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "owq_last_error": (ctypes.c_char_p, []),
@@ -75,6 +82,8 @@ EXPORTS = {
     "owq_linear": (ctypes.c_int, [ctypes.POINTER(OwqLayer), _P, _I64, _P, _P]),
     "owq_linear_batched": (ctypes.c_int, [ctypes.POINTER(OwqLayer), ctypes.POINTER(_P),
                                           ctypes.POINTER(_P), _I32, _I64, _P]),
+    "owq_pack_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _I64, _P, _P, _P, _P, _P]),
+    "owq_linear_grouped": (ctypes.c_int, [ctypes.POINTER(OwqGroupedLayer), _P, _I64, _P, _P]),
     "owq_stream_read_sink_words": (_I64, [_I64]),
     "owq_stream_read": (ctypes.c_int, [_P, _I64, _P, _I64, _P]),
 }
@@ -636,6 +645,72 @@ def linear(layer: dict, x: torch.Tensor, y: torch.Tensor | None = None, stream=N
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     _check(lib().owq_linear(ctypes.byref(L), _ptr(x), M, _ptr(y), _stream(stream)), "owq_linear")
+    return y
+
+
+def pack_grouped(W: torch.Tensor, weak_idx: torch.Tensor, G: int, out: dict | None = None, stream=None) -> dict:
+    """Group-wise packed layer (owq_pack_grouped): qcodes int32 [N][K/32][3],
+    scales fp16 [N][K/G], zeros uint8 [N][K/G], w_weak fp16 [N][k], weak_idx,
+    and the group size under "group"."""
+    _meta(W, torch.float16, "W")
+    _meta(weak_idx, torch.int32, "weak_idx")
+    if W.dim() != 2 or weak_idx.dim() != 1:
+        raise ValueError(f"W must be 2-D and weak_idx 1-D, got {tuple(W.shape)} and {tuple(weak_idx.shape)}")
+    N, K = W.shape
+    k = weak_idx.numel()
+    G = int(G)
+    if K % 32 or k > K:
+        raise ValueError(f"K = {K} must be a multiple of 32 and k = {k} at most K")
+    if G < 32 or G > 2048 or G & (G - 1) or K % G:
+        raise ValueError(f"G = {G}: need a power of two in [32, 2048] dividing K = {K}")
+    want = {"qcodes": ((N, K // 32, 3), torch.int32), "scales": ((N, K // G), torch.float16),
+            "zeros": ((N, K // G), torch.uint8), "w_weak": ((N, k), torch.float16)}
+    if out is not None:
+        for name, (shape, dt) in want.items():
+            if name not in out:
+                raise ValueError(f"out lacks {name!r}")
+            _meta(out[name], dt, f"out[{name!r}]", shape)
+    _on_device(("W", W), ("weak_idx", weak_idx), *[(f"out[{n!r}]", out[n]) for n in (want if out else ())])
+    if out is None:
+        out = {name: torch.empty(shape, dtype=dt, device=W.device) for name, (shape, dt) in want.items()}
+    out["weak_idx"] = weak_idx
+    out["group"] = G
+    _check(lib().owq_pack_grouped(_ptr(W), N, K, _ptr(weak_idx) if k else None, k, G, _ptr(out["qcodes"]),
+                                  _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["w_weak"]) if k else None,
+                                  _stream(stream)), "owq_pack_grouped")
+    return out
+
+
+def grouped_layer_struct(layer: dict) -> OwqGroupedLayer:
+    """Checked host struct of a group-wise layer dict."""
+    if "group" not in layer:
+        raise ValueError("layer lacks 'group'")
+    G = int(layer["group"])
+    q = _meta(layer["qcodes"], torch.int32, "qcodes")
+    if q.dim() != 3 or q.shape[2] != 3:
+        raise ValueError(f"qcodes must be [N][K/32][3], got {tuple(q.shape)}")
+    N, K = q.shape[0], q.shape[1] * 32
+    if G < 32 or K % G:
+        raise ValueError(f"G = {G} does not divide K = {K}")
+    idx = _meta(layer["weak_idx"], torch.int32, "weak_idx")
+    if idx.dim() != 1:
+        raise ValueError(f"weak_idx must be 1-D, got {tuple(idx.shape)}")
+    k = idx.numel()
+    _meta(layer["scales"], torch.float16, "scales", (N, K // G))
+    _meta(layer["zeros"], torch.uint8, "zeros", (N, K // G))
+    _meta(layer["w_weak"], torch.float16, "w_weak", (N, k))
+    return OwqGroupedLayer(N, K, G, k, 3, q.data_ptr(), layer["scales"].data_ptr(), layer["zeros"].data_ptr(),
+                           idx.data_ptr() if k else None, layer["w_weak"].data_ptr() if k else None)
+
+
+def linear_grouped(layer: dict, x: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = x W^T (fp16 [M][N]) for a group-wise packed layer (owq_linear_grouped)."""
+    L = grouped_layer_struct(layer)
+    M = _xy_shapes(L.N, L.K, x, y)
+    _on_device(("x", x), ("y", y), *_layer_named(layer))
+    if y is None:
+        y = torch.empty((M, L.N), dtype=torch.float16, device=x.device)
+    _check(lib().owq_linear_grouped(ctypes.byref(L), _ptr(x), M, _ptr(y), _stream(stream)), "owq_linear_grouped")
     return y
 
 

@@ -358,3 +358,33 @@ def test_calibrate_noalloc_validation(lib):
     assert lib.owq_calibrate_workspace_bytes(N, 4096, 16) > cap
     assert f(FAKE, N, 4096, FAKE, 16, FAKE, FAKE, None) == 6
     assert "library's own" in _err(lib)
+
+
+def test_pack_grouped_validation(lib):
+    f = lib.owq_pack_grouped
+    assert f(None, 8, 256, FAKE, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE, 8, 256, None, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE, 8, 255, FAKE, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert f(FAKE, 0, 256, FAKE, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
+    for G in (0, 16, 96, 512, 4096):  # not a power of two in [32, 2048] dividing K = 256
+        assert f(FAKE, 8, 256, FAKE, 2, G, FAKE, FAKE, FAKE, FAKE, None) == 5, G
+    assert f(FAKE, 8, 256, FAKE, 257, 128, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert f(FAKE + 8, 8, 256, FAKE, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == 4
+
+
+def test_linear_grouped_validation(lib):
+    from mixed_precision_weight_amd import owq
+
+    def layer(N=8, K=256, G=128, k=2, bits=3):
+        return ctypes.byref(owq.OwqGroupedLayer(N, K, G, k, bits, FAKE, FAKE, FAKE, FAKE, FAKE))
+
+    f = lib.owq_linear_grouped
+    assert f(None, FAKE, 1, FAKE, None) == 1
+    assert f(layer(), None, 1, FAKE, None) == 1
+    assert f(layer(K=250), FAKE, 1, FAKE, None) == 2
+    assert f(layer(), FAKE, 0, FAKE, None) == 2
+    assert f(layer(G=96), FAKE, 1, FAKE, None) == 5
+    assert f(layer(G=512), FAKE, 1, FAKE, None) == 5
+    assert f(layer(bits=4), FAKE, 1, FAKE, None) == 5
+    assert f(layer(k=300), FAKE, 1, FAKE, None) == 3
+    assert f(layer(), FAKE + 8, 1, FAKE, None) == 4

@@ -187,3 +187,34 @@ def test_select_batched_checks_shapes():
     with pytest.raises(ValueError, match="1-D"):
         owq.select_weak_batched([a, b.reshape(2, K)], [3, 4])
     _host_only(owq.select_weak_batched, [a, b], [3, 4])
+
+
+def _grouped_layer(N=N, K=K, k=k, G=64):
+    lay = _layer(N, K, k)
+    lay["scales"] = torch.zeros((N, K // G), dtype=torch.float16)
+    lay["zeros"] = torch.zeros((N, K // G), dtype=torch.uint8)
+    lay["group"] = G
+    return lay
+
+
+def test_grouped_checks_shapes():
+    W = torch.zeros((N, K), dtype=torch.float16)
+    idx = torch.arange(k, dtype=torch.int32)
+    for G in (48, 256, 4096):
+        with pytest.raises(ValueError, match="G ="):
+            owq.pack_grouped(W, idx, G)
+    bad_out = {"qcodes": torch.zeros((N, K // 32, 3), dtype=torch.int32),
+               "scales": torch.zeros(N, dtype=torch.float16),  # per-row shape, not [N][K/G]
+               "zeros": torch.zeros((N, K // 64), dtype=torch.uint8),
+               "w_weak": torch.zeros((N, k), dtype=torch.float16)}
+    with pytest.raises(ValueError, match="scales"):
+        owq.pack_grouped(W, idx, 64, out=bad_out)
+    _host_only(owq.pack_grouped, W, idx, 64)
+    lay = _grouped_layer()
+    with pytest.raises(ValueError, match="columns"):
+        owq.linear_grouped(lay, torch.zeros((1, K - 32), dtype=torch.float16))
+    with pytest.raises(ValueError, match="scales"):
+        owq.linear_grouped(dict(lay, group=32), torch.zeros((1, K), dtype=torch.float16))
+    with pytest.raises(ValueError, match="y has shape"):
+        owq.linear_grouped(lay, torch.zeros((2, K), dtype=torch.float16), torch.zeros((1, N), dtype=torch.float16))
+    _host_only(owq.linear_grouped, lay, torch.zeros((3, K), dtype=torch.float16))
