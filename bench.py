@@ -734,6 +734,39 @@ def main():
             us_latency_form=round(dec_s * 1e6, 2))
         del sto, wss
 
+        # group-wise scales on top of OWQ (the pages' grouped comparison, groups
+        # of 128 columns): pack of the 7 linears, and their product at M = 1
+        # (one launch per linear), 8 copies rotated, from a HIP graph
+        print("bench: group-wise form", file=sys.stderr, flush=True)
+        GW = 128
+        grp = [[owq.pack_grouped(W[li], slots[r][li]["weak_idx"], GW) for li in range(L)] for r in range(ROTATE)]
+        torch.cuda.synchronize()
+
+        def grouped_decode():
+            for r in range(ROTATE):
+                owq.linear_grouped_batched(grp[r], xd, yd)
+
+        def grouped_pack():
+            for r in range(ROTATE):
+                for li in range(L):
+                    owq.pack_grouped(W[li], slots[r][li]["weak_idx"], GW, out=grp[r][li])
+
+        t = graph_time(grouped_decode)
+        tp = graph_time(grouped_pack)
+        g_bytes = sum(3 * s.N * s.K // 8 + 3 * s.N * (s.K // GW) + 2 * s.N * s.k + 2 * s.K for s in specs)
+        gp_bytes = sum(2 * s.N * s.K + 4 * s.k + 3 * s.N * s.K // 8 + 3 * s.N * (s.K // GW) + 2 * s.N * s.k
+                       for s in specs)
+        result["kernels"]["decode_grouped_form"] = dict(
+            hbm_entry(g_bytes, t, f"group-wise form (a step and zero point per row and {GW} columns) at M=1: "
+                                  "owq_linear_grouped_batched over the 7 linears (k_gemv_grouped<1>: the decode kernel "
+                                  "with a zero point and step per 32-column code group), one launch per layer, 8 "
+                                  "copies rotated, replayed from a HIP graph (device time)"),
+            us_latency_form=round(dec_s * 1e6, 2))
+        result["kernels"]["pack_grouped"] = hbm_entry(
+            gp_bytes, tp, f"owq_pack_grouped, G = {GW}, the 7 linears (k_pack_grouped, a thread per 32 columns, "
+                          "+ k_weak_copy), from a HIP graph (device time)")
+        del grp
+
         # one GPU's share of the layer under 8-way column-parallel sharding (the
         # multi-GPU layout: every GPU holds N / 8 rows of each linear, x and the
         # weak index set replicated, no exchange for y = W x): the same batched

@@ -387,11 +387,19 @@ typedef struct {
  *   y[m][i] = sum_g s_ig sum_{j in g} (q_ij - z_ig) x[m][j] + sum_c w_weak[i][c] x[m][weak_idx[c]]
  * with exact fp16 products, fp32 sums (one per 32 columns, scaled by its
  * group's step) and an fp16 output (nearest-even). x: fp16 [M][K], y: fp16
- * [M][N] (must not alias x or the layer). One launch per 4 tokens (a vector-ALU
- * kernel, a wavefront per row). Errors as owq_linear, plus OWQ_ERR_UNSUPPORTED
- * for a G that owq_pack_grouped rejects. */
+ * [M][N] (must not alias x or the layer). One launch of the vector-ALU decode
+ * kernel (owq_linear's, in its group-wise mode) per 4 tokens. Errors as
+ * owq_linear, plus OWQ_ERR_UNSUPPORTED for a G that owq_pack_grouped rejects. */
 owq_status owq_linear_grouped(const owq_grouped_layer* L, const uint16_t* x, int64_t M,
                               uint16_t* y, void* stream);
+
+/* `count` independent group-wise linears with the same M (e.g. the 7 linears of
+ * a decoder layer) in ONE decode launch per 16 layers, bit for bit the results of
+ * owq_linear_grouped one by one. Ls: HOST array [count]; xs, ys: HOST arrays
+ * [count] of device pointers with owq_linear_grouped's shapes. Returns
+ * OWQ_ERR_UNSUPPORTED unless 1 <= M <= 4 and 1 <= count <= 64. */
+owq_status owq_linear_grouped_batched(const owq_grouped_layer* Ls, const uint16_t* const* xs,
+                                      uint16_t* const* ys, int32_t count, int64_t M, void* stream);
 
 /* Bytes of device workspace owq_linear_storage_batched needs for these layers
  * at M tokens: their owq_linear_storage_workspace_bytes, each rounded up to 256

@@ -707,8 +707,51 @@ owq_status owq_linear_grouped(const owq_grouped_layer* L, const uint16_t* x, int
     st = check_idx_on_host(L->weak_idx, L->k, L->K, (hipStream_t)stream);
     if (st != OWQ_OK)
         return st;
-    return hip_status(owq::launch_linear_grouped(desc_of(&base, x, y), L->G, M, (hipStream_t)stream),
-                      "owq_linear_grouped launch");
+    const owq::LinearDesc d = desc_of(&base, x, y);
+    hipError_t e = hipSuccess;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += owq::kGemvMaxM) {  // token slices
+        const int64_t mm = M - m0 < owq::kGemvMaxM ? M - m0 : owq::kGemvMaxM;
+        owq::LinearDesc dm = d;
+        dm.x = d.x + m0 * d.K;
+        dm.y = d.y + m0 * d.N;
+        e = owq::launch_gemv_grouped(&dm, &L->G, 1, (int)mm, (hipStream_t)stream);
+    }
+    return hip_status(e, "owq_linear_grouped launch");
+}
+
+owq_status owq_linear_grouped_batched(const owq_grouped_layer* Ls, const uint16_t* const* xs, uint16_t* const* ys,
+                                      int32_t count, int64_t M, void* stream)
+{
+    if (!Ls || !xs || !ys)
+        return fail(OWQ_ERR_NULL, "Ls, xs and ys must be non-NULL");
+    if (count < 1 || count > 64)
+        return fail(OWQ_ERR_UNSUPPORTED, "count = %d: need 1 <= count <= 64", count);
+    if (M < 1 || M > owq::kGemvMaxM)
+        return fail(OWQ_ERR_UNSUPPORTED, "M = %lld: the batched group-wise launch needs 1 <= M <= %d",
+                    (long long)M, owq::kGemvMaxM);
+    std::vector<owq::LinearDesc> d((size_t)count);
+    std::vector<int64_t> groups((size_t)count);
+    for (int32_t l = 0; l < count; l++) {
+        const owq_grouped_layer& g = Ls[l];
+        owq_layer base{g.N, g.K, g.k, g.bits, g.qcodes, g.scales, g.zeros, g.weak_idx, g.w_weak};
+        owq_status st = check_layer(&base, M, xs[l], ys[l]);
+        if (st != OWQ_OK)
+            return fail_at(st, "layer", l);
+        if (!owq::grouped_size_supported(g.G, g.K))
+            return fail(OWQ_ERR_UNSUPPORTED, "layer %d: G = %lld: need a power of two in [32, 2048] dividing K = %lld",
+                        l, (long long)g.G, (long long)g.K);
+        st = check_idx_on_host(g.weak_idx, g.k, g.K, (hipStream_t)stream);
+        if (st != OWQ_OK)
+            return st;
+        d[l] = desc_of(&base, xs[l], ys[l]);
+        groups[l] = g.G;
+    }
+    hipError_t e = hipSuccess;
+    for (int32_t l0 = 0; l0 < count && e == hipSuccess; l0 += owq::kGemvMaxLayers) {
+        const int n = count - l0 < owq::kGemvMaxLayers ? count - l0 : owq::kGemvMaxLayers;
+        e = owq::launch_gemv_grouped(d.data() + l0, groups.data() + l0, n, (int)M, (hipStream_t)stream);
+    }
+    return hip_status(e, "owq_linear_grouped_batched launch");
 }
 
 owq_status owq_linear(const owq_layer* L, const uint16_t* x, int64_t M, uint16_t* y, void* stream)

@@ -61,6 +61,7 @@ struct GemvLayer {
     uint16_t* y;
     int32_t N, K, k;
     int32_t block0;  // first block of this layer
+    int32_t gsh;     // group-wise form: log2 of the 32-column code groups per scale group
 };
 
 struct GemvBatch {
@@ -120,9 +121,13 @@ __device__ __forceinline__ int reduced_index(int q) { return (q & 1) + ((q >> 1)
 // is issued before the first wait, so a chunk costs one memory latency; the
 // hardware overlaps the arithmetic of resident blocks with the loads of others.
 // Layers of any K share this one kernel, so a batch is a single launch.
-template <int M, bool MMA, int R>
+// GRP: the group-wise form (s and z are [N][K / G], one per row and G columns):
+// each code group is decoded with its own zero point, its dot2 sum starts from 0
+// and is scaled by its group's step into the row's accumulator.
+template <int M, bool MMA, int R, bool GRP = false>
 __device__ __forceinline__ void gemv_body(const GemvBatch& b)
 {
+    static_assert(!(GRP && MMA), "the group-wise form scales each lane's partial sum");
     constexpr int TT = kChunkTiles;
     constexpr int GC = 64 * TT;  // groups per chunk
     extern __shared__ uint4 smem[];
@@ -154,6 +159,9 @@ __device__ __forceinline__ void gemv_body(const GemvBatch& b)
     constexpr int XP = M * PC / 256;  // staged pieces per thread
     uint4 xg[XP];
     u32x3 cw[R][TT];
+    uint32_t zq[GRP ? R : 1][GRP ? TT : 1], sq[GRP ? R : 1][GRP ? TT : 1];  // group-wise zero points, steps
+    const int gsh = b.L[li].gsh;
+    const int NGS = G >> gsh;  // scale groups per row
     // Every load below is unconditional (indices clamped to valid data): a load
     // under a divergent branch makes the compiler wait for it before the branch
     // merges, which would serialise the x latency in front of the code loads.
@@ -174,6 +182,18 @@ __device__ __forceinline__ void gemv_body(const GemvBatch& b)
 #pragma unroll
             for (int u = 0; u < TT; u++)
                 cw[r][u] = __builtin_amdgcn_raw_buffer_load_b96(qr, vrow[r] + (g0 + 64 * u) * 12, 0, kNonTemporal);
+        if constexpr (GRP) {
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const int64_t base = (int64_t)min(row0 + r, N - 1) * NGS;
+#pragma unroll
+                for (int u = 0; u < TT; u++) {
+                    const int gi = min(g0 + 64 * u + lane, G - 1) >> gsh;
+                    zq[r][u] = b.L[li].z[base + gi];
+                    sq[r][u] = b.L[li].s[base + gi];
+                }
+            }
+        }
     };
 
     // row steps and zero points first: they move to scalar registers below, and
@@ -182,8 +202,8 @@ __device__ __forceinline__ void gemv_body(const GemvBatch& b)
 #pragma unroll
     for (int r = 0; r < R; r++) {
         const int row = min(row0 + r, N - 1);
-        sv[r] = b.L[li].s[row];
-        zv[r] = b.L[li].z[row];
+        sv[r] = GRP ? 0x3c00u : b.L[li].s[row];  // the group-wise form scales per group instead
+        zv[r] = GRP ? 0u : b.L[li].z[row];
     }
     const int kc = k > 0 ? k : 1;  // with k == 0 the host passes valid dummy arrays
     int widx[2];  // weak indices: loaded early, so the gather's wait covers no code load
@@ -298,12 +318,12 @@ __device__ __forceinline__ void gemv_body(const GemvBatch& b)
             } else if (g < gc) {
 #pragma unroll
                 for (int r = 0; r < R; r++) {
-                    const ZeroSub nz = make_zero_sub(zr[r]);
+                    const ZeroSub nz = make_zero_sub(GRP ? zq[r][u] : zr[r]);
                     uint32_t p[16];
                     decode_group(cw[r][u].x, cw[r][u].y, cw[r][u].z, mg, nz, p);
 #pragma unroll
                     for (int m = 0; m < M; m++) {
-                        float a = acc[r][m];
+                        float a = GRP ? 0.0f : acc[r][m];
 #pragma unroll
                         for (int qd = 0; qd < 4; qd++) {
                             a = dot2(p[4 * qd + 0], xq[m][qd].x, a);
@@ -311,7 +331,7 @@ __device__ __forceinline__ void gemv_body(const GemvBatch& b)
                             a = dot2(p[4 * qd + 2], xq[m][qd].z, a);
                             a = dot2(p[4 * qd + 3], xq[m][qd].w, a);
                         }
-                        acc[r][m] = a;
+                        acc[r][m] = GRP ? __builtin_fmaf(h2f((uint16_t)sq[r][u]), a, acc[r][m]) : a;
                     }
                 }
             }
@@ -384,6 +404,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
     gemv_body<M, true, kRowsPerWave>(b);
 }
 
+// (97 registers at one token, four waves per SIMD: an occupancy bound of five
+// or six spills)
+template <int M>
+__global__ __launch_bounds__(256) void k_gemv_grouped(GemvBatch b)
+{
+    gemv_body<M, false, kRowsPerWave, true>(b);
+}
+
 template <int M>
 hipError_t launch_m(const GemvBatch& b, int nblocks, size_t lds, hipStream_t s)
 {
@@ -421,11 +449,13 @@ bool gemv_fits(int64_t M, int64_t K)
     return M >= 1 && M <= kGemvMaxM;
 }
 
-// One launch for the batch; blocks of 4 wavefronts, each wavefront owning
-// kRowsPerWave consecutive rows of its layer.
-hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
+namespace {
+
+// The launch arguments of a batch (layers with the longest rows first: their
+// blocks run longest); groups: the group-wise form's columns per scale group,
+// per layer, or NULL for the per-row form. Returns the block count.
+int build_batch(const LinearDesc* d, int count, const int64_t* groups, GemvBatch& b)
 {
-    // layers with the longest rows first: their blocks run longest
     int order[kGemvMaxLayers];
     for (int l = 0; l < count; l++)
         order[l] = l;
@@ -435,7 +465,7 @@ hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
             order[c] = order[c - 1];
             order[c - 1] = t;
         }
-    GemvBatch b{};
+    b = GemvBatch{};
     int nblocks = 0;
     for (int o = 0; o < count; o++) {
         const int l = order[o];
@@ -453,9 +483,24 @@ hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
         L.K = (int32_t)d[l].K;
         L.k = d[l].k;
         L.block0 = nblocks;
+        L.gsh = 0;
+        if (groups)
+            while ((int64_t)32 << L.gsh < groups[l])
+                L.gsh++;
         const int rows = 4 * kRowsPerWave;
         nblocks += (int)((d[l].N + rows - 1) / rows);
     }
+    return nblocks;
+}
+
+}  // namespace
+
+// One launch for the batch; blocks of 4 wavefronts, each wavefront owning
+// kRowsPerWave consecutive rows of its layer.
+hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
+{
+    GemvBatch b;
+    const int nblocks = build_batch(d, count, nullptr, b);
     const size_t lds = (size_t)M * kChunkTiles * 4 * kQuadStride * 16;
     switch (M) {
     case 1: return launch_m<1>(b, nblocks, lds, s);
@@ -463,6 +508,22 @@ hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
     case 3: return launch_m<3>(b, nblocks, lds, s);
     default: return launch_m<4>(b, nblocks, lds, s);
     }
+}
+
+hipError_t launch_gemv_grouped(const LinearDesc* d, const int64_t* groups, int count, int M, hipStream_t s)
+{
+    GemvBatch b;
+    const int nblocks = build_batch(d, count, groups, b);
+    const size_t lds = (size_t)M * kChunkTiles * 4 * kQuadStride * 16;
+#define OWQ_GG(MM) hipLaunchKernelGGL((k_gemv_grouped<MM>), dim3(nblocks), dim3(256), lds, s, b)
+    switch (M) {
+    case 1: OWQ_GG(1); break;
+    case 2: OWQ_GG(2); break;
+    case 3: OWQ_GG(3); break;
+    default: OWQ_GG(4); break;
+    }
+#undef OWQ_GG
+    return hipGetLastError();
 }
 
 }  // namespace owq

@@ -1,4 +1,5 @@
-// grouped.hip -- group-wise scales on top of OWQ (gfx950): pack and product.
+// grouped.hip -- group-wise scales on top of OWQ (gfx950): the pack. The product
+// runs in the decode kernel of gemv.hip (its group-wise mode).
 //
 // Every output row is split into groups of G consecutive input columns and each
 // (row, group) gets its own step size and zero point, on top of the fp16 weak
@@ -15,12 +16,10 @@
 // entries are zeroed first (the fitted range always contains 0, so a zero
 // changes neither end and gets the zero point as code), as in the per-row pack.
 //
-// Product: a wavefront per output row, lane l taking code groups l, l + 64, ...;
-// each group is decoded to exact (q - z) fp16 pairs (owq_decode.h) with its
-// own zero point, its 16 v_dot2 run from 0, and the group's step scales that
-// partial sum into the row's fp32 accumulator (one rounding). x comes straight
-// from global memory (64 contiguous bytes per lane and token). The weak columns
-// are added lane-strided, then a wave reduction and an fp16 store.
+// Product (gemv.hip, group-wise mode of the decode kernel): each 32-column code
+// group is decoded to exact (q - z) fp16 pairs with its own group's zero point,
+// its 16 v_dot2 run from 0, and its group's step scales that partial sum into
+// the row's fp32 accumulator (one rounding).
 //
 // Built with -ffp-contract=off: the quantiser steps are single IEEE operations.
 #include "owq_decode.h"
@@ -125,92 +124,6 @@ __global__ __launch_bounds__(256) void k_weak_copy(const uint16_t* __restrict__ 
     }
 }
 
-// Code groups per lane handled per batch of loads.
-constexpr int kGroupsPerBatch = 2;
-
-template <int M>
-__global__ __launch_bounds__(256) void k_linear_grouped(const uint32_t* __restrict__ q,
-                                                        const uint16_t* __restrict__ sc,
-                                                        const uint8_t* __restrict__ zp,
-                                                        const int32_t* __restrict__ idx,
-                                                        const uint16_t* __restrict__ ww,
-                                                        const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-                                                        int32_t N, int32_t K, int32_t k, int32_t G)
-{
-    const int lane = threadIdx.x & 63;
-    const int row = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (row >= N)
-        return;  // no block barrier below
-    const int NC = K >> 5, CG = G >> 5, NG = K / G;
-    const Magic mg = make_magic();
-    float acc[M];
-#pragma unroll
-    for (int m = 0; m < M; m++)
-        acc[m] = 0.0f;
-
-    for (int c0 = 0; c0 < NC; c0 += 64 * kGroupsPerBatch) {
-        u32x3 cw[kGroupsPerBatch];
-        uint32_t sv[kGroupsPerBatch], zv[kGroupsPerBatch];
-        uint4 xv[kGroupsPerBatch][M][4];
-        bool on[kGroupsPerBatch];
-        // every load of the batch first (clamped indices), then the arithmetic
-#pragma unroll
-        for (int u = 0; u < kGroupsPerBatch; u++) {
-            const int cg = c0 + 64 * u + lane;
-            on[u] = cg < NC;
-            const int cgc = on[u] ? cg : NC - 1;
-            const uint32_t* src = q + ((int64_t)row * NC + cgc) * 3;
-            cw[u] = u32x3{src[0], src[1], src[2]};
-            const int gi = cgc / CG;
-            sv[u] = sc[(int64_t)row * NG + gi];
-            zv[u] = zp[(int64_t)row * NG + gi];
-#pragma unroll
-            for (int m = 0; m < M; m++) {
-                const uint4* xp = reinterpret_cast<const uint4*>(x + (int64_t)m * K + cgc * 32);
-#pragma unroll
-                for (int qd = 0; qd < 4; qd++)
-                    xv[u][m][qd] = xp[qd];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kGroupsPerBatch; u++) {
-            if (!on[u])
-                continue;
-            const ZeroSub nz = make_zero_sub(zv[u]);
-            uint32_t p[16];
-            decode_group(cw[u].x, cw[u].y, cw[u].z, mg, nz, p);
-            const float s = h2f((uint16_t)sv[u]);
-#pragma unroll
-            for (int m = 0; m < M; m++) {
-                float part = 0.0f;
-#pragma unroll
-                for (int qd = 0; qd < 4; qd++) {
-                    part = dot2(p[4 * qd + 0], xv[u][m][qd].x, part);
-                    part = dot2(p[4 * qd + 1], xv[u][m][qd].y, part);
-                    part = dot2(p[4 * qd + 2], xv[u][m][qd].z, part);
-                    part = dot2(p[4 * qd + 3], xv[u][m][qd].w, part);
-                }
-                acc[m] = __builtin_fmaf(s, part, acc[m]);
-            }
-        }
-    }
-    // the weak columns: exact fp16 products, fp32 sums
-    for (int c = lane; c < k; c += 64) {
-        int j = idx[c];
-        j = (j >= 0 && j < K) ? j : 0;
-        const float w = h2f(ww[(int64_t)row * k + c]);
-#pragma unroll
-        for (int m = 0; m < M; m++)
-            acc[m] = __builtin_fmaf(w, h2f(x[(int64_t)m * K + j]), acc[m]);
-    }
-#pragma unroll
-    for (int m = 0; m < M; m++) {
-        const float t = wave_sum(acc[m]);
-        if (lane == 0)
-            y[(int64_t)m * N + row] = f2h(t);
-    }
-}
-
 }  // namespace
 
 bool grouped_size_supported(int64_t G, int64_t K)
@@ -241,32 +154,6 @@ hipError_t launch_pack_grouped(const uint16_t* W, int64_t N, int64_t K, const in
     const int64_t wb = (N * k + 255) / 256;
     hipLaunchKernelGGL(k_weak_copy, dim3((unsigned)(wb < 4096 ? wb : 4096)), dim3(256), 0, s, W, N, K, idx, k, ww);
     return hipGetLastError();
-}
-
-hipError_t launch_linear_grouped(const LinearDesc& d, int64_t G, int64_t M, hipStream_t s)
-{
-    const unsigned blocks = (unsigned)((d.N + 3) / 4);
-    // with no weak columns the weak arrays are never read; pass valid pointers anyway
-    const int32_t* idx = d.k > 0 ? d.idx : reinterpret_cast<const int32_t*>(d.x);
-    const uint16_t* ww = d.k > 0 ? d.ww : d.s;
-    hipError_t e = hipSuccess;
-    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += kGroupedMaxM) {
-        const int64_t mm = M - m0 < kGroupedMaxM ? M - m0 : kGroupedMaxM;
-        const uint16_t* xm = d.x + m0 * d.K;
-        uint16_t* ym = d.y + m0 * d.N;
-#define OWQ_LG(MM)                                                                                         \
-    hipLaunchKernelGGL((k_linear_grouped<MM>), dim3(blocks), dim3(256), 0, s, d.q, d.s, d.z, idx, ww, xm, ym, \
-                       (int32_t)d.N, (int32_t)d.K, d.k, (int32_t)G)
-        switch (mm) {
-        case 1: OWQ_LG(1); break;
-        case 2: OWQ_LG(2); break;
-        case 3: OWQ_LG(3); break;
-        default: OWQ_LG(4); break;
-        }
-#undef OWQ_LG
-        e = hipGetLastError();
-    }
-    return e;
 }
 
 }  // namespace owq

@@ -108,11 +108,12 @@ bool mfv_fits(int64_t M, int64_t K);
 bool decode_on_matrix_cores(int64_t M);
 // Group-wise form: a step and zero point per (row, group of G columns), G in
 // {32, 64, ..., 2048} dividing K; scales / zeros [N][K/G].
-constexpr int kGroupedMaxM = 4;  // tokens per product launch (larger M: token slices)
 bool grouped_size_supported(int64_t G, int64_t K);
 hipError_t launch_pack_grouped(const uint16_t* W, int64_t N, int64_t K, const int32_t* idx, int32_t k, int64_t G,
                                uint32_t* q, uint16_t* scales, uint8_t* zeros, uint16_t* ww, hipStream_t s);
-hipError_t launch_linear_grouped(const LinearDesc& d, int64_t G, int64_t M, hipStream_t s);
+// Group-wise decode of `count` layers (count <= kGemvMaxLayers) in one launch,
+// 1 <= M <= kGemvMaxM tokens; groups[l]: columns per scale group of layer l.
+hipError_t launch_gemv_grouped(const LinearDesc* d, const int64_t* groups, int count, int M, hipStream_t s);
 // Matrix-core GEMM for larger M.
 hipError_t launch_gemm(const LinearDesc& d, int64_t M, hipStream_t s);
 

@@ -84,6 +84,8 @@ EXPORTS = {
                                           ctypes.POINTER(_P), _I32, _I64, _P]),
     "owq_pack_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _I64, _P, _P, _P, _P, _P]),
     "owq_linear_grouped": (ctypes.c_int, [ctypes.POINTER(OwqGroupedLayer), _P, _I64, _P, _P]),
+    "owq_linear_grouped_batched": (ctypes.c_int, [ctypes.POINTER(OwqGroupedLayer), ctypes.POINTER(_P),
+                                                  ctypes.POINTER(_P), _I32, _I64, _P]),
     "owq_stream_read_sink_words": (_I64, [_I64]),
     "owq_stream_read": (ctypes.c_int, [_P, _I64, _P, _I64, _P]),
 }
@@ -712,6 +714,27 @@ def linear_grouped(layer: dict, x: torch.Tensor, y: torch.Tensor | None = None, 
         y = torch.empty((M, L.N), dtype=torch.float16, device=x.device)
     _check(lib().owq_linear_grouped(ctypes.byref(L), _ptr(x), M, _ptr(y), _stream(stream)), "owq_linear_grouped")
     return y
+
+
+def linear_grouped_batched(layers: list, xs: list, ys: list | None = None, stream=None) -> list:
+    """owq_linear_grouped for several group-wise layers at the same M in one
+    launch (M <= 4)."""
+    if not layers or len(xs) != len(layers) or (ys is not None and len(ys) != len(layers)):
+        raise ValueError("layers, xs (and ys) must be non-empty lists of one length")
+    Ls = (OwqGroupedLayer * len(layers))()
+    M = None
+    out = []
+    for i, lay in enumerate(layers):
+        Ls[i] = grouped_layer_struct(lay)
+        y = None if ys is None else ys[i]
+        M = _xy_shapes(Ls[i].N, Ls[i].K, xs[i], y, f"layer {i}: ", M)
+        _on_device((f"layer {i}: x", xs[i]), (f"layer {i}: y", y), *_layer_named(lay, f"layer {i}: "))
+        out.append(y if y is not None else torch.empty((M, Ls[i].N), dtype=torch.float16, device=xs[i].device))
+    xp = (_P * len(layers))(*[x.data_ptr() for x in xs])
+    yp = (_P * len(layers))(*[y.data_ptr() for y in out])
+    _check(lib().owq_linear_grouped_batched(Ls, xp, yp, len(layers), M, _stream(stream)),
+           "owq_linear_grouped_batched")
+    return out
 
 
 def linear_backward_workspace_bytes(N: int, K: int, k: int) -> int:

@@ -388,3 +388,19 @@ def test_linear_grouped_validation(lib):
     assert f(layer(bits=4), FAKE, 1, FAKE, None) == 5
     assert f(layer(k=300), FAKE, 1, FAKE, None) == 3
     assert f(layer(), FAKE + 8, 1, FAKE, None) == 4
+
+
+def test_linear_grouped_batched_validation(lib):
+    from mixed_precision_weight_amd import owq
+    P = ctypes.c_void_p
+    Ls = (owq.OwqGroupedLayer * 2)(owq.OwqGroupedLayer(8, 256, 128, 2, 3, FAKE, FAKE, FAKE, FAKE, FAKE),
+                                   owq.OwqGroupedLayer(8, 256, 96, 2, 3, FAKE, FAKE, FAKE, FAKE, FAKE))
+    xs = (P * 2)(FAKE, FAKE)
+    ys = (P * 2)(FAKE, FAKE)
+    f = lib.owq_linear_grouped_batched
+    assert f(None, xs, ys, 2, 1, None) == 1
+    assert f(Ls, xs, ys, 0, 1, None) == 5
+    assert f(Ls, xs, ys, 1, 5, None) == 5      # more than 4 tokens
+    assert f(Ls, xs, ys, 2, 1, None) == 5      # layer 1: G = 96
+    bad = (P * 2)(FAKE + 8, FAKE)
+    assert f(Ls, bad, ys, 1, 1, None) == 4

@@ -98,3 +98,23 @@ def test_degenerate_groups(owq):
     idx = np.concatenate([np.arange(64, 128), [200, 255]]).astype(np.int32)
     x = synth.activations(synth.LayerSpec("deg", N, K, len(idx), 0.02, 2, 20.0), 13, 2)
     _run(owq, W, idx, G, [x[:1], x], "degenerate groups")
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_batched_matches_single(owq, M):
+    """owq_linear_grouped_batched: several group-wise layers of different shapes
+    and group sizes in one launch give the single calls' outputs bit for bit."""
+    import torch
+    rng = np.random.default_rng(40 + M)
+    layers, xs = [], []
+    for N, K, k, G in [(37, 4096, 130, 2048), (64, 640, 7, 128), (5, 96, 1, 32), (130, 8192, 63, 64), (16, 256, 0, 256)]:
+        W = synth.random_layer(rng, N, K, 0.02)
+        idx = np.sort(rng.choice(K, k, replace=False)).astype(np.int32)
+        layers.append(owq.pack_grouped(dev(W), dev(idx), G))
+        xs.append(dev((rng.standard_normal((M, K)) * 2).astype(np.float16)))
+    print(f"grouped batched: {len(layers)} layers, M={M}", flush=True)
+    singles = [owq.linear_grouped(p, x) for p, x in zip(layers, xs)]
+    ys = owq.linear_grouped_batched(layers, xs)
+    torch.cuda.synchronize()
+    for li, (a, b) in enumerate(zip(ys, singles)):
+        assert host(a).tobytes() == host(b).tobytes(), f"layer {li} M={M}"
