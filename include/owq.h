@@ -46,7 +46,9 @@
  *     reported as OWQ_ERR_HIP.
  *   - Ownership: the caller allocates and owns every buffer; the library keeps no
  *     pointer after a call returns and allocates no device memory in these calls.
- *   - Thread safety: no mutable global state except the thread-local error text.
+ *   - Thread safety: no mutable global state except the thread-local error text
+ *     and, for owq_calibrate_score_noalloc, the per-device address of its static
+ *     scratch array (looked up once per device, under a lock).
  *   - Limits: 1 <= N, M, T; 32 <= K <= 65536 with K % 32 == 0; 0 <= k <= K;
  *     bits == 3. Device pointers must be aligned to their element size (qcodes and
  *     weak_idx: 4 bytes, fp16 arrays: 2 bytes, fp64 arrays: 8 bytes), and x / X / W
