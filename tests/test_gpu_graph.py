@@ -1,7 +1,8 @@
 """The whole path recorded once in a HIP graph and replayed.
 
 Calibration, weak-column selection, packing, decode on the vector ALUs
-(M = 1) and on the matrix cores (M = 8), and prefill (M = 256) are captured
+(M = 1, and M = 2 with its products on the matrix cores) and on the matrix
+cores (M = 8), prefill (M = 256), and the group-wise pack and product are captured
 with torch's graph API. The library launches kernels only: no allocation, no
 copy-engine clears, no host synchronisation. Every replay must then equal the
 eager result bit for bit, since the kernels are deterministic. The outputs are
@@ -30,7 +31,11 @@ def _path(owq, W, X, xs, ws, k):
     idx = owq.select_weak(score, k)
     p = owq.pack(W, idx)
     ys = [owq.linear(p, x) for x in xs]
-    return [lam, score, idx, p["qcodes"], p["scales"], p["zeros"], p["w_weak"]] + ys
+    # the group-wise form (groups of 128 columns) on the same weak set
+    g = owq.pack_grouped(W, idx, 128)
+    yg = owq.linear_grouped_batched([g], [xs[1][:2]])[0]
+    return [lam, score, idx, p["qcodes"], p["scales"], p["zeros"], p["w_weak"]] + ys + \
+        [g["qcodes"], g["scales"], g["zeros"], yg]
 
 
 @pytest.mark.parametrize("workload,li", [("opt125m_q_proj", 0), ("llama7b_layer_decode", 6)])
@@ -43,7 +48,7 @@ def test_graph_replay_matches_eager(owq, workload, li):
     X = dev(synth.calibration(spec, seed, cfg.T))
     x = dev(synth.activations(spec, seed, 8))
     xp = dev(synth.activations(spec, seed + 500, 256))
-    xs = [x[:1], x, xp]
+    xs = [x[:1], x[:2], x, xp]
     ws = torch.empty(max(owq.calibrate_workspace_bytes(spec.N, spec.K, cfg.T), 256), dtype=torch.uint8,
                      device="cuda:0")
     print(f"graph replay: {cfg.name}/{spec.name} {spec.N}x{spec.K} k={spec.k} T={cfg.T}", flush=True)
@@ -63,8 +68,8 @@ def test_graph_replay_matches_eager(owq, workload, li):
         outs = _path(owq, W, X, xs, ws, spec.k)
     torch.cuda.synchronize()
 
-    names = ["lambda", "score", "weak_idx", "qcodes", "scales", "zeros", "w_weak", "y(M=1)", "y(M=8)",
-             "y(M=256)"]
+    names = ["lambda", "score", "weak_idx", "qcodes", "scales", "zeros", "w_weak", "y(M=1)", "y(M=2)", "y(M=8)",
+             "y(M=256)", "grouped qcodes", "grouped scales", "grouped zeros", "grouped y(M=2)"]
     for rep in range(3):
         for t in outs:
             t.zero_()
@@ -74,4 +79,5 @@ def test_graph_replay_matches_eager(owq, workload, li):
             assert host(t).tobytes() == a.tobytes(), f"replay {rep}: {name} differs from the eager result"
         again = _path(owq, W, X, xs, ws, spec.k)  # eager work between replays
         torch.cuda.synchronize()
+        assert host(again[-5]).tobytes() == eager[-5].tobytes()
         assert host(again[-1]).tobytes() == eager[-1].tobytes()
