@@ -342,8 +342,9 @@ size_t owq_linear_storage_workspace_bytes(int64_t K, int32_t k, int64_t M);
  * count and L->qcodes the storage-form codes (NULL allowed when k == K). The
  * extra work of this form: x at the dense columns is gathered into the
  * workspace, the dense product runs as a layer of ceil((K-k)/32)*32 columns, and
- * the weak columns' product is added to y afterwards (so y is rounded to fp16
- * twice when 0 < k < K). workspace: >= owq_linear_storage_workspace_bytes(K, k,
+ * the weak columns' product goes into the same fp32 sum when that product runs
+ * on the vector-ALU decode (M <= 2 by default; one fp16 rounding), else it is
+ * added to y afterwards (y then rounded to fp16 twice when 0 < k < K). workspace: >= owq_linear_storage_workspace_bytes(K, k,
  * M) bytes, 256-byte aligned, contents ignored; calls sharing it must be ordered.
  * Errors as owq_linear, plus OWQ_ERR_WORKSPACE. */
 owq_status owq_linear_storage(const owq_layer* L, const uint16_t* x, int64_t M,

@@ -62,6 +62,8 @@ struct GemvLayer {
     int32_t N, K, k;
     int32_t block0;  // first block of this layer
     int32_t gsh;     // group-wise form: log2 of the 32-column code groups per scale group
+    const uint16_t* xw;  // x of the weak columns (x itself, or the full x of the storage-favoured form)
+    int32_t kw;          // its row length
 };
 
 struct GemvBatch {
@@ -138,7 +140,8 @@ __device__ __forceinline__ void gemv_body(const GemvBatch& b)
     const uint16_t* __restrict__ X = b.L[li].x;
     const int32_t* __restrict__ IDX = b.L[li].idx;
     const uint16_t* __restrict__ WW = b.L[li].ww;
-    const int N = b.L[li].N, K = b.L[li].K, k = b.L[li].k;
+    const uint16_t* __restrict__ XW = b.L[li].xw;
+    const int N = b.L[li].N, K = b.L[li].K, k = b.L[li].k, KW = b.L[li].kw;
     const int G = K >> 5;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -229,10 +232,10 @@ __device__ __forceinline__ void gemv_body(const GemvBatch& b)
     for (int v = 0; v < 2; v++) {
         const int c = lane + 64 * v;
         int j = widx[v];
-        j = (j >= 0 && j < K) ? j : 0;
+        j = (j >= 0 && j < KW) ? j : 0;
 #pragma unroll
         for (int m = 0; m < M; m++) {
-            const float xv = h2f(X[(int64_t)m * K + j]);
+            const float xv = h2f(XW[(int64_t)m * KW + j]);
             xw[m][v] = c < k ? xv : 0.0f;
         }
     }
@@ -379,8 +382,8 @@ __device__ __forceinline__ void gemv_body(const GemvBatch& b)
                 const int row = min(row0 + r, N - 1);
                 for (int c = lane + 128; c < k; c += 64) {
                     int j = IDX[c];
-                    j = (j >= 0 && j < K) ? j : 0;
-                    part[r / 4][r % 4] += h2f(WW[(int64_t)row * k + c]) * h2f(X[(int64_t)m * K + j]);
+                    j = (j >= 0 && j < KW) ? j : 0;
+                    part[r / 4][r % 4] += h2f(WW[(int64_t)row * k + c]) * h2f(XW[(int64_t)m * KW + j]);
                 }
             }
         }
@@ -483,6 +486,8 @@ int build_batch(const LinearDesc* d, int count, const int64_t* groups, GemvBatch
         L.K = (int32_t)d[l].K;
         L.k = d[l].k;
         L.block0 = nblocks;
+        L.xw = d[l].xw ? d[l].xw : d[l].x;
+        L.kw = (int32_t)(d[l].xw ? d[l].kw : d[l].K);
         L.gsh = 0;
         if (groups)
             while ((int64_t)32 << L.gsh < groups[l])

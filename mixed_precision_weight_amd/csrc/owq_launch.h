@@ -83,6 +83,11 @@ struct LinearDesc {
     uint16_t* y;
     int64_t N, K;
     int32_t k;
+    // x the weak columns are gathered from, with rows of kw columns (NULL: x and
+    // K); the storage-favoured form gathers them from the full x while the dense
+    // codes run against x at the dense columns (decode kernel on the vector ALUs only)
+    const uint16_t* xw = nullptr;
+    int64_t kw = 0;
 };
 
 constexpr int kGemvMaxM = 4;        // tokens per GEMV launch

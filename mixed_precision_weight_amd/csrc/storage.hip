@@ -251,6 +251,7 @@ hipError_t launch_linear_storage_batched(const LinearDesc* d, int count, int64_t
             dense.push_back(dd);
         }
         hipError_t e = hipSuccess;
+        bool fused = false;  // the weak columns went with the dense products
         if (g.count > 0) {
             hipLaunchKernelGGL(k_gather_dense_batched, dim3((unsigned)g.b0[g.count], (unsigned)std::min<int64_t>(M, 64)),
                                dim3(256), 0, s, g, M);
@@ -262,6 +263,22 @@ hipError_t launch_linear_storage_batched(const LinearDesc* d, int count, int64_t
             const bool mat = decode_on_matrix_cores(M);
             for (const LinearDesc& dd : dense)
                 one = one && (mat ? mfv_fits(M, dd.K) : gemv_fits(M, dd.K));
+            fused = one && !mat;
+            if (fused) {
+                // the vector-ALU decode adds the weak columns itself, gathered from the
+                // full x at the original indices: one fp32 sum and one fp16 rounding
+                int j = 0;
+                for (int i = 0; i < n; i++) {
+                    if (storage_dense_cols32(dl[i].K, dl[i].k) == 0)
+                        continue;
+                    LinearDesc& dd = dense[j++];
+                    dd.k = dl[i].k;
+                    dd.idx = dl[i].idx;
+                    dd.ww = dl[i].ww;
+                    dd.xw = dl[i].x;
+                    dd.kw = dl[i].K;
+                }
+            }
             if (one) {
                 e = mat ? launch_mfv(dense.data(), (int)dense.size(), (int)M, s)
                         : launch_gemv(dense.data(), (int)dense.size(), (int)M, s);
@@ -278,7 +295,7 @@ hipError_t launch_linear_storage_batched(const LinearDesc* d, int count, int64_t
         StorageBatch w{};
         for (int i = 0; i < n; i++) {
             const int64_t Kd32 = storage_dense_cols32(dl[i].K, dl[i].k);
-            if (dl[i].k == 0 && Kd32 > 0)
+            if ((dl[i].k == 0 || fused) && Kd32 > 0)
                 continue;
             StorageStep& L = w.L[w.count];
             L = StorageStep{dl[i].x, dl[i].idx, dl[i].ww, nullptr, dl[i].y, dl[i].K, Kd32, dl[i].N, dl[i].k,
