@@ -705,8 +705,8 @@ def main():
     if not args.no_extras:
         # the storage-favoured form of the same layer at M = 1 (the pages' other
         # format): the dense codes of K - k columns, x gathered at the dense
-        # columns, the weak columns added after the 3-bit product; 3 launches per
-        # linear, compared with the one launch per layer of the latency form
+        # columns, the weak columns in the decode's own sum; 2 launches per
+        # layer, compared with the one launch per layer of the latency form
         print("bench: storage-favoured decode", file=sys.stderr, flush=True)
         # ROTATE copies in the storage form, the 7 linears of a copy in one
         # owq_linear_storage_batched call; device time from a HIP graph
@@ -727,9 +727,9 @@ def main():
         sto_bytes = sum(3 * s.N * (s.K - s.k) // 8 + 3 * s.N + 2 * s.N * s.k + 2 * s.K for s in specs)
         result["kernels"]["decode_storage_form"] = dict(
             hbm_entry(sto_bytes, t, "storage-favoured form at M=1: owq_linear_storage_batched over the 7 linears "
-                                    "(x gathered at the dense columns, k_gemv<1> over K - k columns, weak columns "
-                                    "added: 3 launches per layer), 8 copies rotated, replayed from a HIP graph "
-                                    "(device time)"),
+                                    "(x gathered at the dense columns, then k_gemv<1> over K - k columns with the weak "
+                                    "columns from the full x in the same sum: 2 launches per layer), 8 copies "
+                                    "rotated, replayed from a HIP graph (device time)"),
             us_one_call_per_linear_graph=round(t_one * 1e6, 2),
             us_latency_form=round(dec_s * 1e6, 2))
         del sto, wss
