@@ -88,6 +88,11 @@ constexpr int kNonTemporal = 2;  // buffer-load cache-policy bits: nt
 // Rows per wavefront: three (71 registers at M = 1, seven waves per SIMD) was
 // faster than two, four (109 registers, four waves) and eight at M = 1 and 2.
 constexpr int kRowsPerWave = 3;
+// Below this many three-row blocks (one linear of a 7B layer: 342-918; the
+// layer's 7 in one launch: 3,543) one token runs two rows per wave: measured
+// 38.9-39.1 against 42.2-42.3 us for the 7 linears as 7 launches, and 21.1
+// against 20.4-20.6 us for them in one launch
+constexpr int kSmallLaunchBlocks = 1024;
 
 __device__ __forceinline__ float f_of(uint32_t v) { return __builtin_bit_cast(float, v); }
 __device__ __forceinline__ uint32_t u_of(float v) { return __builtin_bit_cast(uint32_t, v); }
@@ -399,6 +404,9 @@ __device__ __forceinline__ void gemv_body(const GemvBatch& b)
 
 template <int M>
 __global__ __launch_bounds__(256) void k_gemv(GemvBatch b) { gemv_body<M, false, kRowsPerWave>(b); }
+// one token, two rows per wave: for launches too small to fill the GPU with
+// three-row waves (a single linear), half as many rows per block again
+__global__ __launch_bounds__(256) void k_gemv_r2(GemvBatch b) { gemv_body<1, false, 2>(b); }
 // the matrix-core products at five waves per SIMD (95 registers, no spills);
 // without the occupancy bound the compiler takes 138 and runs three
 template <int M>
@@ -457,7 +465,7 @@ namespace {
 // The launch arguments of a batch (layers with the longest rows first: their
 // blocks run longest); groups: the group-wise form's columns per scale group,
 // per layer, or NULL for the per-row form. Returns the block count.
-int build_batch(const LinearDesc* d, int count, const int64_t* groups, GemvBatch& b)
+int build_batch(const LinearDesc* d, int count, const int64_t* groups, GemvBatch& b, int rows_per_wave)
 {
     int order[kGemvMaxLayers];
     for (int l = 0; l < count; l++)
@@ -492,7 +500,7 @@ int build_batch(const LinearDesc* d, int count, const int64_t* groups, GemvBatch
         if (groups)
             while ((int64_t)32 << L.gsh < groups[l])
                 L.gsh++;
-        const int rows = 4 * kRowsPerWave;
+        const int rows = 4 * rows_per_wave;
         nblocks += (int)((d[l].N + rows - 1) / rows);
     }
     return nblocks;
@@ -505,8 +513,13 @@ int build_batch(const LinearDesc* d, int count, const int64_t* groups, GemvBatch
 hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
 {
     GemvBatch b;
-    const int nblocks = build_batch(d, count, nullptr, b);
+    int nblocks = build_batch(d, count, nullptr, b, kRowsPerWave);
     const size_t lds = (size_t)M * kChunkTiles * 4 * kQuadStride * 16;
+    if (M == 1 && nblocks < kSmallLaunchBlocks && !gemv_products_on_matrix_cores(1)) {
+        nblocks = build_batch(d, count, nullptr, b, 2);
+        hipLaunchKernelGGL(k_gemv_r2, dim3(nblocks), dim3(256), lds, s, b);
+        return hipGetLastError();
+    }
     switch (M) {
     case 1: return launch_m<1>(b, nblocks, lds, s);
     case 2: return launch_m<2>(b, nblocks, lds, s);
@@ -518,7 +531,7 @@ hipError_t launch_gemv(const LinearDesc* d, int count, int M, hipStream_t s)
 hipError_t launch_gemv_grouped(const LinearDesc* d, const int64_t* groups, int count, int M, hipStream_t s)
 {
     GemvBatch b;
-    const int nblocks = build_batch(d, count, groups, b);
+    const int nblocks = build_batch(d, count, groups, b, kRowsPerWave);
     const size_t lds = (size_t)M * kChunkTiles * 4 * kQuadStride * 16;
 #define OWQ_GG(MM) hipLaunchKernelGGL((k_gemv_grouped<MM>), dim3(nblocks), dim3(256), lds, s, b)
     switch (M) {
